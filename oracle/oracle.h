@@ -1,0 +1,80 @@
+/*
+ * oracle.h -- plain sequential fp64 CPU oracle for the seven credit-assignment
+ * estimators.  TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may call it; the product path never does.
+ * It shares no header, helper or constant with the HIP library.
+ *
+ * Source of the definitions: "rl-triton: High-Performance Triton GPU Kernels
+ * for Reinforcement Learning Credit Assignment" (paperlayer.ai summary):
+ *   §1 Introduction          -- the backward recurrence and its forward mirror,
+ *   §2.1 Motivation          -- GAE as a strict T-step chain,
+ *   §3.2 Episode-boundary    -- termination, truncation, rollout-window edge,
+ *   §3.3 Algorithm-specific  -- Retrace uses the next-step importance weight;
+ *                               prefix sums are segmented forward scans,
+ *   §5 Correctness analysis  -- forward resets use the previous step's done,
+ *   §8 Related work          -- V-Trace (Espeholt et al. 2018) and
+ *                               Retrace(lambda) (Munos et al. 2016),
+ *   §6 Benchmark protocol    -- an independent sequential reference.
+ *
+ * Layout: every per-step array is dense row-major [num_envs, T], element
+ * (n, t) at n*T + t.  fp32 inputs are widened to double exactly; flags are
+ * bytes, nonzero = set.  Outputs are double (int32 for the integer prefix sum).
+ * Every function walks each row strictly one step at a time.
+ */
+#ifndef RLCA_ORACLE_H
+#define RLCA_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Forward-scan reset conventions (§3.3 "configurable boundary conventions"). */
+#define ORACLE_RESET_ON_START 0   /* flag[t] = 1: step t starts a new episode      */
+#define ORACLE_RESET_AFTER_DONE 1 /* flag[t-1] = 1: step t-1 ended an episode (§5) */
+
+/* truncated / trunc_values / bootstrap may be NULL (no truncation; zero bootstrap). */
+void oracle_gae(const float *rewards, const float *values, const uint8_t *terminated,
+                const uint8_t *truncated, const float *trunc_values, const float *bootstrap,
+                double gamma, double lam, int64_t num_envs, int64_t T,
+                double *advantages, double *returns);
+
+void oracle_td_lambda(const float *rewards, const float *values, const uint8_t *terminated,
+                      const uint8_t *truncated, const float *trunc_values,
+                      const float *bootstrap, double gamma, double lam, int64_t num_envs,
+                      int64_t T, double *returns);
+
+void oracle_discounted_returns(const float *rewards, const uint8_t *terminated,
+                               const uint8_t *truncated, const float *trunc_values,
+                               const float *bootstrap, double gamma, int64_t num_envs,
+                               int64_t T, double *returns);
+
+void oracle_vtrace(const float *rewards, const float *values, const float *behaviour_logp,
+                   const float *target_logp, const uint8_t *terminated,
+                   const uint8_t *truncated, const float *trunc_values,
+                   const float *bootstrap, double gamma, double lam, double rho_bar,
+                   double c_bar, int64_t num_envs, int64_t T, double *vs,
+                   double *pg_advantages);
+
+void oracle_retrace(const float *rewards, const float *q_values, const float *expected_q,
+                    const float *behaviour_logp, const float *target_logp,
+                    const uint8_t *terminated, const uint8_t *truncated,
+                    const float *trunc_values, const float *bootstrap, double gamma,
+                    double lam, double c_bar, int64_t num_envs, int64_t T, double *q_ret);
+
+void oracle_eligibility_traces(const float *increments, const uint8_t *flags, int convention,
+                               double gamma, double lam, int64_t num_envs, int64_t T,
+                               double *traces);
+
+void oracle_episodic_prefix_sum_f32(const float *x, const uint8_t *flags, int convention,
+                                    int64_t num_envs, int64_t T, double *out);
+
+void oracle_episodic_prefix_sum_i32(const int32_t *x, const uint8_t *flags, int convention,
+                                    int64_t num_envs, int64_t T, int32_t *out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

@@ -1,0 +1,422 @@
+"""Pins for the fp64 oracle: things other than the oracle itself that fix its values.
+
+* brute-force unrolled sums (tests/brute.py) on tiny inputs, exhaustive over the
+  per-step flag patterns (none / terminated / truncated / both);
+* closed forms and textbook special cases;
+* identities between estimators (GAE at lambda=0 and lambda=1, TD(lambda) as
+  GAE plus values, V-Trace on-policy, Retrace at lambda=0 and on-policy);
+* no-leak invariance across done steps and the window-split (carry) invariant;
+* the worked four-thread scan trace of the rl-triton summary, Appendix A.
+"""
+import ast
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import brute
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+RTOL = 1e-11
+
+
+def close(a, b, rtol=RTOL):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    assert a.shape == b.shape
+    err = np.max(np.abs(a - b) / (1.0 + np.abs(b))) if a.size else 0.0
+    assert err <= rtol, f"max scaled error {err}"
+
+
+def flag_patterns(T):
+    """All 4^T per-step (terminated, truncated) patterns as rows."""
+    pats = np.array(list(itertools.product(range(4), repeat=T)), dtype=np.uint8)
+    return (pats & 1).astype(np.uint8), ((pats >> 1) & 1).astype(np.uint8)
+
+
+def rand_inputs(seed, N, T):
+    rng = np.random.default_rng(seed)
+    f = lambda *s: rng.standard_normal(s).astype(np.float32)  # noqa: E731
+    return dict(r=f(N, T), v=f(N, T), tv=f(N, T), b=f(N), q=f(N, T), eq=f(N, T),
+                blogp=rng.normal(-1, 0.5, (N, T)).astype(np.float32),
+                tlogp=rng.normal(-1, 0.5, (N, T)).astype(np.float32),
+                x=rng.random((N, T)).astype(np.float32))
+
+
+# ----------------------------------------------------------------- Appendix A
+
+
+def _eval(expr, env):
+    """Evaluate a +/* expression over named integers (no eval of arbitrary code)."""
+    def go(node):
+        if isinstance(node, ast.Expression):
+            return go(node.body)
+        if isinstance(node, ast.BinOp) and isinstance(node.op, ast.Add):
+            return go(node.left) + go(node.right)
+        if isinstance(node, ast.BinOp) and isinstance(node.op, ast.Mult):
+            return go(node.left) * go(node.right)
+        if isinstance(node, ast.Name):
+            return env[node.id]
+        raise ValueError(f"unsupported node {ast.dump(node)}")
+    return go(ast.parse(expr, mode="eval"))
+
+
+def combine(later, earlier_in_list):
+    """The summary's operator: (aB, bB) (+) (aA, bA) = (aB + bB*aA, bA*bB)."""
+    (ab, bb), (aa, ba) = later, earlier_in_list
+    return (ab + bb * aa, ba * bb)
+
+
+def test_appendix_a_four_thread_trace():
+    g = json.load(open(os.path.join(GOLDEN, "appendix_a_four_thread_trace.json")))
+    rng = np.random.default_rng(0)
+    for _ in range(20):
+        env = {f"a{i}": int(rng.integers(-50, 50)) for i in range(4)}
+        env.update({f"b{i}": int(rng.integers(-50, 50)) for i in range(4)})
+        threads = [tuple(_eval(e, env) for e in g["initial"][f"T{i}"]) for i in range(1, 5)]
+        # Hillis-Steele: at stride s thread i combines its tuple with thread i-s's
+        # tuple from the previous pass (all reads before writes).
+        for p in range(g["passes"]):
+            s = 1 << p
+            prev = list(threads)
+            for i in range(len(threads)):
+                if i - s >= 0:
+                    threads[i] = combine(prev[i], prev[i - s])
+            key = f"after_pass_{p + 1}"
+            for name, exprs in g[key].items():
+                idx = int(name[1:]) - 1
+                assert threads[idx] == tuple(_eval(e, env) for e in exprs), (key, name)
+
+
+def test_combine_is_associative_exact():
+    rng = np.random.default_rng(1)
+    for _ in range(1000):
+        x, y, z = [(int(rng.integers(-10**6, 10**6)), int(rng.integers(-10**6, 10**6)))
+                   for _ in range(3)]
+        assert combine(combine(x, y), z) == combine(x, combine(y, z))
+
+
+def test_oracle_gae_equals_appendix_a_full_fold():
+    """A 4-step row with no flags: alpha_t = delta_t, beta_t = gamma*lambda for
+    t < 3 and 0 at the window edge; the trace's full fold equals A_0."""
+    d = rand_inputs(2, 1, 4)
+    gamma, lam = 0.9, 0.8
+    r, v, b = d["r"][0].astype(float), d["v"][0].astype(float), float(d["b"][0])
+    nv = [v[1], v[2], v[3], b]
+    env = {f"a{t}": r[t] + gamma * nv[t] - v[t] for t in range(4)}
+    env.update({f"b{t}": gamma * lam if t < 3 else 0.0 for t in range(4)})
+    g = json.load(open(os.path.join(GOLDEN, "appendix_a_four_thread_trace.json")))
+    full = _eval(g["after_pass_2"]["T4"][0], env)
+    adv, _ = oracle.gae(d["r"], d["v"], np.zeros((1, 4), np.uint8), bootstrap=d["b"],
+                        gamma=gamma, lam=lam)
+    assert abs(adv[0, 0] - full) <= 1e-12 * (1 + abs(full))
+
+
+# ------------------------------------------------------ brute force, exhaustive
+
+
+@pytest.mark.parametrize("T", [1, 2, 5])
+def test_backward_estimators_vs_brute_force_all_flag_patterns(T):
+    term, trunc = flag_patterns(T)
+    N = term.shape[0]
+    d = rand_inputs(10 + T, N, T)
+    g, lam = 0.93, 0.7
+    adv, ret = oracle.gae(d["r"], d["v"], term, trunc, d["tv"], d["b"], g, lam)
+    badv, bret = brute.gae(d["r"], d["v"], term, trunc, d["tv"], d["b"], g, lam)
+    close(adv, badv)
+    close(ret, bret)
+    close(oracle.td_lambda(d["r"], d["v"], term, trunc, d["tv"], d["b"], g, lam),
+          brute.td_lambda(d["r"], d["v"], term, trunc, d["tv"], d["b"], g, lam))
+    close(oracle.discounted_returns(d["r"], term, trunc, d["tv"], d["b"], g),
+          brute.discounted(d["r"], term, trunc, d["tv"], d["b"], g))
+    vs, pg = oracle.vtrace(d["r"], d["v"], d["blogp"], d["tlogp"], term, trunc, d["tv"],
+                           d["b"], g, lam, 1.3, 0.9)
+    bvs, bpg = brute.vtrace(d["r"], d["v"], d["blogp"], d["tlogp"], term, trunc, d["tv"],
+                            d["b"], g, lam, 1.3, 0.9)
+    close(vs, bvs)
+    close(pg, bpg)
+    close(oracle.retrace(d["r"], d["q"], d["eq"], d["blogp"], d["tlogp"], term, trunc,
+                         d["tv"], d["b"], g, lam, 1.1),
+          brute.retrace(d["r"], d["q"], d["eq"], d["blogp"], d["tlogp"], term, trunc,
+                        d["tv"], d["b"], g, lam, 1.1))
+
+
+@pytest.mark.parametrize("T", [1, 3, 6])
+@pytest.mark.parametrize("conv", [oracle.RESET_ON_START, oracle.RESET_AFTER_DONE])
+def test_forward_scans_vs_brute_force_all_flag_patterns(T, conv):
+    flags = np.array(list(itertools.product(range(2), repeat=T)), dtype=np.uint8)
+    N = flags.shape[0]
+    d = rand_inputs(20 + T, N, T)
+    close(oracle.eligibility_traces(d["x"], flags, conv, 0.97, 0.85),
+          brute.eligibility(d["x"], flags, conv, 0.97, 0.85))
+    close(oracle.episodic_prefix_sum(d["r"], flags, conv), brute.prefix_sum(d["r"], flags, conv))
+    xi = np.random.default_rng(3).integers(-100, 101, (N, T)).astype(np.int32)
+    assert np.array_equal(oracle.episodic_prefix_sum(xi, flags, conv),
+                          brute.prefix_sum(xi, flags, conv))
+
+
+def test_backward_vs_brute_force_random_T8():
+    rng = np.random.default_rng(7)
+    N, T = 64, 8
+    term = (rng.random((N, T)) < 0.15).astype(np.uint8)
+    trunc = (rng.random((N, T)) < 0.15).astype(np.uint8)   # overlaps term: term wins
+    d = rand_inputs(8, N, T)
+    g, lam = 0.99, 0.95
+    close(oracle.gae(d["r"], d["v"], term, trunc, d["tv"], d["b"], g, lam)[0],
+          brute.gae(d["r"], d["v"], term, trunc, d["tv"], d["b"], g, lam)[0])
+    close(oracle.td_lambda(d["r"], d["v"], term, trunc, d["tv"], d["b"], g, lam),
+          brute.td_lambda(d["r"], d["v"], term, trunc, d["tv"], d["b"], g, lam))
+    close(oracle.retrace(d["r"], d["q"], d["eq"], d["blogp"], d["tlogp"], term, trunc,
+                         d["tv"], d["b"], g, lam, 1.0),
+          brute.retrace(d["r"], d["q"], d["eq"], d["blogp"], d["tlogp"], term, trunc,
+                        d["tv"], d["b"], g, lam, 1.0))
+
+
+# --------------------------------------------------------- hand special cases
+
+
+def test_gae_three_step_hand_case():
+    """T=3, terminated after step 1: A_2 bootstraps, A_1 has no successor,
+    A_0 chains into A_1 only."""
+    g, lam = 0.9, 0.5
+    r = np.array([[1.0, 2.0, 3.0]], np.float32)
+    v = np.array([[0.5, -1.0, 2.0]], np.float32)
+    term = np.array([[0, 1, 0]], np.uint8)
+    b = np.array([4.0], np.float32)
+    adv, ret = oracle.gae(r, v, term, bootstrap=b, gamma=g, lam=lam)
+    a2 = 3.0 + g * 4.0 - 2.0
+    a1 = 2.0 - (-1.0)
+    a0 = (1.0 + g * -1.0 - 0.5) + g * lam * a1
+    close(adv[0], [a0, a1, a2], 1e-15)
+    close(ret[0], [a0 + 0.5, a1 - 1.0, a2 + 2.0], 1e-15)
+
+
+def test_last_step_flags_override_bootstrap():
+    r = np.array([[1.0, 1.0]], np.float32)
+    v = np.zeros((1, 2), np.float32)
+    tv = np.array([[0.0, 7.0]], np.float32)
+    b = np.array([100.0], np.float32)
+    g = 0.5
+    none = np.zeros((1, 2), np.uint8)
+    last = np.array([[0, 1]], np.uint8)
+    # not done: bootstrap; terminated: 0; truncated: continuation value.
+    assert oracle.discounted_returns(r, none, None, None, b, g)[0, 1] == 1.0 + 0.5 * 100.0
+    assert oracle.discounted_returns(r, last, None, None, b, g)[0, 1] == 1.0
+    assert oracle.discounted_returns(r, none, last, tv, b, g)[0, 1] == 1.0 + 0.5 * 7.0
+    # both set: terminated wins.
+    assert oracle.discounted_returns(r, last, last, tv, b, g)[0, 1] == 1.0
+
+
+def test_truncation_uses_continuation_not_next_value():
+    d = rand_inputs(30, 4, 6)
+    trunc = np.zeros((4, 6), np.uint8)
+    trunc[:, 2] = 1
+    term = np.zeros((4, 6), np.uint8)
+    a, _ = oracle.gae(d["r"], d["v"], term, trunc, d["tv"], d["b"], 0.9, 0.9)
+    v2 = d["v"].copy()
+    v2[:, 3] += 5.0                    # next episode's first value: must not reach t=2
+    a2, _ = oracle.gae(d["r"], v2, term, trunc, d["tv"], d["b"], 0.9, 0.9)
+    assert np.array_equal(a[:, :3], a2[:, :3])
+    tv2 = d["tv"].copy()
+    tv2[:, 2] += 1.0                   # continuation value: enters A_2 as gamma * 1.0
+    a3, _ = oracle.gae(d["r"], d["v"], term, trunc, tv2, d["b"], 0.9, 0.9)
+    close(a3[:, 2] - a[:, 2], np.full(4, 0.9), 1e-6)
+
+
+def test_vtrace_log_ratio_clip():
+    """One terminated step: vs = v + rho * (r - v), rho = min(rho_bar, exp(clip(l)))."""
+    r = np.array([[2.0], [2.0]], np.float32)
+    v = np.array([[0.5], [0.5]], np.float32)
+    mu = np.array([[0.0], [0.0]], np.float32)
+    pi = np.array([[9.0], [-9.0]], np.float32)
+    term = np.ones((2, 1), np.uint8)
+    vs, pg = oracle.vtrace(r, v, mu, pi, term, gamma=0.9, lam=1.0, rho_bar=1e3, c_bar=1e3)
+    close(vs[:, 0], [0.5 + math.exp(5) * 1.5, 0.5 + math.exp(-5) * 1.5], 1e-15)
+    close(pg[:, 0], [math.exp(5) * 1.5, math.exp(-5) * 1.5], 1e-15)
+
+
+# ---------------------------------------------------- closed forms, identities
+
+
+def test_discounted_constant_reward_closed_form():
+    g, T = 0.97, 40
+    r = np.ones((1, T), np.float32)
+    b = np.array([3.0], np.float32)
+    G = oracle.discounted_returns(r, np.zeros((1, T), np.uint8), bootstrap=b, gamma=g)
+    t = np.arange(T)
+    expect = (1 - g ** (T - t)) / (1 - g) + g ** (T - t) * 3.0
+    close(G[0], expect, 1e-13)
+
+
+def _random_flags(seed, N, T, p=0.1):
+    rng = np.random.default_rng(seed)
+    term = (rng.random((N, T)) < p).astype(np.uint8)
+    trunc = ((rng.random((N, T)) < p) & (term == 0)).astype(np.uint8)
+    return term, trunc
+
+
+def test_gae_lambda_zero_is_one_step_td_error():
+    d = rand_inputs(40, 16, 32)
+    term, trunc = _random_flags(41, 16, 32)
+    g = 0.99
+    adv, _ = oracle.gae(d["r"], d["v"], term, trunc, d["tv"], d["b"], g, 0.0)
+    G0 = oracle.td_lambda(d["r"], d["v"], term, trunc, d["tv"], d["b"], g, 0.0)
+    # TD(0) target r + gamma * next value; minus V gives the TD error.
+    close(adv, G0 - d["v"])
+    # and spelled out directly where the chain continues:
+    cont = (term == 0) & (trunc == 0)
+    cont[:, -1] = False
+    r64, v64 = d["r"].astype(np.float64), d["v"].astype(np.float64)
+    delta = r64[:, :-1] + g * v64[:, 1:] - v64[:, :-1]
+    np.testing.assert_allclose(adv[:, :-1][cont[:, :-1]], delta[cont[:, :-1]], rtol=0,
+                               atol=1e-12)
+
+
+def test_gae_lambda_one_plus_values_is_discounted_return():
+    d = rand_inputs(42, 16, 48)
+    term, trunc = _random_flags(43, 16, 48)
+    _, ret = oracle.gae(d["r"], d["v"], term, trunc, d["tv"], d["b"], 0.98, 1.0)
+    G = oracle.discounted_returns(d["r"], term, trunc, d["tv"], d["b"], 0.98)
+    close(ret, G)
+
+
+def test_td_lambda_equals_gae_return_and_limits():
+    d = rand_inputs(44, 16, 48)
+    term, trunc = _random_flags(45, 16, 48)
+    for lam in (0.0, 0.5, 0.95, 1.0):
+        _, ret = oracle.gae(d["r"], d["v"], term, trunc, d["tv"], d["b"], 0.98, lam)
+        close(oracle.td_lambda(d["r"], d["v"], term, trunc, d["tv"], d["b"], 0.98, lam), ret)
+    close(oracle.td_lambda(d["r"], d["v"], term, trunc, d["tv"], d["b"], 0.98, 1.0),
+          oracle.discounted_returns(d["r"], term, trunc, d["tv"], d["b"], 0.98))
+
+
+def test_vtrace_on_policy_reduces_to_returns():
+    d = rand_inputs(46, 16, 48)
+    term, trunc = _random_flags(47, 16, 48)
+    same = d["blogp"]
+    vs, pg = oracle.vtrace(d["r"], d["v"], same, same, term, trunc, d["tv"], d["b"], 0.99,
+                           1.0, 1.0, 1.0)
+    close(vs, oracle.discounted_returns(d["r"], term, trunc, d["tv"], d["b"], 0.99))
+    vs_l, _ = oracle.vtrace(d["r"], d["v"], same, same, term, trunc, d["tv"], d["b"], 0.99,
+                            0.9, 2.0, 2.0)
+    close(vs_l, oracle.td_lambda(d["r"], d["v"], term, trunc, d["tv"], d["b"], 0.99, 0.9))
+
+
+def test_retrace_lambda_zero_and_on_policy():
+    d = rand_inputs(48, 16, 48)
+    term, trunc = _random_flags(49, 16, 48)
+    g = 0.99
+    q0 = oracle.retrace(d["r"], d["q"], d["eq"], d["blogp"], d["tlogp"], term, trunc,
+                        d["tv"], d["b"], g, 0.0, 1.0)
+    # lambda = 0: expected-SARSA target r + gamma * E_pi Q(s_{t+1}) = TD(0) on expected_q.
+    close(q0, oracle.td_lambda(d["r"], d["eq"], term, trunc, d["tv"], d["b"], g, 0.0))
+    # expected_q == Q and ratios >= 1 with c_bar = 1: c = lambda everywhere, so
+    # Retrace is GAE's return with values := Q.
+    hi = d["blogp"] + 1.0
+    qr = oracle.retrace(d["r"], d["q"], d["q"], d["blogp"], hi, term, trunc, d["tv"], d["b"],
+                        g, 0.9, 1.0)
+    _, ret = oracle.gae(d["r"], d["q"], term, trunc, d["tv"], d["b"], g, 0.9)
+    close(qr, ret)
+
+
+def test_eligibility_closed_form_and_prefix_limit():
+    T = 50
+    x = np.ones((1, T), np.float32)
+    f = np.zeros((1, T), np.uint8)
+    e = oracle.eligibility_traces(x, f, oracle.RESET_ON_START, 0.9, 0.8)
+    t = np.arange(T)
+    close(e[0], (1 - 0.72 ** (t + 1)) / (1 - 0.72), 1e-13)
+    rng = np.random.default_rng(5)
+    x = rng.random((8, T)).astype(np.float32)
+    f = (rng.random((8, T)) < 0.1).astype(np.uint8)
+    close(oracle.eligibility_traces(x, f, 0, 1.0, 1.0), oracle.episodic_prefix_sum(x, f, 0))
+
+
+def test_prefix_sum_plain_cumsum_and_wraparound():
+    rng = np.random.default_rng(6)
+    x = rng.integers(-100, 101, (4, 64)).astype(np.int32)
+    f = np.zeros((4, 64), np.uint8)
+    assert np.array_equal(oracle.episodic_prefix_sum(x, f), np.cumsum(x, axis=1, dtype=np.int32))
+    big = np.full((1, 8), 2**31 - 1, np.int32)
+    out = oracle.episodic_prefix_sum(big, np.zeros((1, 8), np.uint8))
+    expect = (np.arange(1, 9, dtype=np.int64) * (2**31 - 1)).astype(np.uint64)
+    assert np.array_equal(out[0], expect.astype(np.uint32).view(np.int32))
+
+
+def test_reset_conventions_agree_on_shifted_flags():
+    rng = np.random.default_rng(8)
+    N, T = 8, 64
+    starts = (rng.random((N, T)) < 0.1).astype(np.uint8)
+    dones = np.zeros_like(starts)
+    dones[:, :-1] = starts[:, 1:]
+    x = rng.random((N, T)).astype(np.float32)
+    close(oracle.eligibility_traces(x, starts, 0, 0.99, 0.9),
+          oracle.eligibility_traces(x, dones, 1, 0.99, 0.9), 0)
+    xi = rng.integers(-100, 101, (N, T)).astype(np.int32)
+    assert np.array_equal(oracle.episodic_prefix_sum(xi, starts, 0),
+                          oracle.episodic_prefix_sum(xi, dones, 1))
+
+
+# ------------------------------------------------------------------ invariants
+
+
+def test_no_leak_across_done_steps():
+    d = rand_inputs(50, 8, 40)
+    term = np.zeros((8, 40), np.uint8)
+    trunc = np.zeros((8, 40), np.uint8)
+    term[:, 17] = 1
+    trunc[:4, 9] = 1
+    g, lam = 0.99, 0.95
+    base = [
+        oracle.gae(d["r"], d["v"], term, trunc, d["tv"], d["b"], g, lam)[0],
+        oracle.td_lambda(d["r"], d["v"], term, trunc, d["tv"], d["b"], g, lam),
+        oracle.vtrace(d["r"], d["v"], d["blogp"], d["tlogp"], term, trunc, d["tv"], d["b"],
+                      g, 1.0, 1.0, 1.0)[0],
+        oracle.retrace(d["r"], d["q"], d["eq"], d["blogp"], d["tlogp"], term, trunc, d["tv"],
+                       d["b"], g, lam, 1.0),
+    ]
+    p = {k: v.copy() for k, v in d.items()}
+    for k in ("r", "v", "q", "eq", "blogp", "tlogp", "tv"):
+        p[k][:, 18:] += 3.0
+    p["b"] += 1.0
+    pert = [
+        oracle.gae(p["r"], p["v"], term, trunc, p["tv"], p["b"], g, lam)[0],
+        oracle.td_lambda(p["r"], p["v"], term, trunc, p["tv"], p["b"], g, lam),
+        oracle.vtrace(p["r"], p["v"], p["blogp"], p["tlogp"], term, trunc, p["tv"], p["b"],
+                      g, 1.0, 1.0, 1.0)[0],
+        oracle.retrace(p["r"], p["q"], p["eq"], p["blogp"], p["tlogp"], term, trunc, p["tv"],
+                       p["b"], g, lam, 1.0),
+    ]
+    for a, b in zip(base, pert):
+        assert np.array_equal(a[:, :18], b[:, :18])
+    # forward: inputs before a reset do not reach past it.
+    starts = np.zeros((8, 40), np.uint8)
+    starts[:, 11] = 1
+    x = d["x"]
+    x2 = x.copy()
+    x2[:, :11] += 2.0
+    assert np.array_equal(oracle.eligibility_traces(x, starts, 0, 0.9, 0.9)[:, 11:],
+                          oracle.eligibility_traces(x2, starts, 0, 0.9, 0.9)[:, 11:])
+
+
+def test_window_split_carry_invariant():
+    """Discounted returns over [k, T), then over [0, k) with bootstrap := G_k,
+    reproduce the full window when step k-1 is not done (the carry that lets a
+    row be processed in pieces)."""
+    d = rand_inputs(52, 6, 30)
+    term, trunc = _random_flags(53, 6, 30, p=0.05)
+    k = 13
+    term[:, k - 1] = 0
+    trunc[:, k - 1] = 0
+    g = 0.97
+    full = oracle.discounted_returns(d["r"], term, trunc, d["tv"], d["b"], g)
+    tail = oracle.discounted_returns(d["r"][:, k:], term[:, k:], trunc[:, k:], d["tv"][:, k:],
+                                     d["b"], g)
+    head = oracle.discounted_returns(d["r"][:, :k], term[:, :k], trunc[:, :k], d["tv"][:, :k],
+                                     tail[:, 0].astype(np.float32), g)
+    close(tail, full[:, k:], 1e-15)
+    close(head, full[:, :k], 1e-6)   # bootstrap passes through float32
