@@ -1,0 +1,435 @@
+#!/usr/bin/env python3
+"""Throughput benchmark of the fused credit-assignment scans on one MI355X.
+
+Default workload: GAE and TD(lambda) returns over 4096 envs x 128 steps, fp32,
+each with and without per-step truncation handling; one *step* is those four
+library calls over one rollout (inputs resident in HBM).  Prints ONE JSON line.
+
+Measurement:
+  * cold cache: every call reads a different copy of the rollout, rotating
+    over >= 1 GiB of copies, so neither the 4 MB-per-XCD L2 nor the 256 MB
+    Infinity Cache can serve the operands;
+  * launches are eager (pre-bound ctypes calls, asynchronous on one stream);
+    --launch graph captures each step into a HIP graph and replays it;
+  * whole-step time: HIP events around K steps, synchronised on both sides;
+    per-kernel time: HIP events around a back-to-back batch of one call
+    variant (rotating sets), averaged over the batch;
+  * effective GB/s uses the algorithmic byte model: every input array read
+    once and every output written once at dense size (fp32 / int32 4 B, flags
+    1 B per step, bootstrap 4 B per row);
+  * cpu_baseline: the fp64 sequential oracle on this host, single thread.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E peak, 8 TB/s
+METRIC = "effective HBM GB/s (% of peak) + env-steps/s, GAE 4096×128 fp32"
+COLD_BYTES = 1 << 30
+
+
+# ------------------------------------------------------------------ workloads
+# A call: (name, library function, argument template, bytes per launch).
+# Argument templates name buffers of a rotation set ("@key") or give scalars.
+
+
+def _backward_bytes(nt, n, f32_in, flags, f32_out):
+    return nt * (4 * f32_in + flags + 4 * f32_out) + 4 * n
+
+
+def workload_calls(name, cfg, host):
+    """Return (arrays, calls) for a named workload; arrays are the host inputs
+    each rotation set holds, calls the per-step library calls."""
+    n, t = host.num_envs, host.T
+    nt = n * t
+    g = cfg["gamma"]
+    lam = cfg.get("lam", 0.95)
+    if name in ("gae_td_4096x128", "gae_8x16"):
+        arrays = dict(r=host.rewards, v=host.values, term=host.terminated,
+                      trunc=host.truncated, tv=host.trunc_values, b=host.bootstrap)
+        gae_nt = ("gae", "rlca_gae",
+                  ["@r", "@v", "@term", None, None, "@b", g, lam, n, t, "@o0", "@o1"],
+                  _backward_bytes(nt, n, 2, 1, 2), ("o0", "o1"))
+        gae_tr = ("gae+trunc", "rlca_gae",
+                  ["@r", "@v", "@term", "@trunc", "@tv", "@b", g, lam, n, t, "@o0", "@o1"],
+                  _backward_bytes(nt, n, 3, 2, 2), ("o0", "o1"))
+        td_nt = ("td_lambda", "rlca_td_lambda",
+                 ["@r", "@v", "@term", None, None, "@b", g, lam, n, t, "@o0"],
+                 _backward_bytes(nt, n, 2, 1, 1), ("o0",))
+        td_tr = ("td_lambda+trunc", "rlca_td_lambda",
+                 ["@r", "@v", "@term", "@trunc", "@tv", "@b", g, lam, n, t, "@o0"],
+                 _backward_bytes(nt, n, 3, 2, 1), ("o0",))
+        calls = [gae_tr] if name == "gae_8x16" else [gae_nt, gae_tr, td_nt, td_tr]
+        return arrays, calls
+    if name == "vtrace_4096x256":
+        arrays = dict(r=host.rewards, v=host.values, mu=host.behaviour_logp,
+                      pi=host.target_logp, term=host.terminated, b=host.bootstrap)
+        call = ("vtrace", "rlca_vtrace",
+                ["@r", "@v", "@mu", "@pi", "@term", None, None, "@b", g, lam, cfg["rho_bar"],
+                 cfg["c_bar"], n, t, "@o0", "@o1"],
+                _backward_bytes(nt, n, 4, 1, 2), ("o0", "o1"))
+        return arrays, [call]
+    if name == "retrace_2048x1024":
+        arrays = dict(r=host.rewards, q=host.q_values, eq=host.expected_q,
+                      mu=host.behaviour_logp, pi=host.target_logp, term=host.terminated,
+                      trunc=host.truncated, tv=host.trunc_values, b=host.bootstrap)
+        call = ("retrace+trunc", "rlca_retrace",
+                ["@r", "@q", "@eq", "@mu", "@pi", "@term", "@trunc", "@tv", "@b", g, lam,
+                 cfg["c_bar"], n, t, "@o0"],
+                _backward_bytes(nt, n, 6, 2, 1), ("o0",))
+        return arrays, [call]
+    if name == "forward_16384x512":
+        arrays = dict(r=host.rewards, x=host.increments, xi=host.ints, starts=host.starts,
+                      dones=host.dones, b=host.bootstrap)
+        calls = [
+            ("discounted", "rlca_discounted_returns",
+             ["@r", "@dones", None, None, "@b", g, n, t, "@o0"],
+             _backward_bytes(nt, n, 1, 1, 1), ("o0",)),
+            ("eligibility", "rlca_eligibility_traces",
+             ["@x", "@starts", 0, g, lam, n, t, "@o0"], nt * 9, ("o0",)),
+            ("prefix_sum_f32", "rlca_episodic_prefix_sum",
+             ["@r", 0, "@starts", 0, n, t, "@o0"], nt * 9, ("o0",)),
+            ("prefix_sum_i32", "rlca_episodic_prefix_sum",
+             ["@xi", 1, "@starts", 0, n, t, "@oi"], nt * 9, ("oi",)),
+        ]
+        return arrays, calls
+    raise SystemExit(f"unknown workload {name}")
+
+
+# ------------------------------------------------------------------ GPU timing
+
+
+def make_sets(torch, arrays, calls, device, min_call_bytes):
+    """Rotation sets: full copies of the inputs plus every output buffer, as
+    many as needed for >= COLD_BYTES of traffic between reuses of a set."""
+    master = {k: torch.from_numpy(np.ascontiguousarray(v)).to(device) for k, v in arrays.items()}
+    shape = next(v.shape for v in arrays.values() if v.ndim == 2)
+    nsets = max(2, -(-COLD_BYTES // max(1, min_call_bytes)) + 1)
+    per_set = sum(v.numel() * v.element_size() for v in master.values()) + \
+        sum(4 * int(np.prod(shape)) for _ in range(3))
+    nsets = int(min(nsets, max(2, (24 << 30) // per_set)))
+    sets = []
+    for _ in range(nsets):
+        s = {k: v.clone() for k, v in master.items()}
+        s["o0"] = torch.empty(shape, dtype=torch.float32, device=device)
+        s["o1"] = torch.empty(shape, dtype=torch.float32, device=device)
+        s["oi"] = torch.empty(shape, dtype=torch.int32, device=device)
+        sets.append(s)
+    return sets
+
+
+def bind(lib, call, bufs, stream):
+    _, fname, template, _, _ = call
+    fn = getattr(lib, fname)
+    args = []
+    for a in template:
+        if isinstance(a, str) and a.startswith("@"):
+            args.append(bufs[a[1:]].data_ptr())
+        else:
+            args.append(a)
+    args.append(stream)
+    return fn, tuple(args)
+
+
+def run_gpu(args, name, cfg, host):
+    import torch
+    from linear_recurrence_scan_row_amd import rlca
+
+    lib = rlca.lib()
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+    arrays, calls = workload_calls(name, cfg, host)
+    sets = make_sets(torch, arrays, calls, device, min(c[3] for c in calls))
+    nsets = len(sets)
+    ncalls = len(calls)
+    step_bytes = sum(c[3] for c in calls)
+    dominant = max(range(ncalls), key=lambda i: calls[i][3])
+
+    stream = torch.cuda.Stream()  # default priority
+    # bound launches: step s, call c uses set (s * ncalls + c) % nsets
+    cycle = nsets * ncalls // np.gcd(nsets, ncalls)
+    steps_per_cycle = cycle // ncalls
+
+    def launches(h):
+        out = []
+        for s in range(steps_per_cycle):
+            row = []
+            for c in range(ncalls):
+                row.append(bind(lib, calls[c], sets[(s * ncalls + c) % nsets], h))
+            out.append(row)
+        return out
+
+    def check(st, what):
+        if st != 0:
+            raise RuntimeError(f"{what}: {rlca.STATUS_NAMES.get(st, st)}")
+
+    timed_steps = args.steps
+    warm = args.warmup
+    with torch.cuda.stream(stream):
+        h = stream.cuda_stream
+        plan = launches(h)
+        if args.launch == "graph":
+            # One graph per step of the rotation cycle, captured once, replayed.
+            graphs = []
+            for s in range(steps_per_cycle):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    for c, (fn, a) in enumerate(plan[s]):
+                        check(fn(*a), calls[c][0])
+                graphs.append(g)
+            run_step = lambda s: graphs[s % steps_per_cycle].replay()  # noqa: E731
+        else:
+            def run_step(s):
+                for c, (fn, a) in enumerate(plan[s % steps_per_cycle]):
+                    check(fn(*a), calls[c][0])
+
+        for s in range(warm):
+            run_step(s)
+        torch.cuda.synchronize()
+
+        # whole-step time
+        t0 = time.perf_counter()
+        e_start = torch.cuda.Event(enable_timing=True)
+        e_end = torch.cuda.Event(enable_timing=True)
+        e_start.record(stream)
+        for s in range(timed_steps):
+            run_step(warm + s)
+        e_end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        step_ms = e_start.elapsed_time(e_end) / timed_steps
+
+        # per-kernel device time: each call variant launched back to back
+        # `batch` times (rotating sets) between two events on the same stream;
+        # the average is elapsed / batch
+        batch = max(50, min(timed_steps, 2000))
+        per_call_ms = []
+        for c in range(ncalls):
+            bound = [bind(lib, calls[c], sets[i % nsets], h) for i in range(nsets)]
+            for i in range(5):
+                fn, a = bound[i % nsets]
+                check(fn(*a), calls[c][0])
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(batch):
+                fn, a = bound[i % nsets]
+                check(fn(*a), calls[c][0])
+            e1.record(stream)
+            torch.cuda.synchronize()
+            per_call_ms.append(e0.elapsed_time(e1) / batch)
+
+        # same-bytes copy ceiling (cold, rotating): a plain device copy of
+        # step_bytes / 2 read + step_bytes / 2 written
+        nfl = max(1, step_bytes // 8)
+        src = [torch.empty(nfl * 1, dtype=torch.float32, device=device).fill_(1.0)
+               for _ in range(max(2, COLD_BYTES // (nfl * 4) + 1))]
+        dst = [torch.empty_like(x) for x in src]
+        for i in range(10):
+            dst[i % len(dst)].copy_(src[i % len(src)])
+        torch.cuda.synchronize()
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        ncopy = 200
+        for i in range(ncopy):
+            dst[i % len(dst)].copy_(src[i % len(src)])
+        c1.record(stream)
+        torch.cuda.synchronize()
+        copy_ms = c0.elapsed_time(c1) / ncopy
+        copy_gbs = (nfl * 8) / (copy_ms * 1e-3) / 1e9
+
+    nt = host.num_envs * host.T
+    return dict(step_ms=step_ms, wall_s=wall, step_bytes=step_bytes, calls=calls,
+                per_call_ms=per_call_ms, dominant=dominant, nt=nt, nsets=nsets,
+                copy_gbs=copy_gbs, copy_bytes=nfl * 8)
+
+
+# ------------------------------------------------------------------ CPU oracle
+
+
+def run_cpu_baseline(name, cfg, host, seconds):
+    """The fp64 sequential oracle on this host's CPU, single-threaded, over the
+    same rollout and calls, repeated for about `seconds`."""
+    import oracle
+
+    g = cfg["gamma"]
+    lam = cfg.get("lam", 0.95)
+    d = host
+    if name in ("gae_td_4096x128", "gae_8x16"):
+        fns = [
+            lambda: oracle.gae(d.rewards, d.values, d.terminated, None, None, d.bootstrap, g, lam),
+            lambda: oracle.gae(d.rewards, d.values, d.terminated, d.truncated, d.trunc_values,
+                               d.bootstrap, g, lam),
+            lambda: oracle.td_lambda(d.rewards, d.values, d.terminated, None, None, d.bootstrap,
+                                     g, lam),
+            lambda: oracle.td_lambda(d.rewards, d.values, d.terminated, d.truncated,
+                                     d.trunc_values, d.bootstrap, g, lam),
+        ]
+        if name == "gae_8x16":
+            fns = fns[1:2]
+    elif name == "vtrace_4096x256":
+        fns = [lambda: oracle.vtrace(d.rewards, d.values, d.behaviour_logp, d.target_logp,
+                                     d.terminated, None, None, d.bootstrap, g, lam,
+                                     cfg["rho_bar"], cfg["c_bar"])]
+    elif name == "retrace_2048x1024":
+        fns = [lambda: oracle.retrace(d.rewards, d.q_values, d.expected_q, d.behaviour_logp,
+                                      d.target_logp, d.terminated, d.truncated, d.trunc_values,
+                                      d.bootstrap, g, lam, cfg["c_bar"])]
+    else:
+        fns = [
+            lambda: oracle.discounted_returns(d.rewards, d.dones, None, None, d.bootstrap, g),
+            lambda: oracle.eligibility_traces(d.increments, d.starts, 0, g, lam),
+            lambda: oracle.episodic_prefix_sum(d.rewards, d.starts, 0),
+            lambda: oracle.episodic_prefix_sum(d.ints, d.starts, 0),
+        ]
+    for f in fns:   # warm-up (also builds the library if needed)
+        f()
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        for f in fns:
+            f()
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    nt = d.num_envs * d.T
+    return dict(value=passes * len(fns) * nt / el, unit="env-steps/s", cores=1, kind="oracle",
+                sample=(f"full {d.num_envs}x{d.T} rollout, {len(fns)} estimator calls per pass, "
+                        f"{passes} passes in {el:.1f} s, one thread, fp64 sequential C"))
+
+
+# ------------------------------------------------------------------ traffic
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    for rel in ("linear_recurrence_scan_row_amd/csrc/rlca.hip",
+                "linear_recurrence_scan_row_amd/csrc/scan_core.hpp", "include/rlca.h"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_name, workload):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None
+    when the summary is missing or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_name}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_digest") != kernel_source_digest():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ------------------------------------------------------------------ main
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="gae_td_4096x128")
+    ap.add_argument("--launch", choices=("graph", "eager"), default="eager")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this library's hot path has no multi-GPU "
+              f"step (rows are independent; sharding over envs needs no communication). "
+              f"--gpus {args.gpus} is not supported.", file=sys.stderr)
+        sys.exit(2)
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs as a single process on one GPU", file=sys.stderr)
+        sys.exit(2)
+
+    sys.path.insert(0, ROOT)
+    from linear_recurrence_scan_row_amd import workloads
+
+    cfg = dict(workloads.CONFIGS[args.workload])
+    host = workloads.make(args.workload)
+    res = run_gpu(args, args.workload, cfg, host)
+
+    step_s = res["step_ms"] * 1e-3
+    ncalls = len(res["calls"])
+    value = res["step_bytes"] / step_s / 1e9
+    dom = res["dominant"]
+    dcall = res["calls"][dom]
+    dom_ms = res["per_call_ms"][dom]
+    achieved = dcall[3] / (dom_ms * 1e-3) / 1e9
+    kernel_tag = dcall[0].replace("+", "_")
+    traffic = measured_traffic(kernel_tag, args.workload)
+
+    calls_out = {}
+    for i, c in enumerate(res["calls"]):
+        ms = res["per_call_ms"][i]
+        calls_out[c[0]] = dict(us=round(ms * 1e3, 3), bytes=c[3],
+                               gbs=round(c[3] / (ms * 1e-3) / 1e9, 1),
+                               env_steps_per_s=res["nt"] / (ms * 1e-3))
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["step_ms"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded numpy rollouts; cold-cache rotation over "
+                f"{res['nsets']} HBM-resident copies)",
+        "config": {
+            "workload": args.workload,
+            "num_envs": host.num_envs,
+            "T": host.T,
+            "calls_per_step": [c[0] for c in res["calls"]],
+            "launch": args.launch,
+        },
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "env_steps_per_s": ncalls * res["nt"] / step_s,
+        "bytes_per_step": res["step_bytes"],
+        "calls": calls_out,
+        "copy_ceiling": {"gbs": round(res["copy_gbs"], 1), "bytes": res["copy_bytes"],
+                         "kind": "torch device copy, cold rotation, same bytes moved"},
+        "roofline": {
+            "kernel": dcall[0],
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes": dcall[3],
+            "avg_us": round(dom_ms * 1e3, 3),
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = run_cpu_baseline(args.workload, cfg, host, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,181 @@
+/*
+ * rlca.h -- C ABI of the MI355X (gfx950) credit-assignment scan library.
+ *
+ * Seven reinforcement-learning credit-assignment estimators computed as one
+ * first-order affine recurrence over [num_envs, T] rollouts:
+ *   backward  A_t = alpha_t + beta_t * A_{t+1}   (GAE, TD(lambda), discounted
+ *             returns, V-Trace, Retrace(lambda))
+ *   forward   A_t = alpha_t + beta_t * A_{t-1}   (eligibility traces, episodic
+ *             prefix sums)
+ * ("rl-triton: High-Performance Triton GPU Kernels for Reinforcement Learning
+ * Credit Assignment", paperlayer.ai summary, §1 Introduction and §3.1 Shared
+ * scan formulation).  Each call is one kernel launch that reads its inputs
+ * from HBM once and writes each output once.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory:  every array argument is a DEVICE pointer (hipMalloc memory or a
+ *          torch tensor's data_ptr()) owned by the caller.  The library
+ *          allocates nothing, keeps no mutable global state and never
+ *          synchronizes: work is enqueued on `stream` and buffers must stay
+ *          alive until the stream has passed the call.
+ * Layout:  per-step arrays are dense row-major [num_envs, T]; element (n, t)
+ *          is at n*T + t.  `bootstrap` is [num_envs].  fp32 / int32 data must
+ *          be 4-byte aligned; 16-byte alignment (and T % 4 == 0) selects the
+ *          vectorised path but is not required.  Flags are one byte per step,
+ *          any nonzero byte meaning "set" (torch.bool and uint8 both work).
+ * Episode boundaries (summary §3.2 Episode-boundary semantics):
+ *          terminated[t]  the episode ends after step t in a terminal state:
+ *                         successor value 0, no credit flows back past t.
+ *          truncated[t]   the episode is cut after step t (time limit): the
+ *                         successor value is trunc_values[t] (the value of the
+ *                         state the episode was cut in), no credit flows back
+ *                         past t.  Terminated wins when both are set.
+ *                         truncated == NULL means no truncation and selects a
+ *                         specialised fast path; trunc_values is then ignored.
+ *          t = T-1        the rollout window ends: when the last step is not
+ *                         done, its successor value is bootstrap[n]
+ *                         (bootstrap == NULL means 0).  A done last step
+ *                         ignores the bootstrap.
+ * Errors:  the return value is the only error channel.  Arguments are checked
+ *          before anything is enqueued and a failed call has no side effects.
+ *            RLCA_ERR_NULL_POINTER   a required pointer is NULL
+ *            RLCA_ERR_INVALID_SIZE   num_envs < 0, T < 0, T > RLCA_MAX_T,
+ *                                    num_envs > RLCA_MAX_ENVS, or the byte
+ *                                    size of an array overflows
+ *            RLCA_ERR_INVALID_VALUE  gamma or lambda outside [0, 1] or not
+ *                                    finite, a clip threshold <= 0 or not
+ *                                    finite, an unknown enum value
+ *            RLCA_ERR_ALIASING       an output overlaps an input or another
+ *                                    output (in-place is not supported)
+ *            RLCA_ERR_MISALIGNED     an fp32 / int32 pointer is not 4-byte aligned
+ *            RLCA_ERR_HIP            the launch failed (hipGetLastError)
+ *          num_envs * T == 0 is a valid no-op.  Faults inside the kernel
+ *          surface at the caller's next synchronisation, as usual in HIP.
+ *          Non-finite inputs propagate; they are not trapped.
+ * Numerics: fp32 throughout (the summary's §4 requires float32 scans); the
+ *          scan reassociates the recurrence (associativity, summary §5), so
+ *          results match a sequential fp64 evaluation to rounding, not bit
+ *          for bit.  The int32 prefix sum is exact (two's-complement wrap).
+ */
+#ifndef RLCA_H
+#define RLCA_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RLCA_MAX_T ((int64_t)1 << 30)
+#define RLCA_MAX_ENVS ((int64_t)1 << 31)
+
+/* Clamp applied to log(pi/mu) before exp() in V-Trace and Retrace. */
+#define RLCA_LOG_RATIO_CLIP 5.0f
+
+typedef enum {
+    RLCA_OK = 0,
+    RLCA_ERR_NULL_POINTER = 1,
+    RLCA_ERR_INVALID_SIZE = 2,
+    RLCA_ERR_INVALID_VALUE = 3,
+    RLCA_ERR_ALIASING = 4,
+    RLCA_ERR_MISALIGNED = 5,
+    RLCA_ERR_HIP = 6
+} rlca_status;
+
+/* Forward-scan reset conventions (summary §3.3: "configurable boundary
+ * conventions"; §5: the forward scans cut the carry where d_{t-1} = 1). */
+typedef enum {
+    RLCA_RESET_ON_START = 0,  /* flags[t] != 0: step t starts a new episode      */
+    RLCA_RESET_AFTER_DONE = 1 /* flags[t-1] != 0: step t-1 ended the episode      */
+} rlca_reset_convention;
+
+typedef enum { RLCA_F32 = 0, RLCA_I32 = 1 } rlca_dtype;
+
+/* Generalized advantage estimation (Schulman et al. 2016; summary §2.1).
+ *   delta_t = r_t + gamma * V(s_{t+1}) - V(s_t),   V(s_{t+1}) per the boundary rules
+ *   adv_t   = delta_t + gamma * lambda * adv_{t+1}  (chain cut at done steps and t = T-1)
+ *   ret_t   = adv_t + V(s_t)
+ * rewards, values [N,T] f32; terminated [N,T] u8 (required); truncated [N,T] u8
+ * (nullable); trunc_values [N,T] f32 (required iff truncated); bootstrap [N]
+ * f32 (nullable).  Writes advantages [N,T] and, when non-NULL, returns [N,T]. */
+rlca_status rlca_gae(const float *rewards, const float *values, const uint8_t *terminated,
+                     const uint8_t *truncated, const float *trunc_values,
+                     const float *bootstrap, float gamma, float lambda, int64_t num_envs,
+                     int64_t T, float *advantages, float *returns, hipStream_t stream);
+
+/* TD(lambda) returns (summary §1, §3.2):
+ *   G_t = r_t + gamma * ((1 - lambda) * V(s_{t+1}) + lambda * G_{t+1}),
+ *   and G_t = r_t + gamma * successor value at a done step or at t = T-1.
+ * Arguments as rlca_gae; writes returns [N,T]. */
+rlca_status rlca_td_lambda(const float *rewards, const float *values,
+                           const uint8_t *terminated, const uint8_t *truncated,
+                           const float *trunc_values, const float *bootstrap, float gamma,
+                           float lambda, int64_t num_envs, int64_t T, float *returns,
+                           hipStream_t stream);
+
+/* Discounted returns (summary §1, §3.2): G_t = r_t + gamma * G_{t+1}, and
+ * G_t = r_t + gamma * successor value at a done step or at t = T-1
+ * (bootstrap == NULL gives Monte-Carlo returns).  Writes returns [N,T]. */
+rlca_status rlca_discounted_returns(const float *rewards, const uint8_t *terminated,
+                                    const uint8_t *truncated, const float *trunc_values,
+                                    const float *bootstrap, float gamma, int64_t num_envs,
+                                    int64_t T, float *returns, hipStream_t stream);
+
+/* V-Trace (Espeholt et al. 2018; summary §8 Off-policy correction).
+ *   ratio_t = exp(clamp(target_logp_t - behaviour_logp_t, -5, 5))
+ *   rho_t = min(rho_bar, ratio_t),  c_t = lambda * min(c_bar, ratio_t)
+ *   vs_t - V_t = rho_t (r_t + gamma V(s_{t+1}) - V_t) + gamma c_t (vs_{t+1} - V_{t+1})
+ *   pg_t = rho_t (r_t + gamma vs_{t+1} - V_t)
+ * where at a done step or t = T-1 the successor value replaces V(s_{t+1}) and
+ * vs_{t+1}.  lambda = 1 is the IMPALA form.  rho_bar, c_bar > 0.
+ * Writes vs [N,T] and, when non-NULL, pg_advantages [N,T]. */
+rlca_status rlca_vtrace(const float *rewards, const float *values, const float *behaviour_logp,
+                        const float *target_logp, const uint8_t *terminated,
+                        const uint8_t *truncated, const float *trunc_values,
+                        const float *bootstrap, float gamma, float lambda, float rho_bar,
+                        float c_bar, int64_t num_envs, int64_t T, float *vs,
+                        float *pg_advantages, hipStream_t stream);
+
+/* Retrace(lambda) (Munos et al. 2016; summary §3.3: the decay uses the
+ * next step's importance weight).
+ *   c_t = lambda * min(c_bar, exp(clamp(target_logp_t - behaviour_logp_t, -5, 5)))
+ *   Qret_t = r_t + gamma E_pi Q(s_{t+1}, .) + gamma c_{t+1} (Qret_{t+1} - Q_{t+1})
+ * q_values[t] = Q(s_t, a_t); expected_q[t] = E_pi Q(s_t, .).  At a done step
+ * or t = T-1 the successor value (0 / trunc_values[t] = E_pi Q of the cut
+ * state / bootstrap[n] = E_pi Q(s_T, .)) replaces E_pi Q(s_{t+1}, .) and the
+ * correction term is dropped.  Writes q_ret [N,T]. */
+rlca_status rlca_retrace(const float *rewards, const float *q_values, const float *expected_q,
+                         const float *behaviour_logp, const float *target_logp,
+                         const uint8_t *terminated, const uint8_t *truncated,
+                         const float *trunc_values, const float *bootstrap, float gamma,
+                         float lambda, float c_bar, int64_t num_envs, int64_t T,
+                         float *q_ret, hipStream_t stream);
+
+/* Accumulating eligibility traces, forward in time (summary §1, §3.2):
+ *   e_t = x_t + gamma * lambda * e_{t-1},  e_{-1} = 0, and e_{t-1} := 0 where
+ *   a new episode starts under `convention`.
+ * increments [N,T] f32, flags [N,T] u8 (required).  Writes traces [N,T]. */
+rlca_status rlca_eligibility_traces(const float *increments, const uint8_t *flags,
+                                    rlca_reset_convention convention, float gamma,
+                                    float lambda, int64_t num_envs, int64_t T, float *traces,
+                                    hipStream_t stream);
+
+/* Inclusive episodic (segmented) prefix sum, forward in time (summary §3.3):
+ *   S_t = x_t + S_{t-1},  S_{-1} = 0, restarted where a new episode starts.
+ * x and out are [N,T] of `dtype` (f32, or i32 with two's-complement
+ * wrap-around, exact); flags [N,T] u8 (required). */
+rlca_status rlca_episodic_prefix_sum(const void *x, rlca_dtype dtype, const uint8_t *flags,
+                                     rlca_reset_convention convention, int64_t num_envs,
+                                     int64_t T, void *out, hipStream_t stream);
+
+/* Static description of a status code (never NULL). */
+const char *rlca_status_string(rlca_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RLCA_H */

@@ -1,0 +1,370 @@
+"""Parity of the HIP kernels (through the C ABI) with the fp64 CPU oracle.
+
+The bar: fp32 outputs within |gpu - oracle| <= 1e-4 * (1 + |oracle|) element by
+element (the rl-triton summary's §6 validation tolerance, atol = rtol = 1e-4);
+the int32 prefix sum bit-exact.  Inputs are seeded synthetic rollouts; shapes
+span one lane, several tiles, ragged tails, the scalar (unaligned) and vector
+paths, and the five measured workloads at full size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import linear_recurrence_scan_row_amd as rl
+from linear_recurrence_scan_row_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+
+
+def assert_parity(gpu, ref, what=""):
+    g = gpu.detach().cpu().numpy().astype(np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert g.shape == ref.shape, what
+    if g.size == 0:
+        return
+    err = np.abs(g - ref) / (1.0 + np.abs(ref))
+    worst = np.unravel_index(np.argmax(err), err.shape)
+    assert err[worst] <= TOL, (f"{what}: max scaled error {err[worst]:.3e} at {worst}: "
+                               f"gpu {g[worst]!r} oracle {ref[worst]!r}")
+
+
+def dev(x, device):
+    return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(device)
+
+
+def rollout(seed, N, T, p_term=0.05, p_trunc=0.05):
+    return workloads.backward_rollout(seed, N, T, p_term=p_term, p_trunc=p_trunc)
+
+
+# ----------------------------------------------------------- per-estimator runs
+
+
+def check_gae(d, device, trunc=True, boot=True, gamma=0.99, lam=0.95, what=""):
+    tr = d.truncated if trunc else None
+    tv = d.trunc_values if trunc else None
+    b = d.bootstrap if boot else None
+    adv, ret = rl.gae(dev(d.rewards, device), dev(d.values, device), dev(d.terminated, device),
+                      dev(tr, device), dev(tv, device), dev(b, device), gamma, lam)
+    oadv, oret = oracle.gae(d.rewards, d.values, d.terminated, tr, tv, b, gamma, lam)
+    assert_parity(adv, oadv, f"gae adv {what}")
+    assert_parity(ret, oret, f"gae ret {what}")
+
+
+def check_td(d, device, trunc=True, boot=True, gamma=0.99, lam=0.95, what=""):
+    tr = d.truncated if trunc else None
+    tv = d.trunc_values if trunc else None
+    b = d.bootstrap if boot else None
+    g = rl.td_lambda(dev(d.rewards, device), dev(d.values, device), dev(d.terminated, device),
+                     dev(tr, device), dev(tv, device), dev(b, device), gamma, lam)
+    assert_parity(g, oracle.td_lambda(d.rewards, d.values, d.terminated, tr, tv, b, gamma, lam),
+                  f"td_lambda {what}")
+
+
+def check_disc(d, device, trunc=True, boot=True, gamma=0.99, what=""):
+    tr = d.truncated if trunc else None
+    tv = d.trunc_values if trunc else None
+    b = d.bootstrap if boot else None
+    g = rl.discounted_returns(dev(d.rewards, device), dev(d.terminated, device),
+                              dev(tr, device), dev(tv, device), dev(b, device), gamma)
+    assert_parity(g, oracle.discounted_returns(d.rewards, d.terminated, tr, tv, b, gamma),
+                  f"discounted {what}")
+
+
+def check_vtrace(d, device, trunc=True, boot=True, gamma=0.99, lam=1.0, rho_bar=1.0, c_bar=1.0,
+                 what=""):
+    tr = d.truncated if trunc else None
+    tv = d.trunc_values if trunc else None
+    b = d.bootstrap if boot else None
+    vs, pg = rl.vtrace(dev(d.rewards, device), dev(d.values, device),
+                       dev(d.behaviour_logp, device), dev(d.target_logp, device),
+                       dev(d.terminated, device), dev(tr, device), dev(tv, device),
+                       dev(b, device), gamma, lam, rho_bar, c_bar)
+    ovs, opg = oracle.vtrace(d.rewards, d.values, d.behaviour_logp, d.target_logp,
+                             d.terminated, tr, tv, b, gamma, lam, rho_bar, c_bar)
+    assert_parity(vs, ovs, f"vtrace vs {what}")
+    assert_parity(pg, opg, f"vtrace pg {what}")
+
+
+def check_retrace(d, device, trunc=True, boot=True, gamma=0.99, lam=0.95, c_bar=1.0, what=""):
+    tr = d.truncated if trunc else None
+    tv = d.trunc_values if trunc else None
+    b = d.bootstrap if boot else None
+    q = rl.retrace(dev(d.rewards, device), dev(d.q_values, device), dev(d.expected_q, device),
+                   dev(d.behaviour_logp, device), dev(d.target_logp, device),
+                   dev(d.terminated, device), dev(tr, device), dev(tv, device), dev(b, device),
+                   gamma, lam, c_bar)
+    assert_parity(q, oracle.retrace(d.rewards, d.q_values, d.expected_q, d.behaviour_logp,
+                                    d.target_logp, d.terminated, tr, tv, b, gamma, lam, c_bar),
+                  f"retrace {what}")
+
+
+def check_forward(f, device, conv=rl.RESET_ON_START, gamma=0.99, lam=0.9, what=""):
+    flags = f.starts if conv == rl.RESET_ON_START else f.dones
+    fl = dev(flags, device)
+    e = rl.eligibility_traces(dev(f.increments, device), fl, conv, gamma, lam)
+    assert_parity(e, oracle.eligibility_traces(f.increments, flags, conv, gamma, lam),
+                  f"eligibility {what}")
+    s = rl.episodic_prefix_sum(dev(f.rewards, device), fl, conv)
+    assert_parity(s, oracle.episodic_prefix_sum(f.rewards, flags, conv), f"prefix f32 {what}")
+    si = rl.episodic_prefix_sum(dev(f.ints, device), fl, conv)
+    assert np.array_equal(si.cpu().numpy(), oracle.episodic_prefix_sum(f.ints, flags, conv)), \
+        f"prefix i32 {what}"
+
+
+# ------------------------------------------------------------------ shape sweep
+
+SHAPES = [(1, 1), (3, 1), (2, 2), (5, 3), (7, 5), (8, 16), (3, 63), (2, 64), (5, 65),
+          (4, 127), (9, 128), (3, 129), (2, 255), (2, 257), (1, 1023), (2, 1024), (1, 1025),
+          (3, 2049), (1, 4097), (600, 7), (1030, 4), (257, 12), (5, 3001)]
+
+
+@pytest.mark.parametrize("N,T", SHAPES)
+def test_backward_shape_sweep(N, T, gpu_device):
+    d = rollout(100 + N * 7 + T, N, T)
+    what = f"N={N} T={T}"
+    for trunc in (True, False):
+        check_gae(d, gpu_device, trunc=trunc, what=what)
+        check_td(d, gpu_device, trunc=trunc, what=what)
+        check_disc(d, gpu_device, trunc=trunc, what=what)
+        check_vtrace(d, gpu_device, trunc=trunc, lam=0.9, rho_bar=1.2, c_bar=0.8, what=what)
+        check_retrace(d, gpu_device, trunc=trunc, what=what)
+
+
+@pytest.mark.parametrize("N,T", SHAPES)
+def test_forward_shape_sweep(N, T, gpu_device):
+    f = workloads.forward_rollout(200 + N * 7 + T, N, T, p_start=0.08)
+    for conv in (rl.RESET_ON_START, rl.RESET_AFTER_DONE):
+        check_forward(f, gpu_device, conv, what=f"N={N} T={T} conv={conv}")
+
+
+# ------------------------------------------------------------ full-size configs
+
+
+def test_config_gae_8x16(gpu_device):
+    c = workloads.CONFIGS["gae_8x16"]
+    d = workloads.make("gae_8x16")
+    check_gae(d, gpu_device, gamma=c["gamma"], lam=c["lam"], what="8x16")
+
+
+@pytest.mark.parametrize("trunc", [True, False])
+def test_config_gae_td_4096x128(trunc, gpu_device):
+    c = workloads.CONFIGS["gae_td_4096x128"]
+    d = workloads.make("gae_td_4096x128")
+    check_gae(d, gpu_device, trunc=trunc, gamma=c["gamma"], lam=c["lam"], what="4096x128")
+    check_td(d, gpu_device, trunc=trunc, gamma=c["gamma"], lam=c["lam"], what="4096x128")
+
+
+def test_config_vtrace_4096x256(gpu_device):
+    c = workloads.CONFIGS["vtrace_4096x256"]
+    d = workloads.make("vtrace_4096x256")
+    check_vtrace(d, gpu_device, trunc=False, gamma=c["gamma"], lam=c["lam"],
+                 rho_bar=c["rho_bar"], c_bar=c["c_bar"], what="4096x256")
+
+
+def test_config_retrace_2048x1024(gpu_device):
+    c = workloads.CONFIGS["retrace_2048x1024"]
+    d = workloads.make("retrace_2048x1024")
+    check_retrace(d, gpu_device, gamma=c["gamma"], lam=c["lam"], c_bar=c["c_bar"],
+                  what="2048x1024")
+
+
+def test_config_forward_16384x512(gpu_device):
+    c = workloads.CONFIGS["forward_16384x512"]
+    f = workloads.make("forward_16384x512")
+    # discounted returns over the same episode boundaries (dones[t] = starts[t+1])
+    r = rl.discounted_returns(dev(f.rewards, gpu_device), dev(f.dones, gpu_device),
+                              bootstrap=dev(f.bootstrap, gpu_device), gamma=c["gamma"])
+    assert_parity(r, oracle.discounted_returns(f.rewards, f.dones, None, None, f.bootstrap,
+                                               c["gamma"]), "16384x512 discounted")
+    check_forward(f, gpu_device, rl.RESET_ON_START, c["gamma"], c["lam"], what="16384x512")
+    check_forward(f, gpu_device, rl.RESET_AFTER_DONE, c["gamma"], c["lam"], what="16384x512")
+
+
+# ------------------------------------------------------------------- edge cases
+
+
+@pytest.mark.parametrize("pattern", ["none", "all_term", "all_trunc", "both", "first", "last",
+                                     "alternate"])
+def test_flag_patterns(pattern, gpu_device):
+    N, T = 6, 70
+    d = rollout(7, N, T)
+    term = np.zeros((N, T), np.uint8)
+    trunc = np.zeros((N, T), np.uint8)
+    if pattern == "all_term":
+        term[:] = 1
+    elif pattern == "all_trunc":
+        trunc[:] = 1
+    elif pattern == "both":
+        term[:] = 1
+        trunc[:] = 1
+    elif pattern == "first":
+        term[:, 0] = 1
+        trunc[:3, 0] = 1
+    elif pattern == "last":
+        term[:3, -1] = 1
+        trunc[3:, -1] = 1
+    elif pattern == "alternate":
+        term[:, ::3] = 1
+        trunc[:, 1::3] = 1
+    d.terminated, d.truncated = term, trunc
+    for boot in (True, False):
+        check_gae(d, gpu_device, boot=boot, what=pattern)
+        check_td(d, gpu_device, boot=boot, what=pattern)
+        check_disc(d, gpu_device, boot=boot, what=pattern)
+        check_vtrace(d, gpu_device, boot=boot, what=pattern)
+        check_retrace(d, gpu_device, boot=boot, what=pattern)
+
+
+def test_flags_as_bool_and_nonzero_bytes(gpu_device):
+    d = rollout(8, 5, 40)
+    r, v = dev(d.rewards, gpu_device), dev(d.values, gpu_device)
+    t_u8 = dev(d.terminated, gpu_device)
+    t_bool = t_u8.bool()
+    t_big = (t_u8 * 200)      # any nonzero byte counts as set
+    a1, _ = rl.gae(r, v, t_u8)
+    a2, _ = rl.gae(r, v, t_bool)
+    a3, _ = rl.gae(r, v, t_big)
+    assert torch.equal(a1, a2) and torch.equal(a1, a3)
+
+
+def test_unaligned_views_take_the_scalar_path(gpu_device):
+    """Inputs that are 4-byte but not 16-byte aligned (views at an odd element
+    offset of a larger buffer) give the same results as aligned copies."""
+    N, T = 37, 132
+    d = rollout(9, N, T)
+
+    def shifted(x, dtype):
+        flat = torch.zeros(N * T + 1, dtype=dtype, device=gpu_device)
+        flat[1:] = torch.from_numpy(np.ascontiguousarray(x)).reshape(-1).to(gpu_device)
+        return flat[1:].view(N, T)
+
+    r = shifted(d.rewards, torch.float32)
+    v = shifted(d.values, torch.float32)
+    term = shifted(d.terminated, torch.uint8)
+    trunc = shifted(d.truncated, torch.uint8)
+    tv = shifted(d.trunc_values, torch.float32)
+    assert r.data_ptr() % 16 != 0
+    adv, ret = rl.gae(r, v, term, trunc, tv, dev(d.bootstrap, gpu_device))
+    oadv, oret = oracle.gae(d.rewards, d.values, d.terminated, d.truncated, d.trunc_values,
+                            d.bootstrap, 0.99, 0.95)
+    assert_parity(adv, oadv, "unaligned adv")
+    assert_parity(ret, oret, "unaligned ret")
+    xi = shifted(workloads.forward_rollout(3, N, T).ints, torch.int32)
+    fl = shifted(workloads.forward_rollout(3, N, T).starts, torch.uint8)
+    out = rl.episodic_prefix_sum(xi, fl)
+    assert np.array_equal(out.cpu().numpy(),
+                          oracle.episodic_prefix_sum(xi.cpu().numpy(), fl.cpu().numpy()))
+
+
+def test_no_leak_across_done_is_bit_exact_on_gpu(gpu_device):
+    """beta = 0 at a done step makes everything before it independent of what
+    comes after, exactly (summary §5), also in the fp32 scan."""
+    N, T = 16, 3000
+    d = rollout(11, N, T, p_term=0.0, p_trunc=0.0)
+    d.terminated[:, 1500] = 1
+    d.truncated[:, 700] = 1
+    base = []
+    pert = []
+    for target, dd in ((base, d), (pert, None)):
+        if dd is None:
+            dd = rollout(11, N, T, p_term=0.0, p_trunc=0.0)
+            dd.terminated, dd.truncated = d.terminated, d.truncated
+            for k in ("rewards", "values", "q_values", "expected_q", "behaviour_logp",
+                      "target_logp", "trunc_values"):
+                getattr(dd, k)[:, 1501:] += 1.5
+            dd.bootstrap = dd.bootstrap + 2.0
+        r, v = dev(dd.rewards, gpu_device), dev(dd.values, gpu_device)
+        te, tr = dev(dd.terminated, gpu_device), dev(dd.truncated, gpu_device)
+        tv, b = dev(dd.trunc_values, gpu_device), dev(dd.bootstrap, gpu_device)
+        mu, pi = dev(dd.behaviour_logp, gpu_device), dev(dd.target_logp, gpu_device)
+        target.append(rl.gae(r, v, te, tr, tv, b)[0])
+        target.append(rl.td_lambda(r, v, te, tr, tv, b))
+        target.append(rl.discounted_returns(r, te, tr, tv, b))
+        target.append(rl.vtrace(r, v, mu, pi, te, tr, tv, b)[0])
+        target.append(rl.retrace(r, dev(dd.q_values, gpu_device), dev(dd.expected_q, gpu_device),
+                                 mu, pi, te, tr, tv, b))
+    for a, b in zip(base, pert):
+        assert torch.equal(a[:, :1501], b[:, :1501])
+
+
+def test_reset_conventions_agree_bitwise_on_gpu(gpu_device):
+    f = workloads.forward_rollout(12, 33, 777, p_start=0.05)
+    s = dev(f.starts, gpu_device)
+    dn = dev(f.dones, gpu_device)
+    x = dev(f.increments, gpu_device)
+    assert torch.equal(rl.eligibility_traces(x, s, rl.RESET_ON_START),
+                       rl.eligibility_traces(x, dn, rl.RESET_AFTER_DONE))
+    xi = dev(f.ints, gpu_device)
+    assert torch.equal(rl.episodic_prefix_sum(xi, s, rl.RESET_ON_START),
+                       rl.episodic_prefix_sum(xi, dn, rl.RESET_AFTER_DONE))
+
+
+def test_int32_prefix_sum_wraps_exactly(gpu_device):
+    N, T = 3, 5000
+    x = np.full((N, T), 2**31 - 7, np.int32)
+    x[1] = -(2**31)
+    x[2, ::2] = 123456789
+    flags = np.zeros((N, T), np.uint8)
+    flags[0, 2500] = 1
+    out = rl.episodic_prefix_sum(dev(x, gpu_device), dev(flags, gpu_device))
+    assert np.array_equal(out.cpu().numpy(), oracle.episodic_prefix_sum(x, flags))
+
+
+def test_empty_inputs(gpu_device):
+    for N, T in ((0, 16), (4, 0), (0, 0)):
+        z = torch.zeros((N, T), device=gpu_device)
+        f = torch.zeros((N, T), dtype=torch.uint8, device=gpu_device)
+        adv, ret = rl.gae(z, z, f)
+        assert adv.shape == (N, T) and ret.shape == (N, T)
+        assert rl.episodic_prefix_sum(z.int(), f).shape == (N, T)
+
+
+def test_aliasing_rejected_with_real_buffers(gpu_device):
+    d = rollout(13, 4, 32)
+    r, v, te = dev(d.rewards, gpu_device), dev(d.values, gpu_device), dev(d.terminated, gpu_device)
+    with pytest.raises(rl.RlcaError):
+        rl.gae(r, v, te, advantages=r)
+    with pytest.raises(rl.RlcaError):
+        rl.td_lambda(r, v, te, out=v)
+    # adjacent but disjoint halves of one buffer are fine
+    buf = torch.empty((2, 4, 32), device=gpu_device)
+    adv, ret = rl.gae(r, v, te, advantages=buf[0], returns=buf[1])
+    oadv, oret = oracle.gae(d.rewards, d.values, d.terminated, None, None, None, 0.99, 0.95)
+    assert_parity(adv, oadv, "adjacent adv")
+    assert_parity(ret, oret, "adjacent ret")
+
+
+def test_optional_outputs_may_be_omitted(gpu_device):
+    d = rollout(14, 9, 100)
+    r, v, te = dev(d.rewards, gpu_device), dev(d.values, gpu_device), dev(d.terminated, gpu_device)
+    adv, ret = rl.gae(r, v, te, with_returns=False)
+    assert ret is None
+    assert_parity(adv, oracle.gae(d.rewards, d.values, d.terminated, None, None, None,
+                                  0.99, 0.95)[0], "gae adv only")
+    mu, pi = dev(d.behaviour_logp, gpu_device), dev(d.target_logp, gpu_device)
+    vs, pg = rl.vtrace(r, v, mu, pi, te, with_pg=False)
+    assert pg is None
+    assert_parity(vs, oracle.vtrace(d.rewards, d.values, d.behaviour_logp, d.target_logp,
+                                    d.terminated, None, None, None, 0.99, 1.0, 1.0, 1.0)[0],
+                  "vtrace vs only")
+
+
+def test_extreme_log_ratios_are_clipped(gpu_device):
+    d = rollout(15, 4, 50)
+    d.target_logp = d.target_logp.copy()
+    d.target_logp[:, ::2] += 20.0
+    d.target_logp[:, 1::5] -= 20.0
+    check_vtrace(d, gpu_device, rho_bar=1e3, c_bar=1e3, lam=0.5, what="clip")
+    check_retrace(d, gpu_device, c_bar=1e3, lam=0.2, what="clip")
+
+
+def test_repeat_calls_are_deterministic(gpu_device):
+    d = rollout(16, 300, 513)
+    args = [dev(x, gpu_device) for x in (d.rewards, d.values, d.terminated, d.truncated,
+                                         d.trunc_values, d.bootstrap)]
+    a1, _ = rl.gae(*args)
+    a2, _ = rl.gae(*args)
+    assert torch.equal(a1, a2)
