@@ -22,7 +22,6 @@ Measurement:
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -311,15 +310,6 @@ def run_cpu_baseline(name, cfg, host, seconds):
 # ------------------------------------------------------------------ traffic
 
 
-def kernel_source_digest():
-    h = hashlib.sha256()
-    for rel in ("linear_recurrence_scan_row_amd/csrc/rlca.hip",
-                "linear_recurrence_scan_row_amd/csrc/scan_core.hpp", "include/rlca.h"):
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
 def measured_traffic(kernel_name, workload):
     """HBM bytes per launch from a committed rocprofv3 counter summary, or None
     when the summary is missing or the kernel source changed since it was taken."""
@@ -331,7 +321,9 @@ def measured_traffic(kernel_name, workload):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_digest") != kernel_source_digest():
+    from linear_recurrence_scan_row_amd.profiling import source_digest
+
+    if kv.get("source_digest") != source_digest():
         return None
     try:
         return float(kv["traffic_bytes_per_launch"])

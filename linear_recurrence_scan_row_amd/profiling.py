@@ -1,0 +1,124 @@
+"""Summaries of rocprofv3 results (the SQLite ``*_results.db`` it writes) for the
+credit-assignment kernels.
+
+  python -m linear_recurrence_scan_row_amd.profiling stats DB [--command CMD]
+      per-kernel dispatch count and average / min / max duration (us), from a
+      ``rocprofv3 --kernel-trace --stats`` run.
+
+  python -m linear_recurrence_scan_row_amd.profiling traffic --fetch DB --write DB
+         --kernel SUBSTR --copy-bytes N --algorithmic-bytes B --out FILE [...]
+      HBM bytes per launch of one kernel from a ``--pmc FETCH_SIZE`` run and a
+      ``--pmc WRITE_SIZE`` run of the same command.  Both counters are scaled
+      by what they read for a plain device copy of N bytes (N read + N
+      written) captured in the same runs: on gfx950 FETCH_SIZE reads about
+      half of the bytes a copy really fetches, WRITE_SIZE reads them exactly.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import os
+import sqlite3
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KERNEL_SOURCES = ("linear_recurrence_scan_row_amd/csrc/rlca.hip",
+                  "linear_recurrence_scan_row_amd/csrc/scan_core.hpp", "include/rlca.h")
+
+
+def source_digest() -> str:
+    """Digest of the kernel sources; stored with a counter summary so that a
+    summary taken on other code is not reported for this code."""
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def kernel_stats(db: str, match: str = ""):
+    con = sqlite3.connect(db)
+    rows = con.execute(
+        "select name, count(*), avg(duration), min(duration), max(duration) from kernels "
+        "where name like ? group by name order by sum(duration) desc", (f"%{match}%",)).fetchall()
+    return [(n, c, a / 1e3, lo / 1e3, hi / 1e3) for n, c, a, lo, hi in rows]
+
+
+def counter_values(db: str, counter: str):
+    con = sqlite3.connect(db)
+    return con.execute(
+        "select dispatch_id, kernel_name, value from counters_collection where counter_name = ? "
+        "order by dispatch_id", (counter,)).fetchall()
+
+
+def traffic(fetch_db, write_db, kernel, copy_bytes):
+    fetch = counter_values(fetch_db, "FETCH_SIZE")
+    write = counter_values(write_db, "WRITE_SIZE")
+    # calibration: copy dispatches whose writes equal the known copy size
+    copy_ids = {d for d, name, v in write
+                if "copyBuffer" in name and abs(v * 1024 - copy_bytes) <= 0.01 * copy_bytes}
+    if not copy_ids:
+        raise SystemExit("no calibration copy found in the WRITE_SIZE run")
+    cf = [v for d, name, v in fetch if d in copy_ids]
+    cw = [v for d, name, v in write if d in copy_ids]
+    fetch_factor = copy_bytes / (1024 * sum(cf) / len(cf))
+    write_factor = copy_bytes / (1024 * sum(cw) / len(cw))
+    kf = [v for d, name, v in fetch if kernel in name]
+    kw = [v for d, name, v in write if kernel in name]
+    if not kf or not kw:
+        raise SystemExit(f"kernel {kernel!r} not found in the counter runs")
+    f_kib = sum(kf) / len(kf)
+    w_kib = sum(kw) / len(kw)
+    return dict(dispatches=len(kf), fetch_kib_raw=f_kib, write_kib_raw=w_kib,
+                calibration_copy_bytes=copy_bytes, calibration_dispatches=len(copy_ids),
+                fetch_factor=fetch_factor, write_factor=write_factor,
+                traffic_bytes_per_launch=f_kib * 1024 * fetch_factor + w_kib * 1024 * write_factor)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("db")
+    s.add_argument("--match", default="")
+    s.add_argument("--command", default="")
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--algorithmic-bytes", type=int, required=True)
+    t.add_argument("--fetch-command", default="")
+    t.add_argument("--write-command", default="")
+    t.add_argument("--out", default="")
+    a = ap.parse_args(argv)
+    if a.cmd == "stats":
+        lines = []
+        if a.command:
+            lines.append(f"command: {a.command}")
+        lines.append(f"source_digest: {source_digest()}")
+        lines.append("")
+        lines.append("| kernel | dispatches | avg us | min us | max us |")
+        lines.append("|---|---|---|---|---|")
+        for n, c, avg, lo, hi in kernel_stats(a.db, a.match):
+            lines.append(f"| {n} | {c} | {avg:.3f} | {lo:.3f} | {hi:.3f} |")
+        print("\n".join(lines))
+        return
+    r = traffic(a.fetch, a.write, a.kernel, a.copy_bytes)
+    out = [f"kernel: {a.kernel}",
+           f"fetch_command: {a.fetch_command}",
+           f"write_command: {a.write_command}"]
+    out += [f"{k}: {v:.6g}" if isinstance(v, float) else f"{k}: {v}" for k, v in r.items()]
+    out.append(f"algorithmic_bytes_per_launch: {a.algorithmic_bytes}")
+    out.append(f"traffic_over_algorithmic: {r['traffic_bytes_per_launch'] / a.algorithmic_bytes:.4f}")
+    out.append(f"source_digest: {source_digest()}")
+    text = "\n".join(out) + "\n"
+    if a.out:
+        with open(a.out, "w") as f:
+            f.write(text)
+    sys.stdout.write(text)
+
+
+if __name__ == "__main__":
+    main()
