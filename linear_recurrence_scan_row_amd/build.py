@@ -1,13 +1,21 @@
-"""Build the HIP library librlca.so for gfx950 (in-tree, next to this file)."""
+"""Build the HIP library librlca.so for gfx950 (in-tree, next to this file).
+
+Each csrc/*.hip translation unit (one per estimator plus the C-ABI host code)
+is compiled in parallel to an object under _build/, then linked into one
+shared library.
+"""
 from __future__ import annotations
 
+import glob
 import os
 import subprocess
+import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "librlca.so")
-SOURCES = [os.path.join(HERE, "csrc", "rlca.hip")]
+BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -15,26 +23,56 @@ FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-Wall",
     "-Werror",
     "-Wno-unused-command-line-argument",
     # keep the compiler from emitting packed-fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # let the hardware preload the leading kernel arguments into SGPRs
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-I", os.path.join(ROOT, "include"),
-    "-I", os.path.join(HERE, "csrc"),
+    "-I", CSRC,
 ]
 
 
-def build(verbose: bool = False, extra=None) -> str:
-    tmp = LIB_PATH + ".tmp"
-    cmd = [HIPCC, *FLAGS, *(extra or []), "-o", tmp, *SOURCES]
+def sources():
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+
+def build(verbose: bool = False, extra=None, out: str = LIB_PATH, jobs: int = 8) -> str:
+    """Compile every translation unit (up to `jobs` at once) and link `out`."""
+    tag = os.path.splitext(os.path.basename(out))[0]
+    obj_dir = os.path.join(BUILD_DIR, tag)
+    os.makedirs(obj_dir, exist_ok=True)
+    pending = []
+    objs = []
+    for src in sources():
+        obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
+        objs.append(obj)
+        cmd = [HIPCC, *FLAGS, *(extra or []), "-c", "-o", obj, src]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        pending.append((cmd, src))
+    running = []
+    failed = []
+    while pending or running:
+        while pending and len(running) < jobs:
+            cmd, src = pending.pop(0)
+            running.append((subprocess.Popen(cmd), src))
+        proc, src = running.pop(0)
+        if proc.wait() != 0:
+            failed.append(src)
+    if failed:
+        raise RuntimeError(f"hipcc failed for: {', '.join(failed)}")
+    tmp = out + ".tmp"
+    link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+        print(" ".join(link), flush=True)
+    subprocess.run(link, check=True)
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    extra = sys.argv[1:]
+    print(build(verbose=True, extra=extra))

@@ -1,0 +1,621 @@
+// kernels.hpp -- the fused credit-assignment kernels for MI355X (gfx950).
+//
+// Each workgroup owns a contiguous range of whole rows of the [num_envs, T]
+// rollout (rows are independent; "rl-triton", paperlayer.ai summary, §4
+// Kernel design) and walks it in tiles of NW*64*K steps:
+//   1. coalesced loads of the raw rollout, each element read once (dwordx4 per
+//      lane for fp32 streams, one dword per four flag bytes);
+//   2. boundary resolution and the estimator's (alpha_t, beta_t) built in
+//      registers (summary §3.1 / §3.2; §4 Fusion);
+//   3. the shared affine scan of scan_core.hpp (lane fold, wave64 DPP scan,
+//      LDS wave totals, tile carry);
+//   4. one store of each output.
+// Short rows are packed many to a tile: the window edge is folded into
+// alpha_{T-1} with beta_{T-1} = 0, so a row end is a chain cut like any done
+// step and rows never interact.  Long rows take several tiles with the carry
+// kept in registers, so there is no length limit and no LDS growth with T.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "rlca.h"
+#include "scan_core.hpp"
+
+namespace rlca {
+
+// K consecutive steps per lane: one K-wide load per fp32 stream (dwordx4 at
+// K = 4).  Wider per-lane chunks make one load instruction touch lanes 32+
+// bytes apart and lose coalescing.
+#ifndef RLCA_STEPS_PER_LANE
+#define RLCA_STEPS_PER_LANE 4
+#endif
+constexpr int kK = RLCA_STEPS_PER_LANE;
+static_assert(kK == 1 || kK == 2 || kK == 4, "steps per lane: 1, 2 or 4");
+
+enum Estimator : int { kGae = 0, kTdLambda = 1, kDiscounted = 2, kVtrace = 3, kRetrace = 4 };
+
+struct Geometry {
+    int64_t num_envs;
+    uint32_t T;
+    uint32_t rows_per_group;  // whole rows owned by one workgroup iteration
+    uint32_t num_groups;
+};
+
+struct BackwardParams {
+    const float *rewards;
+    const float *values;  // V(s_t); Q(s_t, a_t) for Retrace
+    const float *expected_q;
+    const float *behaviour_logp;
+    const float *target_logp;
+    const uint8_t *terminated;
+    const uint8_t *truncated;
+    const float *trunc_values;
+    const float *bootstrap;
+    float *out0;  // advantages / returns / vs / q_ret
+    float *out1;  // GAE returns or V-Trace pg advantages; may be null
+    float gamma, lambda, rho_bar, c_bar;
+    Geometry geo;
+};
+
+struct ForwardParams {
+    const void *x;
+    const uint8_t *flags;
+    void *out;
+    float decay;  // gamma*lambda for traces, 1 for prefix sums
+    Geometry geo;
+};
+
+// Launch configuration chosen on the host.
+struct LaunchShape {
+    int waves;        // NW: 1, 2, 4 or 8 waves per workgroup
+    bool wave_local;  // rows end at wave boundaries (T divides 64*K)
+    bool vec;         // dwordx4 path: T % 4 == 0 and 16-byte aligned arrays
+};
+
+// ---------------------------------------------------------------- memory access
+// `p` points at the workgroup's first element; `off` is the lane's first step
+// relative to it and `L` the number of valid steps.  With VEC the caller
+// guarantees 4K-byte alignment of p + off and L % K == 0, so a lane's K
+// steps are either wholly valid or wholly past the end.
+
+template <typename E, int N>
+struct VecOf {
+    typedef E type __attribute__((ext_vector_type(N)));
+};
+template <typename E>
+struct VecOf<E, 1> {
+    typedef E type;
+};
+
+// Unsigned integer holding K flag bytes.
+template <int N>
+struct FlagWord;
+template <>
+struct FlagWord<1> {
+    typedef uint8_t type;
+};
+template <>
+struct FlagWord<2> {
+    typedef uint16_t type;
+};
+template <>
+struct FlagWord<4> {
+    typedef uint32_t type;
+};
+
+template <bool VEC, typename E>
+__device__ __forceinline__ void load_steps(E (&x)[kK], const E *__restrict__ p, uint32_t off,
+                                           uint32_t L) {
+    static_assert(sizeof(E) == 4, "32-bit elements");
+    // Element-typed vector: its lanes are read by value (no bit cast of a
+    // vector element, which this compiler lowers as a read of element 0).
+    typedef typename VecOf<E, kK>::type vec;
+    if constexpr (VEC) {
+        vec q = {};
+        if (off < L) q = *reinterpret_cast<const vec *>(p + off);
+        if constexpr (kK == 1) {
+            x[0] = q;
+        } else {
+#pragma unroll
+            for (int i = 0; i < kK; ++i) x[i] = q[i];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kK; ++i) x[i] = (off + i < L) ? p[off + i] : E(0);
+    }
+}
+
+template <bool VEC>
+__device__ __forceinline__ void load_flags(bool (&f)[kK], const uint8_t *__restrict__ p,
+                                           uint32_t off, uint32_t L) {
+    if constexpr (VEC) {
+        typedef typename FlagWord<kK>::type word;
+        uint32_t q = 0;
+        if (off < L) q = *reinterpret_cast<const word *>(p + off);
+#pragma unroll
+        for (int i = 0; i < kK; ++i) f[i] = ((q >> (8 * i)) & 0xffu) != 0;
+    } else {
+#pragma unroll
+        for (int i = 0; i < kK; ++i) f[i] = (off + i < L) ? (p[off + i] != 0) : false;
+    }
+}
+
+template <bool VEC, typename E>
+__device__ __forceinline__ void store_steps(E *__restrict__ p, const E (&x)[kK], uint32_t off,
+                                            uint32_t L) {
+    typedef typename VecOf<E, kK>::type vec;
+    if constexpr (VEC) {
+        if (off < L) {
+            vec q;
+            if constexpr (kK == 1) {
+                q = x[0];
+            } else {
+#pragma unroll
+                for (int i = 0; i < kK; ++i) q[i] = x[i];
+            }
+            __builtin_nontemporal_store(q, reinterpret_cast<vec *>(p + off));
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kK; ++i)
+            if (off + i < L) p[off + i] = x[i];
+    }
+}
+
+// Row-local step index t and row offset of each of the lane's K steps.
+__device__ __forceinline__ void step_positions(uint32_t off, uint32_t T, uint32_t (&t)[kK],
+                                               uint32_t (&row)[kK]) {
+    uint32_t r = off / T;
+    uint32_t s = off - r * T;
+#pragma unroll
+    for (int i = 0; i < kK; ++i) {
+        t[i] = s;
+        row[i] = r;
+        if (++s == T) {
+            s = 0;
+            ++r;
+        }
+    }
+}
+
+__device__ __forceinline__ float importance_ratio(float target_logp, float behaviour_logp) {
+    const float l = fminf(fmaxf(target_logp - behaviour_logp, -RLCA_LOG_RATIO_CLIP),
+                          RLCA_LOG_RATIO_CLIP);
+    return expf(l);
+}
+
+// Rows [row0, row0 + rows) of group g and the flat offset of their first step.
+__device__ __forceinline__ void group_rows(const Geometry &geo, uint32_t g, int64_t &row0,
+                                           uint32_t &L, int64_t &base) {
+    row0 = (int64_t)g * geo.rows_per_group;
+    const int64_t rows_left = geo.num_envs - row0;
+    const uint32_t rows =
+        rows_left < (int64_t)geo.rows_per_group ? (uint32_t)rows_left : geo.rows_per_group;
+    L = rows * geo.T;
+    base = row0 * (int64_t)geo.T;
+}
+
+// ------------------------------------------------------- leading kernel arguments
+// The geometry and the first five input arrays are passed as separate scalar
+// kernel arguments ahead of the parameter block: gfx950 preloads leading
+// kernel arguments into SGPRs before a wave starts (13 dwords here), so each
+// wave can issue its first loads without a scalar-memory round trip for its
+// arguments.  Which five arrays lead depends on the estimator.
+#define LEAD_ARGS                                                                         \
+    const void *lead0, const void *lead1, const void *lead2, const void *lead3,            \
+        const void *lead4, uint32_t lead_T, uint32_t lead_rows_per_group, uint32_t lead_num_envs
+#define LEAD_NAMES lead0, lead1, lead2, lead3, lead4, lead_T, lead_rows_per_group, lead_num_envs
+
+struct Lead {
+    uint32_t T, rows_per_group, num_envs;
+    const void *ptr[5];
+};
+
+// Host side: the estimator's five leading arrays, in argument order.
+template <int EST>
+inline void lead_from(const BackwardParams &p, Lead &l) {
+    if constexpr (EST == kGae || EST == kTdLambda) {
+        l.ptr[0] = p.rewards, l.ptr[1] = p.values, l.ptr[2] = p.terminated;
+        l.ptr[3] = p.truncated, l.ptr[4] = p.trunc_values;
+    } else if constexpr (EST == kDiscounted) {
+        l.ptr[0] = p.rewards, l.ptr[1] = p.terminated, l.ptr[2] = p.truncated;
+        l.ptr[3] = p.trunc_values, l.ptr[4] = p.bootstrap;
+    } else if constexpr (EST == kVtrace) {
+        l.ptr[0] = p.rewards, l.ptr[1] = p.values, l.ptr[2] = p.behaviour_logp;
+        l.ptr[3] = p.target_logp, l.ptr[4] = p.terminated;
+    } else {
+        l.ptr[0] = p.rewards, l.ptr[1] = p.values, l.ptr[2] = p.expected_q;
+        l.ptr[3] = p.behaviour_logp, l.ptr[4] = p.target_logp;
+    }
+}
+
+// Device side: the same five arrays and the geometry, taken from the
+// preloaded arguments.
+template <int EST>
+__device__ __forceinline__ void adopt_lead(BackwardParams &p, LEAD_ARGS) {
+    typedef const float *F;
+    typedef const uint8_t *U;
+    if constexpr (EST == kGae || EST == kTdLambda) {
+        p.rewards = F(lead0), p.values = F(lead1), p.terminated = U(lead2);
+        p.truncated = U(lead3), p.trunc_values = F(lead4);
+    } else if constexpr (EST == kDiscounted) {
+        p.rewards = F(lead0), p.terminated = U(lead1), p.truncated = U(lead2);
+        p.trunc_values = F(lead3), p.bootstrap = F(lead4);
+    } else if constexpr (EST == kVtrace) {
+        p.rewards = F(lead0), p.values = F(lead1), p.behaviour_logp = F(lead2);
+        p.target_logp = F(lead3), p.terminated = U(lead4);
+    } else {
+        p.rewards = F(lead0), p.values = F(lead1), p.expected_q = F(lead2);
+        p.behaviour_logp = F(lead3), p.target_logp = F(lead4);
+    }
+    p.geo.T = lead_T;
+    p.geo.rows_per_group = lead_rows_per_group;
+    p.geo.num_envs = lead_num_envs;
+}
+
+__device__ __forceinline__ void adopt_lead(ForwardParams &p, LEAD_ARGS) {
+    p.x = lead0;
+    p.flags = static_cast<const uint8_t *>(lead1);
+    p.out = const_cast<void *>(lead2);
+    p.geo.T = lead_T;
+    p.geo.rows_per_group = lead_rows_per_group;
+    p.geo.num_envs = lead_num_envs;
+    (void)lead3;
+    (void)lead4;
+}
+
+// ------------------------------------------------------------- backward kernel
+// A_t = alpha_t + beta_t * A_{t+1}.  Lanes take chunks in reverse time order, so
+// the lane-order scan of scan_core.hpp runs from the end of the tile backwards.
+template <int EST, bool TRUNC, bool VEC, int NW, bool WAVE_LOCAL>
+__global__ __launch_bounds__(NW * kWave) void backward_scan(LEAD_ARGS, BackwardParams p) {
+    adopt_lead<EST>(p, LEAD_NAMES);
+    constexpr uint32_t kTile = NW * kWave * kK;
+    __shared__ float lds_a[2 * NW], lds_b[2 * NW];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x / kWave;
+    const uint32_t chunk = (NW - 1 - w) * kWave + (kWave - 1 - lane);
+    const uint32_t T = p.geo.T;
+    const float gamma = p.gamma;
+    int parity = 0;
+
+    // The grid never exceeds the group count, so the first group always
+    // exists; testing only at the bottom lets every kernel-argument load go
+    // out together instead of after a first round trip for the bound.
+    uint32_t g = blockIdx.x;
+    do {
+        int64_t row0, base;
+        uint32_t L;
+        group_rows(p.geo, g, row0, L, base);
+        const uint32_t ntiles = (L + kTile - 1) / kTile;
+        float carry = 0.f;  // A just after the current tile (A_T = 0: edges live in alpha)
+
+        for (uint32_t it = 0; it < ntiles; ++it) {
+            const uint32_t off = (ntiles - 1 - it) * kTile + chunk * kK;
+
+            // ---- 1. loads (each input element once)
+            float r[kK], v[kK], eq[kK], mu[kK], pi[kK], tv[kK];
+            bool term[kK], trunc[kK];
+            load_steps<VEC>(r, p.rewards + base, off, L);
+            if constexpr (EST != kDiscounted) load_steps<VEC>(v, p.values + base, off, L);
+            if constexpr (EST == kRetrace) load_steps<VEC>(eq, p.expected_q + base, off, L);
+            if constexpr (EST == kVtrace || EST == kRetrace) {
+                load_steps<VEC>(mu, p.behaviour_logp + base, off, L);
+                load_steps<VEC>(pi, p.target_logp + base, off, L);
+            }
+            load_flags<VEC>(term, p.terminated + base, off, L);
+            if constexpr (TRUNC) {
+                load_flags<VEC>(trunc, p.truncated + base, off, L);
+                load_steps<VEC>(tv, p.trunc_values + base, off, L);
+            }
+            // Loads whose addresses depend only on positions go out with the
+            // main batch: the bootstrap of rows ending in this chunk, and for
+            // lane 0 the first step of the next chunk in time (its neighbour
+            // lane - 1 sits in another wave or tile).
+            uint32_t t[kK], row[kK];
+            step_positions(off, T, t, row);
+            bool valid[kK];
+            float boot[kK];
+#pragma unroll
+            for (int i = 0; i < kK; ++i) {
+                valid[i] = off + i < L;
+                boot[i] = 0.f;
+                if (valid[i] && t[i] == T - 1 && p.bootstrap != nullptr)
+                    boot[i] = p.bootstrap[row0 + row[i]];
+            }
+            float v_first = 0.f, mu_first = 0.f, pi_first = 0.f, eq_first = 0.f;
+            if (lane == 0 && off + kK < L) {
+                const int64_t jh = base + off + kK;
+                if constexpr (EST == kGae || EST == kTdLambda || EST == kVtrace)
+                    v_first = p.values[jh];
+                if constexpr (EST == kRetrace) {
+                    mu_first = p.behaviour_logp[jh];
+                    pi_first = p.target_logp[jh];
+                    eq_first = p.expected_q[jh];
+                }
+            }
+
+            // ---- 2. boundary resolution
+            bool cont[kK];
+            float succ[kK];  // successor value where the chain stops
+#pragma unroll
+            for (int i = 0; i < kK; ++i) {
+                const bool tr = TRUNC && trunc[i] && !term[i];
+                const bool edge = t[i] == T - 1;
+                cont[i] = valid[i] && !term[i] && !tr && !edge;
+                float sv = term[i] ? 0.f : boot[i];
+                if constexpr (TRUNC) {
+                    if (tr) sv = tv[i];
+                }
+                succ[i] = sv;
+            }
+
+            // ---- 3. halo: the first step of the next chunk in time, from lane - 1
+            float v_next = 0.f, c_next = 0.f, eq_next = 0.f;
+            if constexpr (EST == kGae || EST == kTdLambda || EST == kVtrace)
+                v_next = from_lower_lane(v[0], v_first);
+            float c[kK];
+            if constexpr (EST == kVtrace || EST == kRetrace) {
+#pragma unroll
+                for (int i = 0; i < kK; ++i)
+                    c[i] = p.lambda * fminf(p.c_bar, importance_ratio(pi[i], mu[i]));
+            }
+            if constexpr (EST == kRetrace) {
+                const float c_first =
+                    p.lambda * fminf(p.c_bar, importance_ratio(pi_first, mu_first));
+                c_next = from_lower_lane(c[0], c_first);
+                eq_next = from_lower_lane(eq[0], eq_first);
+            }
+
+            // ---- 4. coefficients in registers
+            float alpha[kK], beta[kK], aux[kK];
+#pragma unroll
+            for (int i = 0; i < kK; ++i) {
+                const bool k = cont[i];
+                float a, b, x = 0.f;
+                if constexpr (EST == kGae) {
+                    const float vn = i + 1 < kK ? v[i + 1] : v_next;
+                    a = r[i] + gamma * (k ? vn : succ[i]) - v[i];
+                    b = k ? gamma * p.lambda : 0.f;
+                } else if constexpr (EST == kTdLambda) {
+                    const float vn = i + 1 < kK ? v[i + 1] : v_next;
+                    a = k ? r[i] + gamma * (1.f - p.lambda) * vn : r[i] + gamma * succ[i];
+                    b = k ? gamma * p.lambda : 0.f;
+                } else if constexpr (EST == kDiscounted) {
+                    a = k ? r[i] : r[i] + gamma * succ[i];
+                    b = k ? gamma : 0.f;
+                } else if constexpr (EST == kVtrace) {
+                    const float vn = i + 1 < kK ? v[i + 1] : v_next;
+                    const float rho = fminf(p.rho_bar, importance_ratio(pi[i], mu[i]));
+                    a = rho * (r[i] + gamma * (k ? vn : succ[i]) - v[i]);
+                    b = k ? gamma * c[i] : 0.f;
+                    x = k ? gamma * rho : 0.f;  // pg_t = alpha_t + gamma rho_t A_{t+1}
+                } else {  // Retrace: the decay uses the next step's trace coefficient
+                    const float cn = i + 1 < kK ? c[i + 1] : c_next;
+                    const float en = i + 1 < kK ? eq[i + 1] : eq_next;
+                    a = r[i] + gamma * (k ? en : succ[i]) - v[i];
+                    b = k ? gamma * cn : 0.f;
+                }
+                alpha[i] = valid[i] ? a : 0.f;
+                beta[i] = valid[i] ? b : 1.f;
+                aux[i] = x;
+            }
+
+            // ---- 5. scan: lane fold (latest step first), then wave / workgroup
+            float fa = 0.f, fb = 1.f;  // identity; step i applied after the later steps
+#pragma unroll
+            for (int i = kK - 1; i >= 0; --i) {
+                fa = alpha[i] + beta[i] * fa;
+                fb = beta[i] * fb;
+            }
+            float carry_out;
+            float A = block_carry_in<NW, WAVE_LOCAL>(fa, fb, carry, lds_a, lds_b, parity,
+                                                      carry_out);
+            parity ^= 1;
+            carry = carry_out;
+
+            // ---- 6. outputs, one store each
+            float o0[kK], o1[kK];
+#pragma unroll
+            for (int i = kK - 1; i >= 0; --i) {
+                const float An = A;  // A_{t+1}
+                A = alpha[i] + beta[i] * An;
+                if constexpr (EST == kGae) {
+                    o0[i] = A;
+                    o1[i] = A + v[i];
+                } else if constexpr (EST == kVtrace) {
+                    o0[i] = v[i] + A;
+                    o1[i] = alpha[i] + aux[i] * An;
+                } else if constexpr (EST == kRetrace) {
+                    o0[i] = v[i] + A;
+                    o1[i] = 0.f;
+                } else {
+                    o0[i] = A;
+                    o1[i] = 0.f;
+                }
+            }
+            store_steps<VEC>(p.out0 + base, o0, off, L);
+            if constexpr (EST == kGae || EST == kVtrace) {
+                if (p.out1 != nullptr) store_steps<VEC>(p.out1 + base, o1, off, L);
+            }
+        }
+        g += gridDim.x;
+    } while (g < p.geo.num_groups);
+}
+
+// -------------------------------------------------------------- forward kernel
+// A_t = alpha_t + beta_t * A_{t-1} with alpha = x, beta = decay, beta = 0 where a
+// new episode starts (summary §5: the forward scans cut where d_{t-1} = 1).
+// V = float (traces, f32 sums) or uint32_t (int32 sums, wrap-around).
+template <typename V, bool AFTER_DONE, bool VEC, int NW, bool WAVE_LOCAL>
+__global__ __launch_bounds__(NW * kWave) void forward_scan(LEAD_ARGS, ForwardParams p) {
+    adopt_lead(p, LEAD_NAMES);
+    constexpr uint32_t kTile = NW * kWave * kK;
+    __shared__ V lds_a[2 * NW], lds_b[2 * NW];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x / kWave;
+    const uint32_t chunk = w * kWave + lane;
+    const uint32_t T = p.geo.T;
+    const V decay = __builtin_bit_cast(V, __builtin_bit_cast(uint32_t, p.decay));
+    const V *__restrict__ xs = static_cast<const V *>(p.x);
+    V *__restrict__ out = static_cast<V *>(p.out);
+    int parity = 0;
+
+    // The grid never exceeds the group count, so the first group always
+    // exists; testing only at the bottom lets every kernel-argument load go
+    // out together instead of after a first round trip for the bound.
+    uint32_t g = blockIdx.x;
+    do {
+        int64_t row0, base;
+        uint32_t L;
+        group_rows(p.geo, g, row0, L, base);
+        const uint32_t ntiles = (L + kTile - 1) / kTile;
+        V carry = V(0);
+
+        for (uint32_t it = 0; it < ntiles; ++it) {
+            const uint32_t off = it * kTile + chunk * kK;
+            V x[kK];
+            bool f[kK];
+            load_steps<VEC>(x, xs + base, off, L);
+            load_flags<VEC>(f, p.flags + base, off, L);
+            bool first = false;  // flag of the step before the lane's chunk (lane 0)
+            if constexpr (AFTER_DONE) {
+                if (lane == 0 && off > 0 && off - 1 < L) first = p.flags[base + off - 1] != 0;
+            }
+            uint32_t t[kK], row[kK];
+            step_positions(off, T, t, row);
+            bool prev_done = false;
+            if constexpr (AFTER_DONE)
+                prev_done = from_lower_lane<uint32_t>(f[kK - 1] ? 1u : 0u, first ? 1u : 0u) != 0;
+            V alpha[kK], beta[kK];
+#pragma unroll
+            for (int i = 0; i < kK; ++i) {
+                const bool valid = off + i < L;
+                bool reset = t[i] == 0;
+                if constexpr (AFTER_DONE) {
+                    reset = reset || (i == 0 ? prev_done : f[i - 1]);
+                } else {
+                    reset = reset || f[i];
+                }
+                alpha[i] = valid ? x[i] : V(0);
+                beta[i] = valid ? (reset ? V(0) : decay) : V(1);
+            }
+            V fa = V(0), fb = V(1);
+#pragma unroll
+            for (int i = 0; i < kK; ++i) {
+                fa = alpha[i] + beta[i] * fa;
+                fb = beta[i] * fb;
+            }
+            V carry_out;
+            V A = block_carry_in<NW, WAVE_LOCAL>(fa, fb, carry, lds_a, lds_b, parity, carry_out);
+            parity ^= 1;
+            carry = carry_out;
+            V o[kK];
+#pragma unroll
+            for (int i = 0; i < kK; ++i) {
+                A = alpha[i] + beta[i] * A;
+                o[i] = A;
+            }
+            store_steps<VEC>(out + base, o, off, L);
+            (void)row;
+        }
+        g += gridDim.x;
+    } while (g < p.geo.num_groups);
+}
+
+// ------------------------------------------------------------------ launching
+
+// Upper bound on the launch grid; larger problems loop over row groups.
+constexpr uint32_t kMaxGrid = 1u << 20;
+
+inline Geometry make_geometry(int64_t num_envs, int64_t T, int waves, uint32_t *grid) {
+    const uint32_t tile = (uint32_t)waves * kWave * kK;
+    Geometry g;
+    g.num_envs = num_envs;
+    g.T = (uint32_t)T;
+    g.rows_per_group = (uint32_t)T <= tile ? tile / (uint32_t)T : 1u;
+    const int64_t groups = (num_envs + g.rows_per_group - 1) / g.rows_per_group;
+    g.num_groups = (uint32_t)groups;
+    *grid = groups < (int64_t)kMaxGrid ? (uint32_t)groups : kMaxGrid;
+    return g;
+}
+
+template <typename P>
+inline rlca_status launch_kernel(const void *kernel, int waves, P &params, Lead &lead,
+                                 hipStream_t stream) {
+    uint32_t grid;
+    params.geo = make_geometry(params.geo.num_envs, params.geo.T, waves, &grid);
+    lead.T = params.geo.T;
+    lead.rows_per_group = params.geo.rows_per_group;
+    lead.num_envs = (uint32_t)params.geo.num_envs;
+    void *args[] = {&lead.ptr[0], &lead.ptr[1], &lead.ptr[2],         &lead.ptr[3],
+                    &lead.ptr[4], &lead.T,      &lead.rows_per_group, &lead.num_envs,
+                    &params};
+    const hipError_t e =
+        hipLaunchKernel(kernel, dim3(grid), dim3(waves * kWave), args, 0, stream);
+    return e == hipSuccess ? RLCA_OK : RLCA_ERR_HIP;
+}
+
+// The vector path instantiates every wave count and the wave-local variant;
+// the scalar (unaligned or T % 4 != 0) path is one general configuration.
+template <int EST, bool TRUNC>
+const void *backward_kernel(const LaunchShape &s) {
+    if (!s.vec) return (const void *)backward_scan<EST, TRUNC, false, 4, false>;
+#define RLCA_PICK(NW)                                                             \
+    return s.wave_local ? (const void *)backward_scan<EST, TRUNC, true, NW, true> \
+                        : (const void *)backward_scan<EST, TRUNC, true, NW, false>
+    switch (s.waves) {
+        case 1: RLCA_PICK(1);
+        case 2: RLCA_PICK(2);
+        case 8: RLCA_PICK(8);
+        default: RLCA_PICK(4);
+    }
+#undef RLCA_PICK
+}
+
+template <int EST>
+rlca_status launch_backward(BackwardParams &p, const LaunchShape &s, hipStream_t stream) {
+    const void *k = p.truncated != nullptr ? backward_kernel<EST, true>(s)
+                                           : backward_kernel<EST, false>(s);
+    Lead lead;
+    lead_from<EST>(p, lead);
+    return launch_kernel(k, s.vec ? s.waves : 4, p, lead, stream);
+}
+
+template <typename V, bool AFTER_DONE>
+const void *forward_kernel(const LaunchShape &s) {
+    if (!s.vec) return (const void *)forward_scan<V, AFTER_DONE, false, 4, false>;
+#define RLCA_PICK(NW)                                                              \
+    return s.wave_local ? (const void *)forward_scan<V, AFTER_DONE, true, NW, true> \
+                        : (const void *)forward_scan<V, AFTER_DONE, true, NW, false>
+    switch (s.waves) {
+        case 1: RLCA_PICK(1);
+        case 2: RLCA_PICK(2);
+        case 8: RLCA_PICK(8);
+        default: RLCA_PICK(4);
+    }
+#undef RLCA_PICK
+}
+
+template <typename V>
+rlca_status launch_forward(ForwardParams &p, bool after_done, const LaunchShape &s,
+                           hipStream_t stream) {
+    const void *k = after_done ? forward_kernel<V, true>(s) : forward_kernel<V, false>(s);
+    Lead lead = {0, 0, 0, {p.x, p.flags, p.out, nullptr, nullptr}};
+    return launch_kernel(k, s.vec ? s.waves : 4, p, lead, stream);
+}
+
+// One translation unit per estimator instantiates these (see est_*.hip).
+rlca_status launch_gae(BackwardParams &p, const LaunchShape &s, hipStream_t stream);
+rlca_status launch_td_lambda(BackwardParams &p, const LaunchShape &s, hipStream_t stream);
+rlca_status launch_discounted(BackwardParams &p, const LaunchShape &s, hipStream_t stream);
+rlca_status launch_vtrace(BackwardParams &p, const LaunchShape &s, hipStream_t stream);
+rlca_status launch_retrace(BackwardParams &p, const LaunchShape &s, hipStream_t stream);
+rlca_status launch_forward_f32(ForwardParams &p, bool after_done, const LaunchShape &s,
+                               hipStream_t stream);
+rlca_status launch_forward_u32(ForwardParams &p, bool after_done, const LaunchShape &s,
+                               hipStream_t stream);
+
+}  // namespace rlca

@@ -14,7 +14,8 @@
 //   * each lane owns K consecutive steps and folds them serially (work-efficient);
 //   * a wave scans its 64 lane aggregates with DPP row_shr 1,2,4,8 and
 //     row_bcast 15/31 (six dependent steps, no LDS);
-//   * the NW wave totals meet in LDS behind one barrier;
+//   * the NW wave totals meet in LDS behind one barrier (skipped when rows
+//     end at wave boundaries);
 //   * a tile carry passes between successive tiles of the workgroup's rows, so
 //     a row of any length streams through registers and LDS never grows with T.
 // Lanes are numbered in *scan order*: for backward scans the lane order is
@@ -73,21 +74,27 @@ __device__ __forceinline__ void wave_inclusive_scan(V &a, V &b) {
     dpp_compose<0x143, 0xc>(a, b);  // row_bcast:31 into rows 2 and 3
 }
 
-// Value held by lane - 1 (lane 0 receives `first`): one ds_bpermute.
+// Value held by lane - 1 (lane 0 receives `first`): one DPP wave_shr:1 move,
+// whose lane 0 has no source and keeps the `old` operand.
 template <typename V>
 __device__ __forceinline__ V from_lower_lane(V x, V first) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int src = (lane == 0 ? 0 : lane - 1) << 2;
-    const V y = from_bits<V>(__builtin_amdgcn_ds_bpermute(src, as_bits(x)));
-    return lane == 0 ? first : y;
+    return from_bits<V>(
+        __builtin_amdgcn_update_dpp(as_bits(first), as_bits(x), 0x138, 0xf, 0xf, false));
 }
 
 // Workgroup-wide scan of per-lane maps (a, b) given in scan order, with an
 // incoming carry for the whole tile.  Returns the value of A just before this
 // lane's chunk in scan order (= after the preceding lanes), and writes the
-// value after the whole tile to `carry_out`.  `lds_a` / `lds_b` hold 2*NW
-// slots; `parity` alternates between tiles so one barrier per tile suffices.
-template <int NW, typename V>
+// value after the whole tile to `carry_out`.  The NW wave totals meet in LDS
+// behind one barrier; `lds_a` / `lds_b` hold 2*NW slots and `parity`
+// alternates between tiles so one barrier per tile suffices.
+//
+// WAVE_LOCAL: every wave's segment starts, in scan order, with a chain cut
+// (rows end at wave boundaries), so whatever enters a wave from outside is
+// multiplied by an exact zero before it reaches any output.  The LDS exchange
+// and the barrier are then skipped and 0 enters each wave instead; the
+// results are the same values the exchange would give.
+template <int NW, bool WAVE_LOCAL, typename V>
 __device__ __forceinline__ V block_carry_in(V a, V b, V carry_in, V *lds_a, V *lds_b, int parity,
                                             V &carry_out) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -95,6 +102,10 @@ __device__ __forceinline__ V block_carry_in(V a, V b, V carry_in, V *lds_a, V *l
     wave_inclusive_scan(a, b);
     const V ea = from_lower_lane(a, V(0));
     const V eb = from_lower_lane(b, V(1));
+    if constexpr (WAVE_LOCAL) {
+        carry_out = V(0);
+        return ea + eb * V(0);
+    }
     if (lane == kWave - 1) {
         lds_a[parity * NW + w] = a;
         lds_b[parity * NW + w] = b;

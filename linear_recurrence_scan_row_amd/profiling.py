@@ -16,21 +16,25 @@ credit-assignment kernels.
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import os
 import sqlite3
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-KERNEL_SOURCES = ("linear_recurrence_scan_row_amd/csrc/rlca.hip",
-                  "linear_recurrence_scan_row_amd/csrc/scan_core.hpp", "include/rlca.h")
+
+
+def _kernel_sources():
+    csrc = sorted(glob.glob(os.path.join(ROOT, "linear_recurrence_scan_row_amd", "csrc", "*")))
+    return [os.path.relpath(p, ROOT) for p in csrc] + ["include/rlca.h"]
 
 
 def source_digest() -> str:
     """Digest of the kernel sources; stored with a counter summary so that a
     summary taken on other code is not reported for this code."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in _kernel_sources():
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
