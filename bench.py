@@ -111,7 +111,7 @@ def make_sets(torch, arrays, calls, device, min_call_bytes):
     many as needed for >= COLD_BYTES of traffic between reuses of a set."""
     master = {k: torch.from_numpy(np.ascontiguousarray(v)).to(device) for k, v in arrays.items()}
     shape = next(v.shape for v in arrays.values() if v.ndim == 2)
-    nsets = max(2, -(-COLD_BYTES // max(1, min_call_bytes)) + 1)
+    nsets = min(4096, max(2, -(-COLD_BYTES // max(1, min_call_bytes)) + 1))
     per_set = sum(v.numel() * v.element_size() for v in master.values()) + \
         sum(4 * int(np.prod(shape)) for _ in range(3))
     nsets = int(min(nsets, max(2, (24 << 30) // per_set)))
@@ -331,6 +331,96 @@ def measured_traffic(kernel_name, workload):
         return None
 
 
+# ------------------------------------------------------------------ size sweep
+
+SWEEP_ENVS = (1024, 4096, 16384, 65536)
+SWEEP_T = (128, 512, 2048)
+
+
+def run_sweep(args):
+    """Effective GB/s of GAE with truncation (22 B/step), Retrace with
+    truncation (30 B/step) and eligibility traces (9 B/step) over a grid of
+    shapes; one JSON line per point.  Rollouts are drawn on the device with a
+    seeded torch generator (values: N(0,1) and U(0,1); flags: Bernoulli 0.01
+    and 0.005); only throughput is measured here."""
+    import torch
+    from linear_recurrence_scan_row_amd import rlca
+
+    lib = rlca.lib()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream()
+    gen = torch.Generator(device=dev)
+    for n in SWEEP_ENVS:
+        for t in SWEEP_T:
+            nt = n * t
+            shape = (n, t)
+            specs = [
+                ("gae+trunc", 22, ("r", "v", "term", "trunc", "tv", "b"), ("o0", "o1")),
+                ("retrace+trunc", 30,
+                 ("r", "v", "eq", "mu", "pi", "term", "trunc", "tv", "b"), ("o0",)),
+                ("eligibility", 9, ("x", "start"), ("o0",)),
+            ]
+            for name, bps, ins, outs in specs:
+                call_bytes = nt * bps + (4 * n if "b" in ins else 0)
+                per_set = nt * (4 * sum(1 for k in ins if k not in ("term", "trunc", "start"))
+                                + sum(1 for k in ins if k in ("term", "trunc", "start"))
+                                + 4 * len(outs))
+                nsets = int(min(max(2, -(-COLD_BYTES // call_bytes) + 1),
+                                max(2, (48 << 30) // per_set)))
+                gen.manual_seed(n * 131 + t)
+                sets = []
+                for _ in range(nsets):
+                    s = {}
+                    for k in ins:
+                        if k in ("term", "trunc", "start"):
+                            p = 0.005 if k == "trunc" else 0.01
+                            s[k] = (torch.rand(shape, generator=gen, device=dev) < p).to(torch.uint8)
+                        elif k == "b":
+                            s[k] = torch.randn(n, generator=gen, device=dev)
+                        elif k == "x":
+                            s[k] = torch.rand(shape, generator=gen, device=dev)
+                        else:
+                            s[k] = torch.randn(shape, generator=gen, device=dev)
+                    for k in outs:
+                        s[k] = torch.empty(shape, device=dev)
+                    sets.append(s)
+                torch.cuda.synchronize()
+                h = stream.cuda_stream
+
+                def launch(s):
+                    if name == "gae+trunc":
+                        return lib.rlca_gae(s["r"].data_ptr(), s["v"].data_ptr(),
+                                            s["term"].data_ptr(), s["trunc"].data_ptr(),
+                                            s["tv"].data_ptr(), s["b"].data_ptr(), 0.99, 0.95, n,
+                                            t, s["o0"].data_ptr(), s["o1"].data_ptr(), h)
+                    if name == "retrace+trunc":
+                        return lib.rlca_retrace(*[s[k].data_ptr() for k in ins], 0.99, 0.95, 1.0,
+                                                n, t, s["o0"].data_ptr(), h)
+                    return lib.rlca_eligibility_traces(s["x"].data_ptr(), s["start"].data_ptr(),
+                                                       0, 0.99, 0.9, n, t, s["o0"].data_ptr(), h)
+
+                with torch.cuda.stream(stream):
+                    for i in range(3):
+                        assert launch(sets[i % nsets]) == 0
+                    batch = max(20, min(400, int(2e9 // call_bytes)))
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    for i in range(batch):
+                        assert launch(sets[i % nsets]) == 0
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) / batch * 1e3
+                gbs = call_bytes / (us * 1e-6) / 1e9
+                print(json.dumps({"sweep": name, "num_envs": n, "T": t, "us": round(us, 3),
+                                  "bytes": call_bytes, "gbs": round(gbs, 1),
+                                  "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+                                  "env_steps_per_s": nt / (us * 1e-6), "sets": nsets}),
+                      flush=True)
+                del sets
+                torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------------ main
 
 
@@ -344,6 +434,8 @@ def main():
     ap.add_argument("--launch", choices=("graph", "eager"), default="eager")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="print one JSON line per (num_envs, T, estimator) of the size sweep")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -356,6 +448,9 @@ def main():
         sys.exit(2)
 
     sys.path.insert(0, ROOT)
+    if args.sweep:
+        run_sweep(args)
+        return
     from linear_recurrence_scan_row_amd import workloads
 
     cfg = dict(workloads.CONFIGS[args.workload])
