@@ -85,8 +85,9 @@ typedef enum {
     RLCA_ERR_HIP = 6
 } rlca_status;
 
-/* Forward-scan reset conventions (summary §3.3: "configurable boundary
- * conventions"; §5: the forward scans cut the carry where d_{t-1} = 1). */
+/* Forward-scan reset conventions.  The summary's §3.3 leaves the boundary
+ * convention of the segmented forward scans configurable; its §5 cuts the
+ * forward carry at the step after a done step. */
 typedef enum {
     RLCA_RESET_ON_START = 0,  /* flags[t] != 0: step t starts a new episode      */
     RLCA_RESET_AFTER_DONE = 1 /* flags[t-1] != 0: step t-1 ended the episode      */

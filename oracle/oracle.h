@@ -30,7 +30,8 @@
 extern "C" {
 #endif
 
-/* Forward-scan reset conventions (§3.3 "configurable boundary conventions"). */
+/* Forward-scan reset conventions (§3.3 leaves the boundary convention of the
+ * segmented forward scans configurable). */
 #define ORACLE_RESET_ON_START 0   /* flag[t] = 1: step t starts a new episode      */
 #define ORACLE_RESET_AFTER_DONE 1 /* flag[t-1] = 1: step t-1 ended an episode (§5) */
 
