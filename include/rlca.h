@@ -10,7 +10,10 @@
  * ("rl-triton: High-Performance Triton GPU Kernels for Reinforcement Learning
  * Credit Assignment", paperlayer.ai summary, §1 Introduction and §3.1 Shared
  * scan formulation).  Each call is one kernel launch that reads its inputs
- * from HBM once and writes each output once.
+ * from HBM once and writes each output once -- except for fewer than 64
+ * rows of more than 4096 steps, where each row is split into chunks that run
+ * in parallel: three launches, inputs read twice, and the first output array
+ * holds the chunk hand-off values until the last launch overwrites them.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -49,7 +52,7 @@
  *            RLCA_ERR_ALIASING       an output overlaps an input or another
  *                                    output (in-place is not supported)
  *            RLCA_ERR_MISALIGNED     an fp32 / int32 pointer is not 4-byte aligned
- *            RLCA_ERR_HIP            the launch failed (hipGetLastError)
+ *            RLCA_ERR_HIP            a kernel launch failed (its hipError_t)
  *          num_envs * T == 0 is a valid no-op.  Faults inside the kernel
  *          surface at the caller's next synchronisation, as usual in HIP.
  *          Non-finite inputs propagate; they are not trapped.
@@ -94,6 +97,8 @@ typedef enum {
 } rlca_reset_convention;
 
 typedef enum { RLCA_F32 = 0, RLCA_I32 = 1 } rlca_dtype;
+
+typedef enum { RLCA_BACKWARD = 0, RLCA_FORWARD = 1 } rlca_direction;
 
 /* Generalized advantage estimation (Schulman et al. 2016; summary §2.1).
  *   delta_t = r_t + gamma * V(s_{t+1}) - V(s_t),   V(s_{t+1}) per the boundary rules
@@ -171,6 +176,18 @@ rlca_status rlca_eligibility_traces(const float *increments, const uint8_t *flag
 rlca_status rlca_episodic_prefix_sum(const void *x, rlca_dtype dtype, const uint8_t *flags,
                                      rlca_reset_convention convention, int64_t num_envs,
                                      int64_t T, void *out, hipStream_t stream);
+
+/* Generic first-order affine scan over caller-built coefficients (the
+ * summary's §4 Scan procedure: the generic kernel that takes precomputed
+ * alpha and beta instead of building them from a rollout).
+ *   RLCA_BACKWARD: A_t = alpha_t + beta_t * A_{t+1},  A_T = carry[n]
+ *   RLCA_FORWARD:  A_t = alpha_t + beta_t * A_{t-1},  A_{-1} = carry[n]
+ * alpha, beta, out [N,T] f32; carry [N] f32, nullable (=> 0).  Episode
+ * boundaries are the caller's business (beta_t = 0 cuts the chain).  Writes
+ * out [N,T]. */
+rlca_status rlca_affine_scan(const float *alpha, const float *beta, const float *carry,
+                             rlca_direction direction, int64_t num_envs, int64_t T, float *out,
+                             hipStream_t stream);
 
 /* Static description of a status code (never NULL). */
 const char *rlca_status_string(rlca_status status);

@@ -4,10 +4,12 @@
 namespace rlca {
 rlca_status launch_forward_f32(ForwardParams &p, bool after_done, const LaunchShape &s,
                                hipStream_t stream) {
-    return launch_forward<float>(p, after_done, s, stream);
+    return after_done ? launch_forward_variant<float, kForwardFlags, true>(p, s, stream)
+                      : launch_forward_variant<float, kForwardFlags, false>(p, s, stream);
 }
 rlca_status launch_forward_u32(ForwardParams &p, bool after_done, const LaunchShape &s,
                                hipStream_t stream) {
-    return launch_forward<uint32_t>(p, after_done, s, stream);
+    return after_done ? launch_forward_variant<uint32_t, kForwardFlags, true>(p, s, stream)
+                      : launch_forward_variant<uint32_t, kForwardFlags, false>(p, s, stream);
 }
 }  // namespace rlca

@@ -1,8 +1,8 @@
 // kernels.hpp -- the fused credit-assignment kernels for MI355X (gfx950).
 //
-// Each workgroup owns a contiguous range of whole rows of the [num_envs, T]
-// rollout (rows are independent; "rl-triton", paperlayer.ai summary, §4
-// Kernel design) and walks it in tiles of NW*64*K steps:
+// Each workgroup owns a window of the [num_envs, T] rollout (rows are
+// independent; "rl-triton", paperlayer.ai summary, §4 Kernel design) and walks
+// it in tiles of NW*64*K steps:
 //   1. coalesced loads of the raw rollout, each element read once (dwordx4 per
 //      lane for fp32 streams, one dword per four flag bytes);
 //   2. boundary resolution and the estimator's (alpha_t, beta_t) built in
@@ -10,10 +10,18 @@
 //   3. the shared affine scan of scan_core.hpp (lane fold, wave64 DPP scan,
 //      LDS wave totals, tile carry);
 //   4. one store of each output.
-// Short rows are packed many to a tile: the window edge is folded into
-// alpha_{T-1} with beta_{T-1} = 0, so a row end is a chain cut like any done
-// step and rows never interact.  Long rows take several tiles with the carry
-// kept in registers, so there is no length limit and no LDS growth with T.
+// Full mode: a window is a range of whole rows.  Short rows are packed many
+// to a tile: the window edge is folded into alpha_{T-1} with beta_{T-1} = 0,
+// so a row end is a chain cut like any done step and rows never interact.
+// Long rows take several tiles with the carry kept in registers, so there is
+// no length limit and no LDS growth with T.
+// Chunk modes (few long rows): a window is one tile-sized chunk of one row,
+// so every chunk of every row runs in parallel.  Three launches: each chunk
+// folds its steps into one affine map (aggregate mode), a small kernel scans
+// the chunk maps of each row into per-chunk carries, and each chunk runs
+// again from its carry (apply mode).  Both hand-offs go through the first
+// word(s) of the chunk's own slice of the first output array, which the
+// apply pass overwrites last; no other memory is used.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -34,34 +42,55 @@ namespace rlca {
 constexpr int kK = RLCA_STEPS_PER_LANE;
 static_assert(kK == 1 || kK == 2 || kK == 4, "steps per lane: 1, 2 or 4");
 
-enum Estimator : int { kGae = 0, kTdLambda = 1, kDiscounted = 2, kVtrace = 3, kRetrace = 4 };
+// Waves per workgroup in the chunk modes; the chunk is one tile.
+constexpr int kChunkWaves = 8;
+constexpr uint32_t kChunkSteps = kChunkWaves * kWave * kK;
+
+enum Estimator : int {
+    kGae = 0,
+    kTdLambda = 1,
+    kDiscounted = 2,
+    kVtrace = 3,
+    kRetrace = 4,
+    kAffineBackward = 5,  // caller-supplied (alpha, beta), backward in time
+};
+
+enum ForwardKind : int {
+    kForwardFlags = 0,   // alpha = x, beta = decay except at episode starts
+    kForwardAffine = 1,  // caller-supplied (alpha, beta), forward in time
+};
+
+enum Mode : int { kFull = 0, kChunkAggregate = 1, kChunkApply = 2 };
 
 struct Geometry {
     int64_t num_envs;
     uint32_t T;
-    uint32_t rows_per_group;  // whole rows owned by one workgroup iteration
+    uint32_t rows_per_group;  // full mode: whole rows owned by one workgroup iteration
     uint32_t num_groups;
+    uint32_t chunks_per_row;  // chunk modes: chunks of kChunkSteps per row
 };
 
 struct BackwardParams {
-    const float *rewards;
-    const float *values;  // V(s_t); Q(s_t, a_t) for Retrace
+    const float *rewards;  // alpha for kAffineBackward
+    const float *values;   // V(s_t); Q(s_t, a_t) for Retrace; beta for kAffineBackward
     const float *expected_q;
     const float *behaviour_logp;
     const float *target_logp;
     const uint8_t *terminated;
     const uint8_t *truncated;
     const float *trunc_values;
-    const float *bootstrap;
-    float *out0;  // advantages / returns / vs / q_ret
-    float *out1;  // GAE returns or V-Trace pg advantages; may be null
+    const float *bootstrap;  // carry A_T for kAffineBackward
+    float *out0;             // advantages / returns / vs / q_ret / A
+    float *out1;             // GAE returns or V-Trace pg advantages; may be null
     float gamma, lambda, rho_bar, c_bar;
     Geometry geo;
 };
 
 struct ForwardParams {
-    const void *x;
-    const uint8_t *flags;
+    const void *x;         // alpha for kForwardAffine
+    const uint8_t *flags;  // kForwardFlags
+    const float *beta;     // kForwardAffine
+    const float *carry;    // kForwardAffine: A_{-1} per row, may be null
     void *out;
     float decay;  // gamma*lambda for traces, 1 for prefix sums
     Geometry geo;
@@ -71,7 +100,8 @@ struct ForwardParams {
 struct LaunchShape {
     int waves;        // NW: 1, 2, 4 or 8 waves per workgroup
     bool wave_local;  // rows end at wave boundaries (T divides 64*K)
-    bool vec;         // dwordx4 path: T % 4 == 0 and 16-byte aligned arrays
+    bool vec;         // K-wide vector path: T % K == 0 and aligned arrays
+    bool chunked;     // few long rows: the three chunk-mode launches
 };
 
 // ---------------------------------------------------------------- memory access
@@ -164,18 +194,79 @@ __device__ __forceinline__ void store_steps(E *__restrict__ p, const E (&x)[kK],
     }
 }
 
-// Row-local step index t and row offset of each of the lane's K steps.
-__device__ __forceinline__ void step_positions(uint32_t off, uint32_t T, uint32_t (&t)[kK],
-                                               uint32_t (&row)[kK]) {
-    uint32_t r = off / T;
-    uint32_t s = off - r * T;
+// The steps one workgroup iteration covers.
+struct Window {
+    int64_t row0;       // first row
+    int64_t base;       // flat index of the window's first step
+    uint32_t L;         // steps in the window
+    uint32_t t0;        // row-local index of the first step (0 in full mode)
+    uint32_t row_rest;  // steps from the window start to the end of its row
+    uint32_t chunk;     // chunk index in scan order (chunk modes)
+};
+
+// Chunk j of a row in scan order: backward scans count chunks from the row
+// end, so only the earliest chunk can be short; forward scans from the start.
+__host__ __device__ inline void chunk_bounds(uint32_t T, uint32_t j, bool backward, uint32_t &lo,
+                                             uint32_t &hi) {
+    if (backward) {
+        hi = T - j * kChunkSteps;
+        lo = hi > kChunkSteps ? hi - kChunkSteps : 0u;
+    } else {
+        lo = j * kChunkSteps;
+        hi = T - lo > kChunkSteps ? lo + kChunkSteps : T;
+    }
+}
+
+template <int MODE, bool BACKWARD>
+__device__ __forceinline__ Window window_of(const Geometry &geo, uint32_t g) {
+    Window w;
+    if constexpr (MODE == kFull) {
+        w.row0 = (int64_t)g * geo.rows_per_group;
+        const int64_t rows_left = geo.num_envs - w.row0;
+        const uint32_t rows =
+            rows_left < (int64_t)geo.rows_per_group ? (uint32_t)rows_left : geo.rows_per_group;
+        w.L = rows * geo.T;
+        w.base = w.row0 * (int64_t)geo.T;
+        w.t0 = 0;
+        w.row_rest = w.L;
+        w.chunk = 0;
+    } else {
+        const uint32_t n = g / geo.chunks_per_row;
+        const uint32_t j = g - n * geo.chunks_per_row;
+        uint32_t lo, hi;
+        chunk_bounds(geo.T, j, BACKWARD, lo, hi);
+        w.row0 = n;
+        w.base = (int64_t)n * geo.T + lo;
+        w.L = hi - lo;
+        w.t0 = lo;
+        w.row_rest = geo.T - lo;
+        w.chunk = j;
+    }
+    return w;
+}
+
+// Row-local step index t and row offset (relative to row0) of each of the
+// lane's K steps.
+template <int MODE>
+__device__ __forceinline__ void step_positions(const Window &w, uint32_t off, uint32_t T,
+                                               uint32_t (&t)[kK], uint32_t (&row)[kK]) {
+    if constexpr (MODE == kFull) {
+        uint32_t r = off / T;
+        uint32_t s = off - r * T;
 #pragma unroll
-    for (int i = 0; i < kK; ++i) {
-        t[i] = s;
-        row[i] = r;
-        if (++s == T) {
-            s = 0;
-            ++r;
+        for (int i = 0; i < kK; ++i) {
+            t[i] = s;
+            row[i] = r;
+            if (++s == T) {
+                s = 0;
+                ++r;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kK; ++i) {
+            t[i] = w.t0 + off + i;
+            row[i] = 0;
         }
     }
 }
@@ -184,17 +275,6 @@ __device__ __forceinline__ float importance_ratio(float target_logp, float behav
     const float l = fminf(fmaxf(target_logp - behaviour_logp, -RLCA_LOG_RATIO_CLIP),
                           RLCA_LOG_RATIO_CLIP);
     return expf(l);
-}
-
-// Rows [row0, row0 + rows) of group g and the flat offset of their first step.
-__device__ __forceinline__ void group_rows(const Geometry &geo, uint32_t g, int64_t &row0,
-                                           uint32_t &L, int64_t &base) {
-    row0 = (int64_t)g * geo.rows_per_group;
-    const int64_t rows_left = geo.num_envs - row0;
-    const uint32_t rows =
-        rows_left < (int64_t)geo.rows_per_group ? (uint32_t)rows_left : geo.rows_per_group;
-    L = rows * geo.T;
-    base = row0 * (int64_t)geo.T;
 }
 
 // ------------------------------------------------------- leading kernel arguments
@@ -209,8 +289,8 @@ __device__ __forceinline__ void group_rows(const Geometry &geo, uint32_t g, int6
 #define LEAD_NAMES lead0, lead1, lead2, lead3, lead4, lead_T, lead_rows_per_group, lead_num_envs
 
 struct Lead {
-    uint32_t T, rows_per_group, num_envs;
     const void *ptr[5];
+    uint32_t T, rows_per_group, num_envs;
 };
 
 // Host side: the estimator's five leading arrays, in argument order.
@@ -225,14 +305,21 @@ inline void lead_from(const BackwardParams &p, Lead &l) {
     } else if constexpr (EST == kVtrace) {
         l.ptr[0] = p.rewards, l.ptr[1] = p.values, l.ptr[2] = p.behaviour_logp;
         l.ptr[3] = p.target_logp, l.ptr[4] = p.terminated;
-    } else {
+    } else if constexpr (EST == kRetrace) {
         l.ptr[0] = p.rewards, l.ptr[1] = p.values, l.ptr[2] = p.expected_q;
         l.ptr[3] = p.behaviour_logp, l.ptr[4] = p.target_logp;
+    } else {
+        l.ptr[0] = p.rewards, l.ptr[1] = p.values, l.ptr[2] = p.bootstrap;
+        l.ptr[3] = p.out0, l.ptr[4] = nullptr;
     }
 }
 
-// Device side: the same five arrays and the geometry, taken from the
-// preloaded arguments.
+inline void lead_from(const ForwardParams &p, Lead &l) {
+    l.ptr[0] = p.x, l.ptr[1] = p.flags, l.ptr[2] = p.out, l.ptr[3] = p.beta, l.ptr[4] = p.carry;
+}
+
+// Device side: the same arrays and the geometry, taken from the preloaded
+// arguments.
 template <int EST>
 __device__ __forceinline__ void adopt_lead(BackwardParams &p, LEAD_ARGS) {
     typedef const float *F;
@@ -246,9 +333,13 @@ __device__ __forceinline__ void adopt_lead(BackwardParams &p, LEAD_ARGS) {
     } else if constexpr (EST == kVtrace) {
         p.rewards = F(lead0), p.values = F(lead1), p.behaviour_logp = F(lead2);
         p.target_logp = F(lead3), p.terminated = U(lead4);
-    } else {
+    } else if constexpr (EST == kRetrace) {
         p.rewards = F(lead0), p.values = F(lead1), p.expected_q = F(lead2);
         p.behaviour_logp = F(lead3), p.target_logp = F(lead4);
+    } else {
+        p.rewards = F(lead0), p.values = F(lead1), p.bootstrap = F(lead2);
+        p.out0 = const_cast<float *>(F(lead3));
+        (void)lead4;
     }
     p.geo.T = lead_T;
     p.geo.rows_per_group = lead_rows_per_group;
@@ -259,20 +350,22 @@ __device__ __forceinline__ void adopt_lead(ForwardParams &p, LEAD_ARGS) {
     p.x = lead0;
     p.flags = static_cast<const uint8_t *>(lead1);
     p.out = const_cast<void *>(lead2);
+    p.beta = static_cast<const float *>(lead3);
+    p.carry = static_cast<const float *>(lead4);
     p.geo.T = lead_T;
     p.geo.rows_per_group = lead_rows_per_group;
     p.geo.num_envs = lead_num_envs;
-    (void)lead3;
-    (void)lead4;
 }
 
 // ------------------------------------------------------------- backward kernel
 // A_t = alpha_t + beta_t * A_{t+1}.  Lanes take chunks in reverse time order, so
 // the lane-order scan of scan_core.hpp runs from the end of the tile backwards.
-template <int EST, bool TRUNC, bool VEC, int NW, bool WAVE_LOCAL>
+template <int EST, bool TRUNC, bool VEC, int NW, bool WAVE_LOCAL, int MODE>
 __global__ __launch_bounds__(NW * kWave) void backward_scan(LEAD_ARGS, BackwardParams p) {
+    static_assert(MODE == kFull || (NW == kChunkWaves && !WAVE_LOCAL), "a chunk is one tile");
     adopt_lead<EST>(p, LEAD_NAMES);
     constexpr uint32_t kTile = NW * kWave * kK;
+    constexpr bool kFlags = EST != kAffineBackward;
     __shared__ float lds_a[2 * NW], lds_b[2 * NW];
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x / kWave;
@@ -286,11 +379,17 @@ __global__ __launch_bounds__(NW * kWave) void backward_scan(LEAD_ARGS, BackwardP
     // out together instead of after a first round trip for the bound.
     uint32_t g = blockIdx.x;
     do {
-        int64_t row0, base;
-        uint32_t L;
-        group_rows(p.geo, g, row0, L, base);
-        const uint32_t ntiles = (L + kTile - 1) / kTile;
-        float carry = 0.f;  // A just after the current tile (A_T = 0: edges live in alpha)
+        const Window win = window_of<MODE, true>(p.geo, g);
+        const int64_t row0 = win.row0, base = win.base;
+        const uint32_t L = win.L;
+        const uint32_t ntiles = MODE == kFull ? (L + kTile - 1) / kTile : 1u;
+        // A just after the current tile: 0 at a row end (edges live in alpha),
+        // or the carry the chunk-carry pass left in the chunk's first slot.
+        float carry = 0.f;
+        if constexpr (MODE == kChunkApply) {
+            carry = p.out0[base];
+            __syncthreads();  // every lane has read the slot before any store
+        }
 
         for (uint32_t it = 0; it < ntiles; ++it) {
             const uint32_t off = (ntiles - 1 - it) * kTile + chunk * kK;
@@ -305,17 +404,19 @@ __global__ __launch_bounds__(NW * kWave) void backward_scan(LEAD_ARGS, BackwardP
                 load_steps<VEC>(mu, p.behaviour_logp + base, off, L);
                 load_steps<VEC>(pi, p.target_logp + base, off, L);
             }
-            load_flags<VEC>(term, p.terminated + base, off, L);
+            if constexpr (kFlags) load_flags<VEC>(term, p.terminated + base, off, L);
             if constexpr (TRUNC) {
                 load_flags<VEC>(trunc, p.truncated + base, off, L);
                 load_steps<VEC>(tv, p.trunc_values + base, off, L);
             }
             // Loads whose addresses depend only on positions go out with the
-            // main batch: the bootstrap of rows ending in this chunk, and for
-            // lane 0 the first step of the next chunk in time (its neighbour
-            // lane - 1 sits in another wave or tile).
+            // main batch: the bootstrap (carry) of rows ending in this chunk,
+            // and the first step of the next chunk in time wherever lane - 1
+            // does not hold it: lane 0 (its neighbour sits in another wave or
+            // tile) and the lane whose chunk ends the window while its row
+            // goes on (a partial chunk in the chunk modes).
             uint32_t t[kK], row[kK];
-            step_positions(off, T, t, row);
+            step_positions<MODE>(win, off, T, t, row);
             bool valid[kK];
             float boot[kK];
 #pragma unroll
@@ -326,7 +427,8 @@ __global__ __launch_bounds__(NW * kWave) void backward_scan(LEAD_ARGS, BackwardP
                     boot[i] = p.bootstrap[row0 + row[i]];
             }
             float v_first = 0.f, mu_first = 0.f, pi_first = 0.f, eq_first = 0.f;
-            if (lane == 0 && off + kK < L) {
+            const bool halo_from_memory = (lane == 0 || off + kK >= L) && off + kK < win.row_rest;
+            if (halo_from_memory) {
                 const int64_t jh = base + off + kK;
                 if constexpr (EST == kGae || EST == kTdLambda || EST == kVtrace)
                     v_first = p.values[jh];
@@ -342,20 +444,27 @@ __global__ __launch_bounds__(NW * kWave) void backward_scan(LEAD_ARGS, BackwardP
             float succ[kK];  // successor value where the chain stops
 #pragma unroll
             for (int i = 0; i < kK; ++i) {
-                const bool tr = TRUNC && trunc[i] && !term[i];
                 const bool edge = t[i] == T - 1;
-                cont[i] = valid[i] && !term[i] && !tr && !edge;
-                float sv = term[i] ? 0.f : boot[i];
-                if constexpr (TRUNC) {
-                    if (tr) sv = tv[i];
+                if constexpr (kFlags) {
+                    const bool tr = TRUNC && trunc[i] && !term[i];
+                    cont[i] = valid[i] && !term[i] && !tr && !edge;
+                    float sv = term[i] ? 0.f : boot[i];
+                    if constexpr (TRUNC) {
+                        if (tr) sv = tv[i];
+                    }
+                    succ[i] = sv;
+                } else {
+                    cont[i] = valid[i] && !edge;
+                    succ[i] = boot[i];
                 }
-                succ[i] = sv;
             }
 
             // ---- 3. halo: the first step of the next chunk in time, from lane - 1
             float v_next = 0.f, c_next = 0.f, eq_next = 0.f;
-            if constexpr (EST == kGae || EST == kTdLambda || EST == kVtrace)
+            if constexpr (EST == kGae || EST == kTdLambda || EST == kVtrace) {
                 v_next = from_lower_lane(v[0], v_first);
+                if (halo_from_memory) v_next = v_first;
+            }
             float c[kK];
             if constexpr (EST == kVtrace || EST == kRetrace) {
 #pragma unroll
@@ -367,6 +476,10 @@ __global__ __launch_bounds__(NW * kWave) void backward_scan(LEAD_ARGS, BackwardP
                     p.lambda * fminf(p.c_bar, importance_ratio(pi_first, mu_first));
                 c_next = from_lower_lane(c[0], c_first);
                 eq_next = from_lower_lane(eq[0], eq_first);
+                if (halo_from_memory) {
+                    c_next = c_first;
+                    eq_next = eq_first;
+                }
             }
 
             // ---- 4. coefficients in registers
@@ -392,11 +505,15 @@ __global__ __launch_bounds__(NW * kWave) void backward_scan(LEAD_ARGS, BackwardP
                     a = rho * (r[i] + gamma * (k ? vn : succ[i]) - v[i]);
                     b = k ? gamma * c[i] : 0.f;
                     x = k ? gamma * rho : 0.f;  // pg_t = alpha_t + gamma rho_t A_{t+1}
-                } else {  // Retrace: the decay uses the next step's trace coefficient
+                } else if constexpr (EST == kRetrace) {
+                    // the decay uses the next step's trace coefficient
                     const float cn = i + 1 < kK ? c[i + 1] : c_next;
                     const float en = i + 1 < kK ? eq[i + 1] : eq_next;
                     a = r[i] + gamma * (k ? en : succ[i]) - v[i];
                     b = k ? gamma * cn : 0.f;
+                } else {  // caller's (alpha, beta); the row's carry enters at t = T-1
+                    a = k ? r[i] : r[i] + v[i] * succ[i];
+                    b = k ? v[i] : 0.f;
                 }
                 alpha[i] = valid[i] ? a : 0.f;
                 beta[i] = valid[i] ? b : 1.f;
@@ -410,35 +527,46 @@ __global__ __launch_bounds__(NW * kWave) void backward_scan(LEAD_ARGS, BackwardP
                 fa = alpha[i] + beta[i] * fa;
                 fb = beta[i] * fb;
             }
-            float carry_out;
-            float A = block_carry_in<NW, WAVE_LOCAL>(fa, fb, carry, lds_a, lds_b, parity,
-                                                      carry_out);
-            parity ^= 1;
-            carry = carry_out;
-
-            // ---- 6. outputs, one store each
-            float o0[kK], o1[kK];
-#pragma unroll
-            for (int i = kK - 1; i >= 0; --i) {
-                const float An = A;  // A_{t+1}
-                A = alpha[i] + beta[i] * An;
-                if constexpr (EST == kGae) {
-                    o0[i] = A;
-                    o1[i] = A + v[i];
-                } else if constexpr (EST == kVtrace) {
-                    o0[i] = v[i] + A;
-                    o1[i] = alpha[i] + aux[i] * An;
-                } else if constexpr (EST == kRetrace) {
-                    o0[i] = v[i] + A;
-                    o1[i] = 0.f;
-                } else {
-                    o0[i] = A;
-                    o1[i] = 0.f;
+            if constexpr (MODE == kChunkAggregate) {
+                // hand the chunk's map to the chunk-carry pass (the earliest
+                // chunk of a row, last in scan order, has no consumer)
+                float ta, tb;
+                block_total<NW>(fa, fb, lds_a, lds_b, ta, tb);
+                if (threadIdx.x == 0 && win.chunk + 1 < p.geo.chunks_per_row) {
+                    p.out0[base] = ta;
+                    p.out0[base + 1] = tb;
                 }
-            }
-            store_steps<VEC>(p.out0 + base, o0, off, L);
-            if constexpr (EST == kGae || EST == kVtrace) {
-                if (p.out1 != nullptr) store_steps<VEC>(p.out1 + base, o1, off, L);
+            } else {
+                float carry_out;
+                float A = block_carry_in<NW, WAVE_LOCAL>(fa, fb, carry, lds_a, lds_b, parity,
+                                                          carry_out);
+                parity ^= 1;
+                carry = carry_out;
+
+                // ---- 6. outputs, one store each
+                float o0[kK], o1[kK];
+#pragma unroll
+                for (int i = kK - 1; i >= 0; --i) {
+                    const float An = A;  // A_{t+1}
+                    A = alpha[i] + beta[i] * An;
+                    if constexpr (EST == kGae) {
+                        o0[i] = A;
+                        o1[i] = A + v[i];
+                    } else if constexpr (EST == kVtrace) {
+                        o0[i] = v[i] + A;
+                        o1[i] = alpha[i] + aux[i] * An;
+                    } else if constexpr (EST == kRetrace) {
+                        o0[i] = v[i] + A;
+                        o1[i] = 0.f;
+                    } else {
+                        o0[i] = A;
+                        o1[i] = 0.f;
+                    }
+                }
+                store_steps<VEC>(p.out0 + base, o0, off, L);
+                if constexpr (EST == kGae || EST == kVtrace) {
+                    if (p.out1 != nullptr) store_steps<VEC>(p.out1 + base, o1, off, L);
+                }
             }
         }
         g += gridDim.x;
@@ -446,11 +574,14 @@ __global__ __launch_bounds__(NW * kWave) void backward_scan(LEAD_ARGS, BackwardP
 }
 
 // -------------------------------------------------------------- forward kernel
-// A_t = alpha_t + beta_t * A_{t-1} with alpha = x, beta = decay, beta = 0 where a
-// new episode starts (summary §5: the forward scans cut where d_{t-1} = 1).
-// V = float (traces, f32 sums) or uint32_t (int32 sums, wrap-around).
-template <typename V, bool AFTER_DONE, bool VEC, int NW, bool WAVE_LOCAL>
+// A_t = alpha_t + beta_t * A_{t-1}.  kForwardFlags: alpha = x, beta = decay and
+// beta = 0 where a new episode starts (summary §5: the forward scans cut where
+// d_{t-1} = 1); V = float (traces, f32 sums) or uint32_t (int32 sums,
+// wrap-around).  kForwardAffine: the caller's (alpha, beta), with the row's
+// carry entering at t = 0.
+template <typename V, int KIND, bool AFTER_DONE, bool VEC, int NW, bool WAVE_LOCAL, int MODE>
 __global__ __launch_bounds__(NW * kWave) void forward_scan(LEAD_ARGS, ForwardParams p) {
+    static_assert(MODE == kFull || (NW == kChunkWaves && !WAVE_LOCAL), "a chunk is one tile");
     adopt_lead(p, LEAD_NAMES);
     constexpr uint32_t kTile = NW * kWave * kK;
     __shared__ V lds_a[2 * NW], lds_b[2 * NW];
@@ -463,44 +594,65 @@ __global__ __launch_bounds__(NW * kWave) void forward_scan(LEAD_ARGS, ForwardPar
     V *__restrict__ out = static_cast<V *>(p.out);
     int parity = 0;
 
-    // The grid never exceeds the group count, so the first group always
-    // exists; testing only at the bottom lets every kernel-argument load go
-    // out together instead of after a first round trip for the bound.
-    uint32_t g = blockIdx.x;
+    uint32_t g = blockIdx.x;  // first group always exists (see backward_scan)
     do {
-        int64_t row0, base;
-        uint32_t L;
-        group_rows(p.geo, g, row0, L, base);
-        const uint32_t ntiles = (L + kTile - 1) / kTile;
+        const Window win = window_of<MODE, false>(p.geo, g);
+        const int64_t row0 = win.row0, base = win.base;
+        const uint32_t L = win.L;
+        const uint32_t ntiles = MODE == kFull ? (L + kTile - 1) / kTile : 1u;
         V carry = V(0);
+        if constexpr (MODE == kChunkApply) {
+            carry = out[base];
+            __syncthreads();  // every lane has read the slot before any store
+        }
 
         for (uint32_t it = 0; it < ntiles; ++it) {
             const uint32_t off = it * kTile + chunk * kK;
             V x[kK];
+            float bt[kK];
             bool f[kK];
             load_steps<VEC>(x, xs + base, off, L);
-            load_flags<VEC>(f, p.flags + base, off, L);
-            bool first = false;  // flag of the step before the lane's chunk (lane 0)
-            if constexpr (AFTER_DONE) {
-                if (lane == 0 && off > 0 && off - 1 < L) first = p.flags[base + off - 1] != 0;
-            }
+            if constexpr (KIND == kForwardFlags) load_flags<VEC>(f, p.flags + base, off, L);
+            if constexpr (KIND == kForwardAffine) load_steps<VEC>(bt, p.beta + base, off, L);
             uint32_t t[kK], row[kK];
-            step_positions(off, T, t, row);
+            step_positions<MODE>(win, off, T, t, row);
+            bool first = false;  // flag of the step before the lane's chunk (lane 0)
+            if constexpr (KIND == kForwardFlags && AFTER_DONE) {
+                if (lane == 0 && win.t0 + off > 0 && off <= L) first = p.flags[base + off - 1] != 0;
+            }
+            float row_carry[kK];
+#pragma unroll
+            for (int i = 0; i < kK; ++i) {
+                row_carry[i] = 0.f;
+                if constexpr (KIND == kForwardAffine) {
+                    if (off + i < L && t[i] == 0 && p.carry != nullptr)
+                        row_carry[i] = p.carry[row0 + row[i]];
+                }
+            }
             bool prev_done = false;
-            if constexpr (AFTER_DONE)
+            if constexpr (KIND == kForwardFlags && AFTER_DONE)
                 prev_done = from_lower_lane<uint32_t>(f[kK - 1] ? 1u : 0u, first ? 1u : 0u) != 0;
             V alpha[kK], beta[kK];
 #pragma unroll
             for (int i = 0; i < kK; ++i) {
                 const bool valid = off + i < L;
-                bool reset = t[i] == 0;
-                if constexpr (AFTER_DONE) {
-                    reset = reset || (i == 0 ? prev_done : f[i - 1]);
+                V a, b;
+                if constexpr (KIND == kForwardFlags) {
+                    bool reset = t[i] == 0;
+                    if constexpr (AFTER_DONE) {
+                        reset = reset || (i == 0 ? prev_done : f[i - 1]);
+                    } else {
+                        reset = reset || f[i];
+                    }
+                    a = x[i];
+                    b = reset ? V(0) : decay;
                 } else {
-                    reset = reset || f[i];
+                    const bool start = t[i] == 0;
+                    a = start ? x[i] + bt[i] * row_carry[i] : x[i];
+                    b = start ? V(0) : bt[i];
                 }
-                alpha[i] = valid ? x[i] : V(0);
-                beta[i] = valid ? (reset ? V(0) : decay) : V(1);
+                alpha[i] = valid ? a : V(0);
+                beta[i] = valid ? b : V(1);
             }
             V fa = V(0), fb = V(1);
 #pragma unroll
@@ -508,45 +660,100 @@ __global__ __launch_bounds__(NW * kWave) void forward_scan(LEAD_ARGS, ForwardPar
                 fa = alpha[i] + beta[i] * fa;
                 fb = beta[i] * fb;
             }
-            V carry_out;
-            V A = block_carry_in<NW, WAVE_LOCAL>(fa, fb, carry, lds_a, lds_b, parity, carry_out);
-            parity ^= 1;
-            carry = carry_out;
-            V o[kK];
+            if constexpr (MODE == kChunkAggregate) {
+                V ta, tb;
+                block_total<NW>(fa, fb, lds_a, lds_b, ta, tb);
+                if (threadIdx.x == 0 && win.chunk + 1 < p.geo.chunks_per_row) {
+                    out[base] = ta;
+                    out[base + 1] = tb;
+                }
+            } else {
+                V carry_out;
+                V A = block_carry_in<NW, WAVE_LOCAL>(fa, fb, carry, lds_a, lds_b, parity,
+                                                      carry_out);
+                parity ^= 1;
+                carry = carry_out;
+                V o[kK];
 #pragma unroll
-            for (int i = 0; i < kK; ++i) {
-                A = alpha[i] + beta[i] * A;
-                o[i] = A;
+                for (int i = 0; i < kK; ++i) {
+                    A = alpha[i] + beta[i] * A;
+                    o[i] = A;
+                }
+                store_steps<VEC>(out + base, o, off, L);
             }
-            store_steps<VEC>(out + base, o, off, L);
-            (void)row;
         }
         g += gridDim.x;
     } while (g < p.geo.num_groups);
 }
 
+// ------------------------------------------------------------ chunk carries
+// Chunk modes, middle pass: one workgroup per row scans the row's chunk maps
+// (left by the aggregate pass in the first two words of each chunk's slice of
+// `slots`) in scan order and leaves in each chunk's first word the value of
+// A entering that chunk.  Lane j of a tile holds chunk j; the last chunk in
+// scan order has no map (identity) but receives its carry.
+template <typename V, int NW>
+__global__ __launch_bounds__(NW * kWave) void chunk_carries(V *slots, int64_t num_envs, uint32_t T,
+                                                            uint32_t chunks_per_row, int backward) {
+    __shared__ V lds_a[2 * NW], lds_b[2 * NW];
+    constexpr uint32_t kLanes = NW * kWave;
+    int parity = 0;
+    int64_t n = blockIdx.x;  // the grid never exceeds num_envs
+    do {
+        V *row = slots + n * (int64_t)T;
+        V carry = V(0);
+        for (uint32_t j0 = 0; j0 < chunks_per_row; j0 += kLanes) {
+            const uint32_t j = j0 + threadIdx.x;
+            uint32_t lo = 0, hi = 0;
+            if (j < chunks_per_row) chunk_bounds(T, j, backward != 0, lo, hi);
+            V a = V(0), b = V(1);
+            if (j + 1 < chunks_per_row) {
+                a = row[lo];
+                b = row[lo + 1];
+            }
+            V carry_out;
+            const V in = block_carry_in<NW, false>(a, b, carry, lds_a, lds_b, parity, carry_out);
+            parity ^= 1;
+            carry = carry_out;
+            if (j < chunks_per_row) row[lo] = in;
+        }
+        n += gridDim.x;
+    } while (n < num_envs);
+}
+
 // ------------------------------------------------------------------ launching
 
-// Upper bound on the launch grid; larger problems loop over row groups.
+// Upper bound on the launch grid; larger problems loop over groups.
 constexpr uint32_t kMaxGrid = 1u << 20;
 
-inline Geometry make_geometry(int64_t num_envs, int64_t T, int waves, uint32_t *grid) {
+inline uint32_t grid_for(int64_t groups) {
+    return groups < (int64_t)kMaxGrid ? (uint32_t)groups : kMaxGrid;
+}
+
+inline Geometry make_geometry(int64_t num_envs, int64_t T, int waves, bool chunked,
+                              uint32_t *grid) {
     const uint32_t tile = (uint32_t)waves * kWave * kK;
     Geometry g;
     g.num_envs = num_envs;
     g.T = (uint32_t)T;
-    g.rows_per_group = (uint32_t)T <= tile ? tile / (uint32_t)T : 1u;
-    const int64_t groups = (num_envs + g.rows_per_group - 1) / g.rows_per_group;
+    int64_t groups;
+    if (chunked) {
+        g.rows_per_group = 1;
+        g.chunks_per_row = (uint32_t)((T + kChunkSteps - 1) / kChunkSteps);
+        groups = num_envs * g.chunks_per_row;
+    } else {
+        g.rows_per_group = (uint32_t)T <= tile ? tile / (uint32_t)T : 1u;
+        g.chunks_per_row = 1;
+        groups = (num_envs + g.rows_per_group - 1) / g.rows_per_group;
+    }
     g.num_groups = (uint32_t)groups;
-    *grid = groups < (int64_t)kMaxGrid ? (uint32_t)groups : kMaxGrid;
+    *grid = grid_for(groups);
     return g;
 }
 
 template <typename P>
-inline rlca_status launch_kernel(const void *kernel, int waves, P &params, Lead &lead,
-                                 hipStream_t stream) {
-    uint32_t grid;
-    params.geo = make_geometry(params.geo.num_envs, params.geo.T, waves, &grid);
+inline rlca_status launch_kernel(const void *kernel, int waves, uint32_t grid, P &params,
+                                 Lead &lead, hipStream_t stream) {
     lead.T = params.geo.T;
     lead.rows_per_group = params.geo.rows_per_group;
     lead.num_envs = (uint32_t)params.geo.num_envs;
@@ -558,14 +765,47 @@ inline rlca_status launch_kernel(const void *kernel, int waves, P &params, Lead 
     return e == hipSuccess ? RLCA_OK : RLCA_ERR_HIP;
 }
 
+template <typename V>
+inline rlca_status launch_chunk_carries(V *slots, const Geometry &geo, bool backward,
+                                        hipStream_t stream) {
+    int64_t n = geo.num_envs;
+    uint32_t T = geo.T, m = geo.chunks_per_row;
+    int dir = backward ? 1 : 0;
+    void *args[] = {&slots, &n, &T, &m, &dir};
+    const hipError_t e =
+        hipLaunchKernel((const void *)chunk_carries<V, kChunkWaves>, dim3(grid_for(n)),
+                        dim3(kChunkWaves * kWave), args, 0, stream);
+    return e == hipSuccess ? RLCA_OK : RLCA_ERR_HIP;
+}
+
+// The three chunk-mode launches, all on one stream: aggregate, carries, apply.
+template <typename P, typename V>
+inline rlca_status launch_chunked(const void *aggregate, const void *apply, P &params, Lead &lead,
+                                  V *slots, bool backward, hipStream_t stream) {
+    uint32_t grid;
+    params.geo = make_geometry(params.geo.num_envs, params.geo.T, kChunkWaves, true, &grid);
+    rlca_status st = launch_kernel(aggregate, kChunkWaves, grid, params, lead, stream);
+    if (st == RLCA_OK) st = launch_chunk_carries(slots, params.geo, backward, stream);
+    if (st == RLCA_OK) st = launch_kernel(apply, kChunkWaves, grid, params, lead, stream);
+    return st;
+}
+
+template <typename P>
+inline rlca_status launch_full(const void *kernel, int waves, P &params, Lead &lead,
+                               hipStream_t stream) {
+    uint32_t grid;
+    params.geo = make_geometry(params.geo.num_envs, params.geo.T, waves, false, &grid);
+    return launch_kernel(kernel, waves, grid, params, lead, stream);
+}
+
 // The vector path instantiates every wave count and the wave-local variant;
-// the scalar (unaligned or T % 4 != 0) path is one general configuration.
+// the scalar (unaligned or T % K != 0) path is one general configuration.
 template <int EST, bool TRUNC>
 const void *backward_kernel(const LaunchShape &s) {
-    if (!s.vec) return (const void *)backward_scan<EST, TRUNC, false, 4, false>;
-#define RLCA_PICK(NW)                                                             \
-    return s.wave_local ? (const void *)backward_scan<EST, TRUNC, true, NW, true> \
-                        : (const void *)backward_scan<EST, TRUNC, true, NW, false>
+    if (!s.vec) return (const void *)backward_scan<EST, TRUNC, false, 4, false, kFull>;
+#define RLCA_PICK(NW)                                                                     \
+    return s.wave_local ? (const void *)backward_scan<EST, TRUNC, true, NW, true, kFull> \
+                        : (const void *)backward_scan<EST, TRUNC, true, NW, false, kFull>
     switch (s.waves) {
         case 1: RLCA_PICK(1);
         case 2: RLCA_PICK(2);
@@ -573,23 +813,32 @@ const void *backward_kernel(const LaunchShape &s) {
         default: RLCA_PICK(4);
     }
 #undef RLCA_PICK
+}
+
+template <int EST, bool TRUNC>
+rlca_status launch_backward_variant(BackwardParams &p, const LaunchShape &s, hipStream_t stream) {
+    Lead lead;
+    lead_from<EST>(p, lead);
+    if (s.chunked)
+        return launch_chunked(
+            (const void *)backward_scan<EST, TRUNC, true, kChunkWaves, false, kChunkAggregate>,
+            (const void *)backward_scan<EST, TRUNC, true, kChunkWaves, false, kChunkApply>, p,
+            lead, p.out0, true, stream);
+    return launch_full(backward_kernel<EST, TRUNC>(s), s.vec ? s.waves : 4, p, lead, stream);
 }
 
 template <int EST>
 rlca_status launch_backward(BackwardParams &p, const LaunchShape &s, hipStream_t stream) {
-    const void *k = p.truncated != nullptr ? backward_kernel<EST, true>(s)
-                                           : backward_kernel<EST, false>(s);
-    Lead lead;
-    lead_from<EST>(p, lead);
-    return launch_kernel(k, s.vec ? s.waves : 4, p, lead, stream);
+    return p.truncated != nullptr ? launch_backward_variant<EST, true>(p, s, stream)
+                                  : launch_backward_variant<EST, false>(p, s, stream);
 }
 
-template <typename V, bool AFTER_DONE>
+template <typename V, int KIND, bool AFTER_DONE>
 const void *forward_kernel(const LaunchShape &s) {
-    if (!s.vec) return (const void *)forward_scan<V, AFTER_DONE, false, 4, false>;
-#define RLCA_PICK(NW)                                                              \
-    return s.wave_local ? (const void *)forward_scan<V, AFTER_DONE, true, NW, true> \
-                        : (const void *)forward_scan<V, AFTER_DONE, true, NW, false>
+    if (!s.vec) return (const void *)forward_scan<V, KIND, AFTER_DONE, false, 4, false, kFull>;
+#define RLCA_PICK(NW)                                                                         \
+    return s.wave_local ? (const void *)forward_scan<V, KIND, AFTER_DONE, true, NW, true, kFull> \
+                        : (const void *)forward_scan<V, KIND, AFTER_DONE, true, NW, false, kFull>
     switch (s.waves) {
         case 1: RLCA_PICK(1);
         case 2: RLCA_PICK(2);
@@ -599,12 +848,18 @@ const void *forward_kernel(const LaunchShape &s) {
 #undef RLCA_PICK
 }
 
-template <typename V>
-rlca_status launch_forward(ForwardParams &p, bool after_done, const LaunchShape &s,
-                           hipStream_t stream) {
-    const void *k = after_done ? forward_kernel<V, true>(s) : forward_kernel<V, false>(s);
-    Lead lead = {0, 0, 0, {p.x, p.flags, p.out, nullptr, nullptr}};
-    return launch_kernel(k, s.vec ? s.waves : 4, p, lead, stream);
+template <typename V, int KIND, bool AFTER_DONE>
+rlca_status launch_forward_variant(ForwardParams &p, const LaunchShape &s, hipStream_t stream) {
+    Lead lead;
+    lead_from(p, lead);
+    if (s.chunked)
+        return launch_chunked(
+            (const void *)forward_scan<V, KIND, AFTER_DONE, true, kChunkWaves, false,
+                                       kChunkAggregate>,
+            (const void *)forward_scan<V, KIND, AFTER_DONE, true, kChunkWaves, false, kChunkApply>,
+            p, lead, static_cast<V *>(p.out), false, stream);
+    return launch_full(forward_kernel<V, KIND, AFTER_DONE>(s), s.vec ? s.waves : 4, p, lead,
+                       stream);
 }
 
 // One translation unit per estimator instantiates these (see est_*.hip).
@@ -613,9 +868,11 @@ rlca_status launch_td_lambda(BackwardParams &p, const LaunchShape &s, hipStream_
 rlca_status launch_discounted(BackwardParams &p, const LaunchShape &s, hipStream_t stream);
 rlca_status launch_vtrace(BackwardParams &p, const LaunchShape &s, hipStream_t stream);
 rlca_status launch_retrace(BackwardParams &p, const LaunchShape &s, hipStream_t stream);
+rlca_status launch_affine_backward(BackwardParams &p, const LaunchShape &s, hipStream_t stream);
 rlca_status launch_forward_f32(ForwardParams &p, bool after_done, const LaunchShape &s,
                                hipStream_t stream);
 rlca_status launch_forward_u32(ForwardParams &p, bool after_done, const LaunchShape &s,
                                hipStream_t stream);
+rlca_status launch_affine_forward(ForwardParams &p, const LaunchShape &s, hipStream_t stream);
 
 }  // namespace rlca

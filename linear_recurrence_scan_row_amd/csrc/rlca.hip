@@ -2,8 +2,9 @@
 //
 // The kernels live in kernels.hpp and are instantiated one estimator per
 // translation unit (est_*.hip).  Every entry point validates its arguments
-// before anything is enqueued, picks a launch shape from (T, alignment) and
-// makes exactly one asynchronous kernel launch on the caller's stream.
+// before anything is enqueued, picks a launch shape from (num_envs, T,
+// alignment) and enqueues its kernel launch(es) on the caller's stream: one
+// launch, or three for a few long rows (the chunk modes).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -70,14 +71,24 @@ static bool vec_ok(int64_t T, const void *const *f32, int nf, const void *const 
 // chosen by measurement on MI355X with cold HBM-resident operands: such short
 // rows run fastest in 8-wave workgroups; rows of 257..1023 steps with one
 // wave walking the row tile by tile; longer rows with 8 waves sharing each
-// tile through LDS.
-static LaunchShape choose_shape(int64_t T, bool vec) {
+// tile through LDS.  Fewer than 64 long rows cannot fill the chip one
+// workgroup per row, so they are split into chunks that run in parallel
+// (three launches, inputs read twice): 50x faster for one row of 1M steps,
+// even at 64 rows, slower from 128 rows on (one workgroup per row then
+// sustains 3.4-5 TB/s).
+static constexpr int64_t kChunkedMaxRows = 64;
+
+static LaunchShape choose_shape(int64_t num_envs, int64_t T, bool vec) {
     LaunchShape s;
     s.vec = vec;
     s.wave_local = vec && T <= kWave * kK && (kWave * kK) % T == 0;
     s.waves = (T <= kWave * kK || T >= 1024) ? 8 : 1;
+    s.chunked = vec && T > 2 * (int64_t)kChunkSteps && num_envs < kChunkedMaxRows;
 #ifdef RLCA_FORCE_WAVES
     s.waves = RLCA_FORCE_WAVES;
+#endif
+#ifdef RLCA_FORCE_CHUNKED
+    s.chunked = vec && T > 2 * (int64_t)kChunkSteps && RLCA_FORCE_CHUNKED;
 #endif
     return s;
 }
@@ -86,14 +97,15 @@ static rlca_status run_backward(int est, BackwardParams &p, int64_t T, hipStream
     const void *f32[] = {p.rewards, p.values, p.expected_q, p.behaviour_logp, p.target_logp,
                          p.trunc_values, p.out0, p.out1};
     const void *u8[] = {p.terminated, p.truncated};
-    const LaunchShape s = choose_shape(T, vec_ok(T, f32, 8, u8, 2));
+    const LaunchShape s = choose_shape(p.geo.num_envs, T, vec_ok(T, f32, 8, u8, 2));
     p.geo.T = (uint32_t)T;
     switch (est) {
         case kGae: return launch_gae(p, s, stream);
         case kTdLambda: return launch_td_lambda(p, s, stream);
         case kDiscounted: return launch_discounted(p, s, stream);
         case kVtrace: return launch_vtrace(p, s, stream);
-        default: return launch_retrace(p, s, stream);
+        case kRetrace: return launch_retrace(p, s, stream);
+        default: return launch_affine_backward(p, s, stream);
     }
 }
 
@@ -301,7 +313,7 @@ static rlca_status run_forward(const void *x, bool is_int, const uint8_t *flags,
     if (st != RLCA_OK) return st;
     const void *f32[] = {x, out};
     const void *u8[] = {flags};
-    const LaunchShape s = choose_shape(T, vec_ok(T, f32, 2, u8, 1));
+    const LaunchShape s = choose_shape(num_envs, T, vec_ok(T, f32, 2, u8, 1));
     ForwardParams p = {};
     p.x = x;
     p.flags = flags;
@@ -328,6 +340,41 @@ rlca_status rlca_episodic_prefix_sum(const void *x, rlca_dtype dtype, const uint
                                      int64_t T, void *out, hipStream_t stream) {
     if (dtype != RLCA_F32 && dtype != RLCA_I32) return RLCA_ERR_INVALID_VALUE;
     return run_forward(x, dtype == RLCA_I32, flags, convention, 1.0f, num_envs, T, out, stream);
+}
+
+rlca_status rlca_affine_scan(const float *alpha, const float *beta, const float *carry,
+                             rlca_direction direction, int64_t num_envs, int64_t T, float *out,
+                             hipStream_t stream) {
+    if (direction != RLCA_BACKWARD && direction != RLCA_FORWARD) return RLCA_ERR_INVALID_VALUE;
+    int64_t n;
+    rlca_status st = check_sizes(num_envs, T, &n);
+    if (st != RLCA_OK || n == 0) return st;
+    if (alpha == nullptr || beta == nullptr || out == nullptr) return RLCA_ERR_NULL_POINTER;
+    const void *al[] = {alpha, beta, carry, out};
+    st = check_aligned4(al, 4);
+    if (st != RLCA_OK) return st;
+    const Span ins[] = {{alpha, (size_t)n * 4}, {beta, (size_t)n * 4}, {carry, (size_t)num_envs * 4}};
+    const Span os[] = {{out, (size_t)n * 4}};
+    st = check_aliasing(os, 1, ins, 3);
+    if (st != RLCA_OK) return st;
+    if (direction == RLCA_BACKWARD) {
+        BackwardParams p = backward_params(num_envs);
+        p.rewards = alpha;
+        p.values = beta;
+        p.bootstrap = carry;
+        p.out0 = out;
+        return run_backward(kAffineBackward, p, T, stream);
+    }
+    const void *f32[] = {alpha, beta, out};
+    const LaunchShape s = choose_shape(num_envs, T, vec_ok(T, f32, 3, nullptr, 0));
+    ForwardParams p = {};
+    p.x = alpha;
+    p.beta = beta;
+    p.carry = carry;
+    p.out = out;
+    p.geo.num_envs = num_envs;
+    p.geo.T = (uint32_t)T;
+    return launch_affine_forward(p, s, stream);
 }
 
 const char *rlca_status_string(rlca_status status) {

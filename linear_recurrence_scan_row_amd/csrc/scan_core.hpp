@@ -122,4 +122,25 @@ __device__ __forceinline__ V block_carry_in(V a, V b, V carry_in, V *lds_a, V *l
     return ea + eb * xw;
 }
 
+// The map of the whole tile: the NW wave totals composed in scan order.  Used
+// where a tile's result is handed to another workgroup instead of applied.
+template <int NW, typename V>
+__device__ __forceinline__ void block_total(V a, V b, V *lds_a, V *lds_b, V &ta, V &tb) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x / kWave;
+    wave_inclusive_scan(a, b);
+    if (lane == kWave - 1) {
+        lds_a[w] = a;
+        lds_b[w] = b;
+    }
+    __syncthreads();
+    ta = V(0);
+    tb = V(1);
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+        ta = lds_a[j] + lds_b[j] * ta;
+        tb = lds_b[j] * tb;
+    }
+}
+
 }  // namespace rlca

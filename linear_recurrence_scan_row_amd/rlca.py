@@ -26,6 +26,8 @@ RESET_ON_START = 0
 RESET_AFTER_DONE = 1
 RLCA_F32 = 0
 RLCA_I32 = 1
+BACKWARD = 0
+FORWARD = 1
 
 _p = ctypes.c_void_p
 _f = ctypes.c_float
@@ -41,6 +43,7 @@ SIGNATURES = {
     "rlca_retrace": [_p, _p, _p, _p, _p, _p, _p, _p, _p, _f, _f, _f, _i64, _i64, _p, _p],
     "rlca_eligibility_traces": [_p, _p, _i, _f, _f, _i64, _i64, _p, _p],
     "rlca_episodic_prefix_sum": [_p, _i, _p, _i, _i64, _i64, _p, _p],
+    "rlca_affine_scan": [_p, _p, _p, _i, _i64, _i64, _p, _p],
 }
 
 _lib = None
@@ -234,4 +237,17 @@ def episodic_prefix_sum(x, flags, convention=RESET_ON_START, out=None):
     _check(lib().rlca_episodic_prefix_sum(_ptr(xs), dtype, _ptr(f), int(convention), shape[0],
                                           shape[1], _ptr(o), _stream(xs)),
            "rlca_episodic_prefix_sum")
+    return o
+
+
+def affine_scan(alpha, beta, carry=None, direction=BACKWARD, out=None):
+    """A_t = alpha_t + beta_t * A_{t+1} (BACKWARD, A_T = carry) or
+    A_t = alpha_t + beta_t * A_{t-1} (FORWARD, A_{-1} = carry), float32."""
+    shape, dev = _rollout_shape(alpha)
+    a = _steps("alpha", alpha, shape, torch.float32, dev)
+    b = _steps("beta", beta, shape, torch.float32, dev)
+    c = _steps("carry", carry, shape[:1], torch.float32, dev, optional=True)
+    o = _out(out, shape, dev)
+    _check(lib().rlca_affine_scan(_ptr(a), _ptr(b), _ptr(c), int(direction), shape[0], shape[1],
+                                  _ptr(o), _stream(a)), "rlca_affine_scan")
     return o

@@ -11,6 +11,7 @@ Reinforcement Learning Credit Assignment" (paperlayer.ai summary), §1, §2.1,
 §3.2, §3.3, §5 and §8; the header of ``oracle.c`` states the boundary rules.
 
 Pins (tests/test_oracle_pins.py): brute-force unrolled sums on tiny inputs,
+products-of-coefficients sums for the generic affine scan,
 closed forms, the cross-estimator identities (GAE lambda=0 / lambda=1,
 V-Trace on-policy, Retrace lambda=0), no-leak invariance at done steps and the
 worked four-thread trace of the summary's Appendix A.  Every function here is
@@ -27,6 +28,8 @@ from .build import LIB_PATH, build
 
 RESET_ON_START = 0
 RESET_AFTER_DONE = 1
+BACKWARD = 0
+FORWARD = 1
 
 _lib = None
 
@@ -59,6 +62,7 @@ def _load():
                                           _f64p],
             "oracle_episodic_prefix_sum_f32": [_f32p, _u8p, ctypes.c_int, _i64, _i64, _f64p],
             "oracle_episodic_prefix_sum_i32": [_i32p, _u8p, ctypes.c_int, _i64, _i64, _i32p],
+            "oracle_affine_scan": [_f32p, _f32p, _f32p, ctypes.c_int, _i64, _i64, _f64p],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -218,4 +222,17 @@ def episodic_prefix_sum(x, flags, convention=RESET_ON_START):
     out = np.empty(shape, np.float64)
     _load().oracle_episodic_prefix_sum_f32(xfp, fp, int(convention), n, t,
                                            out.ctypes.data_as(_f64p))
+    return out
+
+
+def affine_scan(alpha, beta, carry=None, direction=BACKWARD):
+    """A_t = alpha_t + beta_t * A_{t+1} (BACKWARD, A_T = carry) or
+    A_t = alpha_t + beta_t * A_{t-1} (FORWARD, A_{-1} = carry), float64."""
+    shape = _shape(alpha)
+    n, t = shape
+    a, ap = _arr(alpha, np.float32, shape)
+    b, bp = _arr(beta, np.float32, shape)
+    c, cp = _arr(carry, np.float32, (n,))
+    out = np.empty(shape, np.float64)
+    _load().oracle_affine_scan(ap, bp, cp, int(direction), n, t, out.ctypes.data_as(_f64p))
     return out

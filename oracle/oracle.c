@@ -289,3 +289,24 @@ void oracle_episodic_prefix_sum_i32(const int32_t *x, const uint8_t *flags, int 
         }
     }
 }
+
+/* The recurrence itself, one step at a time from the carried end. */
+void oracle_affine_scan(const float *alpha, const float *beta, const float *carry, int direction,
+                        int64_t num_envs, int64_t T, double *out)
+{
+    for (int64_t n = 0; n < num_envs; ++n) {
+        const float *a = alpha + n * T, *b = beta + n * T;
+        double A = carry != NULL ? (double)carry[n] : 0.0;
+        if (direction == 0) {
+            for (int64_t t = T - 1; t >= 0; --t) {
+                A = (double)a[t] + (double)b[t] * A;
+                out[n * T + t] = A;
+            }
+        } else {
+            for (int64_t t = 0; t < T; ++t) {
+                A = (double)a[t] + (double)b[t] * A;
+                out[n * T + t] = A;
+            }
+        }
+    }
+}

@@ -74,6 +74,14 @@ void oracle_episodic_prefix_sum_f32(const float *x, const uint8_t *flags, int co
 void oracle_episodic_prefix_sum_i32(const int32_t *x, const uint8_t *flags, int convention,
                                     int64_t num_envs, int64_t T, int32_t *out);
 
+/* First-order affine recurrence over caller-built coefficients (summary §4,
+ * the generic kernel on precomputed alpha and beta):
+ *   backward (direction 0): A_t = alpha_t + beta_t * A_{t+1},  A_T = carry[n]
+ *   forward  (direction 1): A_t = alpha_t + beta_t * A_{t-1},  A_{-1} = carry[n]
+ * carry may be NULL (zero). */
+void oracle_affine_scan(const float *alpha, const float *beta, const float *carry, int direction,
+                        int64_t num_envs, int64_t T, double *out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -183,3 +183,22 @@ def prefix_sum(x, flags, convention):
     if is_int:
         return out.astype(np.uint64).astype(np.uint32).view(np.int32)
     return out
+
+
+def affine(alpha, beta, carry, direction):
+    """Unrolled: backward A_t = sum_{j>=t} (prod_{i=t}^{j-1} beta_i) alpha_j
+    + (prod_{i=t}^{T-1} beta_i) carry; forward mirrored."""
+    N, T = alpha.shape
+    out = np.zeros((N, T))
+    for n in range(N):
+        c = 0.0 if carry is None else _f(carry[n])
+        for t in range(T):
+            js = range(t, T) if direction == 0 else range(t, -1, -1)
+            s = 0.0
+            for j in js:
+                span = range(t, j) if direction == 0 else range(j + 1, t + 1)
+                s += math.prod(_f(beta[n, i]) for i in span) * _f(alpha[n, j])
+            whole = range(t, T) if direction == 0 else range(0, t + 1)
+            s += math.prod(_f(beta[n, i]) for i in whole) * c
+            out[n, t] = s
+    return out

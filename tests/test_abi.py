@@ -94,6 +94,7 @@ def test_value_errors(lib):
                             None) == VALUE
     assert lib.rlca_eligibility_traces(A, B, 7, 0.9, 0.9, 4, 8, C, None) == VALUE
     assert lib.rlca_episodic_prefix_sum(A, 5, B, 0, 4, 8, C, None) == VALUE
+    assert lib.rlca_affine_scan(A, B, None, 2, 4, 8, C, None) == VALUE
 
 
 def test_null_pointer_errors(lib):
@@ -107,6 +108,8 @@ def test_null_pointer_errors(lib):
                             None) == NULLP
     assert lib.rlca_eligibility_traces(A, None, 0, 0.9, 0.9, 4, 8, C, None) == NULLP
     assert lib.rlca_episodic_prefix_sum(A, 1, B, 0, 4, 8, None, None) == NULLP
+    assert lib.rlca_affine_scan(A, None, None, 0, 4, 8, C, None) == NULLP
+    assert lib.rlca_affine_scan(A, B, None, 1, 4, 8, None, None) == NULLP
 
 
 def test_alignment_errors(lib):
@@ -125,3 +128,6 @@ def test_aliasing_errors(lib):
     assert gae(lib, adv=D, ret=D + 4) == ALIAS              # outputs overlap each other
     assert gae(lib, adv=C) == ALIAS                         # over the flags
     assert lib.rlca_episodic_prefix_sum(A, 0, B, 0, n, t, A + 4, None) == ALIAS
+    assert lib.rlca_affine_scan(A, B, C, 0, n, t, C - 8, None) == ALIAS     # over the carry
+    assert lib.rlca_affine_scan(A, B, None, 1, n, t, B + 4, None) == ALIAS
+    assert lib.rlca_affine_scan(A + 2, B, None, 1, n, t, C, None) == MISAL

@@ -420,3 +420,63 @@ def test_window_split_carry_invariant():
                                      tail[:, 0].astype(np.float32), g)
     close(tail, full[:, k:], 1e-15)
     close(head, full[:, :k], 1e-6)   # bootstrap passes through float32
+
+
+# ------------------------------------------------------------ generic affine scan
+
+
+@pytest.mark.parametrize("direction", [oracle.BACKWARD, oracle.FORWARD])
+def test_affine_scan_vs_brute_force(direction):
+    rng = np.random.default_rng(60 + direction)
+    N, T = 16, 9
+    alpha = rng.standard_normal((N, T)).astype(np.float32)
+    beta = rng.uniform(-1.2, 1.2, (N, T)).astype(np.float32)
+    beta[rng.random((N, T)) < 0.15] = 0.0
+    carry = rng.standard_normal(N).astype(np.float32)
+    close(oracle.affine_scan(alpha, beta, carry, direction),
+          brute.affine(alpha, beta, carry, direction))
+    close(oracle.affine_scan(alpha, beta, None, direction),
+          brute.affine(alpha, beta, None, direction))
+
+
+def test_affine_scan_special_cases():
+    rng = np.random.default_rng(62)
+    a = rng.standard_normal((4, 30)).astype(np.float32)
+    zero = np.zeros_like(a)
+    one = np.ones_like(a)
+    c = rng.standard_normal(4).astype(np.float32)
+    # beta = 0: A = alpha, the carry never enters
+    close(oracle.affine_scan(a, zero, c, oracle.BACKWARD), a, 0)
+    # beta = 1: suffix / prefix sums plus the carry
+    a64 = a.astype(np.float64)
+    close(oracle.affine_scan(a, one, c, oracle.BACKWARD),
+          np.cumsum(a64[:, ::-1], axis=1)[:, ::-1] + c[:, None], 1e-13)
+    close(oracle.affine_scan(a, one, None, oracle.FORWARD), np.cumsum(a64, axis=1), 1e-13)
+
+
+def test_affine_scan_reproduces_the_estimators():
+    """The generic scan fed with hand-built GAE coefficients gives the GAE
+    oracle's advantages; forward with (x, gamma*lambda*(1 - start)) gives the
+    traces.  Ties the two oracle paths together."""
+    d = rand_inputs(64, 8, 40)
+    term, trunc = _random_flags(65, 8, 40)
+    g, lam = 0.97, 0.9
+    T = 40
+    r, v, tv, b = (d[k].astype(np.float64) for k in ("r", "v", "tv", "b"))
+    cont = (term == 0) & (trunc == 0)
+    cont[:, -1] = False
+    nv = np.where(term != 0, 0.0, np.where(trunc != 0, tv, 0.0))
+    nv[:, -1] = np.where((term[:, -1] == 0) & (trunc[:, -1] == 0), b, nv[:, -1])
+    vnext = np.concatenate([v[:, 1:], np.zeros((8, 1))], axis=1)
+    alpha = r + g * np.where(cont, vnext, nv) - v
+    beta = np.where(cont, g * lam, 0.0)
+    adv, _ = oracle.gae(d["r"], d["v"], term, trunc, d["tv"], d["b"], g, lam)
+    # coefficients rounded to float32 on the way in
+    close(oracle.affine_scan(alpha.astype(np.float32), beta.astype(np.float32), None,
+                             oracle.BACKWARD), adv, 1e-5)
+    starts = (np.random.default_rng(66).random((8, T)) < 0.1).astype(np.uint8)
+    x = d["x"]
+    bf = np.where(starts != 0, 0.0, g * lam).astype(np.float32)
+    bf[:, 0] = 0.0
+    close(oracle.affine_scan(x, bf, None, oracle.FORWARD),
+          oracle.eligibility_traces(x, starts, 0, g, lam), 1e-6)

@@ -368,3 +368,72 @@ def test_repeat_calls_are_deterministic(gpu_device):
     a1, _ = rl.gae(*args)
     a2, _ = rl.gae(*args)
     assert torch.equal(a1, a2)
+
+
+# ------------------------------------------------- few long rows: chunked path
+# Fewer than 64 rows of more than 4096 steps (T % 4 == 0, aligned arrays) are
+# split into 2048-step chunks that run in parallel: aggregate, chunk carries,
+# apply.  Shapes cover an exact multiple of the chunk, a short last chunk in
+# scan order, and single rows.
+
+LONG_SHAPES = [(3, 4100), (2, 6144), (5, 10000), (1, 65536), (4, 20480), (63, 4104),
+               (64, 4104)]
+
+
+@pytest.mark.parametrize("N,T", LONG_SHAPES)
+def test_chunked_backward_estimators(N, T, gpu_device):
+    d = rollout(300 + N + T, N, T, p_term=0.002, p_trunc=0.001)
+    what = f"chunked N={N} T={T}"
+    for trunc in (True, False):
+        check_gae(d, gpu_device, trunc=trunc, what=what)
+        check_td(d, gpu_device, trunc=trunc, what=what)
+        check_disc(d, gpu_device, trunc=trunc, what=what)
+        check_vtrace(d, gpu_device, trunc=trunc, lam=0.95, rho_bar=1.2, c_bar=0.9, what=what)
+        check_retrace(d, gpu_device, trunc=trunc, what=what)
+
+
+@pytest.mark.parametrize("N,T", LONG_SHAPES)
+def test_chunked_forward_scans(N, T, gpu_device):
+    f = workloads.forward_rollout(400 + N + T, N, T, p_start=0.002)
+    for conv in (rl.RESET_ON_START, rl.RESET_AFTER_DONE):
+        check_forward(f, gpu_device, conv, what=f"chunked N={N} T={T} conv={conv}")
+
+
+def test_chunked_no_leak_is_bit_exact(gpu_device):
+    N, T = 4, 10000
+    d = rollout(17, N, T, p_term=0.0, p_trunc=0.0)
+    d.terminated[:, 6000] = 1
+    outs = []
+    for shift in (0.0, 1.5):
+        r = d.rewards.copy()
+        v = d.values.copy()
+        r[:, 6001:] += shift
+        v[:, 6001:] += shift
+        adv, _ = rl.gae(dev(r, gpu_device), dev(v, gpu_device), dev(d.terminated, gpu_device),
+                        bootstrap=dev(d.bootstrap + shift, gpu_device))
+        outs.append(adv)
+    assert torch.equal(outs[0][:, :6001], outs[1][:, :6001])
+
+
+# ------------------------------------------------------------ generic affine scan
+
+
+def affine_inputs(seed, N, T):
+    rng = np.random.default_rng(seed)
+    alpha = rng.standard_normal((N, T)).astype(np.float32)
+    beta = rng.uniform(-0.99, 0.99, (N, T)).astype(np.float32)
+    beta[rng.random((N, T)) < 0.01] = 0.0
+    carry = rng.standard_normal(N).astype(np.float32)
+    return alpha, beta, carry
+
+
+@pytest.mark.parametrize("N,T", [(1, 1), (7, 5), (100, 16), (9, 128), (3, 1025), (40, 513),
+                                 (3, 10000), (2, 65536)])
+@pytest.mark.parametrize("direction", [rl.BACKWARD, rl.FORWARD])
+def test_affine_scan(N, T, direction, gpu_device):
+    alpha, beta, carry = affine_inputs(500 + N + T + direction, N, T)
+    for c in (carry, None):
+        out = rl.affine_scan(dev(alpha, gpu_device), dev(beta, gpu_device), dev(c, gpu_device),
+                             direction)
+        assert_parity(out, oracle.affine_scan(alpha, beta, c, direction),
+                      f"affine N={N} T={T} dir={direction} carry={c is not None}")
