@@ -437,3 +437,32 @@ def test_affine_scan(N, T, direction, gpu_device):
                              direction)
         assert_parity(out, oracle.affine_scan(alpha, beta, c, direction),
                       f"affine N={N} T={T} dir={direction} carry={c is not None}")
+
+
+# ------------------------------------------------------- 64-bit indexing, big N*T
+
+
+def test_indexing_beyond_2_pow_31_steps(gpu_device):
+    """2,147,486,720 steps (> 2^31): flat offsets need 64 bits, and the grid
+    (capped at 2^20 workgroups) must loop over the last row groups.  Checked
+    against the oracle on sampled rows at both ends and in the middle.  Inputs
+    are drawn on the device with a seeded generator (about 20 GB of HBM)."""
+    N, T = (1 << 21) + 3, 1024
+    gen = torch.Generator(device=gpu_device)
+    gen.manual_seed(77)
+    r = torch.randn((N, T), generator=gen, device=gpu_device)
+    flags = (torch.rand((N, T), generator=gen, device=gpu_device) < 0.01).to(torch.uint8)
+    boot = torch.randn(N, generator=gen, device=gpu_device)
+    rows = [0, 1, 2, N // 2, N // 2 + 1, N - 3, N - 2, N - 1]
+
+    def sample(x):
+        return x[rows].cpu().numpy()
+
+    out = rl.discounted_returns(r, flags, bootstrap=boot)
+    assert_parity(out[rows], oracle.discounted_returns(sample(r), sample(flags), None, None,
+                                                       sample(boot), 0.99), "discounted 2^31+")
+    rl.eligibility_traces(r, flags, rl.RESET_ON_START, 0.99, 0.9, out=out)
+    assert_parity(out[rows], oracle.eligibility_traces(sample(r), sample(flags), 0, 0.99, 0.9),
+                  "eligibility 2^31+")
+    del out, r, flags
+    torch.cuda.empty_cache()
