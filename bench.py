@@ -9,11 +9,15 @@ Measurement:
   * cold cache: every call reads a different copy of the rollout, rotating
     over >= 1 GiB of copies, so neither the 4 MB-per-XCD L2 nor the 256 MB
     Infinity Cache can serve the operands;
-  * launches are eager (pre-bound ctypes calls, asynchronous on one stream);
-    --launch graph captures each step into a HIP graph and replays it;
+  * each step is one rlca_run_batch holding the step's calls, which share one
+    grouped launch (pre-bound ctypes call, asynchronous on one stream);
+    --launch eager makes one library call per estimator instead, and
+    --launch graph captures those calls into a HIP graph per step and replays
+    it;
   * whole-step time: HIP events around K steps, synchronised on both sides;
-    per-kernel time: HIP events around a back-to-back batch of one call
-    variant (rotating sets), averaged over the batch;
+    per-kernel time: HIP events around back-to-back launches of one call
+    variant (rotating sets), averaged; with --launch batch the roofline is
+    that of the grouped launch over the whole step's bytes;
   * effective GB/s uses the algorithmic byte model: every input array read
     once and every output written once at dense size (fp32 / int32 4 B, flags
     1 B per step, bootstrap 4 B per row);
@@ -125,17 +129,50 @@ def make_sets(torch, arrays, calls, device, min_call_bytes):
     return sets
 
 
+# Positional arguments of each entry point, named as the rlca_call fields they
+# fill when the same call is recorded into a batch.
+_BACKWARD_HEAD = ["rewards", "values", "terminated", "truncated", "trunc_values", "bootstrap",
+                  "gamma", "lambda_", "num_envs", "T"]
+BATCH_FIELDS = {
+    "rlca_gae": (0, _BACKWARD_HEAD + ["out0", "out1"]),
+    "rlca_td_lambda": (1, _BACKWARD_HEAD + ["out0"]),
+    "rlca_discounted_returns": (2, ["rewards", "terminated", "truncated", "trunc_values",
+                                    "bootstrap", "gamma", "num_envs", "T", "out0"]),
+    "rlca_vtrace": (3, ["rewards", "values", "behaviour_logp", "target_logp", "terminated",
+                        "truncated", "trunc_values", "bootstrap", "gamma", "lambda_",
+                        "rho_bar", "c_bar", "num_envs", "T", "out0", "out1"]),
+    "rlca_retrace": (4, ["rewards", "values", "expected_q", "behaviour_logp", "target_logp",
+                         "terminated", "truncated", "trunc_values", "bootstrap", "gamma",
+                         "lambda_", "c_bar", "num_envs", "T", "out0"]),
+    "rlca_eligibility_traces": (5, ["rewards", "terminated", "convention", "gamma", "lambda_",
+                                    "num_envs", "T", "out0"]),
+    "rlca_episodic_prefix_sum": (6, ["rewards", "dtype", "terminated", "convention",
+                                     "num_envs", "T", "out0"]),
+}
+
+
+def _resolve(a, bufs):
+    return bufs[a[1:]].data_ptr() if isinstance(a, str) and a.startswith("@") else a
+
+
+def batch_record(rlca, call, bufs):
+    """The rlca_call that records `call` on rotation set `bufs`."""
+    _, fname, template, _, _ = call
+    op, names = BATCH_FIELDS[fname]
+    c = rlca.RlcaCall(op=op)
+    for name, a in zip(names, template):
+        setattr(c, name, _resolve(a, bufs))
+    return c
+
+
+def bind_batch(lib, rlca, recorded, stream):
+    arr = (rlca.RlcaCall * len(recorded))(*recorded)
+    return lib.rlca_run_batch, (arr, len(recorded), stream)
+
+
 def bind(lib, call, bufs, stream):
     _, fname, template, _, _ = call
-    fn = getattr(lib, fname)
-    args = []
-    for a in template:
-        if isinstance(a, str) and a.startswith("@"):
-            args.append(bufs[a[1:]].data_ptr())
-        else:
-            args.append(a)
-    args.append(stream)
-    return fn, tuple(args)
+    return getattr(lib, fname), tuple(_resolve(a, bufs) for a in template) + (stream,)
 
 
 def run_gpu(args, name, cfg, host):
@@ -158,12 +195,16 @@ def run_gpu(args, name, cfg, host):
     steps_per_cycle = cycle // ncalls
 
     def launches(h):
+        """Per step of the rotation cycle, the bound launches: one per call,
+        or with --launch batch one rlca_run_batch holding every call."""
         out = []
         for s in range(steps_per_cycle):
-            row = []
-            for c in range(ncalls):
-                row.append(bind(lib, calls[c], sets[(s * ncalls + c) % nsets], h))
-            out.append(row)
+            bufs = [sets[(s * ncalls + c) % nsets] for c in range(ncalls)]
+            if args.launch == "batch":
+                out.append([bind_batch(lib, rlca, [batch_record(rlca, calls[c], bufs[c])
+                                                   for c in range(ncalls)], h)])
+            else:
+                out.append([bind(lib, calls[c], bufs[c], h) for c in range(ncalls)])
         return out
 
     def check(st, what):
@@ -181,14 +222,14 @@ def run_gpu(args, name, cfg, host):
             for s in range(steps_per_cycle):
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=stream):
-                    for c, (fn, a) in enumerate(plan[s]):
-                        check(fn(*a), calls[c][0])
+                    for fn, a in plan[s]:
+                        check(fn(*a), fn.__name__)
                 graphs.append(g)
             run_step = lambda s: graphs[s % steps_per_cycle].replay()  # noqa: E731
         else:
             def run_step(s):
-                for c, (fn, a) in enumerate(plan[s % steps_per_cycle]):
-                    check(fn(*a), calls[c][0])
+                for fn, a in plan[s % steps_per_cycle]:
+                    check(fn(*a), fn.__name__)
 
         for s in range(warm):
             run_step(s)
@@ -206,25 +247,29 @@ def run_gpu(args, name, cfg, host):
         wall = time.perf_counter() - t0
         step_ms = e_start.elapsed_time(e_end) / timed_steps
 
-        # per-kernel device time: each call variant launched back to back
-        # `batch` times (rotating sets) between two events on the same stream;
-        # the average is elapsed / batch
-        batch = max(50, min(timed_steps, 2000))
-        per_call_ms = []
-        for c in range(ncalls):
-            bound = [bind(lib, calls[c], sets[i % nsets], h) for i in range(nsets)]
+        # per-kernel device time: each call variant (and with --launch batch
+        # the grouped launch of the whole step) launched back to back `reps`
+        # times (rotating sets) between two events on the same stream; the
+        # average is elapsed / reps
+        reps = max(50, min(timed_steps, 2000))
+
+        def back_to_back(bound):
             for i in range(5):
-                fn, a = bound[i % nsets]
-                check(fn(*a), calls[c][0])
+                fn, a = bound[i % len(bound)]
+                check(fn(*a), fn.__name__)
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            for i in range(batch):
-                fn, a = bound[i % nsets]
-                check(fn(*a), calls[c][0])
+            for i in range(reps):
+                fn, a = bound[i % len(bound)]
+                check(fn(*a), fn.__name__)
             e1.record(stream)
             torch.cuda.synchronize()
-            per_call_ms.append(e0.elapsed_time(e1) / batch)
+            return e0.elapsed_time(e1) / reps
+
+        per_call_ms = [back_to_back([bind(lib, calls[c], sets[i], h) for i in range(nsets)])
+                       for c in range(ncalls)]
+        batch_ms = back_to_back([p[0] for p in plan]) if args.launch == "batch" else None
 
         # same-bytes copy ceiling (cold, rotating): a plain device copy of
         # step_bytes / 2 read + step_bytes / 2 written
@@ -248,7 +293,8 @@ def run_gpu(args, name, cfg, host):
 
     nt = host.num_envs * host.T
     return dict(step_ms=step_ms, wall_s=wall, step_bytes=step_bytes, calls=calls,
-                per_call_ms=per_call_ms, dominant=dominant, nt=nt, nsets=nsets,
+                per_call_ms=per_call_ms, batch_ms=batch_ms, dominant=dominant, nt=nt,
+                nsets=nsets,
                 copy_gbs=copy_gbs, copy_bytes=nfl * 8)
 
 
@@ -431,7 +477,7 @@ def main():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="gae_td_4096x128")
-    ap.add_argument("--launch", choices=("graph", "eager"), default="eager")
+    ap.add_argument("--launch", choices=("batch", "graph", "eager"), default="batch")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
@@ -460,12 +506,14 @@ def main():
     step_s = res["step_ms"] * 1e-3
     ncalls = len(res["calls"])
     value = res["step_bytes"] / step_s / 1e9
-    dom = res["dominant"]
-    dcall = res["calls"][dom]
-    dom_ms = res["per_call_ms"][dom]
-    achieved = dcall[3] / (dom_ms * 1e-3) / 1e9
-    kernel_tag = dcall[0].replace("+", "_")
-    traffic = measured_traffic(kernel_tag, args.workload)
+    if res["batch_ms"] is not None:
+        # one grouped launch runs the whole step: it is the dominant kernel
+        dom_name, dom_bytes, dom_ms = "batch", res["step_bytes"], res["batch_ms"]
+    else:
+        dcall = res["calls"][res["dominant"]]
+        dom_name, dom_bytes, dom_ms = dcall[0], dcall[3], res["per_call_ms"][res["dominant"]]
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    traffic = measured_traffic(dom_name.replace("+", "_"), args.workload)
 
     calls_out = {}
     for i, c in enumerate(res["calls"]):
@@ -502,14 +550,14 @@ def main():
         "copy_ceiling": {"gbs": round(res["copy_gbs"], 1), "bytes": res["copy_bytes"],
                          "kind": "torch device copy, cold rotation, same bytes moved"},
         "roofline": {
-            "kernel": dcall[0],
+            "kernel": dom_name,
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "algorithmic_bytes": dcall[3],
+            "algorithmic_bytes": dom_bytes,
             "avg_us": round(dom_ms * 1e3, 3),
         },
     }

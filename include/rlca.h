@@ -189,6 +189,71 @@ rlca_status rlca_affine_scan(const float *alpha, const float *beta, const float 
                              rlca_direction direction, int64_t num_envs, int64_t T, float *out,
                              hipStream_t stream);
 
+/* ---------------------------------------------------------------- batches
+ * Several of the calls above enqueued together.  Each element is validated
+ * exactly as its own entry point would validate it (the same status codes,
+ * nothing enqueued on any failure), plus: no call may write memory that
+ * another call of the batch reads or writes (RLCA_ERR_ALIASING), because the
+ * calls run concurrently.  Calls on the vectorised path that need a single
+ * launch share grouped launches (one launch for up to 16 calls), which
+ * removes the per-launch overhead that dominates small rollouts; the others
+ * are enqueued one by one, in order.  Results are bit for bit those of the
+ * separate calls, except for vectorised rows of 257..1023 steps: a grouped
+ * launch scans them with eight-wave workgroups where the separate call uses
+ * one wave, so the two differ by rounding order only.  (Launch-overhead reduction for small shapes: the summary's §9
+ * Limitations, where launch and wrapper overhead dominate at 16 steps.) */
+#define RLCA_MAX_BATCH 64
+
+typedef enum {
+    RLCA_OP_GAE = 0,
+    RLCA_OP_TD_LAMBDA = 1,
+    RLCA_OP_DISCOUNTED_RETURNS = 2,
+    RLCA_OP_VTRACE = 3,
+    RLCA_OP_RETRACE = 4,
+    RLCA_OP_ELIGIBILITY_TRACES = 5,
+    RLCA_OP_EPISODIC_PREFIX_SUM = 6,
+    RLCA_OP_AFFINE_SCAN = 7
+} rlca_op;
+
+/* One call of a batch.  Fields carry the arguments of the op's entry point;
+ * fields an op does not take are ignored.
+ *   rewards     rewards (GAE, TD, discounted, V-Trace, Retrace); increments
+ *               (eligibility traces); x (prefix sum, f32 or i32 per dtype);
+ *               alpha (affine scan)
+ *   values      values (GAE, TD, V-Trace); q_values (Retrace); beta (affine)
+ *   terminated  terminated (backward estimators); flags (forward scans)
+ *   bootstrap   bootstrap (backward estimators); carry (affine scan)
+ *   out0        advantages / returns / vs / q_ret / traces / out
+ *   out1        GAE returns or V-Trace pg_advantages; nullable
+ *   convention, dtype, direction: as the forward scans / affine scan take them */
+typedef struct {
+    rlca_op op;
+    int64_t num_envs;
+    int64_t T;
+    const float *rewards;
+    const float *values;
+    const float *expected_q;
+    const float *behaviour_logp;
+    const float *target_logp;
+    const uint8_t *terminated;
+    const uint8_t *truncated;
+    const float *trunc_values;
+    const float *bootstrap;
+    float gamma;
+    float lambda;
+    float rho_bar;
+    float c_bar;
+    int convention;
+    int dtype;
+    int direction;
+    void *out0;
+    void *out1;
+} rlca_call;
+
+/* Enqueue `count` (0..RLCA_MAX_BATCH) calls on `stream`; `calls` is host
+ * memory, read before the function returns. */
+rlca_status rlca_run_batch(const rlca_call *calls, int count, hipStream_t stream);
+
 /* Static description of a status code (never NULL). */
 const char *rlca_status_string(rlca_status status);
 

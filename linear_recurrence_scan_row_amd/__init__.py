@@ -10,6 +10,7 @@ librlca.so, which must be built (``python -m linear_recurrence_scan_row_amd.buil
 from .rlca import (  # noqa: F401
     BACKWARD,
     FORWARD,
+    Batch,
     RESET_AFTER_DONE,
     RESET_ON_START,
     RlcaError,

@@ -360,10 +360,10 @@ __device__ __forceinline__ void adopt_lead(ForwardParams &p, LEAD_ARGS) {
 // ------------------------------------------------------------- backward kernel
 // A_t = alpha_t + beta_t * A_{t+1}.  Lanes take chunks in reverse time order, so
 // the lane-order scan of scan_core.hpp runs from the end of the tile backwards.
+// Groups g, g + g_stride, ... of the launch run through one workgroup.
 template <int EST, bool TRUNC, bool VEC, int NW, bool WAVE_LOCAL, int MODE>
-__global__ __launch_bounds__(NW * kWave) void backward_scan(LEAD_ARGS, BackwardParams p) {
+__device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uint32_t g_stride) {
     static_assert(MODE == kFull || (NW == kChunkWaves && !WAVE_LOCAL), "a chunk is one tile");
-    adopt_lead<EST>(p, LEAD_NAMES);
     constexpr uint32_t kTile = NW * kWave * kK;
     constexpr bool kFlags = EST != kAffineBackward;
     __shared__ float lds_a[2 * NW], lds_b[2 * NW];
@@ -377,7 +377,6 @@ __global__ __launch_bounds__(NW * kWave) void backward_scan(LEAD_ARGS, BackwardP
     // The grid never exceeds the group count, so the first group always
     // exists; testing only at the bottom lets every kernel-argument load go
     // out together instead of after a first round trip for the bound.
-    uint32_t g = blockIdx.x;
     do {
         const Window win = window_of<MODE, true>(p.geo, g);
         const int64_t row0 = win.row0, base = win.base;
@@ -569,8 +568,14 @@ __global__ __launch_bounds__(NW * kWave) void backward_scan(LEAD_ARGS, BackwardP
                 }
             }
         }
-        g += gridDim.x;
+        g += g_stride;
     } while (g < p.geo.num_groups);
+}
+
+template <int EST, bool TRUNC, bool VEC, int NW, bool WAVE_LOCAL, int MODE>
+__global__ __launch_bounds__(NW * kWave) void backward_scan(LEAD_ARGS, BackwardParams p) {
+    adopt_lead<EST>(p, LEAD_NAMES);
+    backward_body<EST, TRUNC, VEC, NW, WAVE_LOCAL, MODE>(p, blockIdx.x, gridDim.x);
 }
 
 // -------------------------------------------------------------- forward kernel
@@ -580,9 +585,8 @@ __global__ __launch_bounds__(NW * kWave) void backward_scan(LEAD_ARGS, BackwardP
 // wrap-around).  kForwardAffine: the caller's (alpha, beta), with the row's
 // carry entering at t = 0.
 template <typename V, int KIND, bool AFTER_DONE, bool VEC, int NW, bool WAVE_LOCAL, int MODE>
-__global__ __launch_bounds__(NW * kWave) void forward_scan(LEAD_ARGS, ForwardParams p) {
+__device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint32_t g_stride) {
     static_assert(MODE == kFull || (NW == kChunkWaves && !WAVE_LOCAL), "a chunk is one tile");
-    adopt_lead(p, LEAD_NAMES);
     constexpr uint32_t kTile = NW * kWave * kK;
     __shared__ V lds_a[2 * NW], lds_b[2 * NW];
     const int lane = threadIdx.x & (kWave - 1);
@@ -594,8 +598,7 @@ __global__ __launch_bounds__(NW * kWave) void forward_scan(LEAD_ARGS, ForwardPar
     V *__restrict__ out = static_cast<V *>(p.out);
     int parity = 0;
 
-    uint32_t g = blockIdx.x;  // first group always exists (see backward_scan)
-    do {
+    do {  // the first group always exists (see backward_body)
         const Window win = window_of<MODE, false>(p.geo, g);
         const int64_t row0 = win.row0, base = win.base;
         const uint32_t L = win.L;
@@ -682,8 +685,14 @@ __global__ __launch_bounds__(NW * kWave) void forward_scan(LEAD_ARGS, ForwardPar
                 store_steps<VEC>(out + base, o, off, L);
             }
         }
-        g += gridDim.x;
+        g += g_stride;
     } while (g < p.geo.num_groups);
+}
+
+template <typename V, int KIND, bool AFTER_DONE, bool VEC, int NW, bool WAVE_LOCAL, int MODE>
+__global__ __launch_bounds__(NW * kWave) void forward_scan(LEAD_ARGS, ForwardParams p) {
+    adopt_lead(p, LEAD_NAMES);
+    forward_body<V, KIND, AFTER_DONE, VEC, NW, WAVE_LOCAL, MODE>(p, blockIdx.x, gridDim.x);
 }
 
 // ------------------------------------------------------------ chunk carries
@@ -861,6 +870,41 @@ rlca_status launch_forward_variant(ForwardParams &p, const LaunchShape &s, hipSt
     return launch_full(forward_kernel<V, KIND, AFTER_DONE>(s), s.vec ? s.waves : 4, p, lead,
                        stream);
 }
+
+// ------------------------------------------------------------- grouped launch
+// Several calls in one launch: workgroup b runs group b - first_group[c] of
+// call c, where c is the call whose group range holds b.  Every member uses
+// the vector path, full mode and 8-wave workgroups; `variant` names the
+// estimator body.  The argument block travels in the kernel arguments.
+constexpr int kGroupWaves = 8;
+constexpr int kMaxGroupedCalls = 16;
+
+struct GroupedCall {
+    int variant;
+    union {
+        BackwardParams b;
+        ForwardParams f;
+    };
+};
+
+struct GroupedArgs {
+    int count;
+    uint32_t first_group[kMaxGroupedCalls + 1];
+    GroupedCall calls[kMaxGroupedCalls];
+};
+
+// Variant numbering: backward estimators 0..23 (estimator x truncation x
+// wave-local), flag-driven forward scans 24..31 (int32 x after-done x
+// wave-local), the forward affine scan 32..33.
+constexpr int grouped_backward_variant(int est, bool trunc, bool wave_local) {
+    return est * 4 + (trunc ? 2 : 0) + (wave_local ? 1 : 0);
+}
+constexpr int grouped_forward_variant(bool is_int, bool after_done, bool wave_local) {
+    return 24 + (is_int ? 4 : 0) + (after_done ? 2 : 0) + (wave_local ? 1 : 0);
+}
+constexpr int grouped_affine_forward_variant(bool wave_local) { return 32 + (wave_local ? 1 : 0); }
+
+rlca_status launch_grouped(const GroupedArgs &args, hipStream_t stream);
 
 // One translation unit per estimator instantiates these (see est_*.hip).
 rlca_status launch_gae(BackwardParams &p, const LaunchShape &s, hipStream_t stream);

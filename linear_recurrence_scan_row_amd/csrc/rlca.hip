@@ -1,10 +1,11 @@
-// rlca.hip -- the C ABI of rlca.h: argument checks and launch-shape choice.
+// rlca.hip -- the C ABI of rlca.h: argument checks, launch-shape choice, batching.
 //
 // The kernels live in kernels.hpp and are instantiated one estimator per
-// translation unit (est_*.hip).  Every entry point validates its arguments
-// before anything is enqueued, picks a launch shape from (num_envs, T,
-// alignment) and enqueues its kernel launch(es) on the caller's stream: one
-// launch, or three for a few long rows (the chunk modes).
+// translation unit (est_*.hip).  Every entry point first turns its arguments
+// into a validated Call (nothing is enqueued when a check fails), then
+// enqueues it on the caller's stream: one launch, or three for a few long
+// rows (the chunk modes).  rlca_run_batch validates a list of calls the same
+// way and runs the eligible ones together in grouped launches.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -93,64 +94,334 @@ static LaunchShape choose_shape(int64_t num_envs, int64_t T, bool vec) {
     return s;
 }
 
-static rlca_status run_backward(int est, BackwardParams &p, int64_t T, hipStream_t stream) {
-    const void *f32[] = {p.rewards, p.values, p.expected_q, p.behaviour_logp, p.target_logp,
-                         p.trunc_values, p.out0, p.out1};
-    const void *u8[] = {p.terminated, p.truncated};
-    const LaunchShape s = choose_shape(p.geo.num_envs, T, vec_ok(T, f32, 8, u8, 2));
-    p.geo.T = (uint32_t)T;
-    switch (est) {
-        case kGae: return launch_gae(p, s, stream);
-        case kTdLambda: return launch_td_lambda(p, s, stream);
-        case kDiscounted: return launch_discounted(p, s, stream);
-        case kVtrace: return launch_vtrace(p, s, stream);
-        case kRetrace: return launch_retrace(p, s, stream);
-        default: return launch_affine_backward(p, s, stream);
-    }
-}
+// ------------------------------------------------------------ validated calls
 
-// Checks shared by the five backward estimators.  `ins_f32` lists the
-// required fp32 per-step inputs (all non-null).
-static rlca_status check_backward(const float *const *req_f32, int nreq, const uint8_t *terminated,
-                                  const uint8_t *truncated, const float *trunc_values,
-                                  const float *bootstrap, float *const *outs, int nouts,
-                                  bool out0_required, int64_t num_envs, int64_t T,
-                                  int64_t *elems) {
-    rlca_status st = check_sizes(num_envs, T, elems);
+// A call whose arguments passed every check, ready to enqueue alone or in a
+// batch.  `ins` / `outs` keep the byte ranges for cross-call aliasing checks.
+struct Call {
+    bool empty;  // num_envs * T == 0: nothing to enqueue
+    bool backward;
+    int est;          // backward estimator
+    int forward;      // forward kind
+    bool is_int;      // forward int32 prefix sum
+    bool after_done;  // forward reset convention
+    LaunchShape shape;
+    BackwardParams bp;
+    ForwardParams fp;
+    Span ins[12];
+    int nin;
+    Span outs[2];
+    int nout;
+};
+
+// Checks shared by the backward estimators; fills the call's parameter
+// block, byte ranges and launch shape.  Arrays an estimator does not use are
+// passed as NULL and neither required nor read.
+static rlca_status prepare_backward(int est, const float *rewards, const float *values,
+                                    const float *expected_q, const float *behaviour_logp,
+                                    const float *target_logp, const uint8_t *terminated,
+                                    const uint8_t *truncated, const float *trunc_values,
+                                    const float *bootstrap, float *out0, float *out1,
+                                    int64_t num_envs, int64_t T, Call *c) {
+    *c = Call{};
+    int64_t n;
+    rlca_status st = check_sizes(num_envs, T, &n);
     if (st != RLCA_OK) return st;
-    if (*elems == 0) return RLCA_OK;
-    for (int i = 0; i < nreq; ++i)
-        if (req_f32[i] == nullptr) return RLCA_ERR_NULL_POINTER;
-    if (terminated == nullptr) return RLCA_ERR_NULL_POINTER;
+    c->empty = n == 0;
+    if (c->empty) return RLCA_OK;
+    const bool needs_values = est != kDiscounted;
+    const bool needs_logp = est == kVtrace || est == kRetrace;
+    const bool needs_flags = est != kAffineBackward;
+    if (rewards == nullptr || out0 == nullptr) return RLCA_ERR_NULL_POINTER;
+    if (needs_values && values == nullptr) return RLCA_ERR_NULL_POINTER;
+    if (est == kRetrace && expected_q == nullptr) return RLCA_ERR_NULL_POINTER;
+    if (needs_logp && (behaviour_logp == nullptr || target_logp == nullptr))
+        return RLCA_ERR_NULL_POINTER;
+    if (needs_flags && terminated == nullptr) return RLCA_ERR_NULL_POINTER;
     if (truncated != nullptr && trunc_values == nullptr) return RLCA_ERR_NULL_POINTER;
-    if (out0_required && outs[0] == nullptr) return RLCA_ERR_NULL_POINTER;
-    const void *al[16];
-    int na = 0;
-    for (int i = 0; i < nreq; ++i) al[na++] = req_f32[i];
-    al[na++] = truncated ? trunc_values : nullptr;
-    al[na++] = bootstrap;
-    for (int i = 0; i < nouts; ++i) al[na++] = outs[i];
-    st = check_aligned4(al, na);
+    if (!needs_flags) terminated = truncated = nullptr;
+    if (truncated == nullptr) trunc_values = nullptr;
+    if (!needs_values) values = nullptr;
+    if (est != kRetrace) expected_q = nullptr;
+    if (!needs_logp) behaviour_logp = target_logp = nullptr;
+    const void *f32[] = {rewards,     values,       expected_q, behaviour_logp, target_logp,
+                         trunc_values, bootstrap,   out0,       out1};
+    st = check_aligned4(f32, 9);
     if (st != RLCA_OK) return st;
-    const size_t fb = (size_t)*elems * 4, ub = (size_t)*elems;
-    Span ins[16];
-    int ni = 0;
-    for (int i = 0; i < nreq; ++i) ins[ni++] = {req_f32[i], fb};
-    ins[ni++] = {terminated, ub};
-    if (truncated) {
-        ins[ni++] = {truncated, ub};
-        ins[ni++] = {trunc_values, fb};
-    }
-    ins[ni++] = {bootstrap, (size_t)num_envs * 4};
-    Span os[4];
-    for (int i = 0; i < nouts; ++i) os[i] = {outs[i], fb};
-    return check_aliasing(os, nouts, ins, ni);
+    const size_t fb = (size_t)n * 4, ub = (size_t)n;
+    const void *f32_steps[] = {rewards, values, expected_q, behaviour_logp, target_logp,
+                               trunc_values};
+    for (const void *p : f32_steps)
+        if (p != nullptr) c->ins[c->nin++] = {p, fb};
+    if (terminated != nullptr) c->ins[c->nin++] = {terminated, ub};
+    if (truncated != nullptr) c->ins[c->nin++] = {truncated, ub};
+    c->ins[c->nin++] = {bootstrap, (size_t)num_envs * 4};
+    c->outs[c->nout++] = {out0, fb};
+    if (out1 != nullptr) c->outs[c->nout++] = {out1, fb};
+    st = check_aliasing(c->outs, c->nout, c->ins, c->nin);
+    if (st != RLCA_OK) return st;
+
+    c->backward = true;
+    c->est = est;
+    BackwardParams &p = c->bp;
+    p.rewards = rewards;
+    p.values = values;
+    p.expected_q = expected_q;
+    p.behaviour_logp = behaviour_logp;
+    p.target_logp = target_logp;
+    p.terminated = terminated;
+    p.truncated = truncated;
+    p.trunc_values = trunc_values;
+    p.bootstrap = bootstrap;
+    p.out0 = out0;
+    p.out1 = out1;
+    p.geo.num_envs = num_envs;
+    p.geo.T = (uint32_t)T;
+    const void *u8[] = {terminated, truncated};
+    c->shape = choose_shape(num_envs, T, vec_ok(T, f32, 9, u8, 2));
+    return RLCA_OK;
 }
 
-static BackwardParams backward_params(int64_t num_envs) {
-    BackwardParams p = {};
+static rlca_status prepare_forward(int kind, const void *x, bool is_int, const uint8_t *flags,
+                                   int convention, float decay, const float *beta,
+                                   const float *carry, int64_t num_envs, int64_t T, void *out,
+                                   Call *c) {
+    *c = Call{};
+    if (kind == kForwardFlags && convention != RLCA_RESET_ON_START &&
+        convention != RLCA_RESET_AFTER_DONE)
+        return RLCA_ERR_INVALID_VALUE;
+    int64_t n;
+    rlca_status st = check_sizes(num_envs, T, &n);
+    if (st != RLCA_OK) return st;
+    c->empty = n == 0;
+    if (c->empty) return RLCA_OK;
+    if (x == nullptr || out == nullptr) return RLCA_ERR_NULL_POINTER;
+    if (kind == kForwardFlags && flags == nullptr) return RLCA_ERR_NULL_POINTER;
+    if (kind == kForwardAffine && beta == nullptr) return RLCA_ERR_NULL_POINTER;
+    if (kind == kForwardFlags) beta = carry = nullptr;
+    if (kind == kForwardAffine) flags = nullptr;
+    const void *al[] = {x, beta, carry, out};
+    st = check_aligned4(al, 4);
+    if (st != RLCA_OK) return st;
+    c->ins[c->nin++] = {x, (size_t)n * 4};
+    if (flags != nullptr) c->ins[c->nin++] = {flags, (size_t)n};
+    if (beta != nullptr) c->ins[c->nin++] = {beta, (size_t)n * 4};
+    c->ins[c->nin++] = {carry, (size_t)num_envs * 4};
+    c->outs[c->nout++] = {out, (size_t)n * 4};
+    st = check_aliasing(c->outs, c->nout, c->ins, c->nin);
+    if (st != RLCA_OK) return st;
+
+    c->backward = false;
+    c->forward = kind;
+    c->is_int = is_int;
+    c->after_done = kind == kForwardFlags && convention == RLCA_RESET_AFTER_DONE;
+    ForwardParams &p = c->fp;
+    p.x = x;
+    p.flags = flags;
+    p.beta = beta;
+    p.carry = carry;
+    p.out = out;
+    p.decay = is_int ? __builtin_bit_cast(float, 1u) : decay;
     p.geo.num_envs = num_envs;
-    return p;
+    p.geo.T = (uint32_t)T;
+    const void *f32[] = {x, beta, out};
+    const void *u8[] = {flags};
+    c->shape = choose_shape(num_envs, T, vec_ok(T, f32, 3, u8, 1));
+    return RLCA_OK;
+}
+
+// Enqueue one call on its own.
+static rlca_status launch_call(Call &c, hipStream_t stream) {
+    if (c.empty) return RLCA_OK;
+    if (c.backward) {
+        switch (c.est) {
+            case kGae: return launch_gae(c.bp, c.shape, stream);
+            case kTdLambda: return launch_td_lambda(c.bp, c.shape, stream);
+            case kDiscounted: return launch_discounted(c.bp, c.shape, stream);
+            case kVtrace: return launch_vtrace(c.bp, c.shape, stream);
+            case kRetrace: return launch_retrace(c.bp, c.shape, stream);
+            default: return launch_affine_backward(c.bp, c.shape, stream);
+        }
+    }
+    if (c.forward == kForwardAffine) return launch_affine_forward(c.fp, c.shape, stream);
+    return c.is_int ? launch_forward_u32(c.fp, c.after_done, c.shape, stream)
+                    : launch_forward_f32(c.fp, c.after_done, c.shape, stream);
+}
+
+// The call as one member of a grouped launch (vector path, full mode, 8 waves).
+static GroupedCall grouped_member(const Call &c, uint32_t *groups) {
+    GroupedCall g;
+    uint32_t grid;
+    const bool wl = c.shape.wave_local;
+    if (c.backward) {
+        g.b = c.bp;
+        g.b.geo = make_geometry(c.bp.geo.num_envs, c.bp.geo.T, kGroupWaves, false, &grid);
+        g.variant = grouped_backward_variant(c.est, c.bp.truncated != nullptr, wl);
+        *groups = g.b.geo.num_groups;
+    } else {
+        g.f = c.fp;
+        g.f.geo = make_geometry(c.fp.geo.num_envs, c.fp.geo.T, kGroupWaves, false, &grid);
+        g.variant = c.forward == kForwardAffine
+                        ? grouped_affine_forward_variant(wl)
+                        : grouped_forward_variant(c.is_int, c.after_done, wl);
+        *groups = g.f.geo.num_groups;
+    }
+    return g;
+}
+
+static rlca_status prepare_gae(const float *rewards, const float *values,
+                               const uint8_t *terminated, const uint8_t *truncated,
+                               const float *trunc_values, const float *bootstrap, float gamma,
+                               float lambda, int64_t num_envs, int64_t T, float *advantages,
+                               float *returns, Call *c) {
+    *c = Call{};
+    if (!unit_interval(gamma) || !unit_interval(lambda)) return RLCA_ERR_INVALID_VALUE;
+    const rlca_status st =
+        prepare_backward(kGae, rewards, values, nullptr, nullptr, nullptr, terminated,
+                         truncated, trunc_values, bootstrap, advantages, returns, num_envs, T, c);
+    c->bp.gamma = gamma;
+    c->bp.lambda = lambda;
+    return st;
+}
+
+static rlca_status prepare_td_lambda(const float *rewards, const float *values,
+                                     const uint8_t *terminated, const uint8_t *truncated,
+                                     const float *trunc_values, const float *bootstrap,
+                                     float gamma, float lambda, int64_t num_envs, int64_t T,
+                                     float *returns, Call *c) {
+    *c = Call{};
+    if (!unit_interval(gamma) || !unit_interval(lambda)) return RLCA_ERR_INVALID_VALUE;
+    const rlca_status st =
+        prepare_backward(kTdLambda, rewards, values, nullptr, nullptr, nullptr, terminated,
+                         truncated, trunc_values, bootstrap, returns, nullptr, num_envs, T, c);
+    c->bp.gamma = gamma;
+    c->bp.lambda = lambda;
+    return st;
+}
+
+static rlca_status prepare_discounted(const float *rewards, const uint8_t *terminated,
+                                      const uint8_t *truncated, const float *trunc_values,
+                                      const float *bootstrap, float gamma, int64_t num_envs,
+                                      int64_t T, float *returns, Call *c) {
+    *c = Call{};
+    if (!unit_interval(gamma)) return RLCA_ERR_INVALID_VALUE;
+    const rlca_status st =
+        prepare_backward(kDiscounted, rewards, nullptr, nullptr, nullptr, nullptr, terminated,
+                         truncated, trunc_values, bootstrap, returns, nullptr, num_envs, T, c);
+    c->bp.gamma = gamma;
+    return st;
+}
+
+static rlca_status prepare_vtrace(const float *rewards, const float *values,
+                                  const float *behaviour_logp, const float *target_logp,
+                                  const uint8_t *terminated, const uint8_t *truncated,
+                                  const float *trunc_values, const float *bootstrap, float gamma,
+                                  float lambda, float rho_bar, float c_bar, int64_t num_envs,
+                                  int64_t T, float *vs, float *pg_advantages, Call *c) {
+    *c = Call{};
+    if (!unit_interval(gamma) || !unit_interval(lambda) || !positive_finite(rho_bar) ||
+        !positive_finite(c_bar))
+        return RLCA_ERR_INVALID_VALUE;
+    const rlca_status st = prepare_backward(kVtrace, rewards, values, nullptr, behaviour_logp,
+                                            target_logp, terminated, truncated, trunc_values,
+                                            bootstrap, vs, pg_advantages, num_envs, T, c);
+    c->bp.gamma = gamma;
+    c->bp.lambda = lambda;
+    c->bp.rho_bar = rho_bar;
+    c->bp.c_bar = c_bar;
+    return st;
+}
+
+static rlca_status prepare_retrace(const float *rewards, const float *q_values,
+                                   const float *expected_q, const float *behaviour_logp,
+                                   const float *target_logp, const uint8_t *terminated,
+                                   const uint8_t *truncated, const float *trunc_values,
+                                   const float *bootstrap, float gamma, float lambda, float c_bar,
+                                   int64_t num_envs, int64_t T, float *q_ret, Call *c) {
+    *c = Call{};
+    if (!unit_interval(gamma) || !unit_interval(lambda) || !positive_finite(c_bar))
+        return RLCA_ERR_INVALID_VALUE;
+    const rlca_status st = prepare_backward(kRetrace, rewards, q_values, expected_q,
+                                            behaviour_logp, target_logp, terminated, truncated,
+                                            trunc_values, bootstrap, q_ret, nullptr, num_envs, T,
+                                            c);
+    c->bp.gamma = gamma;
+    c->bp.lambda = lambda;
+    c->bp.c_bar = c_bar;
+    return st;
+}
+
+static rlca_status prepare_eligibility(const float *increments, const uint8_t *flags,
+                                       int convention, float gamma, float lambda,
+                                       int64_t num_envs, int64_t T, float *traces, Call *c) {
+    *c = Call{};
+    if (!unit_interval(gamma) || !unit_interval(lambda)) return RLCA_ERR_INVALID_VALUE;
+    return prepare_forward(kForwardFlags, increments, false, flags, convention, gamma * lambda,
+                           nullptr, nullptr, num_envs, T, traces, c);
+}
+
+static rlca_status prepare_prefix_sum(const void *x, int dtype, const uint8_t *flags,
+                                      int convention, int64_t num_envs, int64_t T, void *out,
+                                      Call *c) {
+    *c = Call{};
+    if (dtype != RLCA_F32 && dtype != RLCA_I32) return RLCA_ERR_INVALID_VALUE;
+    return prepare_forward(kForwardFlags, x, dtype == RLCA_I32, flags, convention, 1.0f, nullptr,
+                           nullptr, num_envs, T, out, c);
+}
+
+static rlca_status prepare_affine(const float *alpha, const float *beta, const float *carry,
+                                  int direction, int64_t num_envs, int64_t T, float *out,
+                                  Call *c) {
+    *c = Call{};
+    if (direction != RLCA_BACKWARD && direction != RLCA_FORWARD) return RLCA_ERR_INVALID_VALUE;
+    if (direction == RLCA_BACKWARD)
+        return prepare_backward(kAffineBackward, alpha, beta, nullptr, nullptr, nullptr, nullptr,
+                                nullptr, nullptr, carry, out, nullptr, num_envs, T, c);
+    return prepare_forward(kForwardAffine, alpha, false, nullptr, 0, 0.f, beta, carry, num_envs,
+                           T, out, c);
+}
+
+// One rlca_call of a batch, prepared like its own entry point.
+static rlca_status prepare_op(const rlca_call &k, Call *c) {
+    switch (k.op) {
+        case RLCA_OP_GAE:
+            return prepare_gae(k.rewards, k.values, k.terminated, k.truncated, k.trunc_values,
+                               k.bootstrap, k.gamma, k.lambda, k.num_envs, k.T,
+                               static_cast<float *>(k.out0), static_cast<float *>(k.out1), c);
+        case RLCA_OP_TD_LAMBDA:
+            return prepare_td_lambda(k.rewards, k.values, k.terminated, k.truncated,
+                                     k.trunc_values, k.bootstrap, k.gamma, k.lambda, k.num_envs,
+                                     k.T, static_cast<float *>(k.out0), c);
+        case RLCA_OP_DISCOUNTED_RETURNS:
+            return prepare_discounted(k.rewards, k.terminated, k.truncated, k.trunc_values,
+                                      k.bootstrap, k.gamma, k.num_envs, k.T,
+                                      static_cast<float *>(k.out0), c);
+        case RLCA_OP_VTRACE:
+            return prepare_vtrace(k.rewards, k.values, k.behaviour_logp, k.target_logp,
+                                  k.terminated, k.truncated, k.trunc_values, k.bootstrap,
+                                  k.gamma, k.lambda, k.rho_bar, k.c_bar, k.num_envs, k.T,
+                                  static_cast<float *>(k.out0), static_cast<float *>(k.out1), c);
+        case RLCA_OP_RETRACE:
+            return prepare_retrace(k.rewards, k.values, k.expected_q, k.behaviour_logp,
+                                   k.target_logp, k.terminated, k.truncated, k.trunc_values,
+                                   k.bootstrap, k.gamma, k.lambda, k.c_bar, k.num_envs, k.T,
+                                   static_cast<float *>(k.out0), c);
+        case RLCA_OP_ELIGIBILITY_TRACES:
+            return prepare_eligibility(k.rewards, k.terminated, k.convention, k.gamma, k.lambda,
+                                       k.num_envs, k.T, static_cast<float *>(k.out0), c);
+        case RLCA_OP_EPISODIC_PREFIX_SUM:
+            return prepare_prefix_sum(k.rewards, k.dtype, k.terminated, k.convention, k.num_envs,
+                                      k.T, k.out0, c);
+        case RLCA_OP_AFFINE_SCAN:
+            return prepare_affine(k.rewards, k.values, k.bootstrap, k.direction, k.num_envs, k.T,
+                                  static_cast<float *>(k.out0), c);
+    }
+    *c = Call{};
+    return RLCA_ERR_INVALID_VALUE;
+}
+
+static rlca_status run_one(rlca_status prepared, Call &c, hipStream_t stream) {
+    return prepared != RLCA_OK ? prepared : launch_call(c, stream);
 }
 
 }  // namespace rlca
@@ -163,25 +434,10 @@ rlca_status rlca_gae(const float *rewards, const float *values, const uint8_t *t
                      const uint8_t *truncated, const float *trunc_values,
                      const float *bootstrap, float gamma, float lambda, int64_t num_envs,
                      int64_t T, float *advantages, float *returns, hipStream_t stream) {
-    if (!unit_interval(gamma) || !unit_interval(lambda)) return RLCA_ERR_INVALID_VALUE;
-    const float *req[] = {rewards, values};
-    float *outs[] = {advantages, returns};
-    int64_t n;
-    rlca_status st = check_backward(req, 2, terminated, truncated, trunc_values, bootstrap, outs,
-                                    2, true, num_envs, T, &n);
-    if (st != RLCA_OK || n == 0) return st;
-    BackwardParams p = backward_params(num_envs);
-    p.rewards = rewards;
-    p.values = values;
-    p.terminated = terminated;
-    p.truncated = truncated;
-    p.trunc_values = truncated ? trunc_values : nullptr;
-    p.bootstrap = bootstrap;
-    p.out0 = advantages;
-    p.out1 = returns;
-    p.gamma = gamma;
-    p.lambda = lambda;
-    return run_backward(kGae, p, T, stream);
+    Call c;
+    return run_one(prepare_gae(rewards, values, terminated, truncated, trunc_values, bootstrap,
+                               gamma, lambda, num_envs, T, advantages, returns, &c),
+                   c, stream);
 }
 
 rlca_status rlca_td_lambda(const float *rewards, const float *values,
@@ -189,46 +445,20 @@ rlca_status rlca_td_lambda(const float *rewards, const float *values,
                            const float *trunc_values, const float *bootstrap, float gamma,
                            float lambda, int64_t num_envs, int64_t T, float *returns,
                            hipStream_t stream) {
-    if (!unit_interval(gamma) || !unit_interval(lambda)) return RLCA_ERR_INVALID_VALUE;
-    const float *req[] = {rewards, values};
-    float *outs[] = {returns};
-    int64_t n;
-    rlca_status st = check_backward(req, 2, terminated, truncated, trunc_values, bootstrap, outs,
-                                    1, true, num_envs, T, &n);
-    if (st != RLCA_OK || n == 0) return st;
-    BackwardParams p = backward_params(num_envs);
-    p.rewards = rewards;
-    p.values = values;
-    p.terminated = terminated;
-    p.truncated = truncated;
-    p.trunc_values = truncated ? trunc_values : nullptr;
-    p.bootstrap = bootstrap;
-    p.out0 = returns;
-    p.gamma = gamma;
-    p.lambda = lambda;
-    return run_backward(kTdLambda, p, T, stream);
+    Call c;
+    return run_one(prepare_td_lambda(rewards, values, terminated, truncated, trunc_values,
+                                     bootstrap, gamma, lambda, num_envs, T, returns, &c),
+                   c, stream);
 }
 
 rlca_status rlca_discounted_returns(const float *rewards, const uint8_t *terminated,
                                     const uint8_t *truncated, const float *trunc_values,
                                     const float *bootstrap, float gamma, int64_t num_envs,
                                     int64_t T, float *returns, hipStream_t stream) {
-    if (!unit_interval(gamma)) return RLCA_ERR_INVALID_VALUE;
-    const float *req[] = {rewards};
-    float *outs[] = {returns};
-    int64_t n;
-    rlca_status st = check_backward(req, 1, terminated, truncated, trunc_values, bootstrap, outs,
-                                    1, true, num_envs, T, &n);
-    if (st != RLCA_OK || n == 0) return st;
-    BackwardParams p = backward_params(num_envs);
-    p.rewards = rewards;
-    p.terminated = terminated;
-    p.truncated = truncated;
-    p.trunc_values = truncated ? trunc_values : nullptr;
-    p.bootstrap = bootstrap;
-    p.out0 = returns;
-    p.gamma = gamma;
-    return run_backward(kDiscounted, p, T, stream);
+    Call c;
+    return run_one(prepare_discounted(rewards, terminated, truncated, trunc_values, bootstrap,
+                                      gamma, num_envs, T, returns, &c),
+                   c, stream);
 }
 
 rlca_status rlca_vtrace(const float *rewards, const float *values, const float *behaviour_logp,
@@ -237,31 +467,11 @@ rlca_status rlca_vtrace(const float *rewards, const float *values, const float *
                         const float *bootstrap, float gamma, float lambda, float rho_bar,
                         float c_bar, int64_t num_envs, int64_t T, float *vs,
                         float *pg_advantages, hipStream_t stream) {
-    if (!unit_interval(gamma) || !unit_interval(lambda) || !positive_finite(rho_bar) ||
-        !positive_finite(c_bar))
-        return RLCA_ERR_INVALID_VALUE;
-    const float *req[] = {rewards, values, behaviour_logp, target_logp};
-    float *outs[] = {vs, pg_advantages};
-    int64_t n;
-    rlca_status st = check_backward(req, 4, terminated, truncated, trunc_values, bootstrap, outs,
-                                    2, true, num_envs, T, &n);
-    if (st != RLCA_OK || n == 0) return st;
-    BackwardParams p = backward_params(num_envs);
-    p.rewards = rewards;
-    p.values = values;
-    p.behaviour_logp = behaviour_logp;
-    p.target_logp = target_logp;
-    p.terminated = terminated;
-    p.truncated = truncated;
-    p.trunc_values = truncated ? trunc_values : nullptr;
-    p.bootstrap = bootstrap;
-    p.out0 = vs;
-    p.out1 = pg_advantages;
-    p.gamma = gamma;
-    p.lambda = lambda;
-    p.rho_bar = rho_bar;
-    p.c_bar = c_bar;
-    return run_backward(kVtrace, p, T, stream);
+    Call c;
+    return run_one(prepare_vtrace(rewards, values, behaviour_logp, target_logp, terminated,
+                                  truncated, trunc_values, bootstrap, gamma, lambda, rho_bar,
+                                  c_bar, num_envs, T, vs, pg_advantages, &c),
+                   c, stream);
 }
 
 rlca_status rlca_retrace(const float *rewards, const float *q_values, const float *expected_q,
@@ -270,111 +480,88 @@ rlca_status rlca_retrace(const float *rewards, const float *q_values, const floa
                          const float *trunc_values, const float *bootstrap, float gamma,
                          float lambda, float c_bar, int64_t num_envs, int64_t T,
                          float *q_ret, hipStream_t stream) {
-    if (!unit_interval(gamma) || !unit_interval(lambda) || !positive_finite(c_bar))
-        return RLCA_ERR_INVALID_VALUE;
-    const float *req[] = {rewards, q_values, expected_q, behaviour_logp, target_logp};
-    float *outs[] = {q_ret};
-    int64_t n;
-    rlca_status st = check_backward(req, 5, terminated, truncated, trunc_values, bootstrap, outs,
-                                    1, true, num_envs, T, &n);
-    if (st != RLCA_OK || n == 0) return st;
-    BackwardParams p = backward_params(num_envs);
-    p.rewards = rewards;
-    p.values = q_values;
-    p.expected_q = expected_q;
-    p.behaviour_logp = behaviour_logp;
-    p.target_logp = target_logp;
-    p.terminated = terminated;
-    p.truncated = truncated;
-    p.trunc_values = truncated ? trunc_values : nullptr;
-    p.bootstrap = bootstrap;
-    p.out0 = q_ret;
-    p.gamma = gamma;
-    p.lambda = lambda;
-    p.c_bar = c_bar;
-    return run_backward(kRetrace, p, T, stream);
-}
-
-static rlca_status run_forward(const void *x, bool is_int, const uint8_t *flags,
-                               rlca_reset_convention conv, float decay, int64_t num_envs,
-                               int64_t T, void *out, hipStream_t stream) {
-    if (conv != RLCA_RESET_ON_START && conv != RLCA_RESET_AFTER_DONE)
-        return RLCA_ERR_INVALID_VALUE;
-    int64_t n;
-    rlca_status st = check_sizes(num_envs, T, &n);
-    if (st != RLCA_OK || n == 0) return st;
-    if (x == nullptr || flags == nullptr || out == nullptr) return RLCA_ERR_NULL_POINTER;
-    const void *al[] = {x, out};
-    st = check_aligned4(al, 2);
-    if (st != RLCA_OK) return st;
-    const Span ins[] = {{x, (size_t)n * 4}, {flags, (size_t)n}};
-    const Span os[] = {{out, (size_t)n * 4}};
-    st = check_aliasing(os, 1, ins, 2);
-    if (st != RLCA_OK) return st;
-    const void *f32[] = {x, out};
-    const void *u8[] = {flags};
-    const LaunchShape s = choose_shape(num_envs, T, vec_ok(T, f32, 2, u8, 1));
-    ForwardParams p = {};
-    p.x = x;
-    p.flags = flags;
-    p.out = out;
-    p.decay = is_int ? __builtin_bit_cast(float, 1u) : decay;
-    p.geo.num_envs = num_envs;
-    p.geo.T = (uint32_t)T;
-    const bool after = conv == RLCA_RESET_AFTER_DONE;
-    return is_int ? launch_forward_u32(p, after, s, stream)
-                  : launch_forward_f32(p, after, s, stream);
+    Call c;
+    return run_one(prepare_retrace(rewards, q_values, expected_q, behaviour_logp, target_logp,
+                                   terminated, truncated, trunc_values, bootstrap, gamma, lambda,
+                                   c_bar, num_envs, T, q_ret, &c),
+                   c, stream);
 }
 
 rlca_status rlca_eligibility_traces(const float *increments, const uint8_t *flags,
                                     rlca_reset_convention convention, float gamma,
                                     float lambda, int64_t num_envs, int64_t T, float *traces,
                                     hipStream_t stream) {
-    if (!unit_interval(gamma) || !unit_interval(lambda)) return RLCA_ERR_INVALID_VALUE;
-    return run_forward(increments, false, flags, convention, gamma * lambda, num_envs, T,
-                       traces, stream);
+    Call c;
+    return run_one(prepare_eligibility(increments, flags, convention, gamma, lambda, num_envs, T,
+                                       traces, &c),
+                   c, stream);
 }
 
 rlca_status rlca_episodic_prefix_sum(const void *x, rlca_dtype dtype, const uint8_t *flags,
                                      rlca_reset_convention convention, int64_t num_envs,
                                      int64_t T, void *out, hipStream_t stream) {
-    if (dtype != RLCA_F32 && dtype != RLCA_I32) return RLCA_ERR_INVALID_VALUE;
-    return run_forward(x, dtype == RLCA_I32, flags, convention, 1.0f, num_envs, T, out, stream);
+    Call c;
+    return run_one(prepare_prefix_sum(x, dtype, flags, convention, num_envs, T, out, &c), c,
+                   stream);
 }
 
 rlca_status rlca_affine_scan(const float *alpha, const float *beta, const float *carry,
                              rlca_direction direction, int64_t num_envs, int64_t T, float *out,
                              hipStream_t stream) {
-    if (direction != RLCA_BACKWARD && direction != RLCA_FORWARD) return RLCA_ERR_INVALID_VALUE;
-    int64_t n;
-    rlca_status st = check_sizes(num_envs, T, &n);
-    if (st != RLCA_OK || n == 0) return st;
-    if (alpha == nullptr || beta == nullptr || out == nullptr) return RLCA_ERR_NULL_POINTER;
-    const void *al[] = {alpha, beta, carry, out};
-    st = check_aligned4(al, 4);
-    if (st != RLCA_OK) return st;
-    const Span ins[] = {{alpha, (size_t)n * 4}, {beta, (size_t)n * 4}, {carry, (size_t)num_envs * 4}};
-    const Span os[] = {{out, (size_t)n * 4}};
-    st = check_aliasing(os, 1, ins, 3);
-    if (st != RLCA_OK) return st;
-    if (direction == RLCA_BACKWARD) {
-        BackwardParams p = backward_params(num_envs);
-        p.rewards = alpha;
-        p.values = beta;
-        p.bootstrap = carry;
-        p.out0 = out;
-        return run_backward(kAffineBackward, p, T, stream);
+    Call c;
+    return run_one(prepare_affine(alpha, beta, carry, direction, num_envs, T, out, &c), c,
+                   stream);
+}
+
+rlca_status rlca_run_batch(const rlca_call *calls, int count, hipStream_t stream) {
+    if (count < 0 || count > RLCA_MAX_BATCH) return RLCA_ERR_INVALID_SIZE;
+    if (count > 0 && calls == nullptr) return RLCA_ERR_NULL_POINTER;
+    Call prepared[RLCA_MAX_BATCH];
+    for (int i = 0; i < count; ++i) {
+        const rlca_status st = prepare_op(calls[i], &prepared[i]);
+        if (st != RLCA_OK) return st;
     }
-    const void *f32[] = {alpha, beta, out};
-    const LaunchShape s = choose_shape(num_envs, T, vec_ok(T, f32, 3, nullptr, 0));
-    ForwardParams p = {};
-    p.x = alpha;
-    p.beta = beta;
-    p.carry = carry;
-    p.out = out;
-    p.geo.num_envs = num_envs;
-    p.geo.T = (uint32_t)T;
-    return launch_affine_forward(p, s, stream);
+    // The calls run concurrently: no call may write what another reads or writes.
+    for (int i = 0; i < count; ++i) {
+        for (int j = 0; j < count; ++j) {
+            if (i == j || prepared[i].empty || prepared[j].empty) continue;
+            const Call &a = prepared[i], &b = prepared[j];
+            for (int o = 0; o < a.nout; ++o) {
+                for (int k = 0; k < b.nin; ++k)
+                    if (overlaps(a.outs[o].p, a.outs[o].bytes, b.ins[k].p, b.ins[k].bytes))
+                        return RLCA_ERR_ALIASING;
+                for (int k = 0; k < b.nout; ++k)
+                    if (overlaps(a.outs[o].p, a.outs[o].bytes, b.outs[k].p, b.outs[k].bytes))
+                        return RLCA_ERR_ALIASING;
+            }
+        }
+    }
+    // Vector-path, single-launch calls share grouped launches; the rest
+    // (unaligned or chunked) are enqueued one by one.
+    GroupedArgs group;
+    group.count = 0;
+    group.first_group[0] = 0;
+    for (int i = 0; i < count; ++i) {
+        Call &c = prepared[i];
+        if (c.empty) continue;
+        uint32_t groups = 0;
+        GroupedCall member;
+        if (c.shape.vec && !c.shape.chunked) member = grouped_member(c, &groups);
+        if (!c.shape.vec || c.shape.chunked || groups > kMaxGrid) {
+            const rlca_status st = launch_call(c, stream);
+            if (st != RLCA_OK) return st;
+            continue;
+        }
+        if (group.count == kMaxGroupedCalls || group.first_group[group.count] + groups > kMaxGrid) {
+            const rlca_status st = launch_grouped(group, stream);
+            if (st != RLCA_OK) return st;
+            group.count = 0;
+        }
+        group.calls[group.count] = member;
+        group.first_group[group.count + 1] = group.first_group[group.count] + groups;
+        ++group.count;
+    }
+    return group.count > 0 ? launch_grouped(group, stream) : RLCA_OK;
 }
 
 const char *rlca_status_string(rlca_status status) {

@@ -8,6 +8,7 @@ raises instead of degrading.
 from __future__ import annotations
 
 import ctypes
+import inspect
 import os
 from typing import Optional
 
@@ -34,6 +35,24 @@ _f = ctypes.c_float
 _i64 = ctypes.c_int64
 _i = ctypes.c_int
 
+
+class RlcaCall(ctypes.Structure):
+    """One call of a batch (rlca_call in include/rlca.h)."""
+
+    _fields_ = [
+        ("op", ctypes.c_int), ("num_envs", ctypes.c_int64), ("T", ctypes.c_int64),
+        ("rewards", _p), ("values", _p), ("expected_q", _p), ("behaviour_logp", _p),
+        ("target_logp", _p), ("terminated", _p), ("truncated", _p), ("trunc_values", _p),
+        ("bootstrap", _p), ("gamma", _f), ("lambda_", _f), ("rho_bar", _f), ("c_bar", _f),
+        ("convention", ctypes.c_int), ("dtype", ctypes.c_int), ("direction", ctypes.c_int),
+        ("out0", _p), ("out1", _p),
+    ]
+
+
+OP_GAE, OP_TD_LAMBDA, OP_DISCOUNTED, OP_VTRACE, OP_RETRACE, OP_TRACES, OP_PREFIX_SUM, \
+    OP_AFFINE = range(8)
+MAX_BATCH = 64
+
 # name -> argument types, in the order of include/rlca.h
 SIGNATURES = {
     "rlca_gae": [_p, _p, _p, _p, _p, _p, _f, _f, _i64, _i64, _p, _p, _p],
@@ -44,6 +63,7 @@ SIGNATURES = {
     "rlca_eligibility_traces": [_p, _p, _i, _f, _f, _i64, _i64, _p, _p],
     "rlca_episodic_prefix_sum": [_p, _i, _p, _i, _i64, _i64, _p, _p],
     "rlca_affine_scan": [_p, _p, _p, _i, _i64, _i64, _p, _p],
+    "rlca_run_batch": [ctypes.POINTER(RlcaCall), _i, _p],
 }
 
 _lib = None
@@ -78,10 +98,6 @@ def lib():
 def _check(status: int, fn: str):
     if status != RLCA_OK:
         raise RlcaError(status, fn)
-
-
-def _stream(t: torch.Tensor) -> int:
-    return torch.cuda.current_stream(t.device).cuda_stream
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -131,52 +147,61 @@ def _out(out, shape, dev, dtype=torch.float32, name="out"):
     return _steps(name, out, shape, dtype, dev)
 
 
-def gae(rewards, values, terminated, truncated=None, trunc_values=None, bootstrap=None,
-        gamma=0.99, lam=0.95, with_returns=True, advantages=None, returns=None):
-    """GAE advantages (and value targets adv + V).  Returns (advantages, returns|None)."""
+class _Prepared:
+    """One checked call: its op, shape and device, the rlca_call fields it sets
+    (tensors for pointers), and the output tensor(s) handed back to the caller."""
+
+    __slots__ = ("op", "shape", "dev", "fields", "result")
+
+    def __init__(self, op, shape, dev, result, **fields):
+        self.op, self.shape, self.dev, self.result, self.fields = op, shape, dev, result, fields
+
+    def arg(self, name, default=None):
+        v = self.fields.get(name, default)
+        return _ptr(v) if isinstance(v, torch.Tensor) else v
+
+    def stream(self):
+        return torch.cuda.current_stream(self.dev).cuda_stream
+
+
+def _prepare_gae(rewards, values, terminated, truncated=None, trunc_values=None, bootstrap=None,
+                 gamma=0.99, lam=0.95, with_returns=True, advantages=None, returns=None):
     shape, dev = _rollout_shape(rewards)
     r = _steps("rewards", rewards, shape, torch.float32, dev)
     v = _steps("values", values, shape, torch.float32, dev)
     term, trunc, tv, boot = _boundary(terminated, truncated, trunc_values, bootstrap, shape, dev)
     adv = _out(advantages, shape, dev, name="advantages")
     ret = _out(returns, shape, dev, name="returns") if with_returns else None
-    _check(lib().rlca_gae(_ptr(r), _ptr(v), _ptr(term), _ptr(trunc), _ptr(tv), _ptr(boot),
-                          gamma, lam, shape[0], shape[1], _ptr(adv), _ptr(ret), _stream(r)),
-           "rlca_gae")
-    return adv, ret
+    return _Prepared(OP_GAE, shape, dev, (adv, ret), rewards=r, values=v, terminated=term,
+                     truncated=trunc, trunc_values=tv, bootstrap=boot, gamma=gamma, lambda_=lam,
+                     out0=adv, out1=ret)
 
 
-def td_lambda(rewards, values, terminated, truncated=None, trunc_values=None, bootstrap=None,
-              gamma=0.99, lam=0.95, out=None):
-    """TD(lambda) returns."""
+def _prepare_td_lambda(rewards, values, terminated, truncated=None, trunc_values=None,
+                       bootstrap=None, gamma=0.99, lam=0.95, out=None):
     shape, dev = _rollout_shape(rewards)
     r = _steps("rewards", rewards, shape, torch.float32, dev)
     v = _steps("values", values, shape, torch.float32, dev)
     term, trunc, tv, boot = _boundary(terminated, truncated, trunc_values, bootstrap, shape, dev)
     g = _out(out, shape, dev)
-    _check(lib().rlca_td_lambda(_ptr(r), _ptr(v), _ptr(term), _ptr(trunc), _ptr(tv), _ptr(boot),
-                                gamma, lam, shape[0], shape[1], _ptr(g), _stream(r)),
-           "rlca_td_lambda")
-    return g
+    return _Prepared(OP_TD_LAMBDA, shape, dev, g, rewards=r, values=v, terminated=term,
+                     truncated=trunc, trunc_values=tv, bootstrap=boot, gamma=gamma, lambda_=lam,
+                     out0=g)
 
 
-def discounted_returns(rewards, terminated, truncated=None, trunc_values=None, bootstrap=None,
-                       gamma=0.99, out=None):
-    """Discounted returns (Monte-Carlo when bootstrap is None)."""
+def _prepare_discounted_returns(rewards, terminated, truncated=None, trunc_values=None,
+                                bootstrap=None, gamma=0.99, out=None):
     shape, dev = _rollout_shape(rewards)
     r = _steps("rewards", rewards, shape, torch.float32, dev)
     term, trunc, tv, boot = _boundary(terminated, truncated, trunc_values, bootstrap, shape, dev)
     g = _out(out, shape, dev)
-    _check(lib().rlca_discounted_returns(_ptr(r), _ptr(term), _ptr(trunc), _ptr(tv), _ptr(boot),
-                                         gamma, shape[0], shape[1], _ptr(g), _stream(r)),
-           "rlca_discounted_returns")
-    return g
+    return _Prepared(OP_DISCOUNTED, shape, dev, g, rewards=r, terminated=term, truncated=trunc,
+                     trunc_values=tv, bootstrap=boot, gamma=gamma, out0=g)
 
 
-def vtrace(rewards, values, behaviour_logp, target_logp, terminated, truncated=None,
-           trunc_values=None, bootstrap=None, gamma=0.99, lam=1.0, rho_bar=1.0, c_bar=1.0,
-           with_pg=True, vs=None, pg_advantages=None):
-    """V-Trace targets and policy-gradient advantages.  Returns (vs, pg|None)."""
+def _prepare_vtrace(rewards, values, behaviour_logp, target_logp, terminated, truncated=None,
+                    trunc_values=None, bootstrap=None, gamma=0.99, lam=1.0, rho_bar=1.0,
+                    c_bar=1.0, with_pg=True, vs=None, pg_advantages=None):
     shape, dev = _rollout_shape(rewards)
     r = _steps("rewards", rewards, shape, torch.float32, dev)
     v = _steps("values", values, shape, torch.float32, dev)
@@ -185,16 +210,15 @@ def vtrace(rewards, values, behaviour_logp, target_logp, terminated, truncated=N
     term, trunc, tv, boot = _boundary(terminated, truncated, trunc_values, bootstrap, shape, dev)
     o_vs = _out(vs, shape, dev, name="vs")
     o_pg = _out(pg_advantages, shape, dev, name="pg_advantages") if with_pg else None
-    _check(lib().rlca_vtrace(_ptr(r), _ptr(v), _ptr(mu), _ptr(pi), _ptr(term), _ptr(trunc),
-                             _ptr(tv), _ptr(boot), gamma, lam, rho_bar, c_bar, shape[0],
-                             shape[1], _ptr(o_vs), _ptr(o_pg), _stream(r)), "rlca_vtrace")
-    return o_vs, o_pg
+    return _Prepared(OP_VTRACE, shape, dev, (o_vs, o_pg), rewards=r, values=v,
+                     behaviour_logp=mu, target_logp=pi, terminated=term, truncated=trunc,
+                     trunc_values=tv, bootstrap=boot, gamma=gamma, lambda_=lam, rho_bar=rho_bar,
+                     c_bar=c_bar, out0=o_vs, out1=o_pg)
 
 
-def retrace(rewards, q_values, expected_q, behaviour_logp, target_logp, terminated,
-            truncated=None, trunc_values=None, bootstrap=None, gamma=0.99, lam=0.95,
-            c_bar=1.0, out=None):
-    """Retrace(lambda) targets Q^ret."""
+def _prepare_retrace(rewards, q_values, expected_q, behaviour_logp, target_logp, terminated,
+                     truncated=None, trunc_values=None, bootstrap=None, gamma=0.99, lam=0.95,
+                     c_bar=1.0, out=None):
     shape, dev = _rollout_shape(rewards)
     r = _steps("rewards", rewards, shape, torch.float32, dev)
     q = _steps("q_values", q_values, shape, torch.float32, dev)
@@ -203,27 +227,23 @@ def retrace(rewards, q_values, expected_q, behaviour_logp, target_logp, terminat
     pi = _steps("target_logp", target_logp, shape, torch.float32, dev)
     term, trunc, tv, boot = _boundary(terminated, truncated, trunc_values, bootstrap, shape, dev)
     o = _out(out, shape, dev)
-    _check(lib().rlca_retrace(_ptr(r), _ptr(q), _ptr(eq), _ptr(mu), _ptr(pi), _ptr(term),
-                              _ptr(trunc), _ptr(tv), _ptr(boot), gamma, lam, c_bar, shape[0],
-                              shape[1], _ptr(o), _stream(r)), "rlca_retrace")
-    return o
+    return _Prepared(OP_RETRACE, shape, dev, o, rewards=r, values=q, expected_q=eq,
+                     behaviour_logp=mu, target_logp=pi, terminated=term, truncated=trunc,
+                     trunc_values=tv, bootstrap=boot, gamma=gamma, lambda_=lam, c_bar=c_bar,
+                     out0=o)
 
 
-def eligibility_traces(increments, flags, convention=RESET_ON_START, gamma=0.99, lam=0.9,
-                       out=None):
-    """Accumulating eligibility traces, forward in time."""
+def _prepare_eligibility_traces(increments, flags, convention=RESET_ON_START, gamma=0.99,
+                                lam=0.9, out=None):
     shape, dev = _rollout_shape(increments)
     x = _steps("increments", increments, shape, torch.float32, dev)
     f = _steps("flags", flags, shape, "flag", dev)
     o = _out(out, shape, dev)
-    _check(lib().rlca_eligibility_traces(_ptr(x), _ptr(f), int(convention), gamma, lam,
-                                         shape[0], shape[1], _ptr(o), _stream(x)),
-           "rlca_eligibility_traces")
-    return o
+    return _Prepared(OP_TRACES, shape, dev, o, rewards=x, terminated=f,
+                     convention=int(convention), gamma=gamma, lambda_=lam, out0=o)
 
 
-def episodic_prefix_sum(x, flags, convention=RESET_ON_START, out=None):
-    """Inclusive segmented prefix sum over float32 or int32 input (int32 wraps)."""
+def _prepare_episodic_prefix_sum(x, flags, convention=RESET_ON_START, out=None):
     shape, dev = _rollout_shape(x)
     if x.dtype == torch.float32:
         dtype = RLCA_F32
@@ -234,20 +254,175 @@ def episodic_prefix_sum(x, flags, convention=RESET_ON_START, out=None):
     xs = _steps("x", x, shape, x.dtype, dev)
     f = _steps("flags", flags, shape, "flag", dev)
     o = _out(out, shape, dev, dtype=x.dtype)
-    _check(lib().rlca_episodic_prefix_sum(_ptr(xs), dtype, _ptr(f), int(convention), shape[0],
-                                          shape[1], _ptr(o), _stream(xs)),
-           "rlca_episodic_prefix_sum")
-    return o
+    return _Prepared(OP_PREFIX_SUM, shape, dev, o, rewards=xs, terminated=f,
+                     convention=int(convention), dtype=dtype, out0=o)
 
 
-def affine_scan(alpha, beta, carry=None, direction=BACKWARD, out=None):
-    """A_t = alpha_t + beta_t * A_{t+1} (BACKWARD, A_T = carry) or
-    A_t = alpha_t + beta_t * A_{t-1} (FORWARD, A_{-1} = carry), float32."""
+def _prepare_affine_scan(alpha, beta, carry=None, direction=BACKWARD, out=None):
     shape, dev = _rollout_shape(alpha)
     a = _steps("alpha", alpha, shape, torch.float32, dev)
     b = _steps("beta", beta, shape, torch.float32, dev)
     c = _steps("carry", carry, shape[:1], torch.float32, dev, optional=True)
     o = _out(out, shape, dev)
-    _check(lib().rlca_affine_scan(_ptr(a), _ptr(b), _ptr(c), int(direction), shape[0], shape[1],
-                                  _ptr(o), _stream(a)), "rlca_affine_scan")
-    return o
+    return _Prepared(OP_AFFINE, shape, dev, o, rewards=a, values=b, bootstrap=c,
+                     direction=int(direction), out0=o)
+
+
+def _takes_args_of(prepare):
+    """Give a wrapper the signature of the _prepare_* function it forwards to."""
+    def deco(fn):
+        fn.__signature__ = inspect.signature(prepare)
+        return fn
+    return deco
+
+
+@_takes_args_of(_prepare_gae)
+def gae(*args, **kwargs):
+    """GAE advantages (and value targets adv + V).  Returns (advantages, returns|None)."""
+    p = _prepare_gae(*args, **kwargs)
+    _check(lib().rlca_gae(p.arg("rewards"), p.arg("values"), p.arg("terminated"),
+                          p.arg("truncated"), p.arg("trunc_values"), p.arg("bootstrap"),
+                          p.arg("gamma"), p.arg("lambda_"), *p.shape, p.arg("out0"),
+                          p.arg("out1"), p.stream()), "rlca_gae")
+    return p.result
+
+
+@_takes_args_of(_prepare_td_lambda)
+def td_lambda(*args, **kwargs):
+    """TD(lambda) returns."""
+    p = _prepare_td_lambda(*args, **kwargs)
+    _check(lib().rlca_td_lambda(p.arg("rewards"), p.arg("values"), p.arg("terminated"),
+                                p.arg("truncated"), p.arg("trunc_values"), p.arg("bootstrap"),
+                                p.arg("gamma"), p.arg("lambda_"), *p.shape, p.arg("out0"),
+                                p.stream()), "rlca_td_lambda")
+    return p.result
+
+
+@_takes_args_of(_prepare_discounted_returns)
+def discounted_returns(*args, **kwargs):
+    """Discounted returns (Monte-Carlo when bootstrap is None)."""
+    p = _prepare_discounted_returns(*args, **kwargs)
+    _check(lib().rlca_discounted_returns(p.arg("rewards"), p.arg("terminated"),
+                                         p.arg("truncated"), p.arg("trunc_values"),
+                                         p.arg("bootstrap"), p.arg("gamma"), *p.shape,
+                                         p.arg("out0"), p.stream()), "rlca_discounted_returns")
+    return p.result
+
+
+@_takes_args_of(_prepare_vtrace)
+def vtrace(*args, **kwargs):
+    """V-Trace targets and policy-gradient advantages.  Returns (vs, pg|None)."""
+    p = _prepare_vtrace(*args, **kwargs)
+    _check(lib().rlca_vtrace(p.arg("rewards"), p.arg("values"), p.arg("behaviour_logp"),
+                             p.arg("target_logp"), p.arg("terminated"), p.arg("truncated"),
+                             p.arg("trunc_values"), p.arg("bootstrap"), p.arg("gamma"),
+                             p.arg("lambda_"), p.arg("rho_bar"), p.arg("c_bar"), *p.shape,
+                             p.arg("out0"), p.arg("out1"), p.stream()), "rlca_vtrace")
+    return p.result
+
+
+@_takes_args_of(_prepare_retrace)
+def retrace(*args, **kwargs):
+    """Retrace(lambda) targets Q^ret."""
+    p = _prepare_retrace(*args, **kwargs)
+    _check(lib().rlca_retrace(p.arg("rewards"), p.arg("values"), p.arg("expected_q"),
+                              p.arg("behaviour_logp"), p.arg("target_logp"),
+                              p.arg("terminated"), p.arg("truncated"), p.arg("trunc_values"),
+                              p.arg("bootstrap"), p.arg("gamma"), p.arg("lambda_"),
+                              p.arg("c_bar"), *p.shape, p.arg("out0"), p.stream()),
+           "rlca_retrace")
+    return p.result
+
+
+@_takes_args_of(_prepare_eligibility_traces)
+def eligibility_traces(*args, **kwargs):
+    """Accumulating eligibility traces, forward in time."""
+    p = _prepare_eligibility_traces(*args, **kwargs)
+    _check(lib().rlca_eligibility_traces(p.arg("rewards"), p.arg("terminated"),
+                                         p.arg("convention"), p.arg("gamma"),
+                                         p.arg("lambda_"), *p.shape, p.arg("out0"),
+                                         p.stream()), "rlca_eligibility_traces")
+    return p.result
+
+
+@_takes_args_of(_prepare_episodic_prefix_sum)
+def episodic_prefix_sum(*args, **kwargs):
+    """Inclusive segmented prefix sum over float32 or int32 input (int32 wraps)."""
+    p = _prepare_episodic_prefix_sum(*args, **kwargs)
+    _check(lib().rlca_episodic_prefix_sum(p.arg("rewards"), p.arg("dtype"), p.arg("terminated"),
+                                          p.arg("convention"), *p.shape, p.arg("out0"),
+                                          p.stream()), "rlca_episodic_prefix_sum")
+    return p.result
+
+
+@_takes_args_of(_prepare_affine_scan)
+def affine_scan(*args, **kwargs):
+    """A_t = alpha_t + beta_t * A_{t+1} (BACKWARD, A_T = carry) or
+    A_t = alpha_t + beta_t * A_{t-1} (FORWARD, A_{-1} = carry), float32."""
+    p = _prepare_affine_scan(*args, **kwargs)
+    _check(lib().rlca_affine_scan(p.arg("rewards"), p.arg("values"), p.arg("bootstrap"),
+                                  p.arg("direction"), *p.shape, p.arg("out0"), p.stream()),
+           "rlca_affine_scan")
+    return p.result
+
+
+def _recorder(prepare):
+    def record(self, *args, **kwargs):
+        return self._add(prepare(*args, **kwargs))
+    record.__name__ = prepare.__name__[len("_prepare_"):]
+    params = list(inspect.signature(prepare).parameters.values())
+    record.__signature__ = inspect.Signature(
+        [inspect.Parameter("self", inspect.Parameter.POSITIONAL_OR_KEYWORD)] + params)
+    record.__doc__ = (f"Record a {record.__name__} call (arguments as for the function of "
+                      "that name); returns its output tensor(s), filled once run() has been "
+                      "enqueued.")
+    return record
+
+
+class Batch:
+    """Calls recorded here are enqueued together by run() through
+    rlca_run_batch: calls on the vector path share grouped launches (up to 16
+    calls per launch), the rest run one launch each.  Each recording method
+    checks its arguments like the function of the same name.  No call may
+    write what another call of the batch reads or writes (rlca_run_batch
+    rejects that), so the calls of one batch are independent."""
+
+    def __init__(self):
+        self._calls = []
+        self._keep = []
+        self._device = None
+
+    def _add(self, p: _Prepared):
+        if self._device is None:
+            self._device = p.dev
+        elif p.dev != self._device:
+            raise ValueError("all calls of a batch must be on one device")
+        if len(self._calls) >= MAX_BATCH:
+            raise ValueError(f"a batch holds at most {MAX_BATCH} calls")
+        c = RlcaCall(op=p.op, num_envs=p.shape[0], T=p.shape[1])
+        for name in p.fields:
+            setattr(c, name, p.arg(name))
+        self._calls.append(c)
+        self._keep.extend(v for v in p.fields.values() if isinstance(v, torch.Tensor))
+        return p.result
+
+    def __len__(self):
+        return len(self._calls)
+
+    gae = _recorder(_prepare_gae)
+    td_lambda = _recorder(_prepare_td_lambda)
+    discounted_returns = _recorder(_prepare_discounted_returns)
+    vtrace = _recorder(_prepare_vtrace)
+    retrace = _recorder(_prepare_retrace)
+    eligibility_traces = _recorder(_prepare_eligibility_traces)
+    episodic_prefix_sum = _recorder(_prepare_episodic_prefix_sum)
+    affine_scan = _recorder(_prepare_affine_scan)
+
+    def run(self):
+        """Enqueue every recorded call on the current stream of their device.
+        The batch can be run again; its output tensors are rewritten."""
+        if not self._calls:
+            return
+        arr = (RlcaCall * len(self._calls))(*self._calls)
+        stream = torch.cuda.current_stream(self._device).cuda_stream
+        _check(lib().rlca_run_batch(arr, len(self._calls), stream), "rlca_run_batch")

@@ -131,3 +131,67 @@ def test_aliasing_errors(lib):
     assert lib.rlca_affine_scan(A, B, C, 0, n, t, C - 8, None) == ALIAS     # over the carry
     assert lib.rlca_affine_scan(A, B, None, 1, n, t, B + 4, None) == ALIAS
     assert lib.rlca_affine_scan(A + 2, B, None, 1, n, t, C, None) == MISAL
+
+
+def call(op=0, n=4, t=8, **fields):
+    c = binding.RlcaCall(op=op, num_envs=n, T=t, gamma=0.99, lambda_=0.95, rho_bar=1.0,
+                         c_bar=1.0)
+    if op in (binding.OP_GAE, binding.OP_TD_LAMBDA):
+        c.rewards, c.values, c.terminated, c.out0 = A, B, C, D
+    for k, v in fields.items():
+        setattr(c, k, v)
+    return c
+
+
+def run_batch(lib, *calls, count=None):
+    arr = (binding.RlcaCall * max(len(calls), 1))(*calls)
+    return lib.rlca_run_batch(arr, len(calls) if count is None else count, None)
+
+
+def test_batch_struct_matches_header():
+    # rlca_call: int op; two int64; nine pointers; four floats; three ints; two pointers
+    assert ctypes.sizeof(binding.RlcaCall) == 144
+    assert binding.RlcaCall.out0.offset == 128 and binding.RlcaCall.gamma.offset == 96
+    text = open(HEADER).read()
+    assert re.search(r"#define\s+RLCA_MAX_BATCH\s+64\b", text)
+    assert binding.MAX_BATCH == 64
+
+
+def test_batch_count_and_null(lib):
+    assert lib.rlca_run_batch(None, 0, None) == OK
+    assert lib.rlca_run_batch(None, 1, None) == NULLP
+    assert run_batch(lib, call(), count=-1) == SIZE
+    assert run_batch(lib, *[call(n=0)] * 65) == SIZE
+    assert run_batch(lib, *[call(n=0)] * 64) == OK          # all empty: nothing launched
+
+
+def test_batch_rejects_before_launching_anything(lib):
+    # the first call is valid on its own; the batch fails on a later one, and
+    # since every call is checked before the first launch nothing runs
+    assert run_batch(lib, call(), call(op=99)) == VALUE
+    assert run_batch(lib, call(), call(gamma=1.5, rewards=E, values=F, terminated=G,
+                                       out0=H)) == VALUE
+    assert run_batch(lib, call(), call(t=-1)) == SIZE
+    assert run_batch(lib, call(), call(values=None)) == NULLP
+    assert run_batch(lib, call(), call(rewards=A + 2)) == MISAL
+    assert run_batch(lib, call(), call(out0=A)) == ALIAS    # aliasing within the call
+    affine = call(op=binding.OP_AFFINE, rewards=A, values=B, direction=3, out0=C)
+    assert run_batch(lib, affine) == VALUE
+    prefix = call(op=binding.OP_PREFIX_SUM, rewards=A, terminated=B, dtype=7, out0=C)
+    assert run_batch(lib, prefix) == VALUE
+
+
+def test_batch_cross_call_aliasing(lib):
+    n, t = 4, 8
+    first = call(out0=D, out1=E)
+    # a second call reading the first call's output
+    assert run_batch(lib, first, call(op=1, rewards=E + 4, values=F, terminated=G,
+                                      out0=H)) == ALIAS
+    # ... or writing the first call's input
+    assert run_batch(lib, first, call(op=1, rewards=F, values=G, terminated=H,
+                                      out0=C)) == ALIAS
+    # ... or both writing one buffer, in either order
+    assert run_batch(lib, call(op=1, rewards=F, values=G, terminated=H, out0=D + n * t * 4 - 4),
+                     first) == ALIAS
+    # an empty call is exempt
+    assert run_batch(lib, call(n=0, out0=A), call(n=0, rewards=D)) == OK
