@@ -368,7 +368,7 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
     constexpr bool kFlags = EST != kAffineBackward;
     __shared__ float lds_a[2 * NW], lds_b[2 * NW];
     const int lane = threadIdx.x & (kWave - 1);
-    const int w = threadIdx.x / kWave;
+    const int w = NW == 1 ? 0 : threadIdx.x / kWave;  // one-wave tiles: each wave alone
     const uint32_t chunk = (NW - 1 - w) * kWave + (kWave - 1 - lane);
     const uint32_t T = p.geo.T;
     const float gamma = p.gamma;
@@ -590,7 +590,7 @@ __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint3
     constexpr uint32_t kTile = NW * kWave * kK;
     __shared__ V lds_a[2 * NW], lds_b[2 * NW];
     const int lane = threadIdx.x & (kWave - 1);
-    const int w = threadIdx.x / kWave;
+    const int w = NW == 1 ? 0 : threadIdx.x / kWave;  // one-wave tiles: each wave alone
     const uint32_t chunk = w * kWave + lane;
     const uint32_t T = p.geo.T;
     const V decay = __builtin_bit_cast(V, __builtin_bit_cast(uint32_t, p.decay));
@@ -872,39 +872,54 @@ rlca_status launch_forward_variant(ForwardParams &p, const LaunchShape &s, hipSt
 }
 
 // ------------------------------------------------------------- grouped launch
-// Several calls in one launch: workgroup b runs group b - first_group[c] of
-// call c, where c is the call whose group range holds b.  Every member uses
-// the vector path, full mode and 8-wave workgroups; `variant` names the
-// estimator body.  The argument block travels in the kernel arguments.
+// Several calls in one launch of 8-wave workgroups.  Call c owns the
+// workgroups [end(c-1), end(c)); each runs one group of an 8-wave call, or
+// eight groups of a one-wave call (one per wave).  Every member uses the
+// vector path and full mode; `variant` names the estimator body and wave
+// count.  The 14 head words come first among the kernel arguments, which
+// the launch preloads into SGPRs: bits 0..23 of word i hold end(i) (unused
+// calls: kHeadEndMask, above any workgroup index), bits 24..31 the variant
+// of call i.  A workgroup finds its call and variant without a memory load
+// and then fetches only that call's parameters.
 constexpr int kGroupWaves = 8;
-constexpr int kMaxGroupedCalls = 16;
+constexpr int kMaxGroupedCalls = 14;
+constexpr uint32_t kHeadEndMask = 0xffffffu;
+constexpr int kHeadVariantShift = 24;
 
-struct GroupedCall {
-    int variant;
-    union {
-        BackwardParams b;
-        ForwardParams f;
-    };
+union GroupedCall {
+    BackwardParams b;
+    ForwardParams f;
 };
 
 struct GroupedArgs {
-    int count;
-    uint32_t first_group[kMaxGroupedCalls + 1];
     GroupedCall calls[kMaxGroupedCalls];
 };
 
-// Variant numbering: backward estimators 0..23 (estimator x truncation x
-// wave-local), flag-driven forward scans 24..31 (int32 x after-done x
-// wave-local), the forward affine scan 32..33.
-constexpr int grouped_backward_variant(int est, bool trunc, bool wave_local) {
-    return est * 4 + (trunc ? 2 : 0) + (wave_local ? 1 : 0);
-}
-constexpr int grouped_forward_variant(bool is_int, bool after_done, bool wave_local) {
-    return 24 + (is_int ? 4 : 0) + (after_done ? 2 : 0) + (wave_local ? 1 : 0);
-}
-constexpr int grouped_affine_forward_variant(bool wave_local) { return 32 + (wave_local ? 1 : 0); }
+struct GroupedLaunch {
+    uint32_t head[kMaxGroupedCalls];
+    GroupedArgs args;
+    uint32_t workgroups;  // end of the last call's range
+};
 
-rlca_status launch_grouped(const GroupedArgs &args, hipStream_t stream);
+// Variant numbering.  8-wave bodies: backward estimators 0..21 (estimator x
+// truncation x wave-local), flag-driven forward scans 24..31 (int32 x
+// after-done x wave-local), forward affine scan 32..33.  One-wave bodies
+// (never wave-local): backward 34..44 (estimator x truncation), forward
+// 46..49 (int32 x after-done), forward affine 50.
+constexpr int grouped_backward_variant(int est, bool trunc, bool wave_local, bool one_wave) {
+    return one_wave ? 34 + est * 2 + (trunc ? 1 : 0)
+                    : est * 4 + (trunc ? 2 : 0) + (wave_local ? 1 : 0);
+}
+constexpr int grouped_forward_variant(bool is_int, bool after_done, bool wave_local,
+                                      bool one_wave) {
+    return one_wave ? 46 + (is_int ? 2 : 0) + (after_done ? 1 : 0)
+                    : 24 + (is_int ? 4 : 0) + (after_done ? 2 : 0) + (wave_local ? 1 : 0);
+}
+constexpr int grouped_affine_forward_variant(bool wave_local, bool one_wave) {
+    return one_wave ? 50 : 32 + (wave_local ? 1 : 0);
+}
+
+rlca_status launch_grouped(const GroupedLaunch &launch, hipStream_t stream);
 
 // One translation unit per estimator instantiates these (see est_*.hip).
 rlca_status launch_gae(BackwardParams &p, const LaunchShape &s, hipStream_t stream);

@@ -248,25 +248,30 @@ static rlca_status launch_call(Call &c, hipStream_t stream) {
                     : launch_forward_f32(c.fp, c.after_done, c.shape, stream);
 }
 
-// The call as one member of a grouped launch (vector path, full mode, 8 waves).
-static GroupedCall grouped_member(const Call &c, uint32_t *groups) {
-    GroupedCall g;
-    uint32_t grid;
-    const bool wl = c.shape.wave_local;
+// The call as one member of a grouped launch, or false where it cannot be one.
+static bool grouped_member(const Call &c, GroupedCall *g, int *variant, uint32_t *workgroups) {
+    // Grouped launches run 8-wave workgroups: calls shaped for 8 waves take
+    // one workgroup per group, one-wave calls one wave per group.  Both keep
+    // the geometry of their own launch, so results match it bit for bit.
+    if (!c.shape.vec || c.shape.chunked || (c.shape.waves != 1 && c.shape.waves != kGroupWaves))
+        return false;
+    const bool wl = c.shape.wave_local, one = c.shape.waves == 1;
+    uint32_t grid, groups;
     if (c.backward) {
-        g.b = c.bp;
-        g.b.geo = make_geometry(c.bp.geo.num_envs, c.bp.geo.T, kGroupWaves, false, &grid);
-        g.variant = grouped_backward_variant(c.est, c.bp.truncated != nullptr, wl);
-        *groups = g.b.geo.num_groups;
+        g->b = c.bp;
+        g->b.geo = make_geometry(c.bp.geo.num_envs, c.bp.geo.T, c.shape.waves, false, &grid);
+        *variant = grouped_backward_variant(c.est, c.bp.truncated != nullptr, wl, one);
+        groups = g->b.geo.num_groups;
     } else {
-        g.f = c.fp;
-        g.f.geo = make_geometry(c.fp.geo.num_envs, c.fp.geo.T, kGroupWaves, false, &grid);
-        g.variant = c.forward == kForwardAffine
-                        ? grouped_affine_forward_variant(wl)
-                        : grouped_forward_variant(c.is_int, c.after_done, wl);
-        *groups = g.f.geo.num_groups;
+        g->f = c.fp;
+        g->f.geo = make_geometry(c.fp.geo.num_envs, c.fp.geo.T, c.shape.waves, false, &grid);
+        *variant = c.forward == kForwardAffine
+                       ? grouped_affine_forward_variant(wl, one)
+                       : grouped_forward_variant(c.is_int, c.after_done, wl, one);
+        groups = g->f.geo.num_groups;
     }
-    return g;
+    *workgroups = one ? (groups + kGroupWaves - 1) / kGroupWaves : groups;
+    return *workgroups <= kMaxGrid;
 }
 
 static rlca_status prepare_gae(const float *rewards, const float *values,
@@ -537,31 +542,42 @@ rlca_status rlca_run_batch(const rlca_call *calls, int count, hipStream_t stream
         }
     }
     // Vector-path, single-launch calls share grouped launches; the rest
-    // (unaligned or chunked) are enqueued one by one.
-    GroupedArgs group;
-    group.count = 0;
-    group.first_group[0] = 0;
+    // (unaligned or chunked) are enqueued one by one.  A grouped launch that
+    // would hold one call runs that call's own kernel instead.
+    GroupedLaunch group;
+    int members[kMaxGroupedCalls];
+    int count_in_group = 0;
+    auto flush = [&]() -> rlca_status {
+        if (count_in_group == 0) return RLCA_OK;
+        const int n = count_in_group;
+        count_in_group = 0;
+        if (n == 1) return launch_call(prepared[members[0]], stream);
+        for (int m = n; m < kMaxGroupedCalls; ++m) group.head[m] = kHeadEndMask;
+        return launch_grouped(group, stream);
+    };
+    group.workgroups = 0;
     for (int i = 0; i < count; ++i) {
         Call &c = prepared[i];
         if (c.empty) continue;
-        uint32_t groups = 0;
         GroupedCall member;
-        if (c.shape.vec && !c.shape.chunked) member = grouped_member(c, &groups);
-        if (!c.shape.vec || c.shape.chunked || groups > kMaxGrid) {
+        int variant = 0;
+        uint32_t wgs = 0;
+        if (!grouped_member(c, &member, &variant, &wgs)) {
             const rlca_status st = launch_call(c, stream);
             if (st != RLCA_OK) return st;
             continue;
         }
-        if (group.count == kMaxGroupedCalls || group.first_group[group.count] + groups > kMaxGrid) {
-            const rlca_status st = launch_grouped(group, stream);
+        if (count_in_group == kMaxGroupedCalls || group.workgroups + wgs > kMaxGrid) {
+            const rlca_status st = flush();
             if (st != RLCA_OK) return st;
-            group.count = 0;
         }
-        group.calls[group.count] = member;
-        group.first_group[group.count + 1] = group.first_group[group.count] + groups;
-        ++group.count;
+        if (count_in_group == 0) group.workgroups = 0;
+        group.workgroups += wgs;
+        group.args.calls[count_in_group] = member;
+        group.head[count_in_group] = group.workgroups | ((uint32_t)variant << kHeadVariantShift);
+        members[count_in_group++] = i;
     }
-    return group.count > 0 ? launch_grouped(group, stream) : RLCA_OK;
+    return flush();
 }
 
 const char *rlca_status_string(rlca_status status) {

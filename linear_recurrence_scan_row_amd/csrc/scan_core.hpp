@@ -106,6 +106,14 @@ __device__ __forceinline__ V block_carry_in(V a, V b, V carry_in, V *lds_a, V *l
         carry_out = V(0);
         return ea + eb * V(0);
     }
+    if constexpr (NW == 1) {
+        // One wave: its total is lane 63's inclusive value; no LDS, no
+        // barrier (so waves of one workgroup may run unrelated tiles).
+        const V ta = from_bits<V>(__builtin_amdgcn_readlane(as_bits(a), kWave - 1));
+        const V tb = from_bits<V>(__builtin_amdgcn_readlane(as_bits(b), kWave - 1));
+        carry_out = ta + tb * carry_in;
+        return ea + eb * carry_in;
+    }
     if (lane == kWave - 1) {
         lds_a[parity * NW + w] = a;
         lds_b[parity * NW + w] = b;

@@ -381,7 +381,7 @@ def _recorder(prepare):
 
 class Batch:
     """Calls recorded here are enqueued together by run() through
-    rlca_run_batch: calls on the vector path share grouped launches (up to 16
+    rlca_run_batch: calls on the vector path share grouped launches (up to 14
     calls per launch), the rest run one launch each.  Each recording method
     checks its arguments like the function of the same name.  No call may
     write what another call of the batch reads or writes (rlca_run_batch

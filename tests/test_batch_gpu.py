@@ -4,12 +4,10 @@ chunked calls).
 
 Every member of a batch is checked against the fp64 oracle to the same bar as
 the single-call tests (|gpu - oracle| <= 1e-4 * (1 + |oracle|), int32 exact),
-and against the single-call entry point.  Grouped launches always use
-eight-wave workgroups; where the single call does too (T <= 256 or T >= 1024),
-or where the batch launches the call on its own (unaligned or chunked), the
-two agree bit for bit.  Rows of 257..1023 steps run one-wave workgroups as a
-single call, so there the scan associates differently and the two agree to
-the parity bar instead.
+and against the single-call entry point bit for bit: a grouped launch runs
+each call with the tile geometry of the call's own launch (one group per
+workgroup for 8-wave shapes, one per wave for one-wave shapes), and calls
+that cannot join one (unaligned, chunked, or alone) run their own kernel.
 """
 import numpy as np
 import pytest
@@ -47,9 +45,6 @@ class Member:
     def __init__(self, op, seed, N, T, device, trunc=True, boot=True, conv=rl.RESET_ON_START,
                  direction=rl.BACKWARD, int_input=False):
         self.op, self.what = op, f"{op} N={N} T={T} seed={seed}"
-        # every member's tensors are fresh, hence 16-byte aligned: T % 4
-        # decides the vector path
-        self.bitwise = T % 4 != 0 or not 256 < T < 1024
         self.device = device
         tr = lambda x: x if trunc else None         # noqa: E731
         bt = lambda x: x if boot else None          # noqa: E731
@@ -123,10 +118,7 @@ class Member:
             else:
                 assert_parity(g, r, f"{self.what} out{k}")
         for k, (g, s) in enumerate(zip(self.outputs(self.out), self.outputs(self.single()))):
-            if self.bitwise:
-                assert torch.equal(g, s), f"{self.what} out{k}: batch and single call differ"
-            else:
-                assert_parity(g, s.cpu().numpy(), f"{self.what} out{k} vs single call")
+            assert torch.equal(g, s), f"{self.what} out{k}: batch and single call differ"
 
 
 def mixed_members(device):
@@ -168,7 +160,7 @@ def test_mixed_batch_matches_oracle_and_single_calls(gpu_device):
 
 
 def test_more_calls_than_one_grouped_launch_holds(gpu_device):
-    # 40 vector-path calls: three grouped launches of at most 16 calls each
+    # 40 vector-path calls: three grouped launches of at most 14 calls each
     ops = ["gae", "td_lambda", "discounted", "vtrace", "retrace", "traces", "prefix", "affine"]
     members = [Member(ops[i % 8], 100 + i, 5 + 7 * i, (64, 128, 256, 512, 1024)[i % 5],
                       gpu_device) for i in range(40)]
@@ -232,3 +224,21 @@ def test_batch_limits_in_the_binding(gpu_device):
     with pytest.raises(ValueError):
         batch.episodic_prefix_sum(x, f)
     rl.Batch().run()                                      # an empty batch is a no-op
+
+
+def test_single_member_and_one_wave_only_batches(gpu_device):
+    # a lone vector-path call runs its own kernel; a batch of one-wave calls
+    # (rows of 257..1023 steps) runs them one group per wave of the grouped
+    # launch, with a partly filled last workgroup (num_groups not a multiple
+    # of 8)
+    for members in ([Member("gae", 40, 64, 128, gpu_device)],
+                    [Member("retrace", 41, 13, 300, gpu_device),
+                     Member("traces", 42, 21, 1020, gpu_device),
+                     Member("affine", 43, 5, 260, gpu_device, direction=rl.BACKWARD)]):
+        batch = rl.Batch()
+        for m in members:
+            m.record(batch)
+        batch.run()
+        torch.cuda.synchronize(gpu_device)
+        for m in members:
+            m.check()
