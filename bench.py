@@ -506,8 +506,9 @@ def main():
     step_s = res["step_ms"] * 1e-3
     ncalls = len(res["calls"])
     value = res["step_bytes"] / step_s / 1e9
-    if res["batch_ms"] is not None:
+    if res["batch_ms"] is not None and ncalls > 1:
         # one grouped launch runs the whole step: it is the dominant kernel
+        # (a one-call batch runs the call's own kernel, timed per call)
         dom_name, dom_bytes, dom_ms = "batch", res["step_bytes"], res["batch_ms"]
     else:
         dcall = res["calls"][res["dominant"]]
