@@ -44,13 +44,18 @@ COLD_BYTES = 1 << 30
 # Argument templates name buffers of a rotation set ("@key") or give scalars.
 
 
-def _backward_bytes(nt, n, f32_in, flags, f32_out):
-    return nt * (4 * f32_in + flags + 4 * f32_out) + 4 * n
+def _backward_bytes(nt, n, real_in, flags, real_out, es=4):
+    return nt * (es * real_in + flags + es * real_out) + es * n
 
 
-def workload_calls(name, cfg, host):
+# --dtype: storage type of the real-valued arrays (rlca_dtype codes)
+STORAGE = {"f32": 0, "bf16": 2, "f16": 3}
+
+
+def workload_calls(name, cfg, host, es=4):
     """Return (arrays, calls) for a named workload; arrays are the host inputs
-    each rotation set holds, calls the per-step library calls."""
+    each rotation set holds, calls the per-step library calls.  `es` is the
+    byte size of a stored real value."""
     n, t = host.num_envs, host.T
     nt = n * t
     g = cfg["gamma"]
@@ -60,16 +65,16 @@ def workload_calls(name, cfg, host):
                       trunc=host.truncated, tv=host.trunc_values, b=host.bootstrap)
         gae_nt = ("gae", "rlca_gae",
                   ["@r", "@v", "@term", None, None, "@b", g, lam, n, t, "@o0", "@o1"],
-                  _backward_bytes(nt, n, 2, 1, 2), ("o0", "o1"))
+                  _backward_bytes(nt, n, 2, 1, 2, es), ("o0", "o1"))
         gae_tr = ("gae+trunc", "rlca_gae",
                   ["@r", "@v", "@term", "@trunc", "@tv", "@b", g, lam, n, t, "@o0", "@o1"],
-                  _backward_bytes(nt, n, 3, 2, 2), ("o0", "o1"))
+                  _backward_bytes(nt, n, 3, 2, 2, es), ("o0", "o1"))
         td_nt = ("td_lambda", "rlca_td_lambda",
                  ["@r", "@v", "@term", None, None, "@b", g, lam, n, t, "@o0"],
-                 _backward_bytes(nt, n, 2, 1, 1), ("o0",))
+                 _backward_bytes(nt, n, 2, 1, 1, es), ("o0",))
         td_tr = ("td_lambda+trunc", "rlca_td_lambda",
                  ["@r", "@v", "@term", "@trunc", "@tv", "@b", g, lam, n, t, "@o0"],
-                 _backward_bytes(nt, n, 3, 2, 1), ("o0",))
+                 _backward_bytes(nt, n, 3, 2, 1, es), ("o0",))
         calls = [gae_tr] if name == "gae_8x16" else [gae_nt, gae_tr, td_nt, td_tr]
         return arrays, calls
     if name == "vtrace_4096x256":
@@ -78,7 +83,7 @@ def workload_calls(name, cfg, host):
         call = ("vtrace", "rlca_vtrace",
                 ["@r", "@v", "@mu", "@pi", "@term", None, None, "@b", g, lam, cfg["rho_bar"],
                  cfg["c_bar"], n, t, "@o0", "@o1"],
-                _backward_bytes(nt, n, 4, 1, 2), ("o0", "o1"))
+                _backward_bytes(nt, n, 4, 1, 2, es), ("o0", "o1"))
         return arrays, [call]
     if name == "retrace_2048x1024":
         arrays = dict(r=host.rewards, q=host.q_values, eq=host.expected_q,
@@ -87,7 +92,7 @@ def workload_calls(name, cfg, host):
         call = ("retrace+trunc", "rlca_retrace",
                 ["@r", "@q", "@eq", "@mu", "@pi", "@term", "@trunc", "@tv", "@b", g, lam,
                  cfg["c_bar"], n, t, "@o0"],
-                _backward_bytes(nt, n, 6, 2, 1), ("o0",))
+                _backward_bytes(nt, n, 6, 2, 1, es), ("o0",))
         return arrays, [call]
     if name == "forward_16384x512":
         arrays = dict(r=host.rewards, x=host.increments, xi=host.ints, starts=host.starts,
@@ -95,11 +100,11 @@ def workload_calls(name, cfg, host):
         calls = [
             ("discounted", "rlca_discounted_returns",
              ["@r", "@dones", None, None, "@b", g, n, t, "@o0"],
-             _backward_bytes(nt, n, 1, 1, 1), ("o0",)),
+             _backward_bytes(nt, n, 1, 1, 1, es), ("o0",)),
             ("eligibility", "rlca_eligibility_traces",
-             ["@x", "@starts", 0, g, lam, n, t, "@o0"], nt * 9, ("o0",)),
+             ["@x", "@starts", 0, g, lam, n, t, "@o0"], nt * (2 * es + 1), ("o0",)),
             ("prefix_sum_f32", "rlca_episodic_prefix_sum",
-             ["@r", 0, "@starts", 0, n, t, "@o0"], nt * 9, ("o0",)),
+             ["@r", 0, "@starts", 0, n, t, "@o0"], nt * (2 * es + 1), ("o0",)),
             ("prefix_sum_i32", "rlca_episodic_prefix_sum",
              ["@xi", 1, "@starts", 0, n, t, "@oi"], nt * 9, ("oi",)),
         ]
@@ -110,10 +115,15 @@ def workload_calls(name, cfg, host):
 # ------------------------------------------------------------------ GPU timing
 
 
-def make_sets(torch, arrays, calls, device, min_call_bytes):
+def make_sets(torch, arrays, calls, device, min_call_bytes, real=None):
     """Rotation sets: full copies of the inputs plus every output buffer, as
-    many as needed for >= COLD_BYTES of traffic between reuses of a set."""
-    master = {k: torch.from_numpy(np.ascontiguousarray(v)).to(device) for k, v in arrays.items()}
+    many as needed for >= COLD_BYTES of traffic between reuses of a set.
+    Real-valued arrays are stored as `real` (a torch dtype; float32 if None)."""
+    real = real or torch.float32
+    master = {}
+    for k, v in arrays.items():
+        x = torch.from_numpy(np.ascontiguousarray(v)).to(device)
+        master[k] = x.to(real) if x.dtype == torch.float32 else x
     shape = next(v.shape for v in arrays.values() if v.ndim == 2)
     nsets = min(4096, max(2, -(-COLD_BYTES // max(1, min_call_bytes)) + 1))
     per_set = sum(v.numel() * v.element_size() for v in master.values()) + \
@@ -122,8 +132,8 @@ def make_sets(torch, arrays, calls, device, min_call_bytes):
     sets = []
     for _ in range(nsets):
         s = {k: v.clone() for k, v in master.items()}
-        s["o0"] = torch.empty(shape, dtype=torch.float32, device=device)
-        s["o1"] = torch.empty(shape, dtype=torch.float32, device=device)
+        s["o0"] = torch.empty(shape, dtype=real, device=device)
+        s["o1"] = torch.empty(shape, dtype=real, device=device)
         s["oi"] = torch.empty(shape, dtype=torch.int32, device=device)
         sets.append(s)
     return sets
@@ -155,13 +165,16 @@ def _resolve(a, bufs):
     return bufs[a[1:]].data_ptr() if isinstance(a, str) and a.startswith("@") else a
 
 
-def batch_record(rlca, call, bufs):
-    """The rlca_call that records `call` on rotation set `bufs`."""
+def batch_record(rlca, call, bufs, storage=0):
+    """The rlca_call that records `call` on rotation set `bufs`, its real
+    arrays stored as `storage` (an rlca_dtype; int32 sums keep RLCA_I32)."""
     _, fname, template, _, _ = call
     op, names = BATCH_FIELDS[fname]
     c = rlca.RlcaCall(op=op)
     for name, a in zip(names, template):
         setattr(c, name, _resolve(a, bufs))
+    if c.dtype != rlca.RLCA_I32:
+        c.dtype = storage
     return c
 
 
@@ -182,8 +195,17 @@ def run_gpu(args, name, cfg, host):
     lib = rlca.lib()
     device = torch.device("cuda:0")
     torch.cuda.set_device(device)
-    arrays, calls = workload_calls(name, cfg, host)
-    sets = make_sets(torch, arrays, calls, device, min(c[3] for c in calls))
+    storage = STORAGE[args.dtype]
+    real = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[args.dtype]
+    arrays, calls = workload_calls(name, cfg, host, real.itemsize)
+    sets = make_sets(torch, arrays, calls, device, min(c[3] for c in calls), real)
+
+    def bind_call(call, bufs, h):
+        # bf16 / fp16 calls go through rlca_run_batch (the single-call entry
+        # points other than the prefix sum are fp32)
+        if storage == 0:
+            return bind(lib, call, bufs, h)
+        return bind_batch(lib, rlca, [batch_record(rlca, call, bufs, storage)], h)
     nsets = len(sets)
     ncalls = len(calls)
     step_bytes = sum(c[3] for c in calls)
@@ -201,10 +223,10 @@ def run_gpu(args, name, cfg, host):
         for s in range(steps_per_cycle):
             bufs = [sets[(s * ncalls + c) % nsets] for c in range(ncalls)]
             if args.launch == "batch":
-                out.append([bind_batch(lib, rlca, [batch_record(rlca, calls[c], bufs[c])
+                out.append([bind_batch(lib, rlca, [batch_record(rlca, calls[c], bufs[c], storage)
                                                    for c in range(ncalls)], h)])
             else:
-                out.append([bind(lib, calls[c], bufs[c], h) for c in range(ncalls)])
+                out.append([bind_call(calls[c], bufs[c], h) for c in range(ncalls)])
         return out
 
     def check(st, what):
@@ -267,7 +289,7 @@ def run_gpu(args, name, cfg, host):
             torch.cuda.synchronize()
             return e0.elapsed_time(e1) / reps
 
-        per_call_ms = [back_to_back([bind(lib, calls[c], sets[i], h) for i in range(nsets)])
+        per_call_ms = [back_to_back([bind_call(calls[c], sets[i], h) for i in range(nsets)])
                        for c in range(ncalls)]
         batch_ms = back_to_back([p[0] for p in plan]) if args.launch == "batch" else None
 
@@ -478,6 +500,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="gae_td_4096x128")
     ap.add_argument("--launch", choices=("batch", "graph", "eager"), default="batch")
+    ap.add_argument("--dtype", choices=tuple(STORAGE), default="f32",
+                    help="storage type of the real-valued arrays (arithmetic is fp32)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
@@ -514,7 +538,8 @@ def main():
         dcall = res["calls"][res["dominant"]]
         dom_name, dom_bytes, dom_ms = dcall[0], dcall[3], res["per_call_ms"][res["dominant"]]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    traffic = measured_traffic(dom_name.replace("+", "_"), args.workload)
+    tag = dom_name.replace("+", "_") + ("" if args.dtype == "f32" else "_" + args.dtype)
+    traffic = measured_traffic(tag, args.workload)
 
     calls_out = {}
     for i, c in enumerate(res["calls"]):
@@ -534,7 +559,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": args.dtype,
         "data": "synthetic (seeded numpy rollouts; cold-cache rotation over "
                 f"{res['nsets']} HBM-resident copies)",
         "config": {
@@ -543,6 +568,7 @@ def main():
             "T": host.T,
             "calls_per_step": [c[0] for c in res["calls"]],
             "launch": args.launch,
+            "storage": args.dtype,
         },
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "env_steps_per_s": ncalls * res["nt"] / step_s,

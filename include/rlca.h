@@ -23,10 +23,12 @@
  *          synchronizes: work is enqueued on `stream` and buffers must stay
  *          alive until the stream has passed the call.
  * Layout:  per-step arrays are dense row-major [num_envs, T]; element (n, t)
- *          is at n*T + t.  `bootstrap` is [num_envs].  fp32 / int32 data must
- *          be 4-byte aligned; 16-byte alignment (and T % 4 == 0) selects the
- *          vectorised path but is not required.  Flags are one byte per step,
- *          any nonzero byte meaning "set" (torch.bool and uint8 both work).
+ *          is at n*T + t.  `bootstrap` is [num_envs].  Real-valued and int32
+ *          data must be aligned to its element size; alignment to four
+ *          elements (16 bytes for fp32, 8 for bf16 / fp16) and T % 4 == 0
+ *          select the vectorised path but are not required.  Flags are one
+ *          byte per step, any nonzero byte meaning "set" (torch.bool and
+ *          uint8 both work).
  * Episode boundaries (summary §3.2 Episode-boundary semantics):
  *          terminated[t]  the episode ends after step t in a terminal state:
  *                         successor value 0, no credit flows back past t.
@@ -51,15 +53,19 @@
  *                                    finite, an unknown enum value
  *            RLCA_ERR_ALIASING       an output overlaps an input or another
  *                                    output (in-place is not supported)
- *            RLCA_ERR_MISALIGNED     an fp32 / int32 pointer is not 4-byte aligned
+ *            RLCA_ERR_MISALIGNED     an array is not aligned to its element size
  *            RLCA_ERR_HIP            a kernel launch failed (its hipError_t)
  *          num_envs * T == 0 is a valid no-op.  Faults inside the kernel
  *          surface at the caller's next synchronisation, as usual in HIP.
  *          Non-finite inputs propagate; they are not trapped.
- * Numerics: fp32 throughout (the summary's §4 requires float32 scans); the
- *          scan reassociates the recurrence (associativity, summary §5), so
- *          results match a sequential fp64 evaluation to rounding, not bit
- *          for bit.  The int32 prefix sum is exact (two's-complement wrap).
+ * Numerics: fp32 arithmetic throughout (the summary's §4 requires float32
+ *          scans); the scan reassociates the recurrence (associativity,
+ *          summary §5), so results match a sequential fp64 evaluation to
+ *          rounding, not bit for bit.  The int32 prefix sum is exact
+ *          (two's-complement wrap).  Arrays may instead be stored as bf16 or
+ *          fp16 (rlca_dtype; the summary's §9 defers bfloat16 I/O): they are
+ *          widened exactly to fp32 on load and every output is rounded once,
+ *          to nearest even, on store.
  */
 #ifndef RLCA_H
 #define RLCA_H
@@ -96,7 +102,10 @@ typedef enum {
     RLCA_RESET_AFTER_DONE = 1 /* flags[t-1] != 0: step t-1 ended the episode      */
 } rlca_reset_convention;
 
-typedef enum { RLCA_F32 = 0, RLCA_I32 = 1 } rlca_dtype;
+/* Element type of the data arrays.  RLCA_F32, RLCA_BF16 and RLCA_F16 are
+ * storage types of the real-valued arrays (arithmetic is fp32 for all
+ * three); RLCA_I32 is the exact integer prefix sum. */
+typedef enum { RLCA_F32 = 0, RLCA_I32 = 1, RLCA_BF16 = 2, RLCA_F16 = 3 } rlca_dtype;
 
 typedef enum { RLCA_BACKWARD = 0, RLCA_FORWARD = 1 } rlca_direction;
 
@@ -171,8 +180,8 @@ rlca_status rlca_eligibility_traces(const float *increments, const uint8_t *flag
 
 /* Inclusive episodic (segmented) prefix sum, forward in time (summary §3.3):
  *   S_t = x_t + S_{t-1},  S_{-1} = 0, restarted where a new episode starts.
- * x and out are [N,T] of `dtype` (f32, or i32 with two's-complement
- * wrap-around, exact); flags [N,T] u8 (required). */
+ * x and out are [N,T] of `dtype` (f32, bf16 or f16; or i32 with
+ * two's-complement wrap-around, exact); flags [N,T] u8 (required). */
 rlca_status rlca_episodic_prefix_sum(const void *x, rlca_dtype dtype, const uint8_t *flags,
                                      rlca_reset_convention convention, int64_t num_envs,
                                      int64_t T, void *out, hipStream_t stream);
@@ -217,27 +226,31 @@ typedef enum {
 /* One call of a batch.  Fields carry the arguments of the op's entry point;
  * fields an op does not take are ignored.
  *   rewards     rewards (GAE, TD, discounted, V-Trace, Retrace); increments
- *               (eligibility traces); x (prefix sum, f32 or i32 per dtype);
- *               alpha (affine scan)
+ *               (eligibility traces); x (prefix sum); alpha (affine scan)
  *   values      values (GAE, TD, V-Trace); q_values (Retrace); beta (affine)
  *   terminated  terminated (backward estimators); flags (forward scans)
  *   bootstrap   bootstrap (backward estimators); carry (affine scan)
  *   out0        advantages / returns / vs / q_ret / traces / out
  *   out1        GAE returns or V-Trace pg_advantages; nullable
- *   convention, dtype, direction: as the forward scans / affine scan take them */
+ *   dtype       element type of every real-valued array of the call, inputs
+ *               and outputs alike: RLCA_F32 (0), RLCA_BF16 or RLCA_F16; the
+ *               prefix sum also takes RLCA_I32.  This is how the bf16 / fp16
+ *               forms of every op are reached (the single-call entry points
+ *               above are fp32, except the prefix sum, which takes dtype).
+ *   convention, direction: as the forward scans / affine scan take them */
 typedef struct {
     rlca_op op;
     int64_t num_envs;
     int64_t T;
-    const float *rewards;
-    const float *values;
-    const float *expected_q;
-    const float *behaviour_logp;
-    const float *target_logp;
+    const void *rewards;
+    const void *values;
+    const void *expected_q;
+    const void *behaviour_logp;
+    const void *target_logp;
     const uint8_t *terminated;
     const uint8_t *truncated;
-    const float *trunc_values;
-    const float *bootstrap;
+    const void *trunc_values;
+    const void *bootstrap;
     float gamma;
     float lambda;
     float rho_bar;

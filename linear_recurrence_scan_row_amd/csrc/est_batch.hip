@@ -12,6 +12,9 @@ static_assert(kMaxGroupedCalls == 14, "the head is 14 preloaded kernel-argument 
         uint32_t h7, uint32_t h8, uint32_t h9, uint32_t h10, uint32_t h11, uint32_t h12,       \
         uint32_t h13
 
+// S: storage type of every member's real-valued arrays (float also carries
+// the int32 prefix sums).
+template <typename S>
 __global__ __launch_bounds__(kGroupWaves * kWave) void grouped_scan(RLCA_HEAD_ARGS,
                                                                     GroupedArgs a) {
     const uint32_t head[kMaxGroupedCalls] = {h0, h1, h2,  h3,  h4,  h5,  h6,
@@ -40,11 +43,11 @@ __global__ __launch_bounds__(kGroupWaves * kWave) void grouped_scan(RLCA_HEAD_AR
         switch (variant) {
 #define RLCA_B(EST, TR, WL)                                                                  \
     case grouped_backward_variant(EST, TR, WL, false):                                      \
-        backward_body<EST, TR, true, kGroupWaves, WL, kFull>(p, wg, once);                  \
+        backward_body<EST, TR, true, kGroupWaves, WL, kFull, S>(p, wg, once);               \
         return;
 #define RLCA_B1(EST, TR)                                                                     \
     case grouped_backward_variant(EST, TR, false, true):                                    \
-        if (g1 < once) backward_body<EST, TR, true, 1, false, kFull>(p, g1, once);          \
+        if (g1 < once) backward_body<EST, TR, true, 1, false, kFull, S>(p, g1, once);       \
         return;
 #define RLCA_B_ALL(EST)                                                                      \
     RLCA_B(EST, false, false) RLCA_B(EST, false, true) RLCA_B(EST, true, false)             \
@@ -65,47 +68,57 @@ __global__ __launch_bounds__(kGroupWaves * kWave) void grouped_scan(RLCA_HEAD_AR
     }
     ForwardParams p = a.calls[c].f;
     const uint32_t once = p.geo.num_groups;
-    switch (variant) {
-#define RLCA_F(V, INT, AD, WL)                                                               \
+#define RLCA_F(V, ST, INT, AD, WL)                                                           \
     case grouped_forward_variant(INT, AD, WL, false):                                       \
-        forward_body<V, kForwardFlags, AD, true, kGroupWaves, WL, kFull>(p, wg, once);      \
+        forward_body<V, kForwardFlags, AD, true, kGroupWaves, WL, kFull, ST>(p, wg, once);  \
         return;
-#define RLCA_F1(V, INT, AD)                                                                  \
+#define RLCA_F1(V, ST, INT, AD)                                                              \
     case grouped_forward_variant(INT, AD, false, true):                                     \
-        if (g1 < once) forward_body<V, kForwardFlags, AD, true, 1, false, kFull>(p, g1, once); \
+        if (g1 < once)                                                                       \
+            forward_body<V, kForwardFlags, AD, true, 1, false, kFull, ST>(p, g1, once);     \
         return;
-#define RLCA_F_ALL(V, INT, AD)                                                               \
-    RLCA_F(V, INT, AD, false) RLCA_F(V, INT, AD, true) RLCA_F1(V, INT, AD)
-        RLCA_F_ALL(float, false, false)
-        RLCA_F_ALL(float, false, true)
-        RLCA_F_ALL(uint32_t, true, false)
-        RLCA_F_ALL(uint32_t, true, true)
-#undef RLCA_F_ALL
-#undef RLCA_F1
-#undef RLCA_F
+#define RLCA_F_ALL(V, ST, INT, AD)                                                           \
+    RLCA_F(V, ST, INT, AD, false) RLCA_F(V, ST, INT, AD, true) RLCA_F1(V, ST, INT, AD)
+    switch (variant) {
+        RLCA_F_ALL(float, S, false, false)
+        RLCA_F_ALL(float, S, false, true)
         case grouped_affine_forward_variant(false, false):
-            forward_body<float, kForwardAffine, false, true, kGroupWaves, false, kFull>(p, wg,
-                                                                                        once);
+            forward_body<float, kForwardAffine, false, true, kGroupWaves, false, kFull, S>(
+                p, wg, once);
             return;
         case grouped_affine_forward_variant(true, false):
-            forward_body<float, kForwardAffine, false, true, kGroupWaves, true, kFull>(p, wg,
-                                                                                       once);
+            forward_body<float, kForwardAffine, false, true, kGroupWaves, true, kFull, S>(
+                p, wg, once);
             return;
         case grouped_affine_forward_variant(false, true):
             if (g1 < once)
-                forward_body<float, kForwardAffine, false, true, 1, false, kFull>(p, g1, once);
+                forward_body<float, kForwardAffine, false, true, 1, false, kFull, S>(p, g1,
+                                                                                     once);
             return;
-        default: return;
+        default: break;
     }
+    if constexpr (sizeof(S) == 4) {  // int32 sums only travel in the 4-byte group
+        switch (variant) {
+            RLCA_F_ALL(uint32_t, uint32_t, true, false)
+            RLCA_F_ALL(uint32_t, uint32_t, true, true)
+            default: return;
+        }
+    }
+#undef RLCA_F_ALL
+#undef RLCA_F1
+#undef RLCA_F
 }
 
-rlca_status launch_grouped(const GroupedLaunch &launch, hipStream_t stream) {
+rlca_status launch_grouped(const GroupedLaunch &launch, int storage, hipStream_t stream) {
     GroupedLaunch l = launch;
     void *argv[kMaxGroupedCalls + 1];
     for (int i = 0; i < kMaxGroupedCalls; ++i) argv[i] = &l.head[i];
     argv[kMaxGroupedCalls] = &l.args;
-    const hipError_t e = hipLaunchKernel((const void *)grouped_scan, dim3(l.workgroups),
-                                         dim3(kGroupWaves * kWave), argv, 0, stream);
+    const void *kernel = storage == kStoreBF16  ? (const void *)grouped_scan<__bf16>
+                         : storage == kStoreF16 ? (const void *)grouped_scan<_Float16>
+                                                : (const void *)grouped_scan<float>;
+    const hipError_t e = hipLaunchKernel(kernel, dim3(l.workgroups), dim3(kGroupWaves * kWave),
+                                         argv, 0, stream);
     return e == hipSuccess ? RLCA_OK : RLCA_ERR_HIP;
 }
 

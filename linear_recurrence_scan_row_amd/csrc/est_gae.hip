@@ -2,7 +2,8 @@
 #include "kernels.hpp"
 
 namespace rlca {
-rlca_status launch_gae(BackwardParams &p, const LaunchShape &s, hipStream_t stream) {
-    return launch_backward<kGae>(p, s, stream);
+rlca_status launch_gae(BackwardParams &p, const LaunchShape &s, int storage,
+                    hipStream_t stream) {
+    return launch_backward<kGae>(p, s, storage, stream);
 }
 }  // namespace rlca

@@ -2,7 +2,8 @@
 #include "kernels.hpp"
 
 namespace rlca {
-rlca_status launch_retrace(BackwardParams &p, const LaunchShape &s, hipStream_t stream) {
-    return launch_backward<kRetrace>(p, s, stream);
+rlca_status launch_retrace(BackwardParams &p, const LaunchShape &s, int storage,
+                    hipStream_t stream) {
+    return launch_backward<kRetrace>(p, s, storage, stream);
 }
 }  // namespace rlca

@@ -70,18 +70,21 @@ struct Geometry {
     uint32_t chunks_per_row;  // chunk modes: chunks of kChunkSteps per row
 };
 
+// Real-valued arrays are stored as S (float, __bf16 or _Float16: the kernels'
+// storage-type parameter) and computed on in fp32; the pointers below are
+// untyped and take the kernel's S.
 struct BackwardParams {
-    const float *rewards;  // alpha for kAffineBackward
-    const float *values;   // V(s_t); Q(s_t, a_t) for Retrace; beta for kAffineBackward
-    const float *expected_q;
-    const float *behaviour_logp;
-    const float *target_logp;
+    const void *rewards;  // alpha for kAffineBackward
+    const void *values;   // V(s_t); Q(s_t, a_t) for Retrace; beta for kAffineBackward
+    const void *expected_q;
+    const void *behaviour_logp;
+    const void *target_logp;
     const uint8_t *terminated;
     const uint8_t *truncated;
-    const float *trunc_values;
-    const float *bootstrap;  // carry A_T for kAffineBackward
-    float *out0;             // advantages / returns / vs / q_ret / A
-    float *out1;             // GAE returns or V-Trace pg advantages; may be null
+    const void *trunc_values;
+    const void *bootstrap;  // carry A_T for kAffineBackward
+    void *out0;             // advantages / returns / vs / q_ret / A
+    void *out1;             // GAE returns or V-Trace pg advantages; may be null
     float gamma, lambda, rho_bar, c_bar;
     Geometry geo;
 };
@@ -89,12 +92,15 @@ struct BackwardParams {
 struct ForwardParams {
     const void *x;         // alpha for kForwardAffine
     const uint8_t *flags;  // kForwardFlags
-    const float *beta;     // kForwardAffine
-    const float *carry;    // kForwardAffine: A_{-1} per row, may be null
+    const void *beta;      // kForwardAffine
+    const void *carry;     // kForwardAffine: A_{-1} per row, may be null
     void *out;
     float decay;  // gamma*lambda for traces, 1 for prefix sums
     Geometry geo;
 };
+
+// Storage types of real-valued arrays.
+enum Storage : int { kStoreF32 = 0, kStoreBF16 = 1, kStoreF16 = 2 };
 
 // Launch configuration chosen on the host.
 struct LaunchShape {
@@ -107,8 +113,21 @@ struct LaunchShape {
 // ---------------------------------------------------------------- memory access
 // `p` points at the workgroup's first element; `off` is the lane's first step
 // relative to it and `L` the number of valid steps.  With VEC the caller
-// guarantees 4K-byte alignment of p + off and L % K == 0, so a lane's K
+// guarantees K-element alignment of p + off and L % K == 0, so a lane's K
 // steps are either wholly valid or wholly past the end.
+//
+// Stored values S widen to the scan type E on load (bf16 and fp16 widen
+// exactly to fp32) and narrow on store (to nearest even: v_cvt_pk_bf16_f32 /
+// v_cvt_pk_f16_f32 on gfx950).
+
+template <typename E, typename S>
+__device__ __forceinline__ E widen(S x) {
+    return static_cast<E>(x);
+}
+template <typename S, typename E>
+__device__ __forceinline__ S narrow(E x) {
+    return static_cast<S>(x);
+}
 
 template <typename E, int N>
 struct VecOf {
@@ -135,25 +154,25 @@ struct FlagWord<4> {
     typedef uint32_t type;
 };
 
-template <bool VEC, typename E>
-__device__ __forceinline__ void load_steps(E (&x)[kK], const E *__restrict__ p, uint32_t off,
+template <bool VEC, typename E, typename S>
+__device__ __forceinline__ void load_steps(E (&x)[kK], const S *__restrict__ p, uint32_t off,
                                            uint32_t L) {
-    static_assert(sizeof(E) == 4, "32-bit elements");
+    static_assert(sizeof(E) == 4 && (sizeof(S) == 4 || sizeof(S) == 2), "32-bit scan values");
     // Element-typed vector: its lanes are read by value (no bit cast of a
     // vector element, which this compiler lowers as a read of element 0).
-    typedef typename VecOf<E, kK>::type vec;
+    typedef typename VecOf<S, kK>::type vec;
     if constexpr (VEC) {
         vec q = {};
         if (off < L) q = *reinterpret_cast<const vec *>(p + off);
         if constexpr (kK == 1) {
-            x[0] = q;
+            x[0] = widen<E>(q);
         } else {
 #pragma unroll
-            for (int i = 0; i < kK; ++i) x[i] = q[i];
+            for (int i = 0; i < kK; ++i) x[i] = widen<E>(q[i]);
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < kK; ++i) x[i] = (off + i < L) ? p[off + i] : E(0);
+        for (int i = 0; i < kK; ++i) x[i] = (off + i < L) ? widen<E>(p[off + i]) : E(0);
     }
 }
 
@@ -172,26 +191,35 @@ __device__ __forceinline__ void load_flags(bool (&f)[kK], const uint8_t *__restr
     }
 }
 
-template <bool VEC, typename E>
-__device__ __forceinline__ void store_steps(E *__restrict__ p, const E (&x)[kK], uint32_t off,
+template <bool VEC, typename S, typename E>
+__device__ __forceinline__ void store_steps(S *__restrict__ p, const E (&x)[kK], uint32_t off,
                                             uint32_t L) {
-    typedef typename VecOf<E, kK>::type vec;
+    typedef typename VecOf<S, kK>::type vec;
     if constexpr (VEC) {
         if (off < L) {
             vec q;
             if constexpr (kK == 1) {
-                q = x[0];
+                q = narrow<S>(x[0]);
             } else {
 #pragma unroll
-                for (int i = 0; i < kK; ++i) q[i] = x[i];
+                for (int i = 0; i < kK; ++i) q[i] = narrow<S>(x[i]);
             }
             __builtin_nontemporal_store(q, reinterpret_cast<vec *>(p + off));
         }
     } else {
 #pragma unroll
         for (int i = 0; i < kK; ++i)
-            if (off + i < L) p[off + i] = x[i];
+            if (off + i < L) p[off + i] = narrow<S>(x[i]);
     }
+}
+
+// Chunk modes hand two scan values per chunk between launches through the
+// chunk's first output elements, as raw 32-bit words whatever S is (a chunk
+// starts at an even element, so the words are 4-byte aligned, and spans at
+// least 2048 steps).
+template <typename E, typename S>
+__device__ __forceinline__ E *chunk_slot(void *out, int64_t base) {
+    return reinterpret_cast<E *>(static_cast<S *>(out) + base);
 }
 
 // The steps one workgroup iteration covers.
@@ -322,7 +350,7 @@ inline void lead_from(const ForwardParams &p, Lead &l) {
 // arguments.
 template <int EST>
 __device__ __forceinline__ void adopt_lead(BackwardParams &p, LEAD_ARGS) {
-    typedef const float *F;
+    typedef const void *F;
     typedef const uint8_t *U;
     if constexpr (EST == kGae || EST == kTdLambda) {
         p.rewards = F(lead0), p.values = F(lead1), p.terminated = U(lead2);
@@ -338,7 +366,7 @@ __device__ __forceinline__ void adopt_lead(BackwardParams &p, LEAD_ARGS) {
         p.behaviour_logp = F(lead3), p.target_logp = F(lead4);
     } else {
         p.rewards = F(lead0), p.values = F(lead1), p.bootstrap = F(lead2);
-        p.out0 = const_cast<float *>(F(lead3));
+        p.out0 = const_cast<void *>(lead3);
         (void)lead4;
     }
     p.geo.T = lead_T;
@@ -350,8 +378,8 @@ __device__ __forceinline__ void adopt_lead(ForwardParams &p, LEAD_ARGS) {
     p.x = lead0;
     p.flags = static_cast<const uint8_t *>(lead1);
     p.out = const_cast<void *>(lead2);
-    p.beta = static_cast<const float *>(lead3);
-    p.carry = static_cast<const float *>(lead4);
+    p.beta = lead3;
+    p.carry = lead4;
     p.geo.T = lead_T;
     p.geo.rows_per_group = lead_rows_per_group;
     p.geo.num_envs = lead_num_envs;
@@ -361,9 +389,18 @@ __device__ __forceinline__ void adopt_lead(ForwardParams &p, LEAD_ARGS) {
 // A_t = alpha_t + beta_t * A_{t+1}.  Lanes take chunks in reverse time order, so
 // the lane-order scan of scan_core.hpp runs from the end of the tile backwards.
 // Groups g, g + g_stride, ... of the launch run through one workgroup.
-template <int EST, bool TRUNC, bool VEC, int NW, bool WAVE_LOCAL, int MODE>
+template <int EST, bool TRUNC, bool VEC, int NW, bool WAVE_LOCAL, int MODE, typename S>
 __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uint32_t g_stride) {
     static_assert(MODE == kFull || (NW == kChunkWaves && !WAVE_LOCAL), "a chunk is one tile");
+    typedef const S *__restrict__ In;
+    const In rewards = static_cast<In>(p.rewards), values = static_cast<In>(p.values);
+    const In expected_q = static_cast<In>(p.expected_q);
+    const In behaviour_logp = static_cast<In>(p.behaviour_logp);
+    const In target_logp = static_cast<In>(p.target_logp);
+    const In trunc_values = static_cast<In>(p.trunc_values);
+    const In bootstrap = static_cast<In>(p.bootstrap);
+    S *__restrict__ out0 = static_cast<S *>(p.out0);
+    S *__restrict__ out1 = static_cast<S *>(p.out1);
     constexpr uint32_t kTile = NW * kWave * kK;
     constexpr bool kFlags = EST != kAffineBackward;
     __shared__ float lds_a[2 * NW], lds_b[2 * NW];
@@ -386,7 +423,7 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
         // or the carry the chunk-carry pass left in the chunk's first slot.
         float carry = 0.f;
         if constexpr (MODE == kChunkApply) {
-            carry = p.out0[base];
+            carry = chunk_slot<float, S>(p.out0, base)[0];
             __syncthreads();  // every lane has read the slot before any store
         }
 
@@ -396,17 +433,17 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
             // ---- 1. loads (each input element once)
             float r[kK], v[kK], eq[kK], mu[kK], pi[kK], tv[kK];
             bool term[kK], trunc[kK];
-            load_steps<VEC>(r, p.rewards + base, off, L);
-            if constexpr (EST != kDiscounted) load_steps<VEC>(v, p.values + base, off, L);
-            if constexpr (EST == kRetrace) load_steps<VEC>(eq, p.expected_q + base, off, L);
+            load_steps<VEC>(r, rewards + base, off, L);
+            if constexpr (EST != kDiscounted) load_steps<VEC>(v, values + base, off, L);
+            if constexpr (EST == kRetrace) load_steps<VEC>(eq, expected_q + base, off, L);
             if constexpr (EST == kVtrace || EST == kRetrace) {
-                load_steps<VEC>(mu, p.behaviour_logp + base, off, L);
-                load_steps<VEC>(pi, p.target_logp + base, off, L);
+                load_steps<VEC>(mu, behaviour_logp + base, off, L);
+                load_steps<VEC>(pi, target_logp + base, off, L);
             }
             if constexpr (kFlags) load_flags<VEC>(term, p.terminated + base, off, L);
             if constexpr (TRUNC) {
                 load_flags<VEC>(trunc, p.truncated + base, off, L);
-                load_steps<VEC>(tv, p.trunc_values + base, off, L);
+                load_steps<VEC>(tv, trunc_values + base, off, L);
             }
             // Loads whose addresses depend only on positions go out with the
             // main batch: the bootstrap (carry) of rows ending in this chunk,
@@ -422,19 +459,19 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
             for (int i = 0; i < kK; ++i) {
                 valid[i] = off + i < L;
                 boot[i] = 0.f;
-                if (valid[i] && t[i] == T - 1 && p.bootstrap != nullptr)
-                    boot[i] = p.bootstrap[row0 + row[i]];
+                if (valid[i] && t[i] == T - 1 && bootstrap != nullptr)
+                    boot[i] = widen<float>(bootstrap[row0 + row[i]]);
             }
             float v_first = 0.f, mu_first = 0.f, pi_first = 0.f, eq_first = 0.f;
             const bool halo_from_memory = (lane == 0 || off + kK >= L) && off + kK < win.row_rest;
             if (halo_from_memory) {
                 const int64_t jh = base + off + kK;
                 if constexpr (EST == kGae || EST == kTdLambda || EST == kVtrace)
-                    v_first = p.values[jh];
+                    v_first = widen<float>(values[jh]);
                 if constexpr (EST == kRetrace) {
-                    mu_first = p.behaviour_logp[jh];
-                    pi_first = p.target_logp[jh];
-                    eq_first = p.expected_q[jh];
+                    mu_first = widen<float>(behaviour_logp[jh]);
+                    pi_first = widen<float>(target_logp[jh]);
+                    eq_first = widen<float>(expected_q[jh]);
                 }
             }
 
@@ -532,8 +569,9 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
                 float ta, tb;
                 block_total<NW>(fa, fb, lds_a, lds_b, ta, tb);
                 if (threadIdx.x == 0 && win.chunk + 1 < p.geo.chunks_per_row) {
-                    p.out0[base] = ta;
-                    p.out0[base + 1] = tb;
+                    float *slot = chunk_slot<float, S>(p.out0, base);
+                    slot[0] = ta;
+                    slot[1] = tb;
                 }
             } else {
                 float carry_out;
@@ -562,9 +600,9 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
                         o1[i] = 0.f;
                     }
                 }
-                store_steps<VEC>(p.out0 + base, o0, off, L);
+                store_steps<VEC>(out0 + base, o0, off, L);
                 if constexpr (EST == kGae || EST == kVtrace) {
-                    if (p.out1 != nullptr) store_steps<VEC>(p.out1 + base, o1, off, L);
+                    if (out1 != nullptr) store_steps<VEC>(out1 + base, o1, off, L);
                 }
             }
         }
@@ -572,10 +610,10 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
     } while (g < p.geo.num_groups);
 }
 
-template <int EST, bool TRUNC, bool VEC, int NW, bool WAVE_LOCAL, int MODE>
+template <int EST, bool TRUNC, bool VEC, int NW, bool WAVE_LOCAL, int MODE, typename S>
 __global__ __launch_bounds__(NW * kWave) void backward_scan(LEAD_ARGS, BackwardParams p) {
     adopt_lead<EST>(p, LEAD_NAMES);
-    backward_body<EST, TRUNC, VEC, NW, WAVE_LOCAL, MODE>(p, blockIdx.x, gridDim.x);
+    backward_body<EST, TRUNC, VEC, NW, WAVE_LOCAL, MODE, S>(p, blockIdx.x, gridDim.x);
 }
 
 // -------------------------------------------------------------- forward kernel
@@ -584,7 +622,10 @@ __global__ __launch_bounds__(NW * kWave) void backward_scan(LEAD_ARGS, BackwardP
 // d_{t-1} = 1); V = float (traces, f32 sums) or uint32_t (int32 sums,
 // wrap-around).  kForwardAffine: the caller's (alpha, beta), with the row's
 // carry entering at t = 0.
-template <typename V, int KIND, bool AFTER_DONE, bool VEC, int NW, bool WAVE_LOCAL, int MODE>
+// S: storage type of x, out (and beta, carry for kForwardAffine); uint32_t
+// for the integer sums.
+template <typename V, int KIND, bool AFTER_DONE, bool VEC, int NW, bool WAVE_LOCAL, int MODE,
+          typename S>
 __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint32_t g_stride) {
     static_assert(MODE == kFull || (NW == kChunkWaves && !WAVE_LOCAL), "a chunk is one tile");
     constexpr uint32_t kTile = NW * kWave * kK;
@@ -594,8 +635,10 @@ __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint3
     const uint32_t chunk = w * kWave + lane;
     const uint32_t T = p.geo.T;
     const V decay = __builtin_bit_cast(V, __builtin_bit_cast(uint32_t, p.decay));
-    const V *__restrict__ xs = static_cast<const V *>(p.x);
-    V *__restrict__ out = static_cast<V *>(p.out);
+    const S *__restrict__ xs = static_cast<const S *>(p.x);
+    const S *__restrict__ betas = static_cast<const S *>(p.beta);
+    const S *__restrict__ carries = static_cast<const S *>(p.carry);
+    S *__restrict__ out = static_cast<S *>(p.out);
     int parity = 0;
 
     do {  // the first group always exists (see backward_body)
@@ -605,7 +648,7 @@ __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint3
         const uint32_t ntiles = MODE == kFull ? (L + kTile - 1) / kTile : 1u;
         V carry = V(0);
         if constexpr (MODE == kChunkApply) {
-            carry = out[base];
+            carry = chunk_slot<V, S>(p.out, base)[0];
             __syncthreads();  // every lane has read the slot before any store
         }
 
@@ -616,7 +659,7 @@ __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint3
             bool f[kK];
             load_steps<VEC>(x, xs + base, off, L);
             if constexpr (KIND == kForwardFlags) load_flags<VEC>(f, p.flags + base, off, L);
-            if constexpr (KIND == kForwardAffine) load_steps<VEC>(bt, p.beta + base, off, L);
+            if constexpr (KIND == kForwardAffine) load_steps<VEC>(bt, betas + base, off, L);
             uint32_t t[kK], row[kK];
             step_positions<MODE>(win, off, T, t, row);
             bool first = false;  // flag of the step before the lane's chunk (lane 0)
@@ -628,8 +671,8 @@ __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint3
             for (int i = 0; i < kK; ++i) {
                 row_carry[i] = 0.f;
                 if constexpr (KIND == kForwardAffine) {
-                    if (off + i < L && t[i] == 0 && p.carry != nullptr)
-                        row_carry[i] = p.carry[row0 + row[i]];
+                    if (off + i < L && t[i] == 0 && carries != nullptr)
+                        row_carry[i] = widen<float>(carries[row0 + row[i]]);
                 }
             }
             bool prev_done = false;
@@ -667,8 +710,9 @@ __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint3
                 V ta, tb;
                 block_total<NW>(fa, fb, lds_a, lds_b, ta, tb);
                 if (threadIdx.x == 0 && win.chunk + 1 < p.geo.chunks_per_row) {
-                    out[base] = ta;
-                    out[base + 1] = tb;
+                    V *slot = chunk_slot<V, S>(p.out, base);
+                    slot[0] = ta;
+                    slot[1] = tb;
                 }
             } else {
                 V carry_out;
@@ -689,10 +733,11 @@ __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint3
     } while (g < p.geo.num_groups);
 }
 
-template <typename V, int KIND, bool AFTER_DONE, bool VEC, int NW, bool WAVE_LOCAL, int MODE>
+template <typename V, int KIND, bool AFTER_DONE, bool VEC, int NW, bool WAVE_LOCAL, int MODE,
+          typename S>
 __global__ __launch_bounds__(NW * kWave) void forward_scan(LEAD_ARGS, ForwardParams p) {
     adopt_lead(p, LEAD_NAMES);
-    forward_body<V, KIND, AFTER_DONE, VEC, NW, WAVE_LOCAL, MODE>(p, blockIdx.x, gridDim.x);
+    forward_body<V, KIND, AFTER_DONE, VEC, NW, WAVE_LOCAL, MODE, S>(p, blockIdx.x, gridDim.x);
 }
 
 // ------------------------------------------------------------ chunk carries
@@ -701,30 +746,32 @@ __global__ __launch_bounds__(NW * kWave) void forward_scan(LEAD_ARGS, ForwardPar
 // `slots`) in scan order and leaves in each chunk's first word the value of
 // A entering that chunk.  Lane j of a tile holds chunk j; the last chunk in
 // scan order has no map (identity) but receives its carry.
-template <typename V, int NW>
-__global__ __launch_bounds__(NW * kWave) void chunk_carries(V *slots, int64_t num_envs, uint32_t T,
-                                                            uint32_t chunks_per_row, int backward) {
+template <typename V, typename S, int NW>
+__global__ __launch_bounds__(NW * kWave) void chunk_carries(void *slots, int64_t num_envs,
+                                                            uint32_t T, uint32_t chunks_per_row,
+                                                            int backward) {
     __shared__ V lds_a[2 * NW], lds_b[2 * NW];
     constexpr uint32_t kLanes = NW * kWave;
     int parity = 0;
     int64_t n = blockIdx.x;  // the grid never exceeds num_envs
     do {
-        V *row = slots + n * (int64_t)T;
+        const int64_t row = n * (int64_t)T;
         V carry = V(0);
         for (uint32_t j0 = 0; j0 < chunks_per_row; j0 += kLanes) {
             const uint32_t j = j0 + threadIdx.x;
             uint32_t lo = 0, hi = 0;
             if (j < chunks_per_row) chunk_bounds(T, j, backward != 0, lo, hi);
+            V *slot = chunk_slot<V, S>(slots, row + lo);
             V a = V(0), b = V(1);
             if (j + 1 < chunks_per_row) {
-                a = row[lo];
-                b = row[lo + 1];
+                a = slot[0];
+                b = slot[1];
             }
             V carry_out;
             const V in = block_carry_in<NW, false>(a, b, carry, lds_a, lds_b, parity, carry_out);
             parity ^= 1;
             carry = carry_out;
-            if (j < chunks_per_row) row[lo] = in;
+            if (j < chunks_per_row) slot[0] = in;
         }
         n += gridDim.x;
     } while (n < num_envs);
@@ -774,27 +821,27 @@ inline rlca_status launch_kernel(const void *kernel, int waves, uint32_t grid, P
     return e == hipSuccess ? RLCA_OK : RLCA_ERR_HIP;
 }
 
-template <typename V>
-inline rlca_status launch_chunk_carries(V *slots, const Geometry &geo, bool backward,
+template <typename V, typename S>
+inline rlca_status launch_chunk_carries(void *slots, const Geometry &geo, bool backward,
                                         hipStream_t stream) {
     int64_t n = geo.num_envs;
     uint32_t T = geo.T, m = geo.chunks_per_row;
     int dir = backward ? 1 : 0;
     void *args[] = {&slots, &n, &T, &m, &dir};
     const hipError_t e =
-        hipLaunchKernel((const void *)chunk_carries<V, kChunkWaves>, dim3(grid_for(n)),
+        hipLaunchKernel((const void *)chunk_carries<V, S, kChunkWaves>, dim3(grid_for(n)),
                         dim3(kChunkWaves * kWave), args, 0, stream);
     return e == hipSuccess ? RLCA_OK : RLCA_ERR_HIP;
 }
 
 // The three chunk-mode launches, all on one stream: aggregate, carries, apply.
-template <typename P, typename V>
+template <typename V, typename S, typename P>
 inline rlca_status launch_chunked(const void *aggregate, const void *apply, P &params, Lead &lead,
-                                  V *slots, bool backward, hipStream_t stream) {
+                                  void *slots, bool backward, hipStream_t stream) {
     uint32_t grid;
     params.geo = make_geometry(params.geo.num_envs, params.geo.T, kChunkWaves, true, &grid);
     rlca_status st = launch_kernel(aggregate, kChunkWaves, grid, params, lead, stream);
-    if (st == RLCA_OK) st = launch_chunk_carries(slots, params.geo, backward, stream);
+    if (st == RLCA_OK) st = launch_chunk_carries<V, S>(slots, params.geo, backward, stream);
     if (st == RLCA_OK) st = launch_kernel(apply, kChunkWaves, grid, params, lead, stream);
     return st;
 }
@@ -809,12 +856,12 @@ inline rlca_status launch_full(const void *kernel, int waves, P &params, Lead &l
 
 // The vector path instantiates every wave count and the wave-local variant;
 // the scalar (unaligned or T % K != 0) path is one general configuration.
-template <int EST, bool TRUNC>
+template <int EST, bool TRUNC, typename S>
 const void *backward_kernel(const LaunchShape &s) {
-    if (!s.vec) return (const void *)backward_scan<EST, TRUNC, false, 4, false, kFull>;
-#define RLCA_PICK(NW)                                                                     \
-    return s.wave_local ? (const void *)backward_scan<EST, TRUNC, true, NW, true, kFull> \
-                        : (const void *)backward_scan<EST, TRUNC, true, NW, false, kFull>
+    if (!s.vec) return (const void *)backward_scan<EST, TRUNC, false, 4, false, kFull, S>;
+#define RLCA_PICK(NW)                                                                        \
+    return s.wave_local ? (const void *)backward_scan<EST, TRUNC, true, NW, true, kFull, S> \
+                        : (const void *)backward_scan<EST, TRUNC, true, NW, false, kFull, S>
     switch (s.waves) {
         case 1: RLCA_PICK(1);
         case 2: RLCA_PICK(2);
@@ -824,30 +871,42 @@ const void *backward_kernel(const LaunchShape &s) {
 #undef RLCA_PICK
 }
 
-template <int EST, bool TRUNC>
+template <int EST, bool TRUNC, typename S>
 rlca_status launch_backward_variant(BackwardParams &p, const LaunchShape &s, hipStream_t stream) {
     Lead lead;
     lead_from<EST>(p, lead);
     if (s.chunked)
-        return launch_chunked(
-            (const void *)backward_scan<EST, TRUNC, true, kChunkWaves, false, kChunkAggregate>,
-            (const void *)backward_scan<EST, TRUNC, true, kChunkWaves, false, kChunkApply>, p,
+        return launch_chunked<float, S>(
+            (const void *)backward_scan<EST, TRUNC, true, kChunkWaves, false, kChunkAggregate, S>,
+            (const void *)backward_scan<EST, TRUNC, true, kChunkWaves, false, kChunkApply, S>, p,
             lead, p.out0, true, stream);
-    return launch_full(backward_kernel<EST, TRUNC>(s), s.vec ? s.waves : 4, p, lead, stream);
+    return launch_full(backward_kernel<EST, TRUNC, S>(s), s.vec ? s.waves : 4, p, lead, stream);
+}
+
+template <int EST, typename S>
+rlca_status launch_backward_typed(BackwardParams &p, const LaunchShape &s, hipStream_t stream) {
+    return p.truncated != nullptr ? launch_backward_variant<EST, true, S>(p, s, stream)
+                                  : launch_backward_variant<EST, false, S>(p, s, stream);
 }
 
 template <int EST>
-rlca_status launch_backward(BackwardParams &p, const LaunchShape &s, hipStream_t stream) {
-    return p.truncated != nullptr ? launch_backward_variant<EST, true>(p, s, stream)
-                                  : launch_backward_variant<EST, false>(p, s, stream);
+rlca_status launch_backward(BackwardParams &p, const LaunchShape &s, int storage,
+                            hipStream_t stream) {
+    switch (storage) {
+        case kStoreBF16: return launch_backward_typed<EST, __bf16>(p, s, stream);
+        case kStoreF16: return launch_backward_typed<EST, _Float16>(p, s, stream);
+        default: return launch_backward_typed<EST, float>(p, s, stream);
+    }
 }
 
-template <typename V, int KIND, bool AFTER_DONE>
+template <typename V, int KIND, bool AFTER_DONE, typename S>
 const void *forward_kernel(const LaunchShape &s) {
-    if (!s.vec) return (const void *)forward_scan<V, KIND, AFTER_DONE, false, 4, false, kFull>;
-#define RLCA_PICK(NW)                                                                         \
-    return s.wave_local ? (const void *)forward_scan<V, KIND, AFTER_DONE, true, NW, true, kFull> \
-                        : (const void *)forward_scan<V, KIND, AFTER_DONE, true, NW, false, kFull>
+    if (!s.vec)
+        return (const void *)forward_scan<V, KIND, AFTER_DONE, false, 4, false, kFull, S>;
+#define RLCA_PICK(NW)                                                                      \
+    return s.wave_local                                                                    \
+               ? (const void *)forward_scan<V, KIND, AFTER_DONE, true, NW, true, kFull, S> \
+               : (const void *)forward_scan<V, KIND, AFTER_DONE, true, NW, false, kFull, S>
     switch (s.waves) {
         case 1: RLCA_PICK(1);
         case 2: RLCA_PICK(2);
@@ -857,18 +916,30 @@ const void *forward_kernel(const LaunchShape &s) {
 #undef RLCA_PICK
 }
 
-template <typename V, int KIND, bool AFTER_DONE>
+template <typename V, int KIND, bool AFTER_DONE, typename S>
 rlca_status launch_forward_variant(ForwardParams &p, const LaunchShape &s, hipStream_t stream) {
     Lead lead;
     lead_from(p, lead);
     if (s.chunked)
-        return launch_chunked(
+        return launch_chunked<V, S>(
             (const void *)forward_scan<V, KIND, AFTER_DONE, true, kChunkWaves, false,
-                                       kChunkAggregate>,
-            (const void *)forward_scan<V, KIND, AFTER_DONE, true, kChunkWaves, false, kChunkApply>,
-            p, lead, static_cast<V *>(p.out), false, stream);
-    return launch_full(forward_kernel<V, KIND, AFTER_DONE>(s), s.vec ? s.waves : 4, p, lead,
+                                       kChunkAggregate, S>,
+            (const void *)forward_scan<V, KIND, AFTER_DONE, true, kChunkWaves, false, kChunkApply,
+                                       S>,
+            p, lead, p.out, false, stream);
+    return launch_full(forward_kernel<V, KIND, AFTER_DONE, S>(s), s.vec ? s.waves : 4, p, lead,
                        stream);
+}
+
+// The float forward scans in the requested storage type.
+template <int KIND, bool AFTER_DONE>
+rlca_status launch_forward_float(ForwardParams &p, const LaunchShape &s, int storage,
+                                 hipStream_t stream) {
+    switch (storage) {
+        case kStoreBF16: return launch_forward_variant<float, KIND, AFTER_DONE, __bf16>(p, s, stream);
+        case kStoreF16: return launch_forward_variant<float, KIND, AFTER_DONE, _Float16>(p, s, stream);
+        default: return launch_forward_variant<float, KIND, AFTER_DONE, float>(p, s, stream);
+    }
 }
 
 // ------------------------------------------------------------- grouped launch
@@ -919,19 +990,25 @@ constexpr int grouped_affine_forward_variant(bool wave_local, bool one_wave) {
     return one_wave ? 50 : 32 + (wave_local ? 1 : 0);
 }
 
-rlca_status launch_grouped(const GroupedLaunch &launch, hipStream_t stream);
+rlca_status launch_grouped(const GroupedLaunch &launch, int storage, hipStream_t stream);
 
 // One translation unit per estimator instantiates these (see est_*.hip).
-rlca_status launch_gae(BackwardParams &p, const LaunchShape &s, hipStream_t stream);
-rlca_status launch_td_lambda(BackwardParams &p, const LaunchShape &s, hipStream_t stream);
-rlca_status launch_discounted(BackwardParams &p, const LaunchShape &s, hipStream_t stream);
-rlca_status launch_vtrace(BackwardParams &p, const LaunchShape &s, hipStream_t stream);
-rlca_status launch_retrace(BackwardParams &p, const LaunchShape &s, hipStream_t stream);
-rlca_status launch_affine_backward(BackwardParams &p, const LaunchShape &s, hipStream_t stream);
-rlca_status launch_forward_f32(ForwardParams &p, bool after_done, const LaunchShape &s,
-                               hipStream_t stream);
+rlca_status launch_gae(BackwardParams &p, const LaunchShape &s, int storage, hipStream_t stream);
+rlca_status launch_td_lambda(BackwardParams &p, const LaunchShape &s, int storage,
+                             hipStream_t stream);
+rlca_status launch_discounted(BackwardParams &p, const LaunchShape &s, int storage,
+                              hipStream_t stream);
+rlca_status launch_vtrace(BackwardParams &p, const LaunchShape &s, int storage,
+                          hipStream_t stream);
+rlca_status launch_retrace(BackwardParams &p, const LaunchShape &s, int storage,
+                           hipStream_t stream);
+rlca_status launch_affine_backward(BackwardParams &p, const LaunchShape &s, int storage,
+                                   hipStream_t stream);
+rlca_status launch_forward_float(ForwardParams &p, bool after_done, const LaunchShape &s,
+                                 int storage, hipStream_t stream);
 rlca_status launch_forward_u32(ForwardParams &p, bool after_done, const LaunchShape &s,
                                hipStream_t stream);
-rlca_status launch_affine_forward(ForwardParams &p, const LaunchShape &s, hipStream_t stream);
+rlca_status launch_affine_forward(ForwardParams &p, const LaunchShape &s, int storage,
+                                  hipStream_t stream);
 
 }  // namespace rlca

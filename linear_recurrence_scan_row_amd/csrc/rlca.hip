@@ -38,11 +38,25 @@ static rlca_status check_sizes(int64_t num_envs, int64_t T, int64_t *elems) {
     return RLCA_OK;
 }
 
-static rlca_status check_aligned4(const void *const *ptrs, int n) {
+// Every real-valued or int32 array must be aligned to its element size.
+static rlca_status check_aligned(const void *const *ptrs, int n, size_t elem) {
     for (int i = 0; i < n; ++i)
-        if (ptrs[i] != nullptr && ((uintptr_t)ptrs[i] & 3u) != 0) return RLCA_ERR_MISALIGNED;
+        if (ptrs[i] != nullptr && ((uintptr_t)ptrs[i] % elem) != 0) return RLCA_ERR_MISALIGNED;
     return RLCA_OK;
 }
+
+// Storage of real-valued arrays for an rlca_dtype (RLCA_I32 is handled by the
+// prefix sum itself); -1 for a dtype that is not a real storage type.
+static int storage_of(int dtype) {
+    switch (dtype) {
+        case RLCA_F32: return kStoreF32;
+        case RLCA_BF16: return kStoreBF16;
+        case RLCA_F16: return kStoreF16;
+    }
+    return -1;
+}
+
+static size_t storage_bytes(int storage) { return storage == kStoreF32 ? 4 : 2; }
 
 // No output may overlap an input or another output.
 static rlca_status check_aliasing(const Span *outs, int nout, const Span *ins, int nin) {
@@ -58,10 +72,11 @@ static rlca_status check_aliasing(const Span *outs, int nout, const Span *ins, i
 
 // The vector path loads a lane's K steps with one instruction per stream: it
 // needs T % K == 0 and arrays aligned to K elements.
-static bool vec_ok(int64_t T, const void *const *f32, int nf, const void *const *u8, int nu) {
+static bool vec_ok(int64_t T, const void *const *wide, int nw, size_t elem,
+                   const void *const *u8, int nu) {
     if (T % kK != 0) return false;
-    for (int i = 0; i < nf; ++i)
-        if (f32[i] != nullptr && ((uintptr_t)f32[i] % (4 * kK)) != 0) return false;
+    for (int i = 0; i < nw; ++i)
+        if (wide[i] != nullptr && ((uintptr_t)wide[i] % (elem * kK)) != 0) return false;
     for (int i = 0; i < nu; ++i)
         if (u8[i] != nullptr && ((uintptr_t)u8[i] % kK) != 0) return false;
     return true;
@@ -105,6 +120,7 @@ struct Call {
     int forward;      // forward kind
     bool is_int;      // forward int32 prefix sum
     bool after_done;  // forward reset convention
+    int storage;      // Storage of the real-valued arrays (kStoreF32 for int32 sums)
     LaunchShape shape;
     BackwardParams bp;
     ForwardParams fp;
@@ -116,14 +132,17 @@ struct Call {
 
 // Checks shared by the backward estimators; fills the call's parameter
 // block, byte ranges and launch shape.  Arrays an estimator does not use are
-// passed as NULL and neither required nor read.
-static rlca_status prepare_backward(int est, const float *rewards, const float *values,
-                                    const float *expected_q, const float *behaviour_logp,
-                                    const float *target_logp, const uint8_t *terminated,
-                                    const uint8_t *truncated, const float *trunc_values,
-                                    const float *bootstrap, float *out0, float *out1,
-                                    int64_t num_envs, int64_t T, Call *c) {
+// passed as NULL and neither required nor read.  Real-valued arrays are
+// stored as `storage`.
+static rlca_status prepare_backward(int est, int storage, const void *rewards,
+                                    const void *values, const void *expected_q,
+                                    const void *behaviour_logp, const void *target_logp,
+                                    const uint8_t *terminated, const uint8_t *truncated,
+                                    const void *trunc_values, const void *bootstrap, void *out0,
+                                    void *out1, int64_t num_envs, int64_t T, Call *c) {
     *c = Call{};
+    if (storage < 0) return RLCA_ERR_INVALID_VALUE;
+    const size_t es = storage_bytes(storage);
     int64_t n;
     rlca_status st = check_sizes(num_envs, T, &n);
     if (st != RLCA_OK) return st;
@@ -144,18 +163,18 @@ static rlca_status prepare_backward(int est, const float *rewards, const float *
     if (!needs_values) values = nullptr;
     if (est != kRetrace) expected_q = nullptr;
     if (!needs_logp) behaviour_logp = target_logp = nullptr;
-    const void *f32[] = {rewards,     values,       expected_q, behaviour_logp, target_logp,
-                         trunc_values, bootstrap,   out0,       out1};
-    st = check_aligned4(f32, 9);
+    const void *real[] = {rewards,      values,    expected_q, behaviour_logp, target_logp,
+                          trunc_values, bootstrap, out0,       out1};
+    st = check_aligned(real, 9, es);
     if (st != RLCA_OK) return st;
-    const size_t fb = (size_t)n * 4, ub = (size_t)n;
+    const size_t fb = (size_t)n * es, ub = (size_t)n;
     const void *f32_steps[] = {rewards, values, expected_q, behaviour_logp, target_logp,
                                trunc_values};
     for (const void *p : f32_steps)
         if (p != nullptr) c->ins[c->nin++] = {p, fb};
     if (terminated != nullptr) c->ins[c->nin++] = {terminated, ub};
     if (truncated != nullptr) c->ins[c->nin++] = {truncated, ub};
-    c->ins[c->nin++] = {bootstrap, (size_t)num_envs * 4};
+    c->ins[c->nin++] = {bootstrap, (size_t)num_envs * es};
     c->outs[c->nout++] = {out0, fb};
     if (out1 != nullptr) c->outs[c->nout++] = {out1, fb};
     st = check_aliasing(c->outs, c->nout, c->ins, c->nin);
@@ -163,6 +182,7 @@ static rlca_status prepare_backward(int est, const float *rewards, const float *
 
     c->backward = true;
     c->est = est;
+    c->storage = storage;
     BackwardParams &p = c->bp;
     p.rewards = rewards;
     p.values = values;
@@ -178,15 +198,19 @@ static rlca_status prepare_backward(int est, const float *rewards, const float *
     p.geo.num_envs = num_envs;
     p.geo.T = (uint32_t)T;
     const void *u8[] = {terminated, truncated};
-    c->shape = choose_shape(num_envs, T, vec_ok(T, f32, 9, u8, 2));
+    c->shape = choose_shape(num_envs, T, vec_ok(T, real, 9, es, u8, 2));
     return RLCA_OK;
 }
 
-static rlca_status prepare_forward(int kind, const void *x, bool is_int, const uint8_t *flags,
-                                   int convention, float decay, const float *beta,
-                                   const float *carry, int64_t num_envs, int64_t T, void *out,
-                                   Call *c) {
+// Forward scans: x, beta, carry and out are stored as `storage`, or are
+// int32 with `is_int` (then storage is kStoreF32, the 4-byte class).
+static rlca_status prepare_forward(int kind, int storage, const void *x, bool is_int,
+                                   const uint8_t *flags, int convention, float decay,
+                                   const void *beta, const void *carry, int64_t num_envs,
+                                   int64_t T, void *out, Call *c) {
     *c = Call{};
+    if (storage < 0) return RLCA_ERR_INVALID_VALUE;
+    const size_t es = storage_bytes(storage);
     if (kind == kForwardFlags && convention != RLCA_RESET_ON_START &&
         convention != RLCA_RESET_AFTER_DONE)
         return RLCA_ERR_INVALID_VALUE;
@@ -201,19 +225,20 @@ static rlca_status prepare_forward(int kind, const void *x, bool is_int, const u
     if (kind == kForwardFlags) beta = carry = nullptr;
     if (kind == kForwardAffine) flags = nullptr;
     const void *al[] = {x, beta, carry, out};
-    st = check_aligned4(al, 4);
+    st = check_aligned(al, 4, es);
     if (st != RLCA_OK) return st;
-    c->ins[c->nin++] = {x, (size_t)n * 4};
+    c->ins[c->nin++] = {x, (size_t)n * es};
     if (flags != nullptr) c->ins[c->nin++] = {flags, (size_t)n};
-    if (beta != nullptr) c->ins[c->nin++] = {beta, (size_t)n * 4};
-    c->ins[c->nin++] = {carry, (size_t)num_envs * 4};
-    c->outs[c->nout++] = {out, (size_t)n * 4};
+    if (beta != nullptr) c->ins[c->nin++] = {beta, (size_t)n * es};
+    c->ins[c->nin++] = {carry, (size_t)num_envs * es};
+    c->outs[c->nout++] = {out, (size_t)n * es};
     st = check_aliasing(c->outs, c->nout, c->ins, c->nin);
     if (st != RLCA_OK) return st;
 
     c->backward = false;
     c->forward = kind;
     c->is_int = is_int;
+    c->storage = storage;
     c->after_done = kind == kForwardFlags && convention == RLCA_RESET_AFTER_DONE;
     ForwardParams &p = c->fp;
     p.x = x;
@@ -224,9 +249,9 @@ static rlca_status prepare_forward(int kind, const void *x, bool is_int, const u
     p.decay = is_int ? __builtin_bit_cast(float, 1u) : decay;
     p.geo.num_envs = num_envs;
     p.geo.T = (uint32_t)T;
-    const void *f32[] = {x, beta, out};
+    const void *wide[] = {x, beta, out};
     const void *u8[] = {flags};
-    c->shape = choose_shape(num_envs, T, vec_ok(T, f32, 3, u8, 1));
+    c->shape = choose_shape(num_envs, T, vec_ok(T, wide, 3, es, u8, 1));
     return RLCA_OK;
 }
 
@@ -235,17 +260,18 @@ static rlca_status launch_call(Call &c, hipStream_t stream) {
     if (c.empty) return RLCA_OK;
     if (c.backward) {
         switch (c.est) {
-            case kGae: return launch_gae(c.bp, c.shape, stream);
-            case kTdLambda: return launch_td_lambda(c.bp, c.shape, stream);
-            case kDiscounted: return launch_discounted(c.bp, c.shape, stream);
-            case kVtrace: return launch_vtrace(c.bp, c.shape, stream);
-            case kRetrace: return launch_retrace(c.bp, c.shape, stream);
-            default: return launch_affine_backward(c.bp, c.shape, stream);
+            case kGae: return launch_gae(c.bp, c.shape, c.storage, stream);
+            case kTdLambda: return launch_td_lambda(c.bp, c.shape, c.storage, stream);
+            case kDiscounted: return launch_discounted(c.bp, c.shape, c.storage, stream);
+            case kVtrace: return launch_vtrace(c.bp, c.shape, c.storage, stream);
+            case kRetrace: return launch_retrace(c.bp, c.shape, c.storage, stream);
+            default: return launch_affine_backward(c.bp, c.shape, c.storage, stream);
         }
     }
-    if (c.forward == kForwardAffine) return launch_affine_forward(c.fp, c.shape, stream);
+    if (c.forward == kForwardAffine)
+        return launch_affine_forward(c.fp, c.shape, c.storage, stream);
     return c.is_int ? launch_forward_u32(c.fp, c.after_done, c.shape, stream)
-                    : launch_forward_f32(c.fp, c.after_done, c.shape, stream);
+                    : launch_forward_float(c.fp, c.after_done, c.shape, c.storage, stream);
 }
 
 // The call as one member of a grouped launch, or false where it cannot be one.
@@ -274,62 +300,66 @@ static bool grouped_member(const Call &c, GroupedCall *g, int *variant, uint32_t
     return *workgroups <= kMaxGrid;
 }
 
-static rlca_status prepare_gae(const float *rewards, const float *values,
+static rlca_status prepare_gae(int storage, const void *rewards, const void *values,
                                const uint8_t *terminated, const uint8_t *truncated,
-                               const float *trunc_values, const float *bootstrap, float gamma,
-                               float lambda, int64_t num_envs, int64_t T, float *advantages,
-                               float *returns, Call *c) {
+                               const void *trunc_values, const void *bootstrap, float gamma,
+                               float lambda, int64_t num_envs, int64_t T, void *advantages,
+                               void *returns, Call *c) {
     *c = Call{};
     if (!unit_interval(gamma) || !unit_interval(lambda)) return RLCA_ERR_INVALID_VALUE;
-    const rlca_status st =
-        prepare_backward(kGae, rewards, values, nullptr, nullptr, nullptr, terminated,
-                         truncated, trunc_values, bootstrap, advantages, returns, num_envs, T, c);
+    const rlca_status st = prepare_backward(kGae, storage, rewards, values, nullptr, nullptr,
+                                            nullptr, terminated, truncated, trunc_values,
+                                            bootstrap, advantages, returns, num_envs, T, c);
     c->bp.gamma = gamma;
     c->bp.lambda = lambda;
     return st;
 }
 
-static rlca_status prepare_td_lambda(const float *rewards, const float *values,
+static rlca_status prepare_td_lambda(int storage, const void *rewards, const void *values,
                                      const uint8_t *terminated, const uint8_t *truncated,
-                                     const float *trunc_values, const float *bootstrap,
+                                     const void *trunc_values, const void *bootstrap,
                                      float gamma, float lambda, int64_t num_envs, int64_t T,
-                                     float *returns, Call *c) {
+                                     void *returns, Call *c) {
     *c = Call{};
     if (!unit_interval(gamma) || !unit_interval(lambda)) return RLCA_ERR_INVALID_VALUE;
-    const rlca_status st =
-        prepare_backward(kTdLambda, rewards, values, nullptr, nullptr, nullptr, terminated,
-                         truncated, trunc_values, bootstrap, returns, nullptr, num_envs, T, c);
+    const rlca_status st = prepare_backward(kTdLambda, storage, rewards, values, nullptr,
+                                            nullptr, nullptr, terminated, truncated,
+                                            trunc_values, bootstrap, returns, nullptr, num_envs,
+                                            T, c);
     c->bp.gamma = gamma;
     c->bp.lambda = lambda;
     return st;
 }
 
-static rlca_status prepare_discounted(const float *rewards, const uint8_t *terminated,
-                                      const uint8_t *truncated, const float *trunc_values,
-                                      const float *bootstrap, float gamma, int64_t num_envs,
-                                      int64_t T, float *returns, Call *c) {
+static rlca_status prepare_discounted(int storage, const void *rewards,
+                                      const uint8_t *terminated, const uint8_t *truncated,
+                                      const void *trunc_values, const void *bootstrap,
+                                      float gamma, int64_t num_envs, int64_t T, void *returns,
+                                      Call *c) {
     *c = Call{};
     if (!unit_interval(gamma)) return RLCA_ERR_INVALID_VALUE;
-    const rlca_status st =
-        prepare_backward(kDiscounted, rewards, nullptr, nullptr, nullptr, nullptr, terminated,
-                         truncated, trunc_values, bootstrap, returns, nullptr, num_envs, T, c);
+    const rlca_status st = prepare_backward(kDiscounted, storage, rewards, nullptr, nullptr,
+                                            nullptr, nullptr, terminated, truncated,
+                                            trunc_values, bootstrap, returns, nullptr, num_envs,
+                                            T, c);
     c->bp.gamma = gamma;
     return st;
 }
 
-static rlca_status prepare_vtrace(const float *rewards, const float *values,
-                                  const float *behaviour_logp, const float *target_logp,
+static rlca_status prepare_vtrace(int storage, const void *rewards, const void *values,
+                                  const void *behaviour_logp, const void *target_logp,
                                   const uint8_t *terminated, const uint8_t *truncated,
-                                  const float *trunc_values, const float *bootstrap, float gamma,
+                                  const void *trunc_values, const void *bootstrap, float gamma,
                                   float lambda, float rho_bar, float c_bar, int64_t num_envs,
-                                  int64_t T, float *vs, float *pg_advantages, Call *c) {
+                                  int64_t T, void *vs, void *pg_advantages, Call *c) {
     *c = Call{};
     if (!unit_interval(gamma) || !unit_interval(lambda) || !positive_finite(rho_bar) ||
         !positive_finite(c_bar))
         return RLCA_ERR_INVALID_VALUE;
-    const rlca_status st = prepare_backward(kVtrace, rewards, values, nullptr, behaviour_logp,
-                                            target_logp, terminated, truncated, trunc_values,
-                                            bootstrap, vs, pg_advantages, num_envs, T, c);
+    const rlca_status st =
+        prepare_backward(kVtrace, storage, rewards, values, nullptr, behaviour_logp,
+                         target_logp, terminated, truncated, trunc_values, bootstrap, vs,
+                         pg_advantages, num_envs, T, c);
     c->bp.gamma = gamma;
     c->bp.lambda = lambda;
     c->bp.rho_bar = rho_bar;
@@ -337,16 +367,16 @@ static rlca_status prepare_vtrace(const float *rewards, const float *values,
     return st;
 }
 
-static rlca_status prepare_retrace(const float *rewards, const float *q_values,
-                                   const float *expected_q, const float *behaviour_logp,
-                                   const float *target_logp, const uint8_t *terminated,
-                                   const uint8_t *truncated, const float *trunc_values,
-                                   const float *bootstrap, float gamma, float lambda, float c_bar,
-                                   int64_t num_envs, int64_t T, float *q_ret, Call *c) {
+static rlca_status prepare_retrace(int storage, const void *rewards, const void *q_values,
+                                   const void *expected_q, const void *behaviour_logp,
+                                   const void *target_logp, const uint8_t *terminated,
+                                   const uint8_t *truncated, const void *trunc_values,
+                                   const void *bootstrap, float gamma, float lambda, float c_bar,
+                                   int64_t num_envs, int64_t T, void *q_ret, Call *c) {
     *c = Call{};
     if (!unit_interval(gamma) || !unit_interval(lambda) || !positive_finite(c_bar))
         return RLCA_ERR_INVALID_VALUE;
-    const rlca_status st = prepare_backward(kRetrace, rewards, q_values, expected_q,
+    const rlca_status st = prepare_backward(kRetrace, storage, rewards, q_values, expected_q,
                                             behaviour_logp, target_logp, terminated, truncated,
                                             trunc_values, bootstrap, q_ret, nullptr, num_envs, T,
                                             c);
@@ -356,70 +386,75 @@ static rlca_status prepare_retrace(const float *rewards, const float *q_values,
     return st;
 }
 
-static rlca_status prepare_eligibility(const float *increments, const uint8_t *flags,
-                                       int convention, float gamma, float lambda,
-                                       int64_t num_envs, int64_t T, float *traces, Call *c) {
+static rlca_status prepare_eligibility(int storage, const void *increments,
+                                       const uint8_t *flags, int convention, float gamma,
+                                       float lambda, int64_t num_envs, int64_t T, void *traces,
+                                       Call *c) {
     *c = Call{};
     if (!unit_interval(gamma) || !unit_interval(lambda)) return RLCA_ERR_INVALID_VALUE;
-    return prepare_forward(kForwardFlags, increments, false, flags, convention, gamma * lambda,
-                           nullptr, nullptr, num_envs, T, traces, c);
+    return prepare_forward(kForwardFlags, storage, increments, false, flags, convention,
+                           gamma * lambda, nullptr, nullptr, num_envs, T, traces, c);
 }
 
+// dtype: RLCA_I32 (exact, wrapping) or a real storage type.
 static rlca_status prepare_prefix_sum(const void *x, int dtype, const uint8_t *flags,
                                       int convention, int64_t num_envs, int64_t T, void *out,
                                       Call *c) {
     *c = Call{};
-    if (dtype != RLCA_F32 && dtype != RLCA_I32) return RLCA_ERR_INVALID_VALUE;
-    return prepare_forward(kForwardFlags, x, dtype == RLCA_I32, flags, convention, 1.0f, nullptr,
+    const bool is_int = dtype == RLCA_I32;
+    const int storage = is_int ? (int)kStoreF32 : storage_of(dtype);
+    if (storage < 0) return RLCA_ERR_INVALID_VALUE;
+    return prepare_forward(kForwardFlags, storage, x, is_int, flags, convention, 1.0f, nullptr,
                            nullptr, num_envs, T, out, c);
 }
 
-static rlca_status prepare_affine(const float *alpha, const float *beta, const float *carry,
-                                  int direction, int64_t num_envs, int64_t T, float *out,
-                                  Call *c) {
+static rlca_status prepare_affine(int storage, const void *alpha, const void *beta,
+                                  const void *carry, int direction, int64_t num_envs, int64_t T,
+                                  void *out, Call *c) {
     *c = Call{};
     if (direction != RLCA_BACKWARD && direction != RLCA_FORWARD) return RLCA_ERR_INVALID_VALUE;
     if (direction == RLCA_BACKWARD)
-        return prepare_backward(kAffineBackward, alpha, beta, nullptr, nullptr, nullptr, nullptr,
-                                nullptr, nullptr, carry, out, nullptr, num_envs, T, c);
-    return prepare_forward(kForwardAffine, alpha, false, nullptr, 0, 0.f, beta, carry, num_envs,
-                           T, out, c);
+        return prepare_backward(kAffineBackward, storage, alpha, beta, nullptr, nullptr, nullptr,
+                                nullptr, nullptr, nullptr, carry, out, nullptr, num_envs, T, c);
+    return prepare_forward(kForwardAffine, storage, alpha, false, nullptr, 0, 0.f, beta, carry,
+                           num_envs, T, out, c);
 }
 
-// One rlca_call of a batch, prepared like its own entry point.
+// One rlca_call of a batch, prepared like its own entry point; `dtype` gives
+// the storage of every real-valued array (and int32 for the prefix sum).
 static rlca_status prepare_op(const rlca_call &k, Call *c) {
+    const int st = storage_of(k.dtype);  // -1 (rejected) for RLCA_I32 outside the prefix sum
     switch (k.op) {
         case RLCA_OP_GAE:
-            return prepare_gae(k.rewards, k.values, k.terminated, k.truncated, k.trunc_values,
-                               k.bootstrap, k.gamma, k.lambda, k.num_envs, k.T,
-                               static_cast<float *>(k.out0), static_cast<float *>(k.out1), c);
+            return prepare_gae(st, k.rewards, k.values, k.terminated, k.truncated,
+                               k.trunc_values, k.bootstrap, k.gamma, k.lambda, k.num_envs, k.T,
+                               k.out0, k.out1, c);
         case RLCA_OP_TD_LAMBDA:
-            return prepare_td_lambda(k.rewards, k.values, k.terminated, k.truncated,
+            return prepare_td_lambda(st, k.rewards, k.values, k.terminated, k.truncated,
                                      k.trunc_values, k.bootstrap, k.gamma, k.lambda, k.num_envs,
-                                     k.T, static_cast<float *>(k.out0), c);
+                                     k.T, k.out0, c);
         case RLCA_OP_DISCOUNTED_RETURNS:
-            return prepare_discounted(k.rewards, k.terminated, k.truncated, k.trunc_values,
-                                      k.bootstrap, k.gamma, k.num_envs, k.T,
-                                      static_cast<float *>(k.out0), c);
+            return prepare_discounted(st, k.rewards, k.terminated, k.truncated, k.trunc_values,
+                                      k.bootstrap, k.gamma, k.num_envs, k.T, k.out0, c);
         case RLCA_OP_VTRACE:
-            return prepare_vtrace(k.rewards, k.values, k.behaviour_logp, k.target_logp,
+            return prepare_vtrace(st, k.rewards, k.values, k.behaviour_logp, k.target_logp,
                                   k.terminated, k.truncated, k.trunc_values, k.bootstrap,
                                   k.gamma, k.lambda, k.rho_bar, k.c_bar, k.num_envs, k.T,
-                                  static_cast<float *>(k.out0), static_cast<float *>(k.out1), c);
+                                  k.out0, k.out1, c);
         case RLCA_OP_RETRACE:
-            return prepare_retrace(k.rewards, k.values, k.expected_q, k.behaviour_logp,
+            return prepare_retrace(st, k.rewards, k.values, k.expected_q, k.behaviour_logp,
                                    k.target_logp, k.terminated, k.truncated, k.trunc_values,
                                    k.bootstrap, k.gamma, k.lambda, k.c_bar, k.num_envs, k.T,
-                                   static_cast<float *>(k.out0), c);
+                                   k.out0, c);
         case RLCA_OP_ELIGIBILITY_TRACES:
-            return prepare_eligibility(k.rewards, k.terminated, k.convention, k.gamma, k.lambda,
-                                       k.num_envs, k.T, static_cast<float *>(k.out0), c);
+            return prepare_eligibility(st, k.rewards, k.terminated, k.convention, k.gamma,
+                                       k.lambda, k.num_envs, k.T, k.out0, c);
         case RLCA_OP_EPISODIC_PREFIX_SUM:
             return prepare_prefix_sum(k.rewards, k.dtype, k.terminated, k.convention, k.num_envs,
                                       k.T, k.out0, c);
         case RLCA_OP_AFFINE_SCAN:
-            return prepare_affine(k.rewards, k.values, k.bootstrap, k.direction, k.num_envs, k.T,
-                                  static_cast<float *>(k.out0), c);
+            return prepare_affine(st, k.rewards, k.values, k.bootstrap, k.direction, k.num_envs,
+                                  k.T, k.out0, c);
     }
     *c = Call{};
     return RLCA_ERR_INVALID_VALUE;
@@ -440,7 +475,7 @@ rlca_status rlca_gae(const float *rewards, const float *values, const uint8_t *t
                      const float *bootstrap, float gamma, float lambda, int64_t num_envs,
                      int64_t T, float *advantages, float *returns, hipStream_t stream) {
     Call c;
-    return run_one(prepare_gae(rewards, values, terminated, truncated, trunc_values, bootstrap,
+    return run_one(prepare_gae(kStoreF32, rewards, values, terminated, truncated, trunc_values, bootstrap,
                                gamma, lambda, num_envs, T, advantages, returns, &c),
                    c, stream);
 }
@@ -451,7 +486,7 @@ rlca_status rlca_td_lambda(const float *rewards, const float *values,
                            float lambda, int64_t num_envs, int64_t T, float *returns,
                            hipStream_t stream) {
     Call c;
-    return run_one(prepare_td_lambda(rewards, values, terminated, truncated, trunc_values,
+    return run_one(prepare_td_lambda(kStoreF32, rewards, values, terminated, truncated, trunc_values,
                                      bootstrap, gamma, lambda, num_envs, T, returns, &c),
                    c, stream);
 }
@@ -461,7 +496,7 @@ rlca_status rlca_discounted_returns(const float *rewards, const uint8_t *termina
                                     const float *bootstrap, float gamma, int64_t num_envs,
                                     int64_t T, float *returns, hipStream_t stream) {
     Call c;
-    return run_one(prepare_discounted(rewards, terminated, truncated, trunc_values, bootstrap,
+    return run_one(prepare_discounted(kStoreF32, rewards, terminated, truncated, trunc_values, bootstrap,
                                       gamma, num_envs, T, returns, &c),
                    c, stream);
 }
@@ -473,7 +508,7 @@ rlca_status rlca_vtrace(const float *rewards, const float *values, const float *
                         float c_bar, int64_t num_envs, int64_t T, float *vs,
                         float *pg_advantages, hipStream_t stream) {
     Call c;
-    return run_one(prepare_vtrace(rewards, values, behaviour_logp, target_logp, terminated,
+    return run_one(prepare_vtrace(kStoreF32, rewards, values, behaviour_logp, target_logp, terminated,
                                   truncated, trunc_values, bootstrap, gamma, lambda, rho_bar,
                                   c_bar, num_envs, T, vs, pg_advantages, &c),
                    c, stream);
@@ -486,7 +521,7 @@ rlca_status rlca_retrace(const float *rewards, const float *q_values, const floa
                          float lambda, float c_bar, int64_t num_envs, int64_t T,
                          float *q_ret, hipStream_t stream) {
     Call c;
-    return run_one(prepare_retrace(rewards, q_values, expected_q, behaviour_logp, target_logp,
+    return run_one(prepare_retrace(kStoreF32, rewards, q_values, expected_q, behaviour_logp, target_logp,
                                    terminated, truncated, trunc_values, bootstrap, gamma, lambda,
                                    c_bar, num_envs, T, q_ret, &c),
                    c, stream);
@@ -497,7 +532,7 @@ rlca_status rlca_eligibility_traces(const float *increments, const uint8_t *flag
                                     float lambda, int64_t num_envs, int64_t T, float *traces,
                                     hipStream_t stream) {
     Call c;
-    return run_one(prepare_eligibility(increments, flags, convention, gamma, lambda, num_envs, T,
+    return run_one(prepare_eligibility(kStoreF32, increments, flags, convention, gamma, lambda, num_envs, T,
                                        traces, &c),
                    c, stream);
 }
@@ -514,7 +549,7 @@ rlca_status rlca_affine_scan(const float *alpha, const float *beta, const float 
                              rlca_direction direction, int64_t num_envs, int64_t T, float *out,
                              hipStream_t stream) {
     Call c;
-    return run_one(prepare_affine(alpha, beta, carry, direction, num_envs, T, out, &c), c,
+    return run_one(prepare_affine(kStoreF32, alpha, beta, carry, direction, num_envs, T, out, &c), c,
                    stream);
 }
 
@@ -544,16 +579,18 @@ rlca_status rlca_run_batch(const rlca_call *calls, int count, hipStream_t stream
     // Vector-path, single-launch calls share grouped launches; the rest
     // (unaligned or chunked) are enqueued one by one.  A grouped launch that
     // would hold one call runs that call's own kernel instead.
+    // Members of one grouped launch share the storage type of their
+    // real-valued arrays (int32 sums join the 4-byte group).
     GroupedLaunch group;
     int members[kMaxGroupedCalls];
-    int count_in_group = 0;
+    int count_in_group = 0, group_storage = kStoreF32;
     auto flush = [&]() -> rlca_status {
         if (count_in_group == 0) return RLCA_OK;
         const int n = count_in_group;
         count_in_group = 0;
         if (n == 1) return launch_call(prepared[members[0]], stream);
         for (int m = n; m < kMaxGroupedCalls; ++m) group.head[m] = kHeadEndMask;
-        return launch_grouped(group, stream);
+        return launch_grouped(group, group_storage, stream);
     };
     group.workgroups = 0;
     for (int i = 0; i < count; ++i) {
@@ -567,11 +604,12 @@ rlca_status rlca_run_batch(const rlca_call *calls, int count, hipStream_t stream
             if (st != RLCA_OK) return st;
             continue;
         }
-        if (count_in_group == kMaxGroupedCalls || group.workgroups + wgs > kMaxGrid) {
+        if (count_in_group == kMaxGroupedCalls || group.workgroups + wgs > kMaxGrid ||
+            (count_in_group > 0 && c.storage != group_storage)) {
             const rlca_status st = flush();
             if (st != RLCA_OK) return st;
         }
-        if (count_in_group == 0) group.workgroups = 0;
+        if (count_in_group == 0) group.workgroups = 0, group_storage = c.storage;
         group.workgroups += wgs;
         group.args.calls[count_in_group] = member;
         group.head[count_in_group] = group.workgroups | ((uint32_t)variant << kHeadVariantShift);

@@ -27,6 +27,10 @@ RESET_ON_START = 0
 RESET_AFTER_DONE = 1
 RLCA_F32 = 0
 RLCA_I32 = 1
+RLCA_BF16 = 2
+RLCA_F16 = 3
+# storage types of real-valued arrays (arithmetic is fp32 for all of them)
+REAL_DTYPES = {torch.float32: RLCA_F32, torch.bfloat16: RLCA_BF16, torch.float16: RLCA_F16}
 BACKWARD = 0
 FORWARD = 1
 
@@ -131,13 +135,21 @@ def _rollout_shape(rewards: torch.Tensor):
     return tuple(rewards.shape), rewards.device
 
 
-def _boundary(terminated, truncated, trunc_values, bootstrap, shape, dev):
+def _real_dtype(name, t: torch.Tensor):
+    """The storage type of a call's real-valued arrays, taken from its first
+    real input: float32, bfloat16 or float16."""
+    if t.dtype not in REAL_DTYPES:
+        raise TypeError(f"{name} must be float32, bfloat16 or float16, got {t.dtype}")
+    return t.dtype
+
+
+def _boundary(terminated, truncated, trunc_values, bootstrap, shape, dev, fdt):
     term = _steps("terminated", terminated, shape, "flag", dev)
     trunc = _steps("truncated", truncated, shape, "flag", dev, optional=True)
-    tv = _steps("trunc_values", trunc_values, shape, torch.float32, dev, optional=True)
+    tv = _steps("trunc_values", trunc_values, shape, fdt, dev, optional=True)
     if trunc is not None and tv is None:
         raise ValueError("trunc_values is required when truncated is given")
-    boot = _steps("bootstrap", bootstrap, shape[:1], torch.float32, dev, optional=True)
+    boot = _steps("bootstrap", bootstrap, shape[:1], fdt, dev, optional=True)
     return term, trunc, tv if trunc is not None else None, boot
 
 
@@ -156,6 +168,10 @@ class _Prepared:
     def __init__(self, op, shape, dev, result, **fields):
         self.op, self.shape, self.dev, self.result, self.fields = op, shape, dev, result, fields
 
+    @property
+    def f32(self):
+        return self.fields.get("dtype", RLCA_F32) == RLCA_F32
+
     def arg(self, name, default=None):
         v = self.fields.get(name, default)
         return _ptr(v) if isinstance(v, torch.Tensor) else v
@@ -167,90 +183,103 @@ class _Prepared:
 def _prepare_gae(rewards, values, terminated, truncated=None, trunc_values=None, bootstrap=None,
                  gamma=0.99, lam=0.95, with_returns=True, advantages=None, returns=None):
     shape, dev = _rollout_shape(rewards)
-    r = _steps("rewards", rewards, shape, torch.float32, dev)
-    v = _steps("values", values, shape, torch.float32, dev)
-    term, trunc, tv, boot = _boundary(terminated, truncated, trunc_values, bootstrap, shape, dev)
-    adv = _out(advantages, shape, dev, name="advantages")
-    ret = _out(returns, shape, dev, name="returns") if with_returns else None
+    fdt = _real_dtype("rewards", rewards)
+    r = _steps("rewards", rewards, shape, fdt, dev)
+    v = _steps("values", values, shape, fdt, dev)
+    term, trunc, tv, boot = _boundary(terminated, truncated, trunc_values, bootstrap, shape, dev,
+                                      fdt)
+    adv = _out(advantages, shape, dev, fdt, name="advantages")
+    ret = _out(returns, shape, dev, fdt, name="returns") if with_returns else None
     return _Prepared(OP_GAE, shape, dev, (adv, ret), rewards=r, values=v, terminated=term,
                      truncated=trunc, trunc_values=tv, bootstrap=boot, gamma=gamma, lambda_=lam,
-                     out0=adv, out1=ret)
+                     out0=adv, out1=ret, dtype=REAL_DTYPES[fdt])
 
 
 def _prepare_td_lambda(rewards, values, terminated, truncated=None, trunc_values=None,
                        bootstrap=None, gamma=0.99, lam=0.95, out=None):
     shape, dev = _rollout_shape(rewards)
-    r = _steps("rewards", rewards, shape, torch.float32, dev)
-    v = _steps("values", values, shape, torch.float32, dev)
-    term, trunc, tv, boot = _boundary(terminated, truncated, trunc_values, bootstrap, shape, dev)
-    g = _out(out, shape, dev)
+    fdt = _real_dtype("rewards", rewards)
+    r = _steps("rewards", rewards, shape, fdt, dev)
+    v = _steps("values", values, shape, fdt, dev)
+    term, trunc, tv, boot = _boundary(terminated, truncated, trunc_values, bootstrap, shape, dev,
+                                      fdt)
+    g = _out(out, shape, dev, fdt)
     return _Prepared(OP_TD_LAMBDA, shape, dev, g, rewards=r, values=v, terminated=term,
                      truncated=trunc, trunc_values=tv, bootstrap=boot, gamma=gamma, lambda_=lam,
-                     out0=g)
+                     out0=g, dtype=REAL_DTYPES[fdt])
 
 
 def _prepare_discounted_returns(rewards, terminated, truncated=None, trunc_values=None,
                                 bootstrap=None, gamma=0.99, out=None):
     shape, dev = _rollout_shape(rewards)
-    r = _steps("rewards", rewards, shape, torch.float32, dev)
-    term, trunc, tv, boot = _boundary(terminated, truncated, trunc_values, bootstrap, shape, dev)
-    g = _out(out, shape, dev)
+    fdt = _real_dtype("rewards", rewards)
+    r = _steps("rewards", rewards, shape, fdt, dev)
+    term, trunc, tv, boot = _boundary(terminated, truncated, trunc_values, bootstrap, shape, dev,
+                                      fdt)
+    g = _out(out, shape, dev, fdt)
     return _Prepared(OP_DISCOUNTED, shape, dev, g, rewards=r, terminated=term, truncated=trunc,
-                     trunc_values=tv, bootstrap=boot, gamma=gamma, out0=g)
+                     trunc_values=tv, bootstrap=boot, gamma=gamma, out0=g,
+                     dtype=REAL_DTYPES[fdt])
 
 
 def _prepare_vtrace(rewards, values, behaviour_logp, target_logp, terminated, truncated=None,
                     trunc_values=None, bootstrap=None, gamma=0.99, lam=1.0, rho_bar=1.0,
                     c_bar=1.0, with_pg=True, vs=None, pg_advantages=None):
     shape, dev = _rollout_shape(rewards)
-    r = _steps("rewards", rewards, shape, torch.float32, dev)
-    v = _steps("values", values, shape, torch.float32, dev)
-    mu = _steps("behaviour_logp", behaviour_logp, shape, torch.float32, dev)
-    pi = _steps("target_logp", target_logp, shape, torch.float32, dev)
-    term, trunc, tv, boot = _boundary(terminated, truncated, trunc_values, bootstrap, shape, dev)
-    o_vs = _out(vs, shape, dev, name="vs")
-    o_pg = _out(pg_advantages, shape, dev, name="pg_advantages") if with_pg else None
+    fdt = _real_dtype("rewards", rewards)
+    r = _steps("rewards", rewards, shape, fdt, dev)
+    v = _steps("values", values, shape, fdt, dev)
+    mu = _steps("behaviour_logp", behaviour_logp, shape, fdt, dev)
+    pi = _steps("target_logp", target_logp, shape, fdt, dev)
+    term, trunc, tv, boot = _boundary(terminated, truncated, trunc_values, bootstrap, shape, dev,
+                                      fdt)
+    o_vs = _out(vs, shape, dev, fdt, name="vs")
+    o_pg = _out(pg_advantages, shape, dev, fdt, name="pg_advantages") if with_pg else None
     return _Prepared(OP_VTRACE, shape, dev, (o_vs, o_pg), rewards=r, values=v,
                      behaviour_logp=mu, target_logp=pi, terminated=term, truncated=trunc,
                      trunc_values=tv, bootstrap=boot, gamma=gamma, lambda_=lam, rho_bar=rho_bar,
-                     c_bar=c_bar, out0=o_vs, out1=o_pg)
+                     c_bar=c_bar, out0=o_vs, out1=o_pg, dtype=REAL_DTYPES[fdt])
 
 
 def _prepare_retrace(rewards, q_values, expected_q, behaviour_logp, target_logp, terminated,
                      truncated=None, trunc_values=None, bootstrap=None, gamma=0.99, lam=0.95,
                      c_bar=1.0, out=None):
     shape, dev = _rollout_shape(rewards)
-    r = _steps("rewards", rewards, shape, torch.float32, dev)
-    q = _steps("q_values", q_values, shape, torch.float32, dev)
-    eq = _steps("expected_q", expected_q, shape, torch.float32, dev)
-    mu = _steps("behaviour_logp", behaviour_logp, shape, torch.float32, dev)
-    pi = _steps("target_logp", target_logp, shape, torch.float32, dev)
-    term, trunc, tv, boot = _boundary(terminated, truncated, trunc_values, bootstrap, shape, dev)
-    o = _out(out, shape, dev)
+    fdt = _real_dtype("rewards", rewards)
+    r = _steps("rewards", rewards, shape, fdt, dev)
+    q = _steps("q_values", q_values, shape, fdt, dev)
+    eq = _steps("expected_q", expected_q, shape, fdt, dev)
+    mu = _steps("behaviour_logp", behaviour_logp, shape, fdt, dev)
+    pi = _steps("target_logp", target_logp, shape, fdt, dev)
+    term, trunc, tv, boot = _boundary(terminated, truncated, trunc_values, bootstrap, shape, dev,
+                                      fdt)
+    o = _out(out, shape, dev, fdt)
     return _Prepared(OP_RETRACE, shape, dev, o, rewards=r, values=q, expected_q=eq,
                      behaviour_logp=mu, target_logp=pi, terminated=term, truncated=trunc,
                      trunc_values=tv, bootstrap=boot, gamma=gamma, lambda_=lam, c_bar=c_bar,
-                     out0=o)
+                     out0=o, dtype=REAL_DTYPES[fdt])
 
 
 def _prepare_eligibility_traces(increments, flags, convention=RESET_ON_START, gamma=0.99,
                                 lam=0.9, out=None):
     shape, dev = _rollout_shape(increments)
-    x = _steps("increments", increments, shape, torch.float32, dev)
+    fdt = _real_dtype("increments", increments)
+    x = _steps("increments", increments, shape, fdt, dev)
     f = _steps("flags", flags, shape, "flag", dev)
-    o = _out(out, shape, dev)
+    o = _out(out, shape, dev, fdt)
     return _Prepared(OP_TRACES, shape, dev, o, rewards=x, terminated=f,
-                     convention=int(convention), gamma=gamma, lambda_=lam, out0=o)
+                     convention=int(convention), gamma=gamma, lambda_=lam, out0=o,
+                     dtype=REAL_DTYPES[fdt])
 
 
 def _prepare_episodic_prefix_sum(x, flags, convention=RESET_ON_START, out=None):
     shape, dev = _rollout_shape(x)
-    if x.dtype == torch.float32:
-        dtype = RLCA_F32
-    elif x.dtype == torch.int32:
+    if x.dtype == torch.int32:
         dtype = RLCA_I32
+    elif x.dtype in REAL_DTYPES:
+        dtype = REAL_DTYPES[x.dtype]
     else:
-        raise TypeError(f"x must be float32 or int32, got {x.dtype}")
+        raise TypeError(f"x must be float32, bfloat16, float16 or int32, got {x.dtype}")
     xs = _steps("x", x, shape, x.dtype, dev)
     f = _steps("flags", flags, shape, "flag", dev)
     o = _out(out, shape, dev, dtype=x.dtype)
@@ -260,12 +289,22 @@ def _prepare_episodic_prefix_sum(x, flags, convention=RESET_ON_START, out=None):
 
 def _prepare_affine_scan(alpha, beta, carry=None, direction=BACKWARD, out=None):
     shape, dev = _rollout_shape(alpha)
-    a = _steps("alpha", alpha, shape, torch.float32, dev)
-    b = _steps("beta", beta, shape, torch.float32, dev)
-    c = _steps("carry", carry, shape[:1], torch.float32, dev, optional=True)
-    o = _out(out, shape, dev)
+    fdt = _real_dtype("alpha", alpha)
+    a = _steps("alpha", alpha, shape, fdt, dev)
+    b = _steps("beta", beta, shape, fdt, dev)
+    c = _steps("carry", carry, shape[:1], fdt, dev, optional=True)
+    o = _out(out, shape, dev, fdt)
     return _Prepared(OP_AFFINE, shape, dev, o, rewards=a, values=b, bootstrap=c,
-                     direction=int(direction), out0=o)
+                     direction=int(direction), out0=o, dtype=REAL_DTYPES[fdt])
+
+
+def _run_alone(p: _Prepared):
+    """Enqueue one bf16 / fp16 call: its entry point is rlca_run_batch (the
+    single-call entry points are fp32)."""
+    b = Batch()
+    b._add(p)
+    b.run()
+    return p.result
 
 
 def _takes_args_of(prepare):
@@ -280,6 +319,8 @@ def _takes_args_of(prepare):
 def gae(*args, **kwargs):
     """GAE advantages (and value targets adv + V).  Returns (advantages, returns|None)."""
     p = _prepare_gae(*args, **kwargs)
+    if not p.f32:
+        return _run_alone(p)
     _check(lib().rlca_gae(p.arg("rewards"), p.arg("values"), p.arg("terminated"),
                           p.arg("truncated"), p.arg("trunc_values"), p.arg("bootstrap"),
                           p.arg("gamma"), p.arg("lambda_"), *p.shape, p.arg("out0"),
@@ -291,6 +332,8 @@ def gae(*args, **kwargs):
 def td_lambda(*args, **kwargs):
     """TD(lambda) returns."""
     p = _prepare_td_lambda(*args, **kwargs)
+    if not p.f32:
+        return _run_alone(p)
     _check(lib().rlca_td_lambda(p.arg("rewards"), p.arg("values"), p.arg("terminated"),
                                 p.arg("truncated"), p.arg("trunc_values"), p.arg("bootstrap"),
                                 p.arg("gamma"), p.arg("lambda_"), *p.shape, p.arg("out0"),
@@ -302,6 +345,8 @@ def td_lambda(*args, **kwargs):
 def discounted_returns(*args, **kwargs):
     """Discounted returns (Monte-Carlo when bootstrap is None)."""
     p = _prepare_discounted_returns(*args, **kwargs)
+    if not p.f32:
+        return _run_alone(p)
     _check(lib().rlca_discounted_returns(p.arg("rewards"), p.arg("terminated"),
                                          p.arg("truncated"), p.arg("trunc_values"),
                                          p.arg("bootstrap"), p.arg("gamma"), *p.shape,
@@ -313,6 +358,8 @@ def discounted_returns(*args, **kwargs):
 def vtrace(*args, **kwargs):
     """V-Trace targets and policy-gradient advantages.  Returns (vs, pg|None)."""
     p = _prepare_vtrace(*args, **kwargs)
+    if not p.f32:
+        return _run_alone(p)
     _check(lib().rlca_vtrace(p.arg("rewards"), p.arg("values"), p.arg("behaviour_logp"),
                              p.arg("target_logp"), p.arg("terminated"), p.arg("truncated"),
                              p.arg("trunc_values"), p.arg("bootstrap"), p.arg("gamma"),
@@ -325,6 +372,8 @@ def vtrace(*args, **kwargs):
 def retrace(*args, **kwargs):
     """Retrace(lambda) targets Q^ret."""
     p = _prepare_retrace(*args, **kwargs)
+    if not p.f32:
+        return _run_alone(p)
     _check(lib().rlca_retrace(p.arg("rewards"), p.arg("values"), p.arg("expected_q"),
                               p.arg("behaviour_logp"), p.arg("target_logp"),
                               p.arg("terminated"), p.arg("truncated"), p.arg("trunc_values"),
@@ -338,6 +387,8 @@ def retrace(*args, **kwargs):
 def eligibility_traces(*args, **kwargs):
     """Accumulating eligibility traces, forward in time."""
     p = _prepare_eligibility_traces(*args, **kwargs)
+    if not p.f32:
+        return _run_alone(p)
     _check(lib().rlca_eligibility_traces(p.arg("rewards"), p.arg("terminated"),
                                          p.arg("convention"), p.arg("gamma"),
                                          p.arg("lambda_"), *p.shape, p.arg("out0"),
@@ -360,6 +411,8 @@ def affine_scan(*args, **kwargs):
     """A_t = alpha_t + beta_t * A_{t+1} (BACKWARD, A_T = carry) or
     A_t = alpha_t + beta_t * A_{t-1} (FORWARD, A_{-1} = carry), float32."""
     p = _prepare_affine_scan(*args, **kwargs)
+    if not p.f32:
+        return _run_alone(p)
     _check(lib().rlca_affine_scan(p.arg("rewards"), p.arg("values"), p.arg("bootstrap"),
                                   p.arg("direction"), *p.shape, p.arg("out0"), p.stream()),
            "rlca_affine_scan")

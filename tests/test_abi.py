@@ -195,3 +195,24 @@ def test_batch_cross_call_aliasing(lib):
                      first) == ALIAS
     # an empty call is exempt
     assert run_batch(lib, call(n=0, out0=A), call(n=0, rewards=D)) == OK
+
+
+def test_batch_dtype_validation(lib):
+    bf16, f16, i32 = 2, 3, 1
+    assert run_batch(lib, call(dtype=9)) == VALUE
+    assert run_batch(lib, call(dtype=i32)) == VALUE          # int32 only for the prefix sum
+    affine = dict(op=binding.OP_AFFINE, rewards=A, values=B, out0=C)
+    assert run_batch(lib, call(dtype=i32, **affine)) == VALUE
+    # 16-bit storage: 2-byte alignment suffices, odd addresses do not
+    assert run_batch(lib, call(dtype=bf16, rewards=A + 1)) == MISAL
+    assert run_batch(lib, call(dtype=f16, out0=D + 3)) == MISAL
+    assert run_batch(lib, call(dtype=bf16, rewards=A + 2, n=0)) == OK
+    assert run_batch(lib, call(dtype=0, rewards=A + 2)) == MISAL          # fp32 needs 4 bytes
+    # byte ranges use the storage size: with bf16 the values span n*T*2 bytes
+    n, t = 4, 8
+    assert run_batch(lib, call(dtype=bf16, out0=B + n * t * 2 - 2)) == ALIAS
+    assert run_batch(lib, call(dtype=bf16, out0=B + n * t * 4 - 4, t=-1)) == SIZE
+    prefix = dict(op=binding.OP_PREFIX_SUM, rewards=A + 1, terminated=B, out0=C)
+    assert run_batch(lib, call(dtype=f16, **prefix)) == MISAL
+    assert lib.rlca_episodic_prefix_sum(A + 1, bf16, B, 0, 4, 8, C, None) == MISAL
+    assert lib.rlca_episodic_prefix_sum(A, 7, B, 0, 4, 8, C, None) == VALUE
