@@ -10,6 +10,10 @@ Definitions follow "rl-triton: High-Performance Triton GPU Kernels for
 Reinforcement Learning Credit Assignment" (paperlayer.ai summary), §1, §2.1,
 §3.2, §3.3, §5 and §8; the header of ``oracle.c`` states the boundary rules.
 
+The fused consumers (``mean_std``, ``ppo_clip_loss``) follow the standard
+advantage normalization and the PPO clipped surrogate of Schulman et al. 2017;
+the summary's §9 names fused loss operations as the next step.
+
 Pins (tests/test_oracle_pins.py): brute-force unrolled sums on tiny inputs,
 products-of-coefficients sums for the generic affine scan,
 closed forms, the cross-estimator identities (GAE lambda=0 / lambda=1,
@@ -63,6 +67,9 @@ def _load():
             "oracle_episodic_prefix_sum_f32": [_f32p, _u8p, ctypes.c_int, _i64, _i64, _f64p],
             "oracle_episodic_prefix_sum_i32": [_i32p, _u8p, ctypes.c_int, _i64, _i64, _i32p],
             "oracle_affine_scan": [_f32p, _f32p, _f32p, ctypes.c_int, _i64, _i64, _f64p],
+            "oracle_mean_std": [_f64p, _i64, _f64p, _f64p],
+            "oracle_ppo_clip_loss": [_f32p, _f32p, _f32p, _i64, ctypes.c_int, _dbl, _dbl, _dbl,
+                                     _dbl, _f64p, _f64p],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -236,3 +243,28 @@ def affine_scan(alpha, beta, carry=None, direction=BACKWARD):
     out = np.empty(shape, np.float64)
     _load().oracle_affine_scan(ap, bp, cp, int(direction), n, t, out.ctypes.data_as(_f64p))
     return out
+
+
+def mean_std(x):
+    """(mean, sample std with divisor M - 1) of all elements of x, in fp64."""
+    a = np.ascontiguousarray(np.asarray(x, np.float64).ravel())
+    mean, std = ctypes.c_double(), ctypes.c_double()
+    _load().oracle_mean_std(a.ctypes.data_as(_f64p), a.size, ctypes.byref(mean),
+                            ctypes.byref(std))
+    return mean.value, std.value
+
+
+def ppo_clip_loss(adv, logp_new, logp_old, stats=None, clip_eps=0.2, norm_eps=1e-8):
+    """PPO clipped-surrogate loss and its gradient w.r.t. logp_new, float64.
+    stats = (mean, std) normalizes the advantages first; None uses them raw."""
+    a = np.ascontiguousarray(np.asarray(adv, np.float32).ravel())
+    shape = np.asarray(adv).shape
+    new, newp = _arr(np.asarray(logp_new, np.float32).ravel(), np.float32, a.shape)
+    old, oldp = _arr(np.asarray(logp_old, np.float32).ravel(), np.float32, a.shape)
+    mean, std = stats if stats is not None else (0.0, 1.0)
+    loss = ctypes.c_double()
+    grad = np.empty(a.shape, np.float64)
+    _load().oracle_ppo_clip_loss(a.ctypes.data_as(_f32p), newp, oldp, a.size,
+                                 1 if stats is not None else 0, mean, std, norm_eps, clip_eps,
+                                 ctypes.byref(loss), grad.ctypes.data_as(_f64p))
+    return loss.value, grad.reshape(shape)

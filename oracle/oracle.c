@@ -310,3 +310,36 @@ void oracle_affine_scan(const float *alpha, const float *beta, const float *carr
         }
     }
 }
+
+/* Two passes over the data: the mean first, then the sum of squared
+ * deviations from it. */
+void oracle_mean_std(const double *x, int64_t M, double *mean, double *std)
+{
+    double s = 0.0;
+    for (int64_t i = 0; i < M; ++i) s += x[i];
+    const double mu = M > 0 ? s / (double)M : 0.0;
+    double ss = 0.0;
+    for (int64_t i = 0; i < M; ++i) ss += (x[i] - mu) * (x[i] - mu);
+    *mean = mu;
+    *std = M > 1 ? sqrt(ss / (double)(M - 1)) : 0.0;
+}
+
+/* The clipped surrogate term by term, then its mean. */
+void oracle_ppo_clip_loss(const float *adv, const float *logp_new, const float *logp_old,
+                          int64_t M, int normalize, double mean, double std, double norm_eps,
+                          double clip_eps, double *loss, double *grad)
+{
+    double total = 0.0;
+    for (int64_t i = 0; i < M; ++i) {
+        const double a = normalize ? ((double)adv[i] - mean) / (std + norm_eps) : (double)adv[i];
+        const double rho = exp((double)logp_new[i] - (double)logp_old[i]);
+        double clipped_rho = rho;
+        if (clipped_rho < 1.0 - clip_eps) clipped_rho = 1.0 - clip_eps;
+        if (clipped_rho > 1.0 + clip_eps) clipped_rho = 1.0 + clip_eps;
+        const double unclipped = rho * a, clipped = clipped_rho * a;
+        const int take_unclipped = unclipped <= clipped;
+        total += take_unclipped ? unclipped : clipped;
+        if (grad != NULL) grad[i] = take_unclipped ? -unclipped / (double)M : 0.0;
+    }
+    *loss = M > 0 ? -total / (double)M : 0.0;
+}

@@ -82,6 +82,27 @@ void oracle_episodic_prefix_sum_i32(const int32_t *x, const uint8_t *flags, int 
 void oracle_affine_scan(const float *alpha, const float *beta, const float *carry, int direction,
                         int64_t num_envs, int64_t T, double *out);
 
+/* ---- fused consumers of the advantages (summary §9 Discussion and Future
+ * Work names fused loss operations; the definitions below are the standard
+ * ones the pages leave implicit). */
+
+/* Mean and sample standard deviation (divisor M - 1; 0 when M < 2) of
+ * x[0..M), in two passes: the mean, then the squared deviations from it. */
+void oracle_mean_std(const double *x, int64_t M, double *mean, double *std);
+
+/* PPO clipped surrogate (Schulman et al. 2017, "Proximal Policy Optimization
+ * Algorithms", the L^CLIP objective) over M steps, as a loss to minimize:
+ *   A_hat_t = normalize ? (A_t - mean) / (std + norm_eps) : A_t
+ *   rho_t   = exp(logp_new_t - logp_old_t)
+ *   loss    = -(1/M) sum_t min(rho_t A_hat_t, clip(rho_t, 1-eps, 1+eps) A_hat_t)
+ *   grad_t  = d loss / d logp_new_t
+ *           = -(1/M) rho_t A_hat_t where the unclipped term is the smaller
+ *             of the two (ties included), 0 where the clipped one is.
+ * grad may be NULL. */
+void oracle_ppo_clip_loss(const float *adv, const float *logp_new, const float *logp_old,
+                          int64_t M, int normalize, double mean, double std, double norm_eps,
+                          double clip_eps, double *loss, double *grad);
+
 #ifdef __cplusplus
 }
 #endif

@@ -480,3 +480,90 @@ def test_affine_scan_reproduces_the_estimators():
     bf[:, 0] = 0.0
     close(oracle.affine_scan(x, bf, None, oracle.FORWARD),
           oracle.eligibility_traces(x, starts, 0, g, lam), 1e-6)
+
+
+# ------------------------------------------------ fused consumers of the advantages
+
+
+def test_mean_std_closed_forms():
+    # 1..n: mean (n+1)/2, sample variance n(n+1)/12
+    for n in (2, 3, 10, 1001):
+        mean, std = oracle.mean_std(np.arange(1, n + 1))
+        assert mean == pytest.approx((n + 1) / 2, rel=1e-15)
+        assert std == pytest.approx(math.sqrt(n * (n + 1) / 12), rel=1e-14)
+    assert oracle.mean_std([3.5] * 17) == (3.5, 0.0)
+    assert oracle.mean_std([2.0, -1.0]) == (0.5, pytest.approx(3 / math.sqrt(2), rel=1e-15))
+    assert oracle.mean_std([7.0]) == (7.0, 0.0)      # fewer than two values: std 0
+
+
+def _ppo_inputs(seed, M, spread):
+    rng = np.random.default_rng(seed)
+    adv = rng.standard_normal(M).astype(np.float32) * 2 + 0.5
+    old = rng.normal(-1.0, 0.5, M).astype(np.float32)
+    new = (old + rng.normal(0.0, spread, M)).astype(np.float32)
+    return adv, new, old
+
+
+def test_ppo_on_policy_recovers_normalized_advantages():
+    """rho = 1: the loss is -mean(A_hat), which normalization makes 0, and the
+    gradient is -A_hat / M, so A_hat = -M grad must have mean 0 and sample
+    std 1 (norm_eps = 0).  Pins the normalization and the gradient scale."""
+    adv, _, old = _ppo_inputs(1, 500, 0.0)
+    stats = oracle.mean_std(adv)
+    loss, grad = oracle.ppo_clip_loss(adv, old, old, stats, 0.2, 0.0)
+    a_hat = -500 * grad
+    assert abs(loss) < 1e-14
+    assert abs(a_hat.mean()) < 1e-13
+    assert a_hat.std(ddof=1) == pytest.approx(1.0, rel=1e-13)
+    assert np.allclose(a_hat, (adv.astype(np.float64) - stats[0]) / stats[1], rtol=1e-13,
+                       atol=1e-13)
+    # without normalization the raw advantages pass through
+    loss, grad = oracle.ppo_clip_loss(adv, old, old, None, 0.2)
+    assert loss == pytest.approx(-adv.astype(np.float64).mean(), rel=1e-13)
+
+
+def test_ppo_clip_branches():
+    """Each sign of A_hat against each side of the clip interval, eps = 0.2."""
+    M = 4
+    adv = np.array([1.0, 1.0, -1.0, -1.0], np.float32)
+    old = np.zeros(M, np.float32)
+    new = np.log(np.array([1.5, 0.5, 1.5, 0.5])).astype(np.float32)
+    rho = np.exp(new.astype(np.float64))
+    loss, grad = oracle.ppo_clip_loss(adv, new, old, None, 0.2)
+    # A > 0: the clip caps the gain above 1.2 (no gradient); below 0.8 the
+    # unclipped, smaller term is kept.  A < 0: above 1.2 the unclipped, more
+    # negative term is kept; below 0.8 the clip holds the term at 0.8 A.
+    terms = np.array([1.2 * 1.0, rho[1] * 1.0, rho[2] * -1.0, 0.8 * -1.0])
+    assert loss == pytest.approx(-terms.mean(), rel=1e-15)
+    assert np.allclose(grad, [0.0, -rho[1] / M, rho[2] / M, 0.0], rtol=1e-15, atol=0)
+
+
+def test_ppo_inside_the_clip_interval_is_the_plain_surrogate():
+    adv, new, old = _ppo_inputs(2, 300, 0.02)          # |ratio - 1| < 0.2 everywhere
+    rho = np.exp(new.astype(np.float64) - old)
+    assert np.all(np.abs(rho - 1) < 0.2)
+    loss, grad = oracle.ppo_clip_loss(adv, new, old, None, 0.2)
+    assert loss == pytest.approx(-(rho * adv).mean(), rel=1e-13)
+    assert np.allclose(grad, -rho * adv / 300, rtol=1e-13, atol=0)
+
+
+def test_ppo_gradient_matches_finite_differences():
+    """Central differences of the loss in each logp_new, away from the kinks
+    at the clip edges, with normalization on."""
+    adv, new, old = _ppo_inputs(3, 24, 0.3)
+    rho = np.exp(new.astype(np.float64) - old)
+    stats = oracle.mean_std(adv)
+    _, grad = oracle.ppo_clip_loss(adv, new, old, stats, 0.2, 1e-8)
+    checked = 0
+    for i in range(24):
+        if min(abs(rho[i] - 0.8), abs(rho[i] - 1.2)) < 0.02:
+            continue
+        plus, minus = new.copy(), new.copy()
+        plus[i] = np.float32(new[i] + np.float32(1e-3))
+        minus[i] = np.float32(new[i] - np.float32(1e-3))
+        h = float(plus[i]) - float(minus[i])           # the step the float inputs really take
+        lp, _ = oracle.ppo_clip_loss(adv, plus, old, stats, 0.2, 1e-8)
+        lm, _ = oracle.ppo_clip_loss(adv, minus, old, stats, 0.2, 1e-8)
+        assert (lp - lm) / h == pytest.approx(grad[i], rel=1e-5, abs=1e-9), i
+        checked += 1
+    assert checked >= 18
