@@ -37,6 +37,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E peak, 8 TB/s
 METRIC = "effective HBM GB/s (% of peak) + env-steps/s, GAE 4096×128 fp32"
 COLD_BYTES = 1 << 30
+WORKSPACE_BYTES = 1 << 20   # per workspace buffer of the fused consumers
 
 
 # ------------------------------------------------------------------ workloads
@@ -76,6 +77,23 @@ def workload_calls(name, cfg, host, es=4):
                  ["@r", "@v", "@term", "@trunc", "@tv", "@b", g, lam, n, t, "@o0"],
                  _backward_bytes(nt, n, 3, 2, 1, es), ("o0",))
         calls = [gae_tr] if name == "gae_8x16" else [gae_nt, gae_tr, td_nt, td_tr]
+        return arrays, calls
+    if name == "ppo_4096x128":
+        # the fused consumers: GAE + advantage statistics, then the PPO loss
+        # and its gradient with on-the-fly normalization
+        arrays = dict(r=host.rewards, v=host.values, term=host.terminated,
+                      trunc=host.truncated, tv=host.trunc_values, b=host.bootstrap,
+                      mu=host.behaviour_logp, pi=host.target_logp)
+        calls = [
+            ("gae_stats", "rlca_gae_stats",
+             ["@r", "@v", "@term", "@trunc", "@tv", "@b", g, lam, n, t, "@o0", "@o1", "@stats",
+              "@ws", WORKSPACE_BYTES],
+             _backward_bytes(nt, n, 3, 2, 2) + 16, ("o0", "o1")),
+            ("ppo_clip_loss", "rlca_ppo_clip_loss",
+             ["@o0", "@stats", "@pi", "@mu", cfg["clip_eps"], 1e-8, n, t, "@grad", "@loss",
+              "@ws2", WORKSPACE_BYTES],
+             nt * 16 + 16 + 8, ("grad",)),
+        ]
         return arrays, calls
     if name == "vtrace_4096x256":
         arrays = dict(r=host.rewards, v=host.values, mu=host.behaviour_logp,
@@ -130,11 +148,20 @@ def make_sets(torch, arrays, calls, device, min_call_bytes, real=None):
         sum(4 * int(np.prod(shape)) for _ in range(3))
     nsets = int(min(nsets, max(2, (24 << 30) // per_set)))
     sets = []
+    named = {a[1:] for c in calls for a in c[2] if isinstance(a, str) and a.startswith("@")}
     for _ in range(nsets):
         s = {k: v.clone() for k, v in master.items()}
-        s["o0"] = torch.empty(shape, dtype=real, device=device)
-        s["o1"] = torch.empty(shape, dtype=real, device=device)
+        s["o0"] = torch.zeros(shape, dtype=real, device=device)
+        s["o1"] = torch.zeros(shape, dtype=real, device=device)
         s["oi"] = torch.empty(shape, dtype=torch.int32, device=device)
+        if "grad" in named:
+            s["grad"] = torch.empty(shape, dtype=torch.float32, device=device)
+        for k in ("stats", "loss"):
+            if k in named:
+                s[k] = torch.zeros(2, dtype=torch.float64, device=device)
+        for k in ("ws", "ws2"):
+            if k in named:
+                s[k] = torch.empty(WORKSPACE_BYTES, dtype=torch.uint8, device=device)
         sets.append(s)
     return sets
 
@@ -196,6 +223,10 @@ def run_gpu(args, name, cfg, host):
     device = torch.device("cuda:0")
     torch.cuda.set_device(device)
     storage = STORAGE[args.dtype]
+    if any(c[1] not in BATCH_FIELDS for c in workload_calls(name, cfg, host)[1]):
+        if args.dtype != "f32":
+            raise SystemExit(f"{name} runs in fp32 only")
+        args.launch = "eager"   # calls that rlca_run_batch does not take
     real = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[args.dtype]
     arrays, calls = workload_calls(name, cfg, host, real.itemsize)
     sets = make_sets(torch, arrays, calls, device, min(c[3] for c in calls), real)
@@ -351,6 +382,14 @@ def run_cpu_baseline(name, cfg, host, seconds):
         fns = [lambda: oracle.retrace(d.rewards, d.q_values, d.expected_q, d.behaviour_logp,
                                       d.target_logp, d.terminated, d.truncated, d.trunc_values,
                                       d.bootstrap, g, lam, cfg["c_bar"])]
+    elif name == "ppo_4096x128":
+        def ppo_step():
+            adv, _ = oracle.gae(d.rewards, d.values, d.terminated, d.truncated, d.trunc_values,
+                                d.bootstrap, g, lam)
+            stats = oracle.mean_std(adv)
+            oracle.ppo_clip_loss(adv.astype(np.float32), d.target_logp, d.behaviour_logp, stats,
+                                 cfg["clip_eps"], 1e-8)
+        fns = [ppo_step]
     else:
         fns = [
             lambda: oracle.discounted_returns(d.rewards, d.dones, None, None, d.bootstrap, g),
@@ -571,7 +610,9 @@ def main():
             "storage": args.dtype,
         },
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-        "env_steps_per_s": ncalls * res["nt"] / step_s,
+        # independent estimator calls each cover the rollout; the fused PPO
+        # calls form one pipeline over it
+        "env_steps_per_s": (1 if args.workload == "ppo_4096x128" else ncalls) * res["nt"] / step_s,
         "bytes_per_step": res["step_bytes"],
         "calls": calls_out,
         "copy_ceiling": {"gbs": round(res["copy_gbs"], 1), "bytes": res["copy_bytes"],

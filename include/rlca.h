@@ -70,6 +70,7 @@
 #ifndef RLCA_H
 #define RLCA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #include <hip/hip_runtime_api.h>
@@ -265,6 +266,51 @@ typedef struct {
 /* Enqueue `count` (0..RLCA_MAX_BATCH) calls on `stream`; `calls` is host
  * memory, read before the function returns. */
 rlca_status rlca_run_batch(const rlca_call *calls, int count, hipStream_t stream);
+
+/* ------------------------------------------------- fused consumers of GAE
+ * The summary's §9 (Discussion and Future Work) names fused loss operations
+ * as the next step for the library; these two calls fuse the usual PPO
+ * consumers of the advantages into the scan's epilogue and into one
+ * streaming pass.  Both reduce in a fixed order (reproducible bit for bit)
+ * through a caller-owned device workspace, whose size the *_workspace_size
+ * call returns (0 for an empty rollout or invalid sizes); its contents on
+ * entry do not matter and are overwritten.  workspace, stats and loss must
+ * be 8-byte aligned; RLCA_ERR_INVALID_SIZE if workspace_bytes is too small;
+ * RLCA_ERR_ALIASING if the workspace, stats or loss overlap any other array
+ * of the call.  An empty rollout (num_envs * T == 0) writes nothing. */
+size_t rlca_gae_stats_workspace_size(int64_t num_envs, int64_t T);
+
+/* rlca_gae (fp32) that also reduces the advantages it computes: stats is
+ * double[2] in device memory, {mean, sample standard deviation (divisor
+ * N*T - 1; 0 when N*T == 1)} over all N*T steps, accumulated in fp64.  The
+ * usual advantage normalization (A - mean) / (std + eps) needs exactly
+ * these, without a second pass over the advantages.  advantages and returns
+ * are bit for bit those of rlca_gae. */
+rlca_status rlca_gae_stats(const float *rewards, const float *values, const uint8_t *terminated,
+                           const uint8_t *truncated, const float *trunc_values,
+                           const float *bootstrap, float gamma, float lambda, int64_t num_envs,
+                           int64_t T, float *advantages, float *returns, double *stats,
+                           void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+size_t rlca_ppo_clip_loss_workspace_size(int64_t num_envs, int64_t T);
+
+/* PPO clipped surrogate (Schulman et al. 2017, L^CLIP) as a loss, over the
+ * M = num_envs * T steps of the [num_envs, T] arrays:
+ *   A_hat_t = stats ? (A_t - stats[0]) / (stats[1] + norm_eps) : A_t
+ *   rho_t   = exp(logp_new_t - logp_old_t)
+ *   loss[0] = -(1/M) sum_t min(rho_t A_hat_t, clip(rho_t, 1-clip_eps, 1+clip_eps) A_hat_t)
+ *   grad_logp_new[t] = d loss / d logp_new_t: -(1/M) rho_t A_hat_t where the
+ *                      unclipped term is the smaller (ties included), else 0.
+ * advantages, logp_new, logp_old [N,T] f32; stats double[2] as written by
+ * rlca_gae_stats, nullable (no normalization); grad_logp_new [N,T] f32,
+ * nullable; loss double[1] (device).  0 <= clip_eps < 1 and norm_eps >= 0,
+ * finite, else RLCA_ERR_INVALID_VALUE.  Arithmetic per step is fp32, the
+ * sums fp64. */
+rlca_status rlca_ppo_clip_loss(const float *advantages, const double *stats,
+                               const float *logp_new, const float *logp_old, float clip_eps,
+                               float norm_eps, int64_t num_envs, int64_t T, float *grad_logp_new,
+                               double *loss, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream);
 
 /* Static description of a status code (never NULL). */
 const char *rlca_status_string(rlca_status status);

@@ -2,8 +2,10 @@
 
 The seven estimators of the rl-triton summary (GAE, TD(lambda) returns,
 discounted returns, V-Trace, Retrace(lambda), eligibility traces, episodic
-prefix sums) and the generic affine scan over caller-built coefficients, each
-a HIP kernel launch behind the C ABI of include/rlca.h.
+prefix sums), the generic affine scan over caller-built coefficients, batches
+of those calls, and the fused PPO consumers of the advantages (gae_stats,
+ppo_clip_loss), each HIP kernel launches behind the C ABI of include/rlca.h.
+Real-valued arrays may be float32, bfloat16 or float16 (fp32 arithmetic).
 PyTorch supplies device memory and the stream; the computation is entirely in
 librlca.so, which must be built (``python -m linear_recurrence_scan_row_amd.build``).
 """
@@ -19,7 +21,9 @@ from .rlca import (  # noqa: F401
     eligibility_traces,
     episodic_prefix_sum,
     gae,
+    gae_stats,
     lib,
+    ppo_clip_loss,
     retrace,
     td_lambda,
     vtrace,

@@ -85,6 +85,7 @@ struct BackwardParams {
     const void *bootstrap;  // carry A_T for kAffineBackward
     void *out0;             // advantages / returns / vs / q_ret / A
     void *out1;             // GAE returns or V-Trace pg advantages; may be null
+    double *stats_partials;  // with STATS: (sum, sum of squares) of out0 per workgroup
     float gamma, lambda, rho_bar, c_bar;
     Geometry geo;
 };
@@ -305,6 +306,62 @@ __device__ __forceinline__ float importance_ratio(float target_logp, float behav
     return expf(l);
 }
 
+// fp64 DPP step: x plus the value of the lane CTRL selects (0 where there
+// is none), moved as two 32-bit halves.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_add_f64(double x) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL,
+                                                              ROW_MASK, 0xf, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL,
+                                                              ROW_MASK, 0xf, false);
+    return x + __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ double read_lane_f64(double x, int lane) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Sum over the 64 lanes of a wave, in a fixed order (the prefix pattern of
+// wave_inclusive_scan; lane 63 ends with the total), returned to every lane.
+__device__ __forceinline__ double wave_sum_f64(double x) {
+    x = dpp_add_f64<0x111, 0xf>(x);  // row_shr:1
+    x = dpp_add_f64<0x112, 0xf>(x);  // row_shr:2
+    x = dpp_add_f64<0x114, 0xf>(x);  // row_shr:4
+    x = dpp_add_f64<0x118, 0xf>(x);  // row_shr:8
+    x = dpp_add_f64<0x142, 0xa>(x);  // row_bcast:15
+    x = dpp_add_f64<0x143, 0xc>(x);  // row_bcast:31
+    return read_lane_f64(x, kWave - 1);
+}
+
+// Sum of (a, b) over the workgroup, left in every lane: each wave's sum
+// (wave_sum_f64), then the NW wave sums in order through LDS.  Every wave of
+// the workgroup must call it.
+template <int NW>
+__device__ __forceinline__ void workgroup_sum2(double &a, double &b) {
+    a = wave_sum_f64(a);
+    b = wave_sum_f64(b);
+    if constexpr (NW > 1) {
+        __shared__ double lds[2 * NW];
+        const int w = threadIdx.x / kWave;
+        if ((threadIdx.x & (kWave - 1)) == 0) {
+            lds[2 * w] = a;
+            lds[2 * w + 1] = b;
+        }
+        __syncthreads();
+        a = 0.0;
+        b = 0.0;
+#pragma unroll
+        for (int j = 0; j < NW; ++j) {
+            a += lds[2 * j];
+            b += lds[2 * j + 1];
+        }
+    }
+}
+
 // ------------------------------------------------------- leading kernel arguments
 // The geometry and the first five input arrays are passed as separate scalar
 // kernel arguments ahead of the parameter block: gfx950 preloads leading
@@ -389,8 +446,12 @@ __device__ __forceinline__ void adopt_lead(ForwardParams &p, LEAD_ARGS) {
 // A_t = alpha_t + beta_t * A_{t+1}.  Lanes take chunks in reverse time order, so
 // the lane-order scan of scan_core.hpp runs from the end of the tile backwards.
 // Groups g, g + g_stride, ... of the launch run through one workgroup.
-template <int EST, bool TRUNC, bool VEC, int NW, bool WAVE_LOCAL, int MODE, typename S>
+// STATS: also sum out0 and its square over the workgroup's valid steps (in
+// fp64) and store the pair in stats_partials[2 * blockIdx.x ...].
+template <int EST, bool TRUNC, bool VEC, int NW, bool WAVE_LOCAL, int MODE, typename S,
+          bool STATS = false>
 __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uint32_t g_stride) {
+    static_assert(!STATS || MODE != kChunkAggregate, "statistics come from the outputs");
     static_assert(MODE == kFull || (NW == kChunkWaves && !WAVE_LOCAL), "a chunk is one tile");
     typedef const S *__restrict__ In;
     const In rewards = static_cast<In>(p.rewards), values = static_cast<In>(p.values);
@@ -401,6 +462,7 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
     const In bootstrap = static_cast<In>(p.bootstrap);
     S *__restrict__ out0 = static_cast<S *>(p.out0);
     S *__restrict__ out1 = static_cast<S *>(p.out1);
+    double sum = 0.0, sum_sq = 0.0;  // STATS
     constexpr uint32_t kTile = NW * kWave * kK;
     constexpr bool kFlags = EST != kAffineBackward;
     __shared__ float lds_a[2 * NW], lds_b[2 * NW];
@@ -604,16 +666,32 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
                 if constexpr (EST == kGae || EST == kVtrace) {
                     if (out1 != nullptr) store_steps<VEC>(out1 + base, o1, off, L);
                 }
+                if constexpr (STATS) {
+#pragma unroll
+                    for (int i = 0; i < kK; ++i) {
+                        const double x = valid[i] ? (double)o0[i] : 0.0;
+                        sum += x;
+                        sum_sq += x * x;
+                    }
+                }
             }
         }
         g += g_stride;
     } while (g < p.geo.num_groups);
+    if constexpr (STATS) {
+        workgroup_sum2<NW>(sum, sum_sq);
+        if (threadIdx.x == 0) {
+            p.stats_partials[2 * (size_t)blockIdx.x] = sum;
+            p.stats_partials[2 * (size_t)blockIdx.x + 1] = sum_sq;
+        }
+    }
 }
 
-template <int EST, bool TRUNC, bool VEC, int NW, bool WAVE_LOCAL, int MODE, typename S>
+template <int EST, bool TRUNC, bool VEC, int NW, bool WAVE_LOCAL, int MODE, typename S,
+          bool STATS = false>
 __global__ __launch_bounds__(NW * kWave) void backward_scan(LEAD_ARGS, BackwardParams p) {
     adopt_lead<EST>(p, LEAD_NAMES);
-    backward_body<EST, TRUNC, VEC, NW, WAVE_LOCAL, MODE, S>(p, blockIdx.x, gridDim.x);
+    backward_body<EST, TRUNC, VEC, NW, WAVE_LOCAL, MODE, S, STATS>(p, blockIdx.x, gridDim.x);
 }
 
 // -------------------------------------------------------------- forward kernel
@@ -781,13 +859,17 @@ __global__ __launch_bounds__(NW * kWave) void chunk_carries(void *slots, int64_t
 
 // Upper bound on the launch grid; larger problems loop over groups.
 constexpr uint32_t kMaxGrid = 1u << 20;
+// Launches that leave one partial sum per workgroup use fewer, longer-lived
+// workgroups (2048 are resident on the chip at once), which keeps the final
+// reduction to one round of loads.
+constexpr uint32_t kStatsMaxGrid = 4096;
 
-inline uint32_t grid_for(int64_t groups) {
-    return groups < (int64_t)kMaxGrid ? (uint32_t)groups : kMaxGrid;
+inline uint32_t grid_for(int64_t groups, uint32_t cap = kMaxGrid) {
+    return groups < (int64_t)cap ? (uint32_t)groups : cap;
 }
 
 inline Geometry make_geometry(int64_t num_envs, int64_t T, int waves, bool chunked,
-                              uint32_t *grid) {
+                              uint32_t *grid, uint32_t cap = kMaxGrid) {
     const uint32_t tile = (uint32_t)waves * kWave * kK;
     Geometry g;
     g.num_envs = num_envs;
@@ -803,7 +885,7 @@ inline Geometry make_geometry(int64_t num_envs, int64_t T, int waves, bool chunk
         groups = (num_envs + g.rows_per_group - 1) / g.rows_per_group;
     }
     g.num_groups = (uint32_t)groups;
-    *grid = grid_for(groups);
+    *grid = grid_for(groups, cap);
     return g;
 }
 
@@ -834,34 +916,52 @@ inline rlca_status launch_chunk_carries(void *slots, const Geometry &geo, bool b
     return e == hipSuccess ? RLCA_OK : RLCA_ERR_HIP;
 }
 
-// The three chunk-mode launches, all on one stream: aggregate, carries, apply.
+// The three chunk-mode launches, all on one stream: aggregate, carries,
+// apply (the apply grid capped at `apply_cap`).
 template <typename V, typename S, typename P>
 inline rlca_status launch_chunked(const void *aggregate, const void *apply, P &params, Lead &lead,
-                                  void *slots, bool backward, hipStream_t stream) {
+                                  void *slots, bool backward, hipStream_t stream,
+                                  uint32_t apply_cap = kMaxGrid) {
     uint32_t grid;
     params.geo = make_geometry(params.geo.num_envs, params.geo.T, kChunkWaves, true, &grid);
+    const uint32_t apply_grid = grid_for(params.geo.num_groups, apply_cap);
     rlca_status st = launch_kernel(aggregate, kChunkWaves, grid, params, lead, stream);
     if (st == RLCA_OK) st = launch_chunk_carries<V, S>(slots, params.geo, backward, stream);
-    if (st == RLCA_OK) st = launch_kernel(apply, kChunkWaves, grid, params, lead, stream);
+    if (st == RLCA_OK) st = launch_kernel(apply, kChunkWaves, apply_grid, params, lead, stream);
     return st;
 }
 
 template <typename P>
 inline rlca_status launch_full(const void *kernel, int waves, P &params, Lead &lead,
-                               hipStream_t stream) {
+                               hipStream_t stream, uint32_t cap = kMaxGrid) {
     uint32_t grid;
-    params.geo = make_geometry(params.geo.num_envs, params.geo.T, waves, false, &grid);
+    params.geo = make_geometry(params.geo.num_envs, params.geo.T, waves, false, &grid, cap);
     return launch_kernel(kernel, waves, grid, params, lead, stream);
+}
+
+// Workgroups of the launch (the last one, for the chunk modes) of a call of
+// this shape, the grid capped at `cap`: the scalar path runs 4-wave
+// workgroups.
+inline uint32_t launch_grid(const LaunchShape &s, int64_t num_envs, int64_t T,
+                            uint32_t cap = kMaxGrid) {
+    uint32_t grid;
+    if (s.chunked)
+        make_geometry(num_envs, T, kChunkWaves, true, &grid, cap);
+    else
+        make_geometry(num_envs, T, s.vec ? s.waves : 4, false, &grid, cap);
+    return grid;
 }
 
 // The vector path instantiates every wave count and the wave-local variant;
 // the scalar (unaligned or T % K != 0) path is one general configuration.
-template <int EST, bool TRUNC, typename S>
+template <int EST, bool TRUNC, typename S, bool STATS = false>
 const void *backward_kernel(const LaunchShape &s) {
-    if (!s.vec) return (const void *)backward_scan<EST, TRUNC, false, 4, false, kFull, S>;
-#define RLCA_PICK(NW)                                                                        \
-    return s.wave_local ? (const void *)backward_scan<EST, TRUNC, true, NW, true, kFull, S> \
-                        : (const void *)backward_scan<EST, TRUNC, true, NW, false, kFull, S>
+    if (!s.vec)
+        return (const void *)backward_scan<EST, TRUNC, false, 4, false, kFull, S, STATS>;
+#define RLCA_PICK(NW)                                                                          \
+    return s.wave_local                                                                        \
+               ? (const void *)backward_scan<EST, TRUNC, true, NW, true, kFull, S, STATS>     \
+               : (const void *)backward_scan<EST, TRUNC, true, NW, false, kFull, S, STATS>
     switch (s.waves) {
         case 1: RLCA_PICK(1);
         case 2: RLCA_PICK(2);
@@ -871,16 +971,19 @@ const void *backward_kernel(const LaunchShape &s) {
 #undef RLCA_PICK
 }
 
-template <int EST, bool TRUNC, typename S>
+template <int EST, bool TRUNC, typename S, bool STATS = false>
 rlca_status launch_backward_variant(BackwardParams &p, const LaunchShape &s, hipStream_t stream) {
     Lead lead;
     lead_from<EST>(p, lead);
+    const uint32_t cap = STATS ? kStatsMaxGrid : kMaxGrid;
     if (s.chunked)
         return launch_chunked<float, S>(
             (const void *)backward_scan<EST, TRUNC, true, kChunkWaves, false, kChunkAggregate, S>,
-            (const void *)backward_scan<EST, TRUNC, true, kChunkWaves, false, kChunkApply, S>, p,
-            lead, p.out0, true, stream);
-    return launch_full(backward_kernel<EST, TRUNC, S>(s), s.vec ? s.waves : 4, p, lead, stream);
+            (const void *)backward_scan<EST, TRUNC, true, kChunkWaves, false, kChunkApply, S,
+                                        STATS>,
+            p, lead, p.out0, true, stream, cap);
+    return launch_full(backward_kernel<EST, TRUNC, S, STATS>(s), s.vec ? s.waves : 4, p, lead,
+                       stream, cap);
 }
 
 template <int EST, typename S>
@@ -994,6 +1097,17 @@ rlca_status launch_grouped(const GroupedLaunch &launch, int storage, hipStream_t
 
 // One translation unit per estimator instantiates these (see est_*.hip).
 rlca_status launch_gae(BackwardParams &p, const LaunchShape &s, int storage, hipStream_t stream);
+// GAE (fp32) that also leaves per-workgroup (sum, sum of squares) of the
+// advantages in p.stats_partials: launch_grid(s, ..., kStatsMaxGrid) pairs.
+rlca_status launch_gae_stats(BackwardParams &p, const LaunchShape &s, hipStream_t stream);
+// Fused consumers (est_ppo.hip).
+rlca_status launch_finish_stats(const double *partials, uint32_t count, int64_t M,
+                                double *stats, hipStream_t stream);
+uint32_t ppo_grid(int64_t M);
+rlca_status launch_ppo_clip_loss(const float *adv, const double *stats, const float *logp_new,
+                                 const float *logp_old, float clip_eps, float norm_eps,
+                                 int64_t M, bool vec, float *grad, double *partials,
+                                 double *loss, hipStream_t stream);
 rlca_status launch_td_lambda(BackwardParams &p, const LaunchShape &s, int storage,
                              hipStream_t stream);
 rlca_status launch_discounted(BackwardParams &p, const LaunchShape &s, int storage,

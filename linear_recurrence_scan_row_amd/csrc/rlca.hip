@@ -468,6 +468,34 @@ static rlca_status run_one(rlca_status prepared, Call &c, hipStream_t stream) {
 
 using namespace rlca;
 
+// ------------------------------------------------------------ fused consumers
+
+// One (sum, sum of squares) pair per workgroup of the GAE launch, for
+// whichever launch shape the pointers will select.
+static uint32_t gae_stats_pairs(int64_t num_envs, int64_t T) {
+    const uint32_t v = launch_grid(choose_shape(num_envs, T, true), num_envs, T, kStatsMaxGrid);
+    const uint32_t s = launch_grid(choose_shape(num_envs, T, false), num_envs, T, kStatsMaxGrid);
+    return v > s ? v : s;
+}
+
+static bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// No span of `extra` may overlap another one or any of the call's arrays.
+static rlca_status check_extra_aliasing(const Call &c, const Span *extra, int n) {
+    for (int i = 0; i < n; ++i) {
+        for (int j = 0; j < c.nin; ++j)
+            if (overlaps(extra[i].p, extra[i].bytes, c.ins[j].p, c.ins[j].bytes))
+                return RLCA_ERR_ALIASING;
+        for (int j = 0; j < c.nout; ++j)
+            if (overlaps(extra[i].p, extra[i].bytes, c.outs[j].p, c.outs[j].bytes))
+                return RLCA_ERR_ALIASING;
+        for (int j = i + 1; j < n; ++j)
+            if (overlaps(extra[i].p, extra[i].bytes, extra[j].p, extra[j].bytes))
+                return RLCA_ERR_ALIASING;
+    }
+    return RLCA_OK;
+}
+
 extern "C" {
 
 rlca_status rlca_gae(const float *rewards, const float *values, const uint8_t *terminated,
@@ -551,6 +579,78 @@ rlca_status rlca_affine_scan(const float *alpha, const float *beta, const float 
     Call c;
     return run_one(prepare_affine(kStoreF32, alpha, beta, carry, direction, num_envs, T, out, &c), c,
                    stream);
+}
+
+size_t rlca_gae_stats_workspace_size(int64_t num_envs, int64_t T) {
+    int64_t n;
+    if (check_sizes(num_envs, T, &n) != RLCA_OK || n == 0) return 0;
+    return 16 * (size_t)gae_stats_pairs(num_envs, T);
+}
+
+rlca_status rlca_gae_stats(const float *rewards, const float *values, const uint8_t *terminated,
+                           const uint8_t *truncated, const float *trunc_values,
+                           const float *bootstrap, float gamma, float lambda, int64_t num_envs,
+                           int64_t T, float *advantages, float *returns, double *stats,
+                           void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    Call c;
+    rlca_status st = prepare_gae(kStoreF32, rewards, values, terminated, truncated,
+                                 trunc_values, bootstrap, gamma, lambda, num_envs, T, advantages,
+                                 returns, &c);
+    if (st != RLCA_OK || c.empty) return st;
+    if (stats == nullptr || workspace == nullptr) return RLCA_ERR_NULL_POINTER;
+    if (!aligned(stats, 8) || !aligned(workspace, 8)) return RLCA_ERR_MISALIGNED;
+    const uint32_t pairs = launch_grid(c.shape, num_envs, T, kStatsMaxGrid);
+    if (workspace_bytes < 16 * (size_t)pairs) return RLCA_ERR_INVALID_SIZE;
+    const Span extra[] = {{stats, 16}, {workspace, 16 * (size_t)pairs}};
+    st = check_extra_aliasing(c, extra, 2);
+    if (st != RLCA_OK) return st;
+    c.bp.stats_partials = static_cast<double *>(workspace);
+    st = launch_gae_stats(c.bp, c.shape, stream);
+    if (st != RLCA_OK) return st;
+    return launch_finish_stats(c.bp.stats_partials, pairs, num_envs * T, stats, stream);
+}
+
+size_t rlca_ppo_clip_loss_workspace_size(int64_t num_envs, int64_t T) {
+    int64_t n;
+    if (check_sizes(num_envs, T, &n) != RLCA_OK || n == 0) return 0;
+    return 8 * (size_t)ppo_grid(n);
+}
+
+rlca_status rlca_ppo_clip_loss(const float *advantages, const double *stats,
+                               const float *logp_new, const float *logp_old, float clip_eps,
+                               float norm_eps, int64_t num_envs, int64_t T, float *grad_logp_new,
+                               double *loss, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+    int64_t n;
+    rlca_status st = check_sizes(num_envs, T, &n);
+    if (st != RLCA_OK) return st;
+    if (!(clip_eps >= 0.f && clip_eps < 1.f) || !(norm_eps >= 0.f && isfinite(norm_eps)))
+        return RLCA_ERR_INVALID_VALUE;
+    if (n == 0) return RLCA_OK;
+    if (advantages == nullptr || logp_new == nullptr || logp_old == nullptr || loss == nullptr ||
+        workspace == nullptr)
+        return RLCA_ERR_NULL_POINTER;
+    const void *f32[] = {advantages, logp_new, logp_old, grad_logp_new};
+    st = check_aligned(f32, 4, 4);
+    if (st != RLCA_OK) return st;
+    if (!aligned(stats, 8) || !aligned(loss, 8) || !aligned(workspace, 8))
+        return RLCA_ERR_MISALIGNED;
+    const uint32_t grid = ppo_grid(n);
+    if (workspace_bytes < 8 * (size_t)grid) return RLCA_ERR_INVALID_SIZE;
+    Call c = Call{};  // byte ranges only, for the aliasing check
+    const size_t fb = (size_t)n * 4;
+    c.ins[c.nin++] = {advantages, fb};
+    c.ins[c.nin++] = {logp_new, fb};
+    c.ins[c.nin++] = {logp_old, fb};
+    c.ins[c.nin++] = {stats, 16};
+    const Span outs[] = {{grad_logp_new, fb}, {loss, 8}, {workspace, 8 * (size_t)grid}};
+    st = check_extra_aliasing(c, outs, 3);
+    if (st != RLCA_OK) return st;
+    const bool vec = n % 4 == 0 && aligned(advantages, 16) && aligned(logp_new, 16) &&
+                     aligned(logp_old, 16) && aligned(grad_logp_new, 16);
+    return launch_ppo_clip_loss(advantages, stats, logp_new, logp_old, clip_eps, norm_eps, n,
+                                vec, grad_logp_new, static_cast<double *>(workspace), loss,
+                                stream);
 }
 
 rlca_status rlca_run_batch(const rlca_call *calls, int count, hipStream_t stream) {

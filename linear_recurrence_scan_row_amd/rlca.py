@@ -38,6 +38,7 @@ _p = ctypes.c_void_p
 _f = ctypes.c_float
 _i64 = ctypes.c_int64
 _i = ctypes.c_int
+_sz = ctypes.c_size_t
 
 
 class RlcaCall(ctypes.Structure):
@@ -68,6 +69,13 @@ SIGNATURES = {
     "rlca_episodic_prefix_sum": [_p, _i, _p, _i, _i64, _i64, _p, _p],
     "rlca_affine_scan": [_p, _p, _p, _i, _i64, _i64, _p, _p],
     "rlca_run_batch": [ctypes.POINTER(RlcaCall), _i, _p],
+    "rlca_gae_stats": [_p, _p, _p, _p, _p, _p, _f, _f, _i64, _i64, _p, _p, _p, _p, _sz, _p],
+    "rlca_ppo_clip_loss": [_p, _p, _p, _p, _f, _f, _i64, _i64, _p, _p, _p, _sz, _p],
+}
+# workspace-size queries (return size_t)
+SIZE_QUERIES = {
+    "rlca_gae_stats_workspace_size": [_i64, _i64],
+    "rlca_ppo_clip_loss_workspace_size": [_i64, _i64],
 }
 
 _lib = None
@@ -93,6 +101,10 @@ def lib():
             fn = getattr(l, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int
+        for name, args in SIZE_QUERIES.items():
+            fn = getattr(l, name)
+            fn.argtypes = args
+            fn.restype = _sz
         l.rlca_status_string.argtypes = [ctypes.c_int]
         l.rlca_status_string.restype = ctypes.c_char_p
         _lib = l
@@ -296,6 +308,51 @@ def _prepare_affine_scan(alpha, beta, carry=None, direction=BACKWARD, out=None):
     o = _out(out, shape, dev, fdt)
     return _Prepared(OP_AFFINE, shape, dev, o, rewards=a, values=b, bootstrap=c,
                      direction=int(direction), out0=o, dtype=REAL_DTYPES[fdt])
+
+
+def _workspace(query, shape, dev):
+    nbytes = getattr(lib(), query)(*shape)
+    return torch.empty(max(nbytes, 8), dtype=torch.uint8, device=dev), nbytes
+
+
+def gae_stats(rewards, values, terminated, truncated=None, trunc_values=None, bootstrap=None,
+              gamma=0.99, lam=0.95, with_returns=True, advantages=None, returns=None,
+              stats=None):
+    """GAE (float32) plus the mean and sample std of the advantages over all
+    steps, reduced in the same pass.  Returns (advantages, returns|None,
+    stats), stats a float64 tensor [mean, std] on the device."""
+    p = _prepare_gae(rewards, values, terminated, truncated, trunc_values, bootstrap, gamma,
+                     lam, with_returns, advantages, returns)
+    if not p.f32:
+        raise TypeError("gae_stats takes float32 arrays")
+    st = _out(stats, (2,), p.dev, torch.float64, name="stats")
+    ws, nbytes = _workspace("rlca_gae_stats_workspace_size", p.shape, p.dev)
+    _check(lib().rlca_gae_stats(p.arg("rewards"), p.arg("values"), p.arg("terminated"),
+                                p.arg("truncated"), p.arg("trunc_values"), p.arg("bootstrap"),
+                                p.arg("gamma"), p.arg("lambda_"), *p.shape, p.arg("out0"),
+                                p.arg("out1"), _ptr(st), _ptr(ws), nbytes, p.stream()),
+           "rlca_gae_stats")
+    return p.result + (st,)
+
+
+def ppo_clip_loss(advantages, logp_new, logp_old, stats=None, clip_eps=0.2, norm_eps=1e-8,
+                  with_grad=True, grad=None):
+    """PPO clipped-surrogate loss (float64 scalar tensor on the device) and its
+    gradient in logp_new (float32, or None).  stats = [mean, std] (float64,
+    e.g. from gae_stats) normalizes the advantages on the fly."""
+    shape, dev = _rollout_shape(advantages)
+    a = _steps("advantages", advantages, shape, torch.float32, dev)
+    new = _steps("logp_new", logp_new, shape, torch.float32, dev)
+    old = _steps("logp_old", logp_old, shape, torch.float32, dev)
+    st = _steps("stats", stats, (2,), torch.float64, dev, optional=True)
+    g = _out(grad, shape, dev, name="grad") if with_grad else None
+    loss = torch.empty(1, dtype=torch.float64, device=dev)
+    ws, nbytes = _workspace("rlca_ppo_clip_loss_workspace_size", shape, dev)
+    _check(lib().rlca_ppo_clip_loss(_ptr(a), _ptr(st), _ptr(new), _ptr(old), clip_eps, norm_eps,
+                                    *shape, _ptr(g), _ptr(loss), _ptr(ws), nbytes,
+                                    torch.cuda.current_stream(dev).cuda_stream),
+           "rlca_ppo_clip_loss")
+    return loss, g
 
 
 def _run_alone(p: _Prepared):

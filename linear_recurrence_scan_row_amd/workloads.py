@@ -141,12 +141,17 @@ CONFIGS = {
                               p_trunc=0.001, gamma=0.99, lam=0.95, c_bar=1.0),
     "forward_16384x512": dict(kind="forward", seed=5, num_envs=16384, T=512, p_start=0.01,
                               gamma=0.99, lam=0.9),
+    # the fused PPO consumers on the 4096 x 128 rollout above (same seed and
+    # recipe); behaviour / target log-probs serve as old / new policy
+    "ppo_4096x128": dict(kind="backward", seed=2, num_envs=4096, T=128, p_term=0.01,
+                         p_trunc=0.005, gamma=0.99, lam=0.95, clip_eps=0.2),
 }
 
 
 def make(name: str, num_envs: int | None = None, T: int | None = None):
     """Draw the named workload; ``num_envs`` / ``T`` override the shape (same recipe)."""
     cfg = dict(CONFIGS[name])
+    cfg.pop("clip_eps", None)
     kind = cfg.pop("kind")
     seed = cfg.pop("seed")
     n = cfg.pop("num_envs") if num_envs is None else (cfg.pop("num_envs"), num_envs)[1]

@@ -30,7 +30,7 @@ H = 0x80000000
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:rlca_status|const char \*)\s*(rlca_\w+)\s*\(",
+    return sorted(set(re.findall(r"^\s*(?:rlca_status|const char \*|size_t)\s*(rlca_\w+)\s*\(",
                                  text, re.M)))
 
 
@@ -52,7 +52,7 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), name
     # and the binding's signature table covers every compute entry point
     compute = [n for n in declared_functions() if n != "rlca_status_string"]
-    assert sorted(binding.SIGNATURES) == sorted(compute)
+    assert sorted(list(binding.SIGNATURES) + list(binding.SIZE_QUERIES)) == sorted(compute)
 
 
 def test_status_strings(lib):
@@ -216,3 +216,61 @@ def test_batch_dtype_validation(lib):
     assert run_batch(lib, call(dtype=f16, **prefix)) == MISAL
     assert lib.rlca_episodic_prefix_sum(A + 1, bf16, B, 0, 4, 8, C, None) == MISAL
     assert lib.rlca_episodic_prefix_sum(A, 7, B, 0, 4, 8, C, None) == VALUE
+
+
+def test_workspace_size_queries(lib):
+    assert lib.rlca_gae_stats_workspace_size(0, 128) == 0
+    assert lib.rlca_gae_stats_workspace_size(-1, 128) == 0
+    assert lib.rlca_ppo_clip_loss_workspace_size(4, 0) == 0
+    # one (sum, sum of squares) pair of doubles per workgroup: 4096 x 128 packs
+    # 16 rows per 8-wave workgroup; the unaligned path packs 8 per 4-wave one
+    assert lib.rlca_gae_stats_workspace_size(4096, 128) == 16 * 512
+    assert lib.rlca_gae_stats_workspace_size(3, 100000) == 16 * 3 * 49   # chunked: 2048-step chunks
+    assert lib.rlca_ppo_clip_loss_workspace_size(4096, 128) == 8 * 512
+    assert lib.rlca_ppo_clip_loss_workspace_size(1 << 20, 512) == 8 * 2048
+
+
+def gae_stats(lib, stats=F, ws=G, nbytes=1 << 20, **kw):
+    a = dict(r=A, v=B, term=C, adv=D, ret=E, n=4, t=8, gamma=0.99, lam=0.95)
+    a.update(kw)
+    return lib.rlca_gae_stats(a["r"], a["v"], a["term"], None, None, None, a["gamma"],
+                              a["lam"], a["n"], a["t"], a["adv"], a["ret"], stats, ws, nbytes,
+                              None)
+
+
+def ppo(lib, adv=A, stats=None, new=B, old=C, clip=0.2, eps=1e-8, n=4, t=8, grad=D, loss=E,
+        ws=F, nbytes=1 << 20):
+    return lib.rlca_ppo_clip_loss(adv, stats, new, old, clip, eps, n, t, grad, loss, ws, nbytes,
+                                  None)
+
+
+def test_gae_stats_validation(lib):
+    assert gae_stats(lib, n=0) == OK
+    assert gae_stats(lib, stats=None) == NULLP
+    assert gae_stats(lib, ws=None) == NULLP
+    assert gae_stats(lib, stats=F + 4) == MISAL
+    assert gae_stats(lib, ws=G + 4) == MISAL
+    assert gae_stats(lib, nbytes=15) == SIZE                 # one pair needs 16 bytes
+    assert gae_stats(lib, gamma=2.0) == VALUE
+    assert gae_stats(lib, stats=D + 8) == ALIAS              # stats inside the advantages
+    assert gae_stats(lib, ws=B) == ALIAS                     # workspace over the values
+    assert gae_stats(lib, ws=F + 8) == ALIAS                 # workspace over the stats
+
+
+def test_ppo_clip_loss_validation(lib):
+    assert ppo(lib, n=0) == OK
+    for clip in (-0.1, 1.0, float("nan")):
+        assert ppo(lib, clip=clip) == VALUE
+    assert ppo(lib, eps=-1.0) == VALUE
+    assert ppo(lib, eps=float("inf")) == VALUE
+    assert ppo(lib, adv=None) == NULLP
+    assert ppo(lib, loss=None) == NULLP
+    assert ppo(lib, ws=None) == NULLP
+    assert ppo(lib, new=B + 2) == MISAL
+    assert ppo(lib, loss=E + 4) == MISAL
+    assert ppo(lib, stats=G + 4) == MISAL
+    assert ppo(lib, nbytes=7) == SIZE
+    assert ppo(lib, grad=B) == ALIAS                         # gradient over logp_new
+    assert ppo(lib, loss=A + 8) == ALIAS                     # loss inside the advantages
+    assert ppo(lib, ws=E) == ALIAS                           # workspace over the loss
+    assert ppo(lib, stats=G, ws=G + 8) == ALIAS              # workspace over the stats
