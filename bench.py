@@ -18,10 +18,15 @@ Measurement:
     per-kernel time: HIP events around back-to-back launches of one call
     variant (rotating sets), averaged; with --launch batch the roofline is
     that of the grouped launch over the whole step's bytes;
+  * full_call_us: the pages' protocol per call (20 untimed calls, 5 trials
+    of 50 calls each between its own events and followed by a synchronize;
+    minimum of the trial medians), host launch included;
   * effective GB/s uses the algorithmic byte model: every input array read
-    once and every output written once at dense size (fp32 / int32 4 B, flags
-    1 B per step, bootstrap 4 B per row);
-  * cpu_baseline: the fp64 sequential oracle on this host, single thread.
+    once and every output written once at dense size (fp32 / int32 4 B, bf16
+    / fp16 2 B, flags 1 B per step, bootstrap one value per row);
+  * cpu_baseline: the fp64 sequential oracle on this host, single thread;
+    cpu_baseline_all_cores: the same with the rows split over up to 16
+    worker processes.
 """
 from __future__ import annotations
 
@@ -324,6 +329,36 @@ def run_gpu(args, name, cfg, host):
                        for c in range(ncalls)]
         batch_ms = back_to_back([p[0] for p in plan]) if args.launch == "batch" else None
 
+        # the pages' protocol: 20 untimed calls, then 5 trials of 50 calls,
+        # each call between its own pair of events and followed by a
+        # synchronize (full-call time: host launch included); the median of
+        # each trial, the minimum over trials
+        def pages_protocol(bound):
+            for i in range(20):
+                fn, a = bound[i % len(bound)]
+                check(fn(*a), fn.__name__)
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            medians = []
+            for trial in range(5):
+                times = []
+                for i in range(50):
+                    fn, a = bound[(trial * 50 + i) % len(bound)]
+                    e0.record(stream)
+                    check(fn(*a), fn.__name__)
+                    e1.record(stream)
+                    e1.synchronize()
+                    times.append(e0.elapsed_time(e1))
+                medians.append(float(np.median(times)))
+            return min(medians)
+
+        protocol_ms = {calls[c][0]: pages_protocol([bind_call(calls[c], sets[i], h)
+                                                    for i in range(nsets)])
+                       for c in range(ncalls)}
+        if args.launch == "batch":
+            protocol_ms["batch"] = pages_protocol([p[0] for p in plan])
+
         # same-bytes copy ceiling (cold, rotating): a plain device copy of
         # step_bytes / 2 read + step_bytes / 2 written
         nfl = max(1, step_bytes // 8)
@@ -346,7 +381,8 @@ def run_gpu(args, name, cfg, host):
 
     nt = host.num_envs * host.T
     return dict(step_ms=step_ms, wall_s=wall, step_bytes=step_bytes, calls=calls,
-                per_call_ms=per_call_ms, batch_ms=batch_ms, dominant=dominant, nt=nt,
+                per_call_ms=per_call_ms, batch_ms=batch_ms, protocol_ms=protocol_ms,
+                dominant=dominant, nt=nt,
                 nsets=nsets,
                 copy_gbs=copy_gbs, copy_bytes=nfl * 8)
 
@@ -354,14 +390,12 @@ def run_gpu(args, name, cfg, host):
 # ------------------------------------------------------------------ CPU oracle
 
 
-def run_cpu_baseline(name, cfg, host, seconds):
-    """The fp64 sequential oracle on this host's CPU, single-threaded, over the
-    same rollout and calls, repeated for about `seconds`."""
+def oracle_calls(name, cfg, d):
+    """The workload's per-step calls on the fp64 oracle, over rollout d."""
     import oracle
 
     g = cfg["gamma"]
     lam = cfg.get("lam", 0.95)
-    d = host
     if name in ("gae_td_4096x128", "gae_8x16"):
         fns = [
             lambda: oracle.gae(d.rewards, d.values, d.terminated, None, None, d.bootstrap, g, lam),
@@ -372,31 +406,54 @@ def run_cpu_baseline(name, cfg, host, seconds):
             lambda: oracle.td_lambda(d.rewards, d.values, d.terminated, d.truncated,
                                      d.trunc_values, d.bootstrap, g, lam),
         ]
-        if name == "gae_8x16":
-            fns = fns[1:2]
-    elif name == "vtrace_4096x256":
-        fns = [lambda: oracle.vtrace(d.rewards, d.values, d.behaviour_logp, d.target_logp,
-                                     d.terminated, None, None, d.bootstrap, g, lam,
-                                     cfg["rho_bar"], cfg["c_bar"])]
-    elif name == "retrace_2048x1024":
-        fns = [lambda: oracle.retrace(d.rewards, d.q_values, d.expected_q, d.behaviour_logp,
-                                      d.target_logp, d.terminated, d.truncated, d.trunc_values,
-                                      d.bootstrap, g, lam, cfg["c_bar"])]
-    elif name == "ppo_4096x128":
+        return fns[1:2] if name == "gae_8x16" else fns
+    if name == "vtrace_4096x256":
+        return [lambda: oracle.vtrace(d.rewards, d.values, d.behaviour_logp, d.target_logp,
+                                      d.terminated, None, None, d.bootstrap, g, lam,
+                                      cfg["rho_bar"], cfg["c_bar"])]
+    if name == "retrace_2048x1024":
+        return [lambda: oracle.retrace(d.rewards, d.q_values, d.expected_q, d.behaviour_logp,
+                                       d.target_logp, d.terminated, d.truncated, d.trunc_values,
+                                       d.bootstrap, g, lam, cfg["c_bar"])]
+    if name == "ppo_4096x128":
         def ppo_step():
             adv, _ = oracle.gae(d.rewards, d.values, d.terminated, d.truncated, d.trunc_values,
                                 d.bootstrap, g, lam)
             stats = oracle.mean_std(adv)
             oracle.ppo_clip_loss(adv.astype(np.float32), d.target_logp, d.behaviour_logp, stats,
                                  cfg["clip_eps"], 1e-8)
-        fns = [ppo_step]
-    else:
-        fns = [
-            lambda: oracle.discounted_returns(d.rewards, d.dones, None, None, d.bootstrap, g),
-            lambda: oracle.eligibility_traces(d.increments, d.starts, 0, g, lam),
-            lambda: oracle.episodic_prefix_sum(d.rewards, d.starts, 0),
-            lambda: oracle.episodic_prefix_sum(d.ints, d.starts, 0),
-        ]
+        return [ppo_step]
+    return [
+        lambda: oracle.discounted_returns(d.rewards, d.dones, None, None, d.bootstrap, g),
+        lambda: oracle.eligibility_traces(d.increments, d.starts, 0, g, lam),
+        lambda: oracle.episodic_prefix_sum(d.rewards, d.starts, 0),
+        lambda: oracle.episodic_prefix_sum(d.ints, d.starts, 0),
+    ]
+
+
+def _rows(d, lo, hi):
+    """Rows lo..hi of a rollout (every per-env array sliced, views only)."""
+    import dataclasses
+
+    out = {}
+    for f in dataclasses.fields(d):
+        v = getattr(d, f.name)
+        if isinstance(v, np.ndarray) and v.shape[:1] == (d.num_envs,):
+            v = v[lo:hi]
+        out[f.name] = v
+    out["num_envs"] = hi - lo
+    return dataclasses.replace(d, **out)
+
+
+def _oracle_passes(name, lo, hi, seconds):
+    """Worker: rows lo..hi of the named workload through the oracle, repeated
+    for about `seconds`; returns (passes, seconds taken)."""
+    sys.path.insert(0, ROOT)
+    from linear_recurrence_scan_row_amd import workloads
+
+    cfg = dict(workloads.CONFIGS[name])
+    d = _rows(workloads.make(name), lo, hi)
+    fns = oracle_calls(name, cfg, d)
     for f in fns:   # warm-up (also builds the library if needed)
         f()
     passes = 0
@@ -407,11 +464,37 @@ def run_cpu_baseline(name, cfg, host, seconds):
         passes += 1
         el = time.perf_counter() - t0
         if el >= seconds:
-            break
+            return passes, el
+
+
+def run_cpu_baseline(name, cfg, host, seconds, workers=1):
+    """The fp64 sequential oracle on this host's CPU over the same rollout and
+    calls, repeated for about `seconds`.  workers > 1 splits the rows evenly
+    over that many worker processes (fresh interpreters, no GPU state) that
+    run at the same time."""
+    d = host
+    nfns = len(oracle_calls(name, cfg, d))
     nt = d.num_envs * d.T
-    return dict(value=passes * len(fns) * nt / el, unit="env-steps/s", cores=1, kind="oracle",
-                sample=(f"full {d.num_envs}x{d.T} rollout, {len(fns)} estimator calls per pass, "
-                        f"{passes} passes in {el:.1f} s, one thread, fp64 sequential C"))
+    if workers == 1:
+        passes, el = _oracle_passes(name, 0, d.num_envs, seconds)
+        return dict(value=passes * nfns * nt / el, unit="env-steps/s", cores=1, kind="oracle",
+                    sample=(f"full {d.num_envs}x{d.T} rollout, {nfns} estimator calls per "
+                            f"pass, {passes} passes in {el:.1f} s, one thread, fp64 "
+                            f"sequential C"))
+    import multiprocessing
+    from concurrent.futures import ProcessPoolExecutor
+
+    bounds = np.linspace(0, d.num_envs, workers + 1).astype(int)
+    jobs = [(bounds[k], bounds[k + 1]) for k in range(workers) if bounds[k + 1] > bounds[k]]
+    with ProcessPoolExecutor(len(jobs), mp_context=multiprocessing.get_context("spawn")) as ex:
+        res = list(ex.map(_oracle_passes, [name] * len(jobs), [lo for lo, _ in jobs],
+                          [hi for _, hi in jobs], [seconds] * len(jobs)))
+    steps = sum(p * nfns * (hi - lo) * d.T for (p, _), (lo, hi) in zip(res, jobs))
+    el = max(e for _, e in res)
+    return dict(value=float(steps / el), unit="env-steps/s", cores=len(jobs), kind="oracle",
+                sample=(f"full {d.num_envs}x{d.T} rollout, {nfns} estimator calls per pass, "
+                        f"rows split over {len(jobs)} worker processes running together for "
+                        f"{el:.1f} s, fp64 sequential C"))
 
 
 # ------------------------------------------------------------------ traffic
@@ -615,6 +698,7 @@ def main():
         "env_steps_per_s": (1 if args.workload == "ppo_4096x128" else ncalls) * res["nt"] / step_s,
         "bytes_per_step": res["step_bytes"],
         "calls": calls_out,
+        "full_call_us": {k: round(v * 1e3, 3) for k, v in res["protocol_ms"].items()},
         "copy_ceiling": {"gbs": round(res["copy_gbs"], 1), "bytes": res["copy_bytes"],
                          "kind": "torch device copy, cold rotation, same bytes moved"},
         "roofline": {
@@ -631,6 +715,12 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = run_cpu_baseline(args.workload, cfg, host, args.cpu_seconds)
+        # the same oracle with the rows split over the host's cores (at most
+        # 16, the CPU share of one GPU), for context
+        cores = min(16, len(os.sched_getaffinity(0)))
+        if cores > 1:
+            out["cpu_baseline_all_cores"] = run_cpu_baseline(args.workload, cfg, host,
+                                                             args.cpu_seconds / 2, cores)
     print(json.dumps(out), flush=True)
 
 
