@@ -275,20 +275,36 @@ __device__ __forceinline__ Window window_of(const Geometry &geo, uint32_t g) {
 }
 
 // Row-local step index t and row offset (relative to row0) of each of the
-// lane's K steps.
-template <int MODE>
+// lane's K steps.  VEC: T % K == 0 and off % K == 0, so the K steps lie in
+// one row and only the last can end it (only the first can start it).
+// WAVE_LOCAL: T divides the 256-step wave span, so it is a power of two.
+template <int MODE, bool VEC = false, bool WAVE_LOCAL = false>
 __device__ __forceinline__ void step_positions(const Window &w, uint32_t off, uint32_t T,
                                                uint32_t (&t)[kK], uint32_t (&row)[kK]) {
     if constexpr (MODE == kFull) {
-        uint32_t r = off / T;
-        uint32_t s = off - r * T;
+        uint32_t r, s;
+        if constexpr (WAVE_LOCAL) {
+            r = off >> __builtin_ctz(T);
+            s = off & (T - 1);
+        } else {
+            r = off / T;
+            s = off - r * T;
+        }
+        if constexpr (VEC) {
 #pragma unroll
-        for (int i = 0; i < kK; ++i) {
-            t[i] = s;
-            row[i] = r;
-            if (++s == T) {
-                s = 0;
-                ++r;
+            for (int i = 0; i < kK; ++i) {
+                t[i] = s + i;
+                row[i] = r;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kK; ++i) {
+                t[i] = s;
+                row[i] = r;
+                if (++s == T) {
+                    s = 0;
+                    ++r;
+                }
             }
         }
     } else {
@@ -514,18 +530,23 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
             // tile) and the lane whose chunk ends the window while its row
             // goes on (a partial chunk in the chunk modes).
             uint32_t t[kK], row[kK];
-            step_positions<MODE>(win, off, T, t, row);
-            bool valid[kK];
+            step_positions<MODE, VEC, WAVE_LOCAL>(win, off, T, t, row);
+            bool valid[kK], edge[kK];
             float boot[kK];
 #pragma unroll
             for (int i = 0; i < kK; ++i) {
                 valid[i] = off + i < L;
+                // on the vector path only the lane's last step can end a row
+                edge[i] = (!VEC || i == kK - 1) && t[i] == T - 1;
                 boot[i] = 0.f;
-                if (valid[i] && t[i] == T - 1 && bootstrap != nullptr)
+                if (valid[i] && edge[i] && bootstrap != nullptr)
                     boot[i] = widen<float>(bootstrap[row0 + row[i]]);
             }
             float v_first = 0.f, mu_first = 0.f, pi_first = 0.f, eq_first = 0.f;
-            const bool halo_from_memory = (lane == 0 || off + kK >= L) && off + kK < win.row_rest;
+            // With WAVE_LOCAL every wave (and so lane 0's chunk and the
+            // window) ends at a row end: the halo is never used.
+            const bool halo_from_memory =
+                !WAVE_LOCAL && (lane == 0 || off + kK >= L) && off + kK < win.row_rest;
             if (halo_from_memory) {
                 const int64_t jh = base + off + kK;
                 if constexpr (EST == kGae || EST == kTdLambda || EST == kVtrace)
@@ -542,17 +563,16 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
             float succ[kK];  // successor value where the chain stops
 #pragma unroll
             for (int i = 0; i < kK; ++i) {
-                const bool edge = t[i] == T - 1;
                 if constexpr (kFlags) {
                     const bool tr = TRUNC && trunc[i] && !term[i];
-                    cont[i] = valid[i] && !term[i] && !tr && !edge;
+                    cont[i] = valid[i] && !term[i] && !tr && !edge[i];
                     float sv = term[i] ? 0.f : boot[i];
                     if constexpr (TRUNC) {
                         if (tr) sv = tv[i];
                     }
                     succ[i] = sv;
                 } else {
-                    cont[i] = valid[i] && !edge;
+                    cont[i] = valid[i] && !edge[i];
                     succ[i] = boot[i];
                 }
             }
@@ -739,9 +759,14 @@ __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint3
             if constexpr (KIND == kForwardFlags) load_flags<VEC>(f, p.flags + base, off, L);
             if constexpr (KIND == kForwardAffine) load_steps<VEC>(bt, betas + base, off, L);
             uint32_t t[kK], row[kK];
-            step_positions<MODE>(win, off, T, t, row);
-            bool first = false;  // flag of the step before the lane's chunk (lane 0)
-            if constexpr (KIND == kForwardFlags && AFTER_DONE) {
+            step_positions<MODE, VEC, WAVE_LOCAL>(win, off, T, t, row);
+            bool start[kK];  // t = 0: on the vector path only the lane's first step
+#pragma unroll
+            for (int i = 0; i < kK; ++i) start[i] = (!VEC || i == 0) && t[i] == 0;
+            // flag of the step before the lane's chunk (lane 0; with WAVE_LOCAL
+            // every wave starts a row, so it is never needed)
+            bool first = false;
+            if constexpr (KIND == kForwardFlags && AFTER_DONE && !WAVE_LOCAL) {
                 if (lane == 0 && win.t0 + off > 0 && off <= L) first = p.flags[base + off - 1] != 0;
             }
             float row_carry[kK];
@@ -749,7 +774,7 @@ __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint3
             for (int i = 0; i < kK; ++i) {
                 row_carry[i] = 0.f;
                 if constexpr (KIND == kForwardAffine) {
-                    if (off + i < L && t[i] == 0 && carries != nullptr)
+                    if (off + i < L && start[i] && carries != nullptr)
                         row_carry[i] = widen<float>(carries[row0 + row[i]]);
                 }
             }
@@ -762,7 +787,7 @@ __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint3
                 const bool valid = off + i < L;
                 V a, b;
                 if constexpr (KIND == kForwardFlags) {
-                    bool reset = t[i] == 0;
+                    bool reset = start[i];
                     if constexpr (AFTER_DONE) {
                         reset = reset || (i == 0 ? prev_done : f[i - 1]);
                     } else {
@@ -771,9 +796,8 @@ __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint3
                     a = x[i];
                     b = reset ? V(0) : decay;
                 } else {
-                    const bool start = t[i] == 0;
-                    a = start ? x[i] + bt[i] * row_carry[i] : x[i];
-                    b = start ? V(0) : bt[i];
+                    a = start[i] ? x[i] + bt[i] * row_carry[i] : x[i];
+                    b = start[i] ? V(0) : bt[i];
                 }
                 alpha[i] = valid ? a : V(0);
                 beta[i] = valid ? b : V(1);
