@@ -14,9 +14,13 @@ static_assert(kMaxGroupedCalls == 14, "the head is 14 preloaded kernel-argument 
 
 // S: storage type of every member's real-valued arrays (float also carries
 // the int32 prefix sums).
+// Eight waves per SIMD must fit: a one-shot step places eight 8-wave
+// workgroups' worth of waves on every SIMD, and at seven (the occupancy the
+// compiler picks on its own, for its SGPR count) an eighth of them waits
+// for a second round.
 template <typename S>
-__global__ __launch_bounds__(kGroupWaves * kWave) void grouped_scan(RLCA_HEAD_ARGS,
-                                                                    GroupedArgs a) {
+__global__ __launch_bounds__(kGroupWaves * kWave) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void grouped_scan(RLCA_HEAD_ARGS, GroupedArgs a) {
     const uint32_t head[kMaxGroupedCalls] = {h0, h1, h2,  h3,  h4,  h5,  h6,
                                              h7, h8, h9, h10, h11, h12, h13};
     // The call whose workgroup range holds this workgroup: ends increase, so

@@ -707,9 +707,18 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
     }
 }
 
+// 8-wave kernels whose rows span waves ask for eight waves per SIMD: a
+// one-shot launch of up to 1024 such workgroups needs every slot, and at the
+// seven the compiler picks on its own for these heavier bodies (their SGPR
+// count) an eighth of the waves waits for a second round.  The SGPRs over
+// the limit spill to VGPR lanes.  Lighter variants reach eight by themselves
+// and keep their registers.
+#define RLCA_EIGHT_WAVES(NEED) __attribute__((amdgpu_waves_per_eu((NEED) ? 8 : 1)))
+
 template <int EST, bool TRUNC, bool VEC, int NW, bool WAVE_LOCAL, int MODE, typename S,
           bool STATS = false>
-__global__ __launch_bounds__(NW * kWave) void backward_scan(LEAD_ARGS, BackwardParams p) {
+__global__ __launch_bounds__(NW * kWave) RLCA_EIGHT_WAVES(NW == 8 && !WAVE_LOCAL && VEC)
+void backward_scan(LEAD_ARGS, BackwardParams p) {
     adopt_lead<EST>(p, LEAD_NAMES);
     backward_body<EST, TRUNC, VEC, NW, WAVE_LOCAL, MODE, S, STATS>(p, blockIdx.x, gridDim.x);
 }
@@ -837,7 +846,8 @@ __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint3
 
 template <typename V, int KIND, bool AFTER_DONE, bool VEC, int NW, bool WAVE_LOCAL, int MODE,
           typename S>
-__global__ __launch_bounds__(NW * kWave) void forward_scan(LEAD_ARGS, ForwardParams p) {
+__global__ __launch_bounds__(NW * kWave) RLCA_EIGHT_WAVES(NW == 8 && !WAVE_LOCAL && VEC)
+void forward_scan(LEAD_ARGS, ForwardParams p) {
     adopt_lead(p, LEAD_NAMES);
     forward_body<V, KIND, AFTER_DONE, VEC, NW, WAVE_LOCAL, MODE, S>(p, blockIdx.x, gridDim.x);
 }
