@@ -205,9 +205,9 @@ rlca_status rlca_affine_scan(const float *alpha, const float *beta, const float 
  * nothing enqueued on any failure), plus: no call may write memory that
  * another call of the batch reads or writes (RLCA_ERR_ALIASING), because the
  * calls run concurrently.  Calls on the vectorised path that need a single
- * launch share grouped launches (one launch for up to 14 calls), which
- * removes the per-launch overhead that dominates small rollouts; the others
- * are enqueued one by one, in order.  Results are bit for bit those of the
+ * launch share grouped launches (one launch for up to 14 calls of one shape
+ * class and storage type), which removes the per-launch overhead that
+ * dominates small rollouts; the others are enqueued one by one.  Results are bit for bit those of the
  * separate calls (a grouped launch keeps each call's tile geometry).
  * (Launch-overhead reduction for small shapes: the summary's §9
  * Limitations, where launch and wrapper overhead dominate at 16 steps.) */

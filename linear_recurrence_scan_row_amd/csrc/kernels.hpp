@@ -1127,7 +1127,32 @@ constexpr int grouped_affine_forward_variant(bool wave_local, bool one_wave) {
     return one_wave ? 50 : 32 + (wave_local ? 1 : 0);
 }
 
-rlca_status launch_grouped(const GroupedLaunch &launch, int storage, hipStream_t stream);
+// Classes of grouped launches, one kernel each (see est_batch.hip): 8-wave
+// calls whose rows end at wave boundaries (wave-local), split into the light
+// bodies and the importance-weighted ones (V-Trace, Retrace: more registers);
+// other 8-wave calls; one-wave calls.
+enum GroupClass : int {
+    kGroupWaveLocal = 0,
+    kGroupWaveLocalWeighted = 1,
+    kGroupWaves8 = 2,
+    kGroupOneWave = 3,
+};
+constexpr int kGroupClasses = 4;
+// Minimum waves per SIMD each class kernel is compiled for (one-shot shapes
+// need all eight slots; the light wave-local bodies fit eight by themselves).
+#ifndef RLCA_GROUP_CLASS_WAVES
+#define RLCA_GROUP_CLASS_WAVES {1, 8, 8, 8}
+#endif
+constexpr int kGroupClassWaves[kGroupClasses] = RLCA_GROUP_CLASS_WAVES;
+
+inline int group_class(const LaunchShape &s, bool weighted) {
+    if (s.waves == 1) return kGroupOneWave;
+    if (!s.wave_local) return kGroupWaves8;
+    return weighted ? kGroupWaveLocalWeighted : kGroupWaveLocal;
+}
+
+rlca_status launch_grouped(const GroupedLaunch &launch, int storage, int cls,
+                           hipStream_t stream);
 
 // One translation unit per estimator instantiates these (see est_*.hip).
 rlca_status launch_gae(BackwardParams &p, const LaunchShape &s, int storage, hipStream_t stream);

@@ -677,22 +677,27 @@ rlca_status rlca_run_batch(const rlca_call *calls, int count, hipStream_t stream
         }
     }
     // Vector-path, single-launch calls share grouped launches; the rest
-    // (unaligned or chunked) are enqueued one by one.  A grouped launch that
-    // would hold one call runs that call's own kernel instead.
-    // Members of one grouped launch share the storage type of their
-    // real-valued arrays (int32 sums join the 4-byte group).
-    GroupedLaunch group;
-    int members[kMaxGroupedCalls];
-    int count_in_group = 0, group_storage = kStoreF32;
-    auto flush = [&]() -> rlca_status {
-        if (count_in_group == 0) return RLCA_OK;
-        const int n = count_in_group;
-        count_in_group = 0;
-        if (n == 1) return launch_call(prepared[members[0]], stream);
-        for (int m = n; m < kMaxGroupedCalls; ++m) group.head[m] = kHeadEndMask;
-        return launch_grouped(group, group_storage, stream);
+    // (unaligned or chunked) are enqueued one by one.  Members of one grouped
+    // launch share a shape class (one kernel per class) and the storage type
+    // of their real-valued arrays (int32 sums join the 4-byte group).  A
+    // grouped launch that would hold one call runs that call's own kernel.
+    struct Pending {
+        GroupedLaunch launch;
+        int members[kMaxGroupedCalls];
+        int count;
+        int storage;
     };
-    group.workgroups = 0;
+    Pending pending[kGroupClasses];
+    for (Pending &g : pending) g.count = 0, g.storage = kStoreF32, g.launch.workgroups = 0;
+    auto flush = [&](int cls) -> rlca_status {
+        Pending &g = pending[cls];
+        if (g.count == 0) return RLCA_OK;
+        const int n = g.count;
+        g.count = 0;
+        if (n == 1) return launch_call(prepared[g.members[0]], stream);
+        for (int m = n; m < kMaxGroupedCalls; ++m) g.launch.head[m] = kHeadEndMask;
+        return launch_grouped(g.launch, g.storage, cls, stream);
+    };
     for (int i = 0; i < count; ++i) {
         Call &c = prepared[i];
         if (c.empty) continue;
@@ -704,18 +709,24 @@ rlca_status rlca_run_batch(const rlca_call *calls, int count, hipStream_t stream
             if (st != RLCA_OK) return st;
             continue;
         }
-        if (count_in_group == kMaxGroupedCalls || group.workgroups + wgs > kMaxGrid ||
-            (count_in_group > 0 && c.storage != group_storage)) {
-            const rlca_status st = flush();
+        const int cls = group_class(c.shape, c.backward && (c.est == kVtrace || c.est == kRetrace));
+        Pending &g = pending[cls];
+        if (g.count == kMaxGroupedCalls || g.launch.workgroups + wgs > kMaxGrid ||
+            (g.count > 0 && c.storage != g.storage)) {
+            const rlca_status st = flush(cls);
             if (st != RLCA_OK) return st;
         }
-        if (count_in_group == 0) group.workgroups = 0, group_storage = c.storage;
-        group.workgroups += wgs;
-        group.args.calls[count_in_group] = member;
-        group.head[count_in_group] = group.workgroups | ((uint32_t)variant << kHeadVariantShift);
-        members[count_in_group++] = i;
+        if (g.count == 0) g.launch.workgroups = 0, g.storage = c.storage;
+        g.launch.workgroups += wgs;
+        g.launch.args.calls[g.count] = member;
+        g.launch.head[g.count] = g.launch.workgroups | ((uint32_t)variant << kHeadVariantShift);
+        g.members[g.count++] = i;
     }
-    return flush();
+    for (int cls = 0; cls < kGroupClasses; ++cls) {
+        const rlca_status st = flush(cls);
+        if (st != RLCA_OK) return st;
+    }
+    return RLCA_OK;
 }
 
 const char *rlca_status_string(rlca_status status) {
