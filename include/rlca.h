@@ -207,8 +207,9 @@ rlca_status rlca_affine_scan(const float *alpha, const float *beta, const float 
  * calls run concurrently.  Calls on the vectorised path that need a single
  * launch share grouped launches (one launch for up to 14 calls of one shape
  * class and storage type), which removes the per-launch overhead that
- * dominates small rollouts; the others are enqueued one by one.  Results are bit for bit those of the
- * separate calls (a grouped launch keeps each call's tile geometry).
+ * dominates small rollouts; the others are enqueued one by one.  Results
+ * are bit for bit those of the separate calls (a grouped launch keeps each
+ * call's tile geometry).
  * (Launch-overhead reduction for small shapes: the summary's §9
  * Limitations, where launch and wrapper overhead dominate at 16 steps.) */
 #define RLCA_MAX_BATCH 64

@@ -3,7 +3,7 @@
 
 namespace rlca {
 rlca_status launch_discounted(BackwardParams &p, const LaunchShape &s, int storage,
-                    hipStream_t stream) {
+                              hipStream_t stream) {
     return launch_backward<kDiscounted>(p, s, storage, stream);
 }
 }  // namespace rlca

@@ -3,7 +3,7 @@
 
 namespace rlca {
 rlca_status launch_gae(BackwardParams &p, const LaunchShape &s, int storage,
-                    hipStream_t stream) {
+                       hipStream_t stream) {
     return launch_backward<kGae>(p, s, storage, stream);
 }
 rlca_status launch_gae_stats(BackwardParams &p, const LaunchShape &s, hipStream_t stream) {

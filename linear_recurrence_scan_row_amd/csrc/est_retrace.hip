@@ -3,7 +3,7 @@
 
 namespace rlca {
 rlca_status launch_retrace(BackwardParams &p, const LaunchShape &s, int storage,
-                    hipStream_t stream) {
+                           hipStream_t stream) {
     return launch_backward<kRetrace>(p, s, storage, stream);
 }
 }  // namespace rlca

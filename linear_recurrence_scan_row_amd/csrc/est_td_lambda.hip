@@ -3,7 +3,7 @@
 
 namespace rlca {
 rlca_status launch_td_lambda(BackwardParams &p, const LaunchShape &s, int storage,
-                    hipStream_t stream) {
+                             hipStream_t stream) {
     return launch_backward<kTdLambda>(p, s, storage, stream);
 }
 }  // namespace rlca

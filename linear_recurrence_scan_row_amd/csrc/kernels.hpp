@@ -1073,8 +1073,10 @@ template <int KIND, bool AFTER_DONE>
 rlca_status launch_forward_float(ForwardParams &p, const LaunchShape &s, int storage,
                                  hipStream_t stream) {
     switch (storage) {
-        case kStoreBF16: return launch_forward_variant<float, KIND, AFTER_DONE, __bf16>(p, s, stream);
-        case kStoreF16: return launch_forward_variant<float, KIND, AFTER_DONE, _Float16>(p, s, stream);
+        case kStoreBF16:
+            return launch_forward_variant<float, KIND, AFTER_DONE, __bf16>(p, s, stream);
+        case kStoreF16:
+            return launch_forward_variant<float, KIND, AFTER_DONE, _Float16>(p, s, stream);
         default: return launch_forward_variant<float, KIND, AFTER_DONE, float>(p, s, stream);
     }
 }

@@ -62,7 +62,8 @@ static size_t storage_bytes(int storage) { return storage == kStoreF32 ? 4 : 2; 
 static rlca_status check_aliasing(const Span *outs, int nout, const Span *ins, int nin) {
     for (int i = 0; i < nout; ++i) {
         for (int j = 0; j < nin; ++j)
-            if (overlaps(outs[i].p, outs[i].bytes, ins[j].p, ins[j].bytes)) return RLCA_ERR_ALIASING;
+            if (overlaps(outs[i].p, outs[i].bytes, ins[j].p, ins[j].bytes))
+                return RLCA_ERR_ALIASING;
         for (int j = i + 1; j < nout; ++j)
             if (overlaps(outs[i].p, outs[i].bytes, outs[j].p, outs[j].bytes))
                 return RLCA_ERR_ALIASING;
@@ -503,9 +504,10 @@ rlca_status rlca_gae(const float *rewards, const float *values, const uint8_t *t
                      const float *bootstrap, float gamma, float lambda, int64_t num_envs,
                      int64_t T, float *advantages, float *returns, hipStream_t stream) {
     Call c;
-    return run_one(prepare_gae(kStoreF32, rewards, values, terminated, truncated, trunc_values, bootstrap,
-                               gamma, lambda, num_envs, T, advantages, returns, &c),
-                   c, stream);
+    const rlca_status st =
+        prepare_gae(kStoreF32, rewards, values, terminated, truncated, trunc_values, bootstrap,
+                    gamma, lambda, num_envs, T, advantages, returns, &c);
+    return run_one(st, c, stream);
 }
 
 rlca_status rlca_td_lambda(const float *rewards, const float *values,
@@ -514,9 +516,10 @@ rlca_status rlca_td_lambda(const float *rewards, const float *values,
                            float lambda, int64_t num_envs, int64_t T, float *returns,
                            hipStream_t stream) {
     Call c;
-    return run_one(prepare_td_lambda(kStoreF32, rewards, values, terminated, truncated, trunc_values,
-                                     bootstrap, gamma, lambda, num_envs, T, returns, &c),
-                   c, stream);
+    const rlca_status st =
+        prepare_td_lambda(kStoreF32, rewards, values, terminated, truncated, trunc_values,
+                          bootstrap, gamma, lambda, num_envs, T, returns, &c);
+    return run_one(st, c, stream);
 }
 
 rlca_status rlca_discounted_returns(const float *rewards, const uint8_t *terminated,
@@ -524,9 +527,10 @@ rlca_status rlca_discounted_returns(const float *rewards, const uint8_t *termina
                                     const float *bootstrap, float gamma, int64_t num_envs,
                                     int64_t T, float *returns, hipStream_t stream) {
     Call c;
-    return run_one(prepare_discounted(kStoreF32, rewards, terminated, truncated, trunc_values, bootstrap,
-                                      gamma, num_envs, T, returns, &c),
-                   c, stream);
+    const rlca_status st =
+        prepare_discounted(kStoreF32, rewards, terminated, truncated, trunc_values, bootstrap,
+                           gamma, num_envs, T, returns, &c);
+    return run_one(st, c, stream);
 }
 
 rlca_status rlca_vtrace(const float *rewards, const float *values, const float *behaviour_logp,
@@ -536,10 +540,11 @@ rlca_status rlca_vtrace(const float *rewards, const float *values, const float *
                         float c_bar, int64_t num_envs, int64_t T, float *vs,
                         float *pg_advantages, hipStream_t stream) {
     Call c;
-    return run_one(prepare_vtrace(kStoreF32, rewards, values, behaviour_logp, target_logp, terminated,
-                                  truncated, trunc_values, bootstrap, gamma, lambda, rho_bar,
-                                  c_bar, num_envs, T, vs, pg_advantages, &c),
-                   c, stream);
+    const rlca_status st =
+        prepare_vtrace(kStoreF32, rewards, values, behaviour_logp, target_logp, terminated,
+                       truncated, trunc_values, bootstrap, gamma, lambda, rho_bar, c_bar,
+                       num_envs, T, vs, pg_advantages, &c);
+    return run_one(st, c, stream);
 }
 
 rlca_status rlca_retrace(const float *rewards, const float *q_values, const float *expected_q,
@@ -549,10 +554,11 @@ rlca_status rlca_retrace(const float *rewards, const float *q_values, const floa
                          float lambda, float c_bar, int64_t num_envs, int64_t T,
                          float *q_ret, hipStream_t stream) {
     Call c;
-    return run_one(prepare_retrace(kStoreF32, rewards, q_values, expected_q, behaviour_logp, target_logp,
-                                   terminated, truncated, trunc_values, bootstrap, gamma, lambda,
-                                   c_bar, num_envs, T, q_ret, &c),
-                   c, stream);
+    const rlca_status st =
+        prepare_retrace(kStoreF32, rewards, q_values, expected_q, behaviour_logp, target_logp,
+                        terminated, truncated, trunc_values, bootstrap, gamma, lambda, c_bar,
+                        num_envs, T, q_ret, &c);
+    return run_one(st, c, stream);
 }
 
 rlca_status rlca_eligibility_traces(const float *increments, const uint8_t *flags,
@@ -560,9 +566,9 @@ rlca_status rlca_eligibility_traces(const float *increments, const uint8_t *flag
                                     float lambda, int64_t num_envs, int64_t T, float *traces,
                                     hipStream_t stream) {
     Call c;
-    return run_one(prepare_eligibility(kStoreF32, increments, flags, convention, gamma, lambda, num_envs, T,
-                                       traces, &c),
-                   c, stream);
+    const rlca_status st = prepare_eligibility(kStoreF32, increments, flags, convention, gamma,
+                                               lambda, num_envs, T, traces, &c);
+    return run_one(st, c, stream);
 }
 
 rlca_status rlca_episodic_prefix_sum(const void *x, rlca_dtype dtype, const uint8_t *flags,
@@ -577,8 +583,9 @@ rlca_status rlca_affine_scan(const float *alpha, const float *beta, const float 
                              rlca_direction direction, int64_t num_envs, int64_t T, float *out,
                              hipStream_t stream) {
     Call c;
-    return run_one(prepare_affine(kStoreF32, alpha, beta, carry, direction, num_envs, T, out, &c), c,
-                   stream);
+    const rlca_status st =
+        prepare_affine(kStoreF32, alpha, beta, carry, direction, num_envs, T, out, &c);
+    return run_one(st, c, stream);
 }
 
 size_t rlca_gae_stats_workspace_size(int64_t num_envs, int64_t T) {
@@ -709,7 +716,8 @@ rlca_status rlca_run_batch(const rlca_call *calls, int count, hipStream_t stream
             if (st != RLCA_OK) return st;
             continue;
         }
-        const int cls = group_class(c.shape, c.backward && (c.est == kVtrace || c.est == kRetrace));
+        const bool weighted = c.backward && (c.est == kVtrace || c.est == kRetrace);
+        const int cls = group_class(c.shape, weighted);
         Pending &g = pending[cls];
         if (g.count == kMaxGroupedCalls || g.launch.workgroups + wgs > kMaxGrid ||
             (g.count > 0 && c.storage != g.storage)) {
