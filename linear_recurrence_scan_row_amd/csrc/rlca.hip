@@ -87,19 +87,22 @@ static bool vec_ok(int64_t T, const void *const *wide, int nw, size_t elem,
 // wave span) need no cross-wave exchange.  The wave count per workgroup was
 // chosen by measurement on MI355X with cold HBM-resident operands: such short
 // rows run fastest in 8-wave workgroups; rows of 257..1023 steps with one
-// wave walking the row tile by tile; longer rows with 8 waves sharing each
-// tile through LDS.  Fewer than 64 long rows cannot fill the chip one
+// wave walking the row tile by tile when there are at least 4096 rows (with
+// fewer, one wave per row leaves most wave slots empty, and 8-wave
+// workgroups packing several rows per tile win by 8-19%); longer rows with 8
+// waves sharing each tile through LDS.  Fewer than 64 long rows cannot fill the chip one
 // workgroup per row, so they are split into chunks that run in parallel
 // (three launches, inputs read twice): 50x faster for one row of 1M steps,
 // even at 64 rows, slower from 128 rows on (one workgroup per row then
 // sustains 3.4-5 TB/s).
 static constexpr int64_t kChunkedMaxRows = 64;
+static constexpr int64_t kOneWaveMinRows = 4096;
 
 static LaunchShape choose_shape(int64_t num_envs, int64_t T, bool vec) {
     LaunchShape s;
     s.vec = vec;
     s.wave_local = vec && T <= kWave * kK && (kWave * kK) % T == 0;
-    s.waves = (T <= kWave * kK || T >= 1024) ? 8 : 1;
+    s.waves = (T <= kWave * kK || T >= 1024 || num_envs < kOneWaveMinRows) ? 8 : 1;
     s.chunked = vec && T > 2 * (int64_t)kChunkSteps && num_envs < kChunkedMaxRows;
 #ifdef RLCA_FORCE_WAVES
     s.waves = RLCA_FORCE_WAVES;

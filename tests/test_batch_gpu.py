@@ -123,8 +123,9 @@ class Member:
 
 def mixed_members(device):
     """Every op, both flag conventions, both affine directions; wave-local
-    (T | 256), one-wave (256 < T < 1024) and eight-wave (T >= 1024) shapes; an
-    unaligned T (scalar path), a chunked few-long-rows call, and an empty one."""
+    (T | 256), eight-wave (T >= 1024, or fewer than 4096 rows) and one-wave
+    (4096 rows and more of 257..1023 steps) shapes; an unaligned T (scalar
+    path), a chunked few-long-rows call, and an empty one."""
     return [
         Member("gae", 1, 300, 128, device),
         Member("gae", 2, 17, 48, device, trunc=False, boot=False),
@@ -144,6 +145,11 @@ def mixed_members(device):
         Member("affine", 16, 11, 520, device, direction=rl.FORWARD, boot=False),
         Member("affine", 17, 2, 9000, device, direction=rl.FORWARD),   # chunked forward
         Member("gae", 18, 0, 128, device),                       # empty
+        # one-wave members (>= 4096 rows of 257..1023 steps), the last
+        # workgroup of each only partly filled
+        Member("vtrace", 19, 4100, 516, device),
+        Member("traces", 20, 4097, 300, device, conv=rl.RESET_AFTER_DONE),
+        Member("affine", 21, 4099, 260, device, direction=rl.BACKWARD),
     ]
 
 
@@ -232,9 +238,9 @@ def test_single_member_and_one_wave_only_batches(gpu_device):
     # launch, with a partly filled last workgroup (num_groups not a multiple
     # of 8)
     for members in ([Member("gae", 40, 64, 128, gpu_device)],
-                    [Member("retrace", 41, 13, 300, gpu_device),
-                     Member("traces", 42, 21, 1020, gpu_device),
-                     Member("affine", 43, 5, 260, gpu_device, direction=rl.BACKWARD)]):
+                    [Member("retrace", 41, 4097, 300, gpu_device),
+                     Member("traces", 42, 4100, 1020, gpu_device),
+                     Member("affine", 43, 4101, 260, gpu_device, direction=rl.BACKWARD)]):
         batch = rl.Batch()
         for m in members:
             m.record(batch)

@@ -43,8 +43,8 @@ def rollout_args(seed, N, T, trunc=True):
 
 
 # launch shapes: scalar path (T % 4), wave-local, one-wave, eight-wave, chunked
-SHAPES = [(7, 37), (1, 1), (2, 2), (300, 128), (4096, 128), (33, 512), (9, 1024), (3, 4100),
-          (2, 20000)]
+SHAPES = [(7, 37), (1, 1), (2, 2), (300, 128), (4096, 128), (33, 512), (4096, 300), (9, 1024),
+          (3, 4100), (2, 20000)]
 
 
 @pytest.mark.parametrize("N,T", SHAPES)

@@ -22,8 +22,9 @@ pytestmark = pytest.mark.gpu
 
 UNIT_ROUNDOFF = {torch.bfloat16: 2.0 ** -8, torch.float16: 2.0 ** -11}
 DTYPES = [torch.bfloat16, torch.float16]
-# scalar path (T % 4 != 0), wave-local, one-wave, eight-wave, chunked (few long rows)
-SHAPES = [(5, 37), (300, 128), (33, 512), (9, 1024), (3, 4100), (2, 9000)]
+# scalar path (T % 4 != 0), wave-local, eight-wave (rows sharing tiles), one-wave
+# (>= 4096 rows of 257..1023 steps), eight-wave, chunked (few long rows)
+SHAPES = [(5, 37), (300, 128), (33, 512), (4097, 300), (9, 1024), (3, 4100), (2, 9000)]
 
 
 def assert_lowp(gpu, ref, dtype, what):

@@ -118,7 +118,9 @@ def check_forward(f, device, conv=rl.RESET_ON_START, gamma=0.99, lam=0.9, what="
 
 SHAPES = [(1, 1), (3, 1), (2, 2), (5, 3), (7, 5), (8, 16), (3, 63), (2, 64), (5, 65),
           (4, 127), (9, 128), (3, 129), (2, 255), (2, 257), (1, 1023), (2, 1024), (1, 1025),
-          (3, 2049), (1, 4097), (600, 7), (1030, 4), (257, 12), (5, 3001)]
+          (3, 2049), (1, 4097), (600, 7), (1030, 4), (257, 12), (5, 3001),
+          # rows of 257..1023 steps take one-wave workgroups from 4096 rows on
+          (4096, 260), (4099, 516), (4096, 1020)]
 
 
 @pytest.mark.parametrize("N,T", SHAPES)
