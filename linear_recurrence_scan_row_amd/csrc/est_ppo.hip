@@ -94,9 +94,10 @@ __global__ __launch_bounds__(kPpoThreads) void ppo_clip_loss(
         typedef float f4 __attribute__((ext_vector_type(4)));
         const int64_t n4 = M / 4;
         for (int64_t i = (int64_t)blockIdx.x * kPpoThreads + threadIdx.x; i < n4; i += stride) {
-            const f4 a = reinterpret_cast<const f4 *>(adv)[i];
-            const f4 pn = reinterpret_cast<const f4 *>(logp_new)[i];
-            const f4 po = reinterpret_cast<const f4 *>(logp_old)[i];
+            // each input is read once: non-temporal loads
+            const f4 a = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(adv) + i);
+            const f4 pn = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(logp_new) + i);
+            const f4 po = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(logp_old) + i);
             f4 g;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {

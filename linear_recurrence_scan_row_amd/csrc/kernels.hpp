@@ -155,7 +155,11 @@ struct FlagWord<4> {
     typedef uint32_t type;
 };
 
-template <bool VEC, typename E, typename S>
+// LAST: this is the last read of the data, so the vector loads carry the
+// non-temporal hint (measured 3-5% faster for streams read once; the chunk
+// modes' aggregate pass, whose inputs the apply pass reads again, keeps
+// them cacheable).
+template <bool VEC, bool LAST = true, typename E, typename S>
 __device__ __forceinline__ void load_steps(E (&x)[kK], const S *__restrict__ p, uint32_t off,
                                            uint32_t L) {
     static_assert(sizeof(E) == 4 && (sizeof(S) == 4 || sizeof(S) == 2), "32-bit scan values");
@@ -164,7 +168,10 @@ __device__ __forceinline__ void load_steps(E (&x)[kK], const S *__restrict__ p, 
     typedef typename VecOf<S, kK>::type vec;
     if constexpr (VEC) {
         vec q = {};
-        if (off < L) q = *reinterpret_cast<const vec *>(p + off);
+        if (off < L) {
+            const vec *src = reinterpret_cast<const vec *>(p + off);
+            q = LAST ? __builtin_nontemporal_load(src) : *src;
+        }
         if constexpr (kK == 1) {
             x[0] = widen<E>(q);
         } else {
@@ -177,13 +184,16 @@ __device__ __forceinline__ void load_steps(E (&x)[kK], const S *__restrict__ p, 
     }
 }
 
-template <bool VEC>
+template <bool VEC, bool LAST = true>
 __device__ __forceinline__ void load_flags(bool (&f)[kK], const uint8_t *__restrict__ p,
                                            uint32_t off, uint32_t L) {
     if constexpr (VEC) {
         typedef typename FlagWord<kK>::type word;
         uint32_t q = 0;
-        if (off < L) q = *reinterpret_cast<const word *>(p + off);
+        if (off < L) {
+            const word *src = reinterpret_cast<const word *>(p + off);
+            q = LAST ? __builtin_nontemporal_load(src) : *src;
+        }
 #pragma unroll
         for (int i = 0; i < kK; ++i) f[i] = ((q >> (8 * i)) & 0xffu) != 0;
     } else {
@@ -511,17 +521,18 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
             // ---- 1. loads (each input element once)
             float r[kK], v[kK], eq[kK], mu[kK], pi[kK], tv[kK];
             bool term[kK], trunc[kK];
-            load_steps<VEC>(r, rewards + base, off, L);
-            if constexpr (EST != kDiscounted) load_steps<VEC>(v, values + base, off, L);
-            if constexpr (EST == kRetrace) load_steps<VEC>(eq, expected_q + base, off, L);
+            constexpr bool kLast = MODE != kChunkAggregate;
+            load_steps<VEC, kLast>(r, rewards + base, off, L);
+            if constexpr (EST != kDiscounted) load_steps<VEC, kLast>(v, values + base, off, L);
+            if constexpr (EST == kRetrace) load_steps<VEC, kLast>(eq, expected_q + base, off, L);
             if constexpr (EST == kVtrace || EST == kRetrace) {
-                load_steps<VEC>(mu, behaviour_logp + base, off, L);
-                load_steps<VEC>(pi, target_logp + base, off, L);
+                load_steps<VEC, kLast>(mu, behaviour_logp + base, off, L);
+                load_steps<VEC, kLast>(pi, target_logp + base, off, L);
             }
-            if constexpr (kFlags) load_flags<VEC>(term, p.terminated + base, off, L);
+            if constexpr (kFlags) load_flags<VEC, kLast>(term, p.terminated + base, off, L);
             if constexpr (TRUNC) {
-                load_flags<VEC>(trunc, p.truncated + base, off, L);
-                load_steps<VEC>(tv, trunc_values + base, off, L);
+                load_flags<VEC, kLast>(trunc, p.truncated + base, off, L);
+                load_steps<VEC, kLast>(tv, trunc_values + base, off, L);
             }
             // Loads whose addresses depend only on positions go out with the
             // main batch: the bootstrap (carry) of rows ending in this chunk,
@@ -764,9 +775,10 @@ __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint3
             V x[kK];
             float bt[kK];
             bool f[kK];
-            load_steps<VEC>(x, xs + base, off, L);
-            if constexpr (KIND == kForwardFlags) load_flags<VEC>(f, p.flags + base, off, L);
-            if constexpr (KIND == kForwardAffine) load_steps<VEC>(bt, betas + base, off, L);
+            constexpr bool kLast = MODE != kChunkAggregate;
+            load_steps<VEC, kLast>(x, xs + base, off, L);
+            if constexpr (KIND == kForwardFlags) load_flags<VEC, kLast>(f, p.flags + base, off, L);
+            if constexpr (KIND == kForwardAffine) load_steps<VEC, kLast>(bt, betas + base, off, L);
             uint32_t t[kK], row[kK];
             step_positions<MODE, VEC, WAVE_LOCAL>(win, off, T, t, row);
             bool start[kK];  // t = 0: on the vector path only the lane's first step
