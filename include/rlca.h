@@ -24,11 +24,16 @@
  *          alive until the stream has passed the call.
  * Layout:  per-step arrays are dense row-major [num_envs, T]; element (n, t)
  *          is at n*T + t.  `bootstrap` is [num_envs].  Real-valued and int32
- *          data must be aligned to its element size; alignment to four
- *          elements (16 bytes for fp32, 8 for bf16 / fp16) and T % 4 == 0
- *          select the vectorised path but are not required.  Flags are one
- *          byte per step, any nonzero byte meaning "set" (torch.bool and
- *          uint8 both work).
+ *          data must be aligned to its element size; alignment of every
+ *          per-step array to four elements (16 bytes for fp32, 8 for bf16 /
+ *          fp16, 4 for flags) selects the vectorised paths (with T % 4 == 0
+ *          the fastest) but is not required.  Flags are one byte per step,
+ *          any nonzero byte meaning "set" (torch.bool and uint8 both work).
+ *          On the vectorised paths with T % 4 != 0 the library reads whole
+ *          aligned four-element blocks, so it may read (never write) up to
+ *          three elements past the end of a per-step input, inside the
+ *          aligned block that holds its last element; such reads cannot
+ *          fault and their values are not used.
  * Episode boundaries (summary §3.2 Episode-boundary semantics):
  *          terminated[t]  the episode ends after step t in a terminal state:
  *                         successor value 0, no credit flows back past t.

@@ -49,7 +49,7 @@ void grouped_scan(RLCA_HEAD_ARGS, GroupedArgs a) {
     case grouped_backward_variant(EST, TR, false, true): {                                  \
         BackwardParams p = a.calls[c].b;                                                     \
         if (g1 < p.geo.num_groups)                                                           \
-            backward_body<EST, TR, true, 1, false, kFull, S>(p, g1, p.geo.num_groups);      \
+            backward_body<EST, TR, kVecRows, 1, false, kFull, S>(p, g1, p.geo.num_groups);      \
         return;                                                                              \
     }
 #define RLCA_F1(V, ST, INT, AD)                                                              \
@@ -57,7 +57,7 @@ void grouped_scan(RLCA_HEAD_ARGS, GroupedArgs a) {
         if constexpr (!INT || kWide) {                                                       \
             ForwardParams p = a.calls[c].f;                                                  \
             if (g1 < p.geo.num_groups)                                                       \
-                forward_body<V, kForwardFlags, AD, true, 1, false, kFull, ST>(              \
+                forward_body<V, kForwardFlags, AD, kVecRows, 1, false, kFull, ST>(              \
                     p, g1, p.geo.num_groups);                                                \
         }                                                                                    \
         return;                                                                              \
@@ -75,7 +75,7 @@ void grouped_scan(RLCA_HEAD_ARGS, GroupedArgs a) {
             case grouped_affine_forward_variant(false, true): {
                 ForwardParams p = a.calls[c].f;
                 if (g1 < p.geo.num_groups)
-                    forward_body<float, kForwardAffine, false, true, 1, false, kFull, S>(
+                    forward_body<float, kForwardAffine, false, kVecRows, 1, false, kFull, S>(
                         p, g1, p.geo.num_groups);
                 return;
             }
@@ -92,7 +92,7 @@ void grouped_scan(RLCA_HEAD_ARGS, GroupedArgs a) {
         constexpr bool kHeavy = EST == kVtrace || EST == kRetrace;                           \
         if constexpr (kHeavy ? kWeighted : kLight) {                                         \
             BackwardParams p = a.calls[c].b;                                                 \
-            backward_body<EST, TR, true, kGroupWaves, WL, kFull, S>(p, wg,                  \
+            backward_body<EST, TR, kVecRows, kGroupWaves, WL, kFull, S>(p, wg,                  \
                                                                   p.geo.num_groups);        \
         }                                                                                    \
         return;                                                                              \
@@ -101,7 +101,7 @@ void grouped_scan(RLCA_HEAD_ARGS, GroupedArgs a) {
     case grouped_forward_variant(INT, AD, WL, false): {                                     \
         if constexpr ((!INT || kWide) && kLight) {                                           \
             ForwardParams p = a.calls[c].f;                                                  \
-            forward_body<V, kForwardFlags, AD, true, kGroupWaves, WL, kFull, ST>(           \
+            forward_body<V, kForwardFlags, AD, kVecRows, kGroupWaves, WL, kFull, ST>(           \
                 p, wg, p.geo.num_groups);                                                    \
         }                                                                                    \
         return;                                                                              \
@@ -119,7 +119,7 @@ void grouped_scan(RLCA_HEAD_ARGS, GroupedArgs a) {
             case grouped_affine_forward_variant(WL, false): {
                 if constexpr (kLight) {
                     ForwardParams p = a.calls[c].f;
-                    forward_body<float, kForwardAffine, false, true, kGroupWaves, WL, kFull, S>(
+                    forward_body<float, kForwardAffine, false, kVecRows, kGroupWaves, WL, kFull, S>(
                         p, wg, p.geo.num_groups);
                 }
                 return;

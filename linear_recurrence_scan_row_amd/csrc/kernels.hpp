@@ -45,6 +45,15 @@ static_assert(kK == 1 || kK == 2 || kK == 4, "steps per lane: 1, 2 or 4");
 // Waves per workgroup in the chunk modes; the chunk is one tile.
 constexpr int kChunkWaves = 8;
 constexpr uint32_t kChunkSteps = kChunkWaves * kWave * kK;
+// Steps per chunk, and chunks per row: every chunk but the last in scan
+// order spans `span` steps, the last the rest of the row (1 to span steps).
+// Windows widened to K-aligned starts (kVecSkew below) leave room in the tile
+// for the skew (< K <= 4 steps) and give the last chunk 4 to span + 3 steps,
+// room for its hand-off word (chunk_slot).
+constexpr uint32_t chunk_span(bool skew) { return skew ? kChunkSteps - 8 : kChunkSteps; }
+constexpr uint32_t chunk_count(uint32_t T, bool skew) {
+    return (T - (skew ? 4u : 1u)) / chunk_span(skew) + 1;
+}
 
 enum Estimator : int {
     kGae = 0,
@@ -67,7 +76,7 @@ struct Geometry {
     uint32_t T;
     uint32_t rows_per_group;  // full mode: whole rows owned by one workgroup iteration
     uint32_t num_groups;
-    uint32_t chunks_per_row;  // chunk modes: chunks of kChunkSteps per row
+    uint32_t chunks_per_row;  // chunk modes: chunk_count(T, skew)
 };
 
 // Real-valued arrays are stored as S (float, __bf16 or _Float16: the kernels'
@@ -107,15 +116,28 @@ enum Storage : int { kStoreF32 = 0, kStoreBF16 = 1, kStoreF16 = 2 };
 struct LaunchShape {
     int waves;        // NW: 1, 2, 4 or 8 waves per workgroup
     bool wave_local;  // rows end at wave boundaries (T divides 64*K)
-    bool vec;         // K-wide vector path: T % K == 0 and aligned arrays
+    bool vec;         // K-wide accesses: arrays aligned to K elements
+    bool skew;        // ... and T % K != 0: windows widened to K-aligned starts
+                      // (kVecSkew below; 8 waves, never wave-local)
+    uint32_t quantum;  // skewed path: rows per window a multiple of this (skew_rows)
     bool chunked;     // few long rows: the three chunk-mode launches
 };
 
 // ---------------------------------------------------------------- memory access
 // `p` points at the workgroup's first element; `off` is the lane's first step
-// relative to it and `L` the number of valid steps.  With VEC the caller
-// guarantees K-element alignment of p + off and L % K == 0, so a lane's K
-// steps are either wholly valid or wholly past the end.
+// relative to it and `L` the number of valid steps.  The memory path VEC:
+//   kScalarIO   one access per element (any alignment, any T);
+//   kVecRows    K-wide accesses; T % K == 0 and K-element alignment of p + off,
+//               so a lane's K steps are wholly valid or wholly past the end,
+//               and lie in one row;
+//   kVecSkew    K-wide accesses for any T with K-element aligned arrays: the
+//               window is widened at its start to the K-aligned step before
+//               it (by its skew, < K steps, which are in the array and read
+//               but never written), so a lane's steps may cross a row end,
+//               and its first and last K steps may be partly valid (`lo` ..
+//               `L`): those are written, and past the end read, element by
+//               element.
+enum IoPath : int { kScalarIO = 0, kVecRows = 1, kVecSkew = 2 };
 //
 // Stored values S widen to the scan type E on load (bf16 and fp16 widen
 // exactly to fp32) and narrow on store (to nearest even: v_cvt_pk_bf16_f32 /
@@ -159,14 +181,22 @@ struct FlagWord<4> {
 // non-temporal hint (measured 3-5% faster for streams read once; the chunk
 // modes' aggregate pass, whose inputs the apply pass reads again, keeps
 // them cacheable).
-template <bool VEC, bool LAST = true, typename E, typename S>
+//
+// kVecSkew reads whole aligned K-element blocks: a lane whose first step is
+// below L reads its K steps even where later ones lie past L, up to K - 1
+// elements past the window and, for the array's last window, past the
+// array's end.  Such a block shares its first element's alignment block, so
+// it never crosses a page boundary and cannot fault; the steps past L are
+// invalid and their values are never used (the scan takes them as identity
+// by selection, not arithmetic).  Writes stay inside [lo, L).
+template <int VEC, bool LAST = true, typename E, typename S>
 __device__ __forceinline__ void load_steps(E (&x)[kK], const S *__restrict__ p, uint32_t off,
                                            uint32_t L) {
     static_assert(sizeof(E) == 4 && (sizeof(S) == 4 || sizeof(S) == 2), "32-bit scan values");
     // Element-typed vector: its lanes are read by value (no bit cast of a
     // vector element, which this compiler lowers as a read of element 0).
     typedef typename VecOf<S, kK>::type vec;
-    if constexpr (VEC) {
+    if constexpr (VEC != kScalarIO) {
         vec q = {};
         if (off < L) {
             const vec *src = reinterpret_cast<const vec *>(p + off);
@@ -184,10 +214,10 @@ __device__ __forceinline__ void load_steps(E (&x)[kK], const S *__restrict__ p, 
     }
 }
 
-template <bool VEC, bool LAST = true>
+template <int VEC, bool LAST = true>
 __device__ __forceinline__ void load_flags(bool (&f)[kK], const uint8_t *__restrict__ p,
                                            uint32_t off, uint32_t L) {
-    if constexpr (VEC) {
+    if constexpr (VEC != kScalarIO) {
         typedef typename FlagWord<kK>::type word;
         uint32_t q = 0;
         if (off < L) {
@@ -202,12 +232,18 @@ __device__ __forceinline__ void load_flags(bool (&f)[kK], const uint8_t *__restr
     }
 }
 
-template <bool VEC, typename S, typename E>
+// kVecSkew: a lane whose K steps straddle the window's start (lo) or end
+// writes its steps in [lo, L) element by element.
+template <int VEC, typename S, typename E>
 __device__ __forceinline__ void store_steps(S *__restrict__ p, const E (&x)[kK], uint32_t off,
-                                            uint32_t L) {
+                                            uint32_t L, uint32_t lo = 0) {
     typedef typename VecOf<S, kK>::type vec;
-    if constexpr (VEC) {
-        if (off < L) {
+    if constexpr (VEC != kScalarIO) {
+        if (VEC == kVecSkew && off < L && (off < lo || off + kK > L)) {
+#pragma unroll
+            for (int i = 0; i < kK; ++i)
+                if (off + i >= lo && off + i < L) p[off + i] = narrow<S>(x[i]);
+        } else if (off < L) {
             vec q;
             if constexpr (kK == 1) {
                 q = narrow<S>(x[0]);
@@ -225,11 +261,14 @@ __device__ __forceinline__ void store_steps(S *__restrict__ p, const E (&x)[kK],
 }
 
 // Chunk modes hand two scan values per chunk between launches through the
-// chunk's first output elements, as raw 32-bit words whatever S is (a chunk
-// starts at an even element, so the words are 4-byte aligned, and spans at
-// least 2048 steps).
+// chunk's first output elements, as raw 32-bit words whatever S is: from the
+// chunk's first even element for 2-byte S, so the words are 4-byte aligned.
+// Every chunk but the last in scan order holds both words (it spans
+// thousands of steps); the last receives one (its 1 or 2 elements lie in
+// the chunk: with 2-byte S and an odd start it spans at least 4 steps).
 template <typename E, typename S>
 __device__ __forceinline__ E *chunk_slot(void *out, int64_t base) {
+    if constexpr (sizeof(S) == 2) base += base & 1;
     return reinterpret_cast<E *>(static_cast<S *>(out) + base);
 }
 
@@ -241,22 +280,24 @@ struct Window {
     uint32_t t0;        // row-local index of the first step (0 in full mode)
     uint32_t row_rest;  // steps from the window start to the end of its row
     uint32_t chunk;     // chunk index in scan order (chunk modes)
+    uint32_t skew;      // base % K
 };
 
-// Chunk j of a row in scan order: backward scans count chunks from the row
-// end, so only the earliest chunk can be short; forward scans from the start.
-__host__ __device__ inline void chunk_bounds(uint32_t T, uint32_t j, bool backward, uint32_t &lo,
-                                             uint32_t &hi) {
+// Chunk j (of m) of a row in scan order, `span` steps each but the last:
+// backward scans count chunks from the row end, so the earliest chunk takes
+// the rest of the row; forward scans count from the start.
+__host__ __device__ inline void chunk_bounds(uint32_t T, uint32_t j, uint32_t m, bool backward,
+                                             uint32_t span, uint32_t &lo, uint32_t &hi) {
     if (backward) {
-        hi = T - j * kChunkSteps;
-        lo = hi > kChunkSteps ? hi - kChunkSteps : 0u;
+        hi = T - j * span;
+        lo = j + 1 < m ? hi - span : 0u;
     } else {
-        lo = j * kChunkSteps;
-        hi = T - lo > kChunkSteps ? lo + kChunkSteps : T;
+        lo = j * span;
+        hi = j + 1 < m ? lo + span : T;
     }
 }
 
-template <int MODE, bool BACKWARD>
+template <int MODE, bool BACKWARD, int VEC = kVecRows>
 __device__ __forceinline__ Window window_of(const Geometry &geo, uint32_t g) {
     Window w;
     if constexpr (MODE == kFull) {
@@ -273,7 +314,8 @@ __device__ __forceinline__ Window window_of(const Geometry &geo, uint32_t g) {
         const uint32_t n = g / geo.chunks_per_row;
         const uint32_t j = g - n * geo.chunks_per_row;
         uint32_t lo, hi;
-        chunk_bounds(geo.T, j, BACKWARD, lo, hi);
+        chunk_bounds(geo.T, j, geo.chunks_per_row, BACKWARD, chunk_span(VEC == kVecSkew), lo,
+                     hi);
         w.row0 = n;
         w.base = (int64_t)n * geo.T + lo;
         w.L = hi - lo;
@@ -281,26 +323,33 @@ __device__ __forceinline__ Window window_of(const Geometry &geo, uint32_t g) {
         w.row_rest = geo.T - lo;
         w.chunk = j;
     }
+    w.skew = (uint32_t)w.base & (kK - 1);
     return w;
 }
 
 // Row-local step index t and row offset (relative to row0) of each of the
-// lane's K steps.  VEC: T % K == 0 and off % K == 0, so the K steps lie in
-// one row and only the last can end it (only the first can start it).
+// lane's K steps; `off` counts from the window start, widened by the skew on
+// the kVecSkew path.  kVecRows: T % K == 0 and off % K == 0, so the K steps
+// lie in one row and only the last can end it (only the first can start it).
+// kVecSkew: the steps before the window (in the lane chunk at off = 0) are
+// invalid and take the position of the window's first step.
 // WAVE_LOCAL: T divides the 256-step wave span, so it is a power of two.
-template <int MODE, bool VEC = false, bool WAVE_LOCAL = false>
+template <int MODE, int VEC = kScalarIO, bool WAVE_LOCAL = false>
 __device__ __forceinline__ void step_positions(const Window &w, uint32_t off, uint32_t T,
                                                uint32_t (&t)[kK], uint32_t (&row)[kK]) {
+    const uint32_t sk = VEC == kVecSkew ? w.skew : 0u;
     if constexpr (MODE == kFull) {
+        const uint32_t head = off < sk ? sk - off : 0u;  // steps before the window
+        const uint32_t u = off + head - sk;              // the first valid step
         uint32_t r, s;
         if constexpr (WAVE_LOCAL) {
-            r = off >> __builtin_ctz(T);
-            s = off & (T - 1);
+            r = u >> __builtin_ctz(T);
+            s = u & (T - 1);
         } else {
-            r = off / T;
-            s = off - r * T;
+            r = u / T;
+            s = u - r * T;
         }
-        if constexpr (VEC) {
+        if constexpr (VEC == kVecRows) {
 #pragma unroll
             for (int i = 0; i < kK; ++i) {
                 t[i] = s + i;
@@ -311,16 +360,17 @@ __device__ __forceinline__ void step_positions(const Window &w, uint32_t off, ui
             for (int i = 0; i < kK; ++i) {
                 t[i] = s;
                 row[i] = r;
-                if (++s == T) {
+                if ((uint32_t)i >= head && ++s == T) {
                     s = 0;
                     ++r;
                 }
             }
         }
     } else {
+        // steps before the window wrap around; they are invalid
 #pragma unroll
         for (int i = 0; i < kK; ++i) {
-            t[i] = w.t0 + off + i;
+            t[i] = w.t0 + off + i - sk;
             row[i] = 0;
         }
     }
@@ -474,7 +524,7 @@ __device__ __forceinline__ void adopt_lead(ForwardParams &p, LEAD_ARGS) {
 // Groups g, g + g_stride, ... of the launch run through one workgroup.
 // STATS: also sum out0 and its square over the workgroup's valid steps (in
 // fp64) and store the pair in stats_partials[2 * blockIdx.x ...].
-template <int EST, bool TRUNC, bool VEC, int NW, bool WAVE_LOCAL, int MODE, typename S,
+template <int EST, bool TRUNC, int VEC, int NW, bool WAVE_LOCAL, int MODE, typename S,
           bool STATS = false>
 __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uint32_t g_stride) {
     static_assert(!STATS || MODE != kChunkAggregate, "statistics come from the outputs");
@@ -503,15 +553,18 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
     // exists; testing only at the bottom lets every kernel-argument load go
     // out together instead of after a first round trip for the bound.
     do {
-        const Window win = window_of<MODE, true>(p.geo, g);
-        const int64_t row0 = win.row0, base = win.base;
-        const uint32_t L = win.L;
+        const Window win = window_of<MODE, true, VEC>(p.geo, g);
+        // Memory base and extent of the window: on the kVecSkew path widened
+        // to the K-aligned step at or before its start, steps [sk, L) valid.
+        const uint32_t sk = VEC == kVecSkew ? win.skew : 0u;
+        const int64_t row0 = win.row0, base = win.base - sk;
+        const uint32_t L = win.L + sk;
         const uint32_t ntiles = MODE == kFull ? (L + kTile - 1) / kTile : 1u;
         // A just after the current tile: 0 at a row end (edges live in alpha),
         // or the carry the chunk-carry pass left in the chunk's first slot.
         float carry = 0.f;
         if constexpr (MODE == kChunkApply) {
-            carry = chunk_slot<float, S>(p.out0, base)[0];
+            carry = chunk_slot<float, S>(p.out0, win.base)[0];
             __syncthreads();  // every lane has read the slot before any store
         }
 
@@ -546,9 +599,9 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
             float boot[kK];
 #pragma unroll
             for (int i = 0; i < kK; ++i) {
-                valid[i] = off + i < L;
-                // on the vector path only the lane's last step can end a row
-                edge[i] = (!VEC || i == kK - 1) && t[i] == T - 1;
+                valid[i] = off + i >= sk && off + i < L;
+                // with whole-row lane chunks only the lane's last step can end a row
+                edge[i] = (VEC != kVecRows || i == kK - 1) && t[i] == T - 1;
                 boot[i] = 0.f;
                 if (valid[i] && edge[i] && bootstrap != nullptr)
                     boot[i] = widen<float>(bootstrap[row0 + row[i]]);
@@ -557,7 +610,7 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
             // With WAVE_LOCAL every wave (and so lane 0's chunk and the
             // window) ends at a row end: the halo is never used.
             const bool halo_from_memory =
-                !WAVE_LOCAL && (lane == 0 || off + kK >= L) && off + kK < win.row_rest;
+                !WAVE_LOCAL && (lane == 0 || off + kK >= L) && off + kK < win.row_rest + sk;
             if (halo_from_memory) {
                 const int64_t jh = base + off + kK;
                 if constexpr (EST == kGae || EST == kTdLambda || EST == kVtrace)
@@ -662,7 +715,7 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
                 float ta, tb;
                 block_total<NW>(fa, fb, lds_a, lds_b, ta, tb);
                 if (threadIdx.x == 0 && win.chunk + 1 < p.geo.chunks_per_row) {
-                    float *slot = chunk_slot<float, S>(p.out0, base);
+                    float *slot = chunk_slot<float, S>(p.out0, win.base);
                     slot[0] = ta;
                     slot[1] = tb;
                 }
@@ -693,9 +746,9 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
                         o1[i] = 0.f;
                     }
                 }
-                store_steps<VEC>(out0 + base, o0, off, L);
+                store_steps<VEC>(out0 + base, o0, off, L, sk);
                 if constexpr (EST == kGae || EST == kVtrace) {
-                    if (out1 != nullptr) store_steps<VEC>(out1 + base, o1, off, L);
+                    if (out1 != nullptr) store_steps<VEC>(out1 + base, o1, off, L, sk);
                 }
                 if constexpr (STATS) {
 #pragma unroll
@@ -726,9 +779,10 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
 // and keep their registers.
 #define RLCA_EIGHT_WAVES(NEED) __attribute__((amdgpu_waves_per_eu((NEED) ? 8 : 1)))
 
-template <int EST, bool TRUNC, bool VEC, int NW, bool WAVE_LOCAL, int MODE, typename S,
+template <int EST, bool TRUNC, int VEC, int NW, bool WAVE_LOCAL, int MODE, typename S,
           bool STATS = false>
-__global__ __launch_bounds__(NW * kWave) RLCA_EIGHT_WAVES(NW == 8 && !WAVE_LOCAL && VEC)
+__global__ __launch_bounds__(NW * kWave)
+RLCA_EIGHT_WAVES(NW == 8 && !WAVE_LOCAL && VEC != kScalarIO)
 void backward_scan(LEAD_ARGS, BackwardParams p) {
     adopt_lead<EST>(p, LEAD_NAMES);
     backward_body<EST, TRUNC, VEC, NW, WAVE_LOCAL, MODE, S, STATS>(p, blockIdx.x, gridDim.x);
@@ -742,7 +796,7 @@ void backward_scan(LEAD_ARGS, BackwardParams p) {
 // carry entering at t = 0.
 // S: storage type of x, out (and beta, carry for kForwardAffine); uint32_t
 // for the integer sums.
-template <typename V, int KIND, bool AFTER_DONE, bool VEC, int NW, bool WAVE_LOCAL, int MODE,
+template <typename V, int KIND, bool AFTER_DONE, int VEC, int NW, bool WAVE_LOCAL, int MODE,
           typename S>
 __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint32_t g_stride) {
     static_assert(MODE == kFull || (NW == kChunkWaves && !WAVE_LOCAL), "a chunk is one tile");
@@ -760,13 +814,14 @@ __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint3
     int parity = 0;
 
     do {  // the first group always exists (see backward_body)
-        const Window win = window_of<MODE, false>(p.geo, g);
-        const int64_t row0 = win.row0, base = win.base;
-        const uint32_t L = win.L;
+        const Window win = window_of<MODE, false, VEC>(p.geo, g);
+        const uint32_t sk = VEC == kVecSkew ? win.skew : 0u;  // as in backward_body
+        const int64_t row0 = win.row0, base = win.base - sk;
+        const uint32_t L = win.L + sk;
         const uint32_t ntiles = MODE == kFull ? (L + kTile - 1) / kTile : 1u;
         V carry = V(0);
         if constexpr (MODE == kChunkApply) {
-            carry = chunk_slot<V, S>(p.out, base)[0];
+            carry = chunk_slot<V, S>(p.out, win.base)[0];
             __syncthreads();  // every lane has read the slot before any store
         }
 
@@ -781,21 +836,26 @@ __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint3
             if constexpr (KIND == kForwardAffine) load_steps<VEC, kLast>(bt, betas + base, off, L);
             uint32_t t[kK], row[kK];
             step_positions<MODE, VEC, WAVE_LOCAL>(win, off, T, t, row);
-            bool start[kK];  // t = 0: on the vector path only the lane's first step
+            bool start[kK];  // t = 0: with whole-row lane chunks only the lane's first step
+            bool valid[kK];
 #pragma unroll
-            for (int i = 0; i < kK; ++i) start[i] = (!VEC || i == 0) && t[i] == 0;
+            for (int i = 0; i < kK; ++i) {
+                start[i] = (VEC != kVecRows || i == 0) && t[i] == 0;
+                valid[i] = off + i >= sk && off + i < L;
+            }
             // flag of the step before the lane's chunk (lane 0; with WAVE_LOCAL
             // every wave starts a row, so it is never needed)
             bool first = false;
             if constexpr (KIND == kForwardFlags && AFTER_DONE && !WAVE_LOCAL) {
-                if (lane == 0 && win.t0 + off > 0 && off <= L) first = p.flags[base + off - 1] != 0;
+                if (lane == 0 && win.t0 + off > sk && off <= L)
+                    first = p.flags[base + off - 1] != 0;
             }
             float row_carry[kK];
 #pragma unroll
             for (int i = 0; i < kK; ++i) {
                 row_carry[i] = 0.f;
                 if constexpr (KIND == kForwardAffine) {
-                    if (off + i < L && start[i] && carries != nullptr)
+                    if (valid[i] && start[i] && carries != nullptr)
                         row_carry[i] = widen<float>(carries[row0 + row[i]]);
                 }
             }
@@ -805,7 +865,6 @@ __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint3
             V alpha[kK], beta[kK];
 #pragma unroll
             for (int i = 0; i < kK; ++i) {
-                const bool valid = off + i < L;
                 V a, b;
                 if constexpr (KIND == kForwardFlags) {
                     bool reset = start[i];
@@ -820,8 +879,8 @@ __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint3
                     a = start[i] ? x[i] + bt[i] * row_carry[i] : x[i];
                     b = start[i] ? V(0) : bt[i];
                 }
-                alpha[i] = valid ? a : V(0);
-                beta[i] = valid ? b : V(1);
+                alpha[i] = valid[i] ? a : V(0);
+                beta[i] = valid[i] ? b : V(1);
             }
             V fa = V(0), fb = V(1);
 #pragma unroll
@@ -833,7 +892,7 @@ __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint3
                 V ta, tb;
                 block_total<NW>(fa, fb, lds_a, lds_b, ta, tb);
                 if (threadIdx.x == 0 && win.chunk + 1 < p.geo.chunks_per_row) {
-                    V *slot = chunk_slot<V, S>(p.out, base);
+                    V *slot = chunk_slot<V, S>(p.out, win.base);
                     slot[0] = ta;
                     slot[1] = tb;
                 }
@@ -849,16 +908,17 @@ __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint3
                     A = alpha[i] + beta[i] * A;
                     o[i] = A;
                 }
-                store_steps<VEC>(out + base, o, off, L);
+                store_steps<VEC>(out + base, o, off, L, sk);
             }
         }
         g += g_stride;
     } while (g < p.geo.num_groups);
 }
 
-template <typename V, int KIND, bool AFTER_DONE, bool VEC, int NW, bool WAVE_LOCAL, int MODE,
+template <typename V, int KIND, bool AFTER_DONE, int VEC, int NW, bool WAVE_LOCAL, int MODE,
           typename S>
-__global__ __launch_bounds__(NW * kWave) RLCA_EIGHT_WAVES(NW == 8 && !WAVE_LOCAL && VEC)
+__global__ __launch_bounds__(NW * kWave)
+RLCA_EIGHT_WAVES(NW == 8 && !WAVE_LOCAL && VEC != kScalarIO)
 void forward_scan(LEAD_ARGS, ForwardParams p) {
     adopt_lead(p, LEAD_NAMES);
     forward_body<V, KIND, AFTER_DONE, VEC, NW, WAVE_LOCAL, MODE, S>(p, blockIdx.x, gridDim.x);
@@ -873,7 +933,7 @@ void forward_scan(LEAD_ARGS, ForwardParams p) {
 template <typename V, typename S, int NW>
 __global__ __launch_bounds__(NW * kWave) void chunk_carries(void *slots, int64_t num_envs,
                                                             uint32_t T, uint32_t chunks_per_row,
-                                                            int backward) {
+                                                            uint32_t span, int backward) {
     __shared__ V lds_a[2 * NW], lds_b[2 * NW];
     constexpr uint32_t kLanes = NW * kWave;
     int parity = 0;
@@ -884,7 +944,7 @@ __global__ __launch_bounds__(NW * kWave) void chunk_carries(void *slots, int64_t
         for (uint32_t j0 = 0; j0 < chunks_per_row; j0 += kLanes) {
             const uint32_t j = j0 + threadIdx.x;
             uint32_t lo = 0, hi = 0;
-            if (j < chunks_per_row) chunk_bounds(T, j, backward != 0, lo, hi);
+            if (j < chunks_per_row) chunk_bounds(T, j, chunks_per_row, backward != 0, span, lo, hi);
             V *slot = chunk_slot<V, S>(slots, row + lo);
             V a = V(0), b = V(1);
             if (j + 1 < chunks_per_row) {
@@ -914,8 +974,34 @@ inline uint32_t grid_for(int64_t groups, uint32_t cap = kMaxGrid) {
     return groups < (int64_t)cap ? (uint32_t)groups : cap;
 }
 
-inline Geometry make_geometry(int64_t num_envs, int64_t T, int waves, bool chunked,
-                              uint32_t *grid, uint32_t cap = kMaxGrid) {
+constexpr uint32_t gcd_k(uint32_t x) {
+    uint32_t d = kK;
+    while (x % d != 0) d /= 2;  // K is a power of two
+    return d;
+}
+// Largest skew a window of x steps can have: window g starts at g * x, whose
+// residues mod K are the multiples of gcd(x, K).
+constexpr uint32_t max_skew(uint32_t x) { return kK - gcd_k(x); }
+// Rows per K-aligned window: K / gcd(T, K).
+constexpr uint32_t aligned_rows(uint32_t T) { return kK / gcd_k(T); }
+
+// Rows per window on the skewed path (windows widened to K-aligned starts):
+// quantum 1 packs as many rows into one tile as leave room for the largest
+// skew their windows can have (a row longer than that takes one window of
+// several tiles); quantum q = aligned_rows(T) > 1 gives every window a
+// multiple of q rows, so each starts K-aligned and walks as many tiles as it
+// needs (q rows when they exceed one tile).
+inline uint32_t skew_rows(uint32_t T, uint32_t tile, uint32_t quantum) {
+    if (quantum > 1) return T * quantum <= tile ? quantum * (tile / (T * quantum)) : quantum;
+    uint32_t r = T <= tile ? tile / T : 1u;
+    while (r > 1 && r * T + max_skew(r * T) > tile) --r;
+    return r;
+}
+
+// skew: windows are widened to K-aligned starts (kVecSkew), rows per window
+// as skew_rows(..., quantum) gives.
+inline Geometry make_geometry(int64_t num_envs, int64_t T, int waves, bool chunked, bool skew,
+                              uint32_t quantum, uint32_t *grid, uint32_t cap = kMaxGrid) {
     const uint32_t tile = (uint32_t)waves * kWave * kK;
     Geometry g;
     g.num_envs = num_envs;
@@ -923,10 +1009,12 @@ inline Geometry make_geometry(int64_t num_envs, int64_t T, int waves, bool chunk
     int64_t groups;
     if (chunked) {
         g.rows_per_group = 1;
-        g.chunks_per_row = (uint32_t)((T + kChunkSteps - 1) / kChunkSteps);
+        g.chunks_per_row = chunk_count((uint32_t)T, skew);
         groups = num_envs * g.chunks_per_row;
     } else {
-        g.rows_per_group = (uint32_t)T <= tile ? tile / (uint32_t)T : 1u;
+        g.rows_per_group = skew                 ? skew_rows((uint32_t)T, tile, quantum)
+                           : (uint32_t)T <= tile ? tile / (uint32_t)T
+                                                 : 1u;
         g.chunks_per_row = 1;
         groups = (num_envs + g.rows_per_group - 1) / g.rows_per_group;
     }
@@ -951,11 +1039,11 @@ inline rlca_status launch_kernel(const void *kernel, int waves, uint32_t grid, P
 
 template <typename V, typename S>
 inline rlca_status launch_chunk_carries(void *slots, const Geometry &geo, bool backward,
-                                        hipStream_t stream) {
+                                        bool skew, hipStream_t stream) {
     int64_t n = geo.num_envs;
-    uint32_t T = geo.T, m = geo.chunks_per_row;
+    uint32_t T = geo.T, m = geo.chunks_per_row, span = chunk_span(skew);
     int dir = backward ? 1 : 0;
-    void *args[] = {&slots, &n, &T, &m, &dir};
+    void *args[] = {&slots, &n, &T, &m, &span, &dir};
     const hipError_t e =
         hipLaunchKernel((const void *)chunk_carries<V, S, kChunkWaves>, dim3(grid_for(n)),
                         dim3(kChunkWaves * kWave), args, 0, stream);
@@ -966,22 +1054,25 @@ inline rlca_status launch_chunk_carries(void *slots, const Geometry &geo, bool b
 // apply (the apply grid capped at `apply_cap`).
 template <typename V, typename S, typename P>
 inline rlca_status launch_chunked(const void *aggregate, const void *apply, P &params, Lead &lead,
-                                  void *slots, bool backward, hipStream_t stream,
+                                  void *slots, bool backward, bool skew, hipStream_t stream,
                                   uint32_t apply_cap = kMaxGrid) {
     uint32_t grid;
-    params.geo = make_geometry(params.geo.num_envs, params.geo.T, kChunkWaves, true, &grid);
+    params.geo =
+        make_geometry(params.geo.num_envs, params.geo.T, kChunkWaves, true, skew, 1, &grid);
     const uint32_t apply_grid = grid_for(params.geo.num_groups, apply_cap);
     rlca_status st = launch_kernel(aggregate, kChunkWaves, grid, params, lead, stream);
-    if (st == RLCA_OK) st = launch_chunk_carries<V, S>(slots, params.geo, backward, stream);
+    if (st == RLCA_OK) st = launch_chunk_carries<V, S>(slots, params.geo, backward, skew, stream);
     if (st == RLCA_OK) st = launch_kernel(apply, kChunkWaves, apply_grid, params, lead, stream);
     return st;
 }
 
 template <typename P>
-inline rlca_status launch_full(const void *kernel, int waves, P &params, Lead &lead,
+inline rlca_status launch_full(const void *kernel, const LaunchShape &s, P &params, Lead &lead,
                                hipStream_t stream, uint32_t cap = kMaxGrid) {
     uint32_t grid;
-    params.geo = make_geometry(params.geo.num_envs, params.geo.T, waves, false, &grid, cap);
+    const int waves = s.vec ? s.waves : 4;
+    params.geo = make_geometry(params.geo.num_envs, params.geo.T, waves, false, s.skew,
+                               s.quantum, &grid, cap);
     return launch_kernel(kernel, waves, grid, params, lead, stream);
 }
 
@@ -992,22 +1083,29 @@ inline uint32_t launch_grid(const LaunchShape &s, int64_t num_envs, int64_t T,
                             uint32_t cap = kMaxGrid) {
     uint32_t grid;
     if (s.chunked)
-        make_geometry(num_envs, T, kChunkWaves, true, &grid, cap);
+        make_geometry(num_envs, T, kChunkWaves, true, s.skew, 1, &grid, cap);
     else
-        make_geometry(num_envs, T, s.vec ? s.waves : 4, false, &grid, cap);
+        make_geometry(num_envs, T, s.vec ? s.waves : 4, false, s.skew, s.quantum, &grid, cap);
     return grid;
 }
 
-// The vector path instantiates every wave count and the wave-local variant;
-// the scalar (unaligned or T % K != 0) path is one general configuration.
+// The memory path of a launch shape.
+inline int io_path(const LaunchShape &s) {
+    return !s.vec ? kScalarIO : s.skew ? kVecSkew : kVecRows;
+}
+
+// The whole-row vector path instantiates every wave count and the wave-local
+// variant; the skewed and the scalar (unaligned) paths one configuration each.
 template <int EST, bool TRUNC, typename S, bool STATS = false>
 const void *backward_kernel(const LaunchShape &s) {
     if (!s.vec)
-        return (const void *)backward_scan<EST, TRUNC, false, 4, false, kFull, S, STATS>;
+        return (const void *)backward_scan<EST, TRUNC, kScalarIO, 4, false, kFull, S, STATS>;
+    if (s.skew)
+        return (const void *)backward_scan<EST, TRUNC, kVecSkew, 8, false, kFull, S, STATS>;
 #define RLCA_PICK(NW)                                                                          \
     return s.wave_local                                                                        \
-               ? (const void *)backward_scan<EST, TRUNC, true, NW, true, kFull, S, STATS>     \
-               : (const void *)backward_scan<EST, TRUNC, true, NW, false, kFull, S, STATS>
+               ? (const void *)backward_scan<EST, TRUNC, kVecRows, NW, true, kFull, S, STATS> \
+               : (const void *)backward_scan<EST, TRUNC, kVecRows, NW, false, kFull, S, STATS>
     switch (s.waves) {
         case 1: RLCA_PICK(1);
         case 2: RLCA_PICK(2);
@@ -1022,14 +1120,17 @@ rlca_status launch_backward_variant(BackwardParams &p, const LaunchShape &s, hip
     Lead lead;
     lead_from<EST>(p, lead);
     const uint32_t cap = STATS ? kStatsMaxGrid : kMaxGrid;
-    if (s.chunked)
-        return launch_chunked<float, S>(
-            (const void *)backward_scan<EST, TRUNC, true, kChunkWaves, false, kChunkAggregate, S>,
-            (const void *)backward_scan<EST, TRUNC, true, kChunkWaves, false, kChunkApply, S,
-                                        STATS>,
-            p, lead, p.out0, true, stream, cap);
-    return launch_full(backward_kernel<EST, TRUNC, S, STATS>(s), s.vec ? s.waves : 4, p, lead,
-                       stream, cap);
+    if (s.chunked) {
+#define RLCA_CHUNKED(IO)                                                                         \
+    return launch_chunked<float, S>(                                                             \
+        (const void *)backward_scan<EST, TRUNC, IO, kChunkWaves, false, kChunkAggregate, S>,     \
+        (const void *)backward_scan<EST, TRUNC, IO, kChunkWaves, false, kChunkApply, S, STATS>,  \
+        p, lead, p.out0, true, s.skew, stream, cap)
+        if (s.skew) RLCA_CHUNKED(kVecSkew);
+        RLCA_CHUNKED(kVecRows);
+#undef RLCA_CHUNKED
+    }
+    return launch_full(backward_kernel<EST, TRUNC, S, STATS>(s), s, p, lead, stream, cap);
 }
 
 template <int EST, typename S>
@@ -1051,11 +1152,12 @@ rlca_status launch_backward(BackwardParams &p, const LaunchShape &s, int storage
 template <typename V, int KIND, bool AFTER_DONE, typename S>
 const void *forward_kernel(const LaunchShape &s) {
     if (!s.vec)
-        return (const void *)forward_scan<V, KIND, AFTER_DONE, false, 4, false, kFull, S>;
-#define RLCA_PICK(NW)                                                                      \
-    return s.wave_local                                                                    \
-               ? (const void *)forward_scan<V, KIND, AFTER_DONE, true, NW, true, kFull, S> \
-               : (const void *)forward_scan<V, KIND, AFTER_DONE, true, NW, false, kFull, S>
+        return (const void *)forward_scan<V, KIND, AFTER_DONE, kScalarIO, 4, false, kFull, S>;
+    if (s.skew) return (const void *)forward_scan<V, KIND, AFTER_DONE, kVecSkew, 8, false, kFull, S>;
+#define RLCA_PICK(NW)                                                                          \
+    return s.wave_local                                                                        \
+               ? (const void *)forward_scan<V, KIND, AFTER_DONE, kVecRows, NW, true, kFull, S> \
+               : (const void *)forward_scan<V, KIND, AFTER_DONE, kVecRows, NW, false, kFull, S>
     switch (s.waves) {
         case 1: RLCA_PICK(1);
         case 2: RLCA_PICK(2);
@@ -1069,15 +1171,19 @@ template <typename V, int KIND, bool AFTER_DONE, typename S>
 rlca_status launch_forward_variant(ForwardParams &p, const LaunchShape &s, hipStream_t stream) {
     Lead lead;
     lead_from(p, lead);
-    if (s.chunked)
-        return launch_chunked<V, S>(
-            (const void *)forward_scan<V, KIND, AFTER_DONE, true, kChunkWaves, false,
-                                       kChunkAggregate, S>,
-            (const void *)forward_scan<V, KIND, AFTER_DONE, true, kChunkWaves, false, kChunkApply,
-                                       S>,
-            p, lead, p.out, false, stream);
-    return launch_full(forward_kernel<V, KIND, AFTER_DONE, S>(s), s.vec ? s.waves : 4, p, lead,
-                       stream);
+    if (s.chunked) {
+#define RLCA_CHUNKED(IO)                                                                    \
+    return launch_chunked<V, S>(                                                            \
+        (const void *)forward_scan<V, KIND, AFTER_DONE, IO, kChunkWaves, false,             \
+                                   kChunkAggregate, S>,                                     \
+        (const void *)forward_scan<V, KIND, AFTER_DONE, IO, kChunkWaves, false, kChunkApply, \
+                                   S>,                                                      \
+        p, lead, p.out, false, s.skew, stream)
+        if (s.skew) RLCA_CHUNKED(kVecSkew);
+        RLCA_CHUNKED(kVecRows);
+#undef RLCA_CHUNKED
+    }
+    return launch_full(forward_kernel<V, KIND, AFTER_DONE, S>(s), s, p, lead, stream);
 }
 
 // The float forward scans in the requested storage type.

@@ -71,16 +71,17 @@ static rlca_status check_aliasing(const Span *outs, int nout, const Span *ins, i
     return RLCA_OK;
 }
 
-// The vector path loads a lane's K steps with one instruction per stream: it
-// needs T % K == 0 and arrays aligned to K elements.
-static bool vec_ok(int64_t T, const void *const *wide, int nw, size_t elem,
-                   const void *const *u8, int nu) {
-    if (T % kK != 0) return false;
+// The vector paths load a lane's K steps with one instruction per stream:
+// they need arrays aligned to K elements.  With T % K == 0 a lane's steps lie
+// in one row (kVecRows); otherwise windows are widened to K-aligned starts
+// (kVecSkew).  Unaligned arrays take the scalar path.
+static int io_of(int64_t T, const void *const *wide, int nw, size_t elem,
+                 const void *const *u8, int nu) {
     for (int i = 0; i < nw; ++i)
-        if (wide[i] != nullptr && ((uintptr_t)wide[i] % (elem * kK)) != 0) return false;
+        if (wide[i] != nullptr && ((uintptr_t)wide[i] % (elem * kK)) != 0) return kScalarIO;
     for (int i = 0; i < nu; ++i)
-        if (u8[i] != nullptr && ((uintptr_t)u8[i] % kK) != 0) return false;
-    return true;
+        if (u8[i] != nullptr && ((uintptr_t)u8[i] % kK) != 0) return kScalarIO;
+    return T % kK == 0 ? kVecRows : kVecSkew;
 }
 
 // Launch shape.  Rows that end at wave boundaries (T divides the 256-step
@@ -97,19 +98,40 @@ static bool vec_ok(int64_t T, const void *const *wide, int nw, size_t elem,
 // sustains 3.4-5 TB/s).
 static constexpr int64_t kChunkedMaxRows = 64;
 static constexpr int64_t kOneWaveMinRows = 4096;
+// Rows of T % K != 0 steps (aligned arrays) are read K-wide from windows
+// widened to K-aligned starts, in 8-wave workgroups for every T (one-wave
+// workgroups walking rows of 257..1023 steps measured 10-50% slower here:
+// a row plus its skew often needs one more 256-step tile).  A row that fits
+// one tile but not together with the largest skew its window can have
+// (T = 2047) would leave most of a second tile idle: with enough rows,
+// windows of K / gcd(T, K) rows, whose starts are all K-aligned, walk their
+// tiles instead (25% faster for eligibility traces over 8192 x 2047, 4%
+// slower for GAE).  Longer rows keep one row per window (aligned windows of
+// 4 rows measured 5-13% slower over 4096 x 4097).
+static constexpr int64_t kSkewAlignedMinWindows = 1024;
 
-static LaunchShape choose_shape(int64_t num_envs, int64_t T, bool vec) {
+static LaunchShape choose_shape(int64_t num_envs, int64_t T, int io) {
     LaunchShape s;
-    s.vec = vec;
-    s.wave_local = vec && T <= kWave * kK && (kWave * kK) % T == 0;
+    s.vec = io != kScalarIO;
+    s.skew = io == kVecSkew;
+    s.wave_local = io == kVecRows && T <= kWave * kK && (kWave * kK) % T == 0;
     s.waves = (T <= kWave * kK || T >= 1024 || num_envs < kOneWaveMinRows) ? 8 : 1;
-    s.chunked = vec && T > 2 * (int64_t)kChunkSteps && num_envs < kChunkedMaxRows;
+    s.chunked = s.vec && T > 2 * (int64_t)kChunkSteps && num_envs < kChunkedMaxRows;
 #ifdef RLCA_FORCE_WAVES
     s.waves = RLCA_FORCE_WAVES;
 #endif
 #ifdef RLCA_FORCE_CHUNKED
-    s.chunked = vec && T > 2 * (int64_t)kChunkSteps && RLCA_FORCE_CHUNKED;
+    s.chunked = s.vec && T > 2 * (int64_t)kChunkSteps && RLCA_FORCE_CHUNKED;
 #endif
+    s.quantum = 1;
+    if (s.skew) {
+        s.waves = 8;
+        const int64_t tile = (int64_t)s.waves * kWave * kK;
+        const int64_t q = aligned_rows((uint32_t)T);
+        if (!s.chunked && T <= tile && T + max_skew((uint32_t)T) > tile &&
+            num_envs / q >= kSkewAlignedMinWindows)
+            s.quantum = (uint32_t)q;
+    }
     return s;
 }
 
@@ -202,7 +224,7 @@ static rlca_status prepare_backward(int est, int storage, const void *rewards,
     p.geo.num_envs = num_envs;
     p.geo.T = (uint32_t)T;
     const void *u8[] = {terminated, truncated};
-    c->shape = choose_shape(num_envs, T, vec_ok(T, real, 9, es, u8, 2));
+    c->shape = choose_shape(num_envs, T, io_of(T, real, 9, es, u8, 2));
     return RLCA_OK;
 }
 
@@ -255,7 +277,7 @@ static rlca_status prepare_forward(int kind, int storage, const void *x, bool is
     p.geo.T = (uint32_t)T;
     const void *wide[] = {x, beta, out};
     const void *u8[] = {flags};
-    c->shape = choose_shape(num_envs, T, vec_ok(T, wide, 3, es, u8, 1));
+    c->shape = choose_shape(num_envs, T, io_of(T, wide, 3, es, u8, 1));
     return RLCA_OK;
 }
 
@@ -283,18 +305,21 @@ static bool grouped_member(const Call &c, GroupedCall *g, int *variant, uint32_t
     // Grouped launches run 8-wave workgroups: calls shaped for 8 waves take
     // one workgroup per group, one-wave calls one wave per group.  Both keep
     // the geometry of their own launch, so results match it bit for bit.
-    if (!c.shape.vec || c.shape.chunked || (c.shape.waves != 1 && c.shape.waves != kGroupWaves))
+    if (!c.shape.vec || c.shape.skew || c.shape.chunked ||
+        (c.shape.waves != 1 && c.shape.waves != kGroupWaves))
         return false;
     const bool wl = c.shape.wave_local, one = c.shape.waves == 1;
     uint32_t grid, groups;
     if (c.backward) {
         g->b = c.bp;
-        g->b.geo = make_geometry(c.bp.geo.num_envs, c.bp.geo.T, c.shape.waves, false, &grid);
+        g->b.geo = make_geometry(c.bp.geo.num_envs, c.bp.geo.T, c.shape.waves, false, false, 1,
+                                 &grid);
         *variant = grouped_backward_variant(c.est, c.bp.truncated != nullptr, wl, one);
         groups = g->b.geo.num_groups;
     } else {
         g->f = c.fp;
-        g->f.geo = make_geometry(c.fp.geo.num_envs, c.fp.geo.T, c.shape.waves, false, &grid);
+        g->f.geo = make_geometry(c.fp.geo.num_envs, c.fp.geo.T, c.shape.waves, false, false, 1,
+                                 &grid);
         *variant = c.forward == kForwardAffine
                        ? grouped_affine_forward_variant(wl, one)
                        : grouped_forward_variant(c.is_int, c.after_done, wl, one);
@@ -477,8 +502,10 @@ using namespace rlca;
 // One (sum, sum of squares) pair per workgroup of the GAE launch, for
 // whichever launch shape the pointers will select.
 static uint32_t gae_stats_pairs(int64_t num_envs, int64_t T) {
-    const uint32_t v = launch_grid(choose_shape(num_envs, T, true), num_envs, T, kStatsMaxGrid);
-    const uint32_t s = launch_grid(choose_shape(num_envs, T, false), num_envs, T, kStatsMaxGrid);
+    const int io = T % kK == 0 ? kVecRows : kVecSkew;
+    const uint32_t v = launch_grid(choose_shape(num_envs, T, io), num_envs, T, kStatsMaxGrid);
+    const uint32_t s =
+        launch_grid(choose_shape(num_envs, T, kScalarIO), num_envs, T, kStatsMaxGrid);
     return v > s ? v : s;
 }
 

@@ -42,9 +42,10 @@ def rollout_args(seed, N, T, trunc=True):
     return host, tuple(dev(x) for x in host)
 
 
-# launch shapes: scalar path (T % 4), wave-local, one-wave, eight-wave, chunked
+# launch shapes: T % 4 != 0 (windows widened to aligned starts), wave-local,
+# one-wave, eight-wave, chunked; the last two also with T % 4 != 0
 SHAPES = [(7, 37), (1, 1), (2, 2), (300, 128), (4096, 128), (33, 512), (4096, 300), (9, 1024),
-          (3, 4100), (2, 20000)]
+          (3, 4100), (2, 20000), (4097, 301), (2, 20001)]
 
 
 @pytest.mark.parametrize("N,T", SHAPES)

@@ -3,8 +3,10 @@
 The bar: fp32 outputs within |gpu - oracle| <= 1e-4 * (1 + |oracle|) element by
 element (the rl-triton summary's §6 validation tolerance, atol = rtol = 1e-4);
 the int32 prefix sum bit-exact.  Inputs are seeded synthetic rollouts; shapes
-span one lane, several tiles, ragged tails, the scalar (unaligned) and vector
-paths, and the five measured workloads at full size.
+span one lane, several tiles, ragged tails, the three memory paths (element
+accesses for unaligned arrays; 4-wide accesses with whole-row lane chunks for
+T % 4 == 0; 4-wide accesses over windows widened to aligned starts for other
+T), and the five measured workloads at full size.
 """
 import numpy as np
 import pytest
@@ -118,9 +120,13 @@ def check_forward(f, device, conv=rl.RESET_ON_START, gamma=0.99, lam=0.9, what="
 
 SHAPES = [(1, 1), (3, 1), (2, 2), (5, 3), (7, 5), (8, 16), (3, 63), (2, 64), (5, 65),
           (4, 127), (9, 128), (3, 129), (2, 255), (2, 257), (1, 1023), (2, 1024), (1, 1025),
-          (3, 2049), (1, 4097), (600, 7), (1030, 4), (257, 12), (5, 3001),
-          # rows of 257..1023 steps take one-wave workgroups from 4096 rows on
-          (4096, 260), (4099, 516), (4096, 1020)]
+          (3, 2049), (1, 4097), (600, 7), (1030, 4), (257, 12), (5, 3001), (700, 3),
+          # windows of one row of T % 4 != 0 steps over two tiles (with skew);
+          # from 4096 rows of 2047 steps, windows of 4 rows over 4 tiles
+          (6, 2046), (5, 2047), (4097, 2047),
+          # rows of 257..1023 steps (T % 4 == 0) take one-wave workgroups from
+          # 4096 rows on; with T % 4 != 0, 8-wave ones
+          (4096, 260), (4099, 516), (4096, 1020), (4097, 301), (4096, 511), (4099, 1023)]
 
 
 @pytest.mark.parametrize("N,T", SHAPES)
@@ -232,10 +238,11 @@ def test_flags_as_bool_and_nonzero_bytes(gpu_device):
     assert torch.equal(a1, a2) and torch.equal(a1, a3)
 
 
-def test_unaligned_views_take_the_scalar_path(gpu_device):
+@pytest.mark.parametrize("T", [132, 131])
+def test_unaligned_views_take_the_scalar_path(T, gpu_device):
     """Inputs that are 4-byte but not 16-byte aligned (views at an odd element
     offset of a larger buffer) give the same results as aligned copies."""
-    N, T = 37, 132
+    N = 37
     d = rollout(9, N, T)
 
     def shifted(x, dtype):
@@ -373,13 +380,16 @@ def test_repeat_calls_are_deterministic(gpu_device):
 
 
 # ------------------------------------------------- few long rows: chunked path
-# Fewer than 64 rows of more than 4096 steps (T % 4 == 0, aligned arrays) are
-# split into 2048-step chunks that run in parallel: aggregate, chunk carries,
-# apply.  Shapes cover an exact multiple of the chunk, a short last chunk in
-# scan order, and single rows.
+# Fewer than 64 rows of more than 4096 steps (aligned arrays) are split into
+# chunks that run in parallel: aggregate, chunk carries, apply.  Chunks span
+# 2048 steps for T % 4 == 0, 2040 otherwise (the last in scan order 4 to 2043).
+# Shapes cover an exact multiple of the chunk, a short last chunk in scan
+# order, a last chunk longer than the others, and single rows.
 
 LONG_SHAPES = [(3, 4100), (2, 6144), (5, 10000), (1, 65536), (4, 20480), (63, 4104),
-               (64, 4104)]
+               (64, 4104),
+               # T % 4 != 0: chunk starts at any offset from an aligned step
+               (3, 4101), (2, 6123), (2, 6125), (5, 10001), (1, 65537), (63, 4103)]
 
 
 @pytest.mark.parametrize("N,T", LONG_SHAPES)
