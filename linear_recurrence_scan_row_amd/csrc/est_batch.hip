@@ -12,12 +12,13 @@ static_assert(kMaxGroupedCalls == 14, "the head is 14 preloaded kernel-argument 
         uint32_t h7, uint32_t h8, uint32_t h9, uint32_t h10, uint32_t h11, uint32_t h12,       \
         uint32_t h13
 
-// Grouped kernels come in four classes (GroupClass): 8-wave calls whose rows
+// Grouped kernels come in five classes (GroupClass): 8-wave calls whose rows
 // end at wave boundaries (wave-local), light or importance-weighted; other
-// 8-wave calls; one-wave calls.  Each class kernel holds only its own
-// bodies, so the light wave-local bodies of short-row batches are not held
-// to the register count of the heavier ones.  S: storage type of every member's real-valued arrays
-// (float also carries the int32 prefix sums).
+// 8-wave calls; one-wave calls; calls over skewed windows.  Each class
+// kernel holds only its own bodies, so the light wave-local bodies of
+// short-row batches are not held to the register count of the heavier ones.
+// S: storage type of every member's real-valued arrays (float also carries
+// the int32 prefix sums).
 template <typename S, int CLASS>
 __global__ __launch_bounds__(kGroupWaves * kWave)
 __attribute__((amdgpu_waves_per_eu(kGroupClassWaves[CLASS], 8)))
@@ -43,7 +44,43 @@ void grouped_scan(RLCA_HEAD_ARGS, GroupedArgs a) {
     const uint32_t g1 = wg * kGroupWaves + wave;
     constexpr bool kWide = sizeof(S) == 4;  // int32 sums only travel in the 4-byte group
 
-    if constexpr (CLASS == kGroupOneWave) {
+    if constexpr (CLASS == kGroupSkew) {
+        switch (variant) {
+#define RLCA_BS(EST, TR)                                                                     \
+    case grouped_skew_backward_variant(EST, TR): {                                           \
+        BackwardParams p = a.calls[c].b;                                                     \
+        backward_body<EST, TR, kVecSkew, kGroupWaves, false, kFull, S>(p, wg,                \
+                                                                      p.geo.num_groups);     \
+        return;                                                                              \
+    }
+#define RLCA_FS(V, ST, INT, AD)                                                              \
+    case grouped_skew_forward_variant(INT, AD): {                                            \
+        if constexpr (!INT || kWide) {                                                       \
+            ForwardParams p = a.calls[c].f;                                                  \
+            forward_body<V, kForwardFlags, AD, kVecSkew, kGroupWaves, false, kFull, ST>(     \
+                p, wg, p.geo.num_groups);                                                    \
+        }                                                                                    \
+        return;                                                                              \
+    }
+            RLCA_BS(kGae, false) RLCA_BS(kGae, true)
+            RLCA_BS(kTdLambda, false) RLCA_BS(kTdLambda, true)
+            RLCA_BS(kDiscounted, false) RLCA_BS(kDiscounted, true)
+            RLCA_BS(kVtrace, false) RLCA_BS(kVtrace, true)
+            RLCA_BS(kRetrace, false) RLCA_BS(kRetrace, true)
+            RLCA_BS(kAffineBackward, false)
+            RLCA_FS(float, S, false, false) RLCA_FS(float, S, false, true)
+            RLCA_FS(uint32_t, uint32_t, true, false) RLCA_FS(uint32_t, uint32_t, true, true)
+#undef RLCA_FS
+#undef RLCA_BS
+            case kGroupedSkewAffineForward: {
+                ForwardParams p = a.calls[c].f;
+                forward_body<float, kForwardAffine, false, kVecSkew, kGroupWaves, false, kFull, S>(
+                    p, wg, p.geo.num_groups);
+                return;
+            }
+            default: return;
+        }
+    } else if constexpr (CLASS == kGroupOneWave) {
         switch (variant) {
 #define RLCA_B1(EST, TR)                                                                     \
     case grouped_backward_variant(EST, TR, false, true): {                                  \
@@ -136,6 +173,7 @@ static const void *grouped_kernel(int cls) {
         case kGroupWaveLocalWeighted:
             return (const void *)grouped_scan<S, kGroupWaveLocalWeighted>;
         case kGroupWaves8: return (const void *)grouped_scan<S, kGroupWaves8>;
+        case kGroupSkew: return (const void *)grouped_scan<S, kGroupSkew>;
         default: return (const void *)grouped_scan<S, kGroupOneWave>;
     }
 }

@@ -1233,7 +1233,8 @@ struct GroupedLaunch {
 // truncation x wave-local), flag-driven forward scans 24..31 (int32 x
 // after-done x wave-local), forward affine scan 32..33.  One-wave bodies
 // (never wave-local): backward 34..44 (estimator x truncation), forward
-// 46..49 (int32 x after-done), forward affine 50.
+// 46..49 (int32 x after-done), forward affine 50.  Skewed-window bodies
+// (T % K != 0; 8 waves): backward 64..74, forward 80..83, forward affine 84.
 constexpr int grouped_backward_variant(int est, bool trunc, bool wave_local, bool one_wave) {
     return one_wave ? 34 + est * 2 + (trunc ? 1 : 0)
                     : est * 4 + (trunc ? 2 : 0) + (wave_local ? 1 : 0);
@@ -1246,26 +1247,35 @@ constexpr int grouped_forward_variant(bool is_int, bool after_done, bool wave_lo
 constexpr int grouped_affine_forward_variant(bool wave_local, bool one_wave) {
     return one_wave ? 50 : 32 + (wave_local ? 1 : 0);
 }
+constexpr int grouped_skew_backward_variant(int est, bool trunc) {
+    return 64 + est * 2 + (trunc ? 1 : 0);
+}
+constexpr int grouped_skew_forward_variant(bool is_int, bool after_done) {
+    return 80 + (is_int ? 2 : 0) + (after_done ? 1 : 0);
+}
+constexpr int kGroupedSkewAffineForward = 84;
 
 // Classes of grouped launches, one kernel each (see est_batch.hip): 8-wave
 // calls whose rows end at wave boundaries (wave-local), split into the light
 // bodies and the importance-weighted ones (V-Trace, Retrace: more registers);
-// other 8-wave calls; one-wave calls.
+// other 8-wave calls; one-wave calls; calls over skewed windows (T % K != 0).
 enum GroupClass : int {
     kGroupWaveLocal = 0,
     kGroupWaveLocalWeighted = 1,
     kGroupWaves8 = 2,
     kGroupOneWave = 3,
+    kGroupSkew = 4,
 };
-constexpr int kGroupClasses = 4;
+constexpr int kGroupClasses = 5;
 // Minimum waves per SIMD each class kernel is compiled for (one-shot shapes
 // need all eight slots; the light wave-local bodies fit eight by themselves).
 #ifndef RLCA_GROUP_CLASS_WAVES
-#define RLCA_GROUP_CLASS_WAVES {1, 8, 8, 8}
+#define RLCA_GROUP_CLASS_WAVES {1, 8, 8, 8, 8}
 #endif
 constexpr int kGroupClassWaves[kGroupClasses] = RLCA_GROUP_CLASS_WAVES;
 
 inline int group_class(const LaunchShape &s, bool weighted) {
+    if (s.skew) return kGroupSkew;
     if (s.waves == 1) return kGroupOneWave;
     if (!s.wave_local) return kGroupWaves8;
     return weighted ? kGroupWaveLocalWeighted : kGroupWaveLocal;

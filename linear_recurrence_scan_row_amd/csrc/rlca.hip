@@ -305,24 +305,30 @@ static bool grouped_member(const Call &c, GroupedCall *g, int *variant, uint32_t
     // Grouped launches run 8-wave workgroups: calls shaped for 8 waves take
     // one workgroup per group, one-wave calls one wave per group.  Both keep
     // the geometry of their own launch, so results match it bit for bit.
-    if (!c.shape.vec || c.shape.skew || c.shape.chunked ||
-        (c.shape.waves != 1 && c.shape.waves != kGroupWaves))
+    if (!c.shape.vec || c.shape.chunked || (c.shape.waves != 1 && c.shape.waves != kGroupWaves))
         return false;
-    const bool wl = c.shape.wave_local, one = c.shape.waves == 1;
+    const bool wl = c.shape.wave_local, one = c.shape.waves == 1, skew = c.shape.skew;
     uint32_t grid, groups;
     if (c.backward) {
         g->b = c.bp;
-        g->b.geo = make_geometry(c.bp.geo.num_envs, c.bp.geo.T, c.shape.waves, false, false, 1,
-                                 &grid);
-        *variant = grouped_backward_variant(c.est, c.bp.truncated != nullptr, wl, one);
+        g->b.geo = make_geometry(c.bp.geo.num_envs, c.bp.geo.T, c.shape.waves, false, skew,
+                                 c.shape.quantum, &grid);
+        const bool trunc = c.bp.truncated != nullptr;
+        *variant = skew ? grouped_skew_backward_variant(c.est, trunc)
+                        : grouped_backward_variant(c.est, trunc, wl, one);
         groups = g->b.geo.num_groups;
     } else {
         g->f = c.fp;
-        g->f.geo = make_geometry(c.fp.geo.num_envs, c.fp.geo.T, c.shape.waves, false, false, 1,
-                                 &grid);
-        *variant = c.forward == kForwardAffine
-                       ? grouped_affine_forward_variant(wl, one)
-                       : grouped_forward_variant(c.is_int, c.after_done, wl, one);
+        g->f.geo = make_geometry(c.fp.geo.num_envs, c.fp.geo.T, c.shape.waves, false, skew,
+                                 c.shape.quantum, &grid);
+        if (skew)
+            *variant = c.forward == kForwardAffine
+                           ? kGroupedSkewAffineForward
+                           : grouped_skew_forward_variant(c.is_int, c.after_done);
+        else
+            *variant = c.forward == kForwardAffine
+                           ? grouped_affine_forward_variant(wl, one)
+                           : grouped_forward_variant(c.is_int, c.after_done, wl, one);
         groups = g->f.geo.num_groups;
     }
     *workgroups = one ? (groups + kGroupWaves - 1) / kGroupWaves : groups;
@@ -714,7 +720,7 @@ rlca_status rlca_run_batch(const rlca_call *calls, int count, hipStream_t stream
         }
     }
     // Vector-path, single-launch calls share grouped launches; the rest
-    // (unaligned or chunked) are enqueued one by one.  Members of one grouped
+    // (unaligned, chunked or beyond the grid cap) are enqueued one by one.  Members of one grouped
     // launch share a shape class (one kernel per class) and the storage type
     // of their real-valued arrays (int32 sums join the 4-byte group).  A
     // grouped launch that would hold one call runs that call's own kernel.

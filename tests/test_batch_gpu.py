@@ -1,14 +1,14 @@
 """rlca_run_batch on the GPU: several calls validated together and enqueued as
-grouped launches (calls on the whole-row vector path) plus single launches
-(unaligned, T % 4 != 0 or chunked calls).
+grouped launches (calls on the vector paths) plus single launches (unaligned
+or chunked calls).
 
 Every member of a batch is checked against the fp64 oracle to the same bar as
 the single-call tests (|gpu - oracle| <= 1e-4 * (1 + |oracle|), int32 exact),
 and against the single-call entry point bit for bit: a grouped launch runs
 each call with the tile geometry of the call's own launch (one group per
 workgroup for 8-wave shapes, one per wave for one-wave shapes), and calls
-that cannot join one (unaligned, T % 4 != 0, chunked, or alone) run their own
-kernel.
+that cannot join one (unaligned, chunked, or alone in its class) run their
+own kernel.
 """
 import numpy as np
 import pytest
@@ -125,15 +125,16 @@ class Member:
 def mixed_members(device):
     """Every op, both flag conventions, both affine directions; wave-local
     (T | 256), eight-wave (T >= 1024, or fewer than 4096 rows) and one-wave
-    (4096 rows and more of 257..1023 steps) shapes; T % 4 != 0 (own launch),
-    a chunked few-long-rows call, and an empty one."""
+    (4096 rows and more of 257..1023 steps) shapes; T % 4 != 0 (skewed
+    windows, their own class, with 4-row windows of 2047-step rows), a
+    chunked few-long-rows call, and an empty one."""
     return [
         Member("gae", 1, 300, 128, device),
         Member("gae", 2, 17, 48, device, trunc=False, boot=False),
         Member("td_lambda", 3, 200, 128, device),
         Member("td_lambda", 4, 9, 1024, device, trunc=False),
         Member("discounted", 5, 33, 512, device),
-        Member("discounted", 6, 5, 37, device),                  # T % 4 != 0: own launch
+        Member("discounted", 6, 5, 37, device),                  # T % 4 != 0: skewed windows
         Member("vtrace", 7, 70, 256, device),
         Member("vtrace", 8, 6, 700, device, boot=False),
         Member("retrace", 9, 40, 1024, device),
@@ -151,6 +152,15 @@ def mixed_members(device):
         Member("vtrace", 19, 4100, 516, device),
         Member("traces", 20, 4097, 300, device, conv=rl.RESET_AFTER_DONE),
         Member("affine", 21, 4099, 260, device, direction=rl.BACKWARD),
+        # more skewed-window members (T % 4 != 0), one grouped class
+        Member("gae", 22, 300, 127, device),
+        Member("vtrace", 23, 70, 255, device, trunc=False),
+        Member("retrace", 24, 40, 1023, device),
+        Member("traces", 25, 150, 511, device, conv=rl.RESET_AFTER_DONE),
+        Member("prefix", 26, 12, 2046, device, int_input=True),
+        Member("affine", 27, 11, 521, device, direction=rl.FORWARD),
+        Member("affine", 28, 80, 253, device, direction=rl.BACKWARD, boot=False),
+        Member("traces", 29, 4100, 2047, device),                # 4-row windows
     ]
 
 
