@@ -1153,7 +1153,8 @@ template <typename V, int KIND, bool AFTER_DONE, typename S>
 const void *forward_kernel(const LaunchShape &s) {
     if (!s.vec)
         return (const void *)forward_scan<V, KIND, AFTER_DONE, kScalarIO, 4, false, kFull, S>;
-    if (s.skew) return (const void *)forward_scan<V, KIND, AFTER_DONE, kVecSkew, 8, false, kFull, S>;
+    if (s.skew)
+        return (const void *)forward_scan<V, KIND, AFTER_DONE, kVecSkew, 8, false, kFull, S>;
 #define RLCA_PICK(NW)                                                                          \
     return s.wave_local                                                                        \
                ? (const void *)forward_scan<V, KIND, AFTER_DONE, kVecRows, NW, true, kFull, S> \
