@@ -74,8 +74,9 @@ __device__ __forceinline__ float ppo_term(float a, float lp_new, float lp_old, f
 }
 
 // NORM: A_hat = (A - mean) * 1/(std + norm_eps) from stats; VEC: four steps
-// per load (M % 4 == 0, 16-byte aligned arrays).  Grid-stride over the steps;
-// each workgroup leaves the sum of its surrogate terms in partials.
+// per load (16-byte aligned arrays), the last M % 4 steps one per lane of
+// workgroup 0.  Grid-stride over the steps; each workgroup leaves the sum of
+// its surrogate terms in partials.
 template <bool NORM, bool GRAD, bool VEC>
 __global__ __launch_bounds__(kPpoThreads) void ppo_clip_loss(
     const float *__restrict__ adv, const double *__restrict__ stats,
@@ -107,6 +108,13 @@ __global__ __launch_bounds__(kPpoThreads) void ppo_clip_loss(
                 g[k] = gk;
             }
             if constexpr (GRAD) __builtin_nontemporal_store(g, reinterpret_cast<f4 *>(grad) + i);
+        }
+        const int64_t i = 4 * n4 + threadIdx.x;
+        if (blockIdx.x == 0 && i < M) {
+            const float ah = NORM ? (adv[i] - mean) * scale : adv[i];
+            float g;
+            acc += (double)ppo_term(ah, logp_new[i], logp_old[i], lo, hi, neg_inv_m, g);
+            if constexpr (GRAD) grad[i] = g;
         }
     } else {
         for (int64_t i = (int64_t)blockIdx.x * kPpoThreads + threadIdx.x; i < M; i += stride) {

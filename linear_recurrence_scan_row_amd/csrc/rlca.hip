@@ -689,8 +689,8 @@ rlca_status rlca_ppo_clip_loss(const float *advantages, const double *stats,
     const Span outs[] = {{grad_logp_new, fb}, {loss, 8}, {workspace, 8 * (size_t)grid}};
     st = check_extra_aliasing(c, outs, 3);
     if (st != RLCA_OK) return st;
-    const bool vec = n % 4 == 0 && aligned(advantages, 16) && aligned(logp_new, 16) &&
-                     aligned(logp_old, 16) && aligned(grad_logp_new, 16);
+    const bool vec = aligned(advantages, 16) && aligned(logp_new, 16) && aligned(logp_old, 16) &&
+                     aligned(grad_logp_new, 16);
     return launch_ppo_clip_loss(advantages, stats, logp_new, logp_old, clip_eps, norm_eps, n,
                                 vec, grad_logp_new, static_cast<double *>(workspace), loss,
                                 stream);
