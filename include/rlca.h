@@ -24,16 +24,21 @@
  *          alive until the stream has passed the call.
  * Layout:  per-step arrays are dense row-major [num_envs, T]; element (n, t)
  *          is at n*T + t.  `bootstrap` is [num_envs].  Real-valued and int32
- *          data must be aligned to its element size; alignment of every
- *          per-step array to four elements (16 bytes for fp32, 8 for bf16 /
- *          fp16, 4 for flags) selects the vectorised paths (with T % 4 == 0
- *          the fastest) but is not required.  Flags are one byte per step,
- *          any nonzero byte meaning "set" (torch.bool and uint8 both work).
- *          On the vectorised paths with T % 4 != 0 the library reads whole
- *          aligned four-element blocks, so it may read (never write) up to
- *          three elements past the end of a per-step input, inside the
- *          aligned block that holds its last element; such reads cannot
- *          fault and their values are not used.
+ *          data must be aligned to its element size.  Flags are one byte per
+ *          step, any nonzero byte meaning "set" (torch.bool and uint8 both
+ *          work).  Speed, not results, depends on where arrays start: call
+ *          an array's phase its start address's element index mod 4 from a
+ *          four-element boundary (16 bytes for fp32, 8 for bf16 / fp16, 4
+ *          for flags).  Every per-step array at phase 0 with T % 4 == 0 is
+ *          the fastest case; per-step inputs all at one phase take the
+ *          vectorised path too (outputs at another phase are then written
+ *          element by element); inputs at different phases are read element
+ *          by element.  On the vectorised path, except in the fastest case,
+ *          the library reads whole aligned four-element blocks: it may read
+ *          (never write) up to three elements before the start or past the
+ *          end of a per-step input, inside the aligned block that holds its
+ *          first or last element.  Such reads cannot fault and their values
+ *          are not used.
  * Episode boundaries (summary §3.2 Episode-boundary semantics):
  *          terminated[t]  the episode ends after step t in a terminal state:
  *                         successor value 0, no credit flows back past t.

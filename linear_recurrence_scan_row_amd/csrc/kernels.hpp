@@ -77,6 +77,11 @@ struct Geometry {
     uint32_t rows_per_group;  // full mode: whole rows owned by one workgroup iteration
     uint32_t num_groups;
     uint32_t chunks_per_row;  // chunk modes: chunk_count(T, skew)
+    // kVecSkew: phase of the per-step inputs (the element index mod K at which
+    // their K-aligned blocks start, the same for every input), phase of out0,
+    // and whether the outputs' phase differs from the inputs' (then they are
+    // written element by element).  0, 0, 0 on the other paths.
+    uint32_t phase, out0_phase, scatter;
 };
 
 // Real-valued arrays are stored as S (float, __bf16 or _Float16: the kernels'
@@ -116,10 +121,13 @@ enum Storage : int { kStoreF32 = 0, kStoreBF16 = 1, kStoreF16 = 2 };
 struct LaunchShape {
     int waves;        // NW: 1, 2, 4 or 8 waves per workgroup
     bool wave_local;  // rows end at wave boundaries (T divides 64*K)
-    bool vec;         // K-wide accesses: arrays aligned to K elements
-    bool skew;        // ... and T % K != 0: windows widened to K-aligned starts
+    bool vec;         // K-wide accesses: per-step inputs at one phase
+    bool skew;        // ... other than T % K == 0 with every per-step array
+                      // K-aligned: windows widened to K-aligned starts
                       // (kVecSkew below; 8 waves, never wave-local)
     uint32_t quantum;  // skewed path: rows per window a multiple of this (skew_rows)
+    uint32_t phase, out0_phase;  // skewed path: as in Geometry
+    bool scatter;                // skewed path: as in Geometry
     bool chunked;     // few long rows: the three chunk-mode launches
 };
 
@@ -130,13 +138,14 @@ struct LaunchShape {
 //   kVecRows    K-wide accesses; T % K == 0 and K-element alignment of p + off,
 //               so a lane's K steps are wholly valid or wholly past the end,
 //               and lie in one row;
-//   kVecSkew    K-wide accesses for any T with K-element aligned arrays: the
-//               window is widened at its start to the K-aligned step before
-//               it (by its skew, < K steps, which are in the array and read
-//               but never written), so a lane's steps may cross a row end,
-//               and its first and last K steps may be partly valid (`lo` ..
-//               `L`): those are written, and past the end read, element by
-//               element.
+//   kVecSkew    K-wide reads for any T with every per-step input at one
+//               phase (its K-aligned blocks start at the same element index
+//               mod K): the window is widened at its start to the block
+//               boundary before it (by its skew, < K steps, read but never
+//               written), so a lane's steps may cross a row end, and its
+//               first and last K steps may be partly valid (`lo` .. `L`):
+//               those are written element by element, and so is every step
+//               when the outputs are at another phase.
 enum IoPath : int { kScalarIO = 0, kVecRows = 1, kVecSkew = 2 };
 //
 // Stored values S widen to the scan type E on load (bf16 and fp16 widen
@@ -185,10 +194,12 @@ struct FlagWord<4> {
 // kVecSkew reads whole aligned K-element blocks: a lane whose first step is
 // below L reads its K steps even where later ones lie past L, up to K - 1
 // elements past the window and, for the array's last window, past the
-// array's end.  Such a block shares its first element's alignment block, so
-// it never crosses a page boundary and cannot fault; the steps past L are
-// invalid and their values are never used (the scan takes them as identity
-// by selection, not arithmetic).  Writes stay inside [lo, L).
+// array's end (and, for inputs at a nonzero phase, up to K - 1 elements
+// before the array's start).  Such a block holds an element of the array
+// and is aligned, so it never crosses a page boundary and cannot fault; the
+// steps outside the window are invalid and their values are never used (the
+// scan takes them as identity by selection, not arithmetic).  Writes stay
+// inside [lo, L).
 template <int VEC, bool LAST = true, typename E, typename S>
 __device__ __forceinline__ void load_steps(E (&x)[kK], const S *__restrict__ p, uint32_t off,
                                            uint32_t L) {
@@ -232,14 +243,15 @@ __device__ __forceinline__ void load_flags(bool (&f)[kK], const uint8_t *__restr
     }
 }
 
-// kVecSkew: a lane whose K steps straddle the window's start (lo) or end
+// kVecSkew: a lane whose K steps straddle the window's start (lo) or end,
+// and every lane when `scatter` (outputs at another phase than the inputs),
 // writes its steps in [lo, L) element by element.
 template <int VEC, typename S, typename E>
 __device__ __forceinline__ void store_steps(S *__restrict__ p, const E (&x)[kK], uint32_t off,
-                                            uint32_t L, uint32_t lo = 0) {
+                                            uint32_t L, uint32_t lo = 0, bool scatter = false) {
     typedef typename VecOf<S, kK>::type vec;
     if constexpr (VEC != kScalarIO) {
-        if (VEC == kVecSkew && off < L && (off < lo || off + kK > L)) {
+        if (VEC == kVecSkew && off < L && (scatter || off < lo || off + kK > L)) {
 #pragma unroll
             for (int i = 0; i < kK; ++i)
                 if (off + i >= lo && off + i < L) p[off + i] = narrow<S>(x[i]);
@@ -261,14 +273,15 @@ __device__ __forceinline__ void store_steps(S *__restrict__ p, const E (&x)[kK],
 }
 
 // Chunk modes hand two scan values per chunk between launches through the
-// chunk's first output elements, as raw 32-bit words whatever S is: from the
-// chunk's first even element for 2-byte S, so the words are 4-byte aligned.
-// Every chunk but the last in scan order holds both words (it spans
-// thousands of steps); the last receives one (its 1 or 2 elements lie in
-// the chunk: with 2-byte S and an odd start it spans at least 4 steps).
+// chunk's first output elements, as raw 32-bit words whatever S is: for
+// 2-byte S from the chunk's first element at a 4-byte aligned address (the
+// output's phase, out_phase, is its start's element index mod K).  Every
+// chunk but the last in scan order holds both words (it spans thousands of
+// steps); the last receives one (its 1 or 2 elements lie in the chunk: with
+// 2-byte S and an odd start it spans at least 4 steps).
 template <typename E, typename S>
-__device__ __forceinline__ E *chunk_slot(void *out, int64_t base) {
-    if constexpr (sizeof(S) == 2) base += base & 1;
+__device__ __forceinline__ E *chunk_slot(void *out, int64_t base, uint32_t out_phase) {
+    if constexpr (sizeof(S) == 2) base += (base + out_phase) & 1;
     return reinterpret_cast<E *>(static_cast<S *>(out) + base);
 }
 
@@ -280,7 +293,7 @@ struct Window {
     uint32_t t0;        // row-local index of the first step (0 in full mode)
     uint32_t row_rest;  // steps from the window start to the end of its row
     uint32_t chunk;     // chunk index in scan order (chunk modes)
-    uint32_t skew;      // base % K
+    uint32_t skew;      // (base + phase) % K: steps from the block boundary to base
 };
 
 // Chunk j (of m) of a row in scan order, `span` steps each but the last:
@@ -323,7 +336,7 @@ __device__ __forceinline__ Window window_of(const Geometry &geo, uint32_t g) {
         w.row_rest = geo.T - lo;
         w.chunk = j;
     }
-    w.skew = (uint32_t)w.base & (kK - 1);
+    w.skew = ((uint32_t)w.base + geo.phase) & (kK - 1);
     return w;
 }
 
@@ -564,7 +577,7 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
         // or the carry the chunk-carry pass left in the chunk's first slot.
         float carry = 0.f;
         if constexpr (MODE == kChunkApply) {
-            carry = chunk_slot<float, S>(p.out0, win.base)[0];
+            carry = chunk_slot<float, S>(p.out0, win.base, p.geo.out0_phase)[0];
             __syncthreads();  // every lane has read the slot before any store
         }
 
@@ -715,7 +728,7 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
                 float ta, tb;
                 block_total<NW>(fa, fb, lds_a, lds_b, ta, tb);
                 if (threadIdx.x == 0 && win.chunk + 1 < p.geo.chunks_per_row) {
-                    float *slot = chunk_slot<float, S>(p.out0, win.base);
+                    float *slot = chunk_slot<float, S>(p.out0, win.base, p.geo.out0_phase);
                     slot[0] = ta;
                     slot[1] = tb;
                 }
@@ -746,9 +759,10 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
                         o1[i] = 0.f;
                     }
                 }
-                store_steps<VEC>(out0 + base, o0, off, L, sk);
+                const bool scatter = p.geo.scatter != 0;
+                store_steps<VEC>(out0 + base, o0, off, L, sk, scatter);
                 if constexpr (EST == kGae || EST == kVtrace) {
-                    if (out1 != nullptr) store_steps<VEC>(out1 + base, o1, off, L, sk);
+                    if (out1 != nullptr) store_steps<VEC>(out1 + base, o1, off, L, sk, scatter);
                 }
                 if constexpr (STATS) {
 #pragma unroll
@@ -821,7 +835,7 @@ __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint3
         const uint32_t ntiles = MODE == kFull ? (L + kTile - 1) / kTile : 1u;
         V carry = V(0);
         if constexpr (MODE == kChunkApply) {
-            carry = chunk_slot<V, S>(p.out, win.base)[0];
+            carry = chunk_slot<V, S>(p.out, win.base, p.geo.out0_phase)[0];
             __syncthreads();  // every lane has read the slot before any store
         }
 
@@ -892,7 +906,7 @@ __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint3
                 V ta, tb;
                 block_total<NW>(fa, fb, lds_a, lds_b, ta, tb);
                 if (threadIdx.x == 0 && win.chunk + 1 < p.geo.chunks_per_row) {
-                    V *slot = chunk_slot<V, S>(p.out, win.base);
+                    V *slot = chunk_slot<V, S>(p.out, win.base, p.geo.out0_phase);
                     slot[0] = ta;
                     slot[1] = tb;
                 }
@@ -908,7 +922,7 @@ __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint3
                     A = alpha[i] + beta[i] * A;
                     o[i] = A;
                 }
-                store_steps<VEC>(out + base, o, off, L, sk);
+                store_steps<VEC>(out + base, o, off, L, sk, p.geo.scatter != 0);
             }
         }
         g += g_stride;
@@ -933,7 +947,8 @@ void forward_scan(LEAD_ARGS, ForwardParams p) {
 template <typename V, typename S, int NW>
 __global__ __launch_bounds__(NW * kWave) void chunk_carries(void *slots, int64_t num_envs,
                                                             uint32_t T, uint32_t chunks_per_row,
-                                                            uint32_t span, int backward) {
+                                                            uint32_t span, uint32_t out_phase,
+                                                            int backward) {
     __shared__ V lds_a[2 * NW], lds_b[2 * NW];
     constexpr uint32_t kLanes = NW * kWave;
     int parity = 0;
@@ -945,7 +960,7 @@ __global__ __launch_bounds__(NW * kWave) void chunk_carries(void *slots, int64_t
             const uint32_t j = j0 + threadIdx.x;
             uint32_t lo = 0, hi = 0;
             if (j < chunks_per_row) chunk_bounds(T, j, chunks_per_row, backward != 0, span, lo, hi);
-            V *slot = chunk_slot<V, S>(slots, row + lo);
+            V *slot = chunk_slot<V, S>(slots, row + lo, out_phase);
             V a = V(0), b = V(1);
             if (j + 1 < chunks_per_row) {
                 a = slot[0];
@@ -979,40 +994,47 @@ constexpr uint32_t gcd_k(uint32_t x) {
     while (x % d != 0) d /= 2;  // K is a power of two
     return d;
 }
-// Largest skew a window of x steps can have: window g starts at g * x, whose
-// residues mod K are the multiples of gcd(x, K).
-constexpr uint32_t max_skew(uint32_t x) { return kK - gcd_k(x); }
-// Rows per K-aligned window: K / gcd(T, K).
+// Largest skew a window of x steps can have: window g starts at g * x, and
+// its skew is (g * x + phase) mod K, which runs over the residues of phase
+// mod gcd(x, K).
+constexpr uint32_t max_skew(uint32_t x, uint32_t phase) {
+    return kK - gcd_k(x) + phase % gcd_k(x);
+}
+// Rows per window whose starts are all at one skew: K / gcd(T, K).
 constexpr uint32_t aligned_rows(uint32_t T) { return kK / gcd_k(T); }
 
 // Rows per window on the skewed path (windows widened to K-aligned starts):
 // quantum 1 packs as many rows into one tile as leave room for the largest
 // skew their windows can have (a row longer than that takes one window of
 // several tiles); quantum q = aligned_rows(T) > 1 gives every window a
-// multiple of q rows, so each starts K-aligned and walks as many tiles as it
-// needs (q rows when they exceed one tile).
-inline uint32_t skew_rows(uint32_t T, uint32_t tile, uint32_t quantum) {
+// multiple of q rows, so all start at the same skew, and each walks as many
+// tiles as it needs (q rows when they exceed one tile).
+inline uint32_t skew_rows(uint32_t T, uint32_t tile, uint32_t quantum, uint32_t phase) {
     if (quantum > 1) return T * quantum <= tile ? quantum * (tile / (T * quantum)) : quantum;
     uint32_t r = T <= tile ? tile / T : 1u;
-    while (r > 1 && r * T + max_skew(r * T) > tile) --r;
+    while (r > 1 && r * T + max_skew(r * T, phase) > tile) --r;
     return r;
 }
 
-// skew: windows are widened to K-aligned starts (kVecSkew), rows per window
-// as skew_rows(..., quantum) gives.
-inline Geometry make_geometry(int64_t num_envs, int64_t T, int waves, bool chunked, bool skew,
-                              uint32_t quantum, uint32_t *grid, uint32_t cap = kMaxGrid) {
+// Geometry of a launch of shape s: chunked shapes use kChunkWaves-wave
+// chunks, the scalar path 4-wave workgroups, the vector paths s.waves.
+inline Geometry make_geometry(int64_t num_envs, int64_t T, const LaunchShape &s, uint32_t *grid,
+                              uint32_t cap = kMaxGrid) {
+    const int waves = s.chunked ? kChunkWaves : s.vec ? s.waves : 4;
     const uint32_t tile = (uint32_t)waves * kWave * kK;
     Geometry g;
     g.num_envs = num_envs;
     g.T = (uint32_t)T;
+    g.phase = s.skew ? s.phase : 0u;
+    g.out0_phase = s.skew ? s.out0_phase : 0u;
+    g.scatter = s.skew && s.scatter ? 1u : 0u;
     int64_t groups;
-    if (chunked) {
+    if (s.chunked) {
         g.rows_per_group = 1;
-        g.chunks_per_row = chunk_count((uint32_t)T, skew);
+        g.chunks_per_row = chunk_count((uint32_t)T, s.skew);
         groups = num_envs * g.chunks_per_row;
     } else {
-        g.rows_per_group = skew                 ? skew_rows((uint32_t)T, tile, quantum)
+        g.rows_per_group = s.skew                ? skew_rows((uint32_t)T, tile, s.quantum, g.phase)
                            : (uint32_t)T <= tile ? tile / (uint32_t)T
                                                  : 1u;
         g.chunks_per_row = 1;
@@ -1041,9 +1063,9 @@ template <typename V, typename S>
 inline rlca_status launch_chunk_carries(void *slots, const Geometry &geo, bool backward,
                                         bool skew, hipStream_t stream) {
     int64_t n = geo.num_envs;
-    uint32_t T = geo.T, m = geo.chunks_per_row, span = chunk_span(skew);
+    uint32_t T = geo.T, m = geo.chunks_per_row, span = chunk_span(skew), phase = geo.out0_phase;
     int dir = backward ? 1 : 0;
-    void *args[] = {&slots, &n, &T, &m, &span, &dir};
+    void *args[] = {&slots, &n, &T, &m, &span, &phase, &dir};
     const hipError_t e =
         hipLaunchKernel((const void *)chunk_carries<V, S, kChunkWaves>, dim3(grid_for(n)),
                         dim3(kChunkWaves * kWave), args, 0, stream);
@@ -1054,14 +1076,14 @@ inline rlca_status launch_chunk_carries(void *slots, const Geometry &geo, bool b
 // apply (the apply grid capped at `apply_cap`).
 template <typename V, typename S, typename P>
 inline rlca_status launch_chunked(const void *aggregate, const void *apply, P &params, Lead &lead,
-                                  void *slots, bool backward, bool skew, hipStream_t stream,
-                                  uint32_t apply_cap = kMaxGrid) {
+                                  void *slots, bool backward, const LaunchShape &s,
+                                  hipStream_t stream, uint32_t apply_cap = kMaxGrid) {
     uint32_t grid;
-    params.geo =
-        make_geometry(params.geo.num_envs, params.geo.T, kChunkWaves, true, skew, 1, &grid);
+    params.geo = make_geometry(params.geo.num_envs, params.geo.T, s, &grid);
     const uint32_t apply_grid = grid_for(params.geo.num_groups, apply_cap);
     rlca_status st = launch_kernel(aggregate, kChunkWaves, grid, params, lead, stream);
-    if (st == RLCA_OK) st = launch_chunk_carries<V, S>(slots, params.geo, backward, skew, stream);
+    if (st == RLCA_OK)
+        st = launch_chunk_carries<V, S>(slots, params.geo, backward, s.skew, stream);
     if (st == RLCA_OK) st = launch_kernel(apply, kChunkWaves, apply_grid, params, lead, stream);
     return st;
 }
@@ -1070,10 +1092,8 @@ template <typename P>
 inline rlca_status launch_full(const void *kernel, const LaunchShape &s, P &params, Lead &lead,
                                hipStream_t stream, uint32_t cap = kMaxGrid) {
     uint32_t grid;
-    const int waves = s.vec ? s.waves : 4;
-    params.geo = make_geometry(params.geo.num_envs, params.geo.T, waves, false, s.skew,
-                               s.quantum, &grid, cap);
-    return launch_kernel(kernel, waves, grid, params, lead, stream);
+    params.geo = make_geometry(params.geo.num_envs, params.geo.T, s, &grid, cap);
+    return launch_kernel(kernel, s.vec ? s.waves : 4, grid, params, lead, stream);
 }
 
 // Workgroups of the launch (the last one, for the chunk modes) of a call of
@@ -1082,10 +1102,7 @@ inline rlca_status launch_full(const void *kernel, const LaunchShape &s, P &para
 inline uint32_t launch_grid(const LaunchShape &s, int64_t num_envs, int64_t T,
                             uint32_t cap = kMaxGrid) {
     uint32_t grid;
-    if (s.chunked)
-        make_geometry(num_envs, T, kChunkWaves, true, s.skew, 1, &grid, cap);
-    else
-        make_geometry(num_envs, T, s.vec ? s.waves : 4, false, s.skew, s.quantum, &grid, cap);
+    make_geometry(num_envs, T, s, &grid, cap);
     return grid;
 }
 
@@ -1125,7 +1142,7 @@ rlca_status launch_backward_variant(BackwardParams &p, const LaunchShape &s, hip
     return launch_chunked<float, S>(                                                             \
         (const void *)backward_scan<EST, TRUNC, IO, kChunkWaves, false, kChunkAggregate, S>,     \
         (const void *)backward_scan<EST, TRUNC, IO, kChunkWaves, false, kChunkApply, S, STATS>,  \
-        p, lead, p.out0, true, s.skew, stream, cap)
+        p, lead, p.out0, true, s, stream, cap)
         if (s.skew) RLCA_CHUNKED(kVecSkew);
         RLCA_CHUNKED(kVecRows);
 #undef RLCA_CHUNKED
@@ -1179,7 +1196,7 @@ rlca_status launch_forward_variant(ForwardParams &p, const LaunchShape &s, hipSt
                                    kChunkAggregate, S>,                                     \
         (const void *)forward_scan<V, KIND, AFTER_DONE, IO, kChunkWaves, false, kChunkApply, \
                                    S>,                                                      \
-        p, lead, p.out, false, s.skew, stream)
+        p, lead, p.out, false, s, stream)
         if (s.skew) RLCA_CHUNKED(kVecSkew);
         RLCA_CHUNKED(kVecRows);
 #undef RLCA_CHUNKED

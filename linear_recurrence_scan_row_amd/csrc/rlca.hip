@@ -71,17 +71,41 @@ static rlca_status check_aliasing(const Span *outs, int nout, const Span *ins, i
     return RLCA_OK;
 }
 
-// The vector paths load a lane's K steps with one instruction per stream:
-// they need arrays aligned to K elements.  With T % K == 0 a lane's steps lie
-// in one row (kVecRows); otherwise windows are widened to K-aligned starts
-// (kVecSkew).  Unaligned arrays take the scalar path.
-static int io_of(int64_t T, const void *const *wide, int nw, size_t elem,
-                 const void *const *u8, int nu) {
-    for (int i = 0; i < nw; ++i)
-        if (wide[i] != nullptr && ((uintptr_t)wide[i] % (elem * kK)) != 0) return kScalarIO;
-    for (int i = 0; i < nu; ++i)
-        if (u8[i] != nullptr && ((uintptr_t)u8[i] % kK) != 0) return kScalarIO;
-    return T % kK == 0 ? kVecRows : kVecSkew;
+// Memory path of a call.  The vector paths read a lane's K steps of each
+// per-step input as one aligned block, so every per-step input must sit at
+// the same phase: the element index, mod K, at which its K-aligned blocks
+// start.  Whole-row lane chunks (kVecRows) further need T % K == 0 and every
+// per-step array, outputs included, at phase 0; otherwise windows are
+// widened to the inputs' block boundaries (kVecSkew), and outputs at another
+// phase are written element by element.  Inputs at different phases take
+// the scalar path.  (The [num_envs] arrays are read element by element.)
+struct IoChoice {
+    int io;
+    uint32_t phase, out0_phase;
+    bool scatter;
+};
+
+static uint32_t phase_of(const void *p, size_t elem) {
+    return (uint32_t)(((uintptr_t)p / elem) % kK);
+}
+
+static IoChoice io_of(int64_t T, const void *const *ins, int nin, size_t elem,
+                      const void *const *u8, int nu, const void *const *outs, int nout) {
+    IoChoice c{kScalarIO, 0, 0, false};
+    int phase = -1;
+    for (int i = 0; i < nin + nu; ++i) {
+        const void *p = i < nin ? ins[i] : u8[i - nin];
+        if (p == nullptr) continue;
+        const int m = (int)phase_of(p, i < nin ? elem : 1);
+        if (phase >= 0 && m != phase) return c;
+        phase = m;
+    }
+    c.phase = phase < 0 ? 0u : (uint32_t)phase;
+    c.out0_phase = phase_of(outs[0], elem);
+    for (int i = 0; i < nout; ++i)
+        if (outs[i] != nullptr && phase_of(outs[i], elem) != c.phase) c.scatter = true;
+    c.io = T % kK == 0 && c.phase == 0 && !c.scatter ? kVecRows : kVecSkew;
+    return c;
 }
 
 // Launch shape.  Rows that end at wave boundaries (T divides the 256-step
@@ -98,8 +122,9 @@ static int io_of(int64_t T, const void *const *wide, int nw, size_t elem,
 // sustains 3.4-5 TB/s).
 static constexpr int64_t kChunkedMaxRows = 64;
 static constexpr int64_t kOneWaveMinRows = 4096;
-// Rows of T % K != 0 steps (aligned arrays) are read K-wide from windows
-// widened to K-aligned starts, in 8-wave workgroups for every T (one-wave
+// Rows of T % K != 0 steps (and inputs or outputs off phase 0) are read
+// K-wide from windows widened to block boundaries, in 8-wave workgroups for
+// every T (one-wave
 // workgroups walking rows of 257..1023 steps measured 10-50% slower here:
 // a row plus its skew often needs one more 256-step tile).  A row that fits
 // one tile but not together with the largest skew its window can have
@@ -110,11 +135,14 @@ static constexpr int64_t kOneWaveMinRows = 4096;
 // 4 rows measured 5-13% slower over 4096 x 4097).
 static constexpr int64_t kSkewAlignedMinWindows = 1024;
 
-static LaunchShape choose_shape(int64_t num_envs, int64_t T, int io) {
+static LaunchShape choose_shape(int64_t num_envs, int64_t T, const IoChoice &io) {
     LaunchShape s;
-    s.vec = io != kScalarIO;
-    s.skew = io == kVecSkew;
-    s.wave_local = io == kVecRows && T <= kWave * kK && (kWave * kK) % T == 0;
+    s.vec = io.io != kScalarIO;
+    s.skew = io.io == kVecSkew;
+    s.phase = s.skew ? io.phase : 0u;
+    s.out0_phase = s.skew ? io.out0_phase : 0u;
+    s.scatter = s.skew && io.scatter;
+    s.wave_local = io.io == kVecRows && T <= kWave * kK && (kWave * kK) % T == 0;
     s.waves = (T <= kWave * kK || T >= 1024 || num_envs < kOneWaveMinRows) ? 8 : 1;
     s.chunked = s.vec && T > 2 * (int64_t)kChunkSteps && num_envs < kChunkedMaxRows;
 #ifdef RLCA_FORCE_WAVES
@@ -128,7 +156,7 @@ static LaunchShape choose_shape(int64_t num_envs, int64_t T, int io) {
         s.waves = 8;
         const int64_t tile = (int64_t)s.waves * kWave * kK;
         const int64_t q = aligned_rows((uint32_t)T);
-        if (!s.chunked && T <= tile && T + max_skew((uint32_t)T) > tile &&
+        if (!s.chunked && T <= tile && T + max_skew((uint32_t)T, s.phase) > tile &&
             num_envs / q >= kSkewAlignedMinWindows)
             s.quantum = (uint32_t)q;
     }
@@ -224,7 +252,8 @@ static rlca_status prepare_backward(int est, int storage, const void *rewards,
     p.geo.num_envs = num_envs;
     p.geo.T = (uint32_t)T;
     const void *u8[] = {terminated, truncated};
-    c->shape = choose_shape(num_envs, T, io_of(T, real, 9, es, u8, 2));
+    const void *outs[] = {out0, out1};
+    c->shape = choose_shape(num_envs, T, io_of(T, f32_steps, 6, es, u8, 2, outs, 2));
     return RLCA_OK;
 }
 
@@ -275,9 +304,10 @@ static rlca_status prepare_forward(int kind, int storage, const void *x, bool is
     p.decay = is_int ? __builtin_bit_cast(float, 1u) : decay;
     p.geo.num_envs = num_envs;
     p.geo.T = (uint32_t)T;
-    const void *wide[] = {x, beta, out};
+    const void *wide[] = {x, beta};
     const void *u8[] = {flags};
-    c->shape = choose_shape(num_envs, T, io_of(T, wide, 3, es, u8, 1));
+    const void *outs[] = {out};
+    c->shape = choose_shape(num_envs, T, io_of(T, wide, 2, es, u8, 1, outs, 1));
     return RLCA_OK;
 }
 
@@ -311,16 +341,14 @@ static bool grouped_member(const Call &c, GroupedCall *g, int *variant, uint32_t
     uint32_t grid, groups;
     if (c.backward) {
         g->b = c.bp;
-        g->b.geo = make_geometry(c.bp.geo.num_envs, c.bp.geo.T, c.shape.waves, false, skew,
-                                 c.shape.quantum, &grid);
+        g->b.geo = make_geometry(c.bp.geo.num_envs, c.bp.geo.T, c.shape, &grid);
         const bool trunc = c.bp.truncated != nullptr;
         *variant = skew ? grouped_skew_backward_variant(c.est, trunc)
                         : grouped_backward_variant(c.est, trunc, wl, one);
         groups = g->b.geo.num_groups;
     } else {
         g->f = c.fp;
-        g->f.geo = make_geometry(c.fp.geo.num_envs, c.fp.geo.T, c.shape.waves, false, skew,
-                                 c.shape.quantum, &grid);
+        g->f.geo = make_geometry(c.fp.geo.num_envs, c.fp.geo.T, c.shape, &grid);
         if (skew)
             *variant = c.forward == kForwardAffine
                            ? kGroupedSkewAffineForward
@@ -508,11 +536,17 @@ using namespace rlca;
 // One (sum, sum of squares) pair per workgroup of the GAE launch, for
 // whichever launch shape the pointers will select.
 static uint32_t gae_stats_pairs(int64_t num_envs, int64_t T) {
-    const int io = T % kK == 0 ? kVecRows : kVecSkew;
-    const uint32_t v = launch_grid(choose_shape(num_envs, T, io), num_envs, T, kStatsMaxGrid);
-    const uint32_t s =
-        launch_grid(choose_shape(num_envs, T, kScalarIO), num_envs, T, kStatsMaxGrid);
-    return v > s ? v : s;
+    IoChoice choices[2 + kK] = {{kScalarIO, 0, 0, false}, {kVecRows, 0, 0, false}};
+    for (int phase = 0; phase < kK; ++phase)
+        choices[2 + phase] = {kVecSkew, (uint32_t)phase, 0, false};
+    uint32_t most = 0;
+    for (int i = 0; i < 2 + kK; ++i) {
+        if (choices[i].io == kVecRows && T % kK != 0) continue;
+        const uint32_t g =
+            launch_grid(choose_shape(num_envs, T, choices[i]), num_envs, T, kStatsMaxGrid);
+        most = g > most ? g : most;
+    }
+    return most;
 }
 
 static bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }

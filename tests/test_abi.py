@@ -225,8 +225,10 @@ def test_workspace_size_queries(lib):
     # one (sum, sum of squares) pair of doubles per workgroup: 4096 x 128 packs
     # 16 rows per 8-wave workgroup; the unaligned path packs 8 per 4-wave one
     assert lib.rlca_gae_stats_workspace_size(4096, 128) == 16 * 512
-    assert lib.rlca_gae_stats_workspace_size(3, 100000) == 16 * 3 * 49   # chunked: 2048-step chunks
-    # T % 4 != 0: 2040-step chunks, the last in scan order 4..2043 steps
+    # chunked: 2048-step chunks (49 per row) for aligned arrays, 2040-step
+    # chunks (50 per row, the last in scan order 4..2043 steps) for T % 4 != 0
+    # or inputs off phase 0; the size covers whichever the pointers select
+    assert lib.rlca_gae_stats_workspace_size(3, 100000) == 16 * 3 * 50
     assert lib.rlca_gae_stats_workspace_size(3, 100001) == 16 * 3 * 50
     assert lib.rlca_ppo_clip_loss_workspace_size(4096, 128) == 8 * 512
     assert lib.rlca_ppo_clip_loss_workspace_size(1 << 20, 512) == 8 * 2048

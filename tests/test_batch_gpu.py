@@ -259,3 +259,48 @@ def test_single_member_and_one_wave_only_batches(gpu_device):
         torch.cuda.synchronize(gpu_device)
         for m in members:
             m.check()
+
+
+def test_members_off_16_byte_alignment(gpu_device):
+    """Calls whose per-step inputs all sit at one phase off the 16-byte
+    boundary (views at an element offset) join the grouped launch of the
+    widened-window path, outputs at another phase written element by
+    element; inputs at different phases run their own (scalar) kernel.  Each
+    matches the oracle and its single call bit for bit."""
+    def at(x, k):
+        x = np.ascontiguousarray(x)
+        flat = torch.zeros(x.size + 4, dtype=torch.from_numpy(x).dtype, device=gpu_device)
+        flat[k:k + x.size] = torch.from_numpy(x.reshape(-1)).to(gpu_device)
+        return flat[k:k + x.size].view(x.shape)
+
+    def out_at(shape, k):
+        n = int(np.prod(shape))
+        return torch.zeros(n + 4, device=gpu_device)[k:k + n].view(shape)
+
+    cases = []
+    for seed, (N, T), pin, pout, mixed in [(60, (300, 128), 1, 0, False),
+                                           (61, (40, 127), 2, 2, False),
+                                           (62, (9, 1024), 3, 1, False),
+                                           (63, (50, 200), 1, 1, True)]:
+        d = workloads.backward_rollout(seed, N, T, p_term=0.05, p_trunc=0.05)
+        args = (at(d.rewards, pin), at(d.values, (pin + 1) % 4 if mixed else pin),
+                at(d.terminated, pin), at(d.truncated, pin), at(d.trunc_values, pin),
+                dev(d.bootstrap, gpu_device), 0.99, 0.95)
+        ref = oracle.gae(d.rewards, d.values, d.terminated, d.truncated, d.trunc_values,
+                         d.bootstrap, 0.99, 0.95)
+        cases.append((args, ref, (N, T), pout, f"gae seed={seed} phases=({pin},{pout})"))
+    batch = rl.Batch()
+    outs = []
+    for args, ref, shape, pout, what in cases:
+        a, r = out_at(shape, pout), out_at(shape, pout)
+        batch.gae(*args, advantages=a, returns=r)
+        outs.append((a, r))
+    batch.run()
+    torch.cuda.synchronize(gpu_device)
+    for (args, ref, shape, pout, what), (a, r) in zip(cases, outs):
+        assert_parity(a, ref[0], f"{what} adv")
+        assert_parity(r, ref[1], f"{what} ret")
+        a1, r1 = out_at(shape, pout), out_at(shape, pout)
+        rl.gae(*args, advantages=a1, returns=r1)
+        torch.cuda.synchronize(gpu_device)
+        assert torch.equal(a, a1) and torch.equal(r, r1), f"{what}: batch and single call differ"

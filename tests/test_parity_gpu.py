@@ -3,10 +3,11 @@
 The bar: fp32 outputs within |gpu - oracle| <= 1e-4 * (1 + |oracle|) element by
 element (the rl-triton summary's §6 validation tolerance, atol = rtol = 1e-4);
 the int32 prefix sum bit-exact.  Inputs are seeded synthetic rollouts; shapes
-span one lane, several tiles, ragged tails, the three memory paths (element
-accesses for unaligned arrays; 4-wide accesses with whole-row lane chunks for
-T % 4 == 0; 4-wide accesses over windows widened to aligned starts for other
-T), and the five measured workloads at full size.
+span one lane, several tiles, ragged tails, the three memory paths (4-wide
+accesses with whole-row lane chunks for T % 4 == 0 and 16-byte aligned
+arrays; 4-wide reads over windows widened to block boundaries for other T or
+inputs all at one other phase; element accesses for inputs at different
+phases), and the five measured workloads at full size.
 """
 import numpy as np
 import pytest
@@ -239,30 +240,33 @@ def test_flags_as_bool_and_nonzero_bytes(gpu_device):
 
 
 @pytest.mark.parametrize("T", [132, 131])
-def test_unaligned_views_take_the_scalar_path(T, gpu_device):
-    """Inputs that are 4-byte but not 16-byte aligned (views at an odd element
-    offset of a larger buffer) give the same results as aligned copies."""
+@pytest.mark.parametrize("shifts", [(1, 1, 1, 1, 1), (1, 2, 1, 1, 1), (0, 0, 3, 0, 0)])
+def test_views_off_16_byte_alignment(T, shifts, gpu_device):
+    """Inputs that are 4-byte but not 16-byte aligned (views at an element
+    offset of a larger buffer) give the same results as aligned copies.  All
+    at one phase (shifts (1, 1, 1, 1, 1)), the vector path reads them from
+    windows widened to their block boundaries; at different phases, the
+    scalar path reads them element by element."""
     N = 37
     d = rollout(9, N, T)
 
-    def shifted(x, dtype):
-        flat = torch.zeros(N * T + 1, dtype=dtype, device=gpu_device)
-        flat[1:] = torch.from_numpy(np.ascontiguousarray(x)).reshape(-1).to(gpu_device)
-        return flat[1:].view(N, T)
+    def shifted(x, dtype, k):
+        flat = torch.zeros(N * T + 4, dtype=dtype, device=gpu_device)
+        flat[k:k + N * T] = torch.from_numpy(np.ascontiguousarray(x)).reshape(-1).to(gpu_device)
+        return flat[k:k + N * T].view(N, T)
 
-    r = shifted(d.rewards, torch.float32)
-    v = shifted(d.values, torch.float32)
-    term = shifted(d.terminated, torch.uint8)
-    trunc = shifted(d.truncated, torch.uint8)
-    tv = shifted(d.trunc_values, torch.float32)
-    assert r.data_ptr() % 16 != 0
+    r = shifted(d.rewards, torch.float32, shifts[0])
+    v = shifted(d.values, torch.float32, shifts[1])
+    term = shifted(d.terminated, torch.uint8, shifts[2])
+    trunc = shifted(d.truncated, torch.uint8, shifts[3])
+    tv = shifted(d.trunc_values, torch.float32, shifts[4])
     adv, ret = rl.gae(r, v, term, trunc, tv, dev(d.bootstrap, gpu_device))
     oadv, oret = oracle.gae(d.rewards, d.values, d.terminated, d.truncated, d.trunc_values,
                             d.bootstrap, 0.99, 0.95)
-    assert_parity(adv, oadv, "unaligned adv")
-    assert_parity(ret, oret, "unaligned ret")
-    xi = shifted(workloads.forward_rollout(3, N, T).ints, torch.int32)
-    fl = shifted(workloads.forward_rollout(3, N, T).starts, torch.uint8)
+    assert_parity(adv, oadv, f"shifted {shifts} adv")
+    assert_parity(ret, oret, f"shifted {shifts} ret")
+    xi = shifted(workloads.forward_rollout(3, N, T).ints, torch.int32, shifts[0])
+    fl = shifted(workloads.forward_rollout(3, N, T).starts, torch.uint8, shifts[2])
     out = rl.episodic_prefix_sum(xi, fl)
     assert np.array_equal(out.cpu().numpy(),
                           oracle.episodic_prefix_sum(xi.cpu().numpy(), fl.cpu().numpy()))
