@@ -48,9 +48,14 @@ _dbl = ctypes.c_double
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            build()
-        lib = ctypes.CDLL(LIB_PATH)
+        # RLCA_ORACLE_LIB names another build of oracle.c to load instead; the
+        # mutation test points it at builds with a planted mistake.
+        path = os.environ.get("RLCA_ORACLE_LIB")
+        if path is None:
+            path = LIB_PATH
+            if not os.path.exists(path):
+                build()
+        lib = ctypes.CDLL(path)
         sig = {
             "oracle_gae": [_f32p, _f32p, _u8p, _u8p, _f32p, _f32p, _dbl, _dbl, _i64, _i64,
                            _f64p, _f64p],

@@ -522,6 +522,24 @@ def test_ppo_on_policy_recovers_normalized_advantages():
     assert loss == pytest.approx(-adv.astype(np.float64).mean(), rel=1e-13)
 
 
+def test_ppo_normalization_adds_epsilon_to_the_std():
+    """A_hat = (A - mean) / (std + eps): the epsilon is added to the standard
+    deviation, not to the variance, and keeps a zero spread finite.  rho = 1,
+    so the gradient is -A_hat / M.  Hand values: A = (1, 3) has mean 2 and
+    sample std sqrt(2); with eps = 0.5, A_hat = (-1, 1) / (sqrt(2) + 0.5) and
+    the gradient is (1, -1) / (2 (sqrt(2) + 0.5)) = +-0.26120387496374144."""
+    zero = np.zeros(2, np.float32)
+    loss, grad = oracle.ppo_clip_loss(np.array([1.0, 3.0], np.float32), zero, zero,
+                                      (2.0, math.sqrt(2.0)), 0.2, 0.5)
+    assert loss == pytest.approx(0.0, abs=1e-16)
+    assert np.allclose(grad, [0.26120387496374144, -0.26120387496374144], rtol=1e-15, atol=0)
+    # equal advantages: zero spread, A_hat = 0 / (0 + eps) = 0 everywhere
+    const = np.full(4, 3.5, np.float32)
+    loss, grad = oracle.ppo_clip_loss(const, np.zeros(4, np.float32), np.zeros(4, np.float32),
+                                      (3.5, 0.0), 0.2, 1e-8)
+    assert loss == 0.0 and np.array_equal(grad, np.zeros(4))
+
+
 def test_ppo_clip_branches():
     """Each sign of A_hat against each side of the clip interval, eps = 0.2."""
     M = 4
