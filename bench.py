@@ -577,27 +577,34 @@ def run_sweep(args):
                 torch.cuda.synchronize()
                 h = stream.cuda_stream
 
-                def launch(s):
+                def bound(s):
+                    """(entry point, arguments) of one launch on set s, bound
+                    before timing so the timed loop makes one ctypes call."""
                     if name == "gae+trunc":
-                        return lib.rlca_gae(s["r"].data_ptr(), s["v"].data_ptr(),
-                                            s["term"].data_ptr(), s["trunc"].data_ptr(),
-                                            s["tv"].data_ptr(), s["b"].data_ptr(), 0.99, 0.95, n,
-                                            t, s["o0"].data_ptr(), s["o1"].data_ptr(), h)
+                        return lib.rlca_gae, (s["r"].data_ptr(), s["v"].data_ptr(),
+                                              s["term"].data_ptr(), s["trunc"].data_ptr(),
+                                              s["tv"].data_ptr(), s["b"].data_ptr(), 0.99, 0.95,
+                                              n, t, s["o0"].data_ptr(), s["o1"].data_ptr(), h)
                     if name == "retrace+trunc":
-                        return lib.rlca_retrace(*[s[k].data_ptr() for k in ins], 0.99, 0.95, 1.0,
-                                                n, t, s["o0"].data_ptr(), h)
-                    return lib.rlca_eligibility_traces(s["x"].data_ptr(), s["start"].data_ptr(),
-                                                       0, 0.99, 0.9, n, t, s["o0"].data_ptr(), h)
+                        return lib.rlca_retrace, (*[s[k].data_ptr() for k in ins], 0.99, 0.95,
+                                                  1.0, n, t, s["o0"].data_ptr(), h)
+                    return lib.rlca_eligibility_traces, (s["x"].data_ptr(), s["start"].data_ptr(),
+                                                         0, 0.99, 0.9, n, t, s["o0"].data_ptr(),
+                                                         h)
 
+                plan = [bound(s) for s in sets]
                 with torch.cuda.stream(stream):
                     for i in range(3):
-                        assert launch(sets[i % nsets]) == 0
+                        fn, a = plan[i % nsets]
+                        assert fn(*a) == 0
                     batch = max(20, min(400, int(2e9 // call_bytes)))
                     e0 = torch.cuda.Event(enable_timing=True)
                     e1 = torch.cuda.Event(enable_timing=True)
                     e0.record(stream)
                     for i in range(batch):
-                        assert launch(sets[i % nsets]) == 0
+                        fn, a = plan[i % nsets]
+                        if fn(*a) != 0:
+                            raise RuntimeError(f"{name} {n}x{t}: launch failed")
                     e1.record(stream)
                     torch.cuda.synchronize()
                 us = e0.elapsed_time(e1) / batch * 1e3
