@@ -278,3 +278,44 @@ def test_ppo_clip_loss_validation(lib):
     assert ppo(lib, loss=A + 8) == ALIAS                     # loss inside the advantages
     assert ppo(lib, ws=E) == ALIAS                           # workspace over the loss
     assert ppo(lib, stats=G, ws=G + 8) == ALIAS              # workspace over the stats
+
+
+def test_missing_library_fails_loudly():
+    """Without librlca.so the binding raises; there is no CPU fallback."""
+    import subprocess
+    import sys
+    code = ("import linear_recurrence_scan_row_amd.rlca as r\n"
+            "r.LIB_PATH = '/nonexistent/librlca.so'\n"
+            "r._lib = None\n"
+            "try:\n"
+            "    r.lib()\n"
+            "except ImportError as e:\n"
+            "    print('raised', e)\n"
+            "else:\n"
+            "    raise SystemExit('lib() returned without the library')\n")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                         timeout=120)
+    assert out.returncode == 0 and "raised" in out.stdout, out.stdout + out.stderr
+
+
+def test_product_package_never_imports_the_oracle():
+    """The oracle is test infrastructure: importing the package (and its
+    binding, build and workload modules) must not load it."""
+    import subprocess
+    import sys
+    code = ("import sys\n"
+            "import linear_recurrence_scan_row_amd as rl\n"
+            "from linear_recurrence_scan_row_amd import rlca, build, workloads, profiling\n"
+            "rl.lib()\n"
+            "bad = [m for m in sys.modules if m == 'oracle' or m.startswith('oracle.')]\n"
+            "raise SystemExit(f'oracle imported: {bad}' if bad else 0)\n")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                         timeout=120)
+    assert out.returncode == 0, out.stdout + out.stderr
+    pkg = os.path.join(ROOT, "linear_recurrence_scan_row_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for name in files:
+            if name.endswith((".py", ".hip", ".hpp", ".h", ".c")):
+                text = open(os.path.join(dirpath, name)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), name
+                assert "liboracle" not in text, name
