@@ -33,14 +33,11 @@
 
 namespace rlca {
 
-// K consecutive steps per lane: one K-wide load per fp32 stream (dwordx4 at
-// K = 4).  Wider per-lane chunks make one load instruction touch lanes 32+
-// bytes apart and lose coalescing.
-#ifndef RLCA_STEPS_PER_LANE
-#define RLCA_STEPS_PER_LANE 4
-#endif
-constexpr int kK = RLCA_STEPS_PER_LANE;
-static_assert(kK == 1 || kK == 2 || kK == 4, "steps per lane: 1, 2 or 4");
+// K = 4 consecutive steps per lane: one dwordx4 load per fp32 stream (dwordx2
+// for 16-bit storage, one dword per flag stream).  Wider per-lane chunks make
+// one load instruction touch lanes 32+ bytes apart and lose coalescing;
+// narrower ones measured no faster at 4096 x 128 and slower beyond.
+constexpr int kK = 4;
 
 // Waves per workgroup in the chunk modes; the chunk is one tile.
 constexpr int kChunkWaves = 8;
@@ -165,22 +162,10 @@ template <typename E, int N>
 struct VecOf {
     typedef E type __attribute__((ext_vector_type(N)));
 };
-template <typename E>
-struct VecOf<E, 1> {
-    typedef E type;
-};
 
 // Unsigned integer holding K flag bytes.
 template <int N>
 struct FlagWord;
-template <>
-struct FlagWord<1> {
-    typedef uint8_t type;
-};
-template <>
-struct FlagWord<2> {
-    typedef uint16_t type;
-};
 template <>
 struct FlagWord<4> {
     typedef uint32_t type;
@@ -213,12 +198,8 @@ __device__ __forceinline__ void load_steps(E (&x)[kK], const S *__restrict__ p, 
             const vec *src = reinterpret_cast<const vec *>(p + off);
             q = LAST ? __builtin_nontemporal_load(src) : *src;
         }
-        if constexpr (kK == 1) {
-            x[0] = widen<E>(q);
-        } else {
 #pragma unroll
-            for (int i = 0; i < kK; ++i) x[i] = widen<E>(q[i]);
-        }
+        for (int i = 0; i < kK; ++i) x[i] = widen<E>(q[i]);
     } else {
 #pragma unroll
         for (int i = 0; i < kK; ++i) x[i] = (off + i < L) ? widen<E>(p[off + i]) : E(0);
@@ -257,12 +238,8 @@ __device__ __forceinline__ void store_steps(S *__restrict__ p, const E (&x)[kK],
                 if (off + i >= lo && off + i < L) p[off + i] = narrow<S>(x[i]);
         } else if (off < L) {
             vec q;
-            if constexpr (kK == 1) {
-                q = narrow<S>(x[0]);
-            } else {
 #pragma unroll
-                for (int i = 0; i < kK; ++i) q[i] = narrow<S>(x[i]);
-            }
+            for (int i = 0; i < kK; ++i) q[i] = narrow<S>(x[i]);
             __builtin_nontemporal_store(q, reinterpret_cast<vec *>(p + off));
         }
     } else {

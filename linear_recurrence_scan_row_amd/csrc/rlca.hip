@@ -145,12 +145,6 @@ static LaunchShape choose_shape(int64_t num_envs, int64_t T, const IoChoice &io)
     s.wave_local = io.io == kVecRows && T <= kWave * kK && (kWave * kK) % T == 0;
     s.waves = (T <= kWave * kK || T >= 1024 || num_envs < kOneWaveMinRows) ? 8 : 1;
     s.chunked = s.vec && T > 2 * (int64_t)kChunkSteps && num_envs < kChunkedMaxRows;
-#ifdef RLCA_FORCE_WAVES
-    s.waves = RLCA_FORCE_WAVES;
-#endif
-#ifdef RLCA_FORCE_CHUNKED
-    s.chunked = s.vec && T > 2 * (int64_t)kChunkSteps && RLCA_FORCE_CHUNKED;
-#endif
     s.quantum = 1;
     if (s.skew) {
         s.waves = 8;
