@@ -82,23 +82,31 @@ __global__ __launch_bounds__(kPpoThreads) void ppo_clip_loss(
     const float *__restrict__ adv, const double *__restrict__ stats,
     const float *__restrict__ logp_new, const float *__restrict__ logp_old, float clip_eps,
     float norm_eps, int64_t M, float *__restrict__ grad, double *__restrict__ partials) {
-    float mean = 0.f, scale = 1.f;
-    if constexpr (NORM) {
-        mean = (float)stats[0];
-        scale = (float)(1.0 / (stats[1] + (double)norm_eps));
-    }
     const float lo = 1.f - clip_eps, hi = 1.f + clip_eps;
     const float neg_inv_m = (float)(-1.0 / (double)M);
     double acc = 0.0;
     const int64_t stride = (int64_t)gridDim.x * kPpoThreads;
+    float mean = 0.f, scale = 1.f;
     if constexpr (VEC) {
         typedef float f4 __attribute__((ext_vector_type(4)));
         const int64_t n4 = M / 4;
-        for (int64_t i = (int64_t)blockIdx.x * kPpoThreads + threadIdx.x; i < n4; i += stride) {
-            // each input is read once: non-temporal loads
-            const f4 a = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(adv) + i);
-            const f4 pn = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(logp_new) + i);
-            const f4 po = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(logp_old) + i);
+        // Each input is read once (non-temporal loads).  A lane's first
+        // block goes out before the statistics are read: they come from the
+        // previous launch, and waiting for them first would put one more
+        // memory round trip ahead of every wave's loads.
+        int64_t i = (int64_t)blockIdx.x * kPpoThreads + threadIdx.x;
+        f4 a = {}, pn = {}, po = {};
+        if (i < n4) {
+            a = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(adv) + i);
+            pn = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(logp_new) + i);
+            po = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(logp_old) + i);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (NORM) {
+            mean = (float)stats[0];
+            scale = (float)(1.0 / (stats[1] + (double)norm_eps));
+        }
+        while (i < n4) {
             f4 g;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
@@ -108,15 +116,25 @@ __global__ __launch_bounds__(kPpoThreads) void ppo_clip_loss(
                 g[k] = gk;
             }
             if constexpr (GRAD) __builtin_nontemporal_store(g, reinterpret_cast<f4 *>(grad) + i);
+            i += stride;
+            if (i < n4) {
+                a = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(adv) + i);
+                pn = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(logp_new) + i);
+                po = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(logp_old) + i);
+            }
         }
-        const int64_t i = 4 * n4 + threadIdx.x;
-        if (blockIdx.x == 0 && i < M) {
-            const float ah = NORM ? (adv[i] - mean) * scale : adv[i];
+        const int64_t j = 4 * n4 + threadIdx.x;  // the last M % 4 steps
+        if (blockIdx.x == 0 && j < M) {
+            const float ah = NORM ? (adv[j] - mean) * scale : adv[j];
             float g;
-            acc += (double)ppo_term(ah, logp_new[i], logp_old[i], lo, hi, neg_inv_m, g);
-            if constexpr (GRAD) grad[i] = g;
+            acc += (double)ppo_term(ah, logp_new[j], logp_old[j], lo, hi, neg_inv_m, g);
+            if constexpr (GRAD) grad[j] = g;
         }
     } else {
+        if constexpr (NORM) {
+            mean = (float)stats[0];
+            scale = (float)(1.0 / (stats[1] + (double)norm_eps));
+        }
         for (int64_t i = (int64_t)blockIdx.x * kPpoThreads + threadIdx.x; i < M; i += stride) {
             const float ah = NORM ? (adv[i] - mean) * scale : adv[i];
             float g;
