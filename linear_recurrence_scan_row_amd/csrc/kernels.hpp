@@ -262,6 +262,18 @@ __device__ __forceinline__ E *chunk_slot(void *out, int64_t base, uint32_t out_p
     return reinterpret_cast<E *>(static_cast<S *>(out) + base);
 }
 
+// Chunk apply mode reads its carry from the chunk's first slot: an output
+// element that one of the workgroup's waves overwrites later.  Each wave
+// takes the value into hand here, before the barrier in block_carry_in (a
+// chunk is one tile of kChunkWaves waves, so that barrier always runs and
+// precedes every store): no wave can store over the slot while another
+// wave's read of it is still in flight.  The slot load was issued ahead of
+// the tile's loads, which return in order, so this wait costs nothing.
+template <typename V>
+__device__ __forceinline__ void hold_chunk_carry(V &carry) {
+    asm volatile("" : "+v"(carry));
+}
+
 // The steps one workgroup iteration covers.
 struct Window {
     int64_t row0;       // first row
@@ -553,10 +565,8 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
         // A just after the current tile: 0 at a row end (edges live in alpha),
         // or the carry the chunk-carry pass left in the chunk's first slot.
         float carry = 0.f;
-        if constexpr (MODE == kChunkApply) {
+        if constexpr (MODE == kChunkApply)  // issued ahead of the tile's loads
             carry = chunk_slot<float, S>(p.out0, win.base, p.geo.out0_phase)[0];
-            __syncthreads();  // every lane has read the slot before any store
-        }
 
         for (uint32_t it = 0; it < ntiles; ++it) {
             const uint32_t off = (ntiles - 1 - it) * kTile + chunk * kK;
@@ -711,6 +721,7 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
                 }
             } else {
                 float carry_out;
+                if constexpr (MODE == kChunkApply) hold_chunk_carry(carry);
                 float A = block_carry_in<NW, WAVE_LOCAL>(fa, fb, carry, lds_a, lds_b, parity,
                                                           carry_out);
                 parity ^= 1;
@@ -811,10 +822,8 @@ __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint3
         const uint32_t L = win.L + sk;
         const uint32_t ntiles = MODE == kFull ? (L + kTile - 1) / kTile : 1u;
         V carry = V(0);
-        if constexpr (MODE == kChunkApply) {
+        if constexpr (MODE == kChunkApply)  // issued ahead of the tile's loads
             carry = chunk_slot<V, S>(p.out, win.base, p.geo.out0_phase)[0];
-            __syncthreads();  // every lane has read the slot before any store
-        }
 
         for (uint32_t it = 0; it < ntiles; ++it) {
             const uint32_t off = it * kTile + chunk * kK;
@@ -889,6 +898,7 @@ __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint3
                 }
             } else {
                 V carry_out;
+                if constexpr (MODE == kChunkApply) hold_chunk_carry(carry);
                 V A = block_carry_in<NW, WAVE_LOCAL>(fa, fb, carry, lds_a, lds_b, parity,
                                                       carry_out);
                 parity ^= 1;
