@@ -3,7 +3,16 @@ ragged, unaligned and long rows), flag densities, discounts, clip
 thresholds, reset conventions and storage types, against the fp64 oracle.
 The bars are those of the fixed-shape tests: 1e-4 * (1 + |o|) for fp32
 storage, plus one output rounding (u |o|, u = 2^-8 / 2^-11) for bf16 /
-fp16, and bit-exact int32 sums."""
+fp16, and bit-exact int32 sums.
+
+Trace clips stay at or below 1, so every coefficient |beta_t| <= 1 (the
+importance-weighted ones are gamma * lambda * min(c_bar, ratio)).  With
+c_bar > 1 the recurrence is expansive: products of beta grow, values reach
+1e10 and more over long rows, and rounding errors grow with them, so that
+even a sequential fp32 evaluation of the same recursion misses the 1e-4 bar
+on some elements (and fp16 storage overflows).  The bar is a statement about
+contracting recurrences; the clip thresholds themselves (rho_bar up to 2)
+are still drawn."""
 import numpy as np
 import pytest
 import torch
@@ -82,7 +91,7 @@ def test_random_case(case, gpu_device):
         check(rl.discounted_returns(D(r), F(term), F(tr_h), D(tv_h), D(b), gamma),
               oracle.discounted_returns(H(r), term, tr_h, H(tv_h), H(b), gamma), dtype, what)
     elif op == 3:
-        rho_bar, c_bar = float(rng.choice([0.5, 1.0, 2.0])), float(rng.choice([0.5, 1.0, 3.0]))
+        rho_bar, c_bar = float(rng.choice([0.5, 1.0, 2.0])), float(rng.choice([0.5, 1.0]))
         vs, pg = rl.vtrace(D(r), D(v), D(mu), D(pi), F(term), F(tr_h), D(tv_h), D(b), gamma,
                            lam, rho_bar, c_bar)
         ovs, opg = oracle.vtrace(H(r), H(v), H(mu), H(pi), term, tr_h, H(tv_h), H(b), gamma,
@@ -90,7 +99,7 @@ def test_random_case(case, gpu_device):
         check(vs, ovs, dtype, what)
         check(pg, opg, dtype, what)
     elif op == 4:
-        c_bar = float(rng.choice([0.5, 1.0, 3.0]))
+        c_bar = float(rng.choice([0.5, 1.0]))
         check(rl.retrace(D(r), D(v), D(eq), D(mu), D(pi), F(term), F(tr_h), D(tv_h), D(b),
                          gamma, lam, c_bar),
               oracle.retrace(H(r), H(v), H(eq), H(mu), H(pi), term, tr_h, H(tv_h), H(b), gamma,
