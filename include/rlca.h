@@ -75,7 +75,12 @@
  *          (two's-complement wrap).  Arrays may instead be stored as bf16 or
  *          fp16 (rlca_dtype; the summary's §9 defers bfloat16 I/O): they are
  *          widened exactly to fp32 on load and every output is rounded once,
- *          to nearest even, on store.
+ *          to nearest even, on store.  These statements assume a contracting
+ *          recurrence, |beta_t| <= 1: trace clips c_bar above 1 (V-Trace,
+ *          Retrace) or affine coefficients beyond +-1 let products of beta
+ *          grow, and rounding errors grow with them (any fp32 evaluation
+ *          order, the sequential one included); 16-bit storage may then
+ *          overflow.
  */
 #ifndef RLCA_H
 #define RLCA_H
