@@ -709,7 +709,8 @@ def main():
         "calls": calls_out,
         "full_call_us": {k: round(v * 1e3, 3) for k, v in res["protocol_ms"].items()},
         "copy_ceiling": {"gbs": round(res["copy_gbs"], 1), "bytes": res["copy_bytes"],
-                         "kind": "torch device copy, cold rotation, same bytes moved"},
+                         "kind": "torch device copy, cold rotation, same bytes moved",
+                         "value_over_copy": round(value / res["copy_gbs"], 4)},
         "roofline": {
             "kernel": dom_name,
             "bound": "hbm",

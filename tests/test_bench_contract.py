@@ -52,6 +52,7 @@ def test_bench_prints_one_json_line(gpu_device):
     assert d["n_gpus"] == 1 and d["steps"] == 20 and d["warmup"] == 2
     assert d["unit"] == "GB/s" and d["value"] > 0 and d["dtype"] == "f32"
     assert d["config"]["workload"] == "gae_td_4096x128"
+    assert d["copy_ceiling"]["value_over_copy"] > 0
     r = d["roofline"]
     assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
     assert r["frac"] == pytest.approx(r["achieved"] / r["peak"], abs=1e-4)
