@@ -1,10 +1,11 @@
-"""Seeded random batches through rlca_run_batch: 1 to 40 calls of random ops
-and shapes (short and long rows, T % 4 != 0, few long rows that take the
-chunked path, empty calls), with random truncation, bootstrap, reset
-conventions and directions.  Every member is checked against the fp64
-oracle (1e-4 * (1 + |o|), int32 exact) and bit for bit against the same call
-made alone, as in test_batch_gpu.py: the grouping (classes, workgroup
-ranges, launches of at most 14 calls) must not change any result."""
+"""Seeded random batches through rlca_run_batch: 1 to 64 calls (the limit)
+of random ops and shapes (short and long rows, T % 4 != 0, few long rows
+that take the chunked path, empty calls), with random truncation,
+bootstrap, reset conventions and directions.  Every member is checked
+against the fp64 oracle (1e-4 * (1 + |o|), int32 exact) and bit for bit
+against the same call made alone, as in test_batch_gpu.py: the grouping
+(classes, workgroup ranges, launches of at most 14 calls) must not change
+any result."""
 import numpy as np
 import pytest
 import torch
@@ -21,7 +22,7 @@ LENGTHS = [1, 2, 3, 4, 16, 37, 64, 127, 128, 129, 255, 256, 257, 300, 511, 512, 
 
 def random_members(rng, device):
     members = []
-    for _ in range(int(rng.integers(1, 41))):
+    for _ in range(int(rng.integers(1, 65))):
         op = str(rng.choice(OPS))
         u = rng.random()
         if u < 0.1:      # few long rows: the chunked path
