@@ -67,7 +67,12 @@
  *            RLCA_ERR_HIP            a kernel launch failed (its hipError_t)
  *          num_envs * T == 0 is a valid no-op.  Faults inside the kernel
  *          surface at the caller's next synchronisation, as usual in HIP.
- *          Non-finite inputs propagate; they are not trapped.
+ *          Non-finite inputs are not trapped; they propagate inside their
+ *          episode segment only.  A chain cut (a terminated or truncated
+ *          step, a row end, a forward reset, a beta of 0) stops them: a NaN
+ *          or infinity in one row never reaches another row, and never
+ *          crosses an episode boundary within its row.  A NaN log-
+ *          probability gives a NaN importance weight (not a clamped one).
  * Numerics: fp32 arithmetic throughout (the summary's §4 requires float32
  *          scans); the scan reassociates the recurrence (associativity,
  *          summary §5), so results match a sequential fp64 evaluation to

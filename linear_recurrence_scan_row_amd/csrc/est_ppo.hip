@@ -67,7 +67,7 @@ __device__ __forceinline__ float ppo_term(float a, float lp_new, float lp_old, f
                                           float neg_inv_m, float &grad) {
     const float rho = expf(lp_new - lp_old);
     const float unclipped = rho * a;
-    const float clipped = fminf(fmaxf(rho, lo), hi) * a;
+    const float clipped = clip_to(rho, lo, hi) * a;  // a NaN ratio stays NaN
     const bool take = unclipped <= clipped;
     grad = take ? unclipped * neg_inv_m : 0.f;
     return take ? unclipped : clipped;

@@ -378,10 +378,17 @@ __device__ __forceinline__ void step_positions(const Window &w, uint32_t off, ui
     }
 }
 
+// NaN-propagating clip and minimum (fminf / fmaxf would return the other
+// operand and turn a NaN log-probability into a plausible ratio): a NaN
+// input yields a NaN coefficient, kept inside its episode segment.
+__device__ __forceinline__ float clip_to(float x, float lo, float hi) {
+    x = x > hi ? hi : x;
+    return x < lo ? lo : x;
+}
+__device__ __forceinline__ float min_keep_nan(float bound, float x) { return bound < x ? bound : x; }
+
 __device__ __forceinline__ float importance_ratio(float target_logp, float behaviour_logp) {
-    const float l = fminf(fmaxf(target_logp - behaviour_logp, -RLCA_LOG_RATIO_CLIP),
-                          RLCA_LOG_RATIO_CLIP);
-    return expf(l);
+    return expf(clip_to(target_logp - behaviour_logp, -RLCA_LOG_RATIO_CLIP, RLCA_LOG_RATIO_CLIP));
 }
 
 // fp64 DPP step: x plus the value of the lane CTRL selects (0 where there
@@ -651,11 +658,11 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
             if constexpr (EST == kVtrace || EST == kRetrace) {
 #pragma unroll
                 for (int i = 0; i < kK; ++i)
-                    c[i] = p.lambda * fminf(p.c_bar, importance_ratio(pi[i], mu[i]));
+                    c[i] = p.lambda * min_keep_nan(p.c_bar, importance_ratio(pi[i], mu[i]));
             }
             if constexpr (EST == kRetrace) {
                 const float c_first =
-                    p.lambda * fminf(p.c_bar, importance_ratio(pi_first, mu_first));
+                    p.lambda * min_keep_nan(p.c_bar, importance_ratio(pi_first, mu_first));
                 c_next = from_lower_lane(c[0], c_first);
                 eq_next = from_lower_lane(eq[0], eq_first);
                 if (halo_from_memory) {
@@ -683,7 +690,7 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
                     b = k ? gamma : 0.f;
                 } else if constexpr (EST == kVtrace) {
                     const float vn = i + 1 < kK ? v[i + 1] : v_next;
-                    const float rho = fminf(p.rho_bar, importance_ratio(pi[i], mu[i]));
+                    const float rho = min_keep_nan(p.rho_bar, importance_ratio(pi[i], mu[i]));
                     a = rho * (r[i] + gamma * (k ? vn : succ[i]) - v[i]);
                     b = k ? gamma * c[i] : 0.f;
                     x = k ? gamma * rho : 0.f;  // pg_t = alpha_t + gamma rho_t A_{t+1}
@@ -691,10 +698,11 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
                     // the decay uses the next step's trace coefficient
                     const float cn = i + 1 < kK ? c[i + 1] : c_next;
                     const float en = i + 1 < kK ? eq[i + 1] : eq_next;
-                    a = r[i] + gamma * (k ? en : succ[i]) - v[i];
+                    x = r[i] + gamma * (k ? en : succ[i]);  // Q^ret_t - gamma c_{t+1} A_{t+1}
+                    a = x - v[i];
                     b = k ? gamma * cn : 0.f;
                 } else {  // caller's (alpha, beta); the row's carry enters at t = T-1
-                    a = k ? r[i] : r[i] + v[i] * succ[i];
+                    a = k ? r[i] : apply_map(r[i], v[i], succ[i]);
                     b = k ? v[i] : 0.f;
                 }
                 alpha[i] = valid[i] ? a : 0.f;
@@ -706,8 +714,10 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
             float fa = 0.f, fb = 1.f;  // identity; step i applied after the later steps
 #pragma unroll
             for (int i = kK - 1; i >= 0; --i) {
-                fa = alpha[i] + beta[i] * fa;
-                fb = beta[i] * fb;
+                float a_i = alpha[i], b_i = beta[i];
+                compose(a_i, b_i, fa, fb);
+                fa = a_i;
+                fb = b_i;
             }
             if constexpr (MODE == kChunkAggregate) {
                 // hand the chunk's map to the chunk-carry pass (the earliest
@@ -732,15 +742,17 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
 #pragma unroll
                 for (int i = kK - 1; i >= 0; --i) {
                     const float An = A;  // A_{t+1}
-                    A = alpha[i] + beta[i] * An;
+                    A = apply_map(alpha[i], beta[i], An);
                     if constexpr (EST == kGae) {
                         o0[i] = A;
                         o1[i] = A + v[i];
                     } else if constexpr (EST == kVtrace) {
                         o0[i] = v[i] + A;
-                        o1[i] = alpha[i] + aux[i] * An;
+                        o1[i] = apply_map(alpha[i], aux[i], An);
                     } else if constexpr (EST == kRetrace) {
-                        o0[i] = v[i] + A;
+                        // Q^ret_t = r_t + gamma E Q_{t+1} + beta_t A_{t+1}, without
+                        // the Q_t that alpha_t subtracts and A_t + Q_t would add back
+                        o0[i] = apply_map(aux[i], beta[i], An);
                         o1[i] = 0.f;
                     } else {
                         o0[i] = A;
@@ -876,7 +888,7 @@ __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint3
                     a = x[i];
                     b = reset ? V(0) : decay;
                 } else {
-                    a = start[i] ? x[i] + bt[i] * row_carry[i] : x[i];
+                    a = start[i] ? apply_map(x[i], bt[i], row_carry[i]) : x[i];
                     b = start[i] ? V(0) : bt[i];
                 }
                 alpha[i] = valid[i] ? a : V(0);
@@ -885,8 +897,10 @@ __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint3
             V fa = V(0), fb = V(1);
 #pragma unroll
             for (int i = 0; i < kK; ++i) {
-                fa = alpha[i] + beta[i] * fa;
-                fb = beta[i] * fb;
+                V a_i = alpha[i], b_i = beta[i];
+                compose(a_i, b_i, fa, fb);
+                fa = a_i;
+                fb = b_i;
             }
             if constexpr (MODE == kChunkAggregate) {
                 V ta, tb;
@@ -906,7 +920,7 @@ __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint3
                 V o[kK];
 #pragma unroll
                 for (int i = 0; i < kK; ++i) {
-                    A = alpha[i] + beta[i] * A;
+                    A = apply_map(alpha[i], beta[i], A);
                     o[i] = A;
                 }
                 store_steps<VEC>(out + base, o, off, L, sk, p.geo.scatter != 0);

@@ -43,10 +43,31 @@ __device__ __forceinline__ V from_bits(int x) {
     return __builtin_bit_cast(V, x);
 }
 
+// Map arithmetic with chain cuts.  A step with beta = 0 severs the chain: its
+// map is x -> alpha whatever x is, and so is every composition that contains
+// it (summary §5 Correctness analysis).  IEEE arithmetic gives that only for
+// finite x (0 * NaN and 0 * inf are NaN), so the float forms select instead
+// of multiplying by zero: a NaN or infinity on the far side of an episode
+// boundary, or in another row of the tile, stays there.  For finite values
+// the results are the same.  One test of the later map's beta serves both
+// halves of a composition: when that beta is NaN the composed value is NaN
+// already, so a NaN composed beta changes nothing.  The int32 prefix sums
+// (uint32 here) have no NaN and keep plain arithmetic.
+__device__ __forceinline__ float apply_map(float a, float b, float x) {
+    return b == 0.f ? a : a + b * x;
+}
+__device__ __forceinline__ uint32_t apply_map(uint32_t a, uint32_t b, uint32_t x) {
+    return a + b * x;
+}
+
 // (a, b) <- (a, b) after (pa, pb): the map of a later run in scan order
 // applied after the map of the earlier run.
-template <typename V>
-__device__ __forceinline__ void compose(V &a, V &b, V pa, V pb) {
+__device__ __forceinline__ void compose(float &a, float &b, float pa, float pb) {
+    const bool cut = b == 0.f;
+    a = cut ? a : a + b * pa;
+    b = cut ? b : b * pb;
+}
+__device__ __forceinline__ void compose(uint32_t &a, uint32_t &b, uint32_t pa, uint32_t pb) {
     a = a + b * pa;
     b = b * pb;
 }
@@ -104,15 +125,15 @@ __device__ __forceinline__ V block_carry_in(V a, V b, V carry_in, V *lds_a, V *l
     const V eb = from_lower_lane(b, V(1));
     if constexpr (WAVE_LOCAL) {
         carry_out = V(0);
-        return ea + eb * V(0);
+        return apply_map(ea, eb, V(0));
     }
     if constexpr (NW == 1) {
         // One wave: its total is lane 63's inclusive value; no LDS, no
         // barrier (so waves of one workgroup may run unrelated tiles).
         const V ta = from_bits<V>(__builtin_amdgcn_readlane(as_bits(a), kWave - 1));
         const V tb = from_bits<V>(__builtin_amdgcn_readlane(as_bits(b), kWave - 1));
-        carry_out = ta + tb * carry_in;
-        return ea + eb * carry_in;
+        carry_out = apply_map(ta, tb, carry_in);
+        return apply_map(ea, eb, carry_in);
     }
     if (lane == kWave - 1) {
         lds_a[parity * NW + w] = a;
@@ -124,10 +145,10 @@ __device__ __forceinline__ V block_carry_in(V a, V b, V carry_in, V *lds_a, V *l
 #pragma unroll
     for (int j = 0; j < NW; ++j) {
         if (j == w) xw = x;
-        x = lds_a[parity * NW + j] + lds_b[parity * NW + j] * x;
+        x = apply_map(lds_a[parity * NW + j], lds_b[parity * NW + j], x);
     }
     carry_out = x;
-    return ea + eb * xw;
+    return apply_map(ea, eb, xw);
 }
 
 // The map of the whole tile: the NW wave totals composed in scan order.  Used
@@ -146,8 +167,10 @@ __device__ __forceinline__ void block_total(V a, V b, V *lds_a, V *lds_b, V &ta,
     tb = V(1);
 #pragma unroll
     for (int j = 0; j < NW; ++j) {
-        ta = lds_a[j] + lds_b[j] * ta;
-        tb = lds_b[j] * tb;
+        V a_j = lds_a[j], b_j = lds_b[j];
+        compose(a_j, b_j, ta, tb);
+        ta = a_j;
+        tb = b_j;
     }
 }
 

@@ -290,6 +290,14 @@ void oracle_episodic_prefix_sum_i32(const int32_t *x, const uint8_t *flags, int 
     }
 }
 
+/* One step of the recurrence.  beta = 0 severs the chain: the step's value
+ * is alpha whatever the carried value is, NaN or infinite included (summary
+ * §5 Correctness analysis: a step with beta = 0 composes to (alpha, 0)). */
+static double affine_step(float a, float b, double carried)
+{
+    return b == 0.0f ? (double)a : (double)a + (double)b * carried;
+}
+
 /* The recurrence itself, one step at a time from the carried end. */
 void oracle_affine_scan(const float *alpha, const float *beta, const float *carry, int direction,
                         int64_t num_envs, int64_t T, double *out)
@@ -299,12 +307,12 @@ void oracle_affine_scan(const float *alpha, const float *beta, const float *carr
         double A = carry != NULL ? (double)carry[n] : 0.0;
         if (direction == 0) {
             for (int64_t t = T - 1; t >= 0; --t) {
-                A = (double)a[t] + (double)b[t] * A;
+                A = affine_step(a[t], b[t], A);
                 out[n * T + t] = A;
             }
         } else {
             for (int64_t t = 0; t < T; ++t) {
-                A = (double)a[t] + (double)b[t] * A;
+                A = affine_step(a[t], b[t], A);
                 out[n * T + t] = A;
             }
         }

@@ -454,6 +454,21 @@ def test_affine_scan_special_cases():
     close(oracle.affine_scan(a, one, None, oracle.FORWARD), np.cumsum(a64, axis=1), 1e-13)
 
 
+def test_affine_scan_zero_beta_severs_a_nonfinite_carry():
+    """[PL] §5: a step with beta = 0 composes to (alpha, 0), so nothing from
+    the carried side reaches it, not even a NaN or an infinity.  Hand values,
+    backward: alpha = (1, 2, 3), beta = (0.5, 0, 0.5), carry A_3 = NaN gives
+    A_2 = NaN, A_1 = 2 (cut), A_0 = 1 + 0.5 * 2 = 2; forward with carry
+    A_{-1} = inf and beta = (0, 0.5, 0.5): A_0 = 1, A_1 = 2.5, A_2 = 4.25."""
+    a = np.array([[1.0, 2.0, 3.0]], np.float32)
+    out = oracle.affine_scan(a, np.array([[0.5, 0.0, 0.5]], np.float32),
+                             np.array([np.nan], np.float32), oracle.BACKWARD)
+    assert out[0, 0] == 2.0 and out[0, 1] == 2.0 and np.isnan(out[0, 2])
+    out = oracle.affine_scan(a, np.array([[0.0, 0.5, 0.5]], np.float32),
+                             np.array([np.inf], np.float32), oracle.FORWARD)
+    assert out.tolist() == [[1.0, 2.5, 4.25]]
+
+
 def test_affine_scan_reproduces_the_estimators():
     """The generic scan fed with hand-built GAE coefficients gives the GAE
     oracle's advantages; forward with (x, gamma*lambda*(1 - start)) gives the
