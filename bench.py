@@ -293,17 +293,30 @@ def run_gpu(args, name, cfg, host):
             run_step(s)
         torch.cuda.synchronize()
 
-        # whole-step time
+        # whole-step time.  The timed loop does as little host work per step
+        # as it can (launches bound beforehand in one flat list, statuses
+        # checked after the loop), so that on a slow host the step time
+        # measures the library's launches rather than this loop.
+        if args.launch == "graph":
+            order = [(graphs[(warm + s) % steps_per_cycle].replay, ())
+                     for s in range(timed_steps)]
+        else:
+            order = [fa for s in range(timed_steps) for fa in plan[(warm + s) % steps_per_cycle]]
+        statuses = []
+        record = statuses.append
         t0 = time.perf_counter()
         e_start = torch.cuda.Event(enable_timing=True)
         e_end = torch.cuda.Event(enable_timing=True)
         e_start.record(stream)
-        for s in range(timed_steps):
-            run_step(warm + s)
+        for fn, a in order:
+            record(fn(*a))
         e_end.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         step_ms = e_start.elapsed_time(e_end) / timed_steps
+        if args.launch != "graph":
+            for (fn, _), st in zip(order, statuses):
+                check(st, fn.__name__)
 
         # per-kernel device time: each call variant (and with --launch batch
         # the grouped launch of the whole step) launched back to back `reps`
@@ -315,14 +328,18 @@ def run_gpu(args, name, cfg, host):
             for i in range(5):
                 fn, a = bound[i % len(bound)]
                 check(fn(*a), fn.__name__)
+            order = [bound[i % len(bound)] for i in range(reps)]
+            statuses = []
+            record = statuses.append
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            for i in range(reps):
-                fn, a = bound[i % len(bound)]
-                check(fn(*a), fn.__name__)
+            for fn, a in order:
+                record(fn(*a))
             e1.record(stream)
             torch.cuda.synchronize()
+            for (fn, _), st in zip(order, statuses):
+                check(st, fn.__name__)
             return e0.elapsed_time(e1) / reps
 
         per_call_ms = [back_to_back([bind_call(calls[c], sets[i], h) for i in range(nsets)])
