@@ -610,26 +610,40 @@ def run_sweep(args):
                                                          h)
 
                 plan = [bound(s) for s in sets]
+                batch = max(20, min(400, int(2e9 // call_bytes)))
+                trials = []
                 with torch.cuda.stream(stream):
-                    for i in range(3):
-                        fn, a = plan[i % nsets]
-                        assert fn(*a) == 0
-                    batch = max(20, min(400, int(2e9 // call_bytes)))
-                    e0 = torch.cuda.Event(enable_timing=True)
-                    e1 = torch.cuda.Event(enable_timing=True)
-                    e0.record(stream)
-                    for i in range(batch):
+                    # warm up for a quarter of a trial, then three trials of
+                    # `batch` back-to-back launches; the fastest trial is
+                    # reported (the pages' protocol also keeps a minimum), so
+                    # that a transient stall of the host or the GPU during
+                    # one trial does not stand for the kernel
+                    for i in range(max(20, batch // 4)):
                         fn, a = plan[i % nsets]
                         if fn(*a) != 0:
                             raise RuntimeError(f"{name} {n}x{t}: launch failed")
-                    e1.record(stream)
                     torch.cuda.synchronize()
-                us = e0.elapsed_time(e1) / batch * 1e3
+                    for _ in range(3):
+                        order = [plan[i % nsets] for i in range(batch)]
+                        statuses = []
+                        record = statuses.append
+                        e0 = torch.cuda.Event(enable_timing=True)
+                        e1 = torch.cuda.Event(enable_timing=True)
+                        e0.record(stream)
+                        for fn, a in order:
+                            record(fn(*a))
+                        e1.record(stream)
+                        torch.cuda.synchronize()
+                        if any(statuses):
+                            raise RuntimeError(f"{name} {n}x{t}: launch failed")
+                        trials.append(e0.elapsed_time(e1) / batch * 1e3)
+                us = min(trials)
                 gbs = call_bytes / (us * 1e-6) / 1e9
                 print(json.dumps({"sweep": name, "num_envs": n, "T": t, "us": round(us, 3),
                                   "bytes": call_bytes, "gbs": round(gbs, 1),
                                   "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-                                  "env_steps_per_s": nt / (us * 1e-6), "sets": nsets}),
+                                  "env_steps_per_s": nt / (us * 1e-6), "sets": nsets,
+                                  "trials_us": [round(x, 3) for x in trials]}),
                       flush=True)
                 del sets
                 torch.cuda.empty_cache()
