@@ -21,7 +21,11 @@
  *          torch tensor's data_ptr()) owned by the caller.  The library
  *          allocates nothing, keeps no mutable global state and never
  *          synchronizes: work is enqueued on `stream` and buffers must stay
- *          alive until the stream has passed the call.
+ *          alive until the stream has passed the call.  With no state
+ *          between calls, any entry point may be called from several host
+ *          threads at once, on one stream or on several; only calls whose
+ *          outputs overlap each other or another call's inputs, with nothing
+ *          ordering them, race.
  * Layout:  per-step arrays are dense row-major [num_envs, T]; element (n, t)
  *          is at n*T + t.  `bootstrap` is [num_envs].  Real-valued and int32
  *          data must be aligned to its element size.  Flags are one byte per
