@@ -9,11 +9,13 @@
  *             prefix sums)
  * ("rl-triton: High-Performance Triton GPU Kernels for Reinforcement Learning
  * Credit Assignment", paperlayer.ai summary, §1 Introduction and §3.1 Shared
- * scan formulation).  Each call is one kernel launch that reads its inputs
- * from HBM once and writes each output once -- except for fewer than 64
- * rows of more than 4096 steps, where each row is split into chunks that run
- * in parallel: three launches, inputs read twice, and the first output array
- * holds the chunk hand-off values until the last launch overwrites them.
+ * scan formulation).  Each estimator call is one kernel launch that reads
+ * its inputs from HBM once and writes each output once -- except for fewer
+ * than 64 rows of more than 4096 steps, where each row is split into chunks
+ * that run in parallel: three launches, inputs read twice, and the first
+ * output array holds the chunk hand-off values until the last launch
+ * overwrites them.  The fused consumers of GAE at the end of this header
+ * add one small launch each, which finishes their reduction.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -296,13 +298,17 @@ rlca_status rlca_run_batch(const rlca_call *calls, int count, hipStream_t stream
  * The summary's §9 (Discussion and Future Work) names fused loss operations
  * as the next step for the library; these two calls fuse the usual PPO
  * consumers of the advantages into the scan's epilogue and into one
- * streaming pass.  Both reduce in a fixed order (reproducible bit for bit)
- * through a caller-owned device workspace, whose size the *_workspace_size
- * call returns (0 for an empty rollout or invalid sizes); its contents on
- * entry do not matter and are overwritten.  workspace, stats and loss must
- * be 8-byte aligned; RLCA_ERR_INVALID_SIZE if workspace_bytes is too small;
- * RLCA_ERR_ALIASING if the workspace, stats or loss overlap any other array
- * of the call.  An empty rollout (num_envs * T == 0) writes nothing. */
+ * streaming pass.  Each is two launches: the pass, which leaves one partial
+ * sum per workgroup in a caller-owned device workspace, then a one-workgroup
+ * launch that adds the partials in a fixed order (reproducible bit for
+ * bit).  The *_workspace_size call returns the workspace's size (0 for an
+ * empty rollout or invalid sizes); its contents on entry do not matter and
+ * are overwritten.  The workspace is written like an output: calls that may
+ * run at the same time need workspaces of their own.  workspace, stats and
+ * loss must be 8-byte aligned; RLCA_ERR_INVALID_SIZE if workspace_bytes is
+ * too small; RLCA_ERR_ALIASING if the workspace, stats or loss overlap any
+ * other array of the call.  An empty rollout (num_envs * T == 0) writes
+ * nothing. */
 size_t rlca_gae_stats_workspace_size(int64_t num_envs, int64_t T);
 
 /* rlca_gae (fp32) that also reduces the advantages it computes: stats is
