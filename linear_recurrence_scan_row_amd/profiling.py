@@ -12,6 +12,11 @@ credit-assignment kernels.
       by what they read for a plain device copy of N bytes (N read + N
       written) captured in the same runs: on gfx950 FETCH_SIZE reads about
       half of the bytes a copy really fetches, WRITE_SIZE reads them exactly.
+
+  python -m linear_recurrence_scan_row_amd.profiling counters DB [DB ...]
+         --kernel SUBSTR [--command CMD ...]
+      median per dispatch of every counter in ``--pmc`` runs, for the kernels
+      whose name contains SUBSTR, and per wave where the runs hold SQ_WAVES.
 """
 from __future__ import annotations
 
@@ -55,6 +60,24 @@ def counter_values(db: str, counter: str):
         "order by dispatch_id", (counter,)).fetchall()
 
 
+def counter_medians(dbs, kernel):
+    """{kernel name: {counter: (dispatches, median value per dispatch)}}."""
+    per = {}
+    for db in dbs:
+        con = sqlite3.connect(db)
+        for name, counter, value in con.execute(
+                "select kernel_name, counter_name, value from counters_collection"):
+            if kernel in name:
+                per.setdefault(name.split("(")[0], {}).setdefault(counter, []).append(value)
+    out = {}
+    for name, counters in per.items():
+        out[name] = {}
+        for counter, values in counters.items():
+            values.sort()
+            out[name][counter] = (len(values), values[len(values) // 2])
+    return out
+
+
 def traffic(fetch_db, write_db, kernel, copy_bytes):
     fetch = counter_values(fetch_db, "FETCH_SIZE")
     write = counter_values(write_db, "WRITE_SIZE")
@@ -96,7 +119,26 @@ def main(argv=None):
     t.add_argument("--fetch-command", default="")
     t.add_argument("--write-command", default="")
     t.add_argument("--out", default="")
+    c = sub.add_parser("counters")
+    c.add_argument("dbs", nargs="+")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--command", action="append", default=[])
     a = ap.parse_args(argv)
+    if a.cmd == "counters":
+        lines = [f"command: {cmd}" for cmd in a.command]
+        lines.append(f"source_digest: {source_digest()}")
+        for name, counters in sorted(counter_medians(a.dbs, a.kernel).items()):
+            waves = counters.get("SQ_WAVES", (0, 0.0))[1]
+            lines += ["", f"kernel: {name}", "",
+                      "| counter | dispatches | median per dispatch | per wave |", "|---|---|---|---|"]
+            for counter, (n, v) in sorted(counters.items()):
+                # counters summed over waves (instructions, wave-cycles); the
+                # others (SQ_BUSY_CYCLES and the like) count per engine
+                summed = counter.startswith(("SQ_INSTS", "SQ_ACTIVE", "SQ_WAIT", "SQ_WAVE"))
+                pw = f"{v / waves:.2f}" if waves and summed else ""
+                lines.append(f"| {counter} | {n} | {v:.6g} | {pw} |")
+        print("\n".join(lines))
+        return
     if a.cmd == "stats":
         lines = []
         if a.command:
