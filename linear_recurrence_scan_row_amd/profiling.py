@@ -7,7 +7,8 @@ credit-assignment kernels.
 
   python -m linear_recurrence_scan_row_amd.profiling traffic --fetch DB --write DB
          --kernel SUBSTR --copy-bytes N --algorithmic-bytes B --out FILE [...]
-      HBM bytes per launch of one kernel from a ``--pmc FETCH_SIZE`` run and a
+      HBM bytes per launch of one kernel (or per step of several, --kernel
+      repeated) from a ``--pmc FETCH_SIZE`` run and a
       ``--pmc WRITE_SIZE`` run of the same command.  Both counters are scaled
       by what they read for a plain device copy of N bytes (N read + N
       written) captured in the same runs: on gfx950 FETCH_SIZE reads about
@@ -90,13 +91,21 @@ def traffic(fetch_db, write_db, kernel, copy_bytes):
     cw = [v for d, name, v in write if d in copy_ids]
     fetch_factor = copy_bytes / (1024 * sum(cf) / len(cf))
     write_factor = copy_bytes / (1024 * sum(cw) / len(cw))
-    kf = [v for d, name, v in fetch if kernel in name]
-    kw = [v for d, name, v in write if kernel in name]
-    if not kf or not kw:
-        raise SystemExit(f"kernel {kernel!r} not found in the counter runs")
-    f_kib = sum(kf) / len(kf)
-    w_kib = sum(kw) / len(kw)
-    return dict(dispatches=len(kf), fetch_kib_raw=f_kib, write_kib_raw=w_kib,
+    # one step may launch several kernels: the step's traffic is the sum of
+    # their average traffic per dispatch
+    kernels = [kernel] if isinstance(kernel, str) else list(kernel)
+    f_kib = w_kib = 0.0
+    counts = []
+    for k in kernels:
+        kf = [v for d, name, v in fetch if k in name]
+        kw = [v for d, name, v in write if k in name]
+        if not kf or not kw:
+            raise SystemExit(f"kernel {k!r} not found in the counter runs")
+        f_kib += sum(kf) / len(kf)
+        w_kib += sum(kw) / len(kw)
+        counts.append(str(len(kf)))
+    return dict(dispatches=counts[0] if len(counts) == 1 else " + ".join(counts),
+                fetch_kib_raw=f_kib, write_kib_raw=w_kib,
                 calibration_copy_bytes=copy_bytes, calibration_dispatches=len(copy_ids),
                 fetch_factor=fetch_factor, write_factor=write_factor,
                 traffic_bytes_per_launch=f_kib * 1024 * fetch_factor + w_kib * 1024 * write_factor)
@@ -113,7 +122,8 @@ def main(argv=None):
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
-    t.add_argument("--kernel", required=True)
+    t.add_argument("--kernel", required=True, action="append",
+                   help="kernel name substring; repeat for a step of several launches")
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--algorithmic-bytes", type=int, required=True)
     t.add_argument("--fetch-command", default="")
@@ -152,7 +162,7 @@ def main(argv=None):
         print("\n".join(lines))
         return
     r = traffic(a.fetch, a.write, a.kernel, a.copy_bytes)
-    out = [f"kernel: {a.kernel}",
+    out = [f"kernel: {' + '.join(a.kernel)}",
            f"fetch_command: {a.fetch_command}",
            f"write_command: {a.write_command}"]
     out += [f"{k}: {v:.6g}" if isinstance(v, float) else f"{k}: {v}" for k, v in r.items()]
