@@ -319,3 +319,34 @@ def test_product_package_never_imports_the_oracle():
                 text = open(os.path.join(dirpath, name)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), name
                 assert "liboracle" not in text, name
+
+
+def test_binding_refuses_host_tensors():
+    """No CPU fallback: every op of the binding, batched or not, raises on
+    host tensors before anything reaches the library."""
+    import torch
+
+    import linear_recurrence_scan_row_amd as rl
+
+    n, t = 4, 8
+    r, v = torch.zeros(n, t), torch.zeros(n, t)
+    f = torch.zeros(n, t, dtype=torch.uint8)
+    calls = {
+        "gae": lambda m: m.gae(r, v, f),
+        "td_lambda": lambda m: m.td_lambda(r, v, f),
+        "discounted_returns": lambda m: m.discounted_returns(r, f),
+        "vtrace": lambda m: m.vtrace(r, v, r, v, f),
+        "retrace": lambda m: m.retrace(r, v, v, r, v, f),
+        "eligibility_traces": lambda m: m.eligibility_traces(r, f, rl.RESET_ON_START, 0.9, 0.9),
+        "episodic_prefix_sum": lambda m: m.episodic_prefix_sum(r, f, rl.RESET_ON_START),
+        "affine_scan": lambda m: m.affine_scan(r, v),
+    }
+    for name, call in calls.items():
+        with pytest.raises(ValueError, match="GPU"):
+            call(rl)
+        with pytest.raises(ValueError, match="GPU"):
+            call(rl.Batch())
+    with pytest.raises(ValueError, match="GPU"):
+        rl.gae_stats(r, v, f)
+    with pytest.raises(ValueError, match="GPU"):
+        rl.ppo_clip_loss(r, v, r)
