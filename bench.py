@@ -24,9 +24,14 @@ Measurement:
   * effective GB/s uses the algorithmic byte model: every input array read
     once and every output written once at dense size (fp32 / int32 4 B, bf16
     / fp16 2 B, flags 1 B per step, bootstrap one value per row);
+  * copy_ceiling: a torch device copy moving the step's bytes, cold and back
+    to back, as the attainable ceiling at this size;
   * cpu_baseline: the fp64 sequential oracle on this host, single thread;
     cpu_baseline_all_cores: the same with the rows split over up to 16
     worker processes.
+
+--sweep prints one JSON line per (num_envs, T, estimator) of a size sweep
+instead (three trials per point, the fastest kept).
 """
 from __future__ import annotations
 
