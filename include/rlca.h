@@ -65,8 +65,9 @@
  *                                    num_envs > RLCA_MAX_ENVS, or the byte
  *                                    size of an array overflows
  *            RLCA_ERR_INVALID_VALUE  gamma or lambda outside [0, 1] or not
- *                                    finite, a clip threshold <= 0 or not
- *                                    finite, an unknown enum value
+ *                                    finite, rho_bar <= 0 or not finite,
+ *                                    c_bar outside (0, 1], an unknown enum
+ *                                    value
  *            RLCA_ERR_ALIASING       an output overlaps an input or another
  *                                    output (in-place is not supported)
  *            RLCA_ERR_MISALIGNED     an array is not aligned to its element size
@@ -86,17 +87,18 @@
  *          (two's-complement wrap).  Arrays may instead be stored as bf16 or
  *          fp16 (rlca_dtype; the summary's §9 defers bfloat16 I/O): they are
  *          widened exactly to fp32 on load and every output is rounded once,
- *          to nearest even, on store.  These statements assume a contracting
- *          recurrence, |beta_t| <= 1: trace clips c_bar above 1 (V-Trace,
- *          Retrace) or affine coefficients beyond +-1 let products of beta
- *          grow, and rounding errors grow with them (any fp32 evaluation
- *          order, the sequential one included); 16-bit storage may then
- *          overflow.  Chains that never break (beta = 1 over a whole row: a
- *          prefix sum without resets, gamma = 1 returns without episode
- *          ends) accumulate rounding with their partial sums: over about
- *          10^5 steps of zero-mean data, the error near a zero crossing of
- *          the sums can pass 1e-4 * (1 + |A|), while staying below that of
- *          a sequential fp32 evaluation.
+ *          to nearest even, on store.  Every estimator's coefficient is a
+ *          contraction, 0 <= beta_t <= 1 (gamma, lambda in [0, 1] and trace
+ *          clips c_bar <= 1).  Where a chain that barely decays (beta near 1)
+ *          carries a value across the 256-step waves of the scan, fp32
+ *          rounding of the beta products and of the carried sums would
+ *          build up along the row; such calls (and every generic affine
+ *          scan over rows longer than 256 steps) scan in fp64 and round
+ *          each output once, so chains that never break (a prefix sum
+ *          without resets, gamma = 1 returns) keep their accuracy over the
+ *          row, 131072 steps and more.  Affine coefficients beyond +-1 let
+ *          products of beta grow, and rounding errors grow with them in
+ *          any evaluation order; 16-bit storage may then overflow.
  */
 #ifndef RLCA_H
 #define RLCA_H
@@ -177,7 +179,8 @@ rlca_status rlca_discounted_returns(const float *rewards, const uint8_t *termina
  *   vs_t - V_t = rho_t (r_t + gamma V(s_{t+1}) - V_t) + gamma c_t (vs_{t+1} - V_{t+1})
  *   pg_t = rho_t (r_t + gamma vs_{t+1} - V_t)
  * where at a done step or t = T-1 the successor value replaces V(s_{t+1}) and
- * vs_{t+1}.  lambda = 1 is the IMPALA form.  rho_bar, c_bar > 0.
+ * vs_{t+1}.  lambda = 1 is the IMPALA form.  rho_bar > 0; 0 < c_bar <= 1 (a
+ * trace clip above 1 would make the recurrence expansive). 
  * Writes vs [N,T] and, when non-NULL, pg_advantages [N,T]. */
 rlca_status rlca_vtrace(const float *rewards, const float *values, const float *behaviour_logp,
                         const float *target_logp, const uint8_t *terminated,
@@ -193,7 +196,8 @@ rlca_status rlca_vtrace(const float *rewards, const float *values, const float *
  * q_values[t] = Q(s_t, a_t); expected_q[t] = E_pi Q(s_t, .).  At a done step
  * or t = T-1 the successor value (0 / trunc_values[t] = E_pi Q of the cut
  * state / bootstrap[n] = E_pi Q(s_T, .)) replaces E_pi Q(s_{t+1}, .) and the
- * correction term is dropped.  Writes q_ret [N,T]. */
+ * correction term is dropped.  0 < c_bar <= 1 (Munos et al. truncate the
+ * trace at 1).  Writes q_ret [N,T]. */
 rlca_status rlca_retrace(const float *rewards, const float *q_values, const float *expected_q,
                          const float *behaviour_logp, const float *target_logp,
                          const uint8_t *terminated, const uint8_t *truncated,

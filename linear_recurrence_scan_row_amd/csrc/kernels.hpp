@@ -107,7 +107,8 @@ struct ForwardParams {
     const void *beta;      // kForwardAffine
     const void *carry;     // kForwardAffine: A_{-1} per row, may be null
     void *out;
-    float decay;  // gamma*lambda for traces, 1 for prefix sums
+    float decay;     // gamma*lambda for traces (rounded to fp32), 1 for prefix sums
+    double decay64;  // the same, exact (fp64 product of the fp32 factors): fp64 scans
     Geometry geo;
 };
 
@@ -126,6 +127,7 @@ struct LaunchShape {
     uint32_t phase, out0_phase;  // skewed path: as in Geometry
     bool scatter;                // skewed path: as in Geometry
     bool chunked;     // few long rows: the three chunk-mode launches
+    bool f64;         // fp64 scan (ScanOf): rows span waves with beta near 1; chunked
 };
 
 // ---------------------------------------------------------------- memory access
@@ -249,17 +251,40 @@ __device__ __forceinline__ void store_steps(S *__restrict__ p, const E (&x)[kK],
     }
 }
 
-// Chunk modes hand two scan values per chunk between launches through the
-// chunk's first output elements, as raw 32-bit words whatever S is: for
-// 2-byte S from the chunk's first element at a 4-byte aligned address (the
-// output's phase, out_phase, is its start's element index mod K).  Every
-// chunk but the last in scan order holds both words (it spans thousands of
-// steps); the last receives one (its 1 or 2 elements lie in the chunk: with
-// 2-byte S and an odd start it spans at least 4 steps).
+// Chunk modes hand values between launches through the chunk's first output
+// elements, as raw 32-bit words whatever S is: for 2-byte S from the chunk's
+// first element at a 4-byte aligned address (the output's phase, out_phase,
+// is its start's element index mod K).  Every chunk but the last in scan
+// order holds its map, two scan values (four words for fp64 scans: it spans
+// thousands of steps); the last receives only its carry, one word (its 1 or
+// 2 elements lie in the chunk: with 2-byte S and an odd start it spans at
+// least 4 steps).
 template <typename E, typename S>
 __device__ __forceinline__ E *chunk_slot(void *out, int64_t base, uint32_t out_phase) {
     if constexpr (sizeof(S) == 2) base += (base + out_phase) & 1;
     return reinterpret_cast<E *>(static_cast<S *>(out) + base);
+}
+
+// A chunk's map (a, b) as scan values C, each as raw 32-bit words (two for
+// fp64), from word 0 of the chunk's slot; the carry comes back in word 0 as
+// one value of the kernel's value type.
+template <typename C>
+__device__ __forceinline__ void put_words(uint32_t *w, C x) {
+    if constexpr (sizeof(C) == 4) {
+        w[0] = __builtin_bit_cast(uint32_t, x);
+    } else {
+        const uint64_t u = __builtin_bit_cast(uint64_t, x);
+        w[0] = (uint32_t)u;
+        w[1] = (uint32_t)(u >> 32);
+    }
+}
+template <typename C>
+__device__ __forceinline__ C get_words(const uint32_t *w) {
+    if constexpr (sizeof(C) == 4) {
+        return __builtin_bit_cast(C, w[0]);
+    } else {
+        return __builtin_bit_cast(C, ((uint64_t)w[1] << 32) | w[0]);
+    }
 }
 
 // Chunk apply mode reads its carry from the chunk's first slot: an output
@@ -533,11 +558,15 @@ __device__ __forceinline__ void adopt_lead(ForwardParams &p, LEAD_ARGS) {
 // Groups g, g + g_stride, ... of the launch run through one workgroup.
 // STATS: also sum out0 and its square over the workgroup's valid steps (in
 // fp64) and store the pair in stats_partials[2 * blockIdx.x ...].
+// F64: the scan runs in fp64 (ScanOf; every chunk mode does); outputs are
+// rounded to fp32 once.
 template <int EST, bool TRUNC, int VEC, int NW, bool WAVE_LOCAL, int MODE, typename S,
-          bool STATS = false>
+          bool STATS = false, bool F64 = false>
 __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uint32_t g_stride) {
     static_assert(!STATS || MODE != kChunkAggregate, "statistics come from the outputs");
-    static_assert(MODE == kFull || (NW == kChunkWaves && !WAVE_LOCAL), "a chunk is one tile");
+    static_assert(MODE == kFull || (NW == kChunkWaves && !WAVE_LOCAL && F64),
+                  "a chunk is one tile, scanned in fp64");
+    typedef typename ScanOf<float, F64>::type SV;
     typedef const S *__restrict__ In;
     const In rewards = static_cast<In>(p.rewards), values = static_cast<In>(p.values);
     const In expected_q = static_cast<In>(p.expected_q);
@@ -550,7 +579,7 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
     double sum = 0.0, sum_sq = 0.0;  // STATS
     constexpr uint32_t kTile = NW * kWave * kK;
     constexpr bool kFlags = EST != kAffineBackward;
-    __shared__ float lds_a[2 * NW], lds_b[2 * NW];
+    __shared__ SV lds_a[2 * NW], lds_b[2 * NW];
     const int lane = threadIdx.x & (kWave - 1);
     const int w = NW == 1 ? 0 : threadIdx.x / kWave;  // one-wave tiles: each wave alone
     const uint32_t chunk = (NW - 1 - w) * kWave + (kWave - 1 - lane);
@@ -571,9 +600,9 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
         const uint32_t ntiles = MODE == kFull ? (L + kTile - 1) / kTile : 1u;
         // A just after the current tile: 0 at a row end (edges live in alpha),
         // or the carry the chunk-carry pass left in the chunk's first slot.
-        float carry = 0.f;
+        SV carry = SV(0);
         if constexpr (MODE == kChunkApply)  // issued ahead of the tile's loads
-            carry = chunk_slot<float, S>(p.out0, win.base, p.geo.out0_phase)[0];
+            carry = SV(chunk_slot<float, S>(p.out0, win.base, p.geo.out0_phase)[0]);
 
         for (uint32_t it = 0; it < ntiles; ++it) {
             const uint32_t off = (ntiles - 1 - it) * kTile + chunk * kK;
@@ -649,72 +678,87 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
             }
 
             // ---- 3. halo: the first step of the next chunk in time, from lane - 1
-            float v_next = 0.f, c_next = 0.f, eq_next = 0.f;
+            float v_next = 0.f, eq_next = 0.f;
             if constexpr (EST == kGae || EST == kTdLambda || EST == kVtrace) {
                 v_next = from_lower_lane(v[0], v_first);
                 if (halo_from_memory) v_next = v_first;
             }
-            float c[kK];
+            // clipped importance ratio min(c_bar, ratio_t); c_t = lambda * m_t
+            float m[kK];
             if constexpr (EST == kVtrace || EST == kRetrace) {
 #pragma unroll
                 for (int i = 0; i < kK; ++i)
-                    c[i] = p.lambda * min_keep_nan(p.c_bar, importance_ratio(pi[i], mu[i]));
+                    m[i] = min_keep_nan(p.c_bar, importance_ratio(pi[i], mu[i]));
             }
+            float m_next = 0.f;
             if constexpr (EST == kRetrace) {
-                const float c_first =
-                    p.lambda * min_keep_nan(p.c_bar, importance_ratio(pi_first, mu_first));
-                c_next = from_lower_lane(c[0], c_first);
+                const float m_first = min_keep_nan(p.c_bar, importance_ratio(pi_first, mu_first));
+                m_next = from_lower_lane(m[0], m_first);
                 eq_next = from_lower_lane(eq[0], eq_first);
                 if (halo_from_memory) {
-                    c_next = c_first;
+                    m_next = m_first;
                     eq_next = eq_first;
                 }
             }
 
-            // ---- 4. coefficients in registers
-            float alpha[kK], beta[kK], aux[kK];
+            // ---- 4. coefficients in registers.  The fp32 scans form beta_t
+            // in fp32 (gamma * (lambda * m_t) for the importance-weighted
+            // ones); the fp64 scans form it in fp64 from the same fp32
+            // factors, so that a chain with beta near 1 runs on the exact
+            // product of the parameters (such chains amplify a one-ulp
+            // change of beta by orders of magnitude).
+            float alpha[kK], aux[kK];
+            SV beta[kK];
+            const SV decay_s = SV(gamma) * SV(p.lambda);  // GAE, TD(lambda)
 #pragma unroll
             for (int i = 0; i < kK; ++i) {
                 const bool k = cont[i];
-                float a, b, x = 0.f;
+                float a, x = 0.f;
+                SV b;
                 if constexpr (EST == kGae) {
                     const float vn = i + 1 < kK ? v[i + 1] : v_next;
                     a = r[i] + gamma * (k ? vn : succ[i]) - v[i];
-                    b = k ? gamma * p.lambda : 0.f;
+                    b = k ? decay_s : SV(0);
                 } else if constexpr (EST == kTdLambda) {
                     const float vn = i + 1 < kK ? v[i + 1] : v_next;
                     a = k ? r[i] + gamma * (1.f - p.lambda) * vn : r[i] + gamma * succ[i];
-                    b = k ? gamma * p.lambda : 0.f;
+                    b = k ? decay_s : SV(0);
                 } else if constexpr (EST == kDiscounted) {
                     a = k ? r[i] : r[i] + gamma * succ[i];
-                    b = k ? gamma : 0.f;
+                    b = k ? SV(gamma) : SV(0);
                 } else if constexpr (EST == kVtrace) {
                     const float vn = i + 1 < kK ? v[i + 1] : v_next;
                     const float rho = min_keep_nan(p.rho_bar, importance_ratio(pi[i], mu[i]));
                     a = rho * (r[i] + gamma * (k ? vn : succ[i]) - v[i]);
-                    b = k ? gamma * c[i] : 0.f;
+                    if constexpr (F64)
+                        b = k ? decay_s * SV(m[i]) : SV(0);
+                    else
+                        b = k ? gamma * (p.lambda * m[i]) : 0.f;
                     x = k ? gamma * rho : 0.f;  // pg_t = alpha_t + gamma rho_t A_{t+1}
                 } else if constexpr (EST == kRetrace) {
                     // the decay uses the next step's trace coefficient
-                    const float cn = i + 1 < kK ? c[i + 1] : c_next;
+                    const float mn = i + 1 < kK ? m[i + 1] : m_next;
                     const float en = i + 1 < kK ? eq[i + 1] : eq_next;
                     x = r[i] + gamma * (k ? en : succ[i]);  // Q^ret_t - gamma c_{t+1} A_{t+1}
                     a = x - v[i];
-                    b = k ? gamma * cn : 0.f;
+                    if constexpr (F64)
+                        b = k ? decay_s * SV(mn) : SV(0);
+                    else
+                        b = k ? gamma * (p.lambda * mn) : 0.f;
                 } else {  // caller's (alpha, beta); the row's carry enters at t = T-1
                     a = k ? r[i] : apply_map(r[i], v[i], succ[i]);
-                    b = k ? v[i] : 0.f;
+                    b = k ? SV(v[i]) : SV(0);
                 }
                 alpha[i] = valid[i] ? a : 0.f;
-                beta[i] = valid[i] ? b : 1.f;
+                beta[i] = valid[i] ? b : SV(1);
                 aux[i] = x;
             }
 
             // ---- 5. scan: lane fold (latest step first), then wave / workgroup
-            float fa = 0.f, fb = 1.f;  // identity; step i applied after the later steps
+            SV fa = SV(0), fb = SV(1);  // identity; step i applied after the later steps
 #pragma unroll
             for (int i = kK - 1; i >= 0; --i) {
-                float a_i = alpha[i], b_i = beta[i];
+                SV a_i = alpha[i], b_i = beta[i];
                 compose(a_i, b_i, fa, fb);
                 fa = a_i;
                 fb = b_i;
@@ -722,18 +766,19 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
             if constexpr (MODE == kChunkAggregate) {
                 // hand the chunk's map to the chunk-carry pass (the earliest
                 // chunk of a row, last in scan order, has no consumer)
-                float ta, tb;
-                block_total<NW>(fa, fb, lds_a, lds_b, ta, tb);
+                SV ta, tb;
+                block_total<NW>(fa, fb, lds_a, lds_b, parity, ta, tb);
+                parity ^= 1;
                 if (threadIdx.x == 0 && win.chunk + 1 < p.geo.chunks_per_row) {
-                    float *slot = chunk_slot<float, S>(p.out0, win.base, p.geo.out0_phase);
-                    slot[0] = ta;
-                    slot[1] = tb;
+                    uint32_t *slot = chunk_slot<uint32_t, S>(p.out0, win.base, p.geo.out0_phase);
+                    put_words(slot, ta);
+                    put_words(slot + sizeof(SV) / 4, tb);
                 }
             } else {
-                float carry_out;
+                SV carry_out;
                 if constexpr (MODE == kChunkApply) hold_chunk_carry(carry);
-                float A = block_carry_in<NW, WAVE_LOCAL>(fa, fb, carry, lds_a, lds_b, parity,
-                                                          carry_out);
+                SV A = block_carry_in<NW, WAVE_LOCAL>(fa, fb, carry, lds_a, lds_b, parity,
+                                                       carry_out);
                 parity ^= 1;
                 carry = carry_out;
 
@@ -741,21 +786,21 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
                 float o0[kK], o1[kK];
 #pragma unroll
                 for (int i = kK - 1; i >= 0; --i) {
-                    const float An = A;  // A_{t+1}
-                    A = apply_map(alpha[i], beta[i], An);
+                    const SV An = A;  // A_{t+1}
+                    A = apply_map(SV(alpha[i]), beta[i], An);
                     if constexpr (EST == kGae) {
-                        o0[i] = A;
-                        o1[i] = A + v[i];
+                        o0[i] = (float)A;
+                        o1[i] = (float)(A + SV(v[i]));
                     } else if constexpr (EST == kVtrace) {
-                        o0[i] = v[i] + A;
-                        o1[i] = apply_map(alpha[i], aux[i], An);
+                        o0[i] = (float)(SV(v[i]) + A);
+                        o1[i] = (float)apply_map(SV(alpha[i]), SV(aux[i]), An);
                     } else if constexpr (EST == kRetrace) {
                         // Q^ret_t = r_t + gamma E Q_{t+1} + beta_t A_{t+1}, without
                         // the Q_t that alpha_t subtracts and A_t + Q_t would add back
-                        o0[i] = apply_map(aux[i], beta[i], An);
+                        o0[i] = (float)apply_map(SV(aux[i]), beta[i], An);
                         o1[i] = 0.f;
                     } else {
-                        o0[i] = A;
+                        o0[i] = (float)A;
                         o1[i] = 0.f;
                     }
                 }
@@ -790,16 +835,18 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
 // seven the compiler picks on its own for these heavier bodies (their SGPR
 // count) an eighth of the waves waits for a second round.  The SGPRs over
 // the limit spill to VGPR lanes.  Lighter variants reach eight by themselves
-// and keep their registers.
+// and keep their registers.  The fp64 scans (F64) do not ask: at eight waves
+// their VGPRs would spill to memory.
 #define RLCA_EIGHT_WAVES(NEED) __attribute__((amdgpu_waves_per_eu((NEED) ? 8 : 1)))
 
 template <int EST, bool TRUNC, int VEC, int NW, bool WAVE_LOCAL, int MODE, typename S,
-          bool STATS = false>
+          bool STATS = false, bool F64 = false>
 __global__ __launch_bounds__(NW * kWave)
-RLCA_EIGHT_WAVES(NW == 8 && !WAVE_LOCAL && VEC != kScalarIO)
+RLCA_EIGHT_WAVES(NW == 8 && !WAVE_LOCAL && VEC != kScalarIO && !F64)
 void backward_scan(LEAD_ARGS, BackwardParams p) {
     adopt_lead<EST>(p, LEAD_NAMES);
-    backward_body<EST, TRUNC, VEC, NW, WAVE_LOCAL, MODE, S, STATS>(p, blockIdx.x, gridDim.x);
+    backward_body<EST, TRUNC, VEC, NW, WAVE_LOCAL, MODE, S, STATS, F64>(p, blockIdx.x,
+                                                                         gridDim.x);
 }
 
 // -------------------------------------------------------------- forward kernel
@@ -810,17 +857,25 @@ void backward_scan(LEAD_ARGS, BackwardParams p) {
 // carry entering at t = 0.
 // S: storage type of x, out (and beta, carry for kForwardAffine); uint32_t
 // for the integer sums.
+// F64 as in backward_body.
 template <typename V, int KIND, bool AFTER_DONE, int VEC, int NW, bool WAVE_LOCAL, int MODE,
-          typename S>
+          typename S, bool F64 = false>
 __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint32_t g_stride) {
-    static_assert(MODE == kFull || (NW == kChunkWaves && !WAVE_LOCAL), "a chunk is one tile");
+    static_assert(MODE == kFull || (NW == kChunkWaves && !WAVE_LOCAL && F64),
+                  "a chunk is one tile, scanned in fp64");
+    typedef typename ScanOf<V, F64>::type SV;
     constexpr uint32_t kTile = NW * kWave * kK;
-    __shared__ V lds_a[2 * NW], lds_b[2 * NW];
+    __shared__ SV lds_a[2 * NW], lds_b[2 * NW];
     const int lane = threadIdx.x & (kWave - 1);
     const int w = NW == 1 ? 0 : threadIdx.x / kWave;  // one-wave tiles: each wave alone
     const uint32_t chunk = w * kWave + lane;
     const uint32_t T = p.geo.T;
     const V decay = __builtin_bit_cast(V, __builtin_bit_cast(uint32_t, p.decay));
+    SV decay_s;  // fp64 scans take the exact product (see backward_body, step 4)
+    if constexpr (__is_same(SV, double))
+        decay_s = p.decay64;
+    else
+        decay_s = decay;
     const S *__restrict__ xs = static_cast<const S *>(p.x);
     const S *__restrict__ betas = static_cast<const S *>(p.beta);
     const S *__restrict__ carries = static_cast<const S *>(p.carry);
@@ -833,9 +888,9 @@ __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint3
         const int64_t row0 = win.row0, base = win.base - sk;
         const uint32_t L = win.L + sk;
         const uint32_t ntiles = MODE == kFull ? (L + kTile - 1) / kTile : 1u;
-        V carry = V(0);
+        SV carry = SV(0);
         if constexpr (MODE == kChunkApply)  // issued ahead of the tile's loads
-            carry = chunk_slot<V, S>(p.out, win.base, p.geo.out0_phase)[0];
+            carry = SV(chunk_slot<V, S>(p.out, win.base, p.geo.out0_phase)[0]);
 
         for (uint32_t it = 0; it < ntiles; ++it) {
             const uint32_t off = it * kTile + chunk * kK;
@@ -874,10 +929,12 @@ __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint3
             bool prev_done = false;
             if constexpr (KIND == kForwardFlags && AFTER_DONE)
                 prev_done = from_lower_lane<uint32_t>(f[kK - 1] ? 1u : 0u, first ? 1u : 0u) != 0;
-            V alpha[kK], beta[kK];
+            V alpha[kK];
+            SV beta[kK];
 #pragma unroll
             for (int i = 0; i < kK; ++i) {
-                V a, b;
+                V a;
+                SV b;
                 if constexpr (KIND == kForwardFlags) {
                     bool reset = start[i];
                     if constexpr (AFTER_DONE) {
@@ -886,42 +943,43 @@ __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint3
                         reset = reset || f[i];
                     }
                     a = x[i];
-                    b = reset ? V(0) : decay;
+                    b = reset ? SV(0) : decay_s;
                 } else {
                     a = start[i] ? apply_map(x[i], bt[i], row_carry[i]) : x[i];
-                    b = start[i] ? V(0) : bt[i];
+                    b = start[i] ? SV(0) : SV(bt[i]);
                 }
                 alpha[i] = valid[i] ? a : V(0);
-                beta[i] = valid[i] ? b : V(1);
+                beta[i] = valid[i] ? b : SV(1);
             }
-            V fa = V(0), fb = V(1);
+            SV fa = SV(0), fb = SV(1);
 #pragma unroll
             for (int i = 0; i < kK; ++i) {
-                V a_i = alpha[i], b_i = beta[i];
+                SV a_i = alpha[i], b_i = beta[i];
                 compose(a_i, b_i, fa, fb);
                 fa = a_i;
                 fb = b_i;
             }
             if constexpr (MODE == kChunkAggregate) {
-                V ta, tb;
-                block_total<NW>(fa, fb, lds_a, lds_b, ta, tb);
+                SV ta, tb;
+                block_total<NW>(fa, fb, lds_a, lds_b, parity, ta, tb);
+                parity ^= 1;
                 if (threadIdx.x == 0 && win.chunk + 1 < p.geo.chunks_per_row) {
-                    V *slot = chunk_slot<V, S>(p.out, win.base, p.geo.out0_phase);
-                    slot[0] = ta;
-                    slot[1] = tb;
+                    uint32_t *slot = chunk_slot<uint32_t, S>(p.out, win.base, p.geo.out0_phase);
+                    put_words(slot, ta);
+                    put_words(slot + sizeof(SV) / 4, tb);
                 }
             } else {
-                V carry_out;
+                SV carry_out;
                 if constexpr (MODE == kChunkApply) hold_chunk_carry(carry);
-                V A = block_carry_in<NW, WAVE_LOCAL>(fa, fb, carry, lds_a, lds_b, parity,
-                                                      carry_out);
+                SV A = block_carry_in<NW, WAVE_LOCAL>(fa, fb, carry, lds_a, lds_b, parity,
+                                                       carry_out);
                 parity ^= 1;
                 carry = carry_out;
                 V o[kK];
 #pragma unroll
                 for (int i = 0; i < kK; ++i) {
-                    A = apply_map(alpha[i], beta[i], A);
-                    o[i] = A;
+                    A = apply_map(SV(alpha[i]), beta[i], A);
+                    o[i] = V(A);
                 }
                 store_steps<VEC>(out + base, o, off, L, sk, p.geo.scatter != 0);
             }
@@ -931,47 +989,50 @@ __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint3
 }
 
 template <typename V, int KIND, bool AFTER_DONE, int VEC, int NW, bool WAVE_LOCAL, int MODE,
-          typename S>
+          typename S, bool F64 = false>
 __global__ __launch_bounds__(NW * kWave)
-RLCA_EIGHT_WAVES(NW == 8 && !WAVE_LOCAL && VEC != kScalarIO)
+RLCA_EIGHT_WAVES(NW == 8 && !WAVE_LOCAL && VEC != kScalarIO && !F64)
 void forward_scan(LEAD_ARGS, ForwardParams p) {
     adopt_lead(p, LEAD_NAMES);
-    forward_body<V, KIND, AFTER_DONE, VEC, NW, WAVE_LOCAL, MODE, S>(p, blockIdx.x, gridDim.x);
+    forward_body<V, KIND, AFTER_DONE, VEC, NW, WAVE_LOCAL, MODE, S, F64>(p, blockIdx.x,
+                                                                          gridDim.x);
 }
 
 // ------------------------------------------------------------ chunk carries
 // Chunk modes, middle pass: one workgroup per row scans the row's chunk maps
-// (left by the aggregate pass in the first two words of each chunk's slice of
-// `slots`) in scan order and leaves in each chunk's first word the value of
-// A entering that chunk.  Lane j of a tile holds chunk j; the last chunk in
-// scan order has no map (identity) but receives its carry.
-template <typename V, typename S, int NW>
+// (left by the aggregate pass as scan values C in the first words of each
+// chunk's slice of `slots`) in scan order and leaves in each chunk's first
+// word the value of A entering that chunk, as a value of type R (the
+// kernels' value type: fp32 for the float scans, whose maps are fp64).
+// Lane j of a tile holds chunk j; the last chunk in scan order has no map
+// (identity) but receives its carry.
+template <typename C, typename R, typename S, int NW>
 __global__ __launch_bounds__(NW * kWave) void chunk_carries(void *slots, int64_t num_envs,
                                                             uint32_t T, uint32_t chunks_per_row,
                                                             uint32_t span, uint32_t out_phase,
                                                             int backward) {
-    __shared__ V lds_a[2 * NW], lds_b[2 * NW];
+    __shared__ C lds_a[2 * NW], lds_b[2 * NW];
     constexpr uint32_t kLanes = NW * kWave;
     int parity = 0;
     int64_t n = blockIdx.x;  // the grid never exceeds num_envs
     do {
         const int64_t row = n * (int64_t)T;
-        V carry = V(0);
+        C carry = C(0);
         for (uint32_t j0 = 0; j0 < chunks_per_row; j0 += kLanes) {
             const uint32_t j = j0 + threadIdx.x;
             uint32_t lo = 0, hi = 0;
             if (j < chunks_per_row) chunk_bounds(T, j, chunks_per_row, backward != 0, span, lo, hi);
-            V *slot = chunk_slot<V, S>(slots, row + lo, out_phase);
-            V a = V(0), b = V(1);
+            uint32_t *slot = chunk_slot<uint32_t, S>(slots, row + lo, out_phase);
+            C a = C(0), b = C(1);
             if (j + 1 < chunks_per_row) {
-                a = slot[0];
-                b = slot[1];
+                a = get_words<C>(slot);
+                b = get_words<C>(slot + sizeof(C) / 4);
             }
-            V carry_out;
-            const V in = block_carry_in<NW, false>(a, b, carry, lds_a, lds_b, parity, carry_out);
+            C carry_out;
+            const C in = block_carry_in<NW, false>(a, b, carry, lds_a, lds_b, parity, carry_out);
             parity ^= 1;
             carry = carry_out;
-            if (j < chunks_per_row) slot[0] = in;
+            if (j < chunks_per_row) put_words(slot, R(in));
         }
         n += gridDim.x;
     } while (n < num_envs);
@@ -1060,7 +1121,7 @@ inline rlca_status launch_kernel(const void *kernel, int waves, uint32_t grid, P
     return e == hipSuccess ? RLCA_OK : RLCA_ERR_HIP;
 }
 
-template <typename V, typename S>
+template <typename C, typename R, typename S>
 inline rlca_status launch_chunk_carries(void *slots, const Geometry &geo, bool backward,
                                         bool skew, hipStream_t stream) {
     int64_t n = geo.num_envs;
@@ -1068,13 +1129,14 @@ inline rlca_status launch_chunk_carries(void *slots, const Geometry &geo, bool b
     int dir = backward ? 1 : 0;
     void *args[] = {&slots, &n, &T, &m, &span, &phase, &dir};
     const hipError_t e =
-        hipLaunchKernel((const void *)chunk_carries<V, S, kChunkWaves>, dim3(grid_for(n)),
+        hipLaunchKernel((const void *)chunk_carries<C, R, S, kChunkWaves>, dim3(grid_for(n)),
                         dim3(kChunkWaves * kWave), args, 0, stream);
     return e == hipSuccess ? RLCA_OK : RLCA_ERR_HIP;
 }
 
 // The three chunk-mode launches, all on one stream: aggregate, carries,
-// apply (the apply grid capped at `apply_cap`).
+// apply (the apply grid capped at `apply_cap`).  V: the kernels' value type;
+// the chunk maps are scanned in ScanOf<V, true>.
 template <typename V, typename S, typename P>
 inline rlca_status launch_chunked(const void *aggregate, const void *apply, P &params, Lead &lead,
                                   void *slots, bool backward, const LaunchShape &s,
@@ -1084,7 +1146,8 @@ inline rlca_status launch_chunked(const void *aggregate, const void *apply, P &p
     const uint32_t apply_grid = grid_for(params.geo.num_groups, apply_cap);
     rlca_status st = launch_kernel(aggregate, kChunkWaves, grid, params, lead, stream);
     if (st == RLCA_OK)
-        st = launch_chunk_carries<V, S>(slots, params.geo, backward, s.skew, stream);
+        st = launch_chunk_carries<typename ScanOf<V, true>::type, V, S>(slots, params.geo,
+                                                                         backward, s.skew, stream);
     if (st == RLCA_OK) st = launch_kernel(apply, kChunkWaves, apply_grid, params, lead, stream);
     return st;
 }
@@ -1114,12 +1177,18 @@ inline int io_path(const LaunchShape &s) {
 
 // The whole-row vector path instantiates every wave count and the wave-local
 // variant; the skewed and the scalar (unaligned) paths one configuration each.
+// Calls whose chains need it (f64) take the fp64-scan instantiations.
 template <int EST, bool TRUNC, typename S, bool STATS = false>
 const void *backward_kernel(const LaunchShape &s) {
-    if (!s.vec)
-        return (const void *)backward_scan<EST, TRUNC, kScalarIO, 4, false, kFull, S, STATS>;
-    if (s.skew)
-        return (const void *)backward_scan<EST, TRUNC, kVecSkew, 8, false, kFull, S, STATS>;
+#define RLCA_PICK_F64(IO, NW)                                                                  \
+    return s.f64                                                                               \
+               ? (const void *)backward_scan<EST, TRUNC, IO, NW, false, kFull, S, STATS, true> \
+               : (const void *)backward_scan<EST, TRUNC, IO, NW, false, kFull, S, STATS, false>
+    if (!s.vec) RLCA_PICK_F64(kScalarIO, 4);
+    if (s.skew) RLCA_PICK_F64(kVecSkew, 8);
+    if (s.waves == 8 && !s.wave_local) RLCA_PICK_F64(kVecRows, 8);
+    if (s.waves == 1) RLCA_PICK_F64(kVecRows, 1);
+#undef RLCA_PICK_F64
 #define RLCA_PICK(NW)                                                                          \
     return s.wave_local                                                                        \
                ? (const void *)backward_scan<EST, TRUNC, kVecRows, NW, true, kFull, S, STATS> \
@@ -1139,10 +1208,12 @@ rlca_status launch_backward_variant(BackwardParams &p, const LaunchShape &s, hip
     lead_from<EST>(p, lead);
     const uint32_t cap = STATS ? kStatsMaxGrid : kMaxGrid;
     if (s.chunked) {
-#define RLCA_CHUNKED(IO)                                                                         \
-    return launch_chunked<float, S>(                                                             \
-        (const void *)backward_scan<EST, TRUNC, IO, kChunkWaves, false, kChunkAggregate, S>,     \
-        (const void *)backward_scan<EST, TRUNC, IO, kChunkWaves, false, kChunkApply, S, STATS>,  \
+#define RLCA_CHUNKED(IO)                                                                       \
+    return launch_chunked<float, S>(                                                           \
+        (const void *)                                                                         \
+            backward_scan<EST, TRUNC, IO, kChunkWaves, false, kChunkAggregate, S, false, true>, \
+        (const void *)                                                                         \
+            backward_scan<EST, TRUNC, IO, kChunkWaves, false, kChunkApply, S, STATS, true>,     \
         p, lead, p.out0, true, s, stream, cap)
         if (s.skew) RLCA_CHUNKED(kVecSkew);
         RLCA_CHUNKED(kVecRows);
@@ -1169,10 +1240,15 @@ rlca_status launch_backward(BackwardParams &p, const LaunchShape &s, int storage
 
 template <typename V, int KIND, bool AFTER_DONE, typename S>
 const void *forward_kernel(const LaunchShape &s) {
-    if (!s.vec)
-        return (const void *)forward_scan<V, KIND, AFTER_DONE, kScalarIO, 4, false, kFull, S>;
-    if (s.skew)
-        return (const void *)forward_scan<V, KIND, AFTER_DONE, kVecSkew, 8, false, kFull, S>;
+#define RLCA_PICK_F64(IO, NW)                                                                   \
+    return s.f64                                                                                \
+               ? (const void *)forward_scan<V, KIND, AFTER_DONE, IO, NW, false, kFull, S, true> \
+               : (const void *)forward_scan<V, KIND, AFTER_DONE, IO, NW, false, kFull, S, false>
+    if (!s.vec) RLCA_PICK_F64(kScalarIO, 4);
+    if (s.skew) RLCA_PICK_F64(kVecSkew, 8);
+    if (s.waves == 8 && !s.wave_local) RLCA_PICK_F64(kVecRows, 8);
+    if (s.waves == 1) RLCA_PICK_F64(kVecRows, 1);
+#undef RLCA_PICK_F64
 #define RLCA_PICK(NW)                                                                          \
     return s.wave_local                                                                        \
                ? (const void *)forward_scan<V, KIND, AFTER_DONE, kVecRows, NW, true, kFull, S> \
@@ -1194,9 +1270,9 @@ rlca_status launch_forward_variant(ForwardParams &p, const LaunchShape &s, hipSt
 #define RLCA_CHUNKED(IO)                                                                    \
     return launch_chunked<V, S>(                                                            \
         (const void *)forward_scan<V, KIND, AFTER_DONE, IO, kChunkWaves, false,             \
-                                   kChunkAggregate, S>,                                     \
+                                   kChunkAggregate, S, true>,                               \
         (const void *)forward_scan<V, KIND, AFTER_DONE, IO, kChunkWaves, false, kChunkApply, \
-                                   S>,                                                      \
+                                   S, true>,                                                \
         p, lead, p.out, false, s, stream)
         if (s.skew) RLCA_CHUNKED(kVecSkew);
         RLCA_CHUNKED(kVecRows);

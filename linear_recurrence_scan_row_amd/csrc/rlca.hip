@@ -23,6 +23,10 @@ static bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 
 static bool unit_interval(float x) { return x >= 0.f && x <= 1.f; }  // false for NaN
 static bool positive_finite(float x) { return x > 0.f && isfinite(x); }
+// Trace clips: 0 < c_bar <= 1, so every importance-weighted coefficient
+// beta_t = gamma * lambda * min(c_bar, ratio_t) stays in [0, 1] (Munos et
+// al. truncate the trace at 1; IMPALA's c_bar <= rho_bar, 1 in its runs).
+static bool trace_clip(float x) { return x > 0.f && x <= 1.f; }  // false for NaN
 
 struct Span {
     const void *p;
@@ -135,6 +139,44 @@ static constexpr int64_t kOneWaveMinRows = 4096;
 // 4 rows measured 5-13% slower over 4096 x 4097).
 static constexpr int64_t kSkewAlignedMinWindows = 1024;
 
+// Scan precision of a call whose coefficients satisfy |beta_t| <= beta.max.
+// Wherever a value crosses the scan's waves (rows longer than one wave),
+// two fp32 effects grow along a chain that barely decays: the rounding of
+// beta products and carried sums (emulating the fp32 evaluation order: 2e-4
+// at beta = 0.999 over 2048 steps, 1.7e-4 at beta = 1 over 131072), and the
+// chain's sensitivity to beta itself, which turns the fp32 rounding of a
+// product of parameters (gamma * lambda) into an output error of order
+// 2^-24 * sqrt(2 / (1 - beta^2)^3).  fp32 keeps the parity bar for beta.max
+// <= 0.95; for beta.max <= 0.99 when the fp32 coefficient is the exact
+// product of the parameters (beta.exact); and at beta.max = 1 (exact
+// products) up to one 2048-step tile.  Other calls scan in fp64 (ScanOf in
+// scan_core.hpp), with beta formed in fp64.  Rows that end at wave
+// boundaries carry nothing between waves and stay fp32; integer sums are
+// exact.
+struct BetaBound {
+    float max;   // largest beta_t, as the fp32 kernels form it
+    bool exact;  // that fp32 value is the exact product of the parameters
+};
+
+static BetaBound product_bound(float a, float b) {
+    const float p = a * b;
+    return {p, (double)p == (double)a * (double)b};
+}
+
+// The importance-weighted estimators: beta_t = gamma * (lambda * min(c_bar,
+// ratio_t)), largest where the ratio is clipped at c_bar.
+static BetaBound weighted_bound(float gamma, float lambda, float c_bar) {
+    const BetaBound c = product_bound(lambda, c_bar);
+    const BetaBound b = product_bound(gamma, c.max);
+    return {b.max, c.exact && b.exact};
+}
+
+static void set_precision(LaunchShape &s, int64_t T, BetaBound beta, bool is_int) {
+    const bool fp32_ok = beta.max <= 0.95f || (beta.exact && beta.max <= 0.99f) ||
+                         (beta.exact && beta.max == 1.f && T <= (int64_t)kChunkSteps);
+    s.f64 = !is_int && !s.wave_local && T > kWave * kK && !fp32_ok;
+}
+
 static LaunchShape choose_shape(int64_t num_envs, int64_t T, const IoChoice &io) {
     LaunchShape s;
     s.vec = io.io != kScalarIO;
@@ -145,6 +187,7 @@ static LaunchShape choose_shape(int64_t num_envs, int64_t T, const IoChoice &io)
     s.wave_local = io.io == kVecRows && T <= kWave * kK && (kWave * kK) % T == 0;
     s.waves = (T <= kWave * kK || T >= 1024 || num_envs < kOneWaveMinRows) ? 8 : 1;
     s.chunked = s.vec && T > 2 * (int64_t)kChunkSteps && num_envs < kChunkedMaxRows;
+    s.f64 = false;  // set_precision
     s.quantum = 1;
     if (s.skew) {
         s.waves = 8;
@@ -255,6 +298,7 @@ static rlca_status prepare_backward(int est, int storage, const void *rewards,
 // int32 with `is_int` (then storage is kStoreF32, the 4-byte class).
 static rlca_status prepare_forward(int kind, int storage, const void *x, bool is_int,
                                    const uint8_t *flags, int convention, float decay,
+                                   double decay64,
                                    const void *beta, const void *carry, int64_t num_envs,
                                    int64_t T, void *out, Call *c) {
     *c = Call{};
@@ -296,6 +340,7 @@ static rlca_status prepare_forward(int kind, int storage, const void *x, bool is
     p.carry = carry;
     p.out = out;
     p.decay = is_int ? __builtin_bit_cast(float, 1u) : decay;
+    p.decay64 = decay64;
     p.geo.num_envs = num_envs;
     p.geo.T = (uint32_t)T;
     const void *wide[] = {x, beta};
@@ -329,7 +374,10 @@ static bool grouped_member(const Call &c, GroupedCall *g, int *variant, uint32_t
     // Grouped launches run 8-wave workgroups: calls shaped for 8 waves take
     // one workgroup per group, one-wave calls one wave per group.  Both keep
     // the geometry of their own launch, so results match it bit for bit.
-    if (!c.shape.vec || c.shape.chunked || (c.shape.waves != 1 && c.shape.waves != kGroupWaves))
+    // Calls that scan in fp64 run their own launch (their kernels are not
+    // part of the grouped classes).
+    if (!c.shape.vec || c.shape.chunked || c.shape.f64 ||
+        (c.shape.waves != 1 && c.shape.waves != kGroupWaves))
         return false;
     const bool wl = c.shape.wave_local, one = c.shape.waves == 1, skew = c.shape.skew;
     uint32_t grid, groups;
@@ -369,6 +417,7 @@ static rlca_status prepare_gae(int storage, const void *rewards, const void *val
                                             bootstrap, advantages, returns, num_envs, T, c);
     c->bp.gamma = gamma;
     c->bp.lambda = lambda;
+    set_precision(c->shape, T, product_bound(gamma, lambda), false);
     return st;
 }
 
@@ -385,6 +434,7 @@ static rlca_status prepare_td_lambda(int storage, const void *rewards, const voi
                                             T, c);
     c->bp.gamma = gamma;
     c->bp.lambda = lambda;
+    set_precision(c->shape, T, product_bound(gamma, lambda), false);
     return st;
 }
 
@@ -400,6 +450,7 @@ static rlca_status prepare_discounted(int storage, const void *rewards,
                                             trunc_values, bootstrap, returns, nullptr, num_envs,
                                             T, c);
     c->bp.gamma = gamma;
+    set_precision(c->shape, T, {gamma, true}, false);
     return st;
 }
 
@@ -411,7 +462,7 @@ static rlca_status prepare_vtrace(int storage, const void *rewards, const void *
                                   int64_t T, void *vs, void *pg_advantages, Call *c) {
     *c = Call{};
     if (!unit_interval(gamma) || !unit_interval(lambda) || !positive_finite(rho_bar) ||
-        !positive_finite(c_bar))
+        !trace_clip(c_bar))
         return RLCA_ERR_INVALID_VALUE;
     const rlca_status st =
         prepare_backward(kVtrace, storage, rewards, values, nullptr, behaviour_logp,
@@ -421,6 +472,7 @@ static rlca_status prepare_vtrace(int storage, const void *rewards, const void *
     c->bp.lambda = lambda;
     c->bp.rho_bar = rho_bar;
     c->bp.c_bar = c_bar;
+    set_precision(c->shape, T, weighted_bound(gamma, lambda, c_bar), false);
     return st;
 }
 
@@ -431,7 +483,7 @@ static rlca_status prepare_retrace(int storage, const void *rewards, const void 
                                    const void *bootstrap, float gamma, float lambda, float c_bar,
                                    int64_t num_envs, int64_t T, void *q_ret, Call *c) {
     *c = Call{};
-    if (!unit_interval(gamma) || !unit_interval(lambda) || !positive_finite(c_bar))
+    if (!unit_interval(gamma) || !unit_interval(lambda) || !trace_clip(c_bar))
         return RLCA_ERR_INVALID_VALUE;
     const rlca_status st = prepare_backward(kRetrace, storage, rewards, q_values, expected_q,
                                             behaviour_logp, target_logp, terminated, truncated,
@@ -440,6 +492,7 @@ static rlca_status prepare_retrace(int storage, const void *rewards, const void 
     c->bp.gamma = gamma;
     c->bp.lambda = lambda;
     c->bp.c_bar = c_bar;
+    set_precision(c->shape, T, weighted_bound(gamma, lambda, c_bar), false);
     return st;
 }
 
@@ -449,8 +502,12 @@ static rlca_status prepare_eligibility(int storage, const void *increments,
                                        Call *c) {
     *c = Call{};
     if (!unit_interval(gamma) || !unit_interval(lambda)) return RLCA_ERR_INVALID_VALUE;
-    return prepare_forward(kForwardFlags, storage, increments, false, flags, convention,
-                           gamma * lambda, nullptr, nullptr, num_envs, T, traces, c);
+    const rlca_status st = prepare_forward(kForwardFlags, storage, increments, false, flags,
+                                           convention, gamma * lambda,
+                                           (double)gamma * (double)lambda, nullptr, nullptr,
+                                           num_envs, T, traces, c);
+    set_precision(c->shape, T, product_bound(gamma, lambda), false);
+    return st;
 }
 
 // dtype: RLCA_I32 (exact, wrapping) or a real storage type.
@@ -461,8 +518,10 @@ static rlca_status prepare_prefix_sum(const void *x, int dtype, const uint8_t *f
     const bool is_int = dtype == RLCA_I32;
     const int storage = is_int ? (int)kStoreF32 : storage_of(dtype);
     if (storage < 0) return RLCA_ERR_INVALID_VALUE;
-    return prepare_forward(kForwardFlags, storage, x, is_int, flags, convention, 1.0f, nullptr,
-                           nullptr, num_envs, T, out, c);
+    const rlca_status st = prepare_forward(kForwardFlags, storage, x, is_int, flags, convention,
+                                           1.0f, 1.0, nullptr, nullptr, num_envs, T, out, c);
+    set_precision(c->shape, T, {1.0f, true}, is_int);
+    return st;
 }
 
 static rlca_status prepare_affine(int storage, const void *alpha, const void *beta,
@@ -470,11 +529,15 @@ static rlca_status prepare_affine(int storage, const void *alpha, const void *be
                                   void *out, Call *c) {
     *c = Call{};
     if (direction != RLCA_BACKWARD && direction != RLCA_FORWARD) return RLCA_ERR_INVALID_VALUE;
-    if (direction == RLCA_BACKWARD)
-        return prepare_backward(kAffineBackward, storage, alpha, beta, nullptr, nullptr, nullptr,
-                                nullptr, nullptr, nullptr, carry, out, nullptr, num_envs, T, c);
-    return prepare_forward(kForwardAffine, storage, alpha, false, nullptr, 0, 0.f, beta, carry,
-                           num_envs, T, out, c);
+    const rlca_status st =
+        direction == RLCA_BACKWARD
+            ? prepare_backward(kAffineBackward, storage, alpha, beta, nullptr, nullptr, nullptr,
+                               nullptr, nullptr, nullptr, carry, out, nullptr, num_envs, T, c)
+            : prepare_forward(kForwardAffine, storage, alpha, false, nullptr, 0, 0.f, 0.0, beta,
+                              carry, num_envs, T, out, c);
+    // the caller's beta is unknown: fp64 wherever a value crosses waves
+    set_precision(c->shape, T, {INFINITY, false}, false);
+    return st;
 }
 
 // One rlca_call of a batch, prepared like its own entry point; `dtype` gives
@@ -808,7 +871,9 @@ const char *rlca_status_string(rlca_status status) {
         case RLCA_ERR_INVALID_SIZE: return "invalid size (negative, too large or overflowing)";
         case RLCA_ERR_INVALID_VALUE: return "invalid parameter value";
         case RLCA_ERR_ALIASING: return "an output overlaps an input or another output";
-        case RLCA_ERR_MISALIGNED: return "a 32-bit array is not 4-byte aligned";
+        case RLCA_ERR_MISALIGNED:
+            return "an array is not aligned to its element size (8 bytes for workspace, stats "
+                   "and loss)";
         case RLCA_ERR_HIP: return "HIP kernel launch failed";
     }
     return "unknown status";

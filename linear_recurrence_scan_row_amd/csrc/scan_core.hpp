@@ -52,24 +52,78 @@ __device__ __forceinline__ V from_bits(int x) {
 // the results are the same.  One test of the later map's beta serves both
 // halves of a composition: when that beta is NaN the composed value is NaN
 // already, so a NaN composed beta changes nothing.  The int32 prefix sums
-// (uint32 here) have no NaN and keep plain arithmetic.
-__device__ __forceinline__ float apply_map(float a, float b, float x) {
-    return b == 0.f ? a : a + b * x;
-}
-__device__ __forceinline__ uint32_t apply_map(uint32_t a, uint32_t b, uint32_t x) {
-    return a + b * x;
+// (uint32 here) have no NaN and keep plain arithmetic.  The double forms
+// serve the fp64 scans (see ScanOf).
+template <typename V>
+__device__ __forceinline__ V apply_map(V a, V b, V x) {
+    if constexpr (__is_same(V, uint32_t)) {
+        return a + b * x;
+    } else {
+        return b == V(0) ? a : a + b * x;
+    }
 }
 
 // (a, b) <- (a, b) after (pa, pb): the map of a later run in scan order
 // applied after the map of the earlier run.
-__device__ __forceinline__ void compose(float &a, float &b, float pa, float pb) {
-    const bool cut = b == 0.f;
-    a = cut ? a : a + b * pa;
-    b = cut ? b : b * pb;
+template <typename V>
+__device__ __forceinline__ void compose(V &a, V &b, V pa, V pb) {
+    if constexpr (__is_same(V, uint32_t)) {
+        a = a + b * pa;
+        b = b * pb;
+    } else {
+        const bool cut = b == V(0);
+        a = cut ? a : a + b * pa;
+        b = cut ? b : b * pb;
+    }
 }
-__device__ __forceinline__ void compose(uint32_t &a, uint32_t &b, uint32_t pa, uint32_t pb) {
-    a = a + b * pa;
-    b = b * pb;
+
+// Scan type of a kernel over values of type V.  fp32 rounding hurts where a
+// value is carried across waves along a chain that barely decays: a product
+// of n factors beta carries a relative error of up to about n * 2^-24, and it
+// scales the carried value once per wave, over the ~1 / (1 - beta^256) waves
+// the chain remembers; at beta = 1 the products are exact, but the carried
+// sums' own rounding then accumulates over the whole row.  Kernels whose
+// calls have rows spanning waves with beta near 1 (the host's choice, F64)
+// therefore scan in fp64 from the lane fold on and round each output to
+// fp32 once.  Integer sums are exact in any case.
+template <typename V, bool F64>
+struct ScanOf {
+    typedef V type;
+};
+template <>
+struct ScanOf<float, true> {
+    typedef double type;
+};
+
+// Value of lane CTRL selects (DPP), or `old` where there is none; 64-bit
+// values move as two 32-bit halves.
+template <int CTRL, int ROW_MASK, typename V>
+__device__ __forceinline__ V dpp_move(V x, V old) {
+    if constexpr (sizeof(V) == 4) {
+        return from_bits<V>(__builtin_amdgcn_update_dpp(as_bits(old), as_bits(x), CTRL, ROW_MASK,
+                                                        0xf, false));
+    } else {
+        static_assert(sizeof(V) == 8, "32- or 64-bit values");
+        const uint64_t u = __builtin_bit_cast(uint64_t, x), o = __builtin_bit_cast(uint64_t, old);
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(
+            (int)(uint32_t)o, (int)(uint32_t)u, CTRL, ROW_MASK, 0xf, false);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(
+            (int)(uint32_t)(o >> 32), (int)(uint32_t)(u >> 32), CTRL, ROW_MASK, 0xf, false);
+        return __builtin_bit_cast(V, ((uint64_t)hi << 32) | lo);
+    }
+}
+
+// Value of `lane` (uniform), 32- or 64-bit.
+template <typename V>
+__device__ __forceinline__ V read_lane(V x, int lane) {
+    if constexpr (sizeof(V) == 4) {
+        return from_bits<V>(__builtin_amdgcn_readlane(as_bits(x), lane));
+    } else {
+        const uint64_t u = __builtin_bit_cast(uint64_t, x);
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+        return __builtin_bit_cast(V, ((uint64_t)hi << 32) | lo);
+    }
 }
 
 // One DPP step: fetch (a, b) from the lane selected by CTRL and compose.
@@ -77,10 +131,8 @@ __device__ __forceinline__ void compose(uint32_t &a, uint32_t &b, uint32_t pa, u
 // identity (0, 1) as fetched value (bound_ctrl = 0 keeps `old`).
 template <int CTRL, int ROW_MASK, typename V>
 __device__ __forceinline__ void dpp_compose(V &a, V &b) {
-    const V pa = from_bits<V>(__builtin_amdgcn_update_dpp(as_bits(V(0)), as_bits(a), CTRL,
-                                                          ROW_MASK, 0xf, false));
-    const V pb = from_bits<V>(__builtin_amdgcn_update_dpp(as_bits(V(1)), as_bits(b), CTRL,
-                                                          ROW_MASK, 0xf, false));
+    const V pa = dpp_move<CTRL, ROW_MASK>(a, V(0));
+    const V pb = dpp_move<CTRL, ROW_MASK>(b, V(1));
     compose(a, b, pa, pb);
 }
 
@@ -99,8 +151,7 @@ __device__ __forceinline__ void wave_inclusive_scan(V &a, V &b) {
 // whose lane 0 has no source and keeps the `old` operand.
 template <typename V>
 __device__ __forceinline__ V from_lower_lane(V x, V first) {
-    return from_bits<V>(
-        __builtin_amdgcn_update_dpp(as_bits(first), as_bits(x), 0x138, 0xf, 0xf, false));
+    return dpp_move<0x138, 0xf>(x, first);
 }
 
 // Workgroup-wide scan of per-lane maps (a, b) given in scan order, with an
@@ -130,8 +181,8 @@ __device__ __forceinline__ V block_carry_in(V a, V b, V carry_in, V *lds_a, V *l
     if constexpr (NW == 1) {
         // One wave: its total is lane 63's inclusive value; no LDS, no
         // barrier (so waves of one workgroup may run unrelated tiles).
-        const V ta = from_bits<V>(__builtin_amdgcn_readlane(as_bits(a), kWave - 1));
-        const V tb = from_bits<V>(__builtin_amdgcn_readlane(as_bits(b), kWave - 1));
+        const V ta = read_lane(a, kWave - 1);
+        const V tb = read_lane(b, kWave - 1);
         carry_out = apply_map(ta, tb, carry_in);
         return apply_map(ea, eb, carry_in);
     }
@@ -153,21 +204,26 @@ __device__ __forceinline__ V block_carry_in(V a, V b, V carry_in, V *lds_a, V *l
 
 // The map of the whole tile: the NW wave totals composed in scan order.  Used
 // where a tile's result is handed to another workgroup instead of applied.
+// Like block_carry_in, the wave totals go to the half of the 2*NW LDS slots
+// that `parity` selects, and the caller alternates it between tiles: a wave
+// that runs ahead into the next tile writes the other half, so it cannot
+// overwrite a total another wave is still reading (one barrier per tile).
 template <int NW, typename V>
-__device__ __forceinline__ void block_total(V a, V b, V *lds_a, V *lds_b, V &ta, V &tb) {
+__device__ __forceinline__ void block_total(V a, V b, V *lds_a, V *lds_b, int parity, V &ta,
+                                            V &tb) {
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x / kWave;
     wave_inclusive_scan(a, b);
     if (lane == kWave - 1) {
-        lds_a[w] = a;
-        lds_b[w] = b;
+        lds_a[parity * NW + w] = a;
+        lds_b[parity * NW + w] = b;
     }
     __syncthreads();
     ta = V(0);
     tb = V(1);
 #pragma unroll
     for (int j = 0; j < NW; ++j) {
-        V a_j = lds_a[j], b_j = lds_b[j];
+        V a_j = lds_a[parity * NW + j], b_j = lds_b[parity * NW + j];
         compose(a_j, b_j, ta, tb);
         ta = a_j;
         tb = b_j;

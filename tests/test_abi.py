@@ -92,6 +92,17 @@ def test_value_errors(lib):
                            8, F, G, None) == VALUE
     assert lib.rlca_retrace(A, B, C, D, E, F, None, None, None, 0.99, 0.95, -1.0, 4, 8, G,
                             None) == VALUE
+    # trace clips above 1 would make the recurrence expansive: refused
+    for c_bar in (1.0001, 3.0, float("inf")):
+        assert lib.rlca_vtrace(A, B, C, D, E, None, None, None, 0.99, 1.0, 1.0, c_bar, 4, 8, F,
+                               G, None) == VALUE
+        assert lib.rlca_retrace(A, B, C, D, E, F, None, None, None, 0.99, 0.95, c_bar, 4, 8, G,
+                                None) == VALUE
+        assert run_batch(lib, call(op=binding.OP_VTRACE, rewards=A, values=B, behaviour_logp=C,
+                                   target_logp=D, terminated=E, out0=F, c_bar=c_bar)) == VALUE
+    # rho_bar above 1 only scales alpha: accepted (nothing to enqueue at n = 0)
+    assert lib.rlca_vtrace(A, B, C, D, E, None, None, None, 0.99, 1.0, 1e3, 1.0, 0, 8, F, G,
+                           None) == OK
     assert lib.rlca_eligibility_traces(A, B, 7, 0.9, 0.9, 4, 8, C, None) == VALUE
     assert lib.rlca_episodic_prefix_sum(A, 5, B, 0, 4, 8, C, None) == VALUE
     assert lib.rlca_affine_scan(A, B, None, 2, 4, 8, C, None) == VALUE

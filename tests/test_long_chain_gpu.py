@@ -1,17 +1,15 @@
-"""fp32 rounding on long chains that never break: beta = 1 over a whole row
+"""fp32 results on long chains that never break: beta = 1 over a whole row
 (an episodic prefix sum without resets, discounted returns with gamma = 1 and
 no episode ends), on the chunked path (8 rows) and the tile-carry path
-(128 rows).
+(128 rows), with T % 4 == 0 and T % 4 != 0.
 
-The absolute rounding error of any fp32 evaluation grows with the partial
-sums, so near their zero crossings it can exceed 1e-4 * (1 + |A|) once rows
-run to about 10^5 steps of zero-mean data.  The tests pin what holds:
-
-  * up to 16384 steps, and for positive increments at any length, every
-    output meets the parity bar against the fp64 oracle;
-  * at 131072 steps of zero-mean data the scan's worst error stays below a
-    sequential fp32 evaluation's (numpy's cumulative sum, one addition per
-    step), which misses the bar by far more.
+Rows longer than one tile carry their scan from tile to tile (and from chunk
+to chunk) in fp64, so rounding no longer accumulates with the row's length:
+every output meets the parity bar 1e-4 * (1 + |A|) against the fp64 oracle
+up to 131072 steps, the longest fused scan on the pages ("rl-triton",
+paperlayer.ai summary, §3.1 Shared scan formulation), zero-mean data
+included.  A sequential fp32 evaluation (numpy's cumulative sum, one
+addition per step) misses that bar on the same zero-mean rows by far.
 """
 import numpy as np
 import pytest
@@ -54,15 +52,15 @@ def test_long_chain_meets_the_bar(N, T, dist, gpu_device):
         assert worst <= TOL, f"{what} N={N} T={T} {dist}: {worst:.3e}"
 
 
-@pytest.mark.parametrize("N", [8, 128])
-def test_very_long_chain(N, gpu_device):
-    T = 131072
-    rng = np.random.default_rng(2000 + N)
+@pytest.mark.parametrize("N,T", [(8, 131072), (128, 131072), (8, 131071), (128, 131071)])
+def test_very_long_chain(N, T, gpu_device):
+    rng = np.random.default_rng(2000 + N + T)
     positive = rng.random((N, T)).astype(np.float32)
     for what, g, o, _ in _run(positive, gpu_device):
         worst = _rel(g, o).max()
         assert worst <= TOL, f"{what} N={N} T={T} positive: {worst:.3e}"
     zero_mean = rng.standard_normal((N, T)).astype(np.float32)
     for what, g, o, s in _run(zero_mean, gpu_device):
-        scan, seq = np.abs(g - o).max(), np.abs(s - o).max()
-        assert scan < seq, f"{what} N={N}: scan error {scan:.3e}, sequential fp32 {seq:.3e}"
+        worst, seq = _rel(g, o).max(), _rel(s, o).max()
+        print(f"{what} N={N} T={T} zero-mean: scan {worst:.3e}, sequential fp32 {seq:.3e}")
+        assert worst <= TOL, f"{what} N={N} T={T} zero-mean: {worst:.3e} (sequential {seq:.3e})"

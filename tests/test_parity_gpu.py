@@ -34,6 +34,14 @@ def assert_parity(gpu, ref, what=""):
                                f"gpu {g[worst]!r} oracle {ref[worst]!r}")
 
 
+def f32(x):
+    """A parameter as the library receives it (the C ABI takes fp32), for the
+    oracle: like the arrays, the oracle evaluates the library's own inputs.
+    (Near beta = 1 a long chain amplifies a parameter's rounding by orders of
+    magnitude, so the oracle must not see a different gamma or lambda.)"""
+    return float(np.float32(x))
+
+
 def dev(x, device):
     return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(device)
 
@@ -51,7 +59,7 @@ def check_gae(d, device, trunc=True, boot=True, gamma=0.99, lam=0.95, what=""):
     b = d.bootstrap if boot else None
     adv, ret = rl.gae(dev(d.rewards, device), dev(d.values, device), dev(d.terminated, device),
                       dev(tr, device), dev(tv, device), dev(b, device), gamma, lam)
-    oadv, oret = oracle.gae(d.rewards, d.values, d.terminated, tr, tv, b, gamma, lam)
+    oadv, oret = oracle.gae(d.rewards, d.values, d.terminated, tr, tv, b, f32(gamma), f32(lam))
     assert_parity(adv, oadv, f"gae adv {what}")
     assert_parity(ret, oret, f"gae ret {what}")
 
@@ -62,8 +70,8 @@ def check_td(d, device, trunc=True, boot=True, gamma=0.99, lam=0.95, what=""):
     b = d.bootstrap if boot else None
     g = rl.td_lambda(dev(d.rewards, device), dev(d.values, device), dev(d.terminated, device),
                      dev(tr, device), dev(tv, device), dev(b, device), gamma, lam)
-    assert_parity(g, oracle.td_lambda(d.rewards, d.values, d.terminated, tr, tv, b, gamma, lam),
-                  f"td_lambda {what}")
+    assert_parity(g, oracle.td_lambda(d.rewards, d.values, d.terminated, tr, tv, b, f32(gamma),
+                                      f32(lam)), f"td_lambda {what}")
 
 
 def check_disc(d, device, trunc=True, boot=True, gamma=0.99, what=""):
@@ -72,7 +80,7 @@ def check_disc(d, device, trunc=True, boot=True, gamma=0.99, what=""):
     b = d.bootstrap if boot else None
     g = rl.discounted_returns(dev(d.rewards, device), dev(d.terminated, device),
                               dev(tr, device), dev(tv, device), dev(b, device), gamma)
-    assert_parity(g, oracle.discounted_returns(d.rewards, d.terminated, tr, tv, b, gamma),
+    assert_parity(g, oracle.discounted_returns(d.rewards, d.terminated, tr, tv, b, f32(gamma)),
                   f"discounted {what}")
 
 
@@ -86,7 +94,8 @@ def check_vtrace(d, device, trunc=True, boot=True, gamma=0.99, lam=1.0, rho_bar=
                        dev(d.terminated, device), dev(tr, device), dev(tv, device),
                        dev(b, device), gamma, lam, rho_bar, c_bar)
     ovs, opg = oracle.vtrace(d.rewards, d.values, d.behaviour_logp, d.target_logp,
-                             d.terminated, tr, tv, b, gamma, lam, rho_bar, c_bar)
+                             d.terminated, tr, tv, b, f32(gamma), f32(lam), f32(rho_bar),
+                             f32(c_bar))
     assert_parity(vs, ovs, f"vtrace vs {what}")
     assert_parity(pg, opg, f"vtrace pg {what}")
 
@@ -100,15 +109,15 @@ def check_retrace(d, device, trunc=True, boot=True, gamma=0.99, lam=0.95, c_bar=
                    dev(d.terminated, device), dev(tr, device), dev(tv, device), dev(b, device),
                    gamma, lam, c_bar)
     assert_parity(q, oracle.retrace(d.rewards, d.q_values, d.expected_q, d.behaviour_logp,
-                                    d.target_logp, d.terminated, tr, tv, b, gamma, lam, c_bar),
-                  f"retrace {what}")
+                                    d.target_logp, d.terminated, tr, tv, b, f32(gamma), f32(lam),
+                                    f32(c_bar)), f"retrace {what}")
 
 
 def check_forward(f, device, conv=rl.RESET_ON_START, gamma=0.99, lam=0.9, what=""):
     flags = f.starts if conv == rl.RESET_ON_START else f.dones
     fl = dev(flags, device)
     e = rl.eligibility_traces(dev(f.increments, device), fl, conv, gamma, lam)
-    assert_parity(e, oracle.eligibility_traces(f.increments, flags, conv, gamma, lam),
+    assert_parity(e, oracle.eligibility_traces(f.increments, flags, conv, f32(gamma), f32(lam)),
                   f"eligibility {what}")
     s = rl.episodic_prefix_sum(dev(f.rewards, device), fl, conv)
     assert_parity(s, oracle.episodic_prefix_sum(f.rewards, flags, conv), f"prefix f32 {what}")
@@ -370,8 +379,9 @@ def test_extreme_log_ratios_are_clipped(gpu_device):
     d.target_logp = d.target_logp.copy()
     d.target_logp[:, ::2] += 20.0
     d.target_logp[:, 1::5] -= 20.0
-    check_vtrace(d, gpu_device, rho_bar=1e3, c_bar=1e3, lam=0.5, what="clip")
-    check_retrace(d, gpu_device, c_bar=1e3, lam=0.2, what="clip")
+    # rho_bar = 1e3 shows the +5 side through rho; c_bar = 1 the -5 side through c
+    check_vtrace(d, gpu_device, rho_bar=1e3, c_bar=1.0, lam=0.5, what="clip")
+    check_retrace(d, gpu_device, c_bar=1.0, lam=0.2, what="clip")
 
 
 def test_repeat_calls_are_deterministic(gpu_device):

@@ -5,14 +5,9 @@ The bars are those of the fixed-shape tests: 1e-4 * (1 + |o|) for fp32
 storage, plus one output rounding (u |o|, u = 2^-8 / 2^-11) for bf16 /
 fp16, and bit-exact int32 sums.
 
-Trace clips stay at or below 1, so every coefficient |beta_t| <= 1 (the
-importance-weighted ones are gamma * lambda * min(c_bar, ratio)).  With
-c_bar > 1 the recurrence is expansive: products of beta grow, values reach
-1e10 and more over long rows, and rounding errors grow with them, so that
-even a sequential fp32 evaluation of the same recursion misses the 1e-4 bar
-on some elements (and fp16 storage overflows).  The bar is a statement about
-contracting recurrences; the clip thresholds themselves (rho_bar up to 2)
-are still drawn."""
+Trace clips are drawn in (0, 1], the range the library accepts (it refuses
+c_bar > 1, which would make the recurrence expansive), so every coefficient
+|beta_t| <= 1; rho_bar, which only scales alpha, is drawn up to 2."""
 import numpy as np
 import pytest
 import torch
