@@ -332,6 +332,29 @@ rlca_status rlca_gae_stats(const float *rewards, const float *values, const uint
                            int64_t T, float *advantages, float *returns, double *stats,
                            void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* rlca_gae_stats for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments without the workspace, the same kernels and the same results
+ * bit for bit.  The partial sums live instead in a buffer the library owns,
+ * RLCA_GAE_STATS_SCRATCH_BYTES of static device memory that each GPU the
+ * library runs on holds until the process ends; every size fits in it (the
+ * statistics launch never has more workgroups than it has pairs), and a
+ * call that would need more returns RLCA_ERR_INVALID_SIZE.  The call
+ * allocates nothing: the first call on each device looks up the buffer's
+ * address there (hipGetSymbolAddress, no allocation; a caller that captures
+ * graphs should make that first call before capturing), and RLCA_ERR_HIP
+ * reports a failed lookup.  Every call on one GPU shares its buffer, which
+ * keeps the last call's contents (nothing in it needs to start at zero):
+ * calls on one stream are ordered and safe, but calls that may overlap on
+ * one GPU (on different streams, or from threads that do not order them)
+ * race and must use rlca_gae_stats with workspaces of their own. */
+#define RLCA_GAE_STATS_SCRATCH_BYTES 65536
+rlca_status rlca_gae_stats_noalloc(const float *rewards, const float *values,
+                                   const uint8_t *terminated, const uint8_t *truncated,
+                                   const float *trunc_values, const float *bootstrap, float gamma,
+                                   float lambda, int64_t num_envs, int64_t T, float *advantages,
+                                   float *returns, double *stats, hipStream_t stream);
+
 size_t rlca_ppo_clip_loss_workspace_size(int64_t num_envs, int64_t T);
 
 /* PPO clipped surrogate (Schulman et al. 2017, L^CLIP) as a loss, over the

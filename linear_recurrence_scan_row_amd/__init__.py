@@ -22,6 +22,7 @@ from .rlca import (  # noqa: F401
     episodic_prefix_sum,
     gae,
     gae_stats,
+    gae_stats_noalloc,
     lib,
     ppo_clip_loss,
     retrace,

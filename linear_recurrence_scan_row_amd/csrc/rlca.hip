@@ -10,6 +10,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "kernels.hpp"
 #include "rlca.h"
 
@@ -624,6 +627,54 @@ static rlca_status check_extra_aliasing(const Call &c, const Span *extra, int n)
     return RLCA_OK;
 }
 
+// -------------------------------------------- statistics without a workspace
+// rlca_gae_stats_noalloc keeps its per-workgroup partial sums in this
+// library-owned buffer instead of a caller's workspace: one (sum, sum of
+// squares) pair per workgroup of the statistics launch, whose grid never
+// exceeds kStatsMaxGrid, so every size fits.  Each GPU the library runs on
+// holds its own copy until the process ends.  In host code `scratch` names
+// a host-side stand-in, never device memory: the kernels get the address
+// hipGetSymbolAddress returns for the current device (scratch_address).
+// Nothing in it needs to start at zero: every pair the finish kernel reads
+// was written by the same call's statistics launch.
+constexpr uint32_t kScratchPairs = 4096;
+static_assert(kScratchPairs >= kStatsMaxGrid, "one pair per statistics workgroup");
+static_assert(sizeof(double) * 2 * kScratchPairs == RLCA_GAE_STATS_SCRATCH_BYTES,
+              "the header states the buffer's size");
+static __device__ __align__(256) double scratch[2 * kScratchPairs];
+
+constexpr int kMaxScratchDevices = 64;
+static std::atomic<double *> scratch_ptr[kMaxScratchDevices];
+static std::mutex scratch_mutex;
+
+// The device address of `scratch` on the device that runs `stream`, looked
+// up on the first call for that device (with it current) and kept.
+static rlca_status scratch_address(hipStream_t stream, double **out) {
+    int device = -1;
+    if (stream == nullptr ? hipGetDevice(&device) != hipSuccess
+                          : hipStreamGetDevice(stream, &device) != hipSuccess)
+        return RLCA_ERR_HIP;
+    if (device < 0 || device >= kMaxScratchDevices) return RLCA_ERR_HIP;
+    double *p = scratch_ptr[device].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(scratch_mutex);
+        p = scratch_ptr[device].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            int current = -1;
+            if (hipGetDevice(&current) != hipSuccess) return RLCA_ERR_HIP;
+            if (current != device && hipSetDevice(device) != hipSuccess) return RLCA_ERR_HIP;
+            void *addr = nullptr;
+            const hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+            if (current != device && hipSetDevice(current) != hipSuccess) return RLCA_ERR_HIP;
+            if (e != hipSuccess || addr == nullptr) return RLCA_ERR_HIP;
+            p = static_cast<double *>(addr);
+            scratch_ptr[device].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return RLCA_OK;
+}
+
 extern "C" {
 
 rlca_status rlca_gae(const float *rewards, const float *values, const uint8_t *terminated,
@@ -742,6 +793,32 @@ rlca_status rlca_gae_stats(const float *rewards, const float *values, const uint
     st = launch_gae_stats(c.bp, c.shape, stream);
     if (st != RLCA_OK) return st;
     return launch_finish_stats(c.bp.stats_partials, pairs, num_envs * T, stats, stream);
+}
+
+rlca_status rlca_gae_stats_noalloc(const float *rewards, const float *values,
+                                   const uint8_t *terminated, const uint8_t *truncated,
+                                   const float *trunc_values, const float *bootstrap, float gamma,
+                                   float lambda, int64_t num_envs, int64_t T, float *advantages,
+                                   float *returns, double *stats, hipStream_t stream) {
+    Call c;
+    rlca_status st = prepare_gae(kStoreF32, rewards, values, terminated, truncated,
+                                 trunc_values, bootstrap, gamma, lambda, num_envs, T, advantages,
+                                 returns, &c);
+    if (st != RLCA_OK || c.empty) return st;
+    if (stats == nullptr) return RLCA_ERR_NULL_POINTER;
+    if (!aligned(stats, 8)) return RLCA_ERR_MISALIGNED;
+    const uint32_t pairs = launch_grid(c.shape, num_envs, T, kStatsMaxGrid);
+    if (pairs > kScratchPairs) return RLCA_ERR_INVALID_SIZE;
+    const Span extra[] = {{stats, 16}};
+    st = check_extra_aliasing(c, extra, 1);
+    if (st != RLCA_OK) return st;
+    double *partials = nullptr;
+    st = scratch_address(stream, &partials);
+    if (st != RLCA_OK) return st;
+    c.bp.stats_partials = partials;
+    st = launch_gae_stats(c.bp, c.shape, stream);
+    if (st != RLCA_OK) return st;
+    return launch_finish_stats(partials, pairs, num_envs * T, stats, stream);
 }
 
 size_t rlca_ppo_clip_loss_workspace_size(int64_t num_envs, int64_t T) {

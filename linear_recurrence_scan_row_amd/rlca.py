@@ -71,6 +71,7 @@ SIGNATURES = {
     "rlca_run_batch": [ctypes.POINTER(RlcaCall), _i, _p],
     "rlca_gae_stats": [_p, _p, _p, _p, _p, _p, _f, _f, _i64, _i64, _p, _p, _p, _p, _sz, _p],
     "rlca_ppo_clip_loss": [_p, _p, _p, _p, _f, _f, _i64, _i64, _p, _p, _p, _sz, _p],
+    "rlca_gae_stats_noalloc": [_p, _p, _p, _p, _p, _p, _f, _f, _i64, _i64, _p, _p, _p, _p],
 }
 # workspace-size queries (return size_t)
 SIZE_QUERIES = {
@@ -351,6 +352,26 @@ def gae_stats(rewards, values, terminated, truncated=None, trunc_values=None, bo
                                 p.arg("gamma"), p.arg("lambda_"), *p.shape, p.arg("out0"),
                                 p.arg("out1"), _ptr(st), _ptr(ws), nbytes, p.stream()),
            "rlca_gae_stats")
+    return p.result + (st,)
+
+
+def gae_stats_noalloc(rewards, values, terminated, truncated=None, trunc_values=None,
+                      bootstrap=None, gamma=0.99, lam=0.95, with_returns=True, advantages=None,
+                      returns=None, stats=None):
+    """gae_stats without a workspace: the partial sums go to the library's own
+    static device buffer (rlca_gae_stats_noalloc).  Pass advantages, returns
+    and stats tensors to make the call allocate nothing at all."""
+    p = _prepare_gae(rewards, values, terminated, truncated, trunc_values, bootstrap, gamma,
+                     lam, with_returns, advantages, returns)
+    if not p.f32:
+        raise TypeError("gae_stats_noalloc takes float32 arrays")
+    st = _out(stats, (2,), p.dev, torch.float64, name="stats")
+    _check(lib().rlca_gae_stats_noalloc(p.arg("rewards"), p.arg("values"), p.arg("terminated"),
+                                        p.arg("truncated"), p.arg("trunc_values"),
+                                        p.arg("bootstrap"), p.arg("gamma"), p.arg("lambda_"),
+                                        *p.shape, p.arg("out0"), p.arg("out1"), _ptr(st),
+                                        p.stream()),
+           "rlca_gae_stats_noalloc")
     return p.result + (st,)
 
 

@@ -272,6 +272,22 @@ def test_gae_stats_validation(lib):
     assert gae_stats(lib, ws=F + 8) == ALIAS                 # workspace over the stats
 
 
+def test_gae_stats_noalloc_validation(lib):
+    """Checks that run before the entry point touches the GPU (the scratch
+    buffer's address is looked up only after them)."""
+    def call(stats=F, gamma=0.99, n=4, r=A):
+        return lib.rlca_gae_stats_noalloc(r, B, C, None, None, None, gamma, 0.95, n, 8, D, E,
+                                          stats, None)
+    assert call(n=0) == OK
+    assert call(stats=None) == NULLP
+    assert call(r=None) == NULLP
+    assert call(stats=F + 4) == MISAL
+    assert call(gamma=1.5) == VALUE
+    assert call(stats=D) == ALIAS            # stats over the advantages
+    text = open(HEADER).read()
+    assert re.search(r"#define\s+RLCA_GAE_STATS_SCRATCH_BYTES\s+65536\b", text)
+
+
 def test_ppo_clip_loss_validation(lib):
     assert ppo(lib, n=0) == OK
     for clip in (-0.1, 1.0, float("nan")):
