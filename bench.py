@@ -533,7 +533,7 @@ def measured_traffic(kernel_name, workload):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    from linear_recurrence_scan_row_amd.profiling import source_digest
+    from profiling import source_digest
 
     if kv.get("source_digest") != source_digest():
         return None

@@ -39,8 +39,10 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False, extra=None, out: str = LIB_PATH, jobs: int = 8) -> str:
-    """Compile every translation unit (up to `jobs` at once) and link `out`."""
+def build(verbose: bool = False, extra=None, out: str = LIB_PATH, jobs: int = 8,
+          link_extra=None) -> str:
+    """Compile every translation unit (up to `jobs` at once, with `extra`
+    flags) and link `out` (with `link_extra` flags)."""
     tag = os.path.splitext(os.path.basename(out))[0]
     obj_dir = os.path.join(BUILD_DIR, tag)
     os.makedirs(obj_dir, exist_ok=True)
@@ -65,7 +67,8 @@ def build(verbose: bool = False, extra=None, out: str = LIB_PATH, jobs: int = 8)
     if failed:
         raise RuntimeError(f"hipcc failed for: {', '.join(failed)}")
     tmp = out + ".tmp"
-    link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+    link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *(link_extra or []), "-o", tmp,
+            *objs]
     if verbose:
         print(" ".join(link), flush=True)
     subprocess.run(link, check=True)

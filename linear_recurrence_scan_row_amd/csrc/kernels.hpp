@@ -1364,10 +1364,7 @@ enum GroupClass : int {
 constexpr int kGroupClasses = 5;
 // Minimum waves per SIMD each class kernel is compiled for (one-shot shapes
 // need all eight slots; the light wave-local bodies fit eight by themselves).
-#ifndef RLCA_GROUP_CLASS_WAVES
-#define RLCA_GROUP_CLASS_WAVES {1, 8, 8, 8, 8}
-#endif
-constexpr int kGroupClassWaves[kGroupClasses] = RLCA_GROUP_CLASS_WAVES;
+constexpr int kGroupClassWaves[kGroupClasses] = {1, 8, 8, 8, 8};
 
 inline int group_class(const LaunchShape &s, bool weighted) {
     if (s.skew) return kGroupSkew;

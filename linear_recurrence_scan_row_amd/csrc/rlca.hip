@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <string.h>
 
 #include <atomic>
 #include <mutex>
@@ -22,6 +23,18 @@ static bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
     if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
     const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
     return a0 < b0 + nb && b0 < a0 + na;
+}
+
+// Enum arguments come from C, where an enum parameter may hold any int; in
+// C++ a load of a value outside the enumerators' range is undefined, so the
+// entry points read enum arguments by their int representation and check
+// them as ints.
+template <typename E>
+static int enum_code(const E &e) {
+    static_assert(sizeof(E) == sizeof(int), "C enums are int-sized on this ABI");
+    int code;
+    memcpy(&code, &e, sizeof code);
+    return code;
 }
 
 static bool unit_interval(float x) { return x >= 0.f && x <= 1.f; }  // false for NaN
@@ -547,7 +560,7 @@ static rlca_status prepare_affine(int storage, const void *alpha, const void *be
 // the storage of every real-valued array (and int32 for the prefix sum).
 static rlca_status prepare_op(const rlca_call &k, Call *c) {
     const int st = storage_of(k.dtype);  // -1 (rejected) for RLCA_I32 outside the prefix sum
-    switch (k.op) {
+    switch (enum_code(k.op)) {
         case RLCA_OP_GAE:
             return prepare_gae(st, k.rewards, k.values, k.terminated, k.truncated,
                                k.trunc_values, k.bootstrap, k.gamma, k.lambda, k.num_envs, k.T,
@@ -744,8 +757,9 @@ rlca_status rlca_eligibility_traces(const float *increments, const uint8_t *flag
                                     float lambda, int64_t num_envs, int64_t T, float *traces,
                                     hipStream_t stream) {
     Call c;
-    const rlca_status st = prepare_eligibility(kStoreF32, increments, flags, convention, gamma,
-                                               lambda, num_envs, T, traces, &c);
+    const rlca_status st = prepare_eligibility(kStoreF32, increments, flags,
+                                               enum_code(convention), gamma, lambda, num_envs, T,
+                                               traces, &c);
     return run_one(st, c, stream);
 }
 
@@ -753,8 +767,9 @@ rlca_status rlca_episodic_prefix_sum(const void *x, rlca_dtype dtype, const uint
                                      rlca_reset_convention convention, int64_t num_envs,
                                      int64_t T, void *out, hipStream_t stream) {
     Call c;
-    return run_one(prepare_prefix_sum(x, dtype, flags, convention, num_envs, T, out, &c), c,
-                   stream);
+    const rlca_status st = prepare_prefix_sum(x, enum_code(dtype), flags, enum_code(convention),
+                                              num_envs, T, out, &c);
+    return run_one(st, c, stream);
 }
 
 rlca_status rlca_affine_scan(const float *alpha, const float *beta, const float *carry,
@@ -762,7 +777,7 @@ rlca_status rlca_affine_scan(const float *alpha, const float *beta, const float 
                              hipStream_t stream) {
     Call c;
     const rlca_status st =
-        prepare_affine(kStoreF32, alpha, beta, carry, direction, num_envs, T, out, &c);
+        prepare_affine(kStoreF32, alpha, beta, carry, enum_code(direction), num_envs, T, out, &c);
     return run_one(st, c, stream);
 }
 
@@ -942,7 +957,7 @@ rlca_status rlca_run_batch(const rlca_call *calls, int count, hipStream_t stream
 }
 
 const char *rlca_status_string(rlca_status status) {
-    switch (status) {
+    switch (enum_code(status)) {
         case RLCA_OK: return "ok";
         case RLCA_ERR_NULL_POINTER: return "a required pointer is NULL";
         case RLCA_ERR_INVALID_SIZE: return "invalid size (negative, too large or overflowing)";

@@ -1,11 +1,11 @@
 """Summaries of rocprofv3 results (the SQLite ``*_results.db`` it writes) for the
 credit-assignment kernels.
 
-  python -m linear_recurrence_scan_row_amd.profiling stats DB [--command CMD]
+  python profiling.py stats DB [--command CMD]
       per-kernel dispatch count and average / min / max duration (us), from a
       ``rocprofv3 --kernel-trace --stats`` run.
 
-  python -m linear_recurrence_scan_row_amd.profiling traffic --fetch DB --write DB
+  python profiling.py traffic --fetch DB --write DB
          --kernel SUBSTR --copy-bytes N --algorithmic-bytes B --out FILE [...]
       HBM bytes per launch of one kernel (or per step of several, --kernel
       repeated) from a ``--pmc FETCH_SIZE`` run and a
@@ -14,7 +14,7 @@ credit-assignment kernels.
       written) captured in the same runs: on gfx950 FETCH_SIZE reads about
       half of the bytes a copy really fetches, WRITE_SIZE reads them exactly.
 
-  python -m linear_recurrence_scan_row_amd.profiling counters DB [DB ...]
+  python profiling.py counters DB [DB ...]
          --kernel SUBSTR [--command CMD ...]
       median per dispatch of every counter in ``--pmc`` runs, for the kernels
       whose name contains SUBSTR, and per wave where the runs hold SQ_WAVES.
@@ -28,7 +28,7 @@ import os
 import sqlite3
 import sys
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
 def _kernel_sources():

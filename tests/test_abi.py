@@ -332,7 +332,7 @@ def test_product_package_never_imports_the_oracle():
     import sys
     code = ("import sys\n"
             "import linear_recurrence_scan_row_amd as rl\n"
-            "from linear_recurrence_scan_row_amd import rlca, build, workloads, profiling\n"
+            "from linear_recurrence_scan_row_amd import rlca, build, workloads\n"
             "rl.lib()\n"
             "bad = [m for m in sys.modules if m == 'oracle' or m.startswith('oracle.')]\n"
             "raise SystemExit(f'oracle imported: {bad}' if bad else 0)\n")
