@@ -170,8 +170,8 @@ def make_sets(torch, arrays, calls, device, min_call_bytes, real=None):
             if k in named:
                 s[k] = torch.zeros(2, dtype=torch.float64, device=device)
         for k in ("ws", "ws2"):
-            if k in named:
-                s[k] = torch.empty(WORKSPACE_BYTES, dtype=torch.uint8, device=device)
+            if k in named:   # zero-filled once; every call leaves it so
+                s[k] = torch.zeros(WORKSPACE_BYTES, dtype=torch.uint8, device=device)
         sets.append(s)
     return sets
 

@@ -15,7 +15,7 @@
  * that run in parallel: three launches, inputs read twice, and the first
  * output array holds the chunk hand-off values until the last launch
  * overwrites them.  The fused consumers of GAE at the end of this header
- * add one small launch each, which finishes their reduction.
+ * are one launch each too.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -307,17 +307,22 @@ rlca_status rlca_run_batch(const rlca_call *calls, int count, hipStream_t stream
  * The summary's §9 (Discussion and Future Work) names fused loss operations
  * as the next step for the library; these two calls fuse the usual PPO
  * consumers of the advantages into the scan's epilogue and into one
- * streaming pass.  Each is two launches: the pass, which leaves one partial
- * sum per workgroup in a caller-owned device workspace, then a one-workgroup
- * launch that adds the partials in a fixed order (reproducible bit for
- * bit).  The *_workspace_size call returns the workspace's size (0 for an
- * empty rollout or invalid sizes); its contents on entry do not matter and
- * are overwritten.  The workspace is written like an output: calls that may
- * run at the same time need workspaces of their own.  workspace, stats and
- * loss must be 8-byte aligned; RLCA_ERR_INVALID_SIZE if workspace_bytes is
- * too small; RLCA_ERR_ALIASING if the workspace, stats or loss overlap any
- * other array of the call.  An empty rollout (num_envs * T == 0) writes
- * nothing. */
+ * streaming pass.  Each is one launch: every workgroup leaves one partial
+ * sum in a caller-owned device workspace and takes a ticket from counters
+ * at the workspace's start; the workgroup that takes the last ticket adds
+ * the partials in a fixed order (reproducible bit for bit, whichever
+ * workgroup is last), writes the result and sets the counters back to
+ * zero.  The *_workspace_size call returns the workspace's size (0 for
+ * an empty rollout or invalid sizes).  The workspace must be zero-filled
+ * before its first use (one hipMemset, or a zero-filled allocation); every
+ * call leaves it so, so it can be reused by later calls of either consumer
+ * and any size up to its own.  A launch that did not run to completion
+ * (a fault) may leave the counter set: zero the workspace again.  The
+ * workspace is written like an output: calls that may run at the same time
+ * need workspaces of their own.  workspace, stats and loss must be 8-byte
+ * aligned; RLCA_ERR_INVALID_SIZE if workspace_bytes is too small;
+ * RLCA_ERR_ALIASING if the workspace, stats or loss overlap any other array
+ * of the call.  An empty rollout (num_envs * T == 0) writes nothing. */
 size_t rlca_gae_stats_workspace_size(int64_t num_envs, int64_t T);
 
 /* rlca_gae (fp32) that also reduces the advantages it computes: stats is
@@ -335,20 +340,21 @@ rlca_status rlca_gae_stats(const float *rewards, const float *values, const uint
 /* rlca_gae_stats for callers that cannot allocate (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same
  * arguments without the workspace, the same kernels and the same results
- * bit for bit.  The partial sums live instead in a buffer the library owns,
- * RLCA_GAE_STATS_SCRATCH_BYTES of static device memory that each GPU the
- * library runs on holds until the process ends; every size fits in it (the
- * statistics launch never has more workgroups than it has pairs), and a
- * call that would need more returns RLCA_ERR_INVALID_SIZE.  The call
- * allocates nothing: the first call on each device looks up the buffer's
- * address there (hipGetSymbolAddress, no allocation; a caller that captures
- * graphs should make that first call before capturing), and RLCA_ERR_HIP
- * reports a failed lookup.  Every call on one GPU shares its buffer, which
- * keeps the last call's contents (nothing in it needs to start at zero):
- * calls on one stream are ordered and safe, but calls that may overlap on
- * one GPU (on different streams, or from threads that do not order them)
- * race and must use rlca_gae_stats with workspaces of their own. */
-#define RLCA_GAE_STATS_SCRATCH_BYTES 65536
+ * bit for bit.  The ticket counter and partial sums live instead in a
+ * buffer the library owns, RLCA_GAE_STATS_SCRATCH_BYTES of static device
+ * memory that each GPU the library runs on holds until the process ends;
+ * every size fits in it (the statistics launch never has more workgroups
+ * than it has pairs), and a call that would need more returns
+ * RLCA_ERR_INVALID_SIZE.  The call allocates nothing: the first call on
+ * each device looks up the buffer's address there (hipGetSymbolAddress, no
+ * allocation) and enqueues the zeroing of its counters on `stream`, one
+ * small kernel (a caller that captures graphs should make that first call
+ * before capturing); RLCA_ERR_HIP reports a failed lookup.  Every call on
+ * one GPU shares its buffer and leaves its counters at zero: calls on one
+ * stream are ordered and safe, but calls that may overlap on one GPU (on
+ * different streams, or from threads that do not order them) race and
+ * must use rlca_gae_stats with workspaces of their own. */
+#define RLCA_GAE_STATS_SCRATCH_BYTES 69760
 rlca_status rlca_gae_stats_noalloc(const float *rewards, const float *values,
                                    const uint8_t *terminated, const uint8_t *truncated,
                                    const float *trunc_values, const float *bootstrap, float gamma,

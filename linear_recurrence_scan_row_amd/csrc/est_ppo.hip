@@ -1,64 +1,15 @@
-// est_ppo.hip -- fused consumers of the advantages: the final reduction of
-// the statistics the GAE epilogue leaves per workgroup, and the PPO clipped
-// surrogate (Schulman et al. 2017), which normalizes the advantages on the fly
-// from those statistics and reduces the loss per workgroup.  Every reduction
-// runs in a fixed order, so results are reproducible bit for bit.
+// est_ppo.hip -- the PPO clipped surrogate (Schulman et al. 2017), a fused
+// consumer of the advantages: it normalizes them on the fly from the
+// statistics rlca_gae_stats computes, and reduces the loss in the same
+// launch (the last workgroup adds the per-workgroup sums, kernels.hpp).
+// Every reduction runs in a fixed order, so results are reproducible bit for
+// bit.
 #include "kernels.hpp"
 
 namespace rlca {
 
-constexpr int kFinishThreads = 4 * kWave;
-constexpr int kFinishBatch = 16;  // independent loads in flight per lane
 constexpr int kPpoThreads = 256;
 constexpr uint32_t kPpoMaxGrid = 2048;
-
-// Sum of `count` (a, b) pairs (b skipped when stride is 1) in fixed order:
-// strided per lane in batches of independent loads, then across the
-// workgroup.  One workgroup.
-__device__ __forceinline__ void sum_pairs(const double *pairs, uint32_t count, int stride,
-                                          double &a, double &b) {
-    a = 0.0;
-    b = 0.0;
-    for (uint32_t i0 = threadIdx.x; i0 < count; i0 += kFinishThreads * kFinishBatch) {
-        double va[kFinishBatch], vb[kFinishBatch];
-#pragma unroll
-        for (int k = 0; k < kFinishBatch; ++k) {
-            const uint32_t i = i0 + k * kFinishThreads;
-            va[k] = i < count ? pairs[(size_t)i * stride] : 0.0;
-            vb[k] = i < count && stride == 2 ? pairs[(size_t)i * 2 + 1] : 0.0;
-        }
-#pragma unroll
-        for (int k = 0; k < kFinishBatch; ++k) {
-            a += va[k];
-            b += vb[k];
-        }
-    }
-    workgroup_sum2<kFinishThreads / kWave>(a, b);
-}
-
-// stats = {mean, sample std (divisor M - 1; 0 when M < 2)} from the (sum,
-// sum of squares) partials.
-__global__ __launch_bounds__(kFinishThreads) void finish_stats(const double *partials,
-                                                               uint32_t count, int64_t M,
-                                                               double *stats) {
-    double s1, s2;
-    sum_pairs(partials, count, 2, s1, s2);
-    if (threadIdx.x == 0) {
-        const double mean = s1 / (double)M;
-        const double var = M > 1 ? fmax(s2 - s1 * mean, 0.0) / (double)(M - 1) : 0.0;
-        stats[0] = mean;
-        stats[1] = sqrt(var);
-    }
-}
-
-// loss = -(sum of the per-workgroup surrogate sums) / M.
-__global__ __launch_bounds__(kFinishThreads) void finish_loss(const double *partials,
-                                                              uint32_t count, int64_t M,
-                                                              double *loss) {
-    double s, unused;
-    sum_pairs(partials, count, 1, s, unused);
-    if (threadIdx.x == 0) loss[0] = -s / (double)M;
-}
 
 // One step of the clipped surrogate: returns min(rho A, clip(rho) A) and sets
 // the gradient of the loss in logp_new (-rho A / M on the unclipped branch,
@@ -76,12 +27,13 @@ __device__ __forceinline__ float ppo_term(float a, float lp_new, float lp_old, f
 // NORM: A_hat = (A - mean) * 1/(std + norm_eps) from stats; VEC: four steps
 // per load (16-byte aligned arrays), the last M % 4 steps one per lane of
 // workgroup 0.  Grid-stride over the steps; each workgroup leaves the sum of
-// its surrogate terms in partials.
+// its surrogate terms in partials, and the last one to finish writes loss.
 template <bool NORM, bool GRAD, bool VEC>
 __global__ __launch_bounds__(kPpoThreads) void ppo_clip_loss(
     const float *__restrict__ adv, const double *__restrict__ stats,
     const float *__restrict__ logp_new, const float *__restrict__ logp_old, float clip_eps,
-    float norm_eps, int64_t M, float *__restrict__ grad, double *__restrict__ partials) {
+    float norm_eps, int64_t M, float *__restrict__ grad, double *__restrict__ partials,
+    double *__restrict__ loss) {
     const float lo = 1.f - clip_eps, hi = 1.f + clip_eps;
     const float neg_inv_m = (float)(-1.0 / (double)M);
     double acc = 0.0;
@@ -144,15 +96,9 @@ __global__ __launch_bounds__(kPpoThreads) void ppo_clip_loss(
     }
     double unused = 0.0;
     workgroup_sum2<kPpoThreads / kWave>(acc, unused);
-    if (threadIdx.x == 0) partials[blockIdx.x] = acc;
-}
-
-rlca_status launch_finish_stats(const double *partials, uint32_t count, int64_t M,
-                                double *stats, hipStream_t stream) {
-    void *args[] = {&partials, &count, &M, &stats};
-    const hipError_t e = hipLaunchKernel((const void *)finish_stats, dim3(1),
-                                         dim3(kFinishThreads), args, 0, stream);
-    return e == hipSuccess ? RLCA_OK : RLCA_ERR_HIP;
+    // loss = -(sum of the per-workgroup surrogate sums) / M
+    finish_in_last_workgroup<kPpoThreads, 1>(
+        partials, acc, 0.0, [=](double s, double) { loss[0] = -s / (double)M; });
 }
 
 uint32_t ppo_grid(int64_t M) {
@@ -163,11 +109,12 @@ uint32_t ppo_grid(int64_t M) {
 
 rlca_status launch_ppo_clip_loss(const float *adv, const double *stats, const float *logp_new,
                                  const float *logp_old, float clip_eps, float norm_eps,
-                                 int64_t M, bool vec, float *grad, double *partials,
+                                 int64_t M, bool vec, float *grad, void *workspace,
                                  double *loss, hipStream_t stream) {
     const uint32_t grid = ppo_grid(M);
+    double *partials = reinterpret_cast<double *>(static_cast<char *>(workspace) + kTicketBytes);
     void *args[] = {&adv, &stats, &logp_new, &logp_old, &clip_eps, &norm_eps,
-                    &M,   &grad,  &partials};
+                    &M,   &grad,  &partials, &loss};
     const bool norm = stats != nullptr, with_grad = grad != nullptr;
 #define RLCA_PPO(N, G, V) (const void *)ppo_clip_loss<N, G, V>
     const void *kernels[8] = {RLCA_PPO(false, false, false), RLCA_PPO(false, false, true),
@@ -176,13 +123,7 @@ rlca_status launch_ppo_clip_loss(const float *adv, const double *stats, const fl
                               RLCA_PPO(true, true, false),   RLCA_PPO(true, true, true)};
 #undef RLCA_PPO
     const void *kernel = kernels[(norm ? 4 : 0) + (with_grad ? 2 : 0) + (vec ? 1 : 0)];
-    hipError_t e = hipLaunchKernel(kernel, dim3(grid), dim3(kPpoThreads), args, 0, stream);
-    if (e != hipSuccess) return RLCA_ERR_HIP;
-    uint32_t count = grid;
-    const double *cp = partials;
-    void *fargs[] = {&cp, &count, &M, &loss};
-    e = hipLaunchKernel((const void *)finish_loss, dim3(1), dim3(kFinishThreads), fargs, 0,
-                        stream);
+    const hipError_t e = hipLaunchKernel(kernel, dim3(grid), dim3(kPpoThreads), args, 0, stream);
     return e == hipSuccess ? RLCA_OK : RLCA_ERR_HIP;
 }
 

@@ -96,7 +96,12 @@ struct BackwardParams {
     const void *bootstrap;  // carry A_T for kAffineBackward
     void *out0;             // advantages / returns / vs / q_ret / A
     void *out1;             // GAE returns or V-Trace pg advantages; may be null
-    double *stats_partials;  // with STATS: (sum, sum of squares) of out0 per workgroup
+    // with STATS: (sum, sum of squares) of out0 per workgroup, after the
+    // workspace's ticket counter (kTicketBytes); the last workgroup writes
+    // {mean, sample std} to stats
+    double *stats_partials;
+    double *stats;
+    int64_t stats_count;  // N * T
     float gamma, lambda, rho_bar, c_bar;
     Geometry geo;
 };
@@ -472,6 +477,112 @@ __device__ __forceinline__ void workgroup_sum2(double &a, double &b) {
     }
 }
 
+// ------------------------------------------------- last-workgroup reductions
+// The fused consumers reduce over the whole launch in one launch: each
+// workgroup publishes one partial (a pair of doubles, STRIDE 2, or one
+// double, STRIDE 1) in a workspace that starts with ticket counters, and
+// the workgroup that takes the last ticket adds all the partials in a fixed
+// order (the same result whichever workgroup finishes last) and restores
+// the counters to zero.  No workgroup waits for another.
+//
+// Visibility without a cache write-back: the partials are written and read
+// with agent-scope atomic stores and loads, which the hardware performs
+// coherently across the chip's XCDs by themselves (an agent-scope release
+// fence would instead write back the XCD's whole L2, once per workgroup).
+// A workgroup takes its ticket only after its stores have completed
+// (s_waitcnt), and a ticket's holder issues later operations only after the
+// ticket has returned, so the last ticket's holder sees every partial.
+//
+// Two levels of tickets: agent-scope atomics on one address serialize at
+// about 12 ns each (measured: 512 workgroups add 5 us to a launch, 4096 add
+// 44 us), while atomics on addresses 128 bytes apart proceed in parallel.
+// Workgroup g takes a ticket on slot g % kTicketSlots; the last workgroup
+// of each slot takes one on the top counter, and the last of those reduces.
+constexpr int kTicketSlots = 32;
+constexpr int kTicketStride = 32;  // words between counters: 128 bytes
+constexpr size_t kTicketBytes = (size_t)(kTicketSlots + 1) * kTicketStride * 4;
+
+__device__ __forceinline__ uint32_t *ticket_counters(double *partials) {
+    return reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(partials) - kTicketBytes);
+}
+
+__device__ __forceinline__ void store_coherent(double *p, double x) {
+    __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ double load_coherent(const double *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t take_ticket(uint32_t *counter) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);  // keep the compiler's order too
+    __builtin_amdgcn_s_waitcnt(0);             // earlier stores have completed
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+constexpr int kFinishBatch = 16;  // independent loads in flight per lane
+
+// Sum of `count` (a, b) partials (b only with STRIDE 2) in fixed order:
+// strided over the NT threads in batches of independent loads, then across
+// the workgroup.
+template <int NT, int STRIDE>
+__device__ __forceinline__ void sum_partials(const double *partials, uint32_t count, double &a,
+                                             double &b) {
+    a = 0.0;
+    b = 0.0;
+    for (uint32_t i0 = threadIdx.x; i0 < count; i0 += NT * kFinishBatch) {
+        double va[kFinishBatch], vb[kFinishBatch];
+#pragma unroll
+        for (int k = 0; k < kFinishBatch; ++k) {
+            const uint32_t i = i0 + k * NT;
+            va[k] = i < count ? load_coherent(partials + (size_t)i * STRIDE) : 0.0;
+            vb[k] = i < count && STRIDE == 2 ? load_coherent(partials + (size_t)i * 2 + 1) : 0.0;
+        }
+#pragma unroll
+        for (int k = 0; k < kFinishBatch; ++k) {
+            a += va[k];
+            b += vb[k];
+        }
+    }
+    workgroup_sum2<NT / kWave>(a, b);
+}
+
+// Publish this workgroup's partial (a, b) -- the values thread 0 holds --
+// and take tickets; the last workgroup sums every partial and calls
+// done(a, b) on thread 0, then clears the top counter (each slot's last
+// workgroup clears its slot's).  Every thread of the workgroup must call
+// it; the barrier also separates this workgroup's own reduction from the
+// final one (they share LDS).
+template <int NT, int STRIDE, typename Done>
+__device__ __forceinline__ void finish_in_last_workgroup(double *partials, double a, double b,
+                                                         Done done) {
+    __shared__ uint32_t last;
+    uint32_t *counters = ticket_counters(partials);
+    if (threadIdx.x == 0) {
+        const uint32_t g = blockIdx.x, groups = gridDim.x;
+        store_coherent(partials + (size_t)g * STRIDE, a);
+        if constexpr (STRIDE == 2) store_coherent(partials + (size_t)g * 2 + 1, b);
+        const uint32_t slot = g % kTicketSlots;
+        const uint32_t in_slot = (groups - 1 - slot) / kTicketSlots + 1;  // workgroups of the slot
+        uint32_t *slot_counter = counters + slot * kTicketStride;
+        bool is_last = false;
+        if (take_ticket(slot_counter) + 1 == in_slot) {
+            __hip_atomic_store(slot_counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint32_t slots = groups < (uint32_t)kTicketSlots ? groups : kTicketSlots;
+            is_last = take_ticket(counters + kTicketSlots * kTicketStride) + 1 == slots;
+        }
+        last = is_last ? 1u : 0u;  // the loads below wait for the tickets
+    }
+    __syncthreads();
+    if (last == 0u) return;
+    double sa, sb;
+    sum_partials<NT, STRIDE>(partials, gridDim.x, sa, sb);
+    if (threadIdx.x == 0) {
+        done(sa, sb);
+        __hip_atomic_store(counters + kTicketSlots * kTicketStride, 0u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 // ------------------------------------------------------- leading kernel arguments
 // The geometry and the first five input arrays are passed as separate scalar
 // kernel arguments ahead of the parameter block: gfx950 preloads leading
@@ -823,10 +934,16 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
     } while (g < p.geo.num_groups);
     if constexpr (STATS) {
         workgroup_sum2<NW>(sum, sum_sq);
-        if (threadIdx.x == 0) {
-            p.stats_partials[2 * (size_t)blockIdx.x] = sum;
-            p.stats_partials[2 * (size_t)blockIdx.x + 1] = sum_sq;
-        }
+        // stats = {mean, sample std (divisor M - 1; 0 when M < 2)}
+        double *stats = p.stats;
+        const int64_t M = p.stats_count;
+        finish_in_last_workgroup<NW * kWave, 2>(p.stats_partials, sum, sum_sq,
+                                                [=](double s1, double s2) {
+            const double mean = s1 / (double)M;
+            const double var = M > 1 ? fmax(s2 - s1 * mean, 0.0) / (double)(M - 1) : 0.0;
+            stats[0] = mean;
+            stats[1] = sqrt(var);
+        });
     }
 }
 
@@ -1378,16 +1495,15 @@ rlca_status launch_grouped(const GroupedLaunch &launch, int storage, int cls,
 
 // One translation unit per estimator instantiates these (see est_*.hip).
 rlca_status launch_gae(BackwardParams &p, const LaunchShape &s, int storage, hipStream_t stream);
-// GAE (fp32) that also leaves per-workgroup (sum, sum of squares) of the
-// advantages in p.stats_partials: launch_grid(s, ..., kStatsMaxGrid) pairs.
+// GAE (fp32) that also reduces the advantages to p.stats in the same launch:
+// launch_grid(s, ..., kStatsMaxGrid) (sum, sum of squares) pairs at
+// p.stats_partials, behind the workspace's ticket counter.
 rlca_status launch_gae_stats(BackwardParams &p, const LaunchShape &s, hipStream_t stream);
-// Fused consumers (est_ppo.hip).
-rlca_status launch_finish_stats(const double *partials, uint32_t count, int64_t M,
-                                double *stats, hipStream_t stream);
+// Fused consumers (est_ppo.hip).  `workspace` starts with the ticket counter.
 uint32_t ppo_grid(int64_t M);
 rlca_status launch_ppo_clip_loss(const float *adv, const double *stats, const float *logp_new,
                                  const float *logp_old, float clip_eps, float norm_eps,
-                                 int64_t M, bool vec, float *grad, double *partials,
+                                 int64_t M, bool vec, float *grad, void *workspace,
                                  double *loss, hipStream_t stream);
 rlca_status launch_td_lambda(BackwardParams &p, const LaunchShape &s, int storage,
                              hipStream_t stream);

@@ -648,27 +648,37 @@ static rlca_status check_extra_aliasing(const Call &c, const Span *extra, int n)
 // holds its own copy until the process ends.  In host code `scratch` names
 // a host-side stand-in, never device memory: the kernels get the address
 // hipGetSymbolAddress returns for the current device (scratch_address).
-// Nothing in it needs to start at zero: every pair the finish kernel reads
-// was written by the same call's statistics launch.
+// Its first kTicketBytes hold the ticket counters of the statistics launch
+// (see kernels.hpp, finish_in_last_workgroup), which must start at zero:
+// the first call on each device clears them, on its stream, and every call
+// leaves them at zero.  Every pair the last workgroup reads was written by
+// the same launch.
 constexpr uint32_t kScratchPairs = 4096;
 static_assert(kScratchPairs >= kStatsMaxGrid, "one pair per statistics workgroup");
-static_assert(sizeof(double) * 2 * kScratchPairs == RLCA_GAE_STATS_SCRATCH_BYTES,
+static_assert(kTicketBytes + 16 * kScratchPairs == RLCA_GAE_STATS_SCRATCH_BYTES,
               "the header states the buffer's size");
-static __device__ __align__(256) double scratch[2 * kScratchPairs];
+static __device__ __align__(256) double scratch[(kTicketBytes + 16 * kScratchPairs) / 8];
+
+// Zero the buffer's ticket counters: run once per device, before its first
+// use (every call leaves them at zero).
+__global__ void clear_tickets(uint32_t *counters) {
+    for (uint32_t i = threadIdx.x; i < kTicketBytes / 4; i += blockDim.x) counters[i] = 0u;
+}
 
 constexpr int kMaxScratchDevices = 64;
-static std::atomic<double *> scratch_ptr[kMaxScratchDevices];
+static std::atomic<void *> scratch_ptr[kMaxScratchDevices];
 static std::mutex scratch_mutex;
 
 // The device address of `scratch` on the device that runs `stream`, looked
-// up on the first call for that device (with it current) and kept.
-static rlca_status scratch_address(hipStream_t stream, double **out) {
+// up on the first call for that device (with it current) and kept; that
+// first call also enqueues the clearing of its ticket counters on `stream`.
+static rlca_status scratch_address(hipStream_t stream, void **out) {
     int device = -1;
     if (stream == nullptr ? hipGetDevice(&device) != hipSuccess
                           : hipStreamGetDevice(stream, &device) != hipSuccess)
         return RLCA_ERR_HIP;
     if (device < 0 || device >= kMaxScratchDevices) return RLCA_ERR_HIP;
-    double *p = scratch_ptr[device].load(std::memory_order_acquire);
+    void *p = scratch_ptr[device].load(std::memory_order_acquire);
     if (p == nullptr) {
         std::lock_guard<std::mutex> lock(scratch_mutex);
         p = scratch_ptr[device].load(std::memory_order_relaxed);
@@ -680,7 +690,12 @@ static rlca_status scratch_address(hipStream_t stream, double **out) {
             const hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
             if (current != device && hipSetDevice(current) != hipSuccess) return RLCA_ERR_HIP;
             if (e != hipSuccess || addr == nullptr) return RLCA_ERR_HIP;
-            p = static_cast<double *>(addr);
+            uint32_t *counters = static_cast<uint32_t *>(addr);
+            void *args[] = {&counters};
+            if (hipLaunchKernel((const void *)clear_tickets, dim3(1), dim3(256), args, 0,
+                                stream) != hipSuccess)
+                return RLCA_ERR_HIP;
+            p = addr;
             scratch_ptr[device].store(p, std::memory_order_release);
         }
     }
@@ -784,7 +799,7 @@ rlca_status rlca_affine_scan(const float *alpha, const float *beta, const float 
 size_t rlca_gae_stats_workspace_size(int64_t num_envs, int64_t T) {
     int64_t n;
     if (check_sizes(num_envs, T, &n) != RLCA_OK || n == 0) return 0;
-    return 16 * (size_t)gae_stats_pairs(num_envs, T);
+    return kTicketBytes + 16 * (size_t)gae_stats_pairs(num_envs, T);
 }
 
 rlca_status rlca_gae_stats(const float *rewards, const float *values, const uint8_t *terminated,
@@ -800,14 +815,16 @@ rlca_status rlca_gae_stats(const float *rewards, const float *values, const uint
     if (stats == nullptr || workspace == nullptr) return RLCA_ERR_NULL_POINTER;
     if (!aligned(stats, 8) || !aligned(workspace, 8)) return RLCA_ERR_MISALIGNED;
     const uint32_t pairs = launch_grid(c.shape, num_envs, T, kStatsMaxGrid);
-    if (workspace_bytes < 16 * (size_t)pairs) return RLCA_ERR_INVALID_SIZE;
-    const Span extra[] = {{stats, 16}, {workspace, 16 * (size_t)pairs}};
+    const size_t need = kTicketBytes + 16 * (size_t)pairs;
+    if (workspace_bytes < need) return RLCA_ERR_INVALID_SIZE;
+    const Span extra[] = {{stats, 16}, {workspace, need}};
     st = check_extra_aliasing(c, extra, 2);
     if (st != RLCA_OK) return st;
-    c.bp.stats_partials = static_cast<double *>(workspace);
-    st = launch_gae_stats(c.bp, c.shape, stream);
-    if (st != RLCA_OK) return st;
-    return launch_finish_stats(c.bp.stats_partials, pairs, num_envs * T, stats, stream);
+    c.bp.stats_partials =
+        reinterpret_cast<double *>(static_cast<char *>(workspace) + kTicketBytes);
+    c.bp.stats = stats;
+    c.bp.stats_count = num_envs * T;
+    return launch_gae_stats(c.bp, c.shape, stream);
 }
 
 rlca_status rlca_gae_stats_noalloc(const float *rewards, const float *values,
@@ -827,19 +844,19 @@ rlca_status rlca_gae_stats_noalloc(const float *rewards, const float *values,
     const Span extra[] = {{stats, 16}};
     st = check_extra_aliasing(c, extra, 1);
     if (st != RLCA_OK) return st;
-    double *partials = nullptr;
-    st = scratch_address(stream, &partials);
+    void *buffer = nullptr;
+    st = scratch_address(stream, &buffer);
     if (st != RLCA_OK) return st;
-    c.bp.stats_partials = partials;
-    st = launch_gae_stats(c.bp, c.shape, stream);
-    if (st != RLCA_OK) return st;
-    return launch_finish_stats(partials, pairs, num_envs * T, stats, stream);
+    c.bp.stats_partials = reinterpret_cast<double *>(static_cast<char *>(buffer) + kTicketBytes);
+    c.bp.stats = stats;
+    c.bp.stats_count = num_envs * T;
+    return launch_gae_stats(c.bp, c.shape, stream);
 }
 
 size_t rlca_ppo_clip_loss_workspace_size(int64_t num_envs, int64_t T) {
     int64_t n;
     if (check_sizes(num_envs, T, &n) != RLCA_OK || n == 0) return 0;
-    return 8 * (size_t)ppo_grid(n);
+    return kTicketBytes + 8 * (size_t)ppo_grid(n);
 }
 
 rlca_status rlca_ppo_clip_loss(const float *advantages, const double *stats,
@@ -861,22 +878,21 @@ rlca_status rlca_ppo_clip_loss(const float *advantages, const double *stats,
     if (st != RLCA_OK) return st;
     if (!aligned(stats, 8) || !aligned(loss, 8) || !aligned(workspace, 8))
         return RLCA_ERR_MISALIGNED;
-    const uint32_t grid = ppo_grid(n);
-    if (workspace_bytes < 8 * (size_t)grid) return RLCA_ERR_INVALID_SIZE;
+    const size_t need = kTicketBytes + 8 * (size_t)ppo_grid(n);
+    if (workspace_bytes < need) return RLCA_ERR_INVALID_SIZE;
     Call c = Call{};  // byte ranges only, for the aliasing check
     const size_t fb = (size_t)n * 4;
     c.ins[c.nin++] = {advantages, fb};
     c.ins[c.nin++] = {logp_new, fb};
     c.ins[c.nin++] = {logp_old, fb};
     c.ins[c.nin++] = {stats, 16};
-    const Span outs[] = {{grad_logp_new, fb}, {loss, 8}, {workspace, 8 * (size_t)grid}};
+    const Span outs[] = {{grad_logp_new, fb}, {loss, 8}, {workspace, need}};
     st = check_extra_aliasing(c, outs, 3);
     if (st != RLCA_OK) return st;
     const bool vec = aligned(advantages, 16) && aligned(logp_new, 16) && aligned(logp_old, 16) &&
                      aligned(grad_logp_new, 16);
     return launch_ppo_clip_loss(advantages, stats, logp_new, logp_old, clip_eps, norm_eps, n,
-                                vec, grad_logp_new, static_cast<double *>(workspace), loss,
-                                stream);
+                                vec, grad_logp_new, workspace, loss, stream);
 }
 
 rlca_status rlca_run_batch(const rlca_call *calls, int count, hipStream_t stream) {

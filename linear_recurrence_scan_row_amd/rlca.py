@@ -8,6 +8,7 @@ raises instead of degrading.
 from __future__ import annotations
 
 import ctypes
+import threading
 import inspect
 import os
 from typing import Optional
@@ -330,9 +331,24 @@ def _prepare_affine_scan(alpha, beta, carry=None, direction=BACKWARD, out=None):
                      direction=int(direction), out0=o, dtype=REAL_DTYPES[fdt])
 
 
-def _workspace(query, shape, dev):
+# Workspaces of the fused consumers, one per (device, stream), zero-filled
+# when allocated: every call leaves its workspace zero-filled again (its
+# ticket counter back at zero), so calls on one stream, which run in order,
+# share it.  Grown by replacement when a call needs more.
+_workspaces = {}
+_workspaces_lock = threading.Lock()
+
+
+def _workspace(query, shape, dev, stream):
     nbytes = getattr(lib(), query)(*shape)
-    return torch.empty(max(nbytes, 8), dtype=torch.uint8, device=dev), nbytes
+    key = (dev.index, stream)
+    with _workspaces_lock:
+        ws = _workspaces.get(key)
+        if ws is None or ws.numel() < nbytes:
+            # enqueued on the current stream, the one the call runs on
+            ws = torch.zeros(max(nbytes, 1 << 16), dtype=torch.uint8, device=dev)
+            _workspaces[key] = ws
+    return ws, ws.numel()
 
 
 def gae_stats(rewards, values, terminated, truncated=None, trunc_values=None, bootstrap=None,
@@ -346,11 +362,12 @@ def gae_stats(rewards, values, terminated, truncated=None, trunc_values=None, bo
     if not p.f32:
         raise TypeError("gae_stats takes float32 arrays")
     st = _out(stats, (2,), p.dev, torch.float64, name="stats")
-    ws, nbytes = _workspace("rlca_gae_stats_workspace_size", p.shape, p.dev)
+    h = p.stream()
+    ws, nbytes = _workspace("rlca_gae_stats_workspace_size", p.shape, p.dev, h)
     _check(lib().rlca_gae_stats(p.arg("rewards"), p.arg("values"), p.arg("terminated"),
                                 p.arg("truncated"), p.arg("trunc_values"), p.arg("bootstrap"),
                                 p.arg("gamma"), p.arg("lambda_"), *p.shape, p.arg("out0"),
-                                p.arg("out1"), _ptr(st), _ptr(ws), nbytes, p.stream()),
+                                p.arg("out1"), _ptr(st), _ptr(ws), nbytes, h),
            "rlca_gae_stats")
     return p.result + (st,)
 
@@ -387,10 +404,10 @@ def ppo_clip_loss(advantages, logp_new, logp_old, stats=None, clip_eps=0.2, norm
     st = _steps("stats", stats, (2,), torch.float64, dev, optional=True)
     g = _out(grad, shape, dev, name="grad") if with_grad else None
     loss = torch.empty(1, dtype=torch.float64, device=dev)
-    ws, nbytes = _workspace("rlca_ppo_clip_loss_workspace_size", shape, dev)
+    h = _current_stream(dev)
+    ws, nbytes = _workspace("rlca_ppo_clip_loss_workspace_size", shape, dev, h)
     _check(lib().rlca_ppo_clip_loss(_ptr(a), _ptr(st), _ptr(new), _ptr(old), clip_eps, norm_eps,
-                                    *shape, _ptr(g), _ptr(loss), _ptr(ws), nbytes,
-                                    _current_stream(dev)),
+                                    *shape, _ptr(g), _ptr(loss), _ptr(ws), nbytes, h),
            "rlca_ppo_clip_loss")
     return loss, g
 

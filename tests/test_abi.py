@@ -233,16 +233,17 @@ def test_workspace_size_queries(lib):
     assert lib.rlca_gae_stats_workspace_size(0, 128) == 0
     assert lib.rlca_gae_stats_workspace_size(-1, 128) == 0
     assert lib.rlca_ppo_clip_loss_workspace_size(4, 0) == 0
-    # one (sum, sum of squares) pair of doubles per workgroup: 4096 x 128 packs
-    # 16 rows per 8-wave workgroup; the unaligned path packs 8 per 4-wave one
-    assert lib.rlca_gae_stats_workspace_size(4096, 128) == 16 * 512
+    # ticket counters (33 words, 128 bytes apart), then one (sum, sum of squares) pair of doubles
+    # per workgroup: 4096 x 128 packs 16 rows per 8-wave workgroup; the
+    # unaligned path packs 8 per 4-wave one
+    assert lib.rlca_gae_stats_workspace_size(4096, 128) == 4224 + 16 * 512
     # chunked: 2048-step chunks (49 per row) for aligned arrays, 2040-step
     # chunks (50 per row, the last in scan order 4..2043 steps) for T % 4 != 0
     # or inputs off phase 0; the size covers whichever the pointers select
-    assert lib.rlca_gae_stats_workspace_size(3, 100000) == 16 * 3 * 50
-    assert lib.rlca_gae_stats_workspace_size(3, 100001) == 16 * 3 * 50
-    assert lib.rlca_ppo_clip_loss_workspace_size(4096, 128) == 8 * 512
-    assert lib.rlca_ppo_clip_loss_workspace_size(1 << 20, 512) == 8 * 2048
+    assert lib.rlca_gae_stats_workspace_size(3, 100000) == 4224 + 16 * 3 * 50
+    assert lib.rlca_gae_stats_workspace_size(3, 100001) == 4224 + 16 * 3 * 50
+    assert lib.rlca_ppo_clip_loss_workspace_size(4096, 128) == 4224 + 8 * 512
+    assert lib.rlca_ppo_clip_loss_workspace_size(1 << 20, 512) == 4224 + 8 * 2048
 
 
 def gae_stats(lib, stats=F, ws=G, nbytes=1 << 20, **kw):
@@ -285,7 +286,7 @@ def test_gae_stats_noalloc_validation(lib):
     assert call(gamma=1.5) == VALUE
     assert call(stats=D) == ALIAS            # stats over the advantages
     text = open(HEADER).read()
-    assert re.search(r"#define\s+RLCA_GAE_STATS_SCRATCH_BYTES\s+65536\b", text)
+    assert re.search(r"#define\s+RLCA_GAE_STATS_SCRATCH_BYTES\s+69760\b", text)
 
 
 def test_ppo_clip_loss_validation(lib):
