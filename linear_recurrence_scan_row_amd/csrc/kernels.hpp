@@ -678,6 +678,10 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
     static_assert(MODE == kFull || (NW == kChunkWaves && !WAVE_LOCAL && F64),
                   "a chunk is one tile, scanned in fp64");
     typedef typename ScanOf<float, F64>::type SV;
+    // the importance-weighted bodies compose with the legacy multiply
+    // (scan_core.hpp): their beta is never infinite, and they are the ones
+    // whose vector issue shows in their time (V-Trace, Retrace)
+    constexpr bool kLegacy = (EST == kVtrace || EST == kRetrace) && !F64;
     typedef const S *__restrict__ In;
     const In rewards = static_cast<In>(p.rewards), values = static_cast<In>(p.values);
     const In expected_q = static_cast<In>(p.expected_q);
@@ -870,7 +874,7 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
 #pragma unroll
             for (int i = kK - 1; i >= 0; --i) {
                 SV a_i = alpha[i], b_i = beta[i];
-                compose(a_i, b_i, fa, fb);
+                compose<kLegacy>(a_i, b_i, fa, fb);
                 fa = a_i;
                 fb = b_i;
             }
@@ -888,8 +892,8 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
             } else {
                 SV carry_out;
                 if constexpr (MODE == kChunkApply) hold_chunk_carry(carry);
-                SV A = block_carry_in<NW, WAVE_LOCAL>(fa, fb, carry, lds_a, lds_b, parity,
-                                                       carry_out);
+                SV A = block_carry_in<NW, WAVE_LOCAL, kLegacy>(fa, fb, carry, lds_a, lds_b,
+                                                                parity, carry_out);
                 parity ^= 1;
                 carry = carry_out;
 
@@ -898,17 +902,17 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
 #pragma unroll
                 for (int i = kK - 1; i >= 0; --i) {
                     const SV An = A;  // A_{t+1}
-                    A = apply_map(SV(alpha[i]), beta[i], An);
+                    A = apply_map<kLegacy>(SV(alpha[i]), beta[i], An);
                     if constexpr (EST == kGae) {
                         o0[i] = (float)A;
                         o1[i] = (float)(A + SV(v[i]));
                     } else if constexpr (EST == kVtrace) {
                         o0[i] = (float)(SV(v[i]) + A);
-                        o1[i] = (float)apply_map(SV(alpha[i]), SV(aux[i]), An);
+                        o1[i] = (float)apply_map<kLegacy>(SV(alpha[i]), SV(aux[i]), An);
                     } else if constexpr (EST == kRetrace) {
                         // Q^ret_t = r_t + gamma E Q_{t+1} + beta_t A_{t+1}, without
                         // the Q_t that alpha_t subtracts and A_t + Q_t would add back
-                        o0[i] = (float)apply_map(SV(aux[i]), beta[i], An);
+                        o0[i] = (float)apply_map<kLegacy>(SV(aux[i]), beta[i], An);
                         o1[i] = 0.f;
                     } else {
                         o0[i] = (float)A;

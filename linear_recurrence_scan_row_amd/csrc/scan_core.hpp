@@ -54,10 +54,23 @@ __device__ __forceinline__ V from_bits(int x) {
 // already, so a NaN composed beta changes nothing.  The int32 prefix sums
 // (uint32 here) have no NaN and keep plain arithmetic.  The double forms
 // serve the fp64 scans (see ScanOf).
-template <typename V>
+//
+// LEGACY (fp32 only): the hardware's legacy multiply, v_mul_legacy_f32,
+// whose product is 0 whenever an operand is 0 (even against NaN or
+// infinity), gives the same cut-safe results in three instructions instead
+// of five (compare, FMA, multiply, two selects): a + b*x as a legacy
+// product and an add, so the fp32 result rounds twice instead of once.
+// It differs from the selects only for an infinite beta (inf * 0 = 0),
+// which the importance-weighted estimators, the only users, never have:
+// their beta is gamma * lambda * min(c_bar, ratio), in [0, 1], or NaN.
+extern "C" __device__ float rlca_fmul_legacy(float, float) __asm("llvm.amdgcn.fmul.legacy");
+
+template <bool LEGACY = false, typename V>
 __device__ __forceinline__ V apply_map(V a, V b, V x) {
     if constexpr (__is_same(V, uint32_t)) {
         return a + b * x;
+    } else if constexpr (LEGACY && __is_same(V, float)) {
+        return a + rlca_fmul_legacy(b, x);
     } else {
         return b == V(0) ? a : a + b * x;
     }
@@ -65,11 +78,14 @@ __device__ __forceinline__ V apply_map(V a, V b, V x) {
 
 // (a, b) <- (a, b) after (pa, pb): the map of a later run in scan order
 // applied after the map of the earlier run.
-template <typename V>
+template <bool LEGACY = false, typename V>
 __device__ __forceinline__ void compose(V &a, V &b, V pa, V pb) {
     if constexpr (__is_same(V, uint32_t)) {
         a = a + b * pa;
         b = b * pb;
+    } else if constexpr (LEGACY && __is_same(V, float)) {
+        a = a + rlca_fmul_legacy(b, pa);
+        b = rlca_fmul_legacy(b, pb);
     } else {
         const bool cut = b == V(0);
         a = cut ? a : a + b * pa;
@@ -129,22 +145,22 @@ __device__ __forceinline__ V read_lane(V x, int lane) {
 // One DPP step: fetch (a, b) from the lane selected by CTRL and compose.
 // Lanes whose source is outside the row or whose row is masked off keep the
 // identity (0, 1) as fetched value (bound_ctrl = 0 keeps `old`).
-template <int CTRL, int ROW_MASK, typename V>
+template <int CTRL, int ROW_MASK, bool LEGACY, typename V>
 __device__ __forceinline__ void dpp_compose(V &a, V &b) {
     const V pa = dpp_move<CTRL, ROW_MASK>(a, V(0));
     const V pb = dpp_move<CTRL, ROW_MASK>(b, V(1));
-    compose(a, b, pa, pb);
+    compose<LEGACY>(a, b, pa, pb);
 }
 
 // Inclusive scan over the 64 lanes of a wave, lane 0 first.
-template <typename V>
+template <bool LEGACY = false, typename V>
 __device__ __forceinline__ void wave_inclusive_scan(V &a, V &b) {
-    dpp_compose<0x111, 0xf>(a, b);  // row_shr:1
-    dpp_compose<0x112, 0xf>(a, b);  // row_shr:2
-    dpp_compose<0x114, 0xf>(a, b);  // row_shr:4
-    dpp_compose<0x118, 0xf>(a, b);  // row_shr:8  -> prefix within each row of 16
-    dpp_compose<0x142, 0xa>(a, b);  // row_bcast:15 into rows 1 and 3
-    dpp_compose<0x143, 0xc>(a, b);  // row_bcast:31 into rows 2 and 3
+    dpp_compose<0x111, 0xf, LEGACY>(a, b);  // row_shr:1
+    dpp_compose<0x112, 0xf, LEGACY>(a, b);  // row_shr:2
+    dpp_compose<0x114, 0xf, LEGACY>(a, b);  // row_shr:4
+    dpp_compose<0x118, 0xf, LEGACY>(a, b);  // row_shr:8  -> prefix within each row of 16
+    dpp_compose<0x142, 0xa, LEGACY>(a, b);  // row_bcast:15 into rows 1 and 3
+    dpp_compose<0x143, 0xc, LEGACY>(a, b);  // row_bcast:31 into rows 2 and 3
 }
 
 // Value held by lane - 1 (lane 0 receives `first`): one DPP wave_shr:1 move,
@@ -166,25 +182,27 @@ __device__ __forceinline__ V from_lower_lane(V x, V first) {
 // multiplied by an exact zero before it reaches any output.  The LDS exchange
 // and the barrier are then skipped and 0 enters each wave instead; the
 // results are the same values the exchange would give.
-template <int NW, bool WAVE_LOCAL, typename V>
+template <int NW, bool WAVE_LOCAL, bool LEGACY = false, typename V>
 __device__ __forceinline__ V block_carry_in(V a, V b, V carry_in, V *lds_a, V *lds_b, int parity,
                                             V &carry_out) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int w = threadIdx.x / kWave;
-    wave_inclusive_scan(a, b);
+    // the wave index is uniform: as a scalar, the fold's `j == w` tests
+    // below are scalar compares, not per-lane masks held across the fold
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    wave_inclusive_scan<LEGACY>(a, b);
     const V ea = from_lower_lane(a, V(0));
     const V eb = from_lower_lane(b, V(1));
     if constexpr (WAVE_LOCAL) {
         carry_out = V(0);
-        return apply_map(ea, eb, V(0));
+        return apply_map<LEGACY>(ea, eb, V(0));
     }
     if constexpr (NW == 1) {
         // One wave: its total is lane 63's inclusive value; no LDS, no
         // barrier (so waves of one workgroup may run unrelated tiles).
         const V ta = read_lane(a, kWave - 1);
         const V tb = read_lane(b, kWave - 1);
-        carry_out = apply_map(ta, tb, carry_in);
-        return apply_map(ea, eb, carry_in);
+        carry_out = apply_map<LEGACY>(ta, tb, carry_in);
+        return apply_map<LEGACY>(ea, eb, carry_in);
     }
     if (lane == kWave - 1) {
         lds_a[parity * NW + w] = a;
@@ -196,10 +214,10 @@ __device__ __forceinline__ V block_carry_in(V a, V b, V carry_in, V *lds_a, V *l
 #pragma unroll
     for (int j = 0; j < NW; ++j) {
         if (j == w) xw = x;
-        x = apply_map(lds_a[parity * NW + j], lds_b[parity * NW + j], x);
+        x = apply_map<LEGACY>(lds_a[parity * NW + j], lds_b[parity * NW + j], x);
     }
     carry_out = x;
-    return apply_map(ea, eb, xw);
+    return apply_map<LEGACY>(ea, eb, xw);
 }
 
 // The map of the whole tile: the NW wave totals composed in scan order.  Used
@@ -212,7 +230,7 @@ template <int NW, typename V>
 __device__ __forceinline__ void block_total(V a, V b, V *lds_a, V *lds_b, int parity, V &ta,
                                             V &tb) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int w = threadIdx.x / kWave;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     wave_inclusive_scan(a, b);
     if (lane == kWave - 1) {
         lds_a[parity * NW + w] = a;
