@@ -26,9 +26,23 @@ Measurement:
     / fp16 2 B, flags 1 B per step, bootstrap one value per row);
   * copy_ceiling: a torch device copy moving the step's bytes, cold and back
     to back, as the attainable ceiling at this size;
+  * floor: bench_floor.hip moving exactly the step's bytes with the
+    library's tiling and access widths and no arithmetic (one launch per
+    step, same rotation); value_over_floor = floor time / step time;
+  * roofline: the dominant kernel's average duration from the committed
+    rocprofv3 kernel-trace summary (profiles/kernels_<workload>.md) when it
+    was taken on the current kernel sources, else from the events; the
+    event-timed figures are kept beside it (*_event); roofline_gae_call is
+    the GAE call's own kernel, the one the metric names;
   * cpu_baseline: the fp64 sequential oracle on this host, single thread;
     cpu_baseline_all_cores: the same with the rows split over up to 16
-    worker processes.
+    worker processes; host_cores: the CPUs this process may run on
+    (affinity), nproc and os.cpu_count().
+
+Workloads: the five configurations (gae_8x16, gae_td_4096x128,
+vtrace_4096x256, retrace_2048x1024, forward_16384x512), the fused PPO
+consumers (ppo_4096x128) and few long rows on the chunked path
+(long_1x1048576, long_8x131072: GAE with truncation and eligibility traces).
 
 --sweep prints one JSON line per (num_envs, T, estimator) of a size sweep
 instead (three trials per point, the fastest kept).
@@ -36,8 +50,10 @@ instead (three trials per point, the fastest kept).
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -87,6 +103,19 @@ def workload_calls(name, cfg, host, es=4):
                  ["@r", "@v", "@term", "@trunc", "@tv", "@b", g, lam, n, t, "@o0"],
                  _backward_bytes(nt, n, 3, 2, 1, es), ("o0",))
         calls = [gae_tr] if name == "gae_8x16" else [gae_nt, gae_tr, td_nt, td_tr]
+        return arrays, calls
+    if name.startswith("long_"):
+        # few long rows: GAE with truncation, and eligibility traces over the
+        # rewards with resets after terminated steps
+        arrays = dict(r=host.rewards, v=host.values, term=host.terminated,
+                      trunc=host.truncated, tv=host.trunc_values, b=host.bootstrap)
+        calls = [
+            ("gae+trunc", "rlca_gae",
+             ["@r", "@v", "@term", "@trunc", "@tv", "@b", g, lam, n, t, "@o0", "@o1"],
+             _backward_bytes(nt, n, 3, 2, 2, es), ("o0", "o1")),
+            ("eligibility", "rlca_eligibility_traces",
+             ["@r", "@term", 1, g, lam, n, t, "@o0"], nt * (2 * es + 1), ("o0",)),
+        ]
         return arrays, calls
     if name == "ppo_4096x128":
         # the fused consumers: GAE + advantage statistics, then the PPO loss
@@ -196,6 +225,63 @@ BATCH_FIELDS = {
     "rlca_episodic_prefix_sum": (6, ["rewards", "dtype", "terminated", "convention",
                                      "num_envs", "T", "out0"]),
 }
+
+
+# ------------------------------------------------------------------ streaming floor
+# bench_floor.hip moves exactly a step's bytes with the library's tiling and
+# access widths and does no arithmetic; one launch per step covers every call.
+FLOOR_LIB = os.path.join(ROOT, "bench_floor.so")
+_PER_STEP_IN = {"rewards", "values", "expected_q", "behaviour_logp", "target_logp",
+                "terminated", "truncated", "trunc_values"}
+
+
+def _roles(names):
+    return ["in" if f in _PER_STEP_IN else "row" if f == "bootstrap" else
+            "out" if f in ("out0", "out1") else None for f in names]
+
+
+FLOOR_ROLES = {fname: _roles(names) for fname, (_, names) in BATCH_FIELDS.items()}
+FLOOR_ROLES["rlca_gae_stats"] = FLOOR_ROLES["rlca_gae"] + [None, None, None]
+FLOOR_ROLES["rlca_ppo_clip_loss"] = ["in", None, "in", "in", None, None, None, None, "out",
+                                     None, None, None]
+
+
+class _FloorCall(ctypes.Structure):
+    _fields_ = [("ins", ctypes.c_void_p * 9), ("outs", ctypes.c_void_p * 2),
+                ("row", ctypes.c_void_p), ("steps", ctypes.c_uint64), ("T", ctypes.c_uint32),
+                ("tiles", ctypes.c_uint32), ("in_bytes", ctypes.c_uint8 * 9),
+                ("out_bytes", ctypes.c_uint8 * 2), ("row_bytes", ctypes.c_uint8),
+                ("nin", ctypes.c_uint8), ("nout", ctypes.c_uint8)]
+
+
+class _FloorLaunch(ctypes.Structure):
+    _fields_ = [("calls", _FloorCall * 8), ("ncalls", ctypes.c_uint32)]
+
+
+def floor_record(calls, bufs_per_call, n, t):
+    """The floor launch moving the bytes of one step: calls[c] on bufs_per_call[c]."""
+    rec = _FloorLaunch()
+    rec.ncalls = len(calls)
+    for c, (call, bufs) in enumerate(zip(calls, bufs_per_call)):
+        _, fname, template, _, _ = call
+        f = rec.calls[c]
+        nin = nout = 0
+        for role, a in zip(FLOOR_ROLES[fname], template):
+            if role is None or not (isinstance(a, str) and a.startswith("@")):
+                continue
+            x = bufs[a[1:]]
+            if role == "in":
+                f.ins[nin], f.in_bytes[nin] = x.data_ptr(), x.element_size()
+                nin += 1
+            elif role == "out":
+                f.outs[nout], f.out_bytes[nout] = x.data_ptr(), x.element_size()
+                nout += 1
+            else:
+                f.row, f.row_bytes = x.data_ptr(), x.element_size()
+        f.nin, f.nout = nin, nout
+        f.steps, f.T = n * t, t
+        f.tiles = (n * t + 2047) // 2048
+    return rec
 
 
 def _resolve(a, bufs):
@@ -351,6 +437,20 @@ def run_gpu(args, name, cfg, host):
                        for c in range(ncalls)]
         batch_ms = back_to_back([p[0] for p in plan]) if args.launch == "batch" else None
 
+        # the streaming floor of the step (bench_floor.hip), the same rotation
+        floor_ms = None
+        if os.path.exists(FLOOR_LIB) and host.T % 4 == 0:
+            flib = ctypes.CDLL(FLOOR_LIB)
+            flib.bench_floor_launch.argtypes = [ctypes.POINTER(_FloorLaunch), ctypes.c_void_p]
+            flib.bench_floor_launch.restype = ctypes.c_int
+            flib.bench_floor_launch_bytes.restype = ctypes.c_size_t
+            if flib.bench_floor_launch_bytes() != ctypes.sizeof(_FloorLaunch):
+                raise RuntimeError("bench_floor.so does not match this bench.py")
+            recs = [floor_record(calls, [sets[(s * ncalls + c) % nsets] for c in range(ncalls)],
+                                 host.num_envs, host.T) for s in range(steps_per_cycle)]
+            floor_ms = back_to_back([(flib.bench_floor_launch, (ctypes.byref(r), h))
+                                     for r in recs])
+
         # the pages' protocol: 20 untimed calls, then 5 trials of 50 calls,
         # each call between its own pair of events and followed by a
         # synchronize (full-call time: host launch included); the median of
@@ -404,6 +504,7 @@ def run_gpu(args, name, cfg, host):
     nt = host.num_envs * host.T
     return dict(step_ms=step_ms, wall_s=wall, step_bytes=step_bytes, calls=calls,
                 per_call_ms=per_call_ms, batch_ms=batch_ms, protocol_ms=protocol_ms,
+                floor_ms=floor_ms,
                 dominant=dominant, nt=nt,
                 nsets=nsets,
                 copy_gbs=copy_gbs, copy_bytes=nfl * 8)
@@ -437,6 +538,12 @@ def oracle_calls(name, cfg, d):
         return [lambda: oracle.retrace(d.rewards, d.q_values, d.expected_q, d.behaviour_logp,
                                        d.target_logp, d.terminated, d.truncated, d.trunc_values,
                                        d.bootstrap, g, lam, cfg["c_bar"])]
+    if name.startswith("long_"):
+        return [
+            lambda: oracle.gae(d.rewards, d.values, d.terminated, d.truncated, d.trunc_values,
+                               d.bootstrap, g, lam),
+            lambda: oracle.eligibility_traces(d.rewards, d.terminated, 1, g, lam),
+        ]
     if name == "ppo_4096x128":
         def ppo_step():
             adv, _ = oracle.gae(d.rewards, d.values, d.terminated, d.truncated, d.trunc_values,
@@ -520,6 +627,29 @@ def run_cpu_baseline(name, cfg, host, seconds, workers=1):
 
 
 # ------------------------------------------------------------------ traffic
+
+
+def profiled_times(workload, dtype):
+    """(step_avg_us, {call: avg_us}, summary file) from the committed rocprofv3
+    kernel-trace summary of this workload, or (None, {}, file) when it is
+    missing or the kernel source changed since it was taken."""
+    name = f"kernels_{workload}" + ("" if dtype == "f32" else f"_{dtype}") + ".md"
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None, {}, name
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("|", "#")):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    from profiling import source_digest
+
+    if kv.get("source_digest") != source_digest():
+        return None, {}, name
+    calls = {k[len("call_avg_us."):]: float(v) for k, v in kv.items()
+             if k.startswith("call_avg_us.")}
+    step = float(kv["step_avg_us"]) if "step_avg_us" in kv else None
+    return step, calls, name
 
 
 def measured_traffic(kernel_name, workload):
@@ -704,9 +834,21 @@ def main():
     else:
         dcall = res["calls"][res["dominant"]]
         dom_name, dom_bytes, dom_ms = dcall[0], dcall[3], res["per_call_ms"][res["dominant"]]
-    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    achieved_event = dom_bytes / (dom_ms * 1e-3) / 1e9
     tag = dom_name.replace("+", "_") + ("" if args.dtype == "f32" else "_" + args.dtype)
     traffic = measured_traffic(tag, args.workload)
+    # the dominant kernel's average duration from the committed rocprofv3
+    # kernel trace of this workload (a step of one grouped launch, or the
+    # one call), when that summary was taken on the current kernel sources;
+    # the tracer runs dispatches one at a time, so it reads a little above
+    # the back-to-back event time, which is kept beside it
+    prof_step_us, prof_calls, prof_file = profiled_times(args.workload, args.dtype)
+    prof_us = prof_step_us if dom_name == "batch" else prof_calls.get(dom_name)
+    if prof_us is not None:
+        achieved, avg_us, source = dom_bytes / (prof_us * 1e-6) / 1e9, prof_us, \
+            f"rocprofv3 kernel trace, profiles/{prof_file}"
+    else:
+        achieved, avg_us, source = achieved_event, dom_ms * 1e3, "HIP events, back to back"
 
     calls_out = {}
     for i, c in enumerate(res["calls"]):
@@ -756,11 +898,47 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "algorithmic_bytes": dom_bytes,
-            "avg_us": round(dom_ms * 1e3, 3),
+            "avg_us": round(avg_us, 3),
+            "source": source,
+            "achieved_event": round(achieved_event, 1),
+            "frac_event": round(achieved_event / HBM_PEAK_GBS, 4),
+            "avg_us_event": round(dom_ms * 1e3, 3),
         },
     }
+    if res["floor_ms"] is not None:
+        out["floor"] = {
+            "us": round(res["floor_ms"] * 1e3, 3),
+            "gbs": round(res["step_bytes"] / (res["floor_ms"] * 1e-3) / 1e9, 1),
+            "kind": "bench_floor.hip: the step's bytes, the library's tiling and access widths, "
+                    "no arithmetic, one launch per step, same cold rotation",
+            "value_over_floor": round(res["floor_ms"] / res["step_ms"], 4),
+        }
+    # the metric names the GAE call: its own kernel's roofline, beside the step's
+    names = [c[0] for c in res["calls"]]
+    if "gae" in names and ncalls > 1:
+        i = names.index("gae")
+        ms, b = res["per_call_ms"][i], res["calls"][i][3]
+        g_prof = prof_calls.get("gae")
+        g_us = g_prof if g_prof is not None else ms * 1e3
+        out["roofline_gae_call"] = {
+            "kernel": "gae (one call, its own launch)",
+            "achieved": round(b / (g_us * 1e-6) / 1e9, 1),
+            "frac": round(b / (g_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "avg_us": round(g_us, 3),
+            "source": (f"rocprofv3 kernel trace, profiles/{prof_file}" if g_prof is not None
+                       else "HIP events, back to back"),
+            "avg_us_event": round(ms * 1e3, 3),
+            "traffic": measured_traffic("gae", args.workload),
+            "algorithmic_bytes": b,
+        }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = run_cpu_baseline(args.workload, cfg, host, args.cpu_seconds)
+        try:
+            nproc = int(subprocess.run(["nproc"], capture_output=True, text=True).stdout)
+        except (OSError, ValueError):
+            nproc = None
+        out["host_cores"] = {"affinity": len(os.sched_getaffinity(0)), "nproc": nproc,
+                             "cpu_count": os.cpu_count()}
         # the same oracle with the rows split over the host's cores (at most
         # 16, the CPU share of one GPU), for context
         cores = min(16, len(os.sched_getaffinity(0)))

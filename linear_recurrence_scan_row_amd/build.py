@@ -76,6 +76,21 @@ def build(verbose: bool = False, extra=None, out: str = LIB_PATH, jobs: int = 8,
     return out
 
 
+def build_floor(verbose: bool = False) -> str:
+    """Compile the benchmark's streaming-floor kernel (bench_floor.hip beside
+    bench.py, a measurement aid, not part of the library) into bench_floor.so."""
+    src = os.path.join(ROOT, "bench_floor.hip")
+    out = os.path.join(ROOT, "bench_floor.so")
+    tmp = out + ".tmp"
+    flags = [f for i, f in enumerate(FLAGS) if f != "-I" and (i == 0 or FLAGS[i - 1] != "-I")]
+    cmd = [HIPCC, *flags, "-shared", "-o", tmp, src]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     extra = sys.argv[1:]
     print(build(verbose=True, extra=extra))

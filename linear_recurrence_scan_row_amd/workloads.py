@@ -129,7 +129,8 @@ def forward_rollout(seed: int, num_envs: int, T: int, p_start: float = 0.01,
                           dict(params))
 
 
-# The five measured workloads (seeds 1..5), with the estimator parameters each uses.
+# The measured workloads, with the estimator parameters each uses: the five
+# configurations (seeds 1..5), the fused PPO consumers and two of few long rows.
 CONFIGS = {
     "gae_8x16": dict(kind="backward", seed=1, num_envs=8, T=16, p_term=0.05, p_trunc=0.02,
                      gamma=0.99, lam=0.95),
@@ -145,6 +146,13 @@ CONFIGS = {
     # recipe); behaviour / target log-probs serve as old / new policy
     "ppo_4096x128": dict(kind="backward", seed=2, num_envs=4096, T=128, p_term=0.01,
                          p_trunc=0.005, gamma=0.99, lam=0.95, clip_eps=0.2),
+    # few long rows (the chunked path): GAE with truncation and eligibility
+    # traces (x = rewards, resets after terminated steps) over one row of
+    # 2^20 steps and over 8 rows of the pages' longest fused scan, 131072
+    "long_1x1048576": dict(kind="backward", seed=6, num_envs=1, T=1 << 20, p_term=0.01,
+                           p_trunc=0.005, gamma=0.99, lam=0.95),
+    "long_8x131072": dict(kind="backward", seed=7, num_envs=8, T=131072, p_term=0.01,
+                          p_trunc=0.005, gamma=0.99, lam=0.95),
 }
 
 

@@ -1,9 +1,13 @@
 """Summaries of rocprofv3 results (the SQLite ``*_results.db`` it writes) for the
 credit-assignment kernels.
 
-  python profiling.py stats DB [--command CMD]
+  python profiling.py stats DB [--command CMD] [--step SUBSTR[xK] ...]
+         [--call NAME=SUBSTR ...] [--out FILE]
       per-kernel dispatch count and average / min / max duration (us), from a
-      ``rocprofv3 --kernel-trace --stats`` run.
+      ``rocprofv3 --kernel-trace --stats`` run; --step names the kernels of one
+      benchmark step (K launches of that kernel per step) and records the sum
+      of their averages as step_avg_us, --call records one call's kernel
+      average as call_avg_us.NAME.  bench.py reads those two back.
 
   python profiling.py traffic --fetch DB --write DB
          --kernel SUBSTR --copy-bytes N --algorithmic-bytes B --out FILE [...]
@@ -119,6 +123,9 @@ def main(argv=None):
     s.add_argument("db")
     s.add_argument("--match", default="")
     s.add_argument("--command", default="")
+    s.add_argument("--step", action="append", default=[])
+    s.add_argument("--call", action="append", default=[])
+    s.add_argument("--out", default="")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -155,11 +162,36 @@ def main(argv=None):
             lines.append(f"command: {a.command}")
         lines.append(f"source_digest: {source_digest()}")
         lines.append("")
+        rows = kernel_stats(a.db, a.match)
+
+        def avg_of(sub):
+            hits = [r for r in rows if sub in r[0]]
+            if len(hits) != 1:
+                raise SystemExit(f"{sub!r} matches {len(hits)} kernels")
+            return hits[0][2]
+
+        if a.step:
+            total, names = 0.0, []
+            for spec in a.step:
+                sub, _, times = spec.rpartition("x") if spec[-1].isdigit() and "x" in spec[-3:] \
+                    else (spec, "", "1")
+                total += int(times) * avg_of(sub)
+                names.append(spec)
+            lines.append(f"step_kernels: {' + '.join(names)}")
+            lines.append(f"step_avg_us: {total:.3f}")
+        for spec in a.call:
+            name, sub = spec.split("=", 1)
+            lines.append(f"call_avg_us.{name}: {avg_of(sub):.3f}")
+        lines.append("")
         lines.append("| kernel | dispatches | avg us | min us | max us |")
         lines.append("|---|---|---|---|---|")
-        for n, c, avg, lo, hi in kernel_stats(a.db, a.match):
+        for n, c, avg, lo, hi in rows:
             lines.append(f"| {n} | {c} | {avg:.3f} | {lo:.3f} | {hi:.3f} |")
-        print("\n".join(lines))
+        text = "\n".join(lines) + "\n"
+        if a.out:
+            with open(a.out, "w") as f:
+                f.write(text)
+        sys.stdout.write(text)
         return
     r = traffic(a.fetch, a.write, a.kernel, a.copy_bytes)
     out = [f"kernel: {' + '.join(a.kernel)}",

@@ -57,5 +57,12 @@ def test_bench_prints_one_json_line(gpu_device):
     assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
     assert r["frac"] == pytest.approx(r["achieved"] / r["peak"], abs=1e-4)
     assert r["traffic"] is None or r["traffic"] > 0
+    assert r["frac_event"] == pytest.approx(r["achieved_event"] / r["peak"], abs=1e-4)
+    assert r["source"]
+    # the streaming floor of the same step, and the metric's own call
+    assert d["floor"]["us"] > 0 and 0 < d["floor"]["value_over_floor"]
+    g = d["roofline_gae_call"]
+    assert g["frac"] == pytest.approx(g["achieved"] / r["peak"], abs=1e-4)
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["cores"] >= 1 and c["value"] > 0
+    assert d["host_cores"]["affinity"] >= 1 and d["host_cores"]["nproc"] >= 1
