@@ -76,10 +76,14 @@
  *          surface at the caller's next synchronisation, as usual in HIP.
  *          Non-finite inputs are not trapped; they propagate inside their
  *          episode segment only.  A chain cut (a terminated or truncated
- *          step, a row end, a forward reset, a beta of 0) stops them: a NaN
- *          or infinity in one row never reaches another row, and never
- *          crosses an episode boundary within its row.  A NaN log-
- *          probability gives a NaN importance weight (not a clamped one).
+ *          step, a row end, a forward reset, a coefficient of exactly 0,
+ *          e.g. lambda = 0 or gamma = 0) stops them: a NaN or infinity in
+ *          one row never reaches another row, and never crosses an episode
+ *          boundary within its row.  Inside a segment they also stop where
+ *          the product of the coefficients between two steps rounds to 0
+ *          (after about 1,700 steps at gamma * lambda = 0.94 in fp32 scans,
+ *          far later in fp64 ones).  A NaN log-probability gives a NaN
+ *          importance weight (not a clamped one).
  * Numerics: fp32 arithmetic throughout (the summary's §4 requires float32
  *          scans); the scan reassociates the recurrence (associativity,
  *          summary §5), so results match a sequential fp64 evaluation to

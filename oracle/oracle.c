@@ -63,6 +63,14 @@ static double clipped_ratio(float target_logp, float behaviour_logp)
 
 static double min_d(double a, double b) { return a < b ? a : b; }
 
+/* The carried term of a recurrence: coefficient times the value carried from
+ * the neighbouring step.  A zero coefficient severs the chain, so the term is
+ * 0 whatever the carried value is, NaN or infinite included (summary §5
+ * Correctness analysis: a step with beta = 0 composes to (alpha, 0), and
+ * nothing beyond it reaches the result).  For finite values this is plain
+ * multiplication. */
+static double carried(double coef, double value) { return coef == 0.0 ? 0.0 : coef * value; }
+
 /* GAE (Schulman et al. 2016; summary §2.1):
  *   delta_t = r_t + gamma * V(s_{t+1}) - V(s_t)
  *   A_t     = delta_t + gamma * lambda * A_{t+1}   (chain cut at a boundary)
@@ -85,7 +93,7 @@ void oracle_gae(const float *rewards, const float *values, const uint8_t *termin
             double delta, adv;
             if (cont) {
                 delta = (double)r[t] + gamma * (double)v[t + 1] - (double)v[t];
-                adv = delta + gamma * lam * next_adv;
+                adv = delta + carried(gamma * lam, next_adv);
             } else {
                 delta = (double)r[t] + gamma * nv - (double)v[t];
                 adv = delta;
@@ -115,7 +123,8 @@ void oracle_td_lambda(const float *rewards, const float *values, const uint8_t *
         for (int64_t t = T - 1; t >= 0; --t) {
             double nv, g;
             if (resolve_step(term, trunc, tv, b, t, T, &nv))
-                g = (double)r[t] + gamma * ((1.0 - lam) * (double)v[t + 1] + lam * next_g);
+                g = (double)r[t] + gamma * (1.0 - lam) * (double)v[t + 1] +
+                    carried(gamma * lam, next_g);
             else
                 g = (double)r[t] + gamma * nv;
             returns[n * T + t] = g;
@@ -141,7 +150,7 @@ void oracle_discounted_returns(const float *rewards, const uint8_t *terminated,
         for (int64_t t = T - 1; t >= 0; --t) {
             double nv, g;
             if (resolve_step(term, trunc, tv, b, t, T, &nv))
-                g = (double)r[t] + gamma * next_g;
+                g = (double)r[t] + carried(gamma, next_g);
             else
                 g = (double)r[t] + gamma * nv;
             returns[n * T + t] = g;
@@ -175,19 +184,22 @@ void oracle_vtrace(const float *rewards, const float *values, const float *behav
             double ratio = clipped_ratio(pi[t], mu[t]);
             double rho = min_d(rho_bar, ratio);
             double c = lam * min_d(c_bar, ratio);
-            double nv, vs_t, target;
+            double nv, vs_t;
             if (resolve_step(term, trunc, tv, b, t, T, &nv)) {
                 double delta = rho * ((double)r[t] + gamma * (double)v[t + 1] - (double)v[t]);
-                vs_t = (double)v[t] + delta + gamma * c * (next_vs - (double)v[t + 1]);
-                target = next_vs;
+                vs_t = (double)v[t] + delta + carried(gamma * c, next_vs - (double)v[t + 1]);
+                /* pg_t = rho (r_t + gamma vs_{t+1} - V_t): its carried term is
+                 * rho gamma (vs_{t+1} - V_{t+1}) on top of rho's TD error */
+                if (pg_advantages)
+                    pg_advantages[n * T + t] =
+                        rho * ((double)r[t] + gamma * (double)v[t + 1] - (double)v[t]) +
+                        carried(rho * gamma, next_vs - (double)v[t + 1]);
             } else {
                 double delta = rho * ((double)r[t] + gamma * nv - (double)v[t]);
                 vs_t = (double)v[t] + delta;
-                target = nv;
+                if (pg_advantages) pg_advantages[n * T + t] = delta;
             }
             vs[n * T + t] = vs_t;
-            if (pg_advantages)
-                pg_advantages[n * T + t] = rho * ((double)r[t] + gamma * target - (double)v[t]);
             next_vs = vs_t;
         }
     }
@@ -219,7 +231,7 @@ void oracle_retrace(const float *rewards, const float *q_values, const float *ex
             if (resolve_step(term, trunc, tv, b, t, T, &nv)) {
                 double c_next = lam * min_d(c_bar, clipped_ratio(pi[t + 1], mu[t + 1]));
                 qr = (double)r[t] + gamma * (double)eq[t + 1] +
-                     gamma * c_next * (next_qret - (double)q[t + 1]);
+                     carried(gamma * c_next, next_qret - (double)q[t + 1]);
             } else {
                 qr = (double)r[t] + gamma * nv;
             }
@@ -250,7 +262,7 @@ void oracle_eligibility_traces(const float *increments, const uint8_t *flags, in
         double e = 0.0;
         for (int64_t t = 0; t < T; ++t) {
             if (starts_episode(f, convention, t)) e = 0.0;
-            e = (double)x[t] + gamma * lam * e;
+            e = (double)x[t] + carried(gamma * lam, e);
             traces[n * T + t] = e;
         }
     }

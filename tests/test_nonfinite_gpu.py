@@ -11,7 +11,8 @@ log-probabilities, alpha), with episode boundaries dense enough that no
 coefficient product underflows inside a segment, and every launch shape is
 run: the GPU's non-finite outputs must sit exactly where the oracle's do,
 the finite ones must meet the parity bar, and rows with no planted value
-must be entirely finite."""
+must be entirely finite.  A zero coefficient (lambda = 0, gamma = 0) is a
+cut as well, on both sides, checked over long unbroken episodes."""
 import numpy as np
 import pytest
 import torch
@@ -109,3 +110,37 @@ def test_affine_scan_zero_beta_severs_nonfinite(N, T, direction, gpu_device):
     carry[bad[:1]] = np.nan   # a non-finite carry only reaches its row's first segment
     compare(rl.affine_scan(dev(alpha), dev(beta), dev(carry), direction),
             oracle.affine_scan(alpha, beta, carry, direction), bad, f"affine {N}x{T} dir {direction}")
+
+
+@pytest.mark.parametrize("N,T", SHAPES)
+def test_zero_coefficients_cut_nonfinite(N, T, gpu_device):
+    """lambda = 0 or gamma = 0: every step's coefficient is 0, so a NaN or
+    infinity reaches no other step through the chain, even inside one long
+    episode (episode ends at 0.1% of the steps)."""
+    rng = np.random.default_rng(N * 43 + T)
+    d = workloads.backward_rollout(int(rng.integers(1 << 20)), N, T, p_term=0.001,
+                                   p_trunc=0.0005)
+    bad = np.unique(rng.integers(0, N, max(1, N // 10)))
+    r = plant(rng, d.rewards, bad)
+    v = plant(rng, d.values, bad[::2])
+    args = (r, v, d.terminated, d.truncated, d.trunc_values, d.bootstrap)
+    adv, _ = rl.gae(*map(dev, args), 0.99, 0.0)
+    compare(adv, oracle.gae(*args, 0.99, 0.0)[0], bad, f"gae lambda 0 {N}x{T}")
+    dargs = (r, d.terminated, d.truncated, d.trunc_values, d.bootstrap)
+    compare(rl.discounted_returns(*map(dev, dargs), 0.0),
+            oracle.discounted_returns(*dargs, 0.0), bad, f"discounted gamma 0 {N}x{T}")
+    vargs = (r, v, d.behaviour_logp, d.target_logp, d.terminated, d.truncated, d.trunc_values,
+             d.bootstrap)
+    vs, pg = rl.vtrace(*map(dev, vargs), 0.99, 0.0, 1.0, 1.0)
+    ovs, opg = oracle.vtrace(*vargs, 0.99, 0.0, 1.0, 1.0)
+    compare(vs, ovs, bad, f"vtrace lambda 0 {N}x{T}")
+    compare(pg, opg, bad, f"vtrace pg lambda 0 {N}x{T}")
+    rargs = (r, v, d.trunc_values, d.behaviour_logp, d.target_logp, d.terminated, d.truncated,
+             d.trunc_values, d.bootstrap)
+    compare(rl.retrace(*map(dev, rargs), 0.99, 0.0, 1.0),
+            oracle.retrace(*rargs, 0.99, 0.0, 1.0), bad, f"retrace lambda 0 {N}x{T}")
+    f = workloads.forward_rollout(int(rng.integers(1 << 20)), N, T, p_start=0.001)
+    x = plant(rng, f.increments, bad)
+    compare(rl.eligibility_traces(dev(x), dev(f.starts), rl.RESET_ON_START, 0.99, 0.0),
+            oracle.eligibility_traces(x, f.starts, rl.RESET_ON_START, 0.99, 0.0), bad,
+            f"traces lambda 0 {N}x{T}")

@@ -24,16 +24,17 @@ PINS = os.path.join(ROOT, "tests", "test_oracle_pins.py")
 # (name, text in oracle.c, replacement); each text occurs exactly once.
 MUTATIONS = [
     ("gae_drops_lambda",
-     "adv = delta + gamma * lam * next_adv;", "adv = delta + gamma * next_adv;"),
+     "adv = delta + carried(gamma * lam, next_adv);", "adv = delta + carried(gamma, next_adv);"),
     ("gae_next_value_index",
      "delta = (double)r[t] + gamma * (double)v[t + 1] - (double)v[t];",
      "delta = (double)r[t] + gamma * (double)v[t] - (double)v[t];"),
     ("gae_returns_without_values",
      "returns[n * T + t] = adv + (double)v[t];", "returns[n * T + t] = adv;"),
     ("td_lambda_drops_one_minus_lambda",
-     "((1.0 - lam) * (double)v[t + 1] + lam * next_g)", "((double)v[t + 1] + lam * next_g)"),
+     "gamma * (1.0 - lam) * (double)v[t + 1] +", "gamma * (double)v[t + 1] +"),
     ("discounted_continues_with_gamma_squared",
-     "g = (double)r[t] + gamma * next_g;", "g = (double)r[t] + gamma * gamma * next_g;"),
+     "g = (double)r[t] + carried(gamma, next_g);",
+     "g = (double)r[t] + carried(gamma * gamma, next_g);"),
     ("edge_ignores_bootstrap",
      "*next_value = bootstrap;", "*next_value = 0.0;"),
     ("truncation_ignored",
@@ -45,17 +46,17 @@ MUTATIONS = [
     ("log_ratio_not_clipped_below",
      "if (l < -ORACLE_LOG_RATIO_CLIP) l = -ORACLE_LOG_RATIO_CLIP;", ""),
     ("vtrace_trace_weight_uses_rho",
-     "gamma * c * (next_vs - (double)v[t + 1]);", "gamma * rho * (next_vs - (double)v[t + 1]);"),
+     "carried(gamma * c, next_vs", "carried(gamma * rho, next_vs"),
     ("vtrace_c_drops_lambda",
      "double c = lam * min_d(c_bar, ratio);", "double c = min_d(c_bar, ratio);"),
     ("vtrace_pg_target_is_value",
-     "target = next_vs;", "target = (double)v[t + 1];"),
+     "carried(rho * gamma, next_vs", "carried(0.0 * rho * gamma, next_vs"),
     ("retrace_uses_current_trace_weight",
      "clipped_ratio(pi[t + 1], mu[t + 1])", "clipped_ratio(pi[t], mu[t])"),
     ("retrace_expected_q_replaced_by_q",
      "gamma * (double)eq[t + 1] +", "gamma * (double)q[t + 1] +"),
     ("eligibility_drops_lambda",
-     "e = (double)x[t] + gamma * lam * e;", "e = (double)x[t] + gamma * e;"),
+     "e = (double)x[t] + carried(gamma * lam, e);", "e = (double)x[t] + carried(gamma, e);"),
     ("reset_after_done_reads_current_flag",
      "return flags[t - 1] != 0;", "return flags[t] != 0;"),
     ("prefix_sum_exclusive",
@@ -90,7 +91,8 @@ MUTATIONS = [
      "double delta = rho * ((double)r[t] + gamma * nv - (double)v[t]);",
      "double delta = ((double)r[t] + gamma * nv - (double)v[t]);"),
     ("retrace_correction_sign",
-     "(next_qret - (double)q[t + 1])", "((double)q[t + 1] - next_qret)"),
+     "carried(gamma * c_next, next_qret - (double)q[t + 1])",
+     "carried(gamma * c_next, (double)q[t + 1] - next_qret)"),
     ("retrace_ignores_c_bar",
      "double c_next = lam * min_d(c_bar,", "double c_next = lam * min_d(1.0,"),
     ("eligibility_never_resets",
@@ -99,6 +101,8 @@ MUTATIONS = [
      "if (starts_episode(f, convention, t)) s = 0;", ""),
     ("mean_with_sample_divisor",
      "s / (double)M : 0.0;", "s / (double)(M - 1) : 0.0;"),
+    ("zero_coefficient_does_not_cut",
+     "return coef == 0.0 ? 0.0 : coef * value;", "return coef * value;"),
     ("ppo_no_lower_clip",
      "if (clipped_rho < 1.0 - clip_eps) clipped_rho = 1.0 - clip_eps;", ""),
     ("ppo_loss_sign",

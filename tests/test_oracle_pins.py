@@ -276,6 +276,45 @@ def test_gae_lambda_zero_is_one_step_td_error():
                                atol=1e-12)
 
 
+def test_zero_coefficient_cuts_non_finite_values():
+    """A coefficient of 0 severs the chain (summary §5 Correctness analysis: a
+    step with beta = 0 composes to (alpha, 0)), NaN and infinity included:
+    with lambda = 0 GAE is the one-step TD error and Retrace the expected-
+    SARSA target, V-Trace's vs - V its rho-weighted TD error; with gamma = 0
+    discounted returns are the rewards; with gamma * lambda = 0 the traces
+    are the increments -- elementwise, non-finite entries exactly where the
+    one-step values have them, however long the episode."""
+    rng = np.random.default_rng(47)
+    N, T = 3, 40
+    r = rng.standard_normal((N, T)).astype(np.float32)
+    v = rng.standard_normal((N, T)).astype(np.float32)
+    eq = rng.standard_normal((N, T)).astype(np.float32)
+    mu = rng.normal(-1, 0.5, (N, T)).astype(np.float32)
+    pi = rng.normal(-1, 0.5, (N, T)).astype(np.float32)
+    r[0, 9], v[1, 20], eq[2, 30], v[2, 5] = np.nan, np.inf, -np.inf, np.nan
+    b = rng.standard_normal(N).astype(np.float32)
+    term = np.zeros((N, T), np.uint8)
+    g = 0.9
+    r64, v64, eq64, b64 = (x.astype(np.float64) for x in (r, v, eq, b))
+    nv = np.concatenate([v64[:, 1:], b64[:, None]], axis=1)    # V(s_{t+1}), bootstrap at the edge
+    neq = np.concatenate([eq64[:, 1:], b64[:, None]], axis=1)
+    delta = r64 + g * nv - v64
+    with np.errstate(invalid="ignore"):
+        adv, _ = oracle.gae(r, v, term, None, None, b, g, 0.0)
+        np.testing.assert_array_equal(adv, delta)
+        np.testing.assert_array_equal(oracle.retrace(r, v, eq, mu, pi, term, None, None, b, g, 0.0),
+                                      r64 + g * neq)
+        vs, _ = oracle.vtrace(r, v, mu, pi, term, None, None, b, g, 0.0, 1.0, 1.0)
+        rho = np.minimum(1.0, np.exp(np.clip(pi.astype(np.float64) - mu, -5, 5)))
+        want = rho * delta
+        fin = np.isfinite(want)
+        assert np.array_equal(np.isfinite(vs - v64), fin)
+        close((vs - v64)[fin], want[fin])
+        np.testing.assert_array_equal(oracle.discounted_returns(r, term, None, None, b, 0.0), r64)
+        np.testing.assert_array_equal(oracle.eligibility_traces(r, term, 0, 0.0, 0.9), r64)
+        np.testing.assert_array_equal(oracle.eligibility_traces(r, term, 0, 0.9, 0.0), r64)
+
+
 def test_gae_lambda_one_plus_values_is_discounted_return():
     d = rand_inputs(42, 16, 48)
     term, trunc = _random_flags(43, 16, 48)
