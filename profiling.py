@@ -50,6 +50,62 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
+# Template arguments of the library's kernels in Itanium mangling, for names
+# the trace leaves mangled (rocprofv3 and c++filt do not demangle __bf16).
+_TYPE_CODES = {"float": "f", "double": "d", "unsigned int": "j", "__bf16": "DF16b",
+               "_Float16": "DF16_", "int": "i"}
+_CODE_TYPES = {v: k for k, v in _TYPE_CODES.items()}
+
+
+def mangled_spec(spec: str) -> str:
+    """'backward_scan<0, true, float>' -> 'backward_scanILi0ELb1EfE' (the part
+    of the mangled name that identifies the instantiation)."""
+    if not spec.endswith(">") or "<" not in spec:
+        return spec
+    name, args = spec[:-1].split("<", 1)
+    codes = []
+    for a in (x.strip() for x in args.split(",")):
+        if a in ("true", "false"):
+            codes.append(f"Lb{int(a == 'true')}E")
+        elif a.lstrip("-").isdigit():
+            codes.append(f"Li{a}E")
+        else:
+            codes.append(_TYPE_CODES[a])
+    return f"{name}I{''.join(codes)}E"
+
+
+def readable(name: str) -> str:
+    """The mangled names of rlca:: kernel instantiations, demangled enough to
+    read (name and template arguments); other names unchanged."""
+    import re
+
+    m = re.match(r"_ZN4rlca(\d+)", name)
+    if not m:
+        return name
+    n = int(m.group(1))
+    base = name[m.end():m.end() + n]
+    rest = name[m.end() + n:]
+    if not rest.startswith("I"):
+        return name
+    rest = rest[1:]
+    args = []
+    while not rest.startswith("E"):
+        t = re.match(r"L([bi])(-?\d+)E", rest)
+        if t:
+            args.append(("true" if t.group(2) == "1" else "false") if t.group(1) == "b"
+                        else t.group(2))
+            rest = rest[t.end():]
+            continue
+        for code, typ in sorted(_CODE_TYPES.items(), key=lambda kv: -len(kv[0])):
+            if rest.startswith(code):
+                args.append(typ)
+                rest = rest[len(code):]
+                break
+        else:
+            return name
+    return f"rlca::{base}<{', '.join(args)}>"
+
+
 def kernel_stats(db: str, match: str = ""):
     con = sqlite3.connect(db)
     rows = con.execute(
@@ -101,8 +157,9 @@ def traffic(fetch_db, write_db, kernel, copy_bytes):
     f_kib = w_kib = 0.0
     counts = []
     for k in kernels:
-        kf = [v for d, name, v in fetch if k in name]
-        kw = [v for d, name, v in write if k in name]
+        alt = mangled_spec(k)
+        kf = [v for d, name, v in fetch if k in name or alt in name]
+        kw = [v for d, name, v in write if k in name or alt in name]
         if not kf or not kw:
             raise SystemExit(f"kernel {k!r} not found in the counter runs")
         f_kib += sum(kf) / len(kf)
@@ -163,9 +220,11 @@ def main(argv=None):
         lines.append(f"source_digest: {source_digest()}")
         lines.append("")
         rows = kernel_stats(a.db, a.match)
+        every = kernel_stats(a.db)
 
         def avg_of(sub):
-            hits = [r for r in rows if sub in r[0]]
+            alt = mangled_spec(sub)
+            hits = [r for r in every if sub in r[0] or alt in r[0]]
             if len(hits) != 1:
                 raise SystemExit(f"{sub!r} matches {len(hits)} kernels")
             return hits[0][2]
@@ -186,7 +245,7 @@ def main(argv=None):
         lines.append("| kernel | dispatches | avg us | min us | max us |")
         lines.append("|---|---|---|---|---|")
         for n, c, avg, lo, hi in rows:
-            lines.append(f"| {n} | {c} | {avg:.3f} | {lo:.3f} | {hi:.3f} |")
+            lines.append(f"| {readable(n)} | {c} | {avg:.3f} | {lo:.3f} | {hi:.3f} |")
         text = "\n".join(lines) + "\n"
         if a.out:
             with open(a.out, "w") as f:
