@@ -44,8 +44,9 @@ vtrace_4096x256, retrace_2048x1024, forward_16384x512), the fused PPO
 consumers (ppo_4096x128) and few long rows on the chunked path
 (long_1x1048576, long_8x131072: GAE with truncation and eligibility traces).
 
---sweep prints one JSON line per (num_envs, T, estimator) of a size sweep
-instead (three trials per point, the fastest kept).
+--sweep [sizes|long] prints one JSON line per (num_envs, T, estimator) of a
+size sweep instead (three trials per point, the fastest kept): rollout shapes,
+or few long rows on both sides of the chunked path's row threshold.
 """
 from __future__ import annotations
 
@@ -675,16 +676,27 @@ def measured_traffic(kernel_name, workload):
 
 # ------------------------------------------------------------------ size sweep
 
-SWEEP_ENVS = (1024, 4096, 16384, 65536)
-SWEEP_T = (128, 512, 2048)
+# (num_envs, T, estimators) of each sweep grid: "sizes" spans the rollout
+# shapes of the workloads above; "long" spans few long rows on both sides of
+# the chunked path's bounds (rows of 16384 steps or more; fewer than 96
+# rows, fewer than 160 from 32768 steps on, and for eligibility traces fewer
+# than 200 from 131072 steps on: 95, 159 and 199 rows are chunked, 96, 160
+# and 200 take one workgroup per row).
+SWEEP_GRIDS = {
+    "sizes": ((1024, 4096, 16384, 65536), (128, 512, 2048),
+              ("gae+trunc", "retrace+trunc", "eligibility")),
+    "long": ((1, 8, 16, 32, 48, 64, 95, 96, 128, 159, 160, 192, 199, 200, 224, 256),
+             (4100, 8192, 12288, 16384, 32768, 131072, 524288),
+             ("gae+trunc", "eligibility")),
+}
 
 
 def run_sweep(args):
     """Effective GB/s of GAE with truncation (22 B/step), Retrace with
-    truncation (30 B/step) and eligibility traces (9 B/step) over a grid of
-    shapes; one JSON line per point.  Rollouts are drawn on the device with a
-    seeded torch generator (values: N(0,1) and U(0,1); flags: Bernoulli 0.01
-    and 0.005); only throughput is measured here."""
+    truncation (30 B/step) and eligibility traces (9 B/step) over the grid of
+    shapes `args.sweep` names; one JSON line per point.  Rollouts are drawn on
+    the device with a seeded torch generator (values: N(0,1) and U(0,1);
+    flags: Bernoulli 0.01 and 0.005); only throughput is measured here."""
     import torch
     from linear_recurrence_scan_row_amd import rlca
 
@@ -692,8 +704,9 @@ def run_sweep(args):
     dev = torch.device("cuda:0")
     stream = torch.cuda.Stream()
     gen = torch.Generator(device=dev)
-    for n in SWEEP_ENVS:
-        for t in SWEEP_T:
+    envs, steps, estimators = SWEEP_GRIDS[args.sweep]
+    for n in envs:
+        for t in steps:
             nt = n * t
             shape = (n, t)
             specs = [
@@ -702,7 +715,7 @@ def run_sweep(args):
                  ("r", "v", "eq", "mu", "pi", "term", "trunc", "tv", "b"), ("o0",)),
                 ("eligibility", 9, ("x", "start"), ("o0",)),
             ]
-            for name, bps, ins, outs in specs:
+            for name, bps, ins, outs in [x for x in specs if x[0] in estimators]:
                 call_bytes = nt * bps + (4 * n if "b" in ins else 0)
                 per_set = nt * (4 * sum(1 for k in ins if k not in ("term", "trunc", "start"))
                                 + sum(1 for k in ins if k in ("term", "trunc", "start"))
@@ -801,8 +814,9 @@ def main():
                     help="storage type of the real-valued arrays (arithmetic is fp32)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--sweep", action="store_true",
-                    help="print one JSON line per (num_envs, T, estimator) of the size sweep")
+    ap.add_argument("--sweep", nargs="?", const="sizes", choices=tuple(SWEEP_GRIDS),
+                    help="print one JSON line per (num_envs, T, estimator) of a size sweep "
+                         "(grid 'sizes' by default, or 'long': few long rows)")
     args = ap.parse_args()
 
     if args.gpus != 1:

@@ -135,12 +135,30 @@ static IoChoice io_of(int64_t T, const void *const *ins, int nin, size_t elem,
 // wave walking the row tile by tile when there are at least 4096 rows (with
 // fewer, one wave per row leaves most wave slots empty, and 8-wave
 // workgroups packing several rows per tile win by 8-19%); longer rows with 8
-// waves sharing each tile through LDS.  Fewer than 64 long rows cannot fill the chip one
-// workgroup per row, so they are split into chunks that run in parallel
-// (three launches, inputs read twice): 50x faster for one row of 1M steps,
-// even at 64 rows, slower from 128 rows on (one workgroup per row then
-// sustains 3.4-5 TB/s).
-static constexpr int64_t kChunkedMaxRows = 64;
+// waves sharing each tile through LDS.  Few long rows cannot fill the chip one
+// workgroup per row (each walks its tiles one after another), so they are
+// split into 2048-step chunks that run in parallel: three dependent launches,
+// inputs read twice.  Measured on MI355X (GAE with truncation and eligibility
+// traces, both paths at every shape): the three launches cost more than they
+// save below 16384 steps (1.1-2.4x slower at 4100..8192 steps, even at
+// 12288); from 16384 steps on, chunking wins below about 96 rows, and from
+// 32768 steps on below about 160 rows (2x at 64 rows of 131072 steps, 30x
+// for one row of 2^19), while one workgroup per row wins above.  A forward
+// scan's row walk moves fewer bytes per tile, so from 131072 steps on its
+// chunks win up to about 200 rows.
+static constexpr int64_t kChunkedMinSteps = 8 * (int64_t)kChunkSteps;
+static constexpr int64_t kChunkedMaxRows = 96;          // rows of 16384..32767 steps
+static constexpr int64_t kChunkedMaxRowsLong = 160;     // rows of 32768 steps or more
+static constexpr int64_t kChunkedMaxRowsForward = 200;  // forward, 131072 steps or more
+
+static bool take_chunked(int64_t num_envs, int64_t T, bool backward) {
+    int64_t rows = kChunkedMaxRows;
+    if (T >= 8 * kChunkedMinSteps && !backward)
+        rows = kChunkedMaxRowsForward;
+    else if (T >= 2 * kChunkedMinSteps)
+        rows = kChunkedMaxRowsLong;
+    return T >= kChunkedMinSteps && num_envs < rows;
+}
 static constexpr int64_t kOneWaveMinRows = 4096;
 // Rows of T % K != 0 steps (and inputs or outputs off phase 0) are read
 // K-wide from windows widened to block boundaries, in 8-wave workgroups for
@@ -193,7 +211,8 @@ static void set_precision(LaunchShape &s, int64_t T, BetaBound beta, bool is_int
     s.f64 = !is_int && !s.wave_local && T > kWave * kK && !fp32_ok;
 }
 
-static LaunchShape choose_shape(int64_t num_envs, int64_t T, const IoChoice &io) {
+static LaunchShape choose_shape(int64_t num_envs, int64_t T, const IoChoice &io,
+                                bool backward) {
     LaunchShape s;
     s.vec = io.io != kScalarIO;
     s.skew = io.io == kVecSkew;
@@ -202,7 +221,7 @@ static LaunchShape choose_shape(int64_t num_envs, int64_t T, const IoChoice &io)
     s.scatter = s.skew && io.scatter;
     s.wave_local = io.io == kVecRows && T <= kWave * kK && (kWave * kK) % T == 0;
     s.waves = (T <= kWave * kK || T >= 1024 || num_envs < kOneWaveMinRows) ? 8 : 1;
-    s.chunked = s.vec && T > 2 * (int64_t)kChunkSteps && num_envs < kChunkedMaxRows;
+    s.chunked = s.vec && take_chunked(num_envs, T, backward);
     s.f64 = false;  // set_precision
     s.quantum = 1;
     if (s.skew) {
@@ -306,7 +325,7 @@ static rlca_status prepare_backward(int est, int storage, const void *rewards,
     p.geo.T = (uint32_t)T;
     const void *u8[] = {terminated, truncated};
     const void *outs[] = {out0, out1};
-    c->shape = choose_shape(num_envs, T, io_of(T, f32_steps, 6, es, u8, 2, outs, 2));
+    c->shape = choose_shape(num_envs, T, io_of(T, f32_steps, 6, es, u8, 2, outs, 2), true);
     return RLCA_OK;
 }
 
@@ -362,7 +381,7 @@ static rlca_status prepare_forward(int kind, int storage, const void *x, bool is
     const void *wide[] = {x, beta};
     const void *u8[] = {flags};
     const void *outs[] = {out};
-    c->shape = choose_shape(num_envs, T, io_of(T, wide, 2, es, u8, 1, outs, 1));
+    c->shape = choose_shape(num_envs, T, io_of(T, wide, 2, es, u8, 1, outs, 1), false);
     return RLCA_OK;
 }
 
@@ -616,7 +635,7 @@ static uint32_t gae_stats_pairs(int64_t num_envs, int64_t T) {
     for (int i = 0; i < 2 + kK; ++i) {
         if (choices[i].io == kVecRows && T % kK != 0) continue;
         const uint32_t g =
-            launch_grid(choose_shape(num_envs, T, choices[i]), num_envs, T, kStatsMaxGrid);
+            launch_grid(choose_shape(num_envs, T, choices[i], true), num_envs, T, kStatsMaxGrid);
         most = g > most ? g : most;
     }
     return most;

@@ -138,14 +138,14 @@ def mixed_members(device):
         Member("vtrace", 7, 70, 256, device),
         Member("vtrace", 8, 6, 700, device, boot=False),
         Member("retrace", 9, 40, 1024, device),
-        Member("retrace", 10, 3, 4100, device),                  # few long rows: chunked
+        Member("retrace", 10, 3, 16400, device),                 # few long rows: chunked
         Member("traces", 11, 150, 512, device),
         Member("traces", 12, 31, 64, device, conv=rl.RESET_AFTER_DONE),
         Member("prefix", 13, 65, 128, device),
         Member("prefix", 14, 12, 2048, device, int_input=True, conv=rl.RESET_AFTER_DONE),
         Member("affine", 15, 80, 256, device, direction=rl.BACKWARD),
         Member("affine", 16, 11, 520, device, direction=rl.FORWARD, boot=False),
-        Member("affine", 17, 2, 9000, device, direction=rl.FORWARD),   # chunked forward
+        Member("affine", 17, 2, 20000, device, direction=rl.FORWARD),  # chunked forward
         Member("gae", 18, 0, 128, device),                       # empty
         # one-wave members (>= 4096 rows of 257..1023 steps), the last
         # workgroup of each only partly filled

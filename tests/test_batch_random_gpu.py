@@ -26,7 +26,7 @@ def random_members(rng, device):
         op = str(rng.choice(OPS))
         u = rng.random()
         if u < 0.1:      # few long rows: the chunked path
-            N, T = int(rng.integers(1, 9)), int(rng.integers(4097, 12000))
+            N, T = int(rng.integers(1, 9)), int(rng.integers(16384, 24000))
         elif u < 0.2:    # empty calls
             N, T = int(rng.choice([0, 3])), int(rng.choice([0, 64]))
         else:

@@ -23,7 +23,7 @@ def test_graph_replays_equal_eager(gpu_device):
     r, v, t, tr, tv, b = (dev(x) for x in (d.rewards, d.values, d.terminated, d.truncated,
                                            d.trunc_values, d.bootstrap))
     mu, pi = dev(d.behaviour_logp), dev(d.target_logp)
-    long = workloads.backward_rollout(12, 3, 9000)
+    long = workloads.backward_rollout(12, 3, 20000)
     lr, lv, lt = dev(long.rewards), dev(long.values), dev(long.terminated)
     f = workloads.forward_rollout(13, 64, 512)
     x, st = dev(f.increments), dev(f.starts)
@@ -32,7 +32,7 @@ def test_graph_replays_equal_eager(gpu_device):
     outs = {k: torch.empty(512, 128, device=gpu_device) for k in ("adv", "ret", "td", "vs", "pg",
                                                                      "adv2", "ret2", "grad")}
     outs["traces"] = torch.empty(64, 512, device=gpu_device)
-    outs["long"] = torch.empty(3, 9000, device=gpu_device)
+    outs["long"] = torch.empty(3, 20000, device=gpu_device)
     outs["bf"] = torch.empty(512, 128, dtype=torch.bfloat16, device=gpu_device)
     stats = torch.empty(2, dtype=torch.float64, device=gpu_device)
     loss = torch.empty(1, dtype=torch.float64, device=gpu_device)

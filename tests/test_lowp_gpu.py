@@ -25,8 +25,8 @@ DTYPES = [torch.bfloat16, torch.float16]
 # T % 4 != 0 (windows widened to aligned starts), wave-local, eight-wave (rows
 # sharing tiles), one-wave (>= 4096 rows of 257..1023 steps, with T % 4 == 0
 # and not), eight-wave, chunked (few long rows, with T % 4 == 0 and not)
-SHAPES = [(5, 37), (300, 128), (33, 512), (4097, 300), (4097, 301), (9, 1024), (3, 4100),
-          (3, 4101), (2, 9000)]
+SHAPES = [(5, 37), (300, 128), (33, 512), (4097, 300), (4097, 301), (9, 1024), (3, 16400),
+          (3, 16401), (2, 20000)]
 
 
 def assert_lowp(gpu, ref, dtype, what):

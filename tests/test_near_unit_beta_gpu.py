@@ -29,7 +29,7 @@ pytestmark = pytest.mark.gpu
 BETAS = [0.995, 0.999, 0.9999, 1.0]
 # (N, T): 8-wave rows spanning waves; one wave per row (>= 4096 rows of
 # 257..1023 steps); skewed windows (T % 4 != 0); one tile; several tiles;
-# chunked (fewer than 64 rows of more than 4096 steps); and short rows
+# chunked (8 rows of 65536 steps); and short rows
 # that stay fp32 (packed across waves, and wave-local)
 SHAPES = [(64, 512), (4096, 520), (64, 1001), (48, 2048), (96, 16384), (8, 65536), (8, 65533),
           (700, 200), (512, 256)]

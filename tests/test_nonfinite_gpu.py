@@ -25,7 +25,7 @@ pytestmark = pytest.mark.gpu
 
 # wave-local, T % 4 != 0 (skewed windows), one-wave (>= 4096 rows), 8-wave
 # rows spanning waves, chunked few long rows
-SHAPES = [(300, 128), (97, 127), (4096, 300), (40, 1000), (3, 9000)]
+SHAPES = [(300, 128), (97, 127), (4096, 300), (40, 1000), (3, 17000)]
 
 
 def dev(x):

@@ -394,16 +394,20 @@ def test_repeat_calls_are_deterministic(gpu_device):
 
 
 # ------------------------------------------------- few long rows: chunked path
-# Fewer than 64 rows of more than 4096 steps (aligned arrays) are split into
-# chunks that run in parallel: aggregate, chunk carries, apply.  Chunks span
-# 2048 steps for T % 4 == 0, 2040 otherwise (the last in scan order 4 to 2043).
-# Shapes cover an exact multiple of the chunk, a short last chunk in scan
-# order, a last chunk longer than the others, and single rows.
+# Few long rows (16384 steps or more; fewer than 96 rows, fewer than 160 from
+# 32768 steps on) are split into chunks that run in parallel: aggregate,
+# chunk carries, apply.  Chunks span 2048 steps for T % 4 == 0, 2040
+# otherwise (the last in scan order 4 to 2043).  Shapes cover an exact
+# multiple of the chunk, a last chunk of 1 step, a short last chunk in scan
+# order, a last chunk longer than the others, single rows, and both sides of
+# each row bound (95 / 96 rows, 159 / 160 rows, and for the forward scans
+# 199 / 200 rows of 131072 steps: the second of each pair takes one
+# workgroup per row).
 
-LONG_SHAPES = [(3, 4100), (2, 6144), (5, 10000), (1, 65536), (4, 20480), (63, 4104),
-               (64, 4104),
+LONG_SHAPES = [(3, 16388), (2, 16384), (3, 16385), (5, 20000), (1, 65536), (4, 20480),
+               (95, 16388), (96, 16388), (159, 32768), (160, 32768),
                # T % 4 != 0: chunk starts at any offset from an aligned step
-               (3, 4101), (2, 6123), (2, 6125), (5, 10001), (1, 65537), (63, 4103)]
+               (3, 16387), (2, 18363), (2, 18365), (5, 20001), (1, 65537), (95, 16387)]
 
 
 @pytest.mark.parametrize("N,T", LONG_SHAPES)
@@ -418,7 +422,7 @@ def test_chunked_backward_estimators(N, T, gpu_device):
         check_retrace(d, gpu_device, trunc=trunc, what=what)
 
 
-@pytest.mark.parametrize("N,T", LONG_SHAPES)
+@pytest.mark.parametrize("N,T", LONG_SHAPES + [(199, 131072), (200, 131072)])
 def test_chunked_forward_scans(N, T, gpu_device):
     f = workloads.forward_rollout(400 + N + T, N, T, p_start=0.002)
     for conv in (rl.RESET_ON_START, rl.RESET_AFTER_DONE):
