@@ -8,7 +8,8 @@ library calls over one rollout (inputs resident in HBM).  Prints ONE JSON line.
 Measurement:
   * cold cache: every call reads a different copy of the rollout, rotating
     over >= 1 GiB of copies, so neither the 4 MB-per-XCD L2 nor the 256 MB
-    Infinity Cache can serve the operands;
+    Infinity Cache can serve the operands (the fused consumers' small
+    workspaces are one per consumer, as a caller keeps them);
   * each step is one rlca_run_batch holding the step's calls, which share one
     grouped launch (pre-bound ctypes call, asynchronous on one stream);
     --launch eager makes one library call per estimator instead, and
@@ -199,10 +200,16 @@ def make_sets(torch, arrays, calls, device, min_call_bytes, real=None):
         for k in ("stats", "loss"):
             if k in named:
                 s[k] = torch.zeros(2, dtype=torch.float64, device=device)
-        for k in ("ws", "ws2"):
-            if k in named:   # zero-filled once; every call leaves it so
-                s[k] = torch.zeros(WORKSPACE_BYTES, dtype=torch.uint8, device=device)
         sets.append(s)
+    # the fused consumers' workspaces (ticket counters and per-workgroup
+    # partial sums, zero-filled once; every call leaves them so) are one per
+    # consumer for the whole rotation, as a caller keeps one per stream: the
+    # rotation keeps the inputs and outputs cold, not the library's state
+    for k in ("ws", "ws2"):
+        if k in named:
+            ws = torch.zeros(WORKSPACE_BYTES, dtype=torch.uint8, device=device)
+            for s in sets:
+                s[k] = ws
     return sets
 
 
@@ -248,11 +255,14 @@ FLOOR_ROLES["rlca_ppo_clip_loss"] = ["in", None, "in", "in", None, None, None, N
 
 
 class _FloorCall(ctypes.Structure):
+    # inputs ordered by element size: n4 4-byte, then n2 2-byte, then n1 1-byte;
+    # magic, shift and sig are filled in by bench_floor_launch
     _fields_ = [("ins", ctypes.c_void_p * 9), ("outs", ctypes.c_void_p * 2),
                 ("row", ctypes.c_void_p), ("steps", ctypes.c_uint64), ("T", ctypes.c_uint32),
-                ("tiles", ctypes.c_uint32), ("in_bytes", ctypes.c_uint8 * 9),
-                ("out_bytes", ctypes.c_uint8 * 2), ("row_bytes", ctypes.c_uint8),
-                ("nin", ctypes.c_uint8), ("nout", ctypes.c_uint8)]
+                ("tiles", ctypes.c_uint32), ("magic", ctypes.c_uint32),
+                ("shift", ctypes.c_uint32), ("n4", ctypes.c_uint8), ("n2", ctypes.c_uint8),
+                ("n1", ctypes.c_uint8), ("nout", ctypes.c_uint8), ("out_bytes", ctypes.c_uint8),
+                ("row_bytes", ctypes.c_uint8), ("sig", ctypes.c_uint8), ("pad", ctypes.c_uint8)]
 
 
 class _FloorLaunch(ctypes.Structure):
@@ -266,20 +276,26 @@ def floor_record(calls, bufs_per_call, n, t):
     for c, (call, bufs) in enumerate(zip(calls, bufs_per_call)):
         _, fname, template, _, _ = call
         f = rec.calls[c]
-        nin = nout = 0
+        ins, outs = [], []
         for role, a in zip(FLOOR_ROLES[fname], template):
             if role is None or not (isinstance(a, str) and a.startswith("@")):
                 continue
             x = bufs[a[1:]]
             if role == "in":
-                f.ins[nin], f.in_bytes[nin] = x.data_ptr(), x.element_size()
-                nin += 1
+                ins.append((x.element_size(), x.data_ptr()))
             elif role == "out":
-                f.outs[nout], f.out_bytes[nout] = x.data_ptr(), x.element_size()
-                nout += 1
+                outs.append((x.element_size(), x.data_ptr()))
             else:
                 f.row, f.row_bytes = x.data_ptr(), x.element_size()
-        f.nin, f.nout = nin, nout
+        ins.sort(key=lambda e: -e[0])   # stable: 4-byte, then 2-byte, then 1-byte streams
+        for k, (_, ptr) in enumerate(ins):
+            f.ins[k] = ptr
+        f.n4, f.n2, f.n1 = (sum(1 for e, _ in ins if e == w) for w in (4, 2, 1))
+        if len({e for e, _ in outs}) != 1 or f.n4 + f.n2 + f.n1 != len(ins):
+            raise ValueError(f"{fname}: streams the floor kernel does not take")
+        for k, (_, ptr) in enumerate(outs):
+            f.outs[k] = ptr
+        f.nout, f.out_bytes = len(outs), outs[0][0]
         f.steps, f.T = n * t, t
         f.tiles = (n * t + 2047) // 2048
     return rec

@@ -11,6 +11,13 @@
 // that ends in its 4 steps, and writes its 4 steps of every output with one
 // access, all non-temporal.  The time this takes is what the estimator
 // kernels' memory traffic costs by itself at that size and shape.
+//
+// Every stream's load goes out back to back, before any loaded value is
+// used: inputs come ordered by element size (4-byte, then 2-byte, then
+// 1-byte), each call runs a straight-line body for its counts of streams, and
+// the row-end test divides by T with a multiply-high (Granlund and
+// Montgomery, "Division by invariant integers using multiplication", 1994,
+// the round-up method for an N-bit dividend), its constants set on the host.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -20,16 +27,19 @@ constexpr int kMaxIn = 9, kMaxOut = 2, kMaxCalls = 8;
 constexpr int kLanes = 512, kSteps = 4, kTile = kLanes * kSteps;
 
 struct FloorCall {
-    const void *in[kMaxIn];
+    const void *in[kMaxIn];  // n4 4-byte streams, then n2 2-byte, then n1 1-byte
     void *out[kMaxOut];
-    const void *row;    // per-row input (bootstrap), nullable
-    uint64_t steps;     // num_envs * T, a multiple of 4
-    uint32_t T;         // a multiple of 4
-    uint32_t tiles;     // ceil(steps / 2048)
-    uint8_t in_bytes[kMaxIn];    // element size of each input: 4, 2 or 1
-    uint8_t out_bytes[kMaxOut];  // 4 or 2
-    uint8_t row_bytes;           // 4 or 2
-    uint8_t nin, nout;
+    const void *row;         // per-row input (bootstrap), nullable
+    uint64_t steps;          // num_envs * T, a multiple of 4, at most 2^31
+    uint32_t T;              // a multiple of 4
+    uint32_t tiles;          // ceil(steps / 2048)
+    uint32_t magic, shift;   // n / T == (h + ((n - h) >> 1)) >> shift, h = mulhi(n, magic)
+                             // (set by bench_floor_prepare)
+    uint8_t n4, n2, n1, nout;
+    uint8_t out_bytes;       // 4 or 2, every output of the call
+    uint8_t row_bytes;       // 4 or 2
+    uint8_t sig;             // index of (n4, n2, n1, nout, out_bytes) in kSigs (likewise)
+    uint8_t pad;
 };
 
 struct FloorLaunch {
@@ -40,25 +50,69 @@ struct FloorLaunch {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ uint32_t load_steps(const void *p, int bytes, uint64_t i) {
-    if (bytes == 4) {
-        const u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4 *>(p) + i / 4);
-        return v.x ^ v.y ^ v.z ^ v.w;
+// The stream signatures the benchmark's calls have: (4-byte inputs, 2-byte
+// inputs, 1-byte inputs, outputs, output element bytes).  A call's body is
+// straight-line code for its signature, every load issued before any value
+// is used.
+struct Sig {
+    int n4, n2, n1, nout, ob;
+};
+constexpr Sig kSigs[] = {
+    {2, 0, 1, 2, 4}, {3, 0, 2, 2, 4}, {2, 0, 1, 1, 4}, {3, 0, 2, 1, 4}, {4, 0, 1, 2, 4},
+    {6, 0, 2, 1, 4}, {1, 0, 1, 1, 4}, {3, 0, 0, 1, 4}, {0, 2, 1, 2, 2}, {0, 3, 2, 2, 2},
+    {0, 2, 1, 1, 2}, {0, 3, 2, 1, 2}, {0, 4, 1, 2, 2}, {0, 6, 2, 1, 2}, {0, 1, 1, 1, 2},
+};
+constexpr int kNumSigs = sizeof(kSigs) / sizeof(kSigs[0]);
+
+template <int S>
+__device__ __forceinline__ void floor_body(const FloorCall &f, uint32_t i) {
+    constexpr Sig g = kSigs[S];
+    const uint32_t q = i / kSteps;  // this lane's 4-step group
+    u32x4 a[g.n4 > 0 ? g.n4 : 1];
+    u32x2 b[g.n2 > 0 ? g.n2 : 1];
+    uint32_t c[g.n1 > 0 ? g.n1 : 1];
+#pragma unroll
+    for (int k = 0; k < g.n4; ++k)
+        a[k] = __builtin_nontemporal_load(static_cast<const u32x4 *>(f.in[k]) + q);
+#pragma unroll
+    for (int k = 0; k < g.n2; ++k)
+        b[k] = __builtin_nontemporal_load(static_cast<const u32x2 *>(f.in[g.n4 + k]) + q);
+#pragma unroll
+    for (int k = 0; k < g.n1; ++k)
+        c[k] = __builtin_nontemporal_load(static_cast<const uint32_t *>(f.in[g.n4 + g.n2 + k]) + q);
+    // the row ending in these 4 steps: (i + 4) % T == 0 (T % 4 == 0)
+    const uint32_t n = i + kSteps;
+    const uint32_t h = __umulhi(n, f.magic);
+    const uint32_t r = (h + ((n - h) >> 1)) >> f.shift;  // n / T
+    uint32_t x = 0u;
+    if (f.row != nullptr && r * f.T == n)
+        x = f.row_bytes == 4 ? static_cast<const uint32_t *>(f.row)[r - 1]
+                             : static_cast<const uint16_t *>(f.row)[r - 1];
+#pragma unroll
+    for (int k = 0; k < g.n4; ++k) x ^= a[k].x ^ a[k].y ^ a[k].z ^ a[k].w;
+#pragma unroll
+    for (int k = 0; k < g.n2; ++k) x ^= b[k].x ^ b[k].y;
+#pragma unroll
+    for (int k = 0; k < g.n1; ++k) x ^= c[k];
+#pragma unroll
+    for (int k = 0; k < g.nout; ++k) {
+        if constexpr (g.ob == 4) {
+            const u32x4 o = {x + k, x ^ 1u, x ^ 2u, x ^ 3u};
+            __builtin_nontemporal_store(o, static_cast<u32x4 *>(f.out[k]) + q);
+        } else {
+            const u32x2 o = {x + k, x ^ 1u};
+            __builtin_nontemporal_store(o, static_cast<u32x2 *>(f.out[k]) + q);
+        }
     }
-    if (bytes == 2) {
-        const u32x2 v = __builtin_nontemporal_load(static_cast<const u32x2 *>(p) + i / 4);
-        return v.x ^ v.y;
-    }
-    return __builtin_nontemporal_load(static_cast<const uint32_t *>(p) + i / 4);
 }
 
-__device__ __forceinline__ void store_steps(void *p, int bytes, uint64_t i, uint32_t x) {
-    if (bytes == 4) {
-        const u32x4 v = {x, x ^ 1u, x ^ 2u, x ^ 3u};
-        __builtin_nontemporal_store(v, static_cast<u32x4 *>(p) + i / 4);
-    } else {
-        const u32x2 v = {x, x ^ 1u};
-        __builtin_nontemporal_store(v, static_cast<u32x2 *>(p) + i / 4);
+template <int S>
+__device__ __forceinline__ void dispatch(const FloorCall &f, uint32_t i) {
+    if constexpr (S < kNumSigs) {
+        if (f.sig == S)
+            floor_body<S>(f, i);
+        else
+            dispatch<S + 1>(f, i);
     }
 }
 
@@ -72,44 +126,70 @@ __global__ __launch_bounds__(kLanes) void stream_floor(FloorLaunch l) {
         }
     }
     const FloorCall &f = l.calls[c];
-    const uint64_t i = ((uint64_t)(blockIdx.x - first) * kLanes + threadIdx.x) * kSteps;
-    if (i >= f.steps) return;
-    uint32_t v[kMaxIn + 1];
-#pragma unroll
-    for (int k = 0; k < kMaxIn; ++k) v[k] = k < f.nin ? load_steps(f.in[k], f.in_bytes[k], i) : 0u;
-    v[kMaxIn] = 0u;
-    if (f.row != nullptr && (i + kSteps) % f.T == 0) {
-        const uint64_t r = (i + kSteps) / f.T - 1;
-        v[kMaxIn] = f.row_bytes == 4 ? static_cast<const uint32_t *>(f.row)[r]
-                                     : static_cast<const uint16_t *>(f.row)[r];
-    }
-    uint32_t x = 0;
-#pragma unroll
-    for (int k = 0; k <= kMaxIn; ++k) x ^= v[k];
-#pragma unroll
-    for (int k = 0; k < kMaxOut; ++k)
-        if (k < f.nout) store_steps(f.out[k], f.out_bytes[k], i, x + k);
+    const uint32_t i = ((blockIdx.x - first) * kLanes + threadIdx.x) * kSteps;
+    if (i >= (uint32_t)f.steps) return;
+    dispatch<0>(f, i);
+}
+
+// The round-up constants for dividing 32-bit n by d >= 2: with l = ceil(log2 d),
+// magic = floor(2^32 (2^l - d) / d) + 1 and shift = l - 1.
+bool division_constants(uint32_t d, uint32_t &magic, uint32_t &shift) {
+    if (d < 2) return false;
+    uint32_t l = 0;
+    while ((uint64_t)1 << l < d) ++l;
+    magic = (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << l) - d)) / d + 1);
+    shift = l - 1;
+    return true;
 }
 
 }  // namespace
 
-// Enqueue one floor launch on `stream`; returns the hipError_t of the launch
-// (0 on success), or -1 for a description the kernel does not take.
-extern "C" int bench_floor_launch(const FloorLaunch *l, hipStream_t stream) {
+// Check a launch description and fill in each call's division constants
+// and signature index; returns the launch's workgroup count, or -1 for a
+// description the kernel does not take.  No GPU call.
+extern "C" int64_t bench_floor_prepare(FloorLaunch *l) {
     if (l == nullptr || l->ncalls == 0 || l->ncalls > (uint32_t)kMaxCalls) return -1;
-    uint32_t tiles = 0;
+    int64_t tiles = 0;
     for (uint32_t k = 0; k < l->ncalls; ++k) {
-        const FloorCall &f = l->calls[k];
-        if (f.nin > kMaxIn || f.nout > kMaxOut || f.T == 0 || f.T % kSteps != 0 ||
-            f.steps % kSteps != 0 || f.tiles != (f.steps + kTile - 1) / kTile)
+        FloorCall &f = l->calls[k];
+        if (f.n4 + f.n2 + f.n1 > kMaxIn || f.nout > kMaxOut || f.T % kSteps != 0 ||
+            f.steps % kSteps != 0 || f.steps > ((uint64_t)1 << 31) ||
+            f.tiles != (f.steps + kTile - 1) / kTile || (f.out_bytes != 4 && f.out_bytes != 2) ||
+            (f.row != nullptr && f.row_bytes != 4 && f.row_bytes != 2) ||
+            !division_constants(f.T, f.magic, f.shift))
             return -1;
+        f.sig = kNumSigs;
+        for (int g = 0; g < kNumSigs; ++g)
+            if (kSigs[g].n4 == f.n4 && kSigs[g].n2 == f.n2 && kSigs[g].n1 == f.n1 &&
+                kSigs[g].nout == f.nout && kSigs[g].ob == f.out_bytes)
+                f.sig = (uint8_t)g;
+        if (f.sig == kNumSigs) return -1;
         tiles += f.tiles;
     }
+    return tiles;
+}
+
+// Enqueue one floor launch on `stream` (the description as bench_floor_prepare
+// takes it; the caller's copy is not changed); returns the hipError_t of the
+// launch (0 on success), or -1 for a description the kernel does not take.
+extern "C" int bench_floor_launch(const FloorLaunch *l, hipStream_t stream) {
+    if (l == nullptr) return -1;
     FloorLaunch copy = *l;
+    const int64_t tiles = bench_floor_prepare(&copy);
+    if (tiles < 0) return -1;
     void *args[] = {&copy};
-    return (int)hipLaunchKernel((const void *)stream_floor, dim3(tiles), dim3(kLanes), args, 0,
-                                stream);
+    return (int)hipLaunchKernel((const void *)stream_floor, dim3((uint32_t)tiles), dim3(kLanes),
+                                args, 0, stream);
 }
 
 // sizeof(FloorLaunch), for the caller's structure layout check
 extern "C" size_t bench_floor_launch_bytes() { return sizeof(FloorLaunch); }
+
+// n / d by the kernel's method, on the host: for the caller's check of the
+// constants (returns UINT32_MAX for a divisor the kernel does not take).
+extern "C" uint32_t bench_floor_divide(uint32_t n, uint32_t d) {
+    uint32_t magic, shift;
+    if (!division_constants(d, magic, shift)) return UINT32_MAX;
+    const uint32_t h = (uint32_t)(((uint64_t)n * magic) >> 32);
+    return (h + ((n - h) >> 1)) >> shift;
+}
