@@ -958,7 +958,8 @@ def main():
             "source": (f"rocprofv3 kernel trace, profiles/{prof_file}" if g_prof is not None
                        else "HIP events, back to back"),
             "avg_us_event": round(ms * 1e3, 3),
-            "traffic": measured_traffic("gae", args.workload),
+            "traffic": measured_traffic("gae" + ("" if args.dtype == "f32" else "_" + args.dtype),
+                                        args.workload),
             "algorithmic_bytes": b,
         }
     if not args.no_cpu_baseline:
