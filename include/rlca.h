@@ -86,10 +86,11 @@
  *          (after about 1,700 steps at gamma * lambda = 0.94 in fp32 scans,
  *          far later in fp64 ones).  A NaN log-probability gives a NaN
  *          importance weight (not a clamped one).
- * Numerics: fp32 arithmetic throughout (the summary's §4 requires float32
- *          scans); the scan reassociates the recurrence (associativity,
- *          summary §5), so results match a sequential fp64 evaluation to
- *          rounding, not bit for bit.  The int32 prefix sum is exact
+ * Numerics: fp32 arithmetic (the summary's §4 requires float32 scans),
+ *          with the fp64 scans stated below where fp32 would miss the
+ *          summary's tolerance; the scan reassociates the recurrence
+ *          (associativity, summary §5), so results match a sequential fp64
+ *          evaluation to rounding, not bit for bit.  The int32 prefix sum is exact
  *          (two's-complement wrap).  Arrays may instead be stored as bf16 or
  *          fp16 (rlca_dtype; the summary's §9 defers bfloat16 I/O): they are
  *          widened exactly to fp32 on load and every output is rounded once,
