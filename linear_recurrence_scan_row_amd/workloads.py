@@ -156,6 +156,50 @@ CONFIGS = {
 }
 
 
+def device_rollout(seed: int, num_envs: int, T: int, device, arrays, p_term: float = 0.001,
+                   p_trunc: float = 0.0005, slab_steps: int = 1 << 28):
+    """Rollout tensors drawn directly on `device` with torch's seeded generator,
+    for sizes whose host copies would be unwieldy (billions of steps).  Only
+    the named `arrays` are drawn, in this fixed order: rewards, values,
+    trunc_values (N(0, 1)), increments (U(0, 1)), ints (int32 U{-100..100}),
+    terminated (Bernoulli p_term), truncated (Bernoulli p_trunc, cleared where
+    terminated), starts (Bernoulli p_term), bootstrap ([num_envs], N(0, 1)).
+    Per-step arrays are drawn slab by slab of about `slab_steps` steps (whole
+    rows, at least one), so the flag draws need no full-size temporaries; a
+    seed, shape and slab size always give the same tensors on one device."""
+    import torch
+
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    shape = (num_envs, T)
+    rows = max(1, slab_steps // max(1, T))
+    out = {}
+    for name in ("rewards", "values", "trunc_values", "increments", "ints", "terminated",
+                 "truncated", "starts"):
+        if name not in arrays:
+            continue
+        dtype = {"ints": torch.int32, "terminated": torch.uint8, "truncated": torch.uint8,
+                 "starts": torch.uint8}.get(name, torch.float32)
+        x = torch.empty(shape, dtype=dtype, device=device)
+        for r0 in range(0, num_envs, rows):
+            part = x[r0:r0 + rows]
+            if name in ("rewards", "values", "trunc_values"):
+                part.normal_(generator=gen)
+            elif name == "increments":
+                part.uniform_(generator=gen)
+            elif name == "ints":
+                part.random_(-100, 101, generator=gen)
+            else:
+                p = p_trunc if name == "truncated" else p_term
+                part.copy_(torch.rand(part.shape, generator=gen, device=device) < p)
+                if name == "truncated" and "terminated" in out:
+                    part.masked_fill_(out["terminated"][r0:r0 + rows].bool(), 0)
+        out[name] = x
+    if "bootstrap" in arrays:
+        out["bootstrap"] = torch.randn(num_envs, generator=gen, device=device)
+    return out
+
+
 def make(name: str, num_envs: int | None = None, T: int | None = None):
     """Draw the named workload; ``num_envs`` / ``T`` override the shape (same recipe)."""
     cfg = dict(CONFIGS[name])
