@@ -613,20 +613,28 @@ def _oracle_passes(name, lo, hi, seconds):
             return passes, el
 
 
-def run_cpu_baseline(name, cfg, host, seconds, workers=1):
+def run_cpu_baseline(name, cfg, host, seconds, workers=1, step_bytes=None):
     """The fp64 sequential oracle on this host's CPU over the same rollout and
     calls, repeated for about `seconds`.  workers > 1 splits the rows evenly
     over that many worker processes (fresh interpreters, no GPU state) that
-    run at the same time."""
+    run at the same time.  With `step_bytes` (the GPU step's algorithmic
+    bytes) the result also carries the same byte model's GB/s, for context."""
     d = host
     nfns = len(oracle_calls(name, cfg, d))
     nt = d.num_envs * d.T
+
+    def with_gbs(rec):
+        if step_bytes is not None:   # passes per second times the bytes of one pass
+            rec["gbs"] = round(rec["value"] / (nfns * nt) * step_bytes / 1e9, 3)
+        return rec
+
     if workers == 1:
         passes, el = _oracle_passes(name, 0, d.num_envs, seconds)
-        return dict(value=passes * nfns * nt / el, unit="env-steps/s", cores=1, kind="oracle",
-                    sample=(f"full {d.num_envs}x{d.T} rollout, {nfns} estimator calls per "
-                            f"pass, {passes} passes in {el:.1f} s, one thread, fp64 "
-                            f"sequential C"))
+        return with_gbs(dict(value=passes * nfns * nt / el, unit="env-steps/s", cores=1,
+                             kind="oracle",
+                             sample=(f"full {d.num_envs}x{d.T} rollout, {nfns} estimator calls "
+                                     f"per pass, {passes} passes in {el:.1f} s, one thread, "
+                                     f"fp64 sequential C")))
     import multiprocessing
     from concurrent.futures import ProcessPoolExecutor
 
@@ -637,10 +645,11 @@ def run_cpu_baseline(name, cfg, host, seconds, workers=1):
                           [hi for _, hi in jobs], [seconds] * len(jobs)))
     steps = sum(p * nfns * (hi - lo) * d.T for (p, _), (lo, hi) in zip(res, jobs))
     el = max(e for _, e in res)
-    return dict(value=float(steps / el), unit="env-steps/s", cores=len(jobs), kind="oracle",
-                sample=(f"full {d.num_envs}x{d.T} rollout, {nfns} estimator calls per pass, "
-                        f"rows split over {len(jobs)} worker processes running together for "
-                        f"{el:.1f} s, fp64 sequential C"))
+    return with_gbs(dict(value=float(steps / el), unit="env-steps/s", cores=len(jobs),
+                         kind="oracle",
+                         sample=(f"full {d.num_envs}x{d.T} rollout, {nfns} estimator calls per "
+                                 f"pass, rows split over {len(jobs)} worker processes running "
+                                 f"together for {el:.1f} s, fp64 sequential C")))
 
 
 # ------------------------------------------------------------------ traffic
@@ -963,7 +972,8 @@ def main():
             "algorithmic_bytes": b,
         }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = run_cpu_baseline(args.workload, cfg, host, args.cpu_seconds)
+        out["cpu_baseline"] = run_cpu_baseline(args.workload, cfg, host, args.cpu_seconds,
+                                               step_bytes=res["step_bytes"])
         try:
             nproc = int(subprocess.run(["nproc"], capture_output=True, text=True).stdout)
         except (OSError, ValueError):
@@ -975,7 +985,8 @@ def main():
         cores = min(16, len(os.sched_getaffinity(0)))
         if cores > 1:
             out["cpu_baseline_all_cores"] = run_cpu_baseline(args.workload, cfg, host,
-                                                             args.cpu_seconds / 2, cores)
+                                                             args.cpu_seconds / 2, cores,
+                                                             step_bytes=res["step_bytes"])
     print(json.dumps(out), flush=True)
 
 

@@ -34,6 +34,9 @@ def test_cpu_baseline_leg_reports_its_sample():
     assert r["value"] > 0 and "8x16" in r["sample"]
     r2 = bench.run_cpu_baseline("gae_8x16", cfg, host, 0.2, workers=2)
     assert r2["cores"] == 2 and r2["value"] > 0
+    # with the step's bytes, the byte model's GB/s: passes per second times bytes per pass
+    r3 = bench.run_cpu_baseline("gae_8x16", cfg, host, 0.2, step_bytes=2848)
+    assert r3["gbs"] == pytest.approx(r3["value"] / (8 * 16) * 2848 / 1e9, rel=1e-3, abs=1e-3)
 
 
 @pytest.mark.gpu
@@ -64,5 +67,5 @@ def test_bench_prints_one_json_line(gpu_device):
     g = d["roofline_gae_call"]
     assert g["frac"] == pytest.approx(g["achieved"] / r["peak"], abs=1e-4)
     c = d["cpu_baseline"]
-    assert c["kind"] == "oracle" and c["cores"] >= 1 and c["value"] > 0
+    assert c["kind"] == "oracle" and c["cores"] >= 1 and c["value"] > 0 and c["gbs"] > 0
     assert d["host_cores"]["affinity"] >= 1 and d["host_cores"]["nproc"] >= 1

@@ -199,6 +199,13 @@ def test_config_forward_16384x512(gpu_device):
                                                c["gamma"]), "16384x512 discounted")
     check_forward(f, gpu_device, rl.RESET_ON_START, c["gamma"], c["lam"], what="16384x512")
     check_forward(f, gpu_device, rl.RESET_AFTER_DONE, c["gamma"], c["lam"], what="16384x512")
+    # the two reset conventions over the same boundaries: the same launch, bit for bit
+    s, dn = dev(f.starts, gpu_device), dev(f.dones, gpu_device)
+    x, xi = dev(f.increments, gpu_device), dev(f.ints, gpu_device)
+    assert torch.equal(rl.eligibility_traces(x, s, rl.RESET_ON_START, c["gamma"], c["lam"]),
+                       rl.eligibility_traces(x, dn, rl.RESET_AFTER_DONE, c["gamma"], c["lam"]))
+    assert torch.equal(rl.episodic_prefix_sum(xi, s, rl.RESET_ON_START),
+                       rl.episodic_prefix_sum(xi, dn, rl.RESET_AFTER_DONE))
 
 
 # ------------------------------------------------------------------- edge cases
