@@ -701,6 +701,8 @@ def measured_traffic(kernel_name, workload):
 
 # ------------------------------------------------------------------ size sweep
 
+SWEEP_WARMUP_S = 0.2   # untimed launches before each point's trials
+
 # (num_envs, T, estimators) of each sweep grid: "sizes" spans the rollout
 # shapes of the workloads above; "long" spans few long rows on both sides of
 # the chunked path's bounds (rows of 16384 steps or more; fewer than 96
@@ -786,16 +788,24 @@ def run_sweep(args):
                 batch = max(20, min(400, int(2e9 // call_bytes)))
                 trials = []
                 with torch.cuda.stream(stream):
-                    # warm up for a quarter of a trial, then three trials of
-                    # `batch` back-to-back launches; the fastest trial is
-                    # reported (the pages' protocol also keeps a minimum), so
-                    # that a transient stall of the host or the GPU during
-                    # one trial does not stand for the kernel
-                    for i in range(max(20, batch // 4)):
-                        fn, a = plan[i % nsets]
-                        if fn(*a) != 0:
-                            raise RuntimeError(f"{name} {n}x{t}: launch failed")
-                    torch.cuda.synchronize()
+                    # warm up for at least SWEEP_WARMUP_S of launches (a
+                    # quarter of a trial alone was too short for the clocks
+                    # to rise at the small points: 4096 x 128 GAE + trunc
+                    # read 4.8 us there against 3.8 us after the bench's
+                    # warm-up), then three trials of `batch` back-to-back
+                    # launches; the fastest trial is reported (the pages'
+                    # protocol also keeps a minimum), so that a transient
+                    # stall of the host or the GPU during one trial does not
+                    # stand for the kernel
+                    warm_until = time.perf_counter() + SWEEP_WARMUP_S
+                    while True:
+                        for i in range(max(20, batch // 4)):
+                            fn, a = plan[i % nsets]
+                            if fn(*a) != 0:
+                                raise RuntimeError(f"{name} {n}x{t}: launch failed")
+                        torch.cuda.synchronize()
+                        if time.perf_counter() >= warm_until:
+                            break
                     for _ in range(3):
                         order = [plan[i % nsets] for i in range(batch)]
                         statuses = []
