@@ -977,14 +977,15 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
 // seven the compiler picks on its own for these heavier bodies (their SGPR
 // count) an eighth of the waves waits for a second round.  The SGPRs over
 // the limit spill to VGPR lanes.  Lighter variants reach eight by themselves
-// and keep their registers.  The fp64 scans (F64) do not ask: at eight waves
-// their VGPRs would spill to memory.
+// and keep their registers.  The fp64 scans (F64) and the statistics
+// epilogue (STATS, fp64 sums) do not ask: at eight waves their VGPRs would
+// spill to memory, and a kernel with memory spills needs scratch memory.
 #define RLCA_EIGHT_WAVES(NEED) __attribute__((amdgpu_waves_per_eu((NEED) ? 8 : 1)))
 
 template <int EST, bool TRUNC, int VEC, int NW, bool WAVE_LOCAL, int MODE, typename S,
           bool STATS = false, bool F64 = false>
 __global__ __launch_bounds__(NW * kWave)
-RLCA_EIGHT_WAVES(NW == 8 && !WAVE_LOCAL && VEC != kScalarIO && !F64)
+RLCA_EIGHT_WAVES(NW == 8 && !WAVE_LOCAL && VEC != kScalarIO && !F64 && !STATS)
 void backward_scan(LEAD_ARGS, BackwardParams p) {
     adopt_lead<EST>(p, LEAD_NAMES);
     backward_body<EST, TRUNC, VEC, NW, WAVE_LOCAL, MODE, S, STATS, F64>(p, blockIdx.x,
