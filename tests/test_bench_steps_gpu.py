@@ -4,7 +4,8 @@ bench.py times each workload as one rlca_run_batch holding the step's calls:
 the four GAE / TD(lambda) calls over 4096 x 128 and the four forward-workload
 calls over 16384 x 512 share one grouped launch each, and a one-call step
 (V-Trace 4096 x 256, Retrace 2048 x 1024, GAE 8 x 16) runs the call's own
-kernel.  These tests build those batches with bench.py's own call tables,
+kernel, and the few-long-rows steps (8 x 131072, 1 x 2^20) run each call's
+three chunked launches.  These tests build those batches with bench.py's own call tables,
 rotation sets and recording code, run one step and compare every output of
 every call with the oracle on the same inputs:
 
@@ -41,9 +42,10 @@ def _seen_by_kernel(arrays, dtype):
 
 
 def _oracle(call_name, h, cfg):
-    """The oracle's outputs for one call of a bench step, in call order."""
-    g = cfg["gamma"]
-    lam = cfg.get("lam", 0.95)
+    """The oracle's outputs for one call of a bench step, in call order, with
+    the parameters as the library receives them (fp32)."""
+    g = float(np.float32(cfg["gamma"]))
+    lam = float(np.float32(cfg.get("lam", 0.95)))
     if call_name in ("gae", "gae+trunc", "td_lambda", "td_lambda+trunc"):
         tr = call_name.endswith("+trunc")
         args = (h["r"], h["v"], h["term"], h["trunc"] if tr else None, h["tv"] if tr else None,
@@ -59,6 +61,10 @@ def _oracle(call_name, h, cfg):
                                h["tv"], h["b"], g, lam, cfg["c_bar"]),)
     if call_name == "discounted":
         return (oracle.discounted_returns(h["r"], h["dones"], None, None, h["b"], g),)
+    if call_name == "eligibility" and "x" not in h:
+        # the few-long-rows steps: traces over the rewards, resets after
+        # terminated steps
+        return (oracle.eligibility_traces(h["r"], h["term"], oracle.RESET_AFTER_DONE, g, lam),)
     if call_name == "eligibility":
         return (oracle.eligibility_traces(h["x"], h["starts"], oracle.RESET_ON_START, g, lam),)
     if call_name == "prefix_sum_f32":
@@ -89,7 +95,7 @@ STEPS = [("gae_td_4096x128", "f32"), ("gae_td_4096x128", "bf16"), ("gae_td_4096x
          ("vtrace_4096x256", "f32"), ("vtrace_4096x256", "bf16"),
          ("retrace_2048x1024", "f32"), ("retrace_2048x1024", "bf16"),
          ("forward_16384x512", "f32"), ("forward_16384x512", "bf16"),
-         ("gae_8x16", "f32")]
+         ("gae_8x16", "f32"), ("long_8x131072", "f32"), ("long_1x1048576", "f32")]
 
 
 @pytest.mark.parametrize("name,dtype", STEPS)
