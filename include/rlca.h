@@ -64,8 +64,12 @@
  *          before anything is enqueued and a failed call has no side effects.
  *            RLCA_ERR_NULL_POINTER   a required pointer is NULL
  *            RLCA_ERR_INVALID_SIZE   num_envs < 0, T < 0, T > RLCA_MAX_T,
- *                                    num_envs > RLCA_MAX_ENVS, or the byte
- *                                    size of an array overflows
+ *                                    num_envs > RLCA_MAX_ENVS, the byte
+ *                                    size of an array overflows, or the
+ *                                    launch would need more than 2^31 - 1
+ *                                    workgroups (only num_envs near
+ *                                    RLCA_MAX_ENVS with rows longer than one
+ *                                    tile: terabytes of input)
  *            RLCA_ERR_INVALID_VALUE  gamma or lambda outside [0, 1] or not
  *                                    finite, rho_bar <= 0 or not finite,
  *                                    c_bar outside (0, 1], an unknown enum

@@ -54,9 +54,9 @@ __global__ __launch_bounds__(kPpoThreads) void ppo_clip_loss(
             po = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(logp_old) + i);
         }
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (NORM) {
-            mean = (float)stats[0];
-            scale = (float)(1.0 / (stats[1] + (double)norm_eps));
+        if constexpr (NORM) {  // written by an earlier launch: coherent loads
+            mean = (float)load_coherent(stats);
+            scale = (float)(1.0 / (load_coherent(stats + 1) + (double)norm_eps));
         }
         while (i < n4) {
             f4 g;
@@ -83,9 +83,9 @@ __global__ __launch_bounds__(kPpoThreads) void ppo_clip_loss(
             if constexpr (GRAD) grad[j] = g;
         }
     } else {
-        if constexpr (NORM) {
-            mean = (float)stats[0];
-            scale = (float)(1.0 / (stats[1] + (double)norm_eps));
+        if constexpr (NORM) {  // written by an earlier launch: coherent loads
+            mean = (float)load_coherent(stats);
+            scale = (float)(1.0 / (load_coherent(stats + 1) + (double)norm_eps));
         }
         for (int64_t i = (int64_t)blockIdx.x * kPpoThreads + threadIdx.x; i < M; i += stride) {
             const float ah = NORM ? (adv[i] - mean) * scale : adv[i];

@@ -270,25 +270,38 @@ __device__ __forceinline__ E *chunk_slot(void *out, int64_t base, uint32_t out_p
     return reinterpret_cast<E *>(static_cast<S *>(out) + base);
 }
 
+// Hand-off words pass between launches: one workgroup writes them, another
+// reads them in a later launch, on any XCD.  They are stored and loaded as
+// agent-scope atomics: coherent across the XCDs' L2 caches, and never read
+// through the scalar cache, as a plain load of a workgroup-uniform address
+// could be (a stale word there would be a wrong carry).
+__device__ __forceinline__ void store_word(uint32_t *w, uint32_t x) {
+    __hip_atomic_store(w, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t load_word(const uint32_t *w) {
+    return __hip_atomic_load(const_cast<uint32_t *>(w), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // A chunk's map (a, b) as scan values C, each as raw 32-bit words (two for
 // fp64), from word 0 of the chunk's slot; the carry comes back in word 0 as
 // one value of the kernel's value type.
 template <typename C>
 __device__ __forceinline__ void put_words(uint32_t *w, C x) {
     if constexpr (sizeof(C) == 4) {
-        w[0] = __builtin_bit_cast(uint32_t, x);
+        store_word(w, __builtin_bit_cast(uint32_t, x));
     } else {
         const uint64_t u = __builtin_bit_cast(uint64_t, x);
-        w[0] = (uint32_t)u;
-        w[1] = (uint32_t)(u >> 32);
+        store_word(w, (uint32_t)u);
+        store_word(w + 1, (uint32_t)(u >> 32));
     }
 }
 template <typename C>
 __device__ __forceinline__ C get_words(const uint32_t *w) {
     if constexpr (sizeof(C) == 4) {
-        return __builtin_bit_cast(C, w[0]);
+        return __builtin_bit_cast(C, load_word(w));
     } else {
-        return __builtin_bit_cast(C, ((uint64_t)w[1] << 32) | w[0]);
+        return __builtin_bit_cast(C, ((uint64_t)load_word(w + 1) << 32) | load_word(w));
     }
 }
 
@@ -687,7 +700,9 @@ __device__ __forceinline__ void adopt_lead(ForwardParams &p, LEAD_ARGS) {
 // ------------------------------------------------------------- backward kernel
 // A_t = alpha_t + beta_t * A_{t+1}.  Lanes take chunks in reverse time order, so
 // the lane-order scan of scan_core.hpp runs from the end of the tile backwards.
-// Groups g, g + g_stride, ... of the launch run through one workgroup.
+// Workgroup g runs group g; with STATS the grid is capped (kStatsMaxGrid,
+// one partial sum per workgroup) and groups g, g + g_stride, ... run
+// through one workgroup.
 // STATS: also sum out0 and its square over the workgroup's valid steps (in
 // fp64) and store the pair in stats_partials[2 * blockIdx.x ...].
 // F64: the scan runs in fp64 (ScanOf; every chunk mode does); outputs are
@@ -725,7 +740,10 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
 
     // The grid never exceeds the group count, so the first group always
     // exists; testing only at the bottom lets every kernel-argument load go
-    // out together instead of after a first round trip for the bound.
+    // out together instead of after a first round trip for the bound.  Only
+    // the statistics launches loop: a loop keeps the array pointers live
+    // across iterations, which at eight waves per SIMD spilled the heavier
+    // bodies' SGPRs (Retrace 2048 x 1024: 3% slower).
     do {
         const Window win = window_of<MODE, true, VEC>(p.geo, g);
         // Memory base and extent of the window: on the kVecSkew path widened
@@ -738,7 +756,8 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
         // or the carry the chunk-carry pass left in the chunk's first slot.
         SV carry = SV(0);
         if constexpr (MODE == kChunkApply)  // issued ahead of the tile's loads
-            carry = SV(chunk_slot<float, S>(p.out0, win.base, p.geo.out0_phase)[0]);
+            carry = SV(get_words<float>(chunk_slot<uint32_t, S>(p.out0, win.base,
+                                                                 p.geo.out0_phase)));
 
         for (uint32_t it = 0; it < ntiles; ++it) {
             const uint32_t off = (ntiles - 1 - it) * kTile + chunk * kK;
@@ -956,7 +975,7 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
             }
         }
         g += g_stride;
-    } while (g < p.geo.num_groups);
+    } while (STATS && g < p.geo.num_groups);
     if constexpr (STATS) {
         workgroup_sum2<NW>(sum, sum_sq);
         // stats = {mean, sample std (divisor M - 1; 0 when M < 2)}
@@ -966,8 +985,8 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
                                                 [=](double s1, double s2) {
             const double mean = s1 / (double)M;
             const double var = M > 1 ? fmax(s2 - s1 * mean, 0.0) / (double)(M - 1) : 0.0;
-            stats[0] = mean;
-            stats[1] = sqrt(var);
+            store_coherent(stats, mean);  // read by the next launch
+            store_coherent(stats + 1, sqrt(var));
         });
     }
 }
@@ -1033,7 +1052,8 @@ __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint3
         const uint32_t ntiles = MODE == kFull ? (L + kTile - 1) / kTile : 1u;
         SV carry = SV(0);
         if constexpr (MODE == kChunkApply)  // issued ahead of the tile's loads
-            carry = SV(chunk_slot<V, S>(p.out, win.base, p.geo.out0_phase)[0]);
+            carry = SV(get_words<V>(chunk_slot<uint32_t, S>(p.out, win.base,
+                                                             p.geo.out0_phase)));
 
         for (uint32_t it = 0; it < ntiles; ++it) {
             const uint32_t off = it * kTile + chunk * kK;
@@ -1128,7 +1148,7 @@ __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint3
             }
         }
         g += g_stride;
-    } while (g < p.geo.num_groups);
+    } while (false);  // one group per workgroup (no statistics launch here)
 }
 
 template <typename V, int KIND, bool AFTER_DONE, int VEC, int NW, bool WAVE_LOCAL, int MODE,
@@ -1183,14 +1203,18 @@ __global__ __launch_bounds__(NW * kWave) void chunk_carries(void *slots, int64_t
 
 // ------------------------------------------------------------------ launching
 
-// Upper bound on the launch grid; larger problems loop over groups.
+// Launch grids: one workgroup per group, up to HIP's largest grid (a call
+// that would need more is refused on the host: it could only come from
+// terabytes of input).  A grouped launch holds at most kMaxGrid workgroups
+// per member (its head words keep workgroup indices in 24 bits).
+constexpr uint32_t kOneShotMaxGrid = 0x7fffffffu;
 constexpr uint32_t kMaxGrid = 1u << 20;
 // Launches that leave one partial sum per workgroup use fewer, longer-lived
 // workgroups (2048 are resident on the chip at once), which keeps the final
 // reduction to one round of loads.
 constexpr uint32_t kStatsMaxGrid = 4096;
 
-inline uint32_t grid_for(int64_t groups, uint32_t cap = kMaxGrid) {
+inline uint32_t grid_for(int64_t groups, uint32_t cap = kOneShotMaxGrid) {
     return groups < (int64_t)cap ? (uint32_t)groups : cap;
 }
 
@@ -1224,7 +1248,7 @@ inline uint32_t skew_rows(uint32_t T, uint32_t tile, uint32_t quantum, uint32_t 
 // Geometry of a launch of shape s: chunked shapes use kChunkWaves-wave
 // chunks, the scalar path 4-wave workgroups, the vector paths s.waves.
 inline Geometry make_geometry(int64_t num_envs, int64_t T, const LaunchShape &s, uint32_t *grid,
-                              uint32_t cap = kMaxGrid) {
+                              uint32_t cap = kOneShotMaxGrid) {
     const int waves = s.chunked ? kChunkWaves : s.vec ? s.waves : 4;
     const uint32_t tile = (uint32_t)waves * kWave * kK;
     Geometry g;
@@ -1248,6 +1272,15 @@ inline Geometry make_geometry(int64_t num_envs, int64_t T, const LaunchShape &s,
     g.num_groups = (uint32_t)groups;
     *grid = grid_for(groups, cap);
     return g;
+}
+
+// Groups of a launch of shape s, before any grid cap: a launch without a
+// group loop needs this many workgroups.
+inline int64_t launch_groups(int64_t num_envs, int64_t T, const LaunchShape &s) {
+    uint32_t grid;
+    const Geometry g = make_geometry(num_envs, T, s, &grid);
+    return s.chunked ? num_envs * (int64_t)g.chunks_per_row
+                     : (num_envs + g.rows_per_group - 1) / g.rows_per_group;
 }
 
 template <typename P>
@@ -1283,7 +1316,7 @@ inline rlca_status launch_chunk_carries(void *slots, const Geometry &geo, bool b
 template <typename V, typename S, typename P>
 inline rlca_status launch_chunked(const void *aggregate, const void *apply, P &params, Lead &lead,
                                   void *slots, bool backward, const LaunchShape &s,
-                                  hipStream_t stream, uint32_t apply_cap = kMaxGrid) {
+                                  hipStream_t stream, uint32_t apply_cap = kOneShotMaxGrid) {
     uint32_t grid;
     params.geo = make_geometry(params.geo.num_envs, params.geo.T, s, &grid);
     const uint32_t apply_grid = grid_for(params.geo.num_groups, apply_cap);
@@ -1297,7 +1330,7 @@ inline rlca_status launch_chunked(const void *aggregate, const void *apply, P &p
 
 template <typename P>
 inline rlca_status launch_full(const void *kernel, const LaunchShape &s, P &params, Lead &lead,
-                               hipStream_t stream, uint32_t cap = kMaxGrid) {
+                               hipStream_t stream, uint32_t cap = kOneShotMaxGrid) {
     uint32_t grid;
     params.geo = make_geometry(params.geo.num_envs, params.geo.T, s, &grid, cap);
     return launch_kernel(kernel, s.vec ? s.waves : 4, grid, params, lead, stream);
@@ -1307,7 +1340,7 @@ inline rlca_status launch_full(const void *kernel, const LaunchShape &s, P &para
 // this shape, the grid capped at `cap`: the scalar path runs 4-wave
 // workgroups.
 inline uint32_t launch_grid(const LaunchShape &s, int64_t num_envs, int64_t T,
-                            uint32_t cap = kMaxGrid) {
+                            uint32_t cap = kOneShotMaxGrid) {
     uint32_t grid;
     make_geometry(num_envs, T, s, &grid, cap);
     return grid;
@@ -1349,7 +1382,7 @@ template <int EST, bool TRUNC, typename S, bool STATS = false>
 rlca_status launch_backward_variant(BackwardParams &p, const LaunchShape &s, hipStream_t stream) {
     Lead lead;
     lead_from<EST>(p, lead);
-    const uint32_t cap = STATS ? kStatsMaxGrid : kMaxGrid;
+    const uint32_t cap = STATS ? kStatsMaxGrid : kOneShotMaxGrid;
     if (s.chunked) {
 #define RLCA_CHUNKED(IO)                                                                       \
     return launch_chunked<float, S>(                                                           \

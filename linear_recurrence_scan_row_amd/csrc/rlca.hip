@@ -326,6 +326,8 @@ static rlca_status prepare_backward(int est, int storage, const void *rewards,
     const void *u8[] = {terminated, truncated};
     const void *outs[] = {out0, out1};
     c->shape = choose_shape(num_envs, T, io_of(T, f32_steps, 6, es, u8, 2, outs, 2), true);
+    if (launch_groups(num_envs, T, c->shape) > (int64_t)kOneShotMaxGrid)
+        return RLCA_ERR_INVALID_SIZE;  // terabytes of input: no launch grid that large
     return RLCA_OK;
 }
 
@@ -382,6 +384,8 @@ static rlca_status prepare_forward(int kind, int storage, const void *x, bool is
     const void *u8[] = {flags};
     const void *outs[] = {out};
     c->shape = choose_shape(num_envs, T, io_of(T, wide, 2, es, u8, 1, outs, 1), false);
+    if (launch_groups(num_envs, T, c->shape) > (int64_t)kOneShotMaxGrid)
+        return RLCA_ERR_INVALID_SIZE;  // terabytes of input: no launch grid that large
     return RLCA_OK;
 }
 

@@ -78,6 +78,13 @@ def test_size_errors(lib):
     assert gae(lib, t=-3) == SIZE
     assert gae(lib, t=(1 << 30) + 1) == SIZE
     assert gae(lib, n=(1 << 31) + 1) == SIZE
+    # 2^31 rows longer than one 2048-step tile would need 2^31 workgroups
+    # (fake arrays 2^45 bytes apart, so that none of them overlaps)
+    far = [k << 45 for k in range(1, 6)]
+    assert gae(lib, r=far[0], v=far[1], term=far[2], adv=far[3], ret=far[4], n=1 << 31,
+               t=2049) == SIZE
+    assert lib.rlca_eligibility_traces(far[0], far[1], 0, 0.9, 0.9, 1 << 31, 2049, far[2],
+                                       None) == SIZE
     assert lib.rlca_discounted_returns(A, C, None, None, None, 0.9, 1 << 31, 1 << 30, D,
                                        None) == SIZE
 

@@ -1,8 +1,8 @@
 """The largest calls: more than 2^31 env-steps in one call, so that every flat
 index passes 32 bits, on each launch shape (rows spanning waves, wave-local
-rows, one-wave row walks, skewed windows, all past the 2^20-workgroup grid
-cap); 2^31 rows of one step, the most rows the ABI takes; and rows of 2^30
-steps, the longest, on the chunked path (past the grid cap as well).
+rows, one-wave row walks, skewed windows, all in grids of more than 2^20
+workgroups); 2^31 rows of one step, the most rows the ABI takes; and rows of
+2^30 steps, the longest, on the chunked path (1.5 million chunks).
 
 Inputs are drawn on the device (workloads.device_rollout, seeded).  Outputs
 are checked against the fp64 oracle on samples whose values they determine
@@ -130,8 +130,8 @@ def _segments(flags_row, T, seed, backward, k=12):
 
 
 def test_longest_rows_chunked(fresh):
-    """Three rows of 2^30 steps: the chunked path, 2^19 chunks per row, so the
-    chunk passes loop past the 2^20-workgroup grid cap."""
+    """Three rows of 2^30 steps: the chunked path, 2^19 chunks per row, one
+    workgroup per chunk in grids of 1.5 million workgroups."""
     N, T = 3, 2**30
     d = workloads.device_rollout(30, N, T, fresh, BACKWARD)
     adv, ret = rl.gae(d["rewards"], d["values"], d["terminated"], d["truncated"],
