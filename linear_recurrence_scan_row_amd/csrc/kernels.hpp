@@ -270,17 +270,15 @@ __device__ __forceinline__ E *chunk_slot(void *out, int64_t base, uint32_t out_p
     return reinterpret_cast<E *>(static_cast<S *>(out) + base);
 }
 
-// Hand-off words pass between launches: one workgroup writes them, another
-// reads them in a later launch, on any XCD.  They are stored as agent-scope
-// atomic words.  The apply pass's carry, one workgroup-uniform word, is read
-// the same way, so that it never comes through the scalar cache, where a
-// plain load of a uniform address would go (a stale word there would be a
-// wrong carry).  The carries pass reads each lane's own map with plain
-// loads, which become merged vector loads (per-word atomic loads measured
-// 2 us slower per call on one row of 2^20 steps).
-__device__ __forceinline__ void store_word(uint32_t *w, uint32_t x) {
-    __hip_atomic_store(w, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+// Hand-off words pass between launches: one workgroup writes them with
+// plain stores, which the end of its launch makes visible to the whole
+// device, and another reads them in a later launch, on any XCD.  The apply
+// pass's carry, one workgroup-uniform word, is read with an agent-scope
+// atomic load, so that it never comes through the scalar cache, where a
+// plain load of a uniform address would go.  The carries pass reads each
+// lane's own map with plain loads, which merge into one vector load.  On one
+// row of 2^20 steps, per-word atomics measured slower: the map stores by
+// 0.3-0.5 us per aggregate launch, the map loads by 2 us per carries launch.
 __device__ __forceinline__ uint32_t load_word(const uint32_t *w) {
     return __hip_atomic_load(const_cast<uint32_t *>(w), __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
@@ -292,16 +290,16 @@ __device__ __forceinline__ uint32_t load_word(const uint32_t *w) {
 template <typename C>
 __device__ __forceinline__ void put_words(uint32_t *w, C x) {
     if constexpr (sizeof(C) == 4) {
-        store_word(w, __builtin_bit_cast(uint32_t, x));
+        w[0] = __builtin_bit_cast(uint32_t, x);
     } else {
         const uint64_t u = __builtin_bit_cast(uint64_t, x);
-        store_word(w, (uint32_t)u);
-        store_word(w + 1, (uint32_t)(u >> 32));
+        w[0] = (uint32_t)u;
+        w[1] = (uint32_t)(u >> 32);
     }
 }
-template <typename C, bool COHERENT = true>
+template <typename C, bool UNIFORM>
 __device__ __forceinline__ C get_words(const uint32_t *w) {
-    if constexpr (!COHERENT) {  // per-lane addresses: vector loads, merged
+    if constexpr (!UNIFORM) {  // per-lane addresses: plain (vector) loads
         if constexpr (sizeof(C) == 4) return __builtin_bit_cast(C, w[0]);
         else return __builtin_bit_cast(C, ((uint64_t)w[1] << 32) | w[0]);
     } else if constexpr (sizeof(C) == 4) {
@@ -762,7 +760,7 @@ __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uin
         // or the carry the chunk-carry pass left in the chunk's first slot.
         SV carry = SV(0);
         if constexpr (MODE == kChunkApply)  // issued ahead of the tile's loads
-            carry = SV(get_words<float>(chunk_slot<uint32_t, S>(p.out0, win.base,
+            carry = SV(get_words<float, true>(chunk_slot<uint32_t, S>(p.out0, win.base,
                                                                  p.geo.out0_phase)));
 
         for (uint32_t it = 0; it < ntiles; ++it) {
@@ -1058,7 +1056,7 @@ __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint3
         const uint32_t ntiles = MODE == kFull ? (L + kTile - 1) / kTile : 1u;
         SV carry = SV(0);
         if constexpr (MODE == kChunkApply)  // issued ahead of the tile's loads
-            carry = SV(get_words<V>(chunk_slot<uint32_t, S>(p.out, win.base,
+            carry = SV(get_words<V, true>(chunk_slot<uint32_t, S>(p.out, win.base,
                                                              p.geo.out0_phase)));
 
         for (uint32_t it = 0; it < ntiles; ++it) {
