@@ -132,7 +132,7 @@ struct LaunchShape {
     uint32_t phase, out0_phase;  // skewed path: as in Geometry
     bool scatter;                // skewed path: as in Geometry
     bool chunked;     // few long rows: the three chunk-mode launches
-    bool f64;         // fp64 scan (ScanOf): rows span waves with beta near 1; chunked
+    bool f64;         // fp64 scan (ScanOf): rows span waves with beta near 1
 };
 
 // ---------------------------------------------------------------- memory access
@@ -709,14 +709,14 @@ __device__ __forceinline__ void adopt_lead(ForwardParams &p, LEAD_ARGS) {
 // through one workgroup.
 // STATS: also sum out0 and its square over the workgroup's valid steps (in
 // fp64) and store the pair in stats_partials[2 * blockIdx.x ...].
-// F64: the scan runs in fp64 (ScanOf; every chunk mode does); outputs are
-// rounded to fp32 once.
+// F64: the scan runs in fp64 (ScanOf; the host's choice, in the chunk modes
+// too); outputs are rounded to fp32 once.
 template <int EST, bool TRUNC, int VEC, int NW, bool WAVE_LOCAL, int MODE, typename S,
           bool STATS = false, bool F64 = false>
 __device__ __forceinline__ void backward_body(BackwardParams &p, uint32_t g, uint32_t g_stride) {
     static_assert(!STATS || MODE != kChunkAggregate, "statistics come from the outputs");
-    static_assert(MODE == kFull || (NW == kChunkWaves && !WAVE_LOCAL && F64),
-                  "a chunk is one tile, scanned in fp64");
+    static_assert(MODE == kFull || (NW == kChunkWaves && !WAVE_LOCAL),
+                  "a chunk is one tile of kChunkWaves waves");
     typedef typename ScanOf<float, F64>::type SV;
     // the importance-weighted bodies compose with the legacy multiply
     // (scan_core.hpp): their beta is never infinite, and they are the ones
@@ -1027,8 +1027,8 @@ void backward_scan(LEAD_ARGS, BackwardParams p) {
 template <typename V, int KIND, bool AFTER_DONE, int VEC, int NW, bool WAVE_LOCAL, int MODE,
           typename S, bool F64 = false>
 __device__ __forceinline__ void forward_body(ForwardParams &p, uint32_t g, uint32_t g_stride) {
-    static_assert(MODE == kFull || (NW == kChunkWaves && !WAVE_LOCAL && F64),
-                  "a chunk is one tile, scanned in fp64");
+    static_assert(MODE == kFull || (NW == kChunkWaves && !WAVE_LOCAL),
+                  "a chunk is one tile of kChunkWaves waves");
     typedef typename ScanOf<V, F64>::type SV;
     constexpr uint32_t kTile = NW * kWave * kK;
     __shared__ SV lds_a[2 * NW], lds_b[2 * NW];
@@ -1170,7 +1170,8 @@ void forward_scan(LEAD_ARGS, ForwardParams p) {
 // (left by the aggregate pass as scan values C in the first words of each
 // chunk's slice of `slots`) in scan order and leaves in each chunk's first
 // word the value of A entering that chunk, as a value of type R (the
-// kernels' value type: fp32 for the float scans, whose maps are fp64).
+// kernels' value type: fp32 for the float scans, whose maps are fp32 or fp64 as
+// their scan is).
 // Lane j of a tile holds chunk j; the last chunk in scan order has no map
 // (identity) but receives its carry.
 template <typename C, typename R, typename S, int NW>
@@ -1316,8 +1317,8 @@ inline rlca_status launch_chunk_carries(void *slots, const Geometry &geo, bool b
 
 // The three chunk-mode launches, all on one stream: aggregate, carries,
 // apply (the apply grid capped at `apply_cap`).  V: the kernels' value type;
-// the chunk maps are scanned in ScanOf<V, true>.
-template <typename V, typename S, typename P>
+// the chunk maps are scanned in ScanOf<V, F64>, the kernels' own scan type.
+template <typename V, typename S, bool F64, typename P>
 inline rlca_status launch_chunked(const void *aggregate, const void *apply, P &params, Lead &lead,
                                   void *slots, bool backward, const LaunchShape &s,
                                   hipStream_t stream, uint32_t apply_cap = kOneShotMaxGrid) {
@@ -1326,8 +1327,8 @@ inline rlca_status launch_chunked(const void *aggregate, const void *apply, P &p
     const uint32_t apply_grid = grid_for(params.geo.num_groups, apply_cap);
     rlca_status st = launch_kernel(aggregate, kChunkWaves, grid, params, lead, stream);
     if (st == RLCA_OK)
-        st = launch_chunk_carries<typename ScanOf<V, true>::type, V, S>(slots, params.geo,
-                                                                         backward, s.skew, stream);
+        st = launch_chunk_carries<typename ScanOf<V, F64>::type, V, S>(slots, params.geo,
+                                                                        backward, s.skew, stream);
     if (st == RLCA_OK) st = launch_kernel(apply, kChunkWaves, apply_grid, params, lead, stream);
     return st;
 }
@@ -1388,15 +1389,19 @@ rlca_status launch_backward_variant(BackwardParams &p, const LaunchShape &s, hip
     lead_from<EST>(p, lead);
     const uint32_t cap = STATS ? kStatsMaxGrid : kOneShotMaxGrid;
     if (s.chunked) {
-#define RLCA_CHUNKED(IO)                                                                       \
-    return launch_chunked<float, S>(                                                           \
+#define RLCA_CHUNKED(IO, F64)                                                                  \
+    return launch_chunked<float, S, F64>(                                                      \
         (const void *)                                                                         \
-            backward_scan<EST, TRUNC, IO, kChunkWaves, false, kChunkAggregate, S, false, true>, \
+            backward_scan<EST, TRUNC, IO, kChunkWaves, false, kChunkAggregate, S, false, F64>,  \
         (const void *)                                                                         \
-            backward_scan<EST, TRUNC, IO, kChunkWaves, false, kChunkApply, S, STATS, true>,     \
+            backward_scan<EST, TRUNC, IO, kChunkWaves, false, kChunkApply, S, STATS, F64>,      \
         p, lead, p.out0, true, s, stream, cap)
-        if (s.skew) RLCA_CHUNKED(kVecSkew);
-        RLCA_CHUNKED(kVecRows);
+        if (s.skew) {
+            if (s.f64) RLCA_CHUNKED(kVecSkew, true);
+            RLCA_CHUNKED(kVecSkew, false);
+        }
+        if (s.f64) RLCA_CHUNKED(kVecRows, true);
+        RLCA_CHUNKED(kVecRows, false);
 #undef RLCA_CHUNKED
     }
     return launch_full(backward_kernel<EST, TRUNC, S, STATS>(s), s, p, lead, stream, cap);
@@ -1447,15 +1452,19 @@ rlca_status launch_forward_variant(ForwardParams &p, const LaunchShape &s, hipSt
     Lead lead;
     lead_from(p, lead);
     if (s.chunked) {
-#define RLCA_CHUNKED(IO)                                                                    \
-    return launch_chunked<V, S>(                                                            \
+#define RLCA_CHUNKED(IO, F64)                                                               \
+    return launch_chunked<V, S, F64>(                                                       \
         (const void *)forward_scan<V, KIND, AFTER_DONE, IO, kChunkWaves, false,             \
-                                   kChunkAggregate, S, true>,                               \
+                                   kChunkAggregate, S, F64>,                                \
         (const void *)forward_scan<V, KIND, AFTER_DONE, IO, kChunkWaves, false, kChunkApply, \
-                                   S, true>,                                                \
+                                   S, F64>,                                                 \
         p, lead, p.out, false, s, stream)
-        if (s.skew) RLCA_CHUNKED(kVecSkew);
-        RLCA_CHUNKED(kVecRows);
+        if (s.skew) {
+            if (s.f64) RLCA_CHUNKED(kVecSkew, true);
+            RLCA_CHUNKED(kVecSkew, false);
+        }
+        if (s.f64) RLCA_CHUNKED(kVecRows, true);
+        RLCA_CHUNKED(kVecRows, false);
 #undef RLCA_CHUNKED
     }
     return launch_full(forward_kernel<V, KIND, AFTER_DONE, S>(s), s, p, lead, stream);

@@ -104,3 +104,26 @@ def test_element_wise_path(beta, gpu_device):
     g = rl.discounted_returns(r, term, gamma=beta)
     assert_parity(g, oracle.discounted_returns(d.rewards, d.terminated, None, None, None,
                                                f32(beta)), f"discounted element-wise beta {beta}")
+
+
+@pytest.mark.parametrize("N,T", SHAPES)
+@pytest.mark.parametrize("gamma,lam", [(0.99, 1.0), (0.999, 0.95)])
+def test_largest_fp32_betas(N, T, gamma, lam, gpu_device):
+    """The largest beta the host still scans in fp32: 0.99 with an exact
+    product, and 0.94905 (0.999 * 0.95, inexact), on every shape above, the
+    tile-carry and chunked paths included, over zero-mean chains that rarely
+    break."""
+    d = rollout(N * 19 + T, N, T)
+    what = f"{N}x{T} gamma {gamma} lambda {lam}"
+    check_disc(d, gpu_device, gamma=gamma * lam, what=what)
+    check_gae(d, gpu_device, gamma=gamma, lam=lam, what=what)
+    check_td(d, gpu_device, gamma=gamma, lam=lam, what=what)
+    check_vtrace(d, gpu_device, gamma=gamma, lam=lam, what=what)
+    check_retrace(d, gpu_device, gamma=lam, lam=gamma, what=what)
+    f = workloads.forward_rollout(N * 23 + T, N, T, p_start=0.0005)
+    for conv in (rl.RESET_ON_START, rl.RESET_AFTER_DONE):
+        flags = f.starts if conv == rl.RESET_ON_START else f.dones
+        e = rl.eligibility_traces(dev(f.rewards, gpu_device), dev(flags, gpu_device), conv,
+                                  gamma, lam)
+        assert_parity(e, oracle.eligibility_traces(f.rewards, flags, conv, f32(gamma), f32(lam)),
+                      f"traces conv {conv} {what}")
