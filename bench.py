@@ -705,15 +705,15 @@ SWEEP_WARMUP_S = 0.2   # untimed launches before each point's trials
 
 # (num_envs, T, estimators) of each sweep grid: "sizes" spans the rollout
 # shapes of the workloads above; "long" spans few long rows on both sides of
-# the chunked path's bounds (rows of 16384 steps or more; fewer than 96
-# rows, fewer than 160 from 32768 steps on, and for eligibility traces fewer
-# than 200 from 131072 steps on: 95, 159 and 199 rows are chunked, 96, 160
-# and 200 take one workgroup per row).
+# the chunked path's bounds (rows of 16384 steps or more; fewer than 160
+# rows, and for eligibility traces fewer than 256 from 32768 steps on and
+# fewer than 320 from 65536 steps on: 159, 255 and 319 rows are chunked,
+# 160, 256 and 320 take one workgroup per row).
 SWEEP_GRIDS = {
     "sizes": ((1024, 4096, 16384, 65536), (128, 512, 2048),
               ("gae+trunc", "retrace+trunc", "eligibility")),
-    "long": ((1, 8, 16, 32, 48, 64, 95, 96, 128, 159, 160, 192, 199, 200, 224, 256),
-             (4100, 8192, 12288, 16384, 32768, 131072, 524288),
+    "long": ((1, 8, 16, 32, 64, 96, 128, 159, 160, 192, 255, 256, 319, 320, 384),
+             (4100, 8192, 12288, 16384, 32768, 65536, 131072, 524288),
              ("gae+trunc", "eligibility")),
 }
 

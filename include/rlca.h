@@ -11,8 +11,8 @@
  * Credit Assignment", paperlayer.ai summary, §1 Introduction and §3.1 Shared
  * scan formulation).  Each estimator call is one kernel launch that reads
  * its inputs from HBM once and writes each output once -- except for few
- * long rows (fewer than 96 rows of 16384..32767 steps, fewer than 160 of
- * 32768 steps or more; for the forward scans fewer than 200 from 131072
+ * long rows (fewer than 160 rows of 16384 steps or more; for the forward
+ * scans fewer than 256 from 32768 steps on and fewer than 320 from 65536
  * steps on), where each row is split into chunks that run in
  * parallel: three launches, inputs read twice, and the first
  * output array holds the chunk hand-off values until the last launch

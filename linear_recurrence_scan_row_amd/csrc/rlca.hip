@@ -139,25 +139,26 @@ static IoChoice io_of(int64_t T, const void *const *ins, int nin, size_t elem,
 // workgroup per row (each walks its tiles one after another), so they are
 // split into 2048-step chunks that run in parallel: three dependent launches,
 // inputs read twice.  Measured on MI355X (GAE with truncation and eligibility
-// traces, both paths at every shape): the three launches cost more than they
-// save below 16384 steps (1.1-2.4x slower at 4100..8192 steps, even at
-// 12288); from 16384 steps on, chunking wins below about 96 rows, and from
-// 32768 steps on below about 160 rows (2x at 64 rows of 131072 steps, 30x
-// for one row of 2^19), while one workgroup per row wins above.  A forward
-// scan's row walk moves fewer bytes per tile, so from 131072 steps on its
-// chunks win up to about 200 rows.
+// traces, both paths at every shape, fp32 chunk scans): the three launches
+// cost more than they save at 8192 steps (1.1-1.9x slower) and gain little at
+// 12288; from 16384 steps on, chunking wins below about 160 rows (1.2-1.6x
+// at 96 rows, 8-40x for one row of 2^17..2^19), while one workgroup per row
+// wins above.  A forward scan's row walk moves fewer bytes per tile, so its
+// chunks win up to about 256 rows from 32768 steps on and about 320 rows
+// from 65536 steps on.
 static constexpr int64_t kChunkedMinSteps = 8 * (int64_t)kChunkSteps;
-static constexpr int64_t kChunkedMaxRows = 96;          // rows of 16384..32767 steps
-static constexpr int64_t kChunkedMaxRowsLong = 160;     // rows of 32768 steps or more
-static constexpr int64_t kChunkedMaxRowsForward = 200;  // forward, 131072 steps or more
+static constexpr int64_t kChunkedMaxRows = 160;            // every scan, 16384 steps or more
+static constexpr int64_t kChunkedMaxRowsForward = 256;     // forward, 32768 steps or more
+static constexpr int64_t kChunkedMaxRowsForwardLong = 320; // forward, 65536 steps or more
 
 static bool take_chunked(int64_t num_envs, int64_t T, bool backward) {
+    if (T < kChunkedMinSteps) return false;
     int64_t rows = kChunkedMaxRows;
-    if (T >= 8 * kChunkedMinSteps && !backward)
+    if (!backward && T >= 4 * kChunkedMinSteps)
+        rows = kChunkedMaxRowsForwardLong;
+    else if (!backward && T >= 2 * kChunkedMinSteps)
         rows = kChunkedMaxRowsForward;
-    else if (T >= 2 * kChunkedMinSteps)
-        rows = kChunkedMaxRowsLong;
-    return T >= kChunkedMinSteps && num_envs < rows;
+    return num_envs < rows;
 }
 static constexpr int64_t kOneWaveMinRows = 4096;
 // Rows of T % K != 0 steps (and inputs or outputs off phase 0) are read

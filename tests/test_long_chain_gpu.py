@@ -1,7 +1,7 @@
 """fp32 results on long chains that never break: beta = 1 over a whole row
 (an episodic prefix sum without resets, discounted returns with gamma = 1 and
 no episode ends), on the chunked path (8 rows) and the tile-carry path
-(128 rows of 16384 steps, 256 rows of 131072), with T % 4 == 0 and
+(160 rows of 16384 steps, 320 rows of 131072), with T % 4 == 0 and
 T % 4 != 0.
 
 Rows longer than one tile carry their scan from tile to tile (and from chunk
@@ -43,7 +43,7 @@ def _rel(g, o):
     return np.abs(g - o) / (1.0 + np.abs(o))
 
 
-@pytest.mark.parametrize("N,T", [(8, 16384), (128, 16384)])
+@pytest.mark.parametrize("N,T", [(8, 16384), (160, 16384)])
 @pytest.mark.parametrize("dist", ["normal", "uniform"])
 def test_long_chain_meets_the_bar(N, T, dist, gpu_device):
     rng = np.random.default_rng(1000 + N + T)
@@ -53,7 +53,7 @@ def test_long_chain_meets_the_bar(N, T, dist, gpu_device):
         assert worst <= TOL, f"{what} N={N} T={T} {dist}: {worst:.3e}"
 
 
-@pytest.mark.parametrize("N,T", [(8, 131072), (256, 131072), (8, 131071), (256, 131071)])
+@pytest.mark.parametrize("N,T", [(8, 131072), (320, 131072), (8, 131071), (320, 131071)])
 def test_very_long_chain(N, T, gpu_device):
     rng = np.random.default_rng(2000 + N + T)
     positive = rng.random((N, T)).astype(np.float32)

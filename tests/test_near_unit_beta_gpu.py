@@ -31,7 +31,7 @@ BETAS = [0.995, 0.999, 0.9999, 1.0]
 # 257..1023 steps); skewed windows (T % 4 != 0); one tile; several tiles;
 # chunked (8 rows of 65536 steps); and short rows
 # that stay fp32 (packed across waves, and wave-local)
-SHAPES = [(64, 512), (4096, 520), (64, 1001), (48, 2048), (96, 16384), (8, 65536), (8, 65533),
+SHAPES = [(64, 512), (4096, 520), (64, 1001), (48, 2048), (160, 16384), (8, 65536), (8, 65533),
           (700, 200), (512, 256)]
 
 
@@ -75,7 +75,7 @@ def test_forward_and_affine(N, T, beta, gpu_device):
                       f"affine dir {direction} {what}")
 
 
-@pytest.mark.parametrize("N,T", [(64, 512), (48, 2048), (96, 16384), (8, 65536)])
+@pytest.mark.parametrize("N,T", [(64, 512), (48, 2048), (160, 16384), (8, 65536)])
 @pytest.mark.parametrize("gamma,lam", [(0.9995, 0.9995), (0.996, 0.97)])
 def test_inexact_products(N, T, gamma, lam, gpu_device):
     """gamma * lambda is not exact in fp32 (beta near 0.999 and 0.966): the

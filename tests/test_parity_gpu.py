@@ -401,18 +401,19 @@ def test_repeat_calls_are_deterministic(gpu_device):
 
 
 # ------------------------------------------------- few long rows: chunked path
-# Few long rows (16384 steps or more; fewer than 96 rows, fewer than 160 from
-# 32768 steps on) are split into chunks that run in parallel: aggregate,
+# Few long rows (16384 steps or more; fewer than 160 rows, and for the
+# forward scans fewer than 256 from 32768 steps on and fewer than 320 from
+# 65536 steps on) are split into chunks that run in parallel: aggregate,
 # chunk carries, apply.  Chunks span 2048 steps for T % 4 == 0, 2040
 # otherwise (the last in scan order 4 to 2043).  Shapes cover an exact
 # multiple of the chunk, a last chunk of 1 step, a short last chunk in scan
 # order, a last chunk longer than the others, single rows, and both sides of
-# each row bound (95 / 96 rows, 159 / 160 rows, and for the forward scans
-# 199 / 200 rows of 131072 steps: the second of each pair takes one
+# each row bound (159 / 160 rows, and for the forward scans 255 / 256 rows of
+# 32768 steps and 319 / 320 rows of 65536: the second of each pair takes one
 # workgroup per row).
 
 LONG_SHAPES = [(3, 16388), (2, 16384), (3, 16385), (5, 20000), (1, 65536), (4, 20480),
-               (95, 16388), (96, 16388), (159, 32768), (160, 32768),
+               (159, 16388), (160, 16388), (159, 32768), (160, 32768),
                # T % 4 != 0: chunk starts at any offset from an aligned step
                (3, 16387), (2, 18363), (2, 18365), (5, 20001), (1, 65537), (95, 16387)]
 
@@ -429,7 +430,8 @@ def test_chunked_backward_estimators(N, T, gpu_device):
         check_retrace(d, gpu_device, trunc=trunc, what=what)
 
 
-@pytest.mark.parametrize("N,T", LONG_SHAPES + [(199, 131072), (200, 131072)])
+@pytest.mark.parametrize("N,T", LONG_SHAPES + [(255, 32768), (256, 32768), (319, 65536),
+                                                 (320, 65536)])
 def test_chunked_forward_scans(N, T, gpu_device):
     f = workloads.forward_rollout(400 + N + T, N, T, p_start=0.002)
     for conv in (rl.RESET_ON_START, rl.RESET_AFTER_DONE):
