@@ -249,6 +249,16 @@ def test_workspace_size_queries(lib):
     # or inputs off phase 0; the size covers whichever the pointers select
     assert lib.rlca_gae_stats_workspace_size(3, 100000) == 4224 + 16 * 3 * 50
     assert lib.rlca_gae_stats_workspace_size(3, 100001) == 4224 + 16 * 3 * 50
+    # the chunked path's bounds for backward scans: rows of 16384 steps or
+    # more, fewer than 160 of them (one pair per chunk: 9 chunks of 16388 or
+    # 16384 steps, 17 of 32768 at 2040 steps each); otherwise one row per
+    # workgroup (rows longer than a 2048-step tile), or several short rows
+    assert lib.rlca_gae_stats_workspace_size(159, 16388) == 4224 + 16 * 159 * 9
+    assert lib.rlca_gae_stats_workspace_size(160, 16388) == 4224 + 16 * 160
+    assert lib.rlca_gae_stats_workspace_size(159, 32768) == 4224 + 16 * 159 * 17
+    assert lib.rlca_gae_stats_workspace_size(160, 32768) == 4224 + 16 * 160
+    assert lib.rlca_gae_stats_workspace_size(1, 16384) == 4224 + 16 * 9
+    assert lib.rlca_gae_stats_workspace_size(1, 16383) == 4224 + 16 * 1
     assert lib.rlca_ppo_clip_loss_workspace_size(4096, 128) == 4224 + 8 * 512
     assert lib.rlca_ppo_clip_loss_workspace_size(1 << 20, 512) == 4224 + 8 * 2048
 
