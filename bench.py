@@ -705,14 +705,14 @@ SWEEP_WARMUP_S = 0.2   # untimed launches before each point's trials
 
 # (num_envs, T, estimators) of each sweep grid: "sizes" spans the rollout
 # shapes of the workloads above; "long" spans few long rows on both sides of
-# the chunked path's bounds (rows of 16384 steps or more; fewer than 160
-# rows, and for eligibility traces fewer than 256 from 32768 steps on and
-# fewer than 320 from 65536 steps on: 159, 255 and 319 rows are chunked,
-# 160, 256 and 320 take one workgroup per row).
+# the chunked path's bounds (backward rows of 16384 steps or more, fewer than
+# 128; forward rows of 32768 steps or more, fewer than 160, and fewer than
+# 208 from 65536 steps on: 127, 159 and 207 rows are chunked, 128, 160 and
+# 208 take one workgroup per row).
 SWEEP_GRIDS = {
     "sizes": ((1024, 4096, 16384, 65536), (128, 512, 2048),
               ("gae+trunc", "retrace+trunc", "eligibility")),
-    "long": ((1, 8, 16, 32, 64, 96, 128, 159, 160, 192, 255, 256, 319, 320, 384),
+    "long": ((1, 8, 16, 32, 64, 96, 127, 128, 159, 160, 192, 207, 208, 256, 384),
              (4100, 8192, 12288, 16384, 32768, 65536, 131072, 524288),
              ("gae+trunc", "eligibility")),
 }

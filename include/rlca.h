@@ -11,9 +11,9 @@
  * Credit Assignment", paperlayer.ai summary, §1 Introduction and §3.1 Shared
  * scan formulation).  Each estimator call is one kernel launch that reads
  * its inputs from HBM once and writes each output once -- except for few
- * long rows (fewer than 160 rows of 16384 steps or more; for the forward
- * scans fewer than 256 from 32768 steps on and fewer than 320 from 65536
- * steps on), where each row is split into chunks that run in
+ * long rows (fewer than 128 rows of 16384 steps or more; for the forward
+ * scans fewer than 160 rows of 32768 steps or more and fewer than 208 from
+ * 65536 steps on), where each row is split into chunks that run in
  * parallel: three launches, inputs read twice, and the first
  * output array holds the chunk hand-off values until the last launch
  * overwrites them.  The fused consumers of GAE at the end of this header

@@ -1370,6 +1370,8 @@ const void *backward_kernel(const LaunchShape &s) {
     if (s.waves == 8 && !s.wave_local) RLCA_PICK_F64(kVecRows, 8);
     if (s.waves == 1) RLCA_PICK_F64(kVecRows, 1);
 #undef RLCA_PICK_F64
+    if (s.waves == 16)  // rows of several 4096-step tiles, fp32 scans only
+        return (const void *)backward_scan<EST, TRUNC, kVecRows, 16, false, kFull, S, STATS>;
 #define RLCA_PICK(NW)                                                                          \
     return s.wave_local                                                                        \
                ? (const void *)backward_scan<EST, TRUNC, kVecRows, NW, true, kFull, S, STATS> \
@@ -1434,6 +1436,8 @@ const void *forward_kernel(const LaunchShape &s) {
     if (s.waves == 8 && !s.wave_local) RLCA_PICK_F64(kVecRows, 8);
     if (s.waves == 1) RLCA_PICK_F64(kVecRows, 1);
 #undef RLCA_PICK_F64
+    if (s.waves == 16)  // rows of several 4096-step tiles, fp32 scans only
+        return (const void *)forward_scan<V, KIND, AFTER_DONE, kVecRows, 16, false, kFull, S>;
 #define RLCA_PICK(NW)                                                                          \
     return s.wave_local                                                                        \
                ? (const void *)forward_scan<V, KIND, AFTER_DONE, kVecRows, NW, true, kFull, S> \

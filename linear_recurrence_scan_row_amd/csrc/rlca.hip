@@ -139,28 +139,36 @@ static IoChoice io_of(int64_t T, const void *const *ins, int nin, size_t elem,
 // workgroup per row (each walks its tiles one after another), so they are
 // split into 2048-step chunks that run in parallel: three dependent launches,
 // inputs read twice.  Measured on MI355X (GAE with truncation and eligibility
-// traces, both paths at every shape, fp32 chunk scans): the three launches
-// cost more than they save at 8192 steps (1.1-1.9x slower) and gain little at
-// 12288; from 16384 steps on, chunking wins below about 160 rows (1.2-1.6x
-// at 96 rows, 8-40x for one row of 2^17..2^19), while one workgroup per row
-// wins above.  A forward scan's row walk moves fewer bytes per tile, so its
-// chunks win up to about 256 rows from 32768 steps on and about 320 rows
-// from 65536 steps on.
+// traces, both paths at every shape, fp32 chunk scans, 16-wave row walks where
+// those apply): the three launches cost more than they save below 16384 steps
+// (1.2-2.1x slower at 8192, even at 12288); from 16384 steps on, a backward
+// scan's chunks win below about 128 rows (1.05x slower at 128, 2-30x faster
+// for one row of 2^15..2^19).  A forward scan's row walk moves fewer bytes
+// per tile, so its chunks only win from 32768 steps on: below about 160 rows
+// there, and below about 208 rows from 65536 steps on.
 static constexpr int64_t kChunkedMinSteps = 8 * (int64_t)kChunkSteps;
-static constexpr int64_t kChunkedMaxRows = 160;            // every scan, 16384 steps or more
-static constexpr int64_t kChunkedMaxRowsForward = 256;     // forward, 32768 steps or more
-static constexpr int64_t kChunkedMaxRowsForwardLong = 320; // forward, 65536 steps or more
+static constexpr int64_t kChunkedMaxRows = 128;                  // backward, 16384+ steps
+static constexpr int64_t kChunkedForwardMinSteps = 2 * kChunkedMinSteps;
+static constexpr int64_t kChunkedMaxRowsForward = 160;           // forward, 32768+ steps
+static constexpr int64_t kChunkedMaxRowsForwardLong = 208;       // forward, 65536+ steps
 
 static bool take_chunked(int64_t num_envs, int64_t T, bool backward) {
-    if (T < kChunkedMinSteps) return false;
-    int64_t rows = kChunkedMaxRows;
-    if (!backward && T >= 4 * kChunkedMinSteps)
-        rows = kChunkedMaxRowsForwardLong;
-    else if (!backward && T >= 2 * kChunkedMinSteps)
-        rows = kChunkedMaxRowsForward;
-    return num_envs < rows;
+    if (backward) return T >= kChunkedMinSteps && num_envs < kChunkedMaxRows;
+    if (T < kChunkedForwardMinSteps) return false;
+    return num_envs < (T >= 2 * kChunkedForwardMinSteps ? kChunkedMaxRowsForwardLong
+                                                        : kChunkedMaxRowsForward);
 }
 static constexpr int64_t kOneWaveMinRows = 4096;
+// Rows of 4096 steps or more walk their tiles one after another, one memory
+// round trip per tile.  With at most 512 of them, 16-wave workgroups (4096-step
+// tiles) put twice the bytes in flight per row and fill the chip's wave slots:
+// measured on MI355X, 10-25% faster than 8-wave ones at 160..512 rows of
+// 4096..131072 steps (GAE with truncation, eligibility traces), and mixed to
+// slower from 1024 rows on, where 8-wave workgroups already fill the chip.
+// Results are bit for bit those of 8-wave tiles: the carry passes through the
+// same wave totals in the same order.  fp64 scans keep 8 waves.
+static constexpr int64_t kWideMinSteps = 4096;
+static constexpr int64_t kWideMaxRows = 512;
 // Rows of T % K != 0 steps (and inputs or outputs off phase 0) are read
 // K-wide from windows widened to block boundaries, in 8-wave workgroups for
 // every T (one-wave
@@ -210,6 +218,8 @@ static void set_precision(LaunchShape &s, int64_t T, BetaBound beta, bool is_int
     const bool fp32_ok = beta.max <= 0.95f || (beta.exact && beta.max <= 0.99f) ||
                          (beta.exact && beta.max == 1.f && T <= (int64_t)kChunkSteps);
     s.f64 = !is_int && !s.wave_local && T > kWave * kK && !fp32_ok;
+    // the fp64 scans' registers allow one 16-wave workgroup per CU only
+    if (s.f64 && s.waves == 16) s.waves = 8;
 }
 
 static LaunchShape choose_shape(int64_t num_envs, int64_t T, const IoChoice &io,
@@ -222,6 +232,8 @@ static LaunchShape choose_shape(int64_t num_envs, int64_t T, const IoChoice &io,
     s.scatter = s.skew && io.scatter;
     s.wave_local = io.io == kVecRows && T <= kWave * kK && (kWave * kK) % T == 0;
     s.waves = (T <= kWave * kK || T >= 1024 || num_envs < kOneWaveMinRows) ? 8 : 1;
+    if (s.vec && io.io == kVecRows && T >= kWideMinSteps && num_envs <= kWideMaxRows)
+        s.waves = 16;
     s.chunked = s.vec && take_chunked(num_envs, T, backward);
     s.f64 = false;  // set_precision
     s.quantum = 1;

@@ -250,13 +250,13 @@ def test_workspace_size_queries(lib):
     assert lib.rlca_gae_stats_workspace_size(3, 100000) == 4224 + 16 * 3 * 50
     assert lib.rlca_gae_stats_workspace_size(3, 100001) == 4224 + 16 * 3 * 50
     # the chunked path's bounds for backward scans: rows of 16384 steps or
-    # more, fewer than 160 of them (one pair per chunk: 9 chunks of 16388 or
+    # more, fewer than 128 of them (one pair per chunk: 9 chunks of 16388 or
     # 16384 steps, 17 of 32768 at 2040 steps each); otherwise one row per
-    # workgroup (rows longer than a 2048-step tile), or several short rows
-    assert lib.rlca_gae_stats_workspace_size(159, 16388) == 4224 + 16 * 159 * 9
-    assert lib.rlca_gae_stats_workspace_size(160, 16388) == 4224 + 16 * 160
-    assert lib.rlca_gae_stats_workspace_size(159, 32768) == 4224 + 16 * 159 * 17
-    assert lib.rlca_gae_stats_workspace_size(160, 32768) == 4224 + 16 * 160
+    # workgroup (rows longer than a tile), or several short rows
+    assert lib.rlca_gae_stats_workspace_size(127, 16388) == 4224 + 16 * 127 * 9
+    assert lib.rlca_gae_stats_workspace_size(128, 16388) == 4224 + 16 * 128
+    assert lib.rlca_gae_stats_workspace_size(127, 32768) == 4224 + 16 * 127 * 17
+    assert lib.rlca_gae_stats_workspace_size(128, 32768) == 4224 + 16 * 128
     assert lib.rlca_gae_stats_workspace_size(1, 16384) == 4224 + 16 * 9
     assert lib.rlca_gae_stats_workspace_size(1, 16383) == 4224 + 16 * 1
     assert lib.rlca_ppo_clip_loss_workspace_size(4096, 128) == 4224 + 8 * 512

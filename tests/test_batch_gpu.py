@@ -145,7 +145,7 @@ def mixed_members(device):
         Member("prefix", 14, 12, 2048, device, int_input=True, conv=rl.RESET_AFTER_DONE),
         Member("affine", 15, 80, 256, device, direction=rl.BACKWARD),
         Member("affine", 16, 11, 520, device, direction=rl.FORWARD, boot=False),
-        Member("affine", 17, 2, 20000, device, direction=rl.FORWARD),  # chunked forward
+        Member("affine", 17, 2, 40000, device, direction=rl.FORWARD),  # chunked forward
         Member("gae", 18, 0, 128, device),                       # empty
         # one-wave members (>= 4096 rows of 257..1023 steps), the last
         # workgroup of each only partly filled

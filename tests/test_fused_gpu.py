@@ -43,7 +43,8 @@ def rollout_args(seed, N, T, trunc=True):
 
 
 # launch shapes: T % 4 != 0 (windows widened to aligned starts), wave-local,
-# one-wave, eight-wave, chunked; the last two also with T % 4 != 0
+# eight-wave, 16-wave (3 rows of 4100 steps), chunked, one-wave, and chunked
+# with T % 4 != 0
 SHAPES = [(7, 37), (1, 1), (2, 2), (300, 128), (4096, 128), (33, 512), (4096, 300), (9, 1024),
           (3, 4100), (2, 20000), (4097, 301), (2, 20001)]
 

@@ -24,10 +24,12 @@ UNIT_ROUNDOFF = {torch.bfloat16: 2.0 ** -8, torch.float16: 2.0 ** -11}
 DTYPES = [torch.bfloat16, torch.float16]
 # T % 4 != 0 (windows widened to aligned starts), wave-local, eight-wave (rows
 # sharing tiles), one-wave (>= 4096 rows of 257..1023 steps, with T % 4 == 0
-# and not), eight-wave, chunked (few long rows, with T % 4 == 0 and not, and
-# both sides of the 160-row bound)
-SHAPES = [(5, 37), (300, 128), (33, 512), (4097, 300), (4097, 301), (9, 1024), (3, 16400),
-          (3, 16401), (2, 20000), (159, 16388), (160, 16388)]
+# and not), eight-wave, 16-wave (rows of 4096+ steps), chunked (few long
+# rows, with T % 4 == 0 and not: backward from 16384 steps, forward from
+# 32768, and both sides of the backward 128-row bound)
+SHAPES = [(5, 37), (300, 128), (33, 512), (4097, 300), (4097, 301), (9, 1024), (5, 8192),
+          (3, 16400), (3, 16401), (2, 20000), (127, 16388), (128, 16388), (3, 32772),
+          (3, 32773)]
 
 
 def assert_lowp(gpu, ref, dtype, what):

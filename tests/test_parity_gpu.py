@@ -136,7 +136,11 @@ SHAPES = [(1, 1), (3, 1), (2, 2), (5, 3), (7, 5), (8, 16), (3, 63), (2, 64), (5,
           (6, 2046), (5, 2047), (4097, 2047),
           # rows of 257..1023 steps (T % 4 == 0) take one-wave workgroups from
           # 4096 rows on; with T % 4 != 0, 8-wave ones
-          (4096, 260), (4099, 516), (4096, 1020), (4097, 301), (4096, 511), (4099, 1023)]
+          (4096, 260), (4099, 516), (4096, 1020), (4097, 301), (4096, 511), (4099, 1023),
+          # rows of 4096 steps or more (T % 4 == 0) take 16-wave workgroups up
+          # to 512 rows: one tile, a partial second tile, several tiles; 513
+          # rows take 8-wave ones
+          (1, 4096), (3, 5000), (2, 8192), (4, 12292), (512, 4100), (513, 4100)]
 
 
 @pytest.mark.parametrize("N,T", SHAPES)
@@ -401,19 +405,19 @@ def test_repeat_calls_are_deterministic(gpu_device):
 
 
 # ------------------------------------------------- few long rows: chunked path
-# Few long rows (16384 steps or more; fewer than 160 rows, and for the
-# forward scans fewer than 256 from 32768 steps on and fewer than 320 from
-# 65536 steps on) are split into chunks that run in parallel: aggregate,
-# chunk carries, apply.  Chunks span 2048 steps for T % 4 == 0, 2040
-# otherwise (the last in scan order 4 to 2043).  Shapes cover an exact
-# multiple of the chunk, a last chunk of 1 step, a short last chunk in scan
-# order, a last chunk longer than the others, single rows, and both sides of
-# each row bound (159 / 160 rows, and for the forward scans 255 / 256 rows of
-# 32768 steps and 319 / 320 rows of 65536: the second of each pair takes one
+# Few long rows are split into chunks that run in parallel: aggregate, chunk
+# carries, apply.  Backward scans chunk rows of 16384 steps or more when
+# there are fewer than 128; forward scans rows of 32768 steps or more, fewer
+# than 160 of them, or fewer than 208 from 65536 steps on.  Chunks span 2048
+# steps for T % 4 == 0, 2040 otherwise (the last in scan order 4 to 2043).
+# Shapes cover an exact multiple of the chunk, a last chunk of 1 step, a
+# short last chunk in scan order, a last chunk longer than the others,
+# single rows, and both sides of each row bound (127 / 128 rows backward,
+# 159 / 160 and 207 / 208 forward: the second of each pair takes one
 # workgroup per row).
 
 LONG_SHAPES = [(3, 16388), (2, 16384), (3, 16385), (5, 20000), (1, 65536), (4, 20480),
-               (159, 16388), (160, 16388), (159, 32768), (160, 32768),
+               (127, 16388), (128, 16388), (127, 32768), (128, 32768),
                # T % 4 != 0: chunk starts at any offset from an aligned step
                (3, 16387), (2, 18363), (2, 18365), (5, 20001), (1, 65537), (95, 16387)]
 
@@ -430,8 +434,13 @@ def test_chunked_backward_estimators(N, T, gpu_device):
         check_retrace(d, gpu_device, trunc=trunc, what=what)
 
 
-@pytest.mark.parametrize("N,T", LONG_SHAPES + [(255, 32768), (256, 32768), (319, 65536),
-                                                 (320, 65536)])
+LONG_FORWARD_SHAPES = [(3, 32772), (2, 32768), (3, 32769), (5, 40000), (1, 65536), (4, 36864),
+                       (159, 32772), (160, 32772), (207, 65536), (208, 65536),
+                       # T % 4 != 0
+                       (3, 32771), (2, 34683), (2, 34685), (5, 40001), (1, 65537), (95, 32771)]
+
+
+@pytest.mark.parametrize("N,T", LONG_FORWARD_SHAPES)
 def test_chunked_forward_scans(N, T, gpu_device):
     f = workloads.forward_rollout(400 + N + T, N, T, p_start=0.002)
     for conv in (rl.RESET_ON_START, rl.RESET_AFTER_DONE):

@@ -57,7 +57,7 @@ def test_random_case(case, gpu_device):
     elif kind == "long":
         N, T = int(rng.integers(1, 200)), int(rng.integers(1000, 5000))
     else:
-        N, T = int(rng.integers(1, 160)), int(rng.integers(16384, 40000))
+        N, T = int(rng.integers(1, 160)), int(rng.integers(16384, 70000))
     p_term, p_trunc = rng.choice([0.0, 0.01, 0.2, 0.9]), rng.choice([0.0, 0.005, 0.3])
     gamma, lam = float(rng.choice([0.0, 0.5, 0.99, 1.0])), float(rng.choice([0.0, 0.9, 1.0]))
     f32 = lambda *s: rng.standard_normal(s).astype(np.float32)      # noqa: E731
