@@ -1366,12 +1366,13 @@ const void *backward_kernel(const LaunchShape &s) {
                ? (const void *)backward_scan<EST, TRUNC, IO, NW, false, kFull, S, STATS, true> \
                : (const void *)backward_scan<EST, TRUNC, IO, NW, false, kFull, S, STATS, false>
     if (!s.vec) RLCA_PICK_F64(kScalarIO, 4);
+    if (s.waves == 16)  // rows of several 4096-step tiles, fp32 scans only
+        return s.skew ? (const void *)backward_scan<EST, TRUNC, kVecSkew, 16, false, kFull, S, STATS>
+                      : (const void *)backward_scan<EST, TRUNC, kVecRows, 16, false, kFull, S, STATS>;
     if (s.skew) RLCA_PICK_F64(kVecSkew, 8);
     if (s.waves == 8 && !s.wave_local) RLCA_PICK_F64(kVecRows, 8);
     if (s.waves == 1) RLCA_PICK_F64(kVecRows, 1);
 #undef RLCA_PICK_F64
-    if (s.waves == 16)  // rows of several 4096-step tiles, fp32 scans only
-        return (const void *)backward_scan<EST, TRUNC, kVecRows, 16, false, kFull, S, STATS>;
 #define RLCA_PICK(NW)                                                                          \
     return s.wave_local                                                                        \
                ? (const void *)backward_scan<EST, TRUNC, kVecRows, NW, true, kFull, S, STATS> \
@@ -1432,12 +1433,13 @@ const void *forward_kernel(const LaunchShape &s) {
                ? (const void *)forward_scan<V, KIND, AFTER_DONE, IO, NW, false, kFull, S, true> \
                : (const void *)forward_scan<V, KIND, AFTER_DONE, IO, NW, false, kFull, S, false>
     if (!s.vec) RLCA_PICK_F64(kScalarIO, 4);
+    if (s.waves == 16)  // rows of several 4096-step tiles, fp32 scans only
+        return s.skew ? (const void *)forward_scan<V, KIND, AFTER_DONE, kVecSkew, 16, false, kFull, S>
+                      : (const void *)forward_scan<V, KIND, AFTER_DONE, kVecRows, 16, false, kFull, S>;
     if (s.skew) RLCA_PICK_F64(kVecSkew, 8);
     if (s.waves == 8 && !s.wave_local) RLCA_PICK_F64(kVecRows, 8);
     if (s.waves == 1) RLCA_PICK_F64(kVecRows, 1);
 #undef RLCA_PICK_F64
-    if (s.waves == 16)  // rows of several 4096-step tiles, fp32 scans only
-        return (const void *)forward_scan<V, KIND, AFTER_DONE, kVecRows, 16, false, kFull, S>;
 #define RLCA_PICK(NW)                                                                          \
     return s.wave_local                                                                        \
                ? (const void *)forward_scan<V, KIND, AFTER_DONE, kVecRows, NW, true, kFull, S> \

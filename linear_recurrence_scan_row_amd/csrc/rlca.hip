@@ -161,14 +161,18 @@ static bool take_chunked(int64_t num_envs, int64_t T, bool backward) {
 static constexpr int64_t kOneWaveMinRows = 4096;
 // Rows of 4096 steps or more walk their tiles one after another, one memory
 // round trip per tile.  With at most 512 of them, 16-wave workgroups (4096-step
-// tiles) put twice the bytes in flight per row and fill the chip's wave slots:
+// tiles, on both vector paths) put twice the bytes in flight per row and fill
+// the chip's wave slots:
 // measured on MI355X, 10-25% faster than 8-wave ones at 160..512 rows of
 // 4096..131072 steps (GAE with truncation, eligibility traces), and mixed to
 // slower from 1024 rows on, where 8-wave workgroups already fill the chip.
+// Skewed windows (T % 4 != 0) gain 6-28% up to 256 rows and are mixed at
+// 512 (GAE 8% slower at 4101..8195 steps).
 // Results are bit for bit those of 8-wave tiles: the carry passes through the
 // same wave totals in the same order.  fp64 scans keep 8 waves.
 static constexpr int64_t kWideMinSteps = 4096;
 static constexpr int64_t kWideMaxRows = 512;
+static constexpr int64_t kWideMaxRowsSkewed = 256;
 // Rows of T % K != 0 steps (and inputs or outputs off phase 0) are read
 // K-wide from windows widened to block boundaries, in 8-wave workgroups for
 // every T (one-wave
@@ -232,13 +236,14 @@ static LaunchShape choose_shape(int64_t num_envs, int64_t T, const IoChoice &io,
     s.scatter = s.skew && io.scatter;
     s.wave_local = io.io == kVecRows && T <= kWave * kK && (kWave * kK) % T == 0;
     s.waves = (T <= kWave * kK || T >= 1024 || num_envs < kOneWaveMinRows) ? 8 : 1;
-    if (s.vec && io.io == kVecRows && T >= kWideMinSteps && num_envs <= kWideMaxRows)
+    if (s.vec && T >= kWideMinSteps &&
+        num_envs <= (s.skew ? kWideMaxRowsSkewed : kWideMaxRows))
         s.waves = 16;
     s.chunked = s.vec && take_chunked(num_envs, T, backward);
     s.f64 = false;  // set_precision
     s.quantum = 1;
     if (s.skew) {
-        s.waves = 8;
+        if (s.waves != 16) s.waves = 8;
         const int64_t tile = (int64_t)s.waves * kWave * kK;
         const int64_t q = aligned_rows((uint32_t)T);
         if (!s.chunked && T <= tile && T + max_skew((uint32_t)T, s.phase) > tile &&

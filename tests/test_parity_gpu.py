@@ -137,10 +137,11 @@ SHAPES = [(1, 1), (3, 1), (2, 2), (5, 3), (7, 5), (8, 16), (3, 63), (2, 64), (5,
           # rows of 257..1023 steps (T % 4 == 0) take one-wave workgroups from
           # 4096 rows on; with T % 4 != 0, 8-wave ones
           (4096, 260), (4099, 516), (4096, 1020), (4097, 301), (4096, 511), (4099, 1023),
-          # rows of 4096 steps or more (T % 4 == 0) take 16-wave workgroups up
-          # to 512 rows: one tile, a partial second tile, several tiles; 513
-          # rows take 8-wave ones
-          (1, 4096), (3, 5000), (2, 8192), (4, 12292), (512, 4100), (513, 4100)]
+          # rows of 4096 steps or more take 16-wave workgroups up to 512 rows
+          # (256 with T % 4 != 0, skewed windows): one tile, a partial second
+          # tile, several tiles; 513 (257) rows take 8-wave ones
+          (1, 4096), (3, 5000), (2, 8192), (4, 12292), (512, 4100), (513, 4100),
+          (1, 4097), (3, 5001), (2, 8195), (4, 12291), (256, 4101), (257, 4101)]
 
 
 @pytest.mark.parametrize("N,T", SHAPES)
@@ -259,7 +260,7 @@ def test_flags_as_bool_and_nonzero_bytes(gpu_device):
     assert torch.equal(a1, a2) and torch.equal(a1, a3)
 
 
-@pytest.mark.parametrize("T", [132, 131])
+@pytest.mark.parametrize("T", [132, 131, 4100, 4097])
 @pytest.mark.parametrize("shifts", [(1, 1, 1, 1, 1), (1, 2, 1, 1, 1), (0, 0, 3, 0, 0)])
 def test_views_off_16_byte_alignment(T, shifts, gpu_device):
     """Inputs that are 4-byte but not 16-byte aligned (views at an element
