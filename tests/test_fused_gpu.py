@@ -43,10 +43,12 @@ def rollout_args(seed, N, T, trunc=True):
 
 
 # launch shapes: T % 4 != 0 (windows widened to aligned starts), wave-local,
-# eight-wave, 16-wave (3 rows of 4100 steps), chunked, one-wave, and chunked
-# with T % 4 != 0
+# eight-wave, 16-wave (up to 256 rows of 4096+ steps, T % 4 == 0 and not),
+# chunked, one-wave, and chunked with T % 4 != 0; 300 rows of 4100 steps run
+# the statistics at 8 waves and plain GAE at 16, whose advantages must agree
+# bit for bit
 SHAPES = [(7, 37), (1, 1), (2, 2), (300, 128), (4096, 128), (33, 512), (4096, 300), (9, 1024),
-          (3, 4100), (2, 20000), (4097, 301), (2, 20001)]
+          (3, 4100), (200, 4100), (200, 4101), (300, 4100), (2, 20000), (4097, 301), (2, 20001)]
 
 
 @pytest.mark.parametrize("N,T", SHAPES)
