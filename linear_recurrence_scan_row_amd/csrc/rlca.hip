@@ -159,18 +159,18 @@ static bool take_chunked(int64_t num_envs, int64_t T, bool backward) {
                                                         : kChunkedMaxRowsForward);
 }
 static constexpr int64_t kOneWaveMinRows = 4096;
-// Rows of 4096 steps or more walk their tiles one after another, one memory
-// round trip per tile.  With at most 512 of them, 16-wave workgroups (4096-step
-// tiles, on both vector paths) put twice the bytes in flight per row and fill
-// the chip's wave slots:
-// measured on MI355X, 10-25% faster than 8-wave ones at 160..512 rows of
-// 4096..131072 steps (GAE with truncation, eligibility traces), and mixed to
-// slower from 1024 rows on, where 8-wave workgroups already fill the chip.
-// Skewed windows (T % 4 != 0) gain 6-28% up to 256 rows and are mixed at
-// 512 (GAE 8% slower at 4101..8195 steps).
-// Results are bit for bit those of 8-wave tiles: the carry passes through the
-// same wave totals in the same order.  fp64 scans keep 8 waves.
-static constexpr int64_t kWideMinSteps = 4096;
+// Rows longer than one 2048-step tile walk their tiles one after another, one
+// memory round trip per tile.  With at most 512 of them, 16-wave workgroups
+// (4096-step tiles, on both vector paths) put twice the bytes in flight per
+// row and fill the chip's wave slots: measured on MI355X (GAE with
+// truncation, eligibility traces), 10-21% faster than 8-wave ones at 64..512
+// rows of 2049..4095 steps and 10-25% at 160..512 rows of 4096..131072, and
+// mixed to slower from 1024 rows on, where 8-wave workgroups already fill the
+// chip.  Skewed windows (T % 4 != 0) gain 6-28% up to 256 rows and are mixed
+// at 512 (GAE 8% slower at 4101..8195 steps).  Results are bit for bit those
+// of 8-wave tiles: the carry passes through the same wave totals in the same
+// order.  fp64 scans keep 8 waves.
+static constexpr int64_t kWideMinSteps = 2 * kChunkSteps + 1;  // longer than one 8-wave tile
 static constexpr int64_t kWideMaxRows = 512;
 static constexpr int64_t kWideMaxRowsSkewed = 256;
 // Rows of T % K != 0 steps (and inputs or outputs off phase 0) are read

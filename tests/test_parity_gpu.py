@@ -137,10 +137,12 @@ SHAPES = [(1, 1), (3, 1), (2, 2), (5, 3), (7, 5), (8, 16), (3, 63), (2, 64), (5,
           # rows of 257..1023 steps (T % 4 == 0) take one-wave workgroups from
           # 4096 rows on; with T % 4 != 0, 8-wave ones
           (4096, 260), (4099, 516), (4096, 1020), (4097, 301), (4096, 511), (4099, 1023),
-          # rows of 4096 steps or more take 16-wave workgroups up to 512 rows
-          # (256 with T % 4 != 0, skewed windows): one tile, a partial second
-          # tile, several tiles; 513 (257) rows take 8-wave ones
-          (1, 4096), (3, 5000), (2, 8192), (4, 12292), (512, 4100), (513, 4100),
+          # rows longer than 2048 steps take 16-wave workgroups up to 512 rows
+          # (256 with T % 4 != 0, skewed windows): one partial tile, one
+          # tile, a partial second tile, several tiles; 513 (257) rows take
+          # 8-wave ones
+          (3, 2052), (2, 3000), (512, 2500), (513, 2500), (1, 4096), (3, 5000), (2, 8192),
+          (4, 12292), (512, 4100), (513, 4100), (5, 3001), (256, 3001), (257, 3001),
           (1, 4097), (3, 5001), (2, 8195), (4, 12291), (256, 4101), (257, 4101)]
 
 
