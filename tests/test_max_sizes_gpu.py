@@ -1,7 +1,8 @@
 """The largest calls: more than 2^31 env-steps in one call, so that every flat
 index passes 32 bits, on each launch shape (rows spanning waves, wave-local
 rows, one-wave row walks, skewed windows, all in grids of more than 2^20
-workgroups); 2^31 rows of one step, the most rows the ABI takes; and rows of
+workgroups, and 512 rows of 2^22 + 4 steps walked by 16-wave workgroups);
+2^31 rows of one step, the most rows the ABI takes; and rows of
 2^30 steps, the longest, on the chunked path (1.5 million chunks).
 
 Inputs are drawn on the device (workloads.device_rollout, seeded).  Outputs
@@ -67,6 +68,7 @@ SHAPES = [
     pytest.param(2**24 + 5, 128, id="wave-local rows"),
     pytest.param(2**22 + 1, 512, id="one-wave row walks"),
     pytest.param(2**21 + 4099, 1023, id="skewed windows"),
+    pytest.param(512, 2**22 + 4, id="16-wave row walks"),
 ]
 
 

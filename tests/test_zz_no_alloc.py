@@ -17,9 +17,10 @@ from linear_recurrence_scan_row_amd import workloads
 pytestmark = pytest.mark.gpu
 
 # 4096 x 128: 256 partials; 300 x 77: fewer (skewed windows); then a
-# one-wave shape, a chunked row pair and 16384 x 512 (the 4096-workgroup cap)
+# one-wave shape, a chunked row pair, 16-wave workgroups (200 rows of 4100
+# steps) and 16384 x 512 (the 4096-workgroup cap)
 SEQUENCE = [(4096, 128, True), (300, 77, False), (4097, 301, True), (2, 20001, True),
-            (16384, 512, False), (5, 9, True), (4096, 128, True)]
+            (200, 4100, True), (16384, 512, False), (5, 9, True), (4096, 128, True)]
 
 
 def args_for(seed, N, T, trunc):
